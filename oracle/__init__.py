@@ -1,0 +1,14 @@
+"""CPU oracle for CSA / HCA (test infrastructure only).
+
+Only the test suite, the repository entry module's smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product path (the
+HIP library and its Python binding) never imports, calls or links it.
+"""
+
+from .csa_oracle import *  # noqa: F401,F403
+from .csa_oracle import (  # noqa: F401  (explicit re-exports for linters)
+    visible_entries, read_counts, compress_overlap, compress_pool,
+    compress_weights_overlap, compress_weights_pool, index_scores, topk_select,
+    index_topk, attend_entries, csa_attend, hca_attend, hca_layer, csa_layer,
+    CsaDecodeState, default_scale, window_rows,
+)

@@ -1,0 +1,390 @@
+"""Plain CPU oracle for one layer of compressed sparse attention (CSA) and its
+heavier-compression sibling (HCA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this module: only the test suite, the smoke check in the repository's
+entry module and the CPU-baseline leg of the benchmark use it.  It shares no
+code with the HIP library and never reads anything the GPU produced.
+
+Every routine is the plain definition written out in float64 NumPy, looping
+or broadcasting in the order the pages state; none is blocked, fused or
+reordered for speed.  Sources (web pages, cited by site, title and section):
+
+  [P1] polysight "06-formulas" (Liang Wenfeng voices), section B9 "CSA + HCA"
+  [P2] songhuiming "DeepSeek-V4 百万 token 上下文", sections 4.1-4.5, 5.1-5.2, 7
+  [P3] AirCoding "deepseek-paper-analysis", sections 7.1-7.3 and 7.6
+  [P5] cooking-agi "DeepSeek-V4: 压缩历史以后，还能读到什么？", sections 2-3
+
+Readings taken where the pages are silent or garbled (each also listed in the
+design notes):
+  * causal visibility: a query at 0-based position t may read compressed entry
+    s iff s < (t + 1) // m ([P5] section 3; [P1]/[P2] write floor(t/m), which
+    would hide an entry that is already complete at t = m(i+1) - 1);
+  * the compressor softmax runs over the 2m rows separately for every one of
+    the c dimensions ([P2] section 4.1: the 2m weights sum to one per dim);
+  * the sink logit adds exp(z'_h) to the softmax denominator only and is not
+    multiplied by the softmax scale ([P1] B9, [P2] sections 4.5/7.3);
+  * softmax scale is an explicit argument (1/sqrt(c) by default); the pages
+    never state it;
+  * index ties: the lower entry index wins the last slot; indices are returned
+    ascending and padded with -1;
+  * fewer than k visible entries: all of them are read ([P1] B9 read count
+    min(k, n/m); [P5] section 2 ledger);
+  * the sliding window for position t holds raw rows max(0, t-n_win+1)..t and
+    is kept separate from the compressed entries, never de-duplicated ([P5]
+    section 2).
+
+parity unpinned: none of the routines here.  Each has at least one test that
+pins it to something other than itself (closed forms, invariants, library
+routines, brute force or the pages' worked numbers).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=F64)
+
+
+# --------------------------------------------------------------------------
+# Causality and the read ledger
+# --------------------------------------------------------------------------
+
+def visible_entries(t: int, m: int) -> int:
+    """Number of compressed entries a query at 0-based position t may read.
+
+    [P5] section 3 (future leakage): after the query at t has been processed
+    t + 1 positions exist; an entry is complete once all m of its tokens are,
+    so (t + 1) // m entries are complete.  Worked checks on that page with
+    block width 4: t = 7 reads the second entry, t = 8 may not read the entry
+    covering 8..11.
+    """
+    if t < 0 or m <= 0:
+        raise ValueError("t must be >= 0 and m > 0")
+    return (t + 1) // m
+
+
+def read_counts(history: int, m: int, m_prime: int, k: int, n_win: int) -> dict:
+    """Entries stored and read by one query, by layer type.
+
+    [P5] section 2 (storage vs reads ledger) and [P1] B9 (read count of one
+    CSA layer is min(k, n/m) + n_win; of one HCA layer n/m' + n_win).
+    `history` counts processed positions including the current query.
+    """
+    for v in (history, m, m_prime, k, n_win):
+        if int(v) != v or v <= 0:
+            raise ValueError("all counts must be positive integers")
+    if m_prime <= m:
+        raise ValueError("the heavy ratio must exceed the light ratio")
+    csa_stored = history // m
+    hca_stored = history // m_prime
+    window = min(history, n_win)
+    return {
+        "csa_stored": csa_stored,
+        "hca_stored": hca_stored,
+        "csa_reads": min(k, csa_stored) + window,
+        "hca_reads": hca_stored + window,
+        "csa_tail": history % m,
+        "hca_tail": history % m_prime,
+    }
+
+
+# --------------------------------------------------------------------------
+# Compressors
+# --------------------------------------------------------------------------
+
+def compress_weights_overlap(Za, Zb, Ba, Bb, m: int, prev_Zb=None):
+    """Per-dimension softmax weights of the overlapped CSA compressor.
+
+    [P1] B9 / [P2] section 4.1 (Eq. 11): entry i scores the m rows of block i
+    from stream a (Z^a + B^a) and the m rows of block i-1 from stream b
+    (Z^b + B^b); the 2m scores are normalised jointly, separately for each
+    dimension.  Block -1 is padded with -inf scores ([P2] section 4.1).
+
+    Returns (Sa, Sb), each [n//m, m, c].
+    """
+    Za, Zb, Ba, Bb = _f64(Za), _f64(Zb), _f64(Ba), _f64(Bb)
+    n, c = Za.shape
+    ne = n // m
+    # scores of the current block, stream a, with the intra-block bias
+    ua = Za[: ne * m].reshape(ne, m, c) + Ba[None, :, :]
+    # scores of the previous block, stream b: block i-1 for entry i
+    prev = np.full((1, m, c), -np.inf) if prev_Zb is None else _f64(prev_Zb).reshape(1, m, c)
+    zb_blocks = Zb[: ne * m].reshape(ne, m, c)
+    zb_prev = np.concatenate([prev, zb_blocks[: ne - 1]], axis=0)[:ne]
+    ub = zb_prev + Bb[None, :, :]
+    u = np.concatenate([ua, ub], axis=1)           # [ne, 2m, c]
+    u_max = u.max(axis=1, keepdims=True)
+    e = np.exp(u - u_max)
+    S = e / e.sum(axis=1, keepdims=True)
+    return S[:, :m, :], S[:, m:, :]
+
+
+def compress_overlap(Ca, Cb, Za, Zb, Ba, Bb, m: int, prev_Cb=None, prev_Zb=None):
+    """Overlapped CSA compressor, one sequence: [n, c] streams -> [n//m, c].
+
+    [P1] B9 / [P2] section 4.1 (Eq. 12): C^Comp_i is the sum over the m rows
+    of block i of S^a (.) C^a plus the sum over the m rows of block i-1 of
+    S^b (.) C^b, where (.) is the element-wise product.  Block -1 has zero
+    values ([P2] section 4.1).  `prev_Cb`/`prev_Zb` ([m, c]) stand for block
+    -1 when the rows given here continue an earlier sequence (decode state,
+    [P3] section 7.6 state cache).
+    """
+    if (prev_Cb is None) != (prev_Zb is None):
+        raise ValueError("prev_Cb and prev_Zb come together")
+    Ca, Cb = _f64(Ca), _f64(Cb)
+    n, c = Ca.shape
+    ne = n // m
+    Sa, Sb = compress_weights_overlap(Za, Zb, Ba, Bb, m, prev_Zb)
+    ca = Ca[: ne * m].reshape(ne, m, c)
+    prev = np.zeros((1, m, c)) if prev_Cb is None else _f64(prev_Cb).reshape(1, m, c)
+    cb = np.concatenate([prev, Cb[: ne * m].reshape(ne, m, c)[: ne - 1]], axis=0)[:ne]
+    return (Sa * ca).sum(axis=1) + (Sb * cb).sum(axis=1)
+
+
+def compress_weights_pool(Z, B, m_prime: int):
+    """Per-dimension softmax weights of the HCA compressor, [n//m', m', c].
+
+    [P1] B9 / [P2] section 5.1 / [P3] section 7.2: a single stream, the m'
+    rows of one block, no overlap with the previous block.
+    """
+    Z, B = _f64(Z), _f64(B)
+    n, c = Z.shape
+    ne = n // m_prime
+    u = Z[: ne * m_prime].reshape(ne, m_prime, c) + B[None, :, :]
+    e = np.exp(u - u.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def compress_pool(C, Z, B, m_prime: int):
+    """HCA compressor, one sequence: [n, c] -> [n//m', c] (same sources)."""
+    C = _f64(C)
+    n, c = C.shape
+    ne = n // m_prime
+    S = compress_weights_pool(Z, B, m_prime)
+    return (S * C[: ne * m_prime].reshape(ne, m_prime, c)).sum(axis=1)
+
+
+# --------------------------------------------------------------------------
+# Lightning indexer and top-k
+# --------------------------------------------------------------------------
+
+def index_scores(qI, w, KI, t_pos, m: int, chunk: int = 64):
+    """Indexer scores I[t, s] for queries at positions t_pos.
+
+    [P1] B9 / [P3] section 7.1: I_{t,s} = sum over indexer heads h of
+    w_{t,h} * ReLU(q^I_{t,h} . K^IComp_s).  Entries a query may not read
+    (s >= (t+1)//m) get -inf.
+
+    qI [n_q, n_hI, c_I], w [n_q, n_hI], KI [n_comp, c_I] -> [n_q, n_comp].
+    Queries are processed `chunk` at a time only to bound memory.
+    """
+    qI, w, KI = _f64(qI), _f64(w), _f64(KI)
+    n_q = qI.shape[0]
+    n_comp = KI.shape[0]
+    t_pos = np.asarray(t_pos, dtype=np.int64)
+    out = np.full((n_q, n_comp), -np.inf)
+    for a in range(0, n_q, chunk):
+        b = min(n_q, a + chunk)
+        dots = qI[a:b] @ KI.T                      # [T, n_hI, n_comp]
+        sc = (w[a:b, :, None] * np.maximum(dots, 0.0)).sum(axis=1)
+        for r in range(a, b):
+            v = min(visible_entries(int(t_pos[r]), m), n_comp)
+            out[r, :v] = sc[r - a, :v]
+    return out
+
+
+def topk_select(scores_row, v: int, k: int):
+    """Indices of the top-k among the first v scores of one query.
+
+    [P1] B9 / [P3] section 7.1: the entries whose scores are among the k
+    largest of I_{t,:}; all v if v <= k.  Reading: the lower index wins a tie;
+    the result is ascending and padded with -1 to length k.
+    """
+    s = np.arange(v)
+    order = np.lexsort((s, -_f64(scores_row)[:v]))   # by score desc, then s asc
+    take = np.sort(order[: min(k, v)])
+    out = np.full(k, -1, dtype=np.int64)
+    out[: take.size] = take
+    return out
+
+
+def index_topk(qI, w, KI, t_pos, m: int, k: int):
+    """Indexer scores followed by top-k, per query: (idx [n_q,k], scores)."""
+    sc = index_scores(qI, w, KI, t_pos, m)
+    n_comp = KI.shape[0]
+    idx = np.stack([
+        topk_select(sc[r], min(visible_entries(int(t), m), n_comp), k)
+        for r, t in enumerate(np.asarray(t_pos))
+    ]) if len(t_pos) else np.zeros((0, k), dtype=np.int64)
+    return idx, sc
+
+
+# --------------------------------------------------------------------------
+# Core attention with window and sink
+# --------------------------------------------------------------------------
+
+def attend_entries(q_t, E, sink, scale: float):
+    """Shared key/value attention of one query over an entry set, with sink.
+
+    [P3] section 7.1 / [P2] section 4.3: each entry is both key and value and
+    all n_h query heads read the same entries.  [P2] sections 4.5 and 7.3,
+    [P1] B9: the compressed and the window entries share one softmax, whose
+    denominator also holds exp(z'_h) of the head's sink logit; the sink adds
+    no value.
+
+    q_t [n_h, c], E [N, c], sink [n_h] -> [n_h, c].
+    """
+    q_t, E, sink = _f64(q_t), _f64(E), _f64(sink)
+    logits = scale * (q_t @ E.T)                     # [n_h, N]
+    if logits.shape[1]:
+        M = np.maximum(logits.max(axis=1), sink)
+    else:
+        M = sink.copy()
+    p = np.exp(logits - M[:, None])
+    den = p.sum(axis=1) + np.exp(sink - M)
+    return (p @ E) / den[:, None]
+
+
+def window_rows(t: int, n_win: int):
+    """Raw positions in the causal window of a query at t ([P2] section 4.5)."""
+    return np.arange(max(0, t - n_win + 1), t + 1)
+
+
+def csa_attend(q, Ccomp, idx, kv_raw, raw_pos0: int, sink, t_pos, n_win: int,
+               scale: float, m: int | None = None):
+    """CSA main attention for queries at t_pos, one sequence.
+
+    q [n_q, n_h, c]; Ccomp [n_comp, c]; idx [n_q, k] (-1 padded); kv_raw
+    [n_raw, c], row j at position raw_pos0 + j; sink [n_h].
+    The entry set of query t is the selected compressed rows plus the window
+    rows ([P2] section 4.5).  If m is given, selected indices must be visible.
+    """
+    q, Ccomp, kv_raw = _f64(q), _f64(Ccomp), _f64(kv_raw)
+    out = np.zeros(q.shape, dtype=F64)
+    for r, t in enumerate(np.asarray(t_pos)):
+        t = int(t)
+        sel = np.asarray(idx[r])
+        sel = sel[sel >= 0]
+        if m is not None and sel.size:
+            assert sel.max() < visible_entries(t, m), "index reads the future"
+        win = window_rows(t, n_win) - raw_pos0
+        assert win.min() >= 0 and win.max() < kv_raw.shape[0], "window outside kv_raw"
+        E = np.concatenate([Ccomp[sel], kv_raw[win]], axis=0)
+        out[r] = attend_entries(q[r], E, sink, scale)
+    return out
+
+
+def hca_attend(q, Ccomp, kv_raw, raw_pos0: int, sink, t_pos, m_prime: int,
+               n_win: int, scale: float):
+    """HCA dense attention: every completed compressed entry plus the window.
+
+    [P1] B9 / [P2] section 5.2 / [P3] section 7.2: no indexer, no selection;
+    the entry set of query t is C^Comp_s for s < (t+1)//m' plus the window.
+    """
+    q, Ccomp, kv_raw = _f64(q), _f64(Ccomp), _f64(kv_raw)
+    out = np.zeros(q.shape, dtype=F64)
+    for r, t in enumerate(np.asarray(t_pos)):
+        t = int(t)
+        v = min(visible_entries(t, m_prime), Ccomp.shape[0])
+        win = window_rows(t, n_win) - raw_pos0
+        E = np.concatenate([Ccomp[:v], kv_raw[win]], axis=0)
+        out[r] = attend_entries(q[r], E, sink, scale)
+    return out
+
+
+def hca_layer(C, Z, B, q, kv_raw, sink, m_prime: int, n_win: int, scale: float,
+              t_rows=None):
+    """Whole HCA prefill of one sequence: compress, then dense attention.
+
+    `t_rows` optionally restricts the queries evaluated (all by default).
+    Returns (Ccomp, out[t_rows]).
+    """
+    Ccomp = compress_pool(C, Z, B, m_prime)
+    n = _f64(C).shape[0]
+    rows = np.arange(n) if t_rows is None else np.asarray(t_rows)
+    out = hca_attend(_f64(q)[rows], Ccomp, kv_raw, 0, sink, rows, m_prime, n_win, scale)
+    return Ccomp, out
+
+
+def csa_layer(streams, istreams, q, qI, w, kv_raw, sink, m: int, k: int,
+              n_win: int, scale: float, t_rows=None):
+    """Whole CSA prefill of one sequence.
+
+    streams = (Ca, Cb, Za, Zb, Ba, Bb) for the main entries; istreams the same
+    six arrays for the indexer keys, "compressed the same way" ([P2] section
+    4.2, step 1).  Returns (Ccomp, KIcomp, idx, out) for the query rows.
+    """
+    Ccomp = compress_overlap(*streams, m)
+    KIcomp = compress_overlap(*istreams, m)
+    n = _f64(q).shape[0]
+    rows = np.arange(n) if t_rows is None else np.asarray(t_rows)
+    idx, _ = index_topk(_f64(qI)[rows], _f64(w)[rows], KIcomp, rows, m, k)
+    out = csa_attend(_f64(q)[rows], Ccomp, idx, kv_raw, 0, sink, rows, n_win, scale, m)
+    return Ccomp, KIcomp, idx, out
+
+
+# --------------------------------------------------------------------------
+# Decode state ([P3] section 7.6 state cache; [P5] section 2 tails)
+# --------------------------------------------------------------------------
+
+@dataclass
+class CsaDecodeState:
+    """Per-sequence CSA decode state.
+
+    [P3] section 7.6: a fixed-size state cache holds the n_win most recent
+    uncompressed entries and the tokens still waiting to be compressed; [P5]
+    section 2 adds that CSA must also keep the previous block's overlap state.
+    Compressed entries (main and indexer keys) accumulate in growing caches.
+    """
+    m: int
+    n_win: int
+    c: int
+    c_I: int
+    Ccomp: list = field(default_factory=list)
+    KIcomp: list = field(default_factory=list)
+    window: list = field(default_factory=list)          # (position, row)
+    tail: list = field(default_factory=list)            # rows of the open block
+    prev_b: tuple | None = None                         # (Cb, Zb, ICb, IZb) of last full block
+    t: int = -1
+
+    def append(self, row: dict, biases: dict):
+        """Add token t+1; emit one entry of each cache when its block fills."""
+        self.t += 1
+        self.window.append((self.t, _f64(row["Ca"])))
+        self.window = self.window[-self.n_win:]
+        self.tail.append({k: _f64(v) for k, v in row.items()})
+        if len(self.tail) == self.m:
+            blk = {k: np.stack([r[k] for r in self.tail]) for k in self.tail[0]}
+            pc, pz, pic, piz = self.prev_b if self.prev_b else (None, None, None, None)
+            e = compress_overlap(blk["Ca"], blk["Cb"], blk["Za"], blk["Zb"],
+                                 biases["Ba"], biases["Bb"], self.m, pc, pz)
+            ei = compress_overlap(blk["ICa"], blk["ICb"], blk["IZa"], blk["IZb"],
+                                  biases["IBa"], biases["IBb"], self.m, pic, piz)
+            self.Ccomp.append(e[0])
+            self.KIcomp.append(ei[0])
+            self.prev_b = (blk["Cb"], blk["Zb"], blk["ICb"], blk["IZb"])
+            self.tail = []
+
+    def query(self, q_t, qI_t, w_t, sink, k: int, scale: float):
+        """Index, select and attend for the newest token's query."""
+        t = self.t
+        KI = np.array(self.KIcomp).reshape(-1, self.c_I)
+        Cc = np.array(self.Ccomp).reshape(-1, self.c)
+        idx, _ = index_topk(_f64(qI_t)[None], _f64(w_t)[None], KI, [t], self.m, k)
+        pos0 = self.window[0][0]
+        raw = np.stack([r for _, r in self.window])
+        out = csa_attend(_f64(q_t)[None], Cc, idx, raw, pos0, sink, [t], self.n_win, scale, self.m)
+        return idx[0], out[0]
+
+
+def default_scale(c: int) -> float:
+    """Softmax scale 1/sqrt(c) (a reading: the pages never state it)."""
+    return 1.0 / math.sqrt(c)

@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test ties one oracle routine to a value the pages print, a closed form,
+an invariant, a library routine or a brute-force formulation written
+independently here.  A dropped term, a wrong sign or index, or a transposed
+operand in the oracle fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- ledger ----
+
+def test_read_ledger_worked_example():
+    g = _golden("read_ledger.json")
+    for case in g["cases"]:
+        r = O.read_counts(case["history"], case["m"], case["m_prime"], case["k"], case["n_win"])
+        for key in ("csa_reads", "hca_reads", "csa_tail"):
+            if key in case:
+                assert r[key] == case[key], (key, r)
+
+
+def test_read_ledger_one_million():
+    g = _golden("one_million_counts.json")
+    r = O.read_counts(g["history"], g["m"], g["m_prime"], g["k"], g["n_win"])
+    for key in ("csa_stored", "hca_stored", "csa_reads", "hca_reads"):
+        assert r[key] == g[key], key
+
+
+def test_read_ledger_rejects_bad_counts():
+    with pytest.raises(ValueError):
+        O.read_counts(0, 4, 128, 32, 128)
+    with pytest.raises(ValueError):
+        O.read_counts(16, 4, 4, 32, 128)
+
+
+def test_visibility_boundaries():
+    g = _golden("visibility.json")
+    for t, v in g["visible"].items():
+        assert O.visible_entries(int(t), g["m"]) == v
+
+
+# ------------------------------------------------------------ compressor ----
+
+def _streams(n, c, m, seed=0, zscale=1.0):
+    r = _rng(seed)
+    Ca, Cb = r.normal(size=(n, c)), r.normal(size=(n, c))
+    Za, Zb = zscale * r.normal(size=(n, c)), zscale * r.normal(size=(n, c))
+    Ba, Bb = 0.1 * r.normal(size=(m, c)), 0.1 * r.normal(size=(m, c))
+    return Ca, Cb, Za, Zb, Ba, Bb
+
+
+def test_compress_weights_sum_to_one_per_dim():
+    Ca, Cb, Za, Zb, Ba, Bb = _streams(40, 7, 4, zscale=3.0)
+    Sa, Sb = O.compress_weights_overlap(Za, Zb, Ba, Bb, 4)
+    tot = Sa.sum(axis=1) + Sb.sum(axis=1)
+    assert np.abs(tot - 1.0).max() < 1e-12
+    # block -1 is padded with -inf scores: entry 0 puts no weight on stream b
+    assert np.all(Sb[0] == 0.0)
+    assert np.all(Sb[1:] > 0.0)
+
+
+def test_compress_equal_scores_give_plain_mean():
+    n, c, m = 24, 5, 4
+    Ca, Cb, _, _, _, _ = _streams(n, c, m, seed=1)
+    Z = np.full((n, c), 0.37)
+    zero = np.zeros((m, c))
+    out = O.compress_overlap(Ca, Cb, Z, Z, zero, zero, m)
+    # entry 0: mean of the m rows of C^a block 0 (block -1 padded away)
+    assert np.allclose(out[0], Ca[0:m].mean(axis=0), atol=1e-14)
+    for i in range(1, n // m):
+        want = (Ca[m * i:m * i + m].sum(axis=0) + Cb[m * (i - 1):m * i].sum(axis=0)) / (2 * m)
+        assert np.allclose(out[i], want, atol=1e-14)
+    pool = O.compress_pool(Ca, Z, zero.repeat(1, axis=0)[:m], m)
+    assert np.allclose(pool, Ca.reshape(-1, m, c).mean(axis=1), atol=1e-14)
+
+
+def test_compress_mean_counterexample():
+    g = _golden("mean_counterexample.json")
+    for blk in g["blocks"]:
+        C = np.array(blk, dtype=float).reshape(2, 1)
+        out = O.compress_pool(C, np.zeros((2, 1)), np.zeros((2, 1)), 2)
+        assert out.shape == (1, 1) and abs(out[0, 0] - g["mean"]) < 1e-15
+
+
+def test_compress_dominant_score_selects_that_row():
+    # A huge score in one row of one dim makes the weights one-hot there.
+    # Stream a must pick the row of block i, stream b the row of block i-1.
+    n, c, m = 16, 4, 4
+    Ca, Cb, Za, Zb, Ba, Bb = _streams(n, c, m, seed=2)
+    Za[:] = 0.0
+    Zb[:] = 0.0
+    i = 2
+    # dim 0: row 1 of block i in stream a; dim 1: row 3 of block i-1 in stream b
+    Za[m * i + 1, 0] = 800.0
+    Zb[m * (i - 1) + 3, 1] = 800.0
+    out = O.compress_overlap(Ca, Cb, Za, Zb, Ba, Bb, m)
+    assert abs(out[i, 0] - Ca[m * i + 1, 0]) < 1e-12
+    assert abs(out[i, 1] - Cb[m * (i - 1) + 3, 1]) < 1e-12
+    # the bias is indexed by the row inside the block: bias row 2 dominates dim 2
+    Ba2 = np.zeros((m, c))
+    Ba2[2, 2] = 800.0
+    out2 = O.compress_overlap(Ca, Cb, Za, Zb, Ba2, np.zeros((m, c)), m)
+    for e in range(n // m):
+        assert abs(out2[e, 2] - Ca[m * e + 2, 2]) < 1e-12
+    Bb2 = np.zeros((m, c))
+    Bb2[0, 3] = 800.0
+    out3 = O.compress_overlap(Ca, Cb, Za, Zb, np.zeros((m, c)), Bb2, m)
+    for e in range(1, n // m):
+        assert abs(out3[e, 3] - Cb[m * (e - 1), 3]) < 1e-12
+
+
+def test_compress_matches_library_softmax():
+    # torch.softmax over the 2m stacked rows, then the weighted sum.
+    n, c, m = 32, 6, 4
+    Ca, Cb, Za, Zb, Ba, Bb = _streams(n, c, m, seed=3, zscale=2.0)
+    out = O.compress_overlap(Ca, Cb, Za, Zb, Ba, Bb, m)
+    T = lambda a: torch.tensor(a, dtype=torch.float64)
+    for i in range(n // m):
+        za = T(Za[m * i:m * i + m]) + T(Ba)
+        ca = T(Ca[m * i:m * i + m])
+        if i == 0:
+            w = torch.softmax(za, dim=0)
+            want = (w * ca).sum(0)
+        else:
+            zb = T(Zb[m * (i - 1):m * i]) + T(Bb)
+            cb = T(Cb[m * (i - 1):m * i])
+            w = torch.softmax(torch.cat([za, zb]), dim=0)
+            want = (w * torch.cat([ca, cb])).sum(0)
+        assert torch.allclose(T(out[i]), want, atol=1e-13, rtol=0)
+
+
+def test_compress_shift_invariance():
+    n, c, m = 20, 3, 4
+    Ca, Cb, Za, Zb, Ba, Bb = _streams(n, c, m, seed=4)
+    shift = np.array([3.0, -7.0, 0.5])
+    a = O.compress_overlap(Ca, Cb, Za, Zb, Ba, Bb, m)
+    b = O.compress_overlap(Ca, Cb, Za + shift, Zb + shift, Ba, Bb, m)
+    assert np.abs(a - b).max() < 1e-12
+
+
+def test_compress_continuation_with_previous_block_state():
+    n, c, m = 32, 5, 4
+    Ca, Cb, Za, Zb, Ba, Bb = _streams(n, c, m, seed=5)
+    whole = O.compress_overlap(Ca, Cb, Za, Zb, Ba, Bb, m)
+    cut = 12
+    head = O.compress_overlap(Ca[:cut], Cb[:cut], Za[:cut], Zb[:cut], Ba, Bb, m)
+    tail = O.compress_overlap(Ca[cut:], Cb[cut:], Za[cut:], Zb[cut:], Ba, Bb, m,
+                              prev_Cb=Cb[cut - m:cut], prev_Zb=Zb[cut - m:cut])
+    assert np.abs(np.concatenate([head, tail]) - whole).max() < 1e-14
+
+
+def test_compress_ragged_tail_is_not_emitted():
+    Ca, Cb, Za, Zb, Ba, Bb = _streams(18, 3, 4, seed=6)
+    assert O.compress_overlap(Ca, Cb, Za, Zb, Ba, Bb, 4).shape == (4, 3)
+    assert O.compress_pool(Ca, Za, Ba, 4).shape == (4, 3)
+    assert O.compress_overlap(Ca[:3], Cb[:3], Za[:3], Zb[:3], Ba, Bb, 4).shape == (0, 3)
+
+
+def test_pool_weights_and_library():
+    n, c, mp = 24, 4, 8
+    r = _rng(7)
+    C, Z, B = r.normal(size=(n, c)), 2 * r.normal(size=(n, c)), 0.1 * r.normal(size=(mp, c))
+    S = O.compress_weights_pool(Z, B, mp)
+    assert np.abs(S.sum(axis=1) - 1).max() < 1e-12
+    out = O.compress_pool(C, Z, B, mp)
+    T = lambda a: torch.tensor(a, dtype=torch.float64)
+    for i in range(n // mp):
+        w = torch.softmax(T(Z[mp * i:mp * i + mp]) + T(B), dim=0)
+        assert torch.allclose(T(out[i]), (w * T(C[mp * i:mp * i + mp])).sum(0), atol=1e-13, rtol=0)
+
+
+# --------------------------------------------------------------- indexer ----
+
+def test_index_single_head_is_relu_dot_and_topk_matches_library():
+    r = _rng(8)
+    n_q, n_comp, cI, m, k = 12, 30, 8, 4, 5
+    qI = r.normal(size=(n_q, 1, cI))
+    KI = r.normal(size=(n_comp, cI))
+    w = np.ones((n_q, 1))
+    t_pos = np.arange(200, 200 + n_q)           # every entry visible
+    sc = O.index_scores(qI, w, KI, t_pos, m)
+    want = torch.relu(torch.tensor(qI[:, 0, :]) @ torch.tensor(KI).T)
+    assert torch.allclose(torch.tensor(sc), want, atol=1e-13, rtol=0)
+    idx, _ = O.index_topk(qI, w, KI, t_pos, m, k)
+    for row in range(n_q):
+        # compare only where the k-th and (k+1)-th scores are distinct
+        vals, top = torch.topk(torch.tensor(sc[row]), k + 1)
+        if vals[k - 1] > vals[k]:
+            assert set(idx[row].tolist()) == set(top[:k].tolist())
+
+
+def test_index_heads_weighted_sum_and_relu():
+    r = _rng(9)
+    n_q, n_h, n_comp, cI, m = 4, 3, 10, 6, 1
+    qI = r.normal(size=(n_q, n_h, cI))
+    KI = r.normal(size=(n_comp, cI))
+    w = np.abs(r.normal(size=(n_q, n_h))) - 0.3    # mixed signs are allowed
+    t_pos = np.full(n_q, 50)
+    sc = O.index_scores(qI, w, KI, t_pos, m)
+    # brute force, one scalar at a time
+    for t in range(n_q):
+        for s in range(n_comp):
+            acc = 0.0
+            for h in range(n_h):
+                d = sum(qI[t, h, j] * KI[s, j] for j in range(cI))
+                acc += w[t, h] * (d if d > 0 else 0.0)
+            assert abs(sc[t, s] - acc) < 1e-12
+
+
+def test_index_causal_mask_counts():
+    r = _rng(10)
+    m, n_comp = 4, 6
+    qI = r.normal(size=(26, 2, 3))
+    w = np.ones((26, 2))
+    KI = r.normal(size=(n_comp, 3))
+    t_pos = np.arange(26)
+    sc = O.index_scores(qI, w, KI, t_pos, m)
+    for t in range(26):
+        finite = np.isfinite(sc[t]).sum()
+        assert finite == min((t + 1) // m, n_comp)
+
+
+def test_topk_tie_lower_index_and_padding():
+    s = np.array([1.0, 3.0, 2.0, 3.0, 2.0, 2.0])
+    # top-3: both 3.0 (idx 1,3) then the lowest-index 2.0 (idx 2)
+    assert O.topk_select(s, 6, 3).tolist() == [1, 2, 3]
+    assert O.topk_select(s, 6, 4).tolist() == [1, 2, 3, 4]
+    # fewer visible than k: all of them, ascending, -1 padded
+    assert O.topk_select(s, 2, 4).tolist() == [0, 1, -1, -1]
+    assert O.topk_select(s, 0, 2).tolist() == [-1, -1]
+    # negative scores are legitimate
+    assert O.topk_select(np.array([-5.0, -1.0, -3.0]), 3, 1).tolist() == [1]
+
+
+# ------------------------------------------------------------- attention ----
+
+def _dense_masked_attention(q, Ccomp, kv_raw, sink, m_vis, n_win, scale):
+    """Independent formulation: one masked score matrix over every compressed
+    entry and every raw row, a sink column with a zero value row, one
+    torch.softmax over the columns."""
+    q = torch.tensor(q)
+    n_q, n_h, c = q.shape
+    K = torch.cat([torch.tensor(Ccomp), torch.tensor(kv_raw)])
+    n_comp = Ccomp.shape[0]
+    n = kv_raw.shape[0]
+    t = torch.arange(n_q)[:, None]
+    j = torch.arange(n_comp)[None, :]
+    p = torch.arange(n)[None, :]
+    mask_c = j < ((t + 1) // m_vis)
+    mask_w = (p <= t) & (p > t - n_win)
+    mask = torch.cat([mask_c, mask_w], dim=1)                    # [n_q, n_comp+n]
+    logits = scale * torch.einsum("thc,jc->thj", q, K)
+    logits = logits.masked_fill(~mask[:, None, :], float("-inf"))
+    sink_col = torch.tensor(sink)[None, :, None].expand(n_q, n_h, 1)
+    P = torch.softmax(torch.cat([logits, sink_col], dim=2), dim=2)
+    V = torch.cat([K, torch.zeros(1, c, dtype=K.dtype)])
+    return torch.einsum("thj,jc->thc", P, V).numpy()
+
+
+def test_csa_with_k_at_least_candidates_is_dense_attention():
+    r = _rng(11)
+    n, c, n_h, m, n_win = 24, 8, 3, 4, 5
+    n_comp = n // m
+    q = r.normal(size=(n, n_h, c))
+    Ccomp = r.normal(size=(n_comp, c))
+    kv_raw = r.normal(size=(n, c))
+    sink = r.normal(size=n_h)
+    scale = 1 / math.sqrt(c)
+    k = n_comp
+    idx = np.stack([O.topk_select(r.normal(size=n_comp), O.visible_entries(t, m), k) for t in range(n)])
+    got = O.csa_attend(q, Ccomp, idx, kv_raw, 0, sink, np.arange(n), n_win, scale, m)
+    want = _dense_masked_attention(q, Ccomp, kv_raw, sink, m, n_win, scale)
+    assert np.abs(got - want).max() < 1e-12
+    # HCA is the same dense read with ratio m' in place of m
+    got_h = O.hca_attend(q, Ccomp, kv_raw, 0, sink, np.arange(n), m, n_win, scale)
+    assert np.abs(got_h - want).max() < 1e-12
+
+
+def test_window_only_without_sink_is_causal_sdpa():
+    # No compressed entries, window covering the whole prefix, sink -> -inf:
+    # a causal multi-query attention where K = V = kv_raw.
+    r = _rng(12)
+    n, c, n_h = 10, 6, 2
+    q = r.normal(size=(n, n_h, c))
+    kv = r.normal(size=(n, c))
+    sink = np.full(n_h, -1e300)
+    idx = np.full((n, 3), -1)
+    scale = 0.37
+    got = O.csa_attend(q, np.zeros((0, c)), idx, kv, 0, sink, np.arange(n), n, scale)
+    Q = torch.tensor(q).permute(1, 0, 2)                    # [n_h, n, c]
+    KV = torch.tensor(kv)[None].expand(n_h, n, c)
+    want = torch.nn.functional.scaled_dot_product_attention(Q, KV, KV, is_causal=True, scale=scale)
+    assert np.abs(got - want.permute(1, 0, 2).numpy()).max() < 1e-12
+
+
+def test_sink_limits():
+    r = _rng(13)
+    q = r.normal(size=(3, 4))
+    E = r.normal(size=(5, 4))
+    big = O.attend_entries(q, E, np.full(3, 1e4), 0.5)
+    assert np.abs(big).max() < 1e-300
+    # finite sink: weights sum to less than one, exactly sum(p)/(sum(p)+e^z)
+    sink = np.array([0.0, 1.0, -2.0])
+    out = O.attend_entries(q, E, sink, 0.5)
+    logits = 0.5 * q @ E.T
+    for h in range(3):
+        p = np.exp(logits[h])
+        want = (p @ E) / (p.sum() + math.exp(sink[h]))
+        assert np.abs(out[h] - want).max() < 1e-12
+
+
+def test_future_tokens_do_not_change_outputs():
+    # cooking-agi section 3: perturb every input row after t; outputs at the
+    # boundary positions 3, 4, 7 and 8 (block width 4) must not move.
+    r = _rng(14)
+    n, c, n_h, m, k, n_win, nI, cI = 16, 6, 2, 4, 2, 3, 2, 5
+
+    def draw(seed):
+        g = _rng(seed)
+        s = [g.normal(size=(n, c)) for _ in range(4)] + [0.1 * g.normal(size=(m, c))] * 2
+        si = [g.normal(size=(n, cI)) for _ in range(4)] + [0.1 * g.normal(size=(m, cI))] * 2
+        return dict(streams=s, istreams=si, q=g.normal(size=(n, n_h, c)),
+                    qI=g.normal(size=(n, nI, cI)), w=np.abs(g.normal(size=(n, nI))))
+
+    base = draw(1)
+    sink = r.normal(size=n_h)
+    kv = base["streams"][0]
+    ref = O.csa_layer(base["streams"], base["istreams"], base["q"], base["qI"], base["w"],
+                      kv, sink, m, k, n_win, 0.4)[3]
+    pert = draw(2)
+    for t in (3, 4, 7, 8):
+        mix = {}
+        for key in ("q", "qI", "w"):
+            a = base[key].copy()
+            a[t + 1:] = pert[key][t + 1:]
+            mix[key] = a
+        for key in ("streams", "istreams"):
+            arrs = []
+            for i, a in enumerate(base[key]):
+                a = a.copy()
+                if i < 4:
+                    a[t + 1:] = pert[key][i][t + 1:]
+                arrs.append(a)
+            mix[key] = arrs
+        got = O.csa_layer(mix["streams"], mix["istreams"], mix["q"], mix["qI"], mix["w"],
+                          mix["streams"][0], sink, m, k, n_win, 0.4)[3]
+        assert np.array_equal(got[t], ref[t]), t
+        # HCA at ratio 4 obeys the same rule
+        Cc_b = O.compress_pool(base["streams"][0], base["streams"][2], base["streams"][4], m)
+        Cc_m = O.compress_pool(mix["streams"][0], mix["streams"][2], mix["streams"][4], m)
+        hb = O.hca_attend(base["q"][[t]], Cc_b, base["streams"][0], 0, sink, [t], m, n_win, 0.4)
+        hm = O.hca_attend(mix["q"][[t]], Cc_m, mix["streams"][0], 0, sink, [t], m, n_win, 0.4)
+        assert np.array_equal(hb, hm), t
+
+
+def test_decode_steps_equal_one_shot_prefill():
+    r = _rng(15)
+    n0, steps, c, cI, n_h, nI, m, k, n_win = 9, 11, 6, 4, 2, 2, 4, 2, 5
+    n = n0 + steps
+    st = {key: r.normal(size=(n, c)) for key in ("Ca", "Cb", "Za", "Zb")}
+    st.update({key: r.normal(size=(n, cI)) for key in ("ICa", "ICb", "IZa", "IZb")})
+    biases = {"Ba": 0.1 * r.normal(size=(m, c)), "Bb": 0.1 * r.normal(size=(m, c)),
+              "IBa": 0.1 * r.normal(size=(m, cI)), "IBb": 0.1 * r.normal(size=(m, cI))}
+    q, qI = r.normal(size=(n, n_h, c)), r.normal(size=(n, nI, cI))
+    w, sink = np.abs(r.normal(size=(n, nI))), r.normal(size=n_h)
+    streams = [st["Ca"], st["Cb"], st["Za"], st["Zb"], biases["Ba"], biases["Bb"]]
+    istreams = [st["ICa"], st["ICb"], st["IZa"], st["IZb"], biases["IBa"], biases["IBb"]]
+    Cc, KIc, idx, out = O.csa_layer(streams, istreams, q, qI, w, st["Ca"], sink, m, k, n_win, 0.3)
+    state = O.CsaDecodeState(m=m, n_win=n_win, c=c, c_I=cI)
+    for t in range(n):
+        state.append({key: st[key][t] for key in st}, biases)
+        if t >= n0:
+            i_t, o_t = state.query(q[t], qI[t], w[t], sink, k, 0.3)
+            assert np.array_equal(i_t, idx[t])
+            assert np.abs(o_t - out[t]).max() < 1e-13
+    assert np.abs(np.array(state.Ccomp) - Cc).max() < 1e-13
+    assert np.abs(np.array(state.KIcomp) - KIc).max() < 1e-13
