@@ -1,0 +1,199 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) library for one layer of compressed
+ * sparse attention (CSA) and heavily compressed attention (HCA).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer to dense row-major data owned
+ *    by the caller; the library never allocates, frees or keeps a pointer
+ *    after the call returns.  Inputs are never written.
+ *  - `dtype` (csa_dtype) is the element type of every floating-point tensor
+ *    argument except `w`, `sink` and `score`, which are always float32.
+ *    Arithmetic is float32 in both modes; bfloat16 results are rounded to
+ *    nearest-even when stored.
+ *  - Positions are 0-based token positions.  A query at position t may read
+ *    compressed entry s only if s < (t + 1) / m (integer division): entry s
+ *    is complete once its m tokens are (cooking-agi "DeepSeek-V4: 压缩历史以后，
+ *    还能读到什么？", section 3).
+ *  - `*_bstride` arguments give the distance, in elements, between two
+ *    consecutive sequences of a batched cache, so that a cache may be larger
+ *    than the part in use; 0 means "dense" (rows-in-use * row length).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns without synchronising.
+ *  - Errors: arguments are validated on the host before anything is
+ *    enqueued.  A negative return code means nothing was launched, except
+ *    CSA_EHIP, which reports a launch failure from the HIP runtime.  No call
+ *    aborts the process.  csa_strerror() names a code.
+ *  - Results are bitwise reproducible from run to run: every reduction has a
+ *    fixed order and no floating-point atomics are used.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+enum {
+  CSA_OK = 0,
+  CSA_EINVAL = -1,  /* an argument is out of range or inconsistent      */
+  CSA_ENOTSUP = -2, /* valid, but no kernel handles this shape / dtype  */
+  CSA_ENOSPC = -3,  /* the workspace given is smaller than required     */
+  CSA_EHIP = -4     /* the HIP runtime reported an error at launch      */
+};
+
+/* Library version string, e.g. "csa-mi355x 0.1.0". */
+const char* csa_version(void);
+
+/* Human-readable name of a return code. */
+const char* csa_strerror(int code);
+
+/*
+ * csa_compress -- token-level KV compressor, CSA (overlap = 1) or HCA
+ * (overlap = 0).
+ *
+ * Overlapped form (polysight "06-formulas" section B9; songhuiming
+ * "DeepSeek-V4 百万 token 上下文" section 4.1, Eq. 11-12): for entry i and
+ * each dimension d, softmax over the 2m scores
+ *     Za[m*i + j][d] + Ba[j][d]        (j < m, block i, stream a)
+ *     Zb[m*(i-1) + j][d] + Bb[j][d]    (j < m, block i-1, stream b)
+ * and Ccomp[i][d] = sum of those weights times Ca / Cb of the same rows.
+ * Block -1 is padded with -inf scores and zero values, unless prev_Cb /
+ * prev_Zb ([b, m, c]) supply the block that precedes row 0 (continuing a
+ * sequence, e.g. in decode).
+ *
+ * Pooling form (same pages, section B9 / section 5.1): overlap = 0, one
+ * stream: softmax over the m rows Za[m*i + j][d] + Ba[j][d] and the weighted
+ * sum of Ca.  Cb, Zb, Bb, prev_Cb and prev_Zb must then be NULL.
+ *
+ *  Ca, Cb, Za, Zb  [b, n, c]   input streams
+ *  Ba, Bb          [m, c]      intra-block position bias
+ *  Ccomp           out, entry i of sequence s at Ccomp + s*out_bstride + i*c,
+ *                  i < n/m  (a ragged tail of n % m rows emits nothing)
+ *
+ * Errors: CSA_EINVAL for b, n, c or m < 1, NULL required pointers, pointers
+ * given that must be NULL, out_bstride < (n/m)*c when non-zero, or only one
+ * of prev_Cb / prev_Zb.  CSA_ENOTSUP for an unknown dtype.
+ */
+int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
+                 const void* Ba, const void* Bb, const void* prev_Cb, const void* prev_Zb,
+                 int64_t b, int64_t n, int64_t c, int64_t m, int overlap, int dtype,
+                 void* Ccomp, int64_t out_bstride, void* stream);
+
+/*
+ * csa_index_topk -- lightning-indexer scores and top-k selection
+ * (polysight "06-formulas" section B9; AirCoding "deepseek-paper-analysis"
+ * section 7.1):
+ *     I[t][s] = sum_h w[t][h] * ReLU(qI[t][h] . KIcomp[s]),  s < (t+1)/m,
+ * then the k entries of largest score.  If fewer than k entries are visible,
+ * all of them are taken.  Ties at the k-th score go to the lower index.
+ *
+ *  qI      [b, n_q, n_hI, c_I]  indexer queries; row r is at position t0 + r
+ *  w       [b, n_q, n_hI]       float32 per-head weights (any sign)
+ *  KIcomp  [b, *, c_I]          compressed indexer keys (comp_bstride)
+ *  idx     out [b, n_q, k] int32, selected entries in ascending order,
+ *          padded with -1
+ *  score   out [b, n_q, k] float32 scores of idx (0 at padding), or NULL
+ *  workspace  device scratch of at least csa_index_topk_workspace_size()
+ *          bytes, 256-byte aligned; its contents on return are unspecified.
+ *
+ * Errors: CSA_EINVAL for sizes < 1 (n_comp may be 0), t0 < 0, NULL required
+ * pointers, or n_comp > (t0 + n_q)/m (entries that no query could have
+ * completed).  CSA_ENOSPC if ws_bytes is too small.
+ */
+int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride,
+                   int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI,
+                   int64_t c_I, int64_t m, int64_t k, int dtype, int32_t* idx, float* score,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+size_t csa_index_topk_workspace_size(int64_t b, int64_t n_q, int64_t n_comp, int64_t k);
+
+/*
+ * csa_attend -- shared key/value multi-query attention over the selected
+ * compressed entries plus the causal sliding window, with one softmax whose
+ * denominator also holds the per-head sink (AirCoding
+ * "deepseek-paper-analysis" section 7.1; songhuiming "DeepSeek-V4 百万
+ * token 上下文" sections 4.3, 4.5 and 7.3; polysight "06-formulas" B9):
+ *   E_t   = { Ccomp[s] : s in idx[t], 0 <= s < (t+1)/m }
+ *           U { kv_raw row at position p : max(0, t-n_win+1) <= p <= t }
+ *   l_j   = scale * (q[t][h] . e_j)
+ *   out[t][h] = sum_j exp(l_j) e_j / (sum_j exp(l_j) + exp(sink[h]))
+ * Every entry is both key and value.  Indices outside [0, (t+1)/m) are
+ * skipped (padding, or a guard against reading the future).
+ *
+ *  q       [b, n_q, n_h, c]   row r at position t0 + r
+ *  Ccomp   [b, *, c]          compressed entries (comp_bstride)
+ *  idx     [b, n_q, k] int32  from csa_index_topk (or any caller choice)
+ *  kv_raw  [b, *, c]          raw rows (raw_bstride); row j is at position
+ *                             raw_pos0 + j; n_raw rows are valid
+ *  sink    [n_h] float32      per-head sink logits (not scaled)
+ *  out     [b, n_q, n_h, c]
+ *
+ *  workspace  device scratch of csa_attend_workspace_size() bytes, 256-byte
+ *          aligned (may be NULL when that size is 0)
+ *
+ * Errors: CSA_EINVAL for sizes < 1 (n_comp and k may be 0), NULL required
+ * pointers, a non-finite scale, or a window that kv_raw does not cover:
+ * rows max(0, t0-n_win+1) .. t0+n_q-1 must lie in [raw_pos0, raw_pos0 +
+ * n_raw).  CSA_ENOSPC if ws_bytes is too small.  CSA_ENOTSUP for c > 1024
+ * outside the bf16 64-head c = 512 kernel.
+ */
+int csa_attend(const void* q, const void* Ccomp, int64_t comp_bstride, const int32_t* idx,
+               const void* kv_raw, int64_t raw_bstride, int64_t raw_pos0, const float* sink,
+               int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw,
+               int64_t n_h, int64_t c, int64_t k, int64_t m, int64_t n_win, float scale,
+               int dtype, void* workspace, size_t ws_bytes, void* out, void* stream);
+
+/* Device scratch csa_attend needs for these shapes (0 = none; then workspace
+ * may be NULL).  Few queries (decode) split each query's entries over
+ * several workgroups and merge the partial softmax states in a fixed order;
+ * the scratch holds those partials. */
+size_t csa_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp,
+                                 int64_t n_h, int64_t c, int64_t k, int64_t m, int64_t n_win,
+                                 int dtype);
+
+/*
+ * hca_attend -- HCA dense attention: every completed compressed entry
+ * (s < (t+1)/m_prime) plus the causal window, one softmax with the sink
+ * (polysight "06-formulas" B9; songhuiming section 5.2; AirCoding section
+ * 7.2).  Arguments as in csa_attend, without idx/k.
+ */
+int hca_attend(const void* q, const void* Ccomp, int64_t comp_bstride, const void* kv_raw,
+               int64_t raw_bstride, int64_t raw_pos0, const float* sink, int64_t b,
+               int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h,
+               int64_t c, int64_t m_prime, int64_t n_win, float scale, int dtype,
+               void* workspace, size_t ws_bytes, void* out, void* stream);
+
+size_t hca_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp,
+                                 int64_t n_h, int64_t c, int64_t m_prime, int64_t n_win,
+                                 int dtype);
+
+/*
+ * hca_layer -- one HCA prefill layer over whole sequences: the pooling
+ * compressor (csa_compress, overlap = 0) writes Ccomp [b, n/m_prime, c],
+ * then hca_attend runs every position 0..n-1 against it, with kv_raw = the
+ * window source [b, n, c].
+ *
+ *  C, Z [b, n, c]; B [m_prime, c]; q [b, n, n_h, c]; sink [n_h] float32
+ *  Ccomp  out (also read by the attention step) [b, n/m_prime, c]
+ *  workspace  as for hca_attend (hca_layer_workspace_size() bytes)
+ *  out    [b, n, n_h, c]
+ */
+int hca_layer(const void* C, const void* Z, const void* B, const void* q, const void* kv_raw,
+              const float* sink, int64_t b, int64_t n, int64_t c, int64_t m_prime, int64_t n_h,
+              int64_t n_win, float scale, int dtype, void* Ccomp, void* workspace,
+              size_t ws_bytes, void* out, void* stream);
+
+size_t hca_layer_workspace_size(int64_t b, int64_t n, int64_t n_h, int64_t c, int64_t m_prime,
+                                int64_t n_win, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

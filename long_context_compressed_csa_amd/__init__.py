@@ -1,0 +1,16 @@
+"""MI355X (gfx950) compressed sparse attention: one CSA / HCA layer.
+
+The compute lives in libcsa.so (hand-written HIP kernels behind the C ABI of
+include/csa.h).  This package is its thin Python binding; torch provides
+device memory and streams only.
+"""
+
+from ._binding import (  # noqa: F401
+    CSA_BF16, CSA_F32, CsaError, LIB_PATH, csa_attend, csa_compress, csa_index_topk,
+    hca_attend, hca_layer, load_library, strerror, version,
+)
+
+__all__ = [
+    "csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "hca_layer",
+    "load_library", "version", "strerror", "CsaError", "CSA_F32", "CSA_BF16", "LIB_PATH",
+]

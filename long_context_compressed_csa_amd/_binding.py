@@ -1,0 +1,266 @@
+"""ctypes binding of libcsa.so: argument marshalling only.
+
+Each function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks that tensors are on the GPU, contiguous and
+of one dtype, takes their data pointers and the current HIP stream, and
+raises CsaError on a non-zero return code.  Output and scratch tensors are
+allocated with torch when the caller does not pass them.  There is no CPU
+path: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+CSA_F32 = 0
+CSA_BF16 = 1
+_DT = {torch.float32: CSA_F32, torch.bfloat16: CSA_BF16}
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+# name -> (restype, argtypes); mirrors include/csa.h
+SIGNATURES = {
+    "csa_version": (ctypes.c_char_p, []),
+    "csa_strerror": (ctypes.c_char_p, [_int]),
+    "csa_compress": (_int, [_vp] * 8 + [_i64] * 4 + [_int, _int, _vp, _i64, _vp]),
+    "csa_index_topk": (_int, [_vp, _vp, _vp, _i64] + [_i64] * 8 + [_int, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_workspace_size": (_sz, [_i64] * 4),
+    "csa_attend": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp] + [_i64] * 10
+                   + [_f32, _int, _vp, _sz, _vp, _vp]),
+    "csa_attend_workspace_size": (_sz, [_i64] * 9 + [_int]),
+    "hca_attend": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp] + [_i64] * 9
+                   + [_f32, _int, _vp, _sz, _vp, _vp]),
+    "hca_attend_workspace_size": (_sz, [_i64] * 8 + [_int]),
+    "hca_layer": (_int, [_vp] * 6 + [_i64] * 6 + [_f32, _int, _vp, _vp, _sz, _vp, _vp]),
+    "hca_layer_workspace_size": (_sz, [_i64] * 6 + [_int]),
+}
+
+
+class CsaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libcsa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m long_context_compressed_csa_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load_library().csa_strerror(code).decode()
+
+
+def version() -> str:
+    return load_library().csa_version().decode()
+
+
+# ----------------------------------------------------------------- helpers --
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype(*ts):
+    dts = {t.dtype for t in ts if t is not None}
+    if len(dts) != 1:
+        raise ValueError(f"tensors must share one dtype, got {dts}")
+    dt = dts.pop()
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    return _DT[dt]
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise CsaError(rc, where)
+
+
+def _f32c(t, name):
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    return _ptr(t)
+
+
+def _batched(t, nd):
+    """View [..] as having a leading batch dim when it is missing."""
+    return t if t is None or t.dim() == nd else t.unsqueeze(0)
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    # 256-byte alignment is guaranteed by the caching allocator
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------ entry points --
+
+def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, m, prev_Cb=None, prev_Zb=None, out=None,
+                 overlap=True, stream=None):
+    """Compressor (overlap=True: CSA form; False: HCA pooling, pass Cb=Zb=Bb=None).
+
+    Streams [b, n, c] or [n, c]; biases [m, c]; returns [b, n//m, c] (or
+    [n//m, c] for 2-D inputs) unless `out` is given.
+    """
+    squeeze = Ca.dim() == 2
+    Ca, Cb, Za, Zb = (_batched(x, 3) for x in (Ca, Cb, Za, Zb))
+    prev_Cb, prev_Zb = _batched(prev_Cb, 3), _batched(prev_Zb, 3)
+    b, n, c = Ca.shape
+    dt = _dtype(Ca, Cb, Za, Zb, Ba, Bb, prev_Cb, prev_Zb)
+    out_bstride = 0
+    if out is None:
+        out = torch.empty((b, n // m, c), dtype=Ca.dtype, device=Ca.device)
+        ret = out[0] if squeeze else out
+    else:
+        ret = out
+        o3 = _batched(out, 3)
+        if o3.dtype != Ca.dtype or not o3.is_cuda:
+            raise ValueError("out must be a GPU tensor of the input dtype")
+        if o3.shape != (b, n // m, c) or o3.stride(2) != 1 or o3.stride(1) != c:
+            raise ValueError("out must be [b, n//m, c] with dense rows")
+        out_bstride = o3.stride(0) if b > 1 else 0
+        out = o3
+    lib = load_library()
+    rc = lib.csa_compress(_ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb),
+                          _ptr(prev_Cb), _ptr(prev_Zb), b, n, c, m, 1 if overlap else 0, dt,
+                          out.data_ptr(), out_bstride, _stream(stream))
+    _check(rc, "csa_compress")
+    return ret
+
+
+def csa_index_topk(qI, w, KIcomp, t0, m, k, n_comp=None, score=False, idx=None,
+                   workspace=None, stream=None):
+    """Indexer scores + top-k.  qI [b, n_q, n_hI, c_I]; w [b, n_q, n_hI] f32;
+    KIcomp [b, cap, c_I] (first n_comp rows used).  Returns idx int32
+    [b, n_q, k] (and the scores when score=True)."""
+    qI, w, KIcomp = _batched(qI, 4), _batched(w, 3), _batched(KIcomp, 3)
+    b, n_q, nh, cI = qI.shape
+    n_comp = KIcomp.shape[1] if n_comp is None else n_comp
+    dt = _dtype(qI, KIcomp)
+    lib = load_library()
+    need = lib.csa_index_topk_workspace_size(b, n_q, n_comp, k)
+    if workspace is None:
+        workspace = _workspace(max(need, 256), qI.device)
+    if idx is None:
+        idx = torch.empty((b, n_q, k), dtype=torch.int32, device=qI.device)
+    sc = torch.empty((b, n_q, k), dtype=torch.float32, device=qI.device) if score else None
+    rc = lib.csa_index_topk(_ptr(qI), _f32c(w, "w"), _ptr(KIcomp), KIcomp.stride(0), b, n_q, t0,
+                            n_comp, nh, cI, m, k, dt, _ptr(idx), _ptr(sc), _ptr(workspace),
+                            workspace.numel(), _stream(stream))
+    _check(rc, "csa_index_topk")
+    return (idx, sc) if score else idx
+
+
+def csa_attend(q, Ccomp, idx, kv_raw, sink, t0, m, n_win, scale=None, raw_pos0=0,
+               n_comp=None, n_raw=None, out=None, workspace=None, stream=None):
+    """CSA main attention.  q [b, n_q, n_h, c]; Ccomp [b, cap, c]; idx
+    [b, n_q, k] int32; kv_raw [b, rows, c] (row j at position raw_pos0+j);
+    sink [n_h] f32.  Returns out [b, n_q, n_h, c]."""
+    q, Ccomp, idx, kv_raw = _batched(q, 4), _batched(Ccomp, 3), _batched(idx, 3), _batched(kv_raw, 3)
+    b, n_q, n_h, c = q.shape
+    k = idx.shape[2]
+    n_comp = Ccomp.shape[1] if n_comp is None else n_comp
+    n_raw = kv_raw.shape[1] if n_raw is None else n_raw
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(q, Ccomp, kv_raw)
+    if idx.dtype != torch.int32:
+        raise ValueError("idx must be int32")
+    lib = load_library()
+    need = lib.csa_attend_workspace_size(b, n_q, t0, n_comp, n_h, c, k, m, n_win, dt)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.csa_attend(_ptr(q), _ptr(Ccomp), Ccomp.stride(0), _ptr(idx), _ptr(kv_raw),
+                        kv_raw.stride(0), raw_pos0, _f32c(sink, "sink"), b, n_q, t0, n_comp, n_raw,
+                        n_h, c, k, m, n_win, scale, dt, _ptr(workspace),
+                        0 if workspace is None else workspace.numel(), _ptr(out), _stream(stream))
+    _check(rc, "csa_attend")
+    return out
+
+
+def hca_attend(q, Ccomp, kv_raw, sink, t0, m_prime, n_win, scale=None, raw_pos0=0,
+               n_comp=None, n_raw=None, out=None, workspace=None, stream=None):
+    """HCA dense attention over every completed entry plus the window."""
+    q, Ccomp, kv_raw = _batched(q, 4), _batched(Ccomp, 3), _batched(kv_raw, 3)
+    b, n_q, n_h, c = q.shape
+    n_comp = Ccomp.shape[1] if n_comp is None else n_comp
+    n_raw = kv_raw.shape[1] if n_raw is None else n_raw
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(q, Ccomp, kv_raw)
+    lib = load_library()
+    need = lib.hca_attend_workspace_size(b, n_q, t0, n_comp, n_h, c, m_prime, n_win, dt)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.hca_attend(_ptr(q), _ptr(Ccomp), Ccomp.stride(0), _ptr(kv_raw), kv_raw.stride(0),
+                        raw_pos0, _f32c(sink, "sink"), b, n_q, t0, n_comp, n_raw, n_h, c, m_prime,
+                        n_win, scale, dt, _ptr(workspace),
+                        0 if workspace is None else workspace.numel(), _ptr(out), _stream(stream))
+    _check(rc, "hca_attend")
+    return out
+
+
+def hca_layer(C, Z, B, q, kv_raw, sink, m_prime, n_win, scale=None, Ccomp=None, out=None,
+              workspace=None, stream=None):
+    """Whole HCA prefill: pooling compressor then dense attention for every
+    position.  C, Z, kv_raw [b, n, c]; q [b, n, n_h, c]; returns (Ccomp, out)."""
+    C, Z, q, kv_raw = _batched(C, 3), _batched(Z, 3), _batched(q, 4), _batched(kv_raw, 3)
+    b, n, c = C.shape
+    n_h = q.shape[2]
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(C, Z, B, q, kv_raw)
+    lib = load_library()
+    need = lib.hca_layer_workspace_size(b, n, n_h, c, m_prime, n_win, dt)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    if Ccomp is None:
+        Ccomp = torch.empty((b, n // m_prime, c), dtype=C.dtype, device=C.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.hca_layer(_ptr(C), _ptr(Z), _ptr(B), _ptr(q), _ptr(kv_raw), _f32c(sink, "sink"), b, n,
+                       c, m_prime, n_h, n_win, scale, dt, _ptr(Ccomp), _ptr(workspace),
+                       0 if workspace is None else workspace.numel(), _ptr(out), _stream(stream))
+    _check(rc, "hca_layer")
+    return Ccomp, out

@@ -1,0 +1,200 @@
+// C ABI of the CSA/HCA library: host-side argument validation, then kernel
+// launches on the caller's stream.  Nothing here allocates device memory or
+// synchronises.  The operations are defined in include/csa.h.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+#include "kernels.hpp"
+
+namespace {
+
+inline bool dtype_ok(int dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+inline int launched(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_EHIP; }
+
+inline int64_t visible(int64_t t, int64_t m) { return (t + 1) / m; }
+
+// Window rows of queries t0..t0+n_q-1 must lie inside kv_raw.
+inline bool window_covered(int64_t t0, int64_t n_q, int64_t n_win, int64_t raw_pos0, int64_t n_raw) {
+  const int64_t lo = t0 - n_win + 1 > 0 ? t0 - n_win + 1 : 0;
+  const int64_t hi = t0 + n_q - 1;
+  return lo >= raw_pos0 && hi < raw_pos0 + n_raw;
+}
+
+int64_t attend_nmax(int dense, int64_t t0, int64_t n_q, int64_t n_comp, int64_t k, int64_t m,
+                    int64_t n_win) {
+  int64_t v = visible(t0 + n_q - 1, m);
+  if (v > n_comp) v = n_comp;
+  return (dense ? v : k) + n_win;
+}
+
+int check_attend(const void* q, const void* Ccomp, int64_t cbs, const void* kv_raw, int64_t rbs,
+                 int64_t raw_pos0, const float* sink, int64_t b, int64_t n_q, int64_t t0,
+                 int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c, int64_t m, int64_t n_win,
+                 float scale, int dtype, const void* out) {
+  if (!dtype_ok(dtype)) return CSA_ENOTSUP;
+  if (!q || !kv_raw || !sink || !out) return CSA_EINVAL;
+  if (n_comp > 0 && !Ccomp) return CSA_EINVAL;
+  if (b < 1 || n_q < 1 || n_h < 1 || c < 1 || m < 1 || n_win < 1 || n_raw < 1) return CSA_EINVAL;
+  if (t0 < 0 || n_comp < 0 || !isfinite(scale)) return CSA_EINVAL;
+  if (cbs < 0 || rbs < 0) return CSA_EINVAL;
+  if (cbs > 0 && cbs < n_comp * c) return CSA_EINVAL;
+  if (rbs > 0 && rbs < n_raw * c) return CSA_EINVAL;
+  if (!window_covered(t0, n_q, n_win, raw_pos0, n_raw)) return CSA_EINVAL;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_version(void) { return "csa-mi355x 0.1.0"; }
+
+const char* csa_strerror(int code) {
+  switch (code) {
+    case CSA_OK: return "ok";
+    case CSA_EINVAL: return "invalid argument";
+    case CSA_ENOTSUP: return "unsupported shape or dtype";
+    case CSA_ENOSPC: return "workspace too small";
+    case CSA_EHIP: return "HIP launch error";
+    default: return "unknown error";
+  }
+}
+
+int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const void* Ba,
+                 const void* Bb, const void* prev_Cb, const void* prev_Zb, int64_t b, int64_t n,
+                 int64_t c, int64_t m, int overlap, int dtype, void* Ccomp, int64_t out_bstride,
+                 void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ENOTSUP;
+  if (b < 1 || n < 1 || c < 1 || m < 1) return CSA_EINVAL;
+  if (overlap != 0 && overlap != 1) return CSA_EINVAL;
+  if (!Ca || !Za || !Ba || !Ccomp) return CSA_EINVAL;
+  if (overlap) {
+    if (!Cb || !Zb || !Bb) return CSA_EINVAL;
+    if ((prev_Cb == nullptr) != (prev_Zb == nullptr)) return CSA_EINVAL;
+  } else {
+    if (Cb || Zb || Bb || prev_Cb || prev_Zb) return CSA_EINVAL;
+  }
+  const int64_t ne = n / m;
+  if (out_bstride < 0 || (out_bstride > 0 && out_bstride < ne * c)) return CSA_EINVAL;
+  if (b > 65535) return CSA_ENOTSUP;
+  const int64_t obs = out_bstride > 0 ? out_bstride : ne * c;
+  return launched(csa::launch_compress(Ca, Cb, Za, Zb, Ba, Bb, prev_Cb, prev_Zb, b, n, c, m,
+                                       overlap, dtype, Ccomp, obs, (hipStream_t)stream));
+}
+
+size_t csa_index_topk_workspace_size(int64_t b, int64_t n_q, int64_t n_comp, int64_t k) {
+  if (b < 1 || n_q < 1 || n_comp < 0 || k < 1) return 0;
+  return csa::index_topk_workspace_bytes(b, n_q, n_comp, k);
+}
+
+int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride,
+                   int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI, int64_t c_I,
+                   int64_t m, int64_t k, int dtype, int32_t* idx, float* score, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ENOTSUP;
+  if (!qI || !w || !idx || !workspace) return CSA_EINVAL;
+  if (n_comp > 0 && !KIcomp) return CSA_EINVAL;
+  if (b < 1 || n_q < 1 || n_hI < 1 || c_I < 1 || m < 1 || k < 1 || t0 < 0 || n_comp < 0)
+    return CSA_EINVAL;
+  if (n_comp > visible(t0 + n_q - 1, m)) return CSA_EINVAL;
+  if (comp_bstride < 0 || (comp_bstride > 0 && comp_bstride < n_comp * c_I)) return CSA_EINVAL;
+  if (n_q > 65535 || b > 65535) return CSA_ENOTSUP;
+  if (!csa::index_topk_supported(n_comp, k)) return CSA_ENOTSUP;
+  if (((uintptr_t)workspace & 255u) != 0) return CSA_EINVAL;
+  if (ws_bytes < csa::index_topk_workspace_bytes(b, n_q, n_comp, k)) return CSA_ENOSPC;
+  const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c_I;
+  return launched(csa::launch_index_topk(qI, w, KIcomp, cbs, b, n_q, t0, n_comp, n_hI, c_I, m, k,
+                                         dtype, idx, score, workspace, (hipStream_t)stream));
+}
+
+size_t csa_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
+                                 int64_t c, int64_t k, int64_t m, int64_t n_win, int dtype) {
+  if (b < 1 || n_q < 1 || m < 1 || t0 < 0 || k < 0 || n_win < 1) return 0;
+  return csa::attend_workspace_bytes(dtype, b, n_q, n_h, c, attend_nmax(0, t0, n_q, n_comp, k, m, n_win));
+}
+
+size_t hca_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
+                                 int64_t c, int64_t m_prime, int64_t n_win, int dtype) {
+  if (b < 1 || n_q < 1 || m_prime < 1 || t0 < 0 || n_win < 1) return 0;
+  return csa::attend_workspace_bytes(dtype, b, n_q, n_h, c,
+                                     attend_nmax(1, t0, n_q, n_comp, 0, m_prime, n_win));
+}
+
+int csa_attend(const void* q, const void* Ccomp, int64_t comp_bstride, const int32_t* idx,
+               const void* kv_raw, int64_t raw_bstride, int64_t raw_pos0, const float* sink,
+               int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h,
+               int64_t c, int64_t k, int64_t m, int64_t n_win, float scale, int dtype,
+               void* workspace, size_t ws_bytes, void* out, void* stream) {
+  int rc = check_attend(q, Ccomp, comp_bstride, kv_raw, raw_bstride, raw_pos0, sink, b, n_q, t0,
+                        n_comp, n_raw, n_h, c, m, n_win, scale, dtype, out);
+  if (rc != CSA_OK) return rc;
+  if (k < 0 || (k > 0 && !idx)) return CSA_EINVAL;
+  if (n_q > 2147483647LL || b > 65535 || n_h > 65535) return CSA_ENOTSUP;
+  if (!csa::attend_supported(dtype, n_h, c, k)) return CSA_ENOTSUP;
+  const size_t need = csa_attend_workspace_size(b, n_q, t0, n_comp, n_h, c, k, m, n_win, dtype);
+  if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) != 0)) return CSA_EINVAL;
+  if (ws_bytes < need) return CSA_ENOSPC;
+  const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c;
+  const int64_t rbs = raw_bstride > 0 ? raw_bstride : n_raw * c;
+  return launched(csa::launch_attend(0, q, Ccomp, cbs, idx, kv_raw, rbs, raw_pos0, sink, b, n_q, t0,
+                                     n_comp, n_h, c, k, m, n_win, scale, dtype, workspace, out,
+                                     (hipStream_t)stream));
+}
+
+int hca_attend(const void* q, const void* Ccomp, int64_t comp_bstride, const void* kv_raw,
+               int64_t raw_bstride, int64_t raw_pos0, const float* sink, int64_t b, int64_t n_q,
+               int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c, int64_t m_prime,
+               int64_t n_win, float scale, int dtype, void* workspace, size_t ws_bytes, void* out,
+               void* stream) {
+  int rc = check_attend(q, Ccomp, comp_bstride, kv_raw, raw_bstride, raw_pos0, sink, b, n_q, t0,
+                        n_comp, n_raw, n_h, c, m_prime, n_win, scale, dtype, out);
+  if (rc != CSA_OK) return rc;
+  if (n_q > 2147483647LL || b > 65535 || n_h > 65535) return CSA_ENOTSUP;
+  if (!csa::attend_supported(dtype, n_h, c, 0)) return CSA_ENOTSUP;
+  const size_t need = hca_attend_workspace_size(b, n_q, t0, n_comp, n_h, c, m_prime, n_win, dtype);
+  if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) != 0)) return CSA_EINVAL;
+  if (ws_bytes < need) return CSA_ENOSPC;
+  const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c;
+  const int64_t rbs = raw_bstride > 0 ? raw_bstride : n_raw * c;
+  return launched(csa::launch_attend(1, q, Ccomp, cbs, nullptr, kv_raw, rbs, raw_pos0, sink, b, n_q,
+                                     t0, n_comp, n_h, c, 0, m_prime, n_win, scale, dtype, workspace,
+                                     out, (hipStream_t)stream));
+}
+
+size_t hca_layer_workspace_size(int64_t b, int64_t n, int64_t n_h, int64_t c, int64_t m_prime,
+                                int64_t n_win, int dtype) {
+  if (b < 1 || n < 1 || m_prime < 1) return 0;
+  return hca_attend_workspace_size(b, n, 0, n / m_prime, n_h, c, m_prime, n_win, dtype);
+}
+
+int hca_layer(const void* C, const void* Z, const void* B, const void* q, const void* kv_raw,
+              const float* sink, int64_t b, int64_t n, int64_t c, int64_t m_prime, int64_t n_h,
+              int64_t n_win, float scale, int dtype, void* Ccomp, void* workspace, size_t ws_bytes,
+              void* out, void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ENOTSUP;
+  if (!C || !Z || !B || !q || !kv_raw || !sink || !Ccomp || !out) return CSA_EINVAL;
+  if (b < 1 || n < 1 || c < 1 || m_prime < 1 || n_h < 1 || n_win < 1 || !isfinite(scale))
+    return CSA_EINVAL;
+  const int64_t ne = n / m_prime;
+  // validate the attention step before enqueuing the compressor
+  int rc = check_attend(q, Ccomp, 0, kv_raw, 0, 0, sink, b, n, 0, ne, n, n_h, c, m_prime, n_win,
+                        scale, dtype, out);
+  if (rc != CSA_OK) return rc;
+  if (b > 65535 || n_h > 65535) return CSA_ENOTSUP;
+  if (!csa::attend_supported(dtype, n_h, c, 0)) return CSA_ENOTSUP;
+  const size_t need = hca_layer_workspace_size(b, n, n_h, c, m_prime, n_win, dtype);
+  if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) != 0)) return CSA_EINVAL;
+  if (ws_bytes < need) return CSA_ENOSPC;
+  hipStream_t st = (hipStream_t)stream;
+  if (ne > 0) {
+    hipError_t e = csa::launch_compress(C, nullptr, Z, nullptr, B, nullptr, nullptr, nullptr, b, n,
+                                        c, m_prime, 0, dtype, Ccomp, ne * c, st);
+    if (e != hipSuccess) return CSA_EHIP;
+  }
+  return launched(csa::launch_attend(1, q, Ccomp, ne * c, nullptr, kv_raw, n * c, 0, sink, b, n, 0,
+                                     ne, n_h, c, 0, m_prime, n_win, scale, dtype, workspace, out, st));
+}
+
+}  // extern "C"

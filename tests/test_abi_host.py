@@ -1,0 +1,173 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry
+point the header declares, and rejects bad arguments before any launch.
+
+No call here reaches a kernel: every argument set is invalid (or a pure
+size query), so these run without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_compressed_csa_amd as L
+from long_context_compressed_csa_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+EINVAL, ENOTSUP, ENOSPC = -1, -2, -3
+FAKE = 0x10000  # a non-NULL address that is never dereferenced
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", src, flags=re.M)) - {"if"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libcsa.so is not built (run `python -m long_context_compressed_csa_amd.build`)")
+    return L.load_library()
+
+
+def test_header_declares_the_four_stages():
+    names = _declared()
+    for fn in ("csa_compress", "csa_index_topk", "csa_attend", "hca_layer"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding declares a signature for each
+    assert set(names) == set(B.SIGNATURES)
+
+
+def test_version_and_strerror(lib):
+    assert L.version().startswith("csa-mi355x")
+    assert L.strerror(0) == "ok"
+    assert "workspace" in L.strerror(ENOSPC)
+    assert L.strerror(12345) == "unknown error"
+
+
+def _compress(lib, **kw):
+    a = dict(Ca=FAKE, Cb=FAKE, Za=FAKE, Zb=FAKE, Ba=FAKE, Bb=FAKE, pCb=None, pZb=None,
+             b=1, n=16, c=8, m=4, overlap=1, dtype=1, out=FAKE, obs=0)
+    a.update(kw)
+    return lib.csa_compress(a["Ca"], a["Cb"], a["Za"], a["Zb"], a["Ba"], a["Bb"], a["pCb"], a["pZb"],
+                            a["b"], a["n"], a["c"], a["m"], a["overlap"], a["dtype"], a["out"],
+                            a["obs"], None)
+
+
+def test_compress_rejects_bad_arguments(lib):
+    assert _compress(lib, dtype=7) == ENOTSUP
+    assert _compress(lib, m=0) == EINVAL
+    assert _compress(lib, n=0) == EINVAL
+    assert _compress(lib, c=-1) == EINVAL
+    assert _compress(lib, Ca=None) == EINVAL
+    assert _compress(lib, Cb=None) == EINVAL                 # overlap needs stream b
+    assert _compress(lib, overlap=0) == EINVAL               # pooling forbids stream b
+    assert _compress(lib, overlap=0, Cb=None, Zb=None, Bb=None, pCb=FAKE) == EINVAL
+    assert _compress(lib, pCb=FAKE) == EINVAL                # prev state comes in pairs
+    assert _compress(lib, overlap=2) == EINVAL
+    assert _compress(lib, obs=5) == EINVAL                   # stride below (n/m)*c
+
+
+def _topk(lib, ws_bytes=1 << 20, **kw):
+    a = dict(qI=FAKE, w=FAKE, KI=FAKE, cbs=0, b=1, n_q=8, t0=0, n_comp=2, nh=2, cI=16, m=4, k=4,
+             dtype=0, idx=FAKE, score=None, ws=0x100000)
+    a.update(kw)
+    return lib.csa_index_topk(a["qI"], a["w"], a["KI"], a["cbs"], a["b"], a["n_q"], a["t0"],
+                              a["n_comp"], a["nh"], a["cI"], a["m"], a["k"], a["dtype"], a["idx"],
+                              a["score"], a["ws"], ws_bytes, None)
+
+
+def test_index_topk_rejects_bad_arguments(lib):
+    assert _topk(lib, k=0) == EINVAL
+    assert _topk(lib, m=0) == EINVAL
+    assert _topk(lib, t0=-1) == EINVAL
+    assert _topk(lib, n_comp=3) == EINVAL        # 8 queries from t0=0 complete only 2 entries
+    assert _topk(lib, ws=None) == EINVAL
+    assert _topk(lib, ws=0x100010) == EINVAL     # workspace must be 256-byte aligned
+    assert _topk(lib, ws_bytes=16) == ENOSPC
+    assert _topk(lib, dtype=9) == ENOTSUP
+    assert _topk(lib, cbs=5) == EINVAL
+    # long lists need k <= 2048 so every selection stage shrinks them
+    assert _topk(lib, n_q=1, t0=4 * 10000, n_comp=10000, k=4000, ws_bytes=1 << 30) == ENOTSUP
+
+
+def test_index_topk_workspace_size_grows_with_candidates(lib):
+    small = lib.csa_index_topk_workspace_size(1, 4, 100, 8)
+    big = lib.csa_index_topk_workspace_size(1, 4, 100000, 8)
+    assert 0 < small < big
+    assert lib.csa_index_topk_workspace_size(1, 8192, 2048, 512) >= 8192 * 2048 * 4
+    assert lib.csa_index_topk_workspace_size(0, 4, 100, 8) == 0
+
+
+def _attend(lib, fn="csa_attend", ws_bytes=0, **kw):
+    a = dict(q=FAKE, Cc=FAKE, cbs=0, idx=FAKE, raw=FAKE, rbs=0, pos0=0, sink=FAKE, b=1, n_q=4, t0=0,
+             n_comp=1, n_raw=4, n_h=2, c=8, k=2, m=4, n_win=4, scale=0.5, dtype=0, ws=None, out=FAKE)
+    a.update(kw)
+    if fn == "csa_attend":
+        return lib.csa_attend(a["q"], a["Cc"], a["cbs"], a["idx"], a["raw"], a["rbs"], a["pos0"],
+                              a["sink"], a["b"], a["n_q"], a["t0"], a["n_comp"], a["n_raw"], a["n_h"],
+                              a["c"], a["k"], a["m"], a["n_win"], a["scale"], a["dtype"], a["ws"],
+                              ws_bytes, a["out"], None)
+    return lib.hca_attend(a["q"], a["Cc"], a["cbs"], a["raw"], a["rbs"], a["pos0"], a["sink"], a["b"],
+                          a["n_q"], a["t0"], a["n_comp"], a["n_raw"], a["n_h"], a["c"], a["m"],
+                          a["n_win"], a["scale"], a["dtype"], a["ws"], ws_bytes, a["out"], None)
+
+
+@pytest.mark.parametrize("fn", ["csa_attend", "hca_attend"])
+def test_attend_rejects_bad_arguments(lib, fn):
+    assert _attend(lib, fn, q=None) == EINVAL
+    assert _attend(lib, fn, sink=None) == EINVAL
+    assert _attend(lib, fn, n_win=0) == EINVAL
+    assert _attend(lib, fn, scale=float("nan")) == EINVAL
+    # the window of queries 0..3 needs raw rows 0..3
+    assert _attend(lib, fn, n_raw=3) == EINVAL
+    assert _attend(lib, fn, pos0=1) == EINVAL
+    assert _attend(lib, fn, t0=10, n_raw=4, pos0=7) == EINVAL
+    assert _attend(lib, fn, dtype=4) == ENOTSUP
+    assert _attend(lib, fn, c=2048) == ENOTSUP
+    assert _attend(lib, fn, rbs=3) == EINVAL
+
+
+def test_attend_decode_needs_workspace(lib):
+    # one bf16 64-head c=512 query splits its entries: scratch is required
+    need = lib.csa_attend_workspace_size(1, 1, 4095, 1024, 64, 512, 512, 4, 128, 1)
+    assert need > 0
+    kw = dict(n_q=1, t0=4095, n_comp=1024, n_raw=128, pos0=3968, n_h=64, c=512, k=512, dtype=1,
+              n_win=128)
+    assert _attend(lib, ws=None, ws_bytes=need, **kw) == EINVAL
+    assert _attend(lib, ws=0x100000, ws_bytes=need - 1, **kw) == ENOSPC
+    # many queries: no scratch
+    assert lib.csa_attend_workspace_size(1, 8192, 0, 2048, 64, 512, 512, 4, 128, 1) == 0
+
+
+def test_hca_layer_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(C=FAKE, Z=FAKE, B=FAKE, q=FAKE, raw=FAKE, sink=FAKE, b=1, n=256, c=512, mp=128,
+                 n_h=64, n_win=128, scale=0.1, dtype=1, Cc=FAKE, ws=0x100000, wsb=1 << 30, out=FAKE)
+        a.update(kw)
+        return lib.hca_layer(a["C"], a["Z"], a["B"], a["q"], a["raw"], a["sink"], a["b"], a["n"], a["c"],
+                             a["mp"], a["n_h"], a["n_win"], a["scale"], a["dtype"], a["Cc"], a["ws"],
+                             a["wsb"], a["out"], None)
+    assert call(C=None) == EINVAL
+    assert call(mp=0) == EINVAL
+    assert call(dtype=3) == ENOTSUP
+    assert call(wsb=0) == ENOSPC
+    assert call(Cc=None) == EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(8, 4)
+    with pytest.raises(ValueError):
+        L.csa_compress(x, x, x, x, torch.zeros(4, 4), torch.zeros(4, 4), 4)
