@@ -1,0 +1,434 @@
+"""Benchmark of one CSA layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill]
+                    [--no-cpu-baseline] [--calibrate-copy]
+
+One step is one CSA prefill layer at n = 8192 (64 heads, c = 512, m = 4,
+k = 512, window 128, indexer 64 x 128, bf16): the main-entry compressor, the
+indexer-key compressor, indexer scoring + top-k, and the main attention, all
+on device-resident synthetic inputs.  The JSON line reports prefill tokens/s
+as `value`, the attention kernel's MFMA roofline fraction from HIP-event
+timings, and the CPU oracle's rate on a bounded sample.  Secondary lines in
+the same JSON object: 1M-context decode (8 sequences, microseconds per step),
+the HCA prefill layer (n = 131072) and the compressor sweep (n = 65536).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA prefill tokens/s @n=8192 (% MFMA roofline); 1M-ctx decode µs/step"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+class KernelTimer:
+    """HIP-event timing of named launches on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.total = {}
+        self.count = {}
+
+    def run(self, name, fn):
+        a, b = _events(self.torch)
+        a.record()
+        r = fn()
+        b.record()
+        self.pending.append((name, a, b))
+        return r
+
+    def collect(self):
+        self.torch.cuda.synchronize()
+        for name, a, b in self.pending:
+            self.total[name] = self.total.get(name, 0.0) + a.elapsed_time(b)
+            self.count[name] = self.count.get(name, 0) + 1
+        self.pending = []
+
+    def avg_us(self, name):
+        return 1000.0 * self.total[name] / self.count[name]
+
+
+# --------------------------------------------------------------- prefill ----
+
+def prefill_pairs(n, m, k, n_win):
+    """(selected, window) query-entry pairs of a causal CSA prefill."""
+    sel = sum(min(k, (t + 1) // m) for t in range(n))
+    win = sum(min(t + 1, n_win) for t in range(n))
+    return sel, win
+
+
+def run_prefill(args, torch, L, synth):
+    p = dict(synth.PREFILL)
+    d = synth.prefill_inputs(device="cuda")
+    n, m, k, nw, nh, c, nI, cI = p["n"], p["m"], p["k"], p["n_win"], p["n_h"], p["c"], p["n_hI"], p["c_I"]
+    ne = n // m
+    lib = L.load_library()
+    st = torch.cuda.current_stream().cuda_stream
+    Cc = torch.empty((1, ne, c), dtype=torch.bfloat16, device="cuda")
+    KI = torch.empty((1, ne, cI), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((1, n, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, n, nh, c), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = lib.csa_index_topk_workspace_size(1, n, ne, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    P = lambda t: t.data_ptr()
+
+    def comp_main():
+        return lib.csa_compress(P(d["Ca"]), P(d["Cb"]), P(d["Za"]), P(d["Zb"]), P(d["Ba"]), P(d["Bb"]),
+                                None, None, 1, n, c, m, 1, 1, P(Cc), 0, st)
+
+    def comp_index():
+        return lib.csa_compress(P(d["ICa"]), P(d["ICb"]), P(d["IZa"]), P(d["IZb"]), P(d["IBa"]),
+                                P(d["IBb"]), None, None, 1, n, cI, m, 1, 1, P(KI), 0, st)
+
+    def index_topk():
+        return lib.csa_index_topk(P(d["qI"]), P(d["w"]), P(KI), 0, 1, n, 0, ne, nI, cI, m, k, 1, P(idx),
+                                  None, P(ws), ws_bytes, st)
+
+    def attend():
+        return lib.csa_attend(P(d["q"]), P(Cc), 0, P(idx), P(d["kv_raw"]), 0, 0, P(d["sink"]), 1, n, 0, ne,
+                              n, nh, c, k, m, nw, d["scale"], 1, None, 0, P(out), st)
+
+    stages = [("compress_main", comp_main), ("compress_index_keys", comp_index),
+              ("index_topk", index_topk), ("attend", attend)]
+
+    def step(timer=None):
+        for name, fn in stages:
+            rc = timer.run(name, fn) if timer else fn()
+            if rc != 0:
+                raise RuntimeError(f"{name} failed: {L.strerror(rc)}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step wall time: K steps between two synchronisations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1000.0 * (time.perf_counter() - t0) / args.steps
+    # per-kernel HIP-event timings over a second pass of K steps
+    timer = KernelTimer(torch)
+    for _ in range(args.steps):
+        step(timer)
+    timer.collect()
+    stage_us = {name: timer.avg_us(name) for name, _ in stages}
+
+    sel, win = prefill_pairs(n, m, k, nw)
+    flop_attend = (sel + win) * 4 * nh * c
+    vis_pairs = sum(min((t + 1) // m, ne) for t in range(n))
+    flop_index = vis_pairs * 2 * nI * cI
+    att_tflops = flop_attend / (stage_us["attend"] * 1e-6) / 1e12
+    return {
+        "ms_per_step": ms,
+        "tokens_per_s": n / (ms / 1000.0),
+        "stage_us": stage_us,
+        "flop_attend": flop_attend,
+        "flop_index": flop_index,
+        "attend_tflops": att_tflops,
+        "index_tflops": flop_index / (stage_us["index_topk"] * 1e-6) / 1e12,
+        "step_tflops": (flop_attend + flop_index) / (ms * 1e-3) / 1e12,
+        "inputs": d,
+    }
+
+
+# ---------------------------------------------------------------- decode ----
+
+def run_decode(args, torch, L, synth):
+    d = synth.decode_inputs(device="cuda")
+    p = d["params"]
+    b, hist, m, nh, c, nw, nI, cI, k, steps = (p["b"], p["history"], p["m"], p["n_h"], p["c"], p["n_win"],
+                                               p["n_hI"], p["c_I"], p["k"], p["steps"])
+    lib = L.load_library()
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    ne0 = d["n_comp0"]
+    cap = d["Ccomp"].shape[1]
+    tails = {key: torch.empty((b, m, c if key[0] != "I" else cI), dtype=torch.bfloat16, device="cuda")
+             for key in ("Ca", "Cb", "Za", "Zb", "ICa", "ICb", "IZa", "IZb")}
+    new_prev = {key: torch.empty_like(d[key]) for key in ("prev_Cb", "prev_Zb", "prev_ICb", "prev_IZb")}
+    idx = torch.empty((b, 1, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((b, 1, nh, c), dtype=torch.bfloat16, device="cuda")
+    wsI_bytes = lib.csa_index_topk_workspace_size(b, 1, ne0 + steps, k)
+    wsI = torch.empty(wsI_bytes, dtype=torch.uint8, device="cuda")
+    wsA_bytes = max(lib.csa_attend_workspace_size(b, 1, hist + s, ne0 + 1, nh, c, k, m, nw, 1)
+                    for s in range(steps))
+    wsA = torch.empty(max(wsA_bytes, 256), dtype=torch.uint8, device="cuda")
+    win = d["window"]
+    raw_pos0 = d["window_pos0"]
+
+    def one_step(i):
+        t = hist + i
+        j = t % m
+        for key in tails:
+            tails[key][:, j].copy_(d["tok"][key][i])
+        win[:, nw + i].copy_(d["tok"]["Ca"][i])
+        if (t + 1) % m == 0:
+            e = (t + 1) // m - 1
+            rc = lib.csa_compress(P(tails["Ca"]), P(tails["Cb"]), P(tails["Za"]), P(tails["Zb"]), P(d["Ba"]),
+                                  P(d["Bb"]), P(d["prev_Cb"]), P(d["prev_Zb"]), b, m, c, m, 1, 1,
+                                  d["Ccomp"][:, e].data_ptr(), cap * c, st)
+            rc |= lib.csa_compress(P(tails["ICa"]), P(tails["ICb"]), P(tails["IZa"]), P(tails["IZb"]),
+                                   P(d["IBa"]), P(d["IBb"]), P(d["prev_ICb"]), P(d["prev_IZb"]), b, m, cI, m,
+                                   1, 1, d["KIcomp"][:, e].data_ptr(), cap * cI, st)
+            new_prev["prev_Cb"].copy_(tails["Cb"])
+            new_prev["prev_Zb"].copy_(tails["Zb"])
+            new_prev["prev_ICb"].copy_(tails["ICb"])
+            new_prev["prev_IZb"].copy_(tails["IZb"])
+            if rc != 0:
+                raise RuntimeError("decode compress failed")
+        n_comp = (t + 1) // m
+        rc = lib.csa_index_topk(P(d["qI"][i]), P(d["w"][i]), P(d["KIcomp"]), cap * cI, b, 1, t, n_comp, nI,
+                                cI, m, k, 1, P(idx), None, P(wsI), wsI_bytes, st)
+        if rc != 0:
+            raise RuntimeError(f"decode index failed: {L.strerror(rc)}")
+        rc = lib.csa_attend(P(d["q"][i]), P(d["Ccomp"]), cap * c, P(idx), P(win), (nw + steps) * c, raw_pos0,
+                            P(d["sink"]), b, 1, t, n_comp, nw + steps, nh, c, k, m, nw, d["scale"], 1,
+                            P(wsA), wsA.numel(), P(out), st)
+        if rc != 0:
+            raise RuntimeError(f"decode attend failed: {L.strerror(rc)}")
+
+    reps = max(1, args.decode_reps)
+    for _ in range(2):
+        for i in range(steps):
+            one_step(i)
+    torch.cuda.synchronize()
+    a, bb = _events(torch)
+    a.record()
+    for _ in range(reps):
+        for i in range(steps):
+            one_step(i)
+    bb.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * a.elapsed_time(bb) / (reps * steps)
+    key_bytes = b * ne0 * cI * 2
+    gathered = b * (k + nw) * c * 2
+    small = b * (nh * c * 2 * 2 + nI * cI * 2 + nI * 4 + k * 4)
+    step_bytes = key_bytes + gathered + small
+    return {"us_per_step": us, "bytes_per_step": step_bytes,
+            "hbm_gbs": step_bytes / (us * 1e-6) / 1e9, "b": b, "history": hist, "k": k}
+
+
+# ------------------------------------------------------------------- HCA ----
+
+def run_hca(args, torch, L, synth):
+    d = synth.hca_inputs(device="cuda")
+    p = d["params"]
+    n, mp, nh, c, nw = p["n"], p["m_prime"], p["n_h"], p["c"], p["n_win"]
+    lib = L.load_library()
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    Cc = torch.empty((1, n // mp, c), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(d["q"])
+    need = lib.hca_layer_workspace_size(1, n, nh, c, mp, nw, 1)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rc = lib.hca_layer(P(d["C"]), P(d["Z"]), P(d["B"]), P(d["q"]), P(d["kv_raw"]), P(d["sink"]), 1, n, c,
+                           mp, nh, nw, d["scale"], 1, P(Cc), P(ws), ws.numel(), P(out), st)
+        if rc != 0:
+            raise RuntimeError(f"hca_layer failed: {L.strerror(rc)}")
+
+    step()
+    torch.cuda.synchronize()
+    a, b = _events(torch)
+    iters = max(1, args.hca_iters)
+    a.record()
+    for _ in range(iters):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    ne = n // mp
+    pairs = sum(min((t + 1) // mp, ne) + min(t + 1, nw) for t in range(n))
+    flop = pairs * 4 * nh * c
+    del d, out
+    torch.cuda.empty_cache()
+    return {"ms_per_layer": ms, "tokens_per_s": n / (ms * 1e-3), "tflops": flop / (ms * 1e-3) / 1e12,
+            "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop": flop}
+
+
+# ------------------------------------------------------------ compressor ----
+
+def run_compress(args, torch, L, synth):
+    lib = L.load_library()
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    res = {}
+    for overlap in (True, False):
+        d = synth.compress_inputs(overlap, device="cuda")
+        m = d["m"]
+        n, c = synth.COMPRESS["n"], synth.COMPRESS["c"]
+        out = torch.empty((1, n // m, c), dtype=torch.bfloat16, device="cuda")
+        if overlap:
+            call = lambda: lib.csa_compress(P(d["Ca"]), P(d["Cb"]), P(d["Za"]), P(d["Zb"]), P(d["Ba"]), P(d["Bb"]),
+                                            None, None, 1, n, c, m, 1, 1, P(out), 0, st)
+            nbytes = 4 * n * c * 2 + 2 * m * c * 2 + (n // m) * c * 2
+        else:
+            call = lambda: lib.csa_compress(P(d["C"]), None, P(d["Z"]), None, P(d["B"]), None, None, None, 1, n,
+                                            c, m, 0, 1, P(out), 0, st)
+            nbytes = 2 * n * c * 2 + m * c * 2 + (n // m) * c * 2
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        a, b = _events(torch)
+        iters = 200
+        a.record()
+        for _ in range(iters):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * a.elapsed_time(b) / iters
+        res["overlap_m4" if overlap else "pool_m128"] = {
+            "us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return res
+
+
+# ---------------------------------------------------------- CPU baseline ----
+
+def cpu_baseline(prefill_inputs, torch, n_queries):
+    """The oracle, as it stands, on a bounded sample of the same prefill:
+    both compressors over all 8192 tokens, then indexer + top-k + attention
+    for `n_queries` query rows spread over the sequence.  The rate is
+    extrapolated to all 8192 queries."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
+    except Exception:  # pragma: no cover
+        threads, blas = os.cpu_count(), "unknown"
+    d = {key: v.detach().to("cpu", torch.float64).numpy() for key, v in prefill_inputs.items()
+         if isinstance(v, torch.Tensor) and key not in ("q", "qI", "w")}
+    p = prefill_inputs["params"]
+    n, m, k, nw = p["n"], p["m"], p["k"], p["n_win"]
+    rows = np.linspace(0, n - 1, n_queries).astype(np.int64)
+    rsel = torch.tensor(rows, device=prefill_inputs["q"].device)
+    q = prefill_inputs["q"][rsel].to("cpu", torch.float64).numpy()
+    qI = prefill_inputs["qI"][rsel].to("cpu", torch.float64).numpy()
+    w = prefill_inputs["w"][rsel].to("cpu", torch.float64).numpy()
+    t0 = time.perf_counter()
+    Cc = O.compress_overlap(d["Ca"], d["Cb"], d["Za"], d["Zb"], d["Ba"], d["Bb"], m)
+    KI = O.compress_overlap(d["ICa"], d["ICb"], d["IZa"], d["IZb"], d["IBa"], d["IBb"], m)
+    t1 = time.perf_counter()
+    idx, _ = O.index_topk(qI, w, KI, rows, m, k)
+    O.csa_attend(q, Cc, idx, d["Ca"], 0, d["sink"], rows, nw, prefill_inputs["scale"], m)
+    t2 = time.perf_counter()
+    full = (t1 - t0) + (t2 - t1) * n / n_queries
+    return {"value": n / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle ({blas}): both compressors over all {n} tokens "
+                       f"({t1 - t0:.2f} s) + indexer/top-k/attention for {n_queries} evenly spaced "
+                       f"queries ({t2 - t1:.2f} s), extrapolated to {n} queries"),
+            "seconds": t2 - t0}
+
+
+def calibrate_copy(torch):
+    """A plain device copy of known size, for scaling HBM counters."""
+    nbytes = 1 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["prefill", "decode", "hca", "compress"], default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-queries", type=int, default=8192)
+    ap.add_argument("--decode-reps", type=int, default=10)
+    ap.add_argument("--hca-iters", type=int, default=3)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_compressed_csa_amd as L
+    from long_context_compressed_csa_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    L.load_library()
+    if a.calibrate_copy:
+        calibrate_copy(torch)
+        return
+    extras = {}
+    pre = None
+    if a.only in (None, "prefill"):
+        print("[bench] prefill", file=sys.stderr, flush=True)
+        pre = run_prefill(a, torch, L, synth)
+    if a.only in (None, "decode"):
+        print("[bench] decode", file=sys.stderr, flush=True)
+        extras["decode_1m"] = run_decode(a, torch, L, synth)
+    if a.only in (None, "hca"):
+        print("[bench] hca", file=sys.stderr, flush=True)
+        extras["hca_prefill"] = run_hca(a, torch, L, synth)
+    if a.only in (None, "compress"):
+        print("[bench] compress", file=sys.stderr, flush=True)
+        extras["compressor"] = run_compress(a, torch, L, synth)
+    if pre is None:
+        print(json.dumps({"extras": extras}))
+        return
+    cpu = None
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(pre["inputs"], torch, a.cpu_queries)
+    att_us = pre["stage_us"]["attend"]
+    line = {
+        "metric": METRIC,
+        "value": pre["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs at the layer's shapes; no trained weights)",
+        "config": {"workload": "CSA prefill layer, n=8192, n_h=64, c=512, m=4, k=512, n_win=128, "
+                               "indexer 64x128, bf16, causal",
+                   "global_batch": 1, "seq_len": 8192},
+        "roofline": {"bound": "mfma", "kernel": "attend_mfma_c512 (csa_attend)",
+                     "achieved": pre["attend_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": pre["attend_tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flop_per_launch": pre["flop_attend"], "avg_launch_us": att_us},
+        "cpu_baseline": cpu,
+        "stage_us": pre["stage_us"],
+        "step_mfma_frac": pre["step_tflops"] / PEAK_BF16_TFLOPS,
+        "index_tflops": pre["index_tflops"],
+    }
+    if "decode_1m" in extras:
+        line["decode_us_per_step"] = extras["decode_1m"]["us_per_step"]
+    line["extras"] = extras
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -150,13 +150,12 @@ def prefill_inputs(n=None, seed=None, device="cpu", n_h=None, k=None, unscaled=F
     return d
 
 
-def hca_inputs(n=None, seed=None, device="cpu", n_h=None):
+def hca_inputs(n=None, seed=None, device="cpu", n_h=None, m_prime=None):
     """HCA prefill layer; q is the big tensor ([n, n_h, c])."""
     p = dict(HCA)
-    if n is not None:
-        p["n"] = n
-    if n_h is not None:
-        p["n_h"] = n_h
+    for key, v in (("n", n), ("n_h", n_h), ("m_prime", m_prime)):
+        if v is not None:
+            p[key] = v
     g = _gen(p["seed"] if seed is None else seed, device)
     n, c, mp, nh, dt = p["n"], p["c"], p["m_prime"], p["n_h"], p["dtype"]
     d = {"C": scaled((n, c), g, dt, device), "Z": scaled((n, c), g, dt, device),
