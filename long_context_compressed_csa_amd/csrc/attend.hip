@@ -9,15 +9,8 @@
 // sink logit); section 5.2 and polysight "06-formulas" B9 for the dense HCA
 // read.
 //
-// MFMA path (bf16, 64 heads x c = 512): one workgroup per (query, 64-head
-// group, entry split).  The four waves split the 512 dimensions: wave w
-// holds q[:, 128w:128w+128] in registers and owns O[:, 128w:128w+128] in
-// accumulators.  Per tile of 32 entries each wave gathers its 128-dim slice
-// of the 32 rows straight from global memory into MFMA B registers (S = Q E^T
-// needs entries with dimensions contiguous, which is how they are stored),
-// the four partial S tiles are summed through LDS, the wave that owns a head
-// runs the online softmax for it, and P V uses each wave's own slice of the
-// tile re-read from LDS with rows as the contraction index.
+// The MFMA path (bf16, c = 512, 64-head groups) is described above its
+// kernel; the generic path covers every other shape and float32.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -113,284 +106,353 @@ __global__ __launch_bounds__(256) void attend_generic(
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path.  Layout constants for one workgroup (4 waves, 64 heads, c=512).
+// MFMA path (bf16, c = 512, 64-head groups).
+//
+// A workgroup serves G consecutive queries of one 64-head group; two waves
+// per query, each owning 32 heads over all 512 dimensions (Q^T operand in
+// 128 VGPRs, O accumulator in 256 AGPRs).  Entries are processed in tiles of
+// 32 rows that all waves of the workgroup share: the rows are gathered from
+// HBM/L2 straight into LDS (global_load_lds_dwordx4, one 1 KiB row per wave
+// instruction), double-buffered with one barrier per tile.
+//
+// Per tile and wave:
+//   S^T = E Q^T      v_mfma_f32_32x32x16_bf16, A = E rows from LDS
+//                    (ds_read_b128), B = Q^T from registers.  The result
+//                    has one head per lane column and 16 entries per lane,
+//                    so the softmax over entries needs only in-lane work and
+//                    one exchange between the two lane halves.
+//   O += P E         A = P taken straight from the S^T accumulators (the
+//                    contraction index is permuted to match their row
+//                    layout), B = E^T read with ds_read_b64_tr_b16, which
+//                    returns a 4-row x 16-column block column-per-lane.
+// LDS rows are 1 KiB with the 16-byte chunks of row r XOR-swizzled by
+// f(r) = 2(r%4) + (r/4)%2, which keeps both the b128 row reads (8 rows, one
+// chunk) and the transposed reads (4 rows, two chunks) free of bank
+// conflicts.
 // ---------------------------------------------------------------------------
 constexpr int kC = 512;
-constexpr int kHG = 64;              // heads per workgroup
-constexpr int kDW = kC / 4;          // dimensions per wave (128)
+constexpr int kHG = 64;              // heads per head group
+constexpr int kHW = 32;              // heads per wave
 constexpr int kT = 32;               // entries per tile
-constexpr int kERow = kDW * 2 + 8;   // LDS row of a wave's E slice, bytes (264)
-constexpr int kSStr = 33;            // S partial row stride, floats
-constexpr int kPRow = kT * 2 + 16;   // P row (one head), bytes (80)
+constexpr int kRowB = kC * 2;        // LDS bytes per entry row
+constexpr int kTileB = kT * kRowB;   // 32 KiB
 constexpr int kMaxSel = 2048;        // selected entries staged in LDS
+constexpr int kStageRowB = 256 * 2;  // output staging row (256 dims), XOR-swizzled
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+template <int DENSE, int G>
 struct AttnSmem {
-  unsigned char E[4][kT * kERow];        // 33 KiB
-  float S[4][kHG * kSStr];               // 33 KiB
-  unsigned char P[kHG * kPRow];          // 5 KiB
-  float alpha[kHG];
-  float fin[kHG];
-  int32_t sel[kMaxSel];                  // 8 KiB
-  int32_t nsel_part[4];
+  unsigned char E[2][kTileB];       // 64 KiB, reused for output staging
+  int32_t sel[DENSE ? 1 : kMaxSel];
+  float bc[2 * G][kHW];             // per-wave broadcast of per-head factors
+  int32_t cnt[2 * G];
+  int32_t gen;                      // restart generation (see the softmax note)
 };
 
-template <int DENSE>
-__global__ __launch_bounds__(256) void attend_mfma_c512(
+template <int DENSE, int G>
+__global__ __launch_bounds__(128 * G) void attend_mfma_c512(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Ccomp, int64_t cbs,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ kv_raw, int64_t rbs,
     int64_t raw_pos0, const float* __restrict__ sink, int64_t n_q, int64_t t0, int64_t n_comp,
     int n_h, int64_t k, int64_t m, int64_t n_win, float scale, int nsplit,
     float* __restrict__ part_o, float* __restrict__ part_ml, bf16_t* __restrict__ out) {
-  __shared__ AttnSmem sm;
+  constexpr int NW = 2 * G;  // waves per workgroup
+  __shared__ AttnSmem<DENSE, G> sm;
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  const int64_t r = (int64_t)gridDim.x - 1 - blockIdx.x;   // later queries (more work) first
+  const int half = l >> 5;
+  const int qw = wave >> 1;          // query slot in the group
+  const int hw = wave & 1;           // which 32 heads of the group
+  const int64_t grp = (int64_t)gridDim.x - 1 - blockIdx.x;   // later queries (more work) first
   const int hg = blockIdx.y / nsplit;
   const int split = blockIdx.y % nsplit;
   const int64_t bi = blockIdx.z;
-  const int64_t t = t0 + r;
-  int64_t vis = (t + 1) / m;
-  if (vis > n_comp) vis = n_comp;
-  const int64_t wlo = t - n_win + 1 > 0 ? t - n_win + 1 : 0;
-  const int64_t nwin = t - wlo + 1;
+  const int64_t r0 = grp * G;
+  const int64_t rlast = (r0 + G - 1 < n_q) ? r0 + G - 1 : n_q - 1;
+  const int64_t rq = r0 + qw;
+  const bool qvalid = rq < n_q;
+  const int64_t t_first = t0 + r0, t_last = t0 + rlast;
+  const int64_t t_q = t0 + (qvalid ? rq : rlast);
 
-  // ---- entry list: selected compressed rows (compacted), then window rows
-  int64_t nsel;
+  // ---- entry list: compressed part (selected or dense), then the union of
+  //      the group's causal windows
+  int64_t nsel, vis_q;
   if (DENSE) {
-    nsel = vis;
+    nsel = (t_last + 1) / m;
+    if (nsel > n_comp) nsel = n_comp;
+    vis_q = (t_q + 1) / m;
+    if (vis_q > n_comp) vis_q = n_comp;
   } else {
-    // stable compaction of valid indices (0 <= s < vis) in list order
-    const int32_t* ir = idx + (bi * n_q + r) * k;
+    // G == 1: stable compaction of the valid indices (0 <= s < visible)
+    int64_t vis = (t_first + 1) / m;
+    if (vis > n_comp) vis = n_comp;
+    const int32_t* ir = idx + (bi * n_q + r0) * k;
     int64_t base = 0;
-    for (int64_t j0 = 0; j0 < k; j0 += 256) {
+    for (int64_t j0 = 0; j0 < k; j0 += 64 * NW) {
       const int64_t j = j0 + tid;
-      const int32_t s = j < k ? ir[j] : -1;
-      const bool ok = s >= 0 && s < vis;
+      const int32_t sv = j < k ? ir[j] : -1;
+      const bool ok = sv >= 0 && sv < vis;
       const uint64_t mk = __ballot(ok);
-      if (l == 0) sm.nsel_part[wave] = __popcll(mk);
+      if (l == 0) sm.cnt[wave] = __popcll(mk);
       __syncthreads();
       int64_t pos = base;
-      for (int w2 = 0; w2 < wave; ++w2) pos += sm.nsel_part[w2];
+      for (int w2 = 0; w2 < wave; ++w2) pos += sm.cnt[w2];
       pos += __popcll(mk & ((l == 0) ? 0ull : (~0ull >> (64 - l))));
-      if (ok && pos < kMaxSel) sm.sel[pos] = s;
-      base += sm.nsel_part[0] + sm.nsel_part[1] + sm.nsel_part[2] + sm.nsel_part[3];
+      if (ok && pos < kMaxSel) sm.sel[pos] = sv;
+      for (int w2 = 0; w2 < NW; ++w2) base += sm.cnt[w2];
       __syncthreads();
     }
     nsel = base < kMaxSel ? base : kMaxSel;
+    vis_q = nsel;
   }
-  const int64_t N = nsel + nwin;
-  // this split's entry range
+  const int64_t wlo = t_first - n_win + 1 > 0 ? t_first - n_win + 1 : 0;
+  const int64_t N = nsel + (t_last - wlo + 1);
   const int64_t per = (N + nsplit - 1) / nsplit;
-  const int64_t jb = split * per;
+  const int64_t jb = (int64_t)split * per;
   const int64_t je = jb + per < N ? jb + per : N;
-
-  // ---- query operand: heads 64*hg + 32*mb + l%32, dims 128*wave + 16*ks + 8*(l/32)
-  bf16x8 qa[2][8];
-  {
-    const bf16_t* qb = q + ((bi * n_q + r) * n_h + kHG * hg) * (int64_t)kC + kDW * wave + 8 * (l >> 5);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        qa[mb][ks] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(qb + (mb * 32 + (l & 31)) * (int64_t)kC + ks * 16));
-  }
-  f32x16 o[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) o[mb][nb] = (f32x16){};
-
-  // softmax state of head 16*wave + l/4 (replicated over 4 lanes)
-  float m_run = -INFINITY, l_run = 0.f;
-  const int own_h = 16 * wave + (l >> 2);
-  const int own_r0 = (l & 3) * 8;
+  const int ntiles = je > jb ? (int)((je - jb + kT - 1) / kT) : 0;
 
   const bf16_t* cbase = Ccomp + bi * cbs;
   const bf16_t* rbase = kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
-  unsigned char* Ew = sm.E[wave];
+  // gather one tile into LDS.  Lane l (< 32) resolves the address of tile
+  // row l; wave w then loads rows w, w+NW, ... with the row base broadcast
+  // to scalar registers, lane l fetching chunk l ^ f(row) so that LDS chunk
+  // position c holds row chunk c ^ f(row).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue_tile = [&](int64_t jt, int buf) {
+    int64_t j = jt + (l & 31);
+    if (j >= je) j = jb;  // tail padding rows: any real row (its weight is 0)
+    const bf16_t* p = j < nsel ? cbase + (int64_t)(DENSE ? j : sm.sel[j]) * kC
+                               : rbase + (j - nsel) * (int64_t)kC;
+    const uint64_t pv = reinterpret_cast<uint64_t>(p);
+    const uint32_t plo = (uint32_t)pv, phi = (uint32_t)(pv >> 32);
+#pragma unroll
+    for (int rr = 0; rr < kT / NW; ++rr) {
+      const int row = wave_u + rr * NW;
+      // readlane returns a signed int: zero-extend both halves
+      const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(phi, row) << 32) |
+                            (uint64_t)(uint32_t)__builtin_amdgcn_readlane(plo, row);
+      const unsigned char* src = reinterpret_cast<const unsigned char*>(base) + ((l ^ swz(row)) << 4);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(&sm.E[buf][row * kRowB]), 16, 0, 0);
+    }
+  };
 
-  for (int64_t j0 = jb; j0 < je; j0 += kT) {
-    // (a) row of entry j0 + l%32
-    const int64_t j = j0 + (l & 31);
-    const bool jvalid = j < je;
-    const int64_t jc = jvalid ? j : jb;   // any valid entry for padding lanes
-    const bf16_t* row = jc < nsel ? cbase + (int64_t)(DENSE ? jc : sm.sel[jc]) * kC
-                                  : rbase + (jc - nsel) * (int64_t)kC;
-    row += kDW * wave + 8 * (l >> 5);
-    // (b) B operand of S: 8 k-steps x 8 dims of that row
-    bf16x8 eb[8];
+  // ---- Q^T operand: head 64*hg + 32*hw + l%32, dims 16*ks + 8*half + (0..7)
+  bf16x8 qT[32];
+  {
+    const int64_t qrow = qvalid ? rq : rlast;
+    const bf16_t* qp = q + ((bi * n_q + qrow) * n_h + kHG * hg + kHW * hw + (l & 31)) * (int64_t)kC + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      eb[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + ks * 16));
-    // (c) partial S over this wave's 128 dims
-    f32x16 sacc[2];
-    sacc[0] = (f32x16){};
-    sacc[1] = (f32x16){};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][ks], eb[ks], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][ks], eb[ks], sacc[1], 0, 0, 0);
-    }
-    // (d) keep the slice in LDS for P V (row-major, 8-byte stores)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint4 v = __builtin_bit_cast(uint4, eb[ks]);
-      uint2* dst = reinterpret_cast<uint2*>(Ew + (l & 31) * kERow + (ks * 16 + 8 * (l >> 5)) * 2);
-      dst[0] = make_uint2(v.x, v.y);
-      dst[1] = make_uint2(v.z, v.w);
-    }
-    // (e) partial S to LDS: S[w][head][entry]
-    {
-      float* Sw = sm.S[wave];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int head = mb * 32 + 8 * (rr >> 2) + 4 * (l >> 5) + (rr & 3);
-          Sw[head * kSStr + (l & 31)] = sacc[mb][rr];
-        }
-    }
-    __syncthreads();
-    // (g) online softmax for the 16 heads this wave owns
-    {
-      float s[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = own_r0 + i;
-        float v = sm.S[0][own_h * kSStr + e] + sm.S[1][own_h * kSStr + e];
-        v += sm.S[2][own_h * kSStr + e] + sm.S[3][own_h * kSStr + e];
-        s[i] = (j0 + e < je) ? v * scale : -INFINITY;
-      }
-      float tm = s[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) tm = fmaxf(tm, s[i]);
-      tm = fmaxf(tm, __shfl_xor(tm, 1, 64));
-      tm = fmaxf(tm, __shfl_xor(tm, 2, 64));
-      const float m_new = fmaxf(m_run, tm);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp(m_run - m_new);
-      float rs = 0.f;
-      uint32_t pk[4];
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float p0 = (s[i] == -INFINITY) ? 0.f : fast_exp(s[i] - m_new);
-        const float p1 = (s[i + 1] == -INFINITY) ? 0.f : fast_exp(s[i + 1] - m_new);
-        const uint16_t b0 = f2bf(p0), b1 = f2bf(p1);
-        // the row sum uses the rounded weights that P V multiplies
-        rs += bf2f(b0) + bf2f(b1);
-        pk[i / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
-      }
-      rs += __shfl_xor(rs, 1, 64);
-      rs += __shfl_xor(rs, 2, 64);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      *reinterpret_cast<uint4*>(sm.P + own_h * kPRow + own_r0 * 2) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      if ((l & 3) == 0) sm.alpha[own_h] = alpha;
-    }
-    __syncthreads();
-    // (i) rescale O, then O += P E over this wave's dims
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 a = *reinterpret_cast<const float4*>(&sm.alpha[mb * 32 + 8 * g + 4 * (l >> 5)]);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          o[mb][nb][4 * g + 0] *= a.x;
-          o[mb][nb][4 * g + 1] *= a.y;
-          o[mb][nb][4 * g + 2] *= a.z;
-          o[mb][nb][4 * g + 3] *= a.w;
-        }
-      }
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      bf16x8 pa[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        pa[mb] = *reinterpret_cast<const bf16x8*>(sm.P + (mb * 32 + (l & 31)) * kPRow + (ks2 * 16 + 8 * (l >> 5)) * 2);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        // B[k = entry][n = dim]: 8 consecutive entries of one dimension
-        const unsigned char* src = Ew + (ks2 * 16 + 8 * (l >> 5)) * kERow + (nb * 32 + (l & 31)) * 2;
-        uint16_t e8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e8[i] = *reinterpret_cast<const uint16_t*>(src + i * kERow);
-        const uint4 pkd = make_uint4((uint32_t)e8[0] | ((uint32_t)e8[1] << 16), (uint32_t)e8[2] | ((uint32_t)e8[3] << 16),
-                                     (uint32_t)e8[4] | ((uint32_t)e8[5] << 16), (uint32_t)e8[6] | ((uint32_t)e8[7] << 16));
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, pkd);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          o[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[mb], bv, o[mb][nb], 0, 0, 0);
-      }
-    }
+    for (int ks = 0; ks < 32; ++ks)
+      qT[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
   }
+  // Softmax without rescaling O.  VALU instructions cannot operate on the
+  // accumulation registers, so an online max that rescales O every time it
+  // grows would force O out of them.  Instead each head keeps a fixed
+  // reference m_ref (log2 domain), set from its first valid logits; weights
+  // 2^(s - m_ref) are exact relative values and may exceed 1.  Should a later
+  // logit exceed m_ref by more than kLogHeadroom (weights up to 2^64; the
+  // float32 range stops at 2^128), the workgroup runs this query's entries
+  // again with m_ref raised to the largest logit seen -- a rare, exact
+  // fallback.
+  constexpr float kLogHeadroom = 64.f;
+  f32x16 o[16];
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;   // head l%32
+  const float sl2 = scale * kLog2e;
+  const int srow = l & 31;                // entry row this lane feeds in S^T
+  const int s16 = l & 15;
+  const int colh = 16 * ((l >> 4) & 1);
+  if (tid == 0) sm.gen = 0;
+  __syncthreads();
+  int gen = 0;
+  for (;;) {
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) o[nb] = (f32x16){};
+    l_run = 0.f;
+    if (ntiles > 0) issue_tile(jb, 0);
+    for (int it = 0; it < ntiles; ++it) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (it + 1 < ntiles) issue_tile(jb + (int64_t)(it + 1) * kT, (it + 1) & 1);
+      const unsigned char* Eb = sm.E[it & 1];
+      const int64_t j0 = jb + (int64_t)it * kT;
 
-  // ---- finish: either normalise with the sink, or publish the split's partials
-  if (nsplit == 1) {
-    if ((l & 3) == 0) {
-      const float z = sink[kHG * hg + own_h];
-      const float Mf = fmaxf(m_run, z);
-      const float fac = (m_run == -INFINITY) ? 0.f : fast_exp(m_run - Mf);
-      sm.fin[own_h] = fac / (l_run * fac + fast_exp(z - Mf));
+      // S^T[entry][head] over 512 dims
+      f32x16 st = (f32x16){};
+      {
+        const unsigned char* er = Eb + srow * kRowB;
+        const int f = swz(srow);
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(er + (((2 * ks + half) ^ f) << 4));
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qT[ks], st, 0, 0, 0);
+          if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the operands in flight
+        }
+      }
+      // weights of head l%32 for the tile's entries
+      uint32_t pk[8];
+      {
+        float sv[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t e = j0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          bool valid = e < je;
+          if (DENSE) {
+            if (e < nsel) {
+              valid = valid && e < vis_q;
+            } else {
+              const int64_t p = wlo + (e - nsel);
+              valid = valid && p > t_q - n_win && p <= t_q;
+            }
+          }
+          sv[r] = valid ? st[r] * sl2 : -INFINITY;
+          tmax = fmaxf(tmax, sv[r]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        m_seen = fmaxf(m_seen, tmax);
+        if (m_ref == -INFINITY) m_ref = tmax;            // first valid logits of this head
+        float rs = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = (sv[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m_ref);
+          const float p1 = (sv[r + 1] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[r + 1] - m_ref);
+          const uint16_t b0 = f2bf(p0), b1 = f2bf(p1);
+          rs += bf2f(b0) + bf2f(b1);   // normalise with the weights P V multiplies
+          pk[r >> 1] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+        }
+        rs += __shfl_xor(rs, 32, 64);
+        l_run += rs;
+      }
+      // O[head][dim] += P[head][entry] E[entry][dim]
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2],
+                                                                pk[4 * ks2 + 3]));
+        const int rowA = 16 * ks2 + 4 * half + (s16 >> 2);
+        const int rowB = rowA + 8;
+        const unsigned char* ea = Eb + rowA * kRowB;
+        const unsigned char* eb2 = Eb + rowB * kRowB;
+        const int fa = swz(rowA), fb = swz(rowB);
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+          const int col = 32 * nb + colh + 4 * (s16 & 3);
+          const int chunk = col >> 3, off = (col & 7) * 2;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4_t*)(ea + ((chunk ^ fa) << 4) + off));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4_t*)(eb2 + ((chunk ^ fb) << 4) + off));
+          const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bv, o[nb], 0, 0, 0);
+          if ((nb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
+    // an attempt whose weights may have overflowed is discarded as a whole;
+    // the decision is workgroup-wide because the waves share the tiles
+    if (m_seen > m_ref + kLogHeadroom) sm.gen = gen + 1;
     __syncthreads();
-    bf16_t* ob = out + ((bi * n_q + r) * n_h + kHG * hg) * (int64_t)kC + kDW * wave + (l & 31);
+    if (sm.gen == gen) break;
+    ++gen;
+    m_ref = m_seen;
+  }
+  const float m_run = m_ref;
+
+  const int head0 = kHG * hg + kHW * hw;   // first head of this wave
+  if (nsplit == 1) {
+    // final per-head factor e^{-M} / (sum + e^{z - M}), broadcast over the O rows
+    if (l < 32) {
+      const float z2 = sink[head0 + l] * kLog2e;
+      const float Mf = fmaxf(m_run, z2);
+      const float fac = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - Mf);
+      sm.bc[wave][l] = fac / (l_run * fac + __builtin_amdgcn_exp2f(z2 - Mf));
+    }
+    float4 g4[4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int g = 0; g < 4; ++g) g4[g] = *reinterpret_cast<const float4*>(&sm.bc[wave][8 * g + 4 * half]);
+    __syncthreads();   // every wave is done with the tile buffers
+    unsigned char* stg = &sm.E[0][0] + wave * (kHW * kStageRowB);
+    bf16_t* ob = out + ((bi * n_q + (qvalid ? rq : rlast)) * n_h + head0) * (int64_t)kC;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int head = mb * 32 + 8 * (rr >> 2) + 4 * (l >> 5) + (rr & 3);
-        const float g = sm.fin[head];
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) ob[head * (int64_t)kC + nb * 32] = f2bf(o[mb][nb][rr] * g);
+      for (int nb8 = 0; nb8 < 8; ++nb8) {
+        const int nb = pass * 8 + nb8;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float gv[4] = {g4[g].x, g4[g].y, g4[g].z, g4[g].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int hr = 8 * g + 4 * half + i;
+            // rows 4 apart would share banks: flip the 64-byte half for odd row quads
+            const int byte = ((nb8 * 32 + (l & 31)) * 2) ^ (((hr >> 2) & 1) << 6);
+            *reinterpret_cast<bf16_t*>(stg + hr * kStageRowB + byte) = f2bf(o[nb][4 * g + i] * gv[i]);
+          }
+        }
       }
-  } else {
-    const int64_t slot = ((bi * n_q + r) * (n_h / kHG) + hg) * nsplit + split;
-    float* po = part_o + slot * (int64_t)kHG * kC + kDW * wave + (l & 31);
+      // the staging area is private to this wave: its own writes are ordered
+      // before its reads
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int head = mb * 32 + 8 * (rr >> 2) + 4 * (l >> 5) + (rr & 3);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) po[head * (int64_t)kC + nb * 32] = o[mb][nb][rr];
+      for (int i = 0; i < 16; ++i) {
+        const int cidx = l + 64 * i;            // 16-byte chunk of the 32 x 512 B block
+        const int hr = cidx >> 5, c16 = cidx & 31;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + hr * kStageRowB + ((c16 * 16) ^ (((hr >> 2) & 1) << 6)));
+        if (qvalid)
+          *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(ob + hr * (int64_t)kC + pass * 256) + c16 * 16) = v;
       }
-    if ((l & 3) == 0) {
-      part_ml[(slot * kHG + own_h) * 2 + 0] = m_run;
-      part_ml[(slot * kHG + own_h) * 2 + 1] = l_run;
+    }
+  } else if (qvalid) {
+    const int64_t slot = ((bi * n_q + rq) * (n_h / kHG) + hg) * nsplit + split;
+    float* po = part_o + slot * (int64_t)kHG * kC + (int64_t)kHW * hw * kC + (l & 31);
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int hr = 8 * (r >> 2) + 4 * half + (r & 3);
+        po[hr * (int64_t)kC + nb * 32] = o[nb][r];
+      }
+    if (l < 32) {
+      part_ml[(slot * kHG + kHW * hw + l) * 2 + 0] = m_run;
+      part_ml[(slot * kHG + kHW * hw + l) * 2 + 1] = l_run;
     }
   }
 }
 
-// Merge the splits of one (query, 64-head group) in split order, then apply
-// the sink: out = sum_s O_s e^{m_s - M} / (sum_s l_s e^{m_s - M} + e^{z - M}).
-__global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ part_o,
+// Merge the splits of one (query, head) in split order (log2-domain maxima),
+// then apply the sink: out = sum_s O_s 2^{m_s - M} / (sum_s l_s 2^{m_s - M} + 2^{z - M}).
+__global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const float* __restrict__ sink, int n_h,
                                                       int nsplit, bf16_t* __restrict__ out) {
-  const int64_t qh = blockIdx.x;  // (b*n_q + r) * (n_h/64) + hg
-  const int hgn = n_h / kHG;
-  const int hg = (int)(qh % hgn);
-  const int64_t br = qh / hgn;
-  for (int hh = 0; hh < kHG; ++hh) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((qh * nsplit + s) * kHG + hh) * 2]);
-    const float z = sink[kHG * hg + hh];
-    const float Mf = fmaxf(M, z);
-    float L = 0.f, acc0 = 0.f, acc1 = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = part_ml[((qh * nsplit + s) * kHG + hh) * 2];
-      const float ls = part_ml[((qh * nsplit + s) * kHG + hh) * 2 + 1];
-      const float f = (ms == -INFINITY) ? 0.f : fast_exp(ms - Mf);
-      L = fmaf(ls, f, L);
-      const float* po = part_o + ((qh * nsplit + s) * kHG + hh) * (int64_t)kC;
-      acc0 = fmaf(po[threadIdx.x], f, acc0);
-      acc1 = fmaf(po[threadIdx.x + 256], f, acc1);
-    }
-    const float den = L + fast_exp(z - Mf);
-    bf16_t* ob = out + (br * n_h + kHG * hg + hh) * (int64_t)kC;
-    ob[threadIdx.x] = f2bf(acc0 / den);
-    ob[threadIdx.x + 256] = f2bf(acc1 / den);
+  const int64_t qr = blockIdx.x;   // b * n_q + r
+  const int h = blockIdx.y;
+  const int hg = h / kHG, hh = h % kHG;
+  const int64_t base = (qr * (n_h / kHG) + hg) * nsplit;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((base + s) * kHG + hh) * 2]);
+  const float z2 = sink[h] * kLog2e;
+  const float Mf = fmaxf(M, z2);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = part_ml[((base + s) * kHG + hh) * 2];
+    const float ls = part_ml[((base + s) * kHG + hh) * 2 + 1];
+    const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - Mf);
+    L = fmaf(ls, f, L);
+    const float4 v = reinterpret_cast<const float4*>(part_o + ((base + s) * kHG + hh) * (int64_t)kC)[threadIdx.x];
+    acc.x = fmaf(v.x, f, acc.x);
+    acc.y = fmaf(v.y, f, acc.y);
+    acc.z = fmaf(v.z, f, acc.z);
+    acc.w = fmaf(v.w, f, acc.w);
   }
+  const float inv = 1.f / (L + __builtin_amdgcn_exp2f(z2 - Mf));
+  bf16_t* ob = out + (qr * n_h + h) * (int64_t)kC + 4 * threadIdx.x;
+  const uint2 pk = make_uint2((uint32_t)f2bf(acc.x * inv) | ((uint32_t)f2bf(acc.y * inv) << 16),
+                              (uint32_t)f2bf(acc.z * inv) | ((uint32_t)f2bf(acc.w * inv) << 16));
+  *reinterpret_cast<uint2*>(ob) = pk;
 }
 
 // ---------------------------------------------------------------------------
@@ -444,19 +506,20 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
       part_o = (float*)ws;
       part_ml = (float*)((unsigned char*)ws + osz);
     }
-    dim3 grid((unsigned)n_q, (unsigned)((n_h / kHG) * ns), (unsigned)b);
+    const int G = dense ? 2 : 1;
+    dim3 grid((unsigned)((n_q + G - 1) / G), (unsigned)((n_h / kHG) * ns), (unsigned)b);
     if (dense)
-      hipLaunchKernelGGL((attend_mfma_c512<1>), grid, dim3(256), 0, st, (const bf16_t*)q,
+      hipLaunchKernelGGL((attend_mfma_c512<1, 2>), grid, dim3(256), 0, st, (const bf16_t*)q,
                          (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
                          n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
                          (bf16_t*)out);
     else
-      hipLaunchKernelGGL((attend_mfma_c512<0>), grid, dim3(256), 0, st, (const bf16_t*)q,
+      hipLaunchKernelGGL((attend_mfma_c512<0, 1>), grid, dim3(128), 0, st, (const bf16_t*)q,
                          (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
                          n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
                          (bf16_t*)out);
     if (ns > 1)
-      hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q * (n_h / kHG))), dim3(256), 0, st,
+      hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q), (unsigned)n_h), dim3(128), 0, st,
                          part_o, part_ml, sink, (int)n_h, ns, (bf16_t*)out);
     return hipGetLastError();
   }
