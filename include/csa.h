@@ -138,7 +138,8 @@ size_t csa_index_topk_workspace_size(int64_t b, int64_t n_q, int64_t n_comp, int
  *          aligned (may be NULL when that size is 0)
  *
  * Errors: CSA_EINVAL for sizes < 1 (n_comp and k may be 0), NULL required
- * pointers, a non-finite scale, or a window that kv_raw does not cover:
+ * pointers, a scale that is not a finite positive number, or a window
+ * that kv_raw does not cover:
  * rows max(0, t0-n_win+1) .. t0+n_q-1 must lie in [raw_pos0, raw_pos0 +
  * n_raw).  CSA_ENOSPC if ws_bytes is too small.  CSA_ENOTSUP for c > 1024
  * outside the bf16 64-head c = 512 kernel.

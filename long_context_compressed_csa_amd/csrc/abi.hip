@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/csa.h"
+#include "csa.h"
 #include "kernels.hpp"
 
 namespace {
@@ -37,7 +37,7 @@ int check_attend(const void* q, const void* Ccomp, int64_t cbs, const void* kv_r
   if (!q || !kv_raw || !sink || !out) return CSA_EINVAL;
   if (n_comp > 0 && !Ccomp) return CSA_EINVAL;
   if (b < 1 || n_q < 1 || n_h < 1 || c < 1 || m < 1 || n_win < 1 || n_raw < 1) return CSA_EINVAL;
-  if (t0 < 0 || n_comp < 0 || !isfinite(scale)) return CSA_EINVAL;
+  if (t0 < 0 || n_comp < 0 || !isfinite(scale) || !(scale > 0.f)) return CSA_EINVAL;
   if (cbs < 0 || rbs < 0) return CSA_EINVAL;
   if (cbs > 0 && cbs < n_comp * c) return CSA_EINVAL;
   if (rbs > 0 && rbs < n_raw * c) return CSA_EINVAL;
@@ -175,7 +175,7 @@ int hca_layer(const void* C, const void* Z, const void* B, const void* q, const 
               void* out, void* stream) {
   if (!dtype_ok(dtype)) return CSA_ENOTSUP;
   if (!C || !Z || !B || !q || !kv_raw || !sink || !Ccomp || !out) return CSA_EINVAL;
-  if (b < 1 || n < 1 || c < 1 || m_prime < 1 || n_h < 1 || n_win < 1 || !isfinite(scale))
+  if (b < 1 || n < 1 || c < 1 || m_prime < 1 || n_h < 1 || n_win < 1 || !isfinite(scale) || !(scale > 0.f))
     return CSA_EINVAL;
   const int64_t ne = n / m_prime;
   // validate the attention step before enqueuing the compressor

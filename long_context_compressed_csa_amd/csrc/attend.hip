@@ -125,28 +125,42 @@ __global__ __launch_bounds__(256) void attend_generic(
 //                    contraction index is permuted to match their row
 //                    layout), B = E^T read with ds_read_b64_tr_b16, which
 //                    returns a 4-row x 16-column block column-per-lane.
-// LDS rows are 1 KiB with the 16-byte chunks of row r XOR-swizzled by
-// f(r) = 2(r%4) + (r/4)%2, which keeps both the b128 row reads (8 rows, one
-// chunk) and the transposed reads (4 rows, two chunks) free of bank
-// conflicts.
+// LDS rows are 1024 + 64 bytes apart and the four 16-byte chunks of every
+// 64-byte column block of row r are XOR-permuted by (r/4)%4.  With gfx950's
+// 64 LDS banks this keeps both access patterns conflict-free: the b128 row
+// reads (16 lanes = 16 consecutive rows, one chunk each) and the transposed
+// reads (32 lanes = 4 consecutive rows x one 64-byte block each), and the
+// offset of column block nb stays a constant 64*nb, so each lane needs only
+// two base addresses per phase.
 // ---------------------------------------------------------------------------
 constexpr int kC = 512;
 constexpr int kHG = 64;              // heads per head group
 constexpr int kHW = 32;              // heads per wave
 constexpr int kT = 32;               // entries per tile
-constexpr int kRowB = kC * 2;        // LDS bytes per entry row
-constexpr int kTileB = kT * kRowB;   // 32 KiB
+constexpr int kRowB = kC * 2 + 64;   // LDS bytes per entry row (64-byte skew)
+constexpr int kTileB = kT * kRowB;   // 34 KiB
 constexpr int kMaxSel = 2048;        // selected entries staged in LDS
 constexpr int kStageRowB = 256 * 2;  // output staging row (256 dims), XOR-swizzled
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// max / sum of a value and its copy in the other 32-lane half
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 template <int DENSE, int G>
 struct AttnSmem {
-  unsigned char E[2][kTileB];       // 64 KiB, reused for output staging
   int32_t sel[DENSE ? 1 : kMaxSel];
   float bc[2 * G][kHW];             // per-wave broadcast of per-head factors
   int32_t cnt[2 * G];
@@ -162,6 +176,9 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
     float* __restrict__ part_o, float* __restrict__ part_ml, bf16_t* __restrict__ out) {
   constexpr int NW = 2 * G;  // waves per workgroup
   __shared__ AttnSmem<DENSE, G> sm;
+  // the two tile buffers (double buffering: gather one while computing the other)
+  __shared__ __attribute__((aligned(16))) unsigned char E0[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char E1[kTileB];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int half = l >> 5;
   const int qw = wave >> 1;          // query slot in the group
@@ -214,6 +231,14 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   const int64_t jb = (int64_t)split * per;
   const int64_t je = jb + per < N ? jb + per : N;
   const int ntiles = je > jb ? (int)((je - jb + kT - 1) / kT) : 0;
+  // entries of the group list this wave's query may not read (-1: none)
+  int64_t exA_abs = -1, exW_abs = -1;
+  if (DENSE) {
+    if (vis_q < nsel) exA_abs = vis_q;                       // at most one: vis differs by <= 1
+    const int64_t wq_lo = t_q - n_win + 1;                   // this query's window starts here
+    if (wlo < wq_lo) exW_abs = nsel;                         // union starts one row earlier
+    if (t_q < t_last) exW_abs = nsel + (t_last - wlo);       // union ends one row later
+  }
 
   const bf16_t* cbase = Ccomp + bi * cbs;
   const bf16_t* rbase = kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
@@ -222,7 +247,7 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   // to scalar registers, lane l fetching chunk l ^ f(row) so that LDS chunk
   // position c holds row chunk c ^ f(row).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_tile = [&](int64_t jt, int buf) {
+  auto issue_tile = [&](int64_t jt, unsigned char* buf) {
     int64_t j = jt + (l & 31);
     if (j >= je) j = jb;  // tail padding rows: any real row (its weight is 0)
     const bf16_t* p = j < nsel ? cbase + (int64_t)(DENSE ? j : sm.sel[j]) * kC
@@ -236,7 +261,7 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
       const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(phi, row) << 32) |
                             (uint64_t)(uint32_t)__builtin_amdgcn_readlane(plo, row);
       const unsigned char* src = reinterpret_cast<const unsigned char*>(base) + ((l ^ swz(row)) << 4);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(&sm.E[buf][row * kRowB]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(buf + row * kRowB), 16, 0, 0);
     }
   };
 
@@ -262,9 +287,19 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   f32x16 o[16];
   float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;   // head l%32
   const float sl2 = scale * kLog2e;
-  const int srow = l & 31;                // entry row this lane feeds in S^T
+  // per-lane LDS byte offsets inside a tile buffer
+  //   S^T A operand: row l%32, chunk 2ks + half -> 16*((2(ks%2) + half) ^ g) + 64*(ks/2)
+  const int srow = l & 31;
+  const int sb0 = srow * kRowB + 16 * (half ^ swz(srow));
+  const int sb1 = srow * kRowB + 16 * ((half ^ swz(srow)) ^ 2);
+  //   P V B operand (transposed read): rows 16ks2 + 8q + 4half + (l%16)/4,
+  //   column block nb, chunk 2*((l/16)%2) + (l%4)/2 of the block, byte 8*(l%2)
   const int s16 = l & 15;
-  const int colh = 16 * ((l >> 4) & 1);
+  const int cpart = 2 * ((l >> 4) & 1) + ((s16 & 3) >> 1);
+  const int boff = 8 * (s16 & 1);
+  auto trbase = [&](int row) { return row * kRowB + 16 * (cpart ^ swz(row)) + boff; };
+  const int tbA0 = trbase(4 * half + (s16 >> 2)), tbB0 = trbase(8 + 4 * half + (s16 >> 2));
+  const int tbA1 = trbase(16 + 4 * half + (s16 >> 2)), tbB1 = trbase(24 + 4 * half + (s16 >> 2));
   if (tid == 0) sm.gen = 0;
   __syncthreads();
   int gen = 0;
@@ -272,84 +307,111 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb) o[nb] = (f32x16){};
     l_run = 0.f;
-    if (ntiles > 0) issue_tile(jb, 0);
-    for (int it = 0; it < ntiles; ++it) {
+    // one tile: wait for its gather, start the next gather into the other
+    // buffer, then S^T, weights and P V from this buffer
+    auto tile = [&](const int it, unsigned char* const Eb, unsigned char* const En) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (it + 1 < ntiles) issue_tile(jb + (int64_t)(it + 1) * kT, (it + 1) & 1);
-      const unsigned char* Eb = sm.E[it & 1];
+      if (it + 1 < ntiles) issue_tile(jb + (int64_t)(it + 1) * kT, En);
       const int64_t j0 = jb + (int64_t)it * kT;
 
-      // S^T[entry][head] over 512 dims
-      f32x16 st = (f32x16){};
+      // S^T[entry][head] over 512 dims: two independent accumulation chains,
+      // LDS operands fetched two steps ahead of the MFMAs that use them
+      f32x16 st0 = (f32x16){}, st1 = (f32x16){};
       {
-        const unsigned char* er = Eb + srow * kRowB;
-        const int f = swz(srow);
+        const unsigned char* e0 = Eb + sb0;
+        const unsigned char* e1 = Eb + sb1;
+        bf16x8 a[3][2];
+        a[0][0] = *reinterpret_cast<const bf16x8*>(e0);
+        a[0][1] = *reinterpret_cast<const bf16x8*>(e1);
+        a[1][0] = *reinterpret_cast<const bf16x8*>(e0 + 64);
+        a[1][1] = *reinterpret_cast<const bf16x8*>(e1 + 64);
 #pragma unroll
-        for (int ks = 0; ks < 32; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(er + (((2 * ks + half) ^ f) << 4));
-          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qT[ks], st, 0, 0, 0);
-          if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the operands in flight
+        for (int u = 0; u < 16; ++u) {
+          if (u + 2 < 16) {
+            a[(u + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(e0 + 64 * (u + 2));
+            a[(u + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(e1 + 64 * (u + 2));
+          }
+          st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % 3][0], qT[2 * u], st0, 0, 0, 0);
+          st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % 3][1], qT[2 * u + 1], st1, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // weights of head l%32 for the tile's entries
+      // first P V operands, independent of the weights: fetch them now
+      bf16x4 tr[3][2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        tr[q2][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Eb + tbA0 + 64 * q2));
+        tr[q2][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Eb + tbB0 + 64 * q2));
+      }
+      // weights of head l%32 for the tile's entries (entry = j0 + local)
       uint32_t pk[8];
       {
+        const int rem = (int)(je - j0 < kT ? je - j0 : kT);   // real entries in this tile
+        // the group's entry list is the union over its G consecutive queries:
+        // this query excludes at most one compressed entry (completed only at
+        // the group's last position) and one window row (outside its window)
+        int exA = -1, exW = -1;
+        if (DENSE) {
+          const int64_t cap = 1 << 20;
+          auto rel = [&](int64_t e) { const int64_t x = e - j0; return (int)(x < -1 || x > cap ? -1 : x); };
+          exA = rel(exA_abs);
+          exW = rel(exW_abs);
+        }
         float sv[16];
         float tmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t e = j0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool valid = e < je;
-          if (DENSE) {
-            if (e < nsel) {
-              valid = valid && e < vis_q;
-            } else {
-              const int64_t p = wlo + (e - nsel);
-              valid = valid && p > t_q - n_win && p <= t_q;
-            }
-          }
-          sv[r] = valid ? st[r] * sl2 : -INFINITY;
+          const int loc = 8 * (r >> 2) + 4 * half + (r & 3);
+          bool valid = loc < rem;
+          if (DENSE) valid = valid & (loc != exA) & (loc != exW);
+          sv[r] = valid ? (st0[r] + st1[r]) * sl2 : -INFINITY;
           tmax = fmaxf(tmax, sv[r]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = half_max(tmax);
         m_seen = fmaxf(m_seen, tmax);
         if (m_ref == -INFINITY) m_ref = tmax;            // first valid logits of this head
+        const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
+        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
         float rs = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = (sv[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m_ref);
-          const float p1 = (sv[r + 1] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[r + 1] - m_ref);
-          const uint16_t b0 = f2bf(p0), b1 = f2bf(p1);
-          rs += bf2f(b0) + bf2f(b1);   // normalise with the weights P V multiplies
-          pk[r >> 1] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+          const float p0 = __builtin_amdgcn_exp2f(sv[r] - mb);
+          const float p1 = __builtin_amdgcn_exp2f(sv[r + 1] - mb);
+          const bf16x2_t b = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);   // round to nearest even
+          rs = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs, false);   // sum of the weights P V multiplies
+          pk[r >> 1] = __builtin_bit_cast(uint32_t, b);
         }
-        rs += __shfl_xor(rs, 32, 64);
-        l_run += rs;
+        l_run += half_sum(rs);
       }
-      // O[head][dim] += P[head][entry] E[entry][dim]
+      // O[head][dim] += P[head][entry] E[entry][dim]; step i = (ks2, nb) = (i/16, i%16),
+      // its transposed operands fetched two steps ahead
+      {
+        bf16x8 pa[2];
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2],
-                                                                pk[4 * ks2 + 3]));
-        const int rowA = 16 * ks2 + 4 * half + (s16 >> 2);
-        const int rowB = rowA + 8;
-        const unsigned char* ea = Eb + rowA * kRowB;
-        const unsigned char* eb2 = Eb + rowB * kRowB;
-        const int fa = swz(rowA), fb = swz(rowB);
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+          pa[ks2] = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2],
+                                                          pk[4 * ks2 + 3]));
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb) {
-          const int col = 32 * nb + colh + 4 * (s16 & 3);
-          const int chunk = col >> 3, off = (col & 7) * 2;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4_t*)(ea + ((chunk ^ fa) << 4) + off));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4_t*)(eb2 + ((chunk ^ fb) << 4) + off));
-          const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bv, o[nb], 0, 0, 0);
-          if ((nb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 32; ++i) {
+          if (i + 2 < 32) {
+            const int i2 = i + 2, k2 = i2 >> 4, n2 = i2 & 15;
+            tr[i2 % 3][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4_t*)(Eb + (k2 ? tbA1 : tbA0) + 64 * n2));
+            tr[i2 % 3][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4_t*)(Eb + (k2 ? tbB1 : tbB0) + 64 * n2));
+          }
+          const bf16x8 bv = __builtin_shufflevector(tr[i % 3][0], tr[i % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i >> 4], bv, o[i & 15], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+    };
+    if (ntiles > 0) issue_tile(jb, E0);
+    for (int it = 0; it < ntiles; ++it) {
+      unsigned char* const Eb = (it & 1) ? E1 : E0;
+      unsigned char* const En = (it & 1) ? E0 : E1;
+      tile(it, Eb, En);
     }
     // an attempt whose weights may have overflowed is discarded as a whole;
     // the decision is workgroup-wide because the waves share the tiles
@@ -374,7 +436,7 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
 #pragma unroll
     for (int g = 0; g < 4; ++g) g4[g] = *reinterpret_cast<const float4*>(&sm.bc[wave][8 * g + 4 * half]);
     __syncthreads();   // every wave is done with the tile buffers
-    unsigned char* stg = &sm.E[0][0] + wave * (kHW * kStageRowB);
+    unsigned char* stg = ((wave < 2) ? E0 : E1) + (wave & 1) * (kHW * kStageRowB);
     bf16_t* ob = out + ((bi * n_q + (qvalid ? rq : rlast)) * n_h + head0) * (int64_t)kC;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {

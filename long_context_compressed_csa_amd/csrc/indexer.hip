@@ -169,144 +169,241 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
 }
 
 // ---------------------------------------------------------------------------
-// Top-k selection over one list segment with 256 threads x R keys.
-// Element e of the segment sits in thread e % 256, slot e / 256, so slot
-// order then thread order is list order.
+// Top-k selection.  A segment (one query's candidate list, or one chunk of
+// it) is held in registers by NT threads (one wave or a 256-thread
+// workgroup), R keys each; element e of the segment sits in thread e % NT,
+// slot e / NT, so slot-major order is list order.  Keys are order-preserving
+// 32-bit images of the float scores.
 //
-// mode 0: keys come from scores[row][base + e], idx = base + e
-// mode 1: keys/idx come from (kin, iin) pairs
-// final:  write idx (int32, ascending list order, -1 padded to k) and the
-//         scores; otherwise write the selected pairs compactly to
-//         (kout, iout) at slot offset chunk * k.
+// The k-th largest key T is found bit by bit from the top, starting below the
+// common prefix of the segment's smallest and largest key; each step counts
+// the keys >= a candidate with wave ballots and scalar popcounts (plus one LDS
+// exchange per step in the workgroup form).  Keys > T are taken, then keys
+// == T in list order until k are taken (ties go to the lower index), and the
+// taken elements are compacted in list order.
 // ---------------------------------------------------------------------------
-template <int R>
-__global__ __launch_bounds__(256) void topk_select_kernel(
-    int mode, int final_stage, const float* __restrict__ scores, int64_t ld_scores,
-    const uint32_t* __restrict__ kin, const int32_t* __restrict__ iin, int64_t ld_in,
-    uint32_t* __restrict__ kout, int32_t* __restrict__ iout, int64_t ld_out, int32_t* __restrict__ idx,
-    float* __restrict__ score_out, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t k,
-    const int64_t* __restrict__ len_override) {
-  constexpr int CHUNK = 256 * R;
-  __shared__ uint32_t red[2][4];
-  __shared__ uint32_t cnt_eq[R][4];
-  __shared__ uint32_t cnt_sel[R][4];
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  const int64_t row = blockIdx.y + (int64_t)blockIdx.z * n_q;  // (b, query)
-  const int64_t chunk = blockIdx.x;
-  // length of this query's full list
-  int64_t L;
-  if (mode == 0) {
-    L = (t0 + blockIdx.y + 1) / m;
-    if (L > n_comp) L = n_comp;
-  } else {
-    L = len_override[row];
-  }
-  const int64_t base = chunk * CHUNK;
-  if (base >= L && !(final_stage && chunk == 0)) return;
-  int64_t len = L - base;
-  if (len > CHUNK) len = CHUNK;
-  if (len < 0) len = 0;
-
-  uint32_t key[R];
-  int32_t ix[R];
-  bool val[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t e = (int64_t)r * 256 + tid;
-    val[r] = e < len;
-    if (mode == 0) {
-      key[r] = val[r] ? f2key(scores[row * ld_scores + base + e]) : 0u;
-      ix[r] = (int32_t)(base + e);
+template <int NT>
+struct SegReduce {
+  // sum of a wave-uniform count over the NT/64 waves (LDS exchange when NT > 64)
+  static __device__ __forceinline__ uint32_t sum(uint32_t c, uint32_t* red, int wave, int& parity) {
+    if constexpr (NT == 64) {
+      return c;
     } else {
-      key[r] = val[r] ? kin[row * ld_in + base + e] : 0u;
-      ix[r] = val[r] ? iin[row * ld_in + base + e] : -1;
+      uint32_t* slot = red + parity * (NT / 64);
+      parity ^= 1;
+      if ((threadIdx.x & 63) == 0) slot[wave] = c;
+      __syncthreads();
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) t += slot[w];
+      return t;
     }
   }
+  static __device__ __forceinline__ uint32_t umax(uint32_t v, uint32_t* red, int wave, int& parity) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    if constexpr (NT == 64) {
+      return v;
+    } else {
+      uint32_t* slot = red + parity * (NT / 64);
+      parity ^= 1;
+      if ((threadIdx.x & 63) == 0) slot[wave] = v;
+      __syncthreads();
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) t = max(t, slot[w]);
+      return t;
+    }
+  }
+};
 
-  const int64_t take = len < k ? len : k;
-  bool sel[R];
+// Select the top k of the segment held in key[] (valid where e < len);
+// writes the selection flags into sel[].  `red` is LDS scratch of
+// 2 * NT/64 words (unused for NT == 64); `pre` is LDS scratch of R * NT/64
+// words used for list-order ranks.
+template <int NT, int R>
+__device__ __forceinline__ void segment_select(const uint32_t (&key)[R], int len, int k, bool (&sel)[R],
+                                               uint32_t* red, uint32_t* pre) {
+  const int tid = threadIdx.x % NT, wave = tid >> 6, l = tid & 63;
+  int parity = 0;
+  bool val[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) val[r] = r * NT + tid < len;
   if (len <= k) {
 #pragma unroll
     for (int r = 0; r < R; ++r) sel[r] = val[r];
+    return;
+  }
+  // common prefix of the largest and smallest key bounds the search
+  uint32_t hi = 0, lo = 0xffffffffu;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (val[r]) { hi = max(hi, key[r]); lo = min(lo, key[r]); }
+  hi = SegReduce<NT>::umax(hi, red, wave, parity);
+  lo = ~SegReduce<NT>::umax(~lo, red, wave, parity);
+  const uint32_t diff = hi ^ lo;
+  uint32_t T = 0;
+  if (diff == 0) {
+    T = hi;
   } else {
-    // largest T with #{key >= T} >= k, one bit at a time from the top
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
+    const int top = 31 - __clz(diff);
+    T = top == 31 ? 0u : (hi >> (top + 1)) << (top + 1);
+    for (int bit = top; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       uint32_t c = 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) c += (val[r] && key[r] >= cand) ? 1u : 0u;
-      c = wave_sum_u32(c);
-      const int slot = bit & 1;
-      if (l == 0) red[slot][wave] = c;
-      __syncthreads();
-      const uint32_t tot = red[slot][0] + red[slot][1] + red[slot][2] + red[slot][3];
-      if (tot >= (uint32_t)k) T = cand;
-    }
-    uint32_t gt = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) gt += (val[r] && key[r] > T) ? 1u : 0u;
-    gt = wave_sum_u32(gt);
-    if (l == 0) red[0][wave] = gt;
-    // exclusive rank of each tie (key == T) in list order
-    uint64_t meq[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      meq[r] = __ballot(val[r] && key[r] == T);
-      if (l == 0) cnt_eq[r][wave] = (uint32_t)__popcll(meq[r]);
-    }
-    __syncthreads();
-    const uint32_t gt_tot = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    const uint32_t need_eq = (uint32_t)k - gt_tot;
-    uint32_t run = 0;
-    const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      uint32_t before = run;
-      for (int w2 = 0; w2 < wave; ++w2) before += cnt_eq[r][w2];
-      before += (uint32_t)__popcll(meq[r] & below);
-      const bool eq = val[r] && key[r] == T;
-      sel[r] = (val[r] && key[r] > T) || (eq && before < need_eq);
-      run += cnt_eq[r][0] + cnt_eq[r][1] + cnt_eq[r][2] + cnt_eq[r][3];
+      for (int r = 0; r < R; ++r) c += (uint32_t)__popcll(__ballot(val[r] && key[r] >= cand));
+      c = SegReduce<NT>::sum(c, red, wave, parity);
+      if (c >= (uint32_t)k) T = cand;
     }
   }
-  // ordered compaction of the selected elements
-  uint64_t msel[R];
+  uint32_t gt = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) gt += (uint32_t)__popcll(__ballot(val[r] && key[r] > T));
+  gt = SegReduce<NT>::sum(gt, red, wave, parity);
+  const uint32_t need_eq = (uint32_t)k - gt;
+  // rank of each tie in list order: wave-local ballot prefix, plus earlier
+  // waves (per slot) and earlier slots
+  const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  uint64_t meq[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    msel[r] = __ballot(sel[r]);
-    if (l == 0) cnt_sel[r][wave] = (uint32_t)__popcll(msel[r]);
+    meq[r] = __ballot(val[r] && key[r] == T);
+    if (NT > 64 && l == 0) pre[r * (NT / 64) + wave] = (uint32_t)__popcll(meq[r]);
   }
-  __syncthreads();
-  {
-    uint32_t run = 0;
-    const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  if (NT > 64) __syncthreads();
+  uint32_t run = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      uint32_t pos = run;
-      for (int w2 = 0; w2 < wave; ++w2) pos += cnt_sel[r][w2];
-      pos += (uint32_t)__popcll(msel[r] & below);
-      if (sel[r]) {
-        if (final_stage) {
-          idx[row * k + pos] = ix[r];
-          if (score_out) score_out[row * k + pos] = key2f(key[r]);
-        } else {
-          kout[row * ld_out + chunk * k + pos] = key[r];
-          iout[row * ld_out + chunk * k + pos] = ix[r];
-        }
+  for (int r = 0; r < R; ++r) {
+    uint32_t before = run + (uint32_t)__popcll(meq[r] & below);
+    uint32_t slot_total = (uint32_t)__popcll(meq[r]);
+    if constexpr (NT > 64) {
+      slot_total = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < NT / 64; ++w2) {
+        const uint32_t cw = pre[r * (NT / 64) + w2];
+        if (w2 < wave) before += cw;
+        slot_total += cw;
       }
-      run += cnt_sel[r][0] + cnt_sel[r][1] + cnt_sel[r][2] + cnt_sel[r][3];
     }
+    const bool eq = val[r] && key[r] == T;
+    sel[r] = (val[r] && key[r] > T) || (eq && before < need_eq);
+    run += slot_total;
   }
-  if (final_stage) {
-    for (int64_t p = take + tid; p < k; p += 256) {
-      idx[row * k + p] = -1;
-      if (score_out) score_out[row * k + p] = 0.f;
+  if (NT > 64) __syncthreads();   // pre[] is reused by the caller's compaction
+}
+
+// Compact the selected elements in list order: returns each element's output
+// position (valid where sel) through pos[].
+template <int NT, int R>
+__device__ __forceinline__ void segment_positions(const bool (&sel)[R], uint32_t (&pos)[R], uint32_t* pre) {
+  const int tid = threadIdx.x % NT, wave = tid >> 6, l = tid & 63;
+  const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  uint64_t ms[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    ms[r] = __ballot(sel[r]);
+    if (NT > 64 && l == 0) pre[r * (NT / 64) + wave] = (uint32_t)__popcll(ms[r]);
+  }
+  if (NT > 64) __syncthreads();
+  uint32_t run = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    uint32_t p = run + (uint32_t)__popcll(ms[r] & below);
+    uint32_t slot_total = (uint32_t)__popcll(ms[r]);
+    if constexpr (NT > 64) {
+      slot_total = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < NT / 64; ++w2) {
+        const uint32_t cw = pre[r * (NT / 64) + w2];
+        if (w2 < wave) p += cw;
+        slot_total += cw;
+      }
     }
+    pos[r] = p;
+    run += slot_total;
   }
 }
 
-// Next-stage list length per query: (nchunks - 1) * k + min(k, last chunk).
+// One segment per wave (NT = 64, four segments per workgroup) or per
+// workgroup (NT = 256).  Segment s of row `row` covers list elements
+// [s*CH, s*CH + CH) with CH = NT*R.
+//   from_scores: keys come from scores[row][e] (idx = e); otherwise from the
+//                previous stage's (key, idx) pairs.
+//   final_stage: write idx (ascending, -1 padded) and scores; otherwise write
+//                min(k, len) pairs at slot s*k of the next list.
+template <int NT, int R>
+__global__ __launch_bounds__(256) void topk_stage(
+    int from_scores, int final_stage, const float* __restrict__ scores, int64_t ld_scores,
+    const uint32_t* __restrict__ kin, const int32_t* __restrict__ iin, int64_t ld_in,
+    uint32_t* __restrict__ kout, int32_t* __restrict__ iout, int64_t ld_out, int32_t* __restrict__ idx,
+    float* __restrict__ score_out, int64_t n_rows, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
+    int64_t k, const int64_t* __restrict__ len_in, int64_t nseg) {
+  constexpr int CH = NT * R;
+  constexpr int SEGS = 256 / NT;   // segments per workgroup
+  __shared__ uint32_t red_all[SEGS][2 * (NT / 64) + 1];
+  __shared__ uint32_t pre_all[SEGS][R * (NT / 64) + 1];
+  const int sub = threadIdx.x / NT;
+  const int tid = threadIdx.x % NT;
+  const int64_t gseg = (int64_t)blockIdx.x * SEGS + sub;   // global segment id over (row, seg)
+  const bool active = gseg < n_rows * nseg;
+  const int64_t row = active ? gseg / nseg : 0;
+  const int64_t seg = active ? gseg % nseg : 0;
+  int64_t L;
+  if (from_scores) {
+    L = (t0 + row % n_q + 1) / m;
+    if (L > n_comp) L = n_comp;
+  } else {
+    L = len_in[row];
+  }
+  const int64_t base = seg * CH;
+  int64_t len64 = L - base;
+  if (len64 > CH) len64 = CH;
+  if (len64 < 0 || !active) len64 = 0;
+  const int len = (int)len64;
+  // a wave with nothing to do still runs the uniform code when NT == 256
+  uint32_t key[R];
+  int32_t ix[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = r * NT + tid;
+    const bool v = e < len;
+    if (from_scores) {
+      key[r] = v ? f2key(scores[row * ld_scores + base + e]) : 0u;
+      ix[r] = (int32_t)(base + e);
+    } else {
+      key[r] = v ? kin[row * ld_in + base + e] : 0u;
+      ix[r] = v ? iin[row * ld_in + base + e] : -1;
+    }
+  }
+  bool sel[R];
+  segment_select<NT, R>(key, len, (int)k, sel, red_all[sub], pre_all[sub]);
+  uint32_t pos[R];
+  segment_positions<NT, R>(sel, pos, pre_all[sub]);
+  if (!active) return;
+  if (final_stage) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (sel[r]) {
+        idx[row * k + pos[r]] = ix[r];
+        if (score_out) score_out[row * k + pos[r]] = key2f(key[r]);
+      }
+    const int64_t take = len64 < k ? len64 : k;
+    for (int64_t p = take + tid; p < k; p += NT) {
+      idx[row * k + p] = -1;
+      if (score_out) score_out[row * k + p] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (sel[r]) {
+        kout[row * ld_out + seg * k + pos[r]] = key[r];
+        iout[row * ld_out + seg * k + pos[r]] = ix[r];
+      }
+  }
+}
+
+// Next-stage list length per row: (nseg - 1) * k + min(k, last segment).
 __global__ void topk_next_len(int64_t n_rows, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
                               int64_t k, int64_t chunk, const int64_t* __restrict__ len_in,
                               int64_t* __restrict__ len_out) {
@@ -328,8 +425,10 @@ __global__ void topk_next_len(int64_t n_rows, int64_t n_q, int64_t t0, int64_t n
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-constexpr int kTopkR = 16;
-constexpr int64_t kTopkChunk = 256 * kTopkR;
+constexpr int kWaveR = 32;                        // wave segment: 64 x 32 = 2048 keys
+constexpr int64_t kWaveChunk = 64 * kWaveR;
+constexpr int kBlockR = 32;                       // workgroup segment: 256 x 32 = 8192 keys
+constexpr int64_t kBlockChunk = 256 * kBlockR;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -342,7 +441,7 @@ struct TopkLayout {
 static TopkLayout topk_layout(int64_t b, int64_t n_q, int64_t n_comp, int64_t k) {
   TopkLayout L{};
   const int64_t rows = b * n_q;
-  const int64_t nch = (n_comp + kTopkChunk - 1) / kTopkChunk;
+  const int64_t nch = (n_comp + kWaveChunk - 1) / kWaveChunk;
   L.cap = nch > 1 ? nch * k : 0;
   size_t off = 0;
   L.scores = off; off = align256(off + (size_t)rows * n_comp * 4);
@@ -361,8 +460,8 @@ size_t index_topk_workspace_bytes(int64_t b, int64_t n_q, int64_t n_comp, int64_
 }
 
 bool index_topk_supported(int64_t n_comp, int64_t k) {
-  // multi-stage selection needs each stage to shrink the list
-  return n_comp <= kTopkChunk || k <= kTopkChunk / 2;
+  // multi-stage selection needs each stage to shrink the list at least 2x
+  return n_comp <= kWaveChunk || k <= kWaveChunk / 2;
 }
 
 template <int NHB, int KS>
@@ -420,14 +519,16 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
     }
     if (err != hipSuccess) return err;
   }
-  // selection: stage 1 reads scores; further stages shrink the candidate list
+  // selection: one wave per row when every list fits one segment; otherwise
+  // wave segments first, then workgroup segments until one segment is left
   const int64_t rows = b * n_q;
-  int64_t nch = std::max<int64_t>(1, (n_comp + kTopkChunk - 1) / kTopkChunk);
-  if (nch == 1) {
-    dim3 grid(1, (unsigned)n_q, (unsigned)b);
-    hipLaunchKernelGGL((topk_select_kernel<kTopkR>), grid, dim3(256), 0, st, 0, 1, scores, n_comp,
-                       nullptr, nullptr, 0, nullptr, nullptr, 0, idx, score, n_q, t0, n_comp, m, k,
-                       nullptr);
+  int64_t lmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
+  int64_t nseg = std::max<int64_t>(1, (lmax + kWaveChunk - 1) / kWaveChunk);
+  if (nseg == 1) {
+    const int64_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL((topk_stage<64, kWaveR>), dim3((unsigned)blocks), dim3(256), 0, st, 1, 1, scores,
+                       n_comp, nullptr, nullptr, 0, nullptr, nullptr, 0, idx, score, rows, n_q, t0, n_comp,
+                       m, k, nullptr, (int64_t)1);
     return hipGetLastError();
   }
   uint32_t* kbuf[2] = {(uint32_t*)(W + L.kA), (uint32_t*)(W + L.kB)};
@@ -435,27 +536,25 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
   int64_t* lbuf[2] = {(int64_t*)(W + L.lenA), (int64_t*)(W + L.lenB)};
   const unsigned lgrid = (unsigned)((rows + 255) / 256);
   {
-    dim3 grid((unsigned)nch, (unsigned)n_q, (unsigned)b);
-    hipLaunchKernelGGL((topk_select_kernel<kTopkR>), grid, dim3(256), 0, st, 0, 0, scores, n_comp,
-                       nullptr, nullptr, 0, kbuf[0], ibuf[0], L.cap, nullptr, nullptr, n_q, t0,
-                       n_comp, m, k, nullptr);
+    const int64_t blocks = (rows * nseg + 3) / 4;
+    hipLaunchKernelGGL((topk_stage<64, kWaveR>), dim3((unsigned)blocks), dim3(256), 0, st, 1, 0, scores,
+                       n_comp, nullptr, nullptr, 0, kbuf[0], ibuf[0], L.cap, nullptr, nullptr, rows, n_q, t0,
+                       n_comp, m, k, nullptr, nseg);
     hipLaunchKernelGGL(topk_next_len, dim3(lgrid), dim3(256), 0, st, rows, n_q, t0, n_comp, m, k,
-                       kTopkChunk, nullptr, lbuf[0]);
+                       kWaveChunk, nullptr, lbuf[0]);
   }
-  // an upper bound of every list length after stage 1
-  int64_t lmax = (nch - 1) * k + std::min<int64_t>(k, kTopkChunk);
+  lmax = (nseg - 1) * k + std::min<int64_t>(k, kWaveChunk);   // bound on every next list
   int cur = 0;
   while (true) {
-    const int64_t nch2 = std::max<int64_t>(1, (lmax + kTopkChunk - 1) / kTopkChunk);
-    const int fin = nch2 == 1 ? 1 : 0;
-    dim3 grid((unsigned)nch2, (unsigned)n_q, (unsigned)b);
-    hipLaunchKernelGGL((topk_select_kernel<kTopkR>), grid, dim3(256), 0, st, 1, fin, nullptr,
-                       0, kbuf[cur], ibuf[cur], L.cap, kbuf[cur ^ 1], ibuf[cur ^ 1], L.cap, idx, score,
-                       n_q, t0, n_comp, m, k, lbuf[cur]);
+    const int64_t nseg2 = std::max<int64_t>(1, (lmax + kBlockChunk - 1) / kBlockChunk);
+    const int fin = nseg2 == 1 ? 1 : 0;
+    hipLaunchKernelGGL((topk_stage<256, kBlockR>), dim3((unsigned)(rows * nseg2)), dim3(256), 0, st, 0, fin,
+                       nullptr, 0, kbuf[cur], ibuf[cur], L.cap, kbuf[cur ^ 1], ibuf[cur ^ 1], L.cap, idx, score,
+                       rows, n_q, t0, n_comp, m, k, lbuf[cur], nseg2);
     if (fin) break;
     hipLaunchKernelGGL(topk_next_len, dim3(lgrid), dim3(256), 0, st, rows, n_q, t0, n_comp, m, k,
-                       kTopkChunk, lbuf[cur], lbuf[cur ^ 1]);
-    lmax = (nch2 - 1) * k + std::min<int64_t>(k, kTopkChunk);
+                       kBlockChunk, lbuf[cur], lbuf[cur ^ 1]);
+    lmax = (nseg2 - 1) * k + std::min<int64_t>(k, kBlockChunk);
     cur ^= 1;
   }
   return hipGetLastError();
