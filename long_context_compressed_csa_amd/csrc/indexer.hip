@@ -169,6 +169,87 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
 }
 
 // ---------------------------------------------------------------------------
+// Streaming MFMA scoring for few queries (decode), bf16.  Nothing is shared
+// between waves, so there is no LDS and no barrier: each wave keeps its
+// query's 32*NHB x c_I operand in registers and walks 32-key tiles of its
+// workgroup's key range (tiles wave, wave+4, ...), loading the B operand of
+// the next tile straight from HBM while the MFMAs of the current one run.
+// Per key the only traffic is its c_I bf16 values and one float score.
+// ---------------------------------------------------------------------------
+template <int NHB, int KS>
+__global__ __launch_bounds__(256) void index_scores_stream(
+    const bf16_t* __restrict__ qI, const float* __restrict__ w, const bf16_t* __restrict__ KI,
+    int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t cand_per_wg,
+    float* __restrict__ scores) {
+  constexpr int CI = KS * 16;
+  constexpr int NH = NHB * 32;
+  const int wave = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63;
+  const int64_t qrow = blockIdx.x;
+  const int64_t bi = blockIdx.z;
+  int64_t vis = (t0 + qrow + 1) / m;
+  if (vis > n_comp) vis = n_comp;
+  const int64_t c0 = (int64_t)blockIdx.y * cand_per_wg;
+  int64_t c1 = c0 + cand_per_wg;
+  if (c1 > vis) c1 = vis;
+  const int64_t first = c0 + 32 * wave;
+  if (first >= c1) return;
+
+  bf16x8 qa[NHB][KS];
+  float wv[NHB][16];
+  const int64_t qoff = (bi * n_q + qrow) * (int64_t)NH;
+#pragma unroll
+  for (int mb = 0; mb < NHB; ++mb) {
+    const bf16_t* qp = qI + (qoff + mb * 32 + (l & 31)) * CI + 8 * (l >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qa[mb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wv[mb][r] = w[qoff + mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)];
+  }
+
+  const bf16_t* kbase = KI + bi * comp_bs;
+  float* srow = scores + (bi * n_q + qrow) * n_comp;
+  const int64_t lastkey = c1 - 1;
+  // lane's 16-byte slice of key (tile + l % 32), dims 8 * (l / 32) + 16 * ks
+  auto load_tile = [&](int64_t kb, uint4 (&dst)[KS]) {
+    int64_t key = kb + (l & 31);
+    key = key < lastkey ? key : lastkey;
+    const bf16_t* kp = kbase + key * CI + 8 * (l >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const uint4*>(kp + ks * 16);
+  };
+  uint4 cur[KS], nxt[KS];
+  load_tile(first, cur);
+  for (int64_t kb = first; kb < c1; kb += 128) {
+    const bool more = kb + 128 < c1;
+    if (more) load_tile(kb + 128, nxt);
+    f32x16 acc[NHB];
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb) acc[mb] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, cur[ks]);
+#pragma unroll
+      for (int mb = 0; mb < NHB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], bv, acc[mb], 0, 0, 0);
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc = fmaf(fmaxf(acc[mb][r], 0.f), wv[mb][r], sc);
+    sc += __shfl_xor(sc, 32, 64);
+    const int64_t key = kb + l;
+    if (l < 32 && key < c1) srow[key] = sc;
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Top-k selection.  A segment (one query's candidate list, or one chunk of
 // it) is held in registers by NT threads (one wave or a 256-thread
 // workgroup), R keys each; element e of the segment sits in thread e % NT,
@@ -217,7 +298,9 @@ struct SegReduce {
   }
 };
 
-// Select the top k of the segment held in key[] (valid where e < len);
+// Select the top k of the segment held in key[] (valid where e < len; the
+// caller zeroes the keys of invalid slots, so that no candidate threshold,
+// which is always >= 1, counts them);
 // writes the selection flags into sel[].  `red` is LDS scratch of
 // 2 * NT/64 words (unused for NT == 64); `pre` is LDS scratch of R * NT/64
 // words used for list-order ranks.
@@ -252,14 +335,14 @@ __device__ __forceinline__ void segment_select(const uint32_t (&key)[R], int len
       const uint32_t cand = T | (1u << bit);
       uint32_t c = 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) c += (uint32_t)__popcll(__ballot(val[r] && key[r] >= cand));
+      for (int r = 0; r < R; ++r) c += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key[r] >= cand));
       c = SegReduce<NT>::sum(c, red, wave, parity);
       if (c >= (uint32_t)k) T = cand;
     }
   }
   uint32_t gt = 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) gt += (uint32_t)__popcll(__ballot(val[r] && key[r] > T));
+  for (int r = 0; r < R; ++r) gt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(val[r] && key[r] > T));
   gt = SegReduce<NT>::sum(gt, red, wave, parity);
   const uint32_t need_eq = (uint32_t)k - gt;
   // rank of each tie in list order: wave-local ballot prefix, plus earlier
@@ -268,7 +351,7 @@ __device__ __forceinline__ void segment_select(const uint32_t (&key)[R], int len
   uint64_t meq[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    meq[r] = __ballot(val[r] && key[r] == T);
+    meq[r] = __builtin_amdgcn_ballot_w64(val[r] && key[r] == T);
     if (NT > 64 && l == 0) pre[r * (NT / 64) + wave] = (uint32_t)__popcll(meq[r]);
   }
   if (NT > 64) __syncthreads();
@@ -302,7 +385,7 @@ __device__ __forceinline__ void segment_positions(const bool (&sel)[R], uint32_t
   uint64_t ms[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    ms[r] = __ballot(sel[r]);
+    ms[r] = __builtin_amdgcn_ballot_w64(sel[r]);
     if (NT > 64 && l == 0) pre[r * (NT / 64) + wave] = (uint32_t)__popcll(ms[r]);
   }
   if (NT > 64) __syncthreads();
@@ -361,20 +444,36 @@ __global__ __launch_bounds__(256) void topk_stage(
   if (len64 > CH) len64 = CH;
   if (len64 < 0 || !active) len64 = 0;
   const int len = (int)len64;
-  // a wave with nothing to do still runs the uniform code when NT == 256
+  // a wave with nothing to do still runs the uniform code when NT == 256.
+  // Loads are unconditional (index clamped into the segment) so that all R
+  // of them are in flight before the first wait.
   uint32_t key[R];
   int32_t ix[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = r * NT + tid;
-    const bool v = e < len;
+  const int lastc = len > 0 ? len - 1 : 0;
+  if (len > 0) {
     if (from_scores) {
-      key[r] = v ? f2key(scores[row * ld_scores + base + e]) : 0u;
-      ix[r] = (int32_t)(base + e);
+      const float* src = scores + row * ld_scores + base;
+      float raw[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) raw[r] = src[min(r * NT + tid, lastc)];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        key[r] = r * NT + tid < len ? f2key(raw[r]) : 0u;
+        ix[r] = (int32_t)(base + r * NT + tid);
+      }
     } else {
-      key[r] = v ? kin[row * ld_in + base + e] : 0u;
-      ix[r] = v ? iin[row * ld_in + base + e] : -1;
+      const uint32_t* ks = kin + row * ld_in + base;
+      const int32_t* is = iin + row * ld_in + base;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = min(r * NT + tid, lastc);
+        key[r] = r * NT + tid < len ? ks[e] : 0u;
+        ix[r] = is[e];
+      }
     }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) { key[r] = 0u; ix[r] = -1; }
   }
   bool sel[R];
   segment_select<NT, R>(key, len, (int)k, sel, red_all[sub], pre_all[sub]);
@@ -464,6 +563,9 @@ bool index_topk_supported(int64_t n_comp, int64_t k) {
   return n_comp <= kWaveChunk || k <= kWaveChunk / 2;
 }
 
+// keys per workgroup of the streaming (decode) scoring kernel
+constexpr int64_t kStreamKeysPerWG = 4096;
+
 template <int NHB, int KS>
 static hipError_t launch_scores_mfma(const void* qI, const float* w, const void* KI, int64_t cbs,
                                      int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
@@ -477,11 +579,11 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
                        (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores);
   } else {
     // few queries (decode): split each query's keys over many workgroups
-    const int64_t cpw = 1024;
+    const int64_t cpw = kStreamKeysPerWG;
     const int64_t nsplit = std::max<int64_t>(1, (vmax + cpw - 1) / cpw);
     dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
-    hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 1>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
-                       (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, n_q, scores);
+    hipLaunchKernelGGL((index_scores_stream<NHB, KS>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
+                       (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, scores);
   }
   return hipGetLastError();
 }
