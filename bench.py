@@ -342,16 +342,95 @@ def cpu_baseline(prefill_inputs, torch, n_queries):
 
 
 def calibrate_copy(torch):
-    """A plain device copy of known size, for scaling HBM counters."""
+    """A plain elementwise copy of known size (1 GiB read, 1 GiB written),
+    for scaling the HBM byte counters."""
     nbytes = 1 << 30
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    a.fill_(1)
+    a.fill_(1.0)
     torch.cuda.synchronize()
     for _ in range(3):
-        b.copy_(a)
+        torch.mul(a, 1.0, out=b)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}))
+
+
+# ------------------------------------------------------- HBM traffic ----
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_mfma_c512_csa_prefill_n8192_hbm_traffic.json")
+ATTEND_SOURCES = [os.path.join(ROOT, "long_context_compressed_csa_amd", "csrc", f)
+                  for f in ("attend.hip", "common.hpp")]
+
+
+def _sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _pmc_mean(csv_dir, counter, name_regex):
+    """Mean of one counter over the dispatches whose kernel name matches."""
+    import csv
+    import glob
+    import re
+    vals = []
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter and re.search(name_regex, row["Kernel_Name"]):
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise RuntimeError(f"no {counter} samples for /{name_regex}/ under {csv_dir}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_summary(pmc_dir, commands):
+    """Per-launch HBM bytes of the attention kernel from four counter runs
+    (attention FETCH_SIZE, attention WRITE_SIZE, copy FETCH_SIZE, copy
+    WRITE_SIZE, each in KiB per dispatch), every counter scaled by what it
+    reads for the 1 GiB copy."""
+    att = "attend_mfma_c512"
+    cp = "vectorized_elementwise_kernel"
+    f_att, nf = _pmc_mean(os.path.join(pmc_dir, "attend_fetch"), "FETCH_SIZE", att)
+    w_att, nw = _pmc_mean(os.path.join(pmc_dir, "attend_write"), "WRITE_SIZE", att)
+    f_cp, _ = _pmc_mean(os.path.join(pmc_dir, "copy_fetch"), "FETCH_SIZE", cp)
+    w_cp, _ = _pmc_mean(os.path.join(pmc_dir, "copy_write"), "WRITE_SIZE", cp)
+    copy_bytes = float(1 << 30)
+    f_scale = copy_bytes / (f_cp * 1024.0)
+    w_scale = copy_bytes / (w_cp * 1024.0)
+    read_b = f_att * 1024.0 * f_scale
+    write_b = w_att * 1024.0 * w_scale
+    rec = {
+        "kernel": "attend_mfma_c512<0,1> (csa_attend), CSA prefill n=8192, n_h=64, c=512, k=512, n_win=128",
+        "attend_sources_sha256": _sources_sha256(ATTEND_SOURCES),
+        "fetch_kib_per_dispatch": f_att, "write_kib_per_dispatch": w_att,
+        "dispatches": {"fetch": nf, "write": nw},
+        "copy_fetch_kib": f_cp, "copy_write_kib": w_cp, "copy_bytes_each_way": copy_bytes,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "read_bytes_per_launch": read_b, "write_bytes_per_launch": write_b,
+        "traffic_bytes_per_launch": read_b + write_b,
+        "commands": commands,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def recorded_traffic():
+    """The recorded per-launch HBM bytes, or None when there is no record or
+    the attention sources have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("attend_sources_sha256") != _sources_sha256(ATTEND_SOURCES):
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def main(argv=None):
@@ -365,7 +444,14 @@ def main(argv=None):
     ap.add_argument("--decode-reps", type=int, default=10)
     ap.add_argument("--hca-iters", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--traffic-summary", metavar="PMC_DIR", default=None,
+                    help="summarise counter runs under PMC_DIR/{attend_fetch,attend_write,copy_fetch,"
+                         "copy_write} into the traffic record under profiles/ (no GPU needed)")
+    ap.add_argument("--traffic-commands", default="", help="the commands that made PMC_DIR, for the record")
     a = ap.parse_args(argv)
+    if a.traffic_summary:
+        traffic_summary(a.traffic_summary, a.traffic_commands)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
@@ -421,7 +507,7 @@ def main(argv=None):
                    "global_batch": 1, "seq_len": 8192},
         "roofline": {"bound": "mfma", "kernel": "attend_mfma_c512 (csa_attend)",
                      "achieved": pre["attend_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": pre["attend_tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": pre["attend_tflops"] / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(),
                      "flop_per_launch": pre["flop_attend"], "avg_launch_us": att_us},
         "cpu_baseline": cpu,
         "stage_us": pre["stage_us"],
