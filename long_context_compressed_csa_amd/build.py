@@ -4,7 +4,8 @@
 
 Every .hip file under csrc/ is compiled for gfx950 by hipcc into an object
 file under _build/, then linked into long_context_compressed_csa_amd/libcsa.so.
-Packed-fp32 instruction forms are disabled for all device code.
+Packed-fp32 instruction forms are disabled for all device code; attend.hip
+also selects the VGPR form of MFMA results (see EXTRA_FLAGS).
 """
 
 from __future__ import annotations
@@ -30,6 +31,13 @@ CXXFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# Per-source extra flags.  attend.hip: MFMA results go to VGPRs by default
+# (its S^T accumulators feed VALU code; its O accumulator is pinned to AGPRs
+# explicitly in the source), and the scheduler tracks register pressure with
+# the AMDGPU trackers, without which its main loop spills.
+EXTRA_FLAGS = {
+    "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-use-amdgpu-trackers=1"],
+}
 
 
 def _hipcc() -> str:
@@ -62,7 +70,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     for s in srcs:
         o = os.path.join(BUILD, os.path.basename(s) + ".o")
         objs.append(o)
-        cmds.append([hipcc, *CXXFLAGS, "-c", s, "-o", o])
+        cmds.append([hipcc, *CXXFLAGS, *EXTRA_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"

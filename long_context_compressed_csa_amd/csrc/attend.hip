@@ -109,42 +109,47 @@ __global__ __launch_bounds__(256) void attend_generic(
 // MFMA path (bf16, c = 512, 64-head groups).
 //
 // A workgroup serves G consecutive queries of one 64-head group; two waves
-// per query, each owning 32 heads over all 512 dimensions (Q^T operand in
-// 128 VGPRs, O accumulator in 256 AGPRs).  Entries are processed in tiles of
-// 32 rows that all waves of the workgroup share: the rows are gathered from
+// per query, each owning 32 heads over all 512 dimensions (the Q operand in
+// 128 VGPRs, the O accumulator in 256 AGPRs).  Entries stream through LDS in
+// tiles of 16 rows that all waves of the workgroup share, gathered from
 // HBM/L2 straight into LDS (global_load_lds_dwordx4, one 1 KiB row per wave
-// instruction), double-buffered with one barrier per tile.
+// instruction) three tiles ahead of use, into four statically distinct
+// buffers, with one barrier per tile.
 //
-// Per tile and wave:
-//   S^T = E Q^T      v_mfma_f32_32x32x16_bf16, A = E rows from LDS
-//                    (ds_read_b128), B = Q^T from registers.  The result
-//                    has one head per lane column and 16 entries per lane,
-//                    so the softmax over entries needs only in-lane work and
-//                    one exchange between the two lane halves.
-//   O += P E         A = P taken straight from the S^T accumulators (the
-//                    contraction index is permuted to match their row
-//                    layout), B = E^T read with ds_read_b64_tr_b16, which
-//                    returns a 4-row x 16-column block column-per-lane.
-// LDS rows are 1024 + 64 bytes apart and the four 16-byte chunks of every
-// 64-byte column block of row r are XOR-permuted by (r/4)%4.  With gfx950's
-// 64 LDS banks this keeps both access patterns conflict-free: the b128 row
-// reads (16 lanes = 16 consecutive rows, one chunk each) and the transposed
-// reads (32 lanes = 4 consecutive rows x one 64-byte block each), and the
-// offset of column block nb stays a constant 64*nb, so each lane needs only
-// two base addresses per phase.
+// Per tile step i and wave the work is software-pipelined:
+//   S^T(i+1) = E Q^T   v_mfma_f32_16x16x32_bf16, A = 16 entry rows from LDS
+//                      (ds_read_b128), B = Q^T (16 heads) from registers; two
+//                      head blocks.  A lane ends up with 4 entries of each of
+//                      two heads.
+//   O += P(i) E(i)     v_mfma_f32_32x32x16_bf16 over the 16 entries of tile
+//                      i, B = E^T read with ds_read_b64_tr_b16 (4 rows x 16
+//                      columns, column-per-lane), A = P(i) in registers;
+//                      the weights of tile i+1 are computed between these
+//                      MFMAs, which do not depend on them.
+// A lane's 32x32 A operand (head l%32, entries 8(l/32)..+7) is its own 4
+// weights of that head plus the 4 held by lane l^16, exchanged with one
+// v_permlane16_swap per register.  LDS rows are 1024 + 64 bytes apart and
+// the four 16-byte chunks of every 64-byte column block of row r are
+// XOR-permuted by (r/4)%4: with gfx950's 64 LDS banks both the b128 row
+// reads (16 lanes = 16 consecutive rows) and the transposed reads (16 lanes
+// = 4 rows x 4 chunks) are conflict-free, and column block nb stays at the
+// constant offset 64*nb.
 // ---------------------------------------------------------------------------
 constexpr int kC = 512;
 constexpr int kHG = 64;              // heads per head group
 constexpr int kHW = 32;              // heads per wave
-constexpr int kT = 32;               // entries per tile
-constexpr int kRowB = kC * 2 + 64;   // LDS bytes per entry row (64-byte skew)
-constexpr int kTileB = kT * kRowB;   // 34 KiB
+constexpr int kT = 16;               // entries per tile
+constexpr int kBlkB = kT * 64;       // one 64-byte column block of all 16 rows
+constexpr int kTileB = kT * kC * 2;  // 16 KiB: 16 column blocks
 constexpr int kMaxSel = 2048;        // selected entries staged in LDS
 constexpr int kStageRowB = 256 * 2;  // output staging row (256 dims), XOR-swizzled
+static_assert(kHW * kStageRowB <= kTileB, "a wave's output staging must fit one tile buffer");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
 // max / sum of a value and its copy in the other 32-lane half
 __device__ __forceinline__ float half_max(float x) {
@@ -155,16 +160,41 @@ __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+// the value held by lane l ^ 16
+__device__ __forceinline__ uint32_t from_lane_xor16(uint32_t x, bool upper16) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);   // {x[l & ~16], x[l | 16]}
+  return upper16 ? r[0] : r[1];
+}
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+// barrier among the workgroup's waves that does not drain outstanding LDS
+// gathers (a __syncthreads fence would wait for every one of them)
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// O += A B on the 32x32x16 bf16 MFMA with O pinned to accumulation registers.
+// This file is compiled with MFMA results in VGPRs (the S^T accumulators are
+// read by VALU code); O alone, 256 registers per lane, is kept in AGPRs by
+// issuing its product here.  The compiler sees only an asm statement, so
+// every place where compiled code touches O next to these instructions
+// (zeroing before the first, reading after the last) pads with o_hazard_pad.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8 a, const bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void o_hazard_pad() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 template <int DENSE, int G>
 struct AttnSmem {
   int32_t sel[DENSE ? 1 : kMaxSel];
-  float bc[2 * G][kHW];             // per-wave broadcast of per-head factors
-  int32_t cnt[2 * G];
-  int32_t gen;                      // restart generation (see the softmax note)
+  int32_t cnt[DENSE ? 1 : kMaxSel / 128][2];   // per-round valid counts of the compaction
+  float bc[2 * G][kHW];                          // per-wave broadcast of per-head factors
+  int32_t gen;                                   // restart generation (see the softmax note)
 };
 
 template <int DENSE, int G>
@@ -174,13 +204,19 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
     int64_t raw_pos0, const float* __restrict__ sink, int64_t n_q, int64_t t0, int64_t n_comp,
     int n_h, int64_t k, int64_t m, int64_t n_win, float scale, int nsplit,
     float* __restrict__ part_o, float* __restrict__ part_ml, bf16_t* __restrict__ out) {
-  constexpr int NW = 2 * G;  // waves per workgroup
+  constexpr int NW = 2 * G;        // waves per workgroup
+  constexpr int R = kT / NW;       // gathered rows per wave and tile
   __shared__ AttnSmem<DENSE, G> sm;
-  // the two tile buffers (double buffering: gather one while computing the other)
-  __shared__ __attribute__((aligned(16))) unsigned char E0[kTileB];
-  __shared__ __attribute__((aligned(16))) unsigned char E1[kTileB];
+  // four tile buffers: tile i lives in buffer i % 4
+  __shared__ __attribute__((aligned(16))) unsigned char T0[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char T1[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char T2[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char T3[kTileB];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int half = l >> 5;
+  const int g4 = l >> 4;             // 16-lane group
+  const bool up16 = (l & 16) != 0;   // odd 16-lane group
+  const int s16 = l & 15;
   const int qw = wave >> 1;          // query slot in the group
   const int hw = wave & 1;           // which 32 heads of the group
   const int64_t grp = (int64_t)gridDim.x - 1 - blockIdx.x;   // later queries (more work) first
@@ -193,35 +229,61 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   const bool qvalid = rq < n_q;
   const int64_t t_first = t0 + r0, t_last = t0 + rlast;
   const int64_t t_q = t0 + (qvalid ? rq : rlast);
+  const int head0 = kHG * hg + kHW * hw;   // first head of this wave
+
+  // ---- Q operand (B of the 16x16x32 MFMA): lane holds head
+  //      head0 + 16*hb + l%16, dims 32*ks + 8*(l/16) + (0..7)
+  bf16x8 qB[16][2];
+  auto load_q = [&]() {
+    const int64_t qrow = qvalid ? rq : rlast;
+    const bf16_t* qp = q + ((bi * n_q + qrow) * n_h + head0 + s16) * (int64_t)kC + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        qB[ks][hb] = *reinterpret_cast<const bf16x8*>(qp + hb * 16 * kC + ks * 32);
+  };
 
   // ---- entry list: compressed part (selected or dense), then the union of
   //      the group's causal windows
   int64_t nsel, vis_q;
   if (DENSE) {
+    load_q();
     nsel = (t_last + 1) / m;
     if (nsel > n_comp) nsel = n_comp;
     vis_q = (t_q + 1) / m;
     if (vis_q > n_comp) vis_q = n_comp;
   } else {
-    // G == 1: stable compaction of the valid indices (0 <= s < visible)
+    // G == 1: stable compaction of the valid indices (0 <= s < visible);
+    // every index load is issued before the first is used
+    constexpr int NT = 64 * NW;
+    constexpr int NR = kMaxSel / NT;
     int64_t vis = (t_first + 1) / m;
     if (vis > n_comp) vis = n_comp;
     const int32_t* ir = idx + (bi * n_q + r0) * k;
-    int64_t base = 0;
-    for (int64_t j0 = 0; j0 < k; j0 += 64 * NW) {
-      const int64_t j = j0 + tid;
-      const int32_t sv = j < k ? ir[j] : -1;
-      const bool ok = sv >= 0 && sv < vis;
-      const uint64_t mk = __ballot(ok);
-      if (l == 0) sm.cnt[wave] = __popcll(mk);
-      __syncthreads();
-      int64_t pos = base;
-      for (int w2 = 0; w2 < wave; ++w2) pos += sm.cnt[w2];
-      pos += __popcll(mk & ((l == 0) ? 0ull : (~0ull >> (64 - l))));
-      if (ok && pos < kMaxSel) sm.sel[pos] = sv;
-      for (int w2 = 0; w2 < NW; ++w2) base += sm.cnt[w2];
-      __syncthreads();
+    int32_t sv[NR];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int64_t j = (int64_t)u * NT + tid;
+      sv[u] = j < k ? ir[j] : -1;
     }
+    load_q();   // in flight while the indices are compacted
+    uint64_t mk[NR];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      mk[u] = __builtin_amdgcn_ballot_w64(sv[u] >= 0 && sv[u] < vis);
+      if (l == 0) sm.cnt[u][wave] = __popcll(mk[u]);
+    }
+    __syncthreads();
+    const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+    int64_t base = 0;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int64_t pos = base + (wave ? sm.cnt[u][0] : 0) + __popcll(mk[u] & below);
+      if (((mk[u] >> l) & 1) && pos < kMaxSel) sm.sel[pos] = sv[u];
+      base += sm.cnt[u][0] + sm.cnt[u][1];
+    }
+    __syncthreads();
     nsel = base < kMaxSel ? base : kMaxSel;
     vis_q = nsel;
   }
@@ -242,38 +304,53 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
 
   const bf16_t* cbase = Ccomp + bi * cbs;
   const bf16_t* rbase = kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
-  // gather one tile into LDS.  Lane l (< 32) resolves the address of tile
-  // row l; wave w then loads rows w, w+NW, ... with the row base broadcast
-  // to scalar registers, lane l fetching chunk l ^ f(row) so that LDS chunk
-  // position c holds row chunk c ^ f(row).
+  // Gather tile ti into a buffer.  Lane l (< 16) resolves the address of
+  // tile row l (rows past the split's end repeat its first entry, weight 0);
+  // wave w loads rows w, w+NW, ... with the row base broadcast to scalar
+  // registers, lane l fetching chunk l ^ f(row), so LDS chunk position c
+  // holds row chunk c ^ f(row).  Always exactly R loads per wave.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_tile = [&](int64_t jt, unsigned char* buf) {
-    int64_t j = jt + (l & 31);
-    if (j >= je) j = jb;  // tail padding rows: any real row (its weight is 0)
-    const bf16_t* p = j < nsel ? cbase + (int64_t)(DENSE ? j : sm.sel[j]) * kC
-                               : rbase + (j - nsel) * (int64_t)kC;
-    const uint64_t pv = reinterpret_cast<uint64_t>(p);
-    const uint32_t plo = (uint32_t)pv, phi = (uint32_t)(pv >> 32);
+  const int jbi = (int)jb, jei = (int)je, nseli = (int)nsel;
+  // Tile layout in LDS (column-block major): 64-byte column block b of
+  // tile row r, 16-byte chunk c of that block, lives at
+  //   b * 1024 + c * 256 + ((r ^ 4c) * 16).
+  // Gather: one wave instruction loads column block b of all 16 rows (lane
+  // l: row (l%16) ^ 4(l/16), chunk l/16, i.e. LDS bytes b*1024 + 16 l); wave
+  // w loads blocks w, w+NW, ...  Rows past the split's end repeat its first
+  // entry (weight 0).  Always exactly R loads per wave and tile.
+  const int grow = s16 ^ (4 * g4);   // tile row this lane fetches
+  auto issue_tile = [&](int ti, unsigned char* buf) {
+    int j = jbi + ti * kT + grow;
+    if (j >= jei) j = jbi;
+    // The selected entry is read with a self-contained asm load (it waits
+    // for its own result): left to the compiler, these per-tile LDS reads
+    // are hoisted across the unrolled steps, and the live ranges that
+    // creates push the Q operand out of registers.  The index is clamped so
+    // that every lane reads, with no branch around the load.
+    int selj = j;
+    if (!DENSE) {
+      const uint32_t a = (uint32_t)(uintptr_t)&sm.sel[j < nseli ? j : 0];
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(selj) : "v"(a));
+    }
+    const int e = j < nseli ? selj : j - nseli;
+    const bf16_t* p = (j < nseli ? cbase : rbase) + (int64_t)e * kC + 8 * g4;
 #pragma unroll
-    for (int rr = 0; rr < kT / NW; ++rr) {
-      const int row = wave_u + rr * NW;
-      // readlane returns a signed int: zero-extend both halves
-      const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(phi, row) << 32) |
-                            (uint64_t)(uint32_t)__builtin_amdgcn_readlane(plo, row);
-      const unsigned char* src = reinterpret_cast<const unsigned char*>(base) + ((l ^ swz(row)) << 4);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(buf + row * kRowB), 16, 0, 0);
+    for (int rr = 0; rr < R; ++rr) {
+      const int b = wave_u + rr * NW;
+      __builtin_amdgcn_global_load_lds((const void*)(p + 32 * b), (lds_void_t*)(buf + b * kBlkB), 16, 0, 0);
     }
   };
 
-  // ---- Q^T operand: head 64*hg + 32*hw + l%32, dims 16*ks + 8*half + (0..7)
-  bf16x8 qT[32];
-  {
-    const int64_t qrow = qvalid ? rq : rlast;
-    const bf16_t* qp = q + ((bi * n_q + qrow) * n_h + kHG * hg + kHW * hw + (l & 31)) * (int64_t)kC + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks)
-      qT[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
-  }
+  // per-lane LDS byte offsets inside a tile buffer (add b * 1024 for column block b)
+  //   S A operand: row l%16, chunk l/16
+  const int sA = g4 * 256 + ((s16 ^ (4 * g4)) * 16);
+  //   P V B operand (transposed read): rows 8*half + 4*u + (l%16)/4, columns
+  //   32*nb + 16*((l/16)%2) + 4*(l%4): chunk 2*((l/16)%2) + (l%4)/2 of the
+  //   block, byte 8*(l%2) of the chunk
+  const int cpart = 2 * (g4 & 1) + ((s16 & 3) >> 1);
+  auto trbase = [&](int row) { return cpart * 256 + ((row ^ (4 * cpart)) * 16) + 8 * (s16 & 1); };
+  const int trB0 = trbase(8 * half + (s16 >> 2)), trB1 = trbase(8 * half + 4 + (s16 >> 2));
+
   // Softmax without rescaling O.  VALU instructions cannot operate on the
   // accumulation registers, so an online max that rescales O every time it
   // grows would force O out of them.  Instead each head keeps a fixed
@@ -282,148 +359,189 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   // logit exceed m_ref by more than kLogHeadroom (weights up to 2^64; the
   // float32 range stops at 2^128), the workgroup runs this query's entries
   // again with m_ref raised to the largest logit seen -- a rare, exact
-  // fallback.
+  // fallback.  A lane holds logits of two heads (16-head blocks hb = 0, 1);
+  // all four lanes that hold a head agree on its m_ref.
   constexpr float kLogHeadroom = 64.f;
-  f32x16 o[16];
-  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;   // head l%32
   const float sl2 = scale * kLog2e;
-  // per-lane LDS byte offsets inside a tile buffer
-  //   S^T A operand: row l%32, chunk 2ks + half -> 16*((2(ks%2) + half) ^ g) + 64*(ks/2)
-  const int srow = l & 31;
-  const int sb0 = srow * kRowB + 16 * (half ^ swz(srow));
-  const int sb1 = srow * kRowB + 16 * ((half ^ swz(srow)) ^ 2);
-  //   P V B operand (transposed read): rows 16ks2 + 8q + 4half + (l%16)/4,
-  //   column block nb, chunk 2*((l/16)%2) + (l%4)/2 of the block, byte 8*(l%2)
-  const int s16 = l & 15;
-  const int cpart = 2 * ((l >> 4) & 1) + ((s16 & 3) >> 1);
-  const int boff = 8 * (s16 & 1);
-  auto trbase = [&](int row) { return row * kRowB + 16 * (cpart ^ swz(row)) + boff; };
-  const int tbA0 = trbase(4 * half + (s16 >> 2)), tbB0 = trbase(8 + 4 * half + (s16 >> 2));
-  const int tbA1 = trbase(16 + 4 * half + (s16 >> 2)), tbB1 = trbase(24 + 4 * half + (s16 >> 2));
+  f32x16 o[16];
+  float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY};
+  float l_part = 0.f;   // sum of this lane's weights of head l%32
+
+  // S^T of one tile: 16 entries x (2 blocks of 16 heads), 4 accumulation
+  // chains, row operands fetched two column blocks ahead
+  auto s_tile = [&](const unsigned char* B, f32x4 (&sacc)[2]) {
+    f32x4 c[2][2] = {{(f32x4){}, (f32x4){}}, {(f32x4){}, (f32x4){}}};
+    const unsigned char* a = B + sA;
+    bf16x8 av[3];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) av[u] = *reinterpret_cast<const bf16x8*>(a + kBlkB * u);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks + 2 < 16) av[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(a + kBlkB * (ks + 2));
+      c[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks % 3], qB[ks][0], c[0][ks & 1], 0, 0, 0);
+      c[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks % 3], qB[ks][1], c[1][ks & 1], 0, 0, 0);
+    }
+    // keep the operand reads ahead of the MFMAs that use them: left alone,
+    // the scheduler sinks every read next to its use and waits on it
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+#pragma unroll
+    for (int ks = 0; ks < 14; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    sacc[0] = c[0][0] + c[0][1];
+    sacc[1] = c[1][0] + c[1][1];
+  };
+  // weights of tile ti from its S^T: the A operand of the P V product
+  auto weights = [&](int ti, const f32x4 (&sacc)[2]) -> bf16x8 {
+    const int64_t j0 = jb + (int64_t)ti * kT;
+    const int64_t remv = je - j0;
+    const int rem = (int)(remv < 0 ? 0 : (remv < kT ? remv : kT));   // real entries in this tile
+    // the group's entry list is the union over its G consecutive queries:
+    // this query excludes at most one compressed entry (completed only at
+    // the group's last position) and one window row (outside its window)
+    int exA = -1, exW = -1;
+    if (DENSE) {
+      const int64_t cap = 1 << 20;
+      auto rel = [&](int64_t e) { const int64_t x = e - j0; return (int)(x < -1 || x > cap ? -1 : x); };
+      exA = rel(exA_abs);
+      exW = rel(exW_abs);
+    }
+    float sv[2][4], tmax[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      tmax[hb] = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int loc = 4 * g4 + r;
+        bool valid = loc < rem;
+        if (DENSE) valid = valid & (loc != exA) & (loc != exW);
+        sv[hb][r] = valid ? sacc[hb][r] * sl2 : -INFINITY;
+        tmax[hb] = fmaxf(tmax[hb], sv[hb][r]);
+      }
+      m_seen[hb] = fmaxf(m_seen[hb], tmax[hb]);
+    }
+    if (__builtin_amdgcn_ballot_w64(m_ref[0] == -INFINITY || m_ref[1] == -INFINITY)) {
+      // first valid logits of a head: its maximum over the four lanes holding it
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        float x = fmaxf(tmax[hb], __uint_as_float(from_lane_xor16(__float_as_uint(tmax[hb]), up16)));
+        x = half_max(x);
+        if (m_ref[hb] == -INFINITY) m_ref[hb] = x;
+      }
+    }
+    uint32_t pk[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float mb = (m_ref[hb] == -INFINITY) ? 0.f : m_ref[hb];
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[hb][r] - mb);
+        const float p1 = __builtin_amdgcn_exp2f(sv[hb][r + 1] - mb);
+        pk[hb][r >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t));
+      }
+    }
+    // own head block (head l%32) and the block lane l^16 needs
+    uint32_t own[2], lo[2], hi[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      own[i] = up16 ? pk[1][i] : pk[0][i];
+      const uint32_t recv = from_lane_xor16(up16 ? pk[0][i] : pk[1][i], up16);
+      lo[i] = up16 ? recv : own[i];   // entries 8*half + 0..3
+      hi[i] = up16 ? own[i] : recv;   // entries 8*half + 4..7
+    }
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float rs = l_part;
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo[0]), ones, rs, false);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo[1]), ones, rs, false);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi[0]), ones, rs, false);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi[1]), ones, rs, false);
+    l_part = rs;
+    return __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], hi[0], hi[1]));
+  };
+  // O[head][dim] += P[head][entry] E[entry][dim] over one tile: 16 column
+  // blocks, transposed operands fetched two blocks ahead
+  auto pv_tile = [&](const unsigned char* B, const bf16x8 pa) {
+    bf16x4 tr[3][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      tr[u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB0 + kBlkB * u));
+      tr[u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB1 + kBlkB * u));
+    }
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) {
+      if (nb + 2 < 16) {
+        tr[(nb + 2) % 3][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB0 + kBlkB * (nb + 2)));
+        tr[(nb + 2) % 3][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB1 + kBlkB * (nb + 2)));
+      }
+      const bf16x8 bv = __builtin_shufflevector(tr[nb % 3][0], tr[nb % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      mfma_acc(o[nb], pa, bv);
+    }
+  };
+  // one pipeline step: tile i is in Bc with its weights in pa; tile i+1 in
+  // Bn (its gather waited for here); tile i+3 is gathered into Bf, whose
+  // previous tile (i-1) every wave has finished once past the barrier
+  auto step = [&](int i, const unsigned char* Bc, const unsigned char* Bn, unsigned char* Bf, bf16x8& pa) {
+    wait_vm<R>();
+    tile_barrier();
+    issue_tile(i + 3, Bf);
+    f32x4 sn[2];
+    s_tile(Bn, sn);
+    pv_tile(Bc, pa);
+    pa = weights(i + 1, sn);
+  };
+
   if (tid == 0) sm.gen = 0;
   __syncthreads();
   int gen = 0;
   for (;;) {
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb) o[nb] = (f32x16){};
-    l_run = 0.f;
-    // one tile: wait for its gather, start the next gather into the other
-    // buffer, then S^T, weights and P V from this buffer
-    auto tile = [&](const int it, unsigned char* const Eb, unsigned char* const En) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (it + 1 < ntiles) issue_tile(jb + (int64_t)(it + 1) * kT, En);
-      const int64_t j0 = jb + (int64_t)it * kT;
-
-      // S^T[entry][head] over 512 dims: two independent accumulation chains,
-      // LDS operands fetched two steps ahead of the MFMAs that use them
-      f32x16 st0 = (f32x16){}, st1 = (f32x16){};
-      {
-        const unsigned char* e0 = Eb + sb0;
-        const unsigned char* e1 = Eb + sb1;
-        bf16x8 a[3][2];
-        a[0][0] = *reinterpret_cast<const bf16x8*>(e0);
-        a[0][1] = *reinterpret_cast<const bf16x8*>(e1);
-        a[1][0] = *reinterpret_cast<const bf16x8*>(e0 + 64);
-        a[1][1] = *reinterpret_cast<const bf16x8*>(e1 + 64);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (u + 2 < 16) {
-            a[(u + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(e0 + 64 * (u + 2));
-            a[(u + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(e1 + 64 * (u + 2));
-          }
-          st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % 3][0], qT[2 * u], st0, 0, 0, 0);
-          st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % 3][1], qT[2 * u + 1], st1, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+    o_hazard_pad();
+    l_part = 0.f;
+    if (ntiles > 0) {
+      issue_tile(0, T0);
+      issue_tile(1, T1);
+      issue_tile(2, T2);
+      wait_vm<2 * R>();
+      tile_barrier();
+      f32x4 s0[2];
+      s_tile(T0, s0);
+      bf16x8 pa = weights(0, s0);
+      for (int it = 0; it < ntiles; it += 4) {
+        step(it, T0, T1, T3, pa);
+        if (it + 1 >= ntiles) break;
+        step(it + 1, T1, T2, T0, pa);
+        if (it + 2 >= ntiles) break;
+        step(it + 2, T2, T3, T1, pa);
+        if (it + 3 >= ntiles) break;
+        step(it + 3, T3, T0, T2, pa);
       }
-      // first P V operands, independent of the weights: fetch them now
-      bf16x4 tr[3][2];
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        tr[q2][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Eb + tbA0 + 64 * q2));
-        tr[q2][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Eb + tbB0 + 64 * q2));
-      }
-      // weights of head l%32 for the tile's entries (entry = j0 + local)
-      uint32_t pk[8];
-      {
-        const int rem = (int)(je - j0 < kT ? je - j0 : kT);   // real entries in this tile
-        // the group's entry list is the union over its G consecutive queries:
-        // this query excludes at most one compressed entry (completed only at
-        // the group's last position) and one window row (outside its window)
-        int exA = -1, exW = -1;
-        if (DENSE) {
-          const int64_t cap = 1 << 20;
-          auto rel = [&](int64_t e) { const int64_t x = e - j0; return (int)(x < -1 || x > cap ? -1 : x); };
-          exA = rel(exA_abs);
-          exW = rel(exW_abs);
-        }
-        float sv[16];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int loc = 8 * (r >> 2) + 4 * half + (r & 3);
-          bool valid = loc < rem;
-          if (DENSE) valid = valid & (loc != exA) & (loc != exW);
-          sv[r] = valid ? (st0[r] + st1[r]) * sl2 : -INFINITY;
-          tmax = fmaxf(tmax, sv[r]);
-        }
-        tmax = half_max(tmax);
-        m_seen = fmaxf(m_seen, tmax);
-        if (m_ref == -INFINITY) m_ref = tmax;            // first valid logits of this head
-        const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
-        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-        float rs = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(sv[r] - mb);
-          const float p1 = __builtin_amdgcn_exp2f(sv[r + 1] - mb);
-          const bf16x2_t b = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);   // round to nearest even
-          rs = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs, false);   // sum of the weights P V multiplies
-          pk[r >> 1] = __builtin_bit_cast(uint32_t, b);
-        }
-        l_run += half_sum(rs);
-      }
-      // O[head][dim] += P[head][entry] E[entry][dim]; step i = (ks2, nb) = (i/16, i%16),
-      // its transposed operands fetched two steps ahead
-      {
-        bf16x8 pa[2];
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2)
-          pa[ks2] = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2],
-                                                          pk[4 * ks2 + 3]));
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          if (i + 2 < 32) {
-            const int i2 = i + 2, k2 = i2 >> 4, n2 = i2 & 15;
-            tr[i2 % 3][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4_t*)(Eb + (k2 ? tbA1 : tbA0) + 64 * n2));
-            tr[i2 % 3][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4_t*)(Eb + (k2 ? tbB1 : tbB0) + 64 * n2));
-          }
-          const bf16x8 bv = __builtin_shufflevector(tr[i % 3][0], tr[i % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i >> 4], bv, o[i & 15], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-    if (ntiles > 0) issue_tile(jb, E0);
-    for (int it = 0; it < ntiles; ++it) {
-      unsigned char* const Eb = (it & 1) ? E1 : E0;
-      unsigned char* const En = (it & 1) ? E0 : E1;
-      tile(it, Eb, En);
+      wait_vm<0>();   // the look-ahead gathers past the last tile
+      o_hazard_pad();
     }
     // an attempt whose weights may have overflowed is discarded as a whole;
     // the decision is workgroup-wide because the waves share the tiles
-    if (m_seen > m_ref + kLogHeadroom) sm.gen = gen + 1;
+    bool over = false;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float x = fmaxf(m_seen[hb], __uint_as_float(from_lane_xor16(__float_as_uint(m_seen[hb]), up16)));
+      x = half_max(x);
+      m_seen[hb] = x;
+      over |= x > m_ref[hb] + kLogHeadroom;
+    }
+    if (over) sm.gen = gen + 1;
     __syncthreads();
     if (sm.gen == gen) break;
     ++gen;
-    m_ref = m_seen;
+    m_ref[0] = m_seen[0];
+    m_ref[1] = m_seen[1];
   }
-  const float m_run = m_ref;
+  // head l%32: block (l/16)%2 of this lane; both 32-lane halves hold half of its weights
+  const float m_run = up16 ? m_ref[1] : m_ref[0];
+  const float l_run = half_sum(l_part);
 
-  const int head0 = kHG * hg + kHW * hw;   // first head of this wave
   if (nsplit == 1) {
     // final per-head factor e^{-M} / (sum + e^{z - M}), broadcast over the O rows
     if (l < 32) {
@@ -432,11 +550,11 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
       const float fac = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - Mf);
       sm.bc[wave][l] = fac / (l_run * fac + __builtin_amdgcn_exp2f(z2 - Mf));
     }
-    float4 g4[4];
+    __syncthreads();   // every wave is done with the tile buffers; bc is visible
+    float4 g4v[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) g4[g] = *reinterpret_cast<const float4*>(&sm.bc[wave][8 * g + 4 * half]);
-    __syncthreads();   // every wave is done with the tile buffers
-    unsigned char* stg = ((wave < 2) ? E0 : E1) + (wave & 1) * (kHW * kStageRowB);
+    for (int g = 0; g < 4; ++g) g4v[g] = *reinterpret_cast<const float4*>(&sm.bc[wave][8 * g + 4 * half]);
+    unsigned char* stg = wave == 0 ? T0 : wave == 1 ? T1 : wave == 2 ? T2 : T3;
     bf16_t* ob = out + ((bi * n_q + (qvalid ? rq : rlast)) * n_h + head0) * (int64_t)kC;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -445,13 +563,18 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
         const int nb = pass * 8 + nb8;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float gv[4] = {g4[g].x, g4[g].y, g4[g].z, g4[g].w};
+          const float gv[4] = {g4v[g].x, g4v[g].y, g4v[g].z, g4v[g].w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < 4; i += 2) {
+            // rows hr and hr + 1 of this column, rounded to bf16 as one pair
             const int hr = 8 * g + 4 * half + i;
+            const uint32_t pk = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector((f32x2_t){o[nb][4 * g + i] * gv[i], o[nb][4 * g + i + 1] * gv[i + 1]},
+                                                  bf16x2_t));
             // rows 4 apart would share banks: flip the 64-byte half for odd row quads
             const int byte = ((nb8 * 32 + (l & 31)) * 2) ^ (((hr >> 2) & 1) << 6);
-            *reinterpret_cast<bf16_t*>(stg + hr * kStageRowB + byte) = f2bf(o[nb][4 * g + i] * gv[i]);
+            *reinterpret_cast<uint16_t*>(stg + hr * kStageRowB + byte) = (uint16_t)pk;
+            *reinterpret_cast<uint16_t*>(stg + (hr + 1) * kStageRowB + byte) = (uint16_t)(pk >> 16);
           }
         }
       }
