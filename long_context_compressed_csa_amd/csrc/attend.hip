@@ -368,28 +368,29 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   float l_part = 0.f;   // sum of this lane's weights of head l%32
 
   // S^T of one tile: 16 entries x (2 blocks of 16 heads), 4 accumulation
-  // chains, row operands fetched two column blocks ahead
+  // chains, row operands fetched three column blocks ahead
   auto s_tile = [&](const unsigned char* B, f32x4 (&sacc)[2]) {
     f32x4 c[2][2] = {{(f32x4){}, (f32x4){}}, {(f32x4){}, (f32x4){}}};
     const unsigned char* a = B + sA;
-    bf16x8 av[3];
+    constexpr int D = 3;   // column blocks read ahead
+    bf16x8 av[D + 1];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) av[u] = *reinterpret_cast<const bf16x8*>(a + kBlkB * u);
+    for (int u = 0; u < D; ++u) av[u] = *reinterpret_cast<const bf16x8*>(a + kBlkB * u);
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      if (ks + 2 < 16) av[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(a + kBlkB * (ks + 2));
-      c[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks % 3], qB[ks][0], c[0][ks & 1], 0, 0, 0);
-      c[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks % 3], qB[ks][1], c[1][ks & 1], 0, 0, 0);
+      if (ks + D < 16) av[(ks + D) % (D + 1)] = *reinterpret_cast<const bf16x8*>(a + kBlkB * (ks + D));
+      c[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks % (D + 1)], qB[ks][0], c[0][ks & 1], 0, 0, 0);
+      c[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks % (D + 1)], qB[ks][1], c[1][ks & 1], 0, 0, 0);
     }
     // keep the operand reads ahead of the MFMAs that use them: left alone,
     // the scheduler sinks every read next to its use and waits on it
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x100, D, 0);   // D LDS reads
 #pragma unroll
-    for (int ks = 0; ks < 14; ++ks) {
+    for (int ks = 0; ks < 16 - D; ++ks) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * D, 0);
     sacc[0] = c[0][0] + c[0][1];
     sacc[1] = c[1][0] + c[1][1];
   };

@@ -172,15 +172,20 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
 // Streaming MFMA scoring for few queries (decode), bf16.  Nothing is shared
 // between waves, so there is no LDS and no barrier: each wave keeps its
 // query's 32*NHB x c_I operand in registers and walks 32-key tiles of its
-// workgroup's key range (tiles wave, wave+4, ...), loading the B operand of
-// the next tile straight from HBM while the MFMAs of the current one run.
-// Per key the only traffic is its c_I bf16 values and one float score.
+// workgroup's key range (tiles wave, wave+4, ...), loading the B operands of
+// the next two tiles straight from HBM while the MFMAs of the current one
+// run.
+// Per key the only traffic is its c_I bf16 values and one float score.  The
+// kernel also records, per group of 128 keys, the largest score (as an
+// order-preserving key): the k-th largest of these group maxima bounds the
+// k-th largest score from below, which lets selection discard almost every
+// key in one pass.
 // ---------------------------------------------------------------------------
 template <int NHB, int KS>
 __global__ __launch_bounds__(256) void index_scores_stream(
     const bf16_t* __restrict__ qI, const float* __restrict__ w, const bf16_t* __restrict__ KI,
     int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t cand_per_wg,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, uint32_t* __restrict__ gmax, int64_t ld_gmax) {
   constexpr int CI = KS * 16;
   constexpr int NH = NHB * 32;
   const int wave = threadIdx.x >> 6;
@@ -193,7 +198,21 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   int64_t c1 = c0 + cand_per_wg;
   if (c1 > vis) c1 = vis;
   const int64_t first = c0 + 32 * wave;
-  if (first >= c1) return;
+  // group maxima (order-preserving keys, 0 = no key): lanes 4q..4q+3 of a
+  // wave form one group, i.e. 4 keys of each of its 32-key tiles; every
+  // group of the grid is written, empty ones as 0
+  uint32_t gm = 0;
+  auto write_gmax = [&]() {
+    if (gmax == nullptr) return;
+    gm = max(gm, (uint32_t)__shfl_xor((int)gm, 1, 64));
+    gm = max(gm, (uint32_t)__shfl_xor((int)gm, 2, 64));
+    if (l < 32 && (l & 3) == 0)
+      gmax[(bi * n_q + qrow) * ld_gmax + (int64_t)blockIdx.y * 32 + wave * 8 + (l >> 2)] = gm;
+  };
+  if (first >= c1) {
+    write_gmax();
+    return;
+  }
 
   bf16x8 qa[NHB][KS];
   float wv[NHB][16];
@@ -219,11 +238,13 @@ __global__ __launch_bounds__(256) void index_scores_stream(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const uint4*>(kp + ks * 16);
   };
-  uint4 cur[KS], nxt[KS];
+  // three tiles in registers: the current one and two in flight
+  uint4 cur[KS], nxt[KS], nx2[KS];
   load_tile(first, cur);
+  if (first + 128 < c1) load_tile(first + 128, nxt);
   for (int64_t kb = first; kb < c1; kb += 128) {
     const bool more = kb + 128 < c1;
-    if (more) load_tile(kb + 128, nxt);
+    if (kb + 256 < c1) load_tile(kb + 256, nx2);
     f32x16 acc[NHB];
 #pragma unroll
     for (int mb = 0; mb < NHB; ++mb) acc[mb] = (f32x16){};
@@ -241,12 +262,19 @@ __global__ __launch_bounds__(256) void index_scores_stream(
       for (int r = 0; r < 16; ++r) sc = fmaf(fmaxf(acc[mb][r], 0.f), wv[mb][r], sc);
     sc += __shfl_xor(sc, 32, 64);
     const int64_t key = kb + l;
-    if (l < 32 && key < c1) srow[key] = sc;
+    if (l < 32 && key < c1) {
+      srow[key] = sc;
+      gm = max(gm, f2key(sc));
+    }
     if (more) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
+      for (int ks = 0; ks < KS; ++ks) {
+        cur[ks] = nxt[ks];
+        nxt[ks] = nx2[ks];
+      }
     }
   }
+  write_gmax();
 }
 
 // ---------------------------------------------------------------------------
@@ -298,21 +326,18 @@ struct SegReduce {
   }
 };
 
-// Select the top k of the segment held in key[] (valid where e < len; the
-// caller zeroes the keys of invalid slots, so that no candidate threshold,
-// which is always >= 1, counts them);
-// writes the selection flags into sel[].  `red` is LDS scratch of
-// 2 * NT/64 words (unused for NT == 64); `pre` is LDS scratch of R * NT/64
-// words used for list-order ranks.
+// Select the top k of the segment held in key[] (valid where val[]; nval
+// of them, the same value in every lane; the caller zeroes the keys of
+// invalid slots, so that no candidate threshold, which is always >= 1,
+// counts them); writes the selection flags into sel[].  `red` is LDS
+// scratch of 2 * NT/64 words (unused for NT == 64); `pre` is LDS scratch of
+// R * NT/64 words used for list-order ranks.
 template <int NT, int R>
-__device__ __forceinline__ void segment_select(const uint32_t (&key)[R], int len, int k, bool (&sel)[R],
-                                               uint32_t* red, uint32_t* pre) {
+__device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const bool (&val)[R], int nval, int k,
+                                               bool (&sel)[R], uint32_t* red, uint32_t* pre) {
   const int tid = threadIdx.x % NT, wave = tid >> 6, l = tid & 63;
   int parity = 0;
-  bool val[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) val[r] = r * NT + tid < len;
-  if (len <= k) {
+  if (nval <= k) {
 #pragma unroll
     for (int r = 0; r < R; ++r) sel[r] = val[r];
     return;
@@ -475,8 +500,10 @@ __global__ __launch_bounds__(256) void topk_stage(
 #pragma unroll
     for (int r = 0; r < R; ++r) { key[r] = 0u; ix[r] = -1; }
   }
-  bool sel[R];
-  segment_select<NT, R>(key, len, (int)k, sel, red_all[sub], pre_all[sub]);
+  bool val[R], sel[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) val[r] = r * NT + tid < len;
+  segment_select<NT, R>(key, val, len, (int)k, sel, red_all[sub], pre_all[sub]);
   uint32_t pos[R];
   segment_positions<NT, R>(sel, pos, pre_all[sub]);
   if (!active) return;
@@ -499,6 +526,218 @@ __global__ __launch_bounds__(256) void topk_stage(
         kout[row * ld_out + seg * k + pos[r]] = key[r];
         iout[row * ld_out + seg * k + pos[r]] = ix[r];
       }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Threshold path for long candidate lists (the decode scorer's group maxima)
+// ---------------------------------------------------------------------------
+// Count of valid slots over NT threads (a ballot sum; NT == 64 only here).
+template <int R>
+__device__ __forceinline__ int wave_count(const bool (&val)[R]) {
+  int c = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) c += (int)__popcll(__builtin_amdgcn_ballot_w64(val[r]));
+  return c;
+}
+
+// tau[row] = the k-th largest of the row's first min(G, 2048) group maxima,
+// or 1 (every valid key) when fewer than k of them are non-empty.  Each
+// maximum is a distinct key of the row, so at least k keys are >= tau.  One
+// workgroup of 256 threads (8 maxima each) per row.
+__global__ __launch_bounds__(256) void topk_threshold(const uint32_t* __restrict__ gmax, int64_t ld_gmax, int64_t G,
+                                                      int64_t rows, int64_t k, uint32_t* __restrict__ tau) {
+  constexpr int NT = 256, R = 8;
+  __shared__ uint32_t red[2 * (NT / 64) + 1];
+  __shared__ uint32_t pre[R * (NT / 64) + 1];
+  __shared__ uint32_t wmin[NT / 64];
+  __shared__ int wcnt[NT / 64];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int64_t row = blockIdx.x;
+  const int g = (int)(G < NT * R ? G : NT * R);
+  const uint32_t* src = gmax + row * ld_gmax;
+  uint32_t key[R];
+  bool val[R], sel[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = r * NT + tid;
+    const uint32_t v = src[min(e, g - 1)];
+    val[r] = e < g && v != 0u;
+    key[r] = val[r] ? v : 0u;
+  }
+  const int c = wave_count(val);
+  if (l == 0) wcnt[wave] = c;
+  __syncthreads();
+  const int nval = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+  if (nval <= k) {
+    if (tid == 0) tau[row] = 1u;
+    return;   // uniform
+  }
+  segment_select<NT, R>(key, val, nval, (int)k, sel, red, pre);
+  // the k-th largest is the smallest selected key
+  uint32_t mn = 0xffffffffu;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (sel[r]) mn = min(mn, key[r]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+  if (l == 0) wmin[wave] = mn;
+  __syncthreads();
+  if (tid == 0) tau[row] = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
+}
+
+// One wave per (row, 2048-key segment): the top k of the segment's scores
+// that are >= tau[row] (usually all of them: only a few keys pass), written
+// in list order at slot seg*k of the row's pair list, their count in
+// cnt[row][seg].  Every count of the grid is written.
+__global__ __launch_bounds__(256) void topk_filter(const float* __restrict__ scores, int64_t ld_scores,
+                                                   const uint32_t* __restrict__ tau, int64_t n_rows, int64_t n_q,
+                                                   int64_t t0, int64_t n_comp, int64_t m, int64_t k, int64_t nseg,
+                                                   uint32_t* __restrict__ kout, int32_t* __restrict__ iout, int64_t ld_out,
+                                                   int32_t* __restrict__ cnt) {
+  constexpr int R = 32, CH = 64 * R;
+  __shared__ uint32_t pre_all[4][R + 1];
+  const int sub = threadIdx.x >> 6, tid = threadIdx.x & 63;
+  const int64_t gseg = (int64_t)blockIdx.x * 4 + sub;
+  if (gseg >= n_rows * nseg) return;   // whole wave
+  const int64_t row = gseg / nseg, seg = gseg % nseg;
+  int64_t L = (t0 + row % n_q + 1) / m;
+  if (L > n_comp) L = n_comp;
+  const int64_t base = seg * CH;
+  int64_t len64 = L - base;
+  if (len64 > CH) len64 = CH;
+  if (len64 < 0) len64 = 0;
+  const int len = (int)len64;
+  const uint32_t th = tau[row];
+  uint32_t key[R];
+  bool val[R], sel[R];
+  if (len > 0) {
+    const float* src = scores + row * ld_scores + base;
+    float raw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) raw[r] = src[min(r * 64 + tid, len - 1)];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t kk = f2key(raw[r]);
+      val[r] = r * 64 + tid < len && kk >= th;
+      key[r] = val[r] ? kk : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) { val[r] = false; key[r] = 0u; }
+  }
+  const int nval = wave_count(val);
+  segment_select<64, R>(key, val, nval, (int)k, sel, nullptr, pre_all[sub]);
+  uint32_t pos[R];
+  segment_positions<64, R>(sel, pos, pre_all[sub]);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (sel[r]) {
+      kout[row * ld_out + seg * k + pos[r]] = key[r];
+      iout[row * ld_out + seg * k + pos[r]] = (int32_t)(base + r * 64 + tid);
+    }
+  if (tid == 0) cnt[row * nseg + seg] = nval < k ? nval : (int)k;
+}
+
+// One workgroup per row: the row's pair list is the concatenation, in
+// segment order, of cnt[row][s] pairs at slot s*k.  The list is taken in
+// chunks of up to 2048 - run entries after the running top k (run of them,
+// earlier in list order), each chunk reduced to its top k; the final set is
+// written in ascending index order, -1 padded.  Usually one chunk.
+constexpr int kMergeMaxSeg = 4096;
+__global__ __launch_bounds__(256) void topk_merge(const uint32_t* __restrict__ kin, const int32_t* __restrict__ iin,
+                                                  int64_t ld_in, const int32_t* __restrict__ cnt, int64_t nseg,
+                                                  int64_t k, int32_t* __restrict__ idx, float* __restrict__ score_out) {
+  constexpr int NT = 256, R = 8, C = NT * R;
+  __shared__ int32_t pref[kMergeMaxSeg + 1];
+  __shared__ uint32_t runK[1024];
+  __shared__ int32_t runI[1024];
+  __shared__ uint32_t red[2 * (NT / 64) + 1];
+  __shared__ uint32_t pre[R * (NT / 64) + 1];
+  __shared__ int32_t part[NT / 64];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int ns = (int)nseg;
+  // exclusive prefix of the segment counts
+  const int per = (ns + NT - 1) / NT;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int sgi = tid * per + i;
+    if (sgi < ns) local += cnt[row * nseg + sgi];
+  }
+  {
+    // exclusive scan of the per-thread sums: wave scans, then wave totals
+    const int lane = tid & 63, wv = tid >> 6;
+    int v = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(v, o, 64);
+      if (lane >= o) v += y;
+    }
+    if (lane == 63) part[wv] = v;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NT / 64; ++w2) {
+      const int t = part[w2];
+      if (w2 < wv) before += t;
+      total += t;
+    }
+    if (tid == 0) pref[ns] = total;
+    local = before + v - local;   // exclusive prefix of this thread's segments
+  }
+  {
+    int acc = local;
+    for (int i = 0; i < per; ++i) {
+      const int sgi = tid * per + i;
+      if (sgi < ns) { pref[sgi] = acc; acc += cnt[row * nseg + sgi]; }
+    }
+  }
+  __syncthreads();
+  const int N = pref[ns];
+  int run = 0, P = 0;
+  while (true) {
+    const int fill = min(C - run, N - P);
+    const int len = run + fill;
+    uint32_t key[R];
+    int32_t ix[R];
+    bool val[R], sel[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = r * NT + tid;
+      val[r] = e < len;
+      key[r] = 0u;
+      ix[r] = -1;
+      if (e < run) {
+        key[r] = runK[e];
+        ix[r] = runI[e];
+      } else if (e < len) {
+        const int p = P + (e - run);
+        int lo = 0, hi = ns;   // last segment s with pref[s] <= p
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pref[mid] <= p) lo = mid; else hi = mid;
+        }
+        const int64_t off = row * ld_in + (int64_t)lo * k + (p - pref[lo]);
+        key[r] = kin[off];
+        ix[r] = iin[off];
+      }
+    }
+    __syncthreads();   // the running set is read; it may be rewritten below
+    segment_select<NT, R>(key, val, len, (int)k, sel, red, pre);
+    uint32_t pos[R];
+    segment_positions<NT, R>(sel, pos, pre);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (sel[r]) { runK[pos[r]] = key[r]; runI[pos[r]] = ix[r]; }
+    run = len < k ? len : (int)k;
+    P += fill;
+    __syncthreads();
+    if (P >= N) break;
+  }
+  for (int p = tid; p < k; p += NT) {
+    idx[row * k + p] = p < run ? runI[p] : -1;
+    if (score_out) score_out[row * k + p] = p < run ? key2f(runK[p]) : 0.f;
   }
 }
 
@@ -531,17 +770,25 @@ constexpr int64_t kBlockChunk = 256 * kBlockR;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// keys per workgroup of the streaming (decode) scoring kernel, and its
+// group maxima per workgroup (4 waves x 8 groups)
+constexpr int64_t kStreamKeysPerWG = 4096;
+constexpr int64_t kStreamGroupsPerWG = 32;
+
 // Workspace: scores [rows, n_comp] f32 | len A, len B [rows] i64 |
-//            pairs A, pairs B [rows, cap] (u32 key + i32 idx each)
+//            pairs A, pairs B [rows, cap] (u32 key + i32 idx each) |
+//            group maxima [rows, gcap] u32 | tau [rows] u32 | counts [rows, nseg] i32
 struct TopkLayout {
-  size_t scores, lenA, lenB, kA, iA, kB, iB, total;
-  int64_t cap;
+  size_t scores, lenA, lenB, kA, iA, kB, iB, gmax, tau, cnt, total;
+  int64_t cap, gcap, nseg;
 };
 static TopkLayout topk_layout(int64_t b, int64_t n_q, int64_t n_comp, int64_t k) {
   TopkLayout L{};
   const int64_t rows = b * n_q;
   const int64_t nch = (n_comp + kWaveChunk - 1) / kWaveChunk;
+  L.nseg = nch;
   L.cap = nch > 1 ? nch * k : 0;
+  L.gcap = nch > 1 ? (n_comp + kStreamKeysPerWG - 1) / kStreamKeysPerWG * kStreamGroupsPerWG : 0;
   size_t off = 0;
   L.scores = off; off = align256(off + (size_t)rows * n_comp * 4);
   L.lenA = off; off = align256(off + (size_t)rows * 8);
@@ -550,6 +797,9 @@ static TopkLayout topk_layout(int64_t b, int64_t n_q, int64_t n_comp, int64_t k)
   L.iA = off; off = align256(off + (size_t)rows * L.cap * 4);
   L.kB = off; off = align256(off + (size_t)rows * L.cap * 4);
   L.iB = off; off = align256(off + (size_t)rows * L.cap * 4);
+  L.gmax = off; off = align256(off + (size_t)rows * L.gcap * 4);
+  L.tau = off; off = align256(off + (size_t)rows * 4);
+  L.cnt = off; off = align256(off + (size_t)rows * (nch > 1 ? nch : 0) * 4);
   L.total = off;
   return L;
 }
@@ -559,18 +809,22 @@ size_t index_topk_workspace_bytes(int64_t b, int64_t n_q, int64_t n_comp, int64_
 }
 
 bool index_topk_supported(int64_t n_comp, int64_t k) {
-  // multi-stage selection needs each stage to shrink the list at least 2x
-  return n_comp <= kWaveChunk || k <= kWaveChunk / 2;
+  // multi-stage selection needs each stage to shrink the list at least 2x,
+  // and the merge of the threshold path holds at most 1024 pairs and
+  // kMergeMaxSeg segment counts
+  if (n_comp <= kWaveChunk) return true;
+  return k <= kWaveChunk / 2 && (n_comp + kWaveChunk - 1) / kWaveChunk <= kMergeMaxSeg;
 }
 
-// keys per workgroup of the streaming (decode) scoring kernel
-constexpr int64_t kStreamKeysPerWG = 4096;
-
+// Scoring on MFMA.  Returns through *gmax_used whether the group maxima
+// were written (the streaming kernel writes them when gmax is given).
 template <int NHB, int KS>
 static hipError_t launch_scores_mfma(const void* qI, const float* w, const void* KI, int64_t cbs,
                                      int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
-                                     float* scores, hipStream_t st) {
+                                     float* scores, uint32_t* gmax, int64_t ld_gmax, bool* gmax_used,
+                                     hipStream_t st) {
   const int64_t vmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
+  *gmax_used = false;
   if (n_q >= 4) {
     const int64_t nqb = (n_q + 3) / 4;
     const int64_t cpw = ((vmax + 63) / 64) * 64;
@@ -583,7 +837,8 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
     const int64_t nsplit = std::max<int64_t>(1, (vmax + cpw - 1) / cpw);
     dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
     hipLaunchKernelGGL((index_scores_stream<NHB, KS>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
-                       (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, scores);
+                       (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, scores, gmax, ld_gmax);
+    *gmax_used = gmax != nullptr;
   }
   return hipGetLastError();
 }
@@ -595,15 +850,18 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
   const TopkLayout L = topk_layout(b, n_q, n_comp, k);
   unsigned char* W = (unsigned char*)ws;
   float* scores = (float*)(W + L.scores);
+  uint32_t* gmax = L.gcap > 0 ? (uint32_t*)(W + L.gmax) : nullptr;
+  bool gmax_used = false;
   hipError_t err = hipSuccess;
   if (n_comp > 0) {
     bool done = false;
     if (dtype == 1 && nh % 32 == 0 && cI % 16 == 0) {
       const int nhb = (int)(nh / 32), ks = (int)(cI / 16);
-#define CSA_SCORES_CASE(A, B)                                                                   \
-  if (!done && nhb == A && ks == B) {                                                           \
-    err = launch_scores_mfma<A, B>(qI, w, KI, cbs, b, n_q, t0, n_comp, m, scores, st);         \
-    done = true;                                                                                \
+#define CSA_SCORES_CASE(A, B)                                                                       \
+  if (!done && nhb == A && ks == B) {                                                               \
+    err = launch_scores_mfma<A, B>(qI, w, KI, cbs, b, n_q, t0, n_comp, m, scores, gmax, L.gcap,     \
+                                   &gmax_used, st);                                                 \
+    done = true;                                                                                    \
   }
       CSA_SCORES_CASE(1, 4) CSA_SCORES_CASE(1, 8) CSA_SCORES_CASE(2, 4) CSA_SCORES_CASE(2, 8)
       CSA_SCORES_CASE(4, 4) CSA_SCORES_CASE(4, 8)
@@ -621,11 +879,10 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
     }
     if (err != hipSuccess) return err;
   }
-  // selection: one wave per row when every list fits one segment; otherwise
-  // wave segments first, then workgroup segments until one segment is left
   const int64_t rows = b * n_q;
   int64_t lmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
   int64_t nseg = std::max<int64_t>(1, (lmax + kWaveChunk - 1) / kWaveChunk);
+  // one wave per row when every list fits one segment
   if (nseg == 1) {
     const int64_t blocks = (rows + 3) / 4;
     hipLaunchKernelGGL((topk_stage<64, kWaveR>), dim3((unsigned)blocks), dim3(256), 0, st, 1, 1, scores,
@@ -635,6 +892,22 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
   }
   uint32_t* kbuf[2] = {(uint32_t*)(W + L.kA), (uint32_t*)(W + L.kB)};
   int32_t* ibuf[2] = {(int32_t*)(W + L.iA), (int32_t*)(W + L.iB)};
+  if (gmax_used) {
+    // threshold path: a lower bound on each row's k-th largest score from the
+    // group maxima, a filtering pass per 2048-key segment, one exact merge
+    uint32_t* tau = (uint32_t*)(W + L.tau);
+    int32_t* cnt = (int32_t*)(W + L.cnt);
+    const int64_t G = std::max<int64_t>(1, (lmax + kStreamKeysPerWG - 1) / kStreamKeysPerWG) * kStreamGroupsPerWG;
+    hipLaunchKernelGGL(topk_threshold, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows,
+                       k, tau);
+    hipLaunchKernelGGL(topk_filter, dim3((unsigned)((rows * nseg + 3) / 4)), dim3(256), 0, st, scores, n_comp, tau,
+                       rows, n_q, t0, n_comp, m, k, nseg, kbuf[0], ibuf[0], L.cap, cnt);
+    hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(256), 0, st, kbuf[0], ibuf[0], L.cap, cnt, nseg, k,
+                       idx, score);
+    return hipGetLastError();
+  }
+  // general path: wave segments first, then workgroup segments until one
+  // segment is left
   int64_t* lbuf[2] = {(int64_t*)(W + L.lenA), (int64_t*)(W + L.lenB)};
   const unsigned lgrid = (unsigned)((rows + 255) / 256);
   {

@@ -206,6 +206,61 @@ def test_index_topk_exact_ties_lower_index_wins():
     assert got[1].tolist() == [0, 1, 2, 3, 7]
 
 
+@pytest.mark.parametrize("n_comp,k,bump", [
+    (5000, 100, [4999, 123, 2048]),   # ties across three segments, a few strictly larger entries
+    (20480, 1000, [7]),               # every segment keeps 1000 ties: the merge takes two chunks
+])
+def test_index_topk_long_lists_exact_ties(n_comp, k, bump):
+    # equal scores everywhere except a few larger entries: the lower indices
+    # must win the ties, however the candidate list is split
+    say(f"index long-list ties n_comp={n_comp} k={k}")
+    m = 1
+    KI = torch.ones((n_comp, 128), dtype=torch.bfloat16)
+    for e in bump:
+        KI[e] = 2.0
+    qI = torch.ones((1, 64, 128), dtype=torch.bfloat16)
+    w = torch.ones((1, 64))
+    idx = L.csa_index_topk(g(qI), g(w), g(KI), n_comp - 1, m, k)
+    torch.cuda.synchronize()
+    want, _, _ = _oracle_index(qI, w, KI, [n_comp - 1], m, k)
+    assert want[0].tolist() == sorted(bump + [e for e in range(n_comp) if e not in bump][: k - len(bump)])
+    assert idx[0, 0].cpu().numpy().tolist() == want[0].tolist()
+
+
+def test_index_topk_long_lists_rows_differ():
+    # few queries whose visible counts differ (4095, 4095, 4096 entries)
+    say("index long lists, rows with different visibility")
+    m, k, n_q, t0, n_comp = 4, 300, 3, 16381, 4096
+    gen = torch.Generator().manual_seed(23)
+    qI = torch.randn((1, n_q, 64, 128), generator=gen).to(torch.bfloat16)
+    KI = torch.randn((1, n_comp, 128), generator=gen).to(torch.bfloat16)
+    w = torch.nn.functional.softplus(torch.randn((1, n_q, 64), generator=gen))
+    idx, sc = L.csa_index_topk(g(qI), g(w), g(KI), t0, m, k, score=True)
+    torch.cuda.synchronize()
+    want, osc, vis = _oracle_index(qI[0], w[0], KI[0], np.arange(t0, t0 + n_q), m, k)
+    assert list(vis) == [4095, 4095, 4096]
+    assert_index_sets(idx[0].cpu().numpy(), want, osc, vis, k, "rows")
+
+
+@pytest.mark.parametrize("dtype,n_q", [(torch.bfloat16, 5), (torch.float32, 2)])
+def test_index_topk_long_lists_general_path(dtype, n_q):
+    # more than 2048 candidates scored by the 4-query MFMA kernel or the
+    # generic kernel: the multi-stage selection without group maxima
+    say(f"index long lists general path dtype={dtype} n_q={n_q}")
+    m, k, b = 4, 256, 2
+    t0 = 12000
+    n_comp = (t0 + n_q) // m
+    gen = torch.Generator().manual_seed(24)
+    qI = torch.randn((b, n_q, 64, 128), generator=gen).to(dtype)
+    KI = torch.randn((b, n_comp, 128), generator=gen).to(dtype)
+    w = torch.nn.functional.softplus(torch.randn((b, n_q, 64), generator=gen))
+    idx = L.csa_index_topk(g(qI), g(w), g(KI), t0, m, k)
+    torch.cuda.synchronize()
+    for s in range(b):
+        want, osc, vis = _oracle_index(qI[s], w[s], KI[s], np.arange(t0, t0 + n_q), m, k)
+        assert_index_sets(idx[s].cpu().numpy(), want, osc, vis, k, f"seq {s}")
+
+
 def test_index_topk_prefill_full_size_sampled():
     say("index prefill n=8192 (sampled queries)")
     d = synth.prefill_inputs()
