@@ -18,6 +18,19 @@
 
 namespace csa {
 
+// LDS DMA of 16 bytes per lane: lane l's bytes land at LDS byte address
+// lds + 16 l (lds is wave-uniform, passed in M0).  Written as inline asm so
+// that the compiler does not track these writes: the kernels that use it
+// order them with explicit vmcnt waits (wait_vmem) before reading the LDS.
+__device__ __forceinline__ void dma_chunk16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Generic scoring (any dtype, any head count / dimension): one thread per
 // (query, key).  Used for float32 and for shapes the MFMA kernel does not
@@ -169,38 +182,55 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
 }
 
 // ---------------------------------------------------------------------------
-// Streaming MFMA scoring for few queries (decode), bf16.  Nothing is shared
-// between waves, so there is no LDS and no barrier: each wave keeps its
+// Streaming MFMA scoring for few queries (decode), bf16.  Each wave keeps its
 // query's 32*NHB x c_I operand in registers and walks 32-key tiles of its
-// workgroup's key range (tiles wave, wave+4, ...), loading the B operands of
-// the next two tiles straight from HBM while the MFMAs of the current one
-// run.
-// Per key the only traffic is its c_I bf16 values and one float score.  The
-// kernel also records, per group of 128 keys, the largest score (as an
+// workgroup's keys on its own, with no barrier until the end.  A tile's 32
+// key rows are one contiguous block in HBM; the wave copies it whole into an
+// LDS ring of its own with 1 KiB LDS-DMA loads (global_load_lds_dwordx4),
+// D - 1 tiles ahead of the MFMAs, and reads the B operands back from LDS.
+// (Loading the operands straight into registers makes every load instruction
+// touch 32 rows x 32 bytes, which HBM serves well below its contiguous
+// rate.)  The DMA writes 16-byte chunks in lane order, so the permutation that
+// keeps the operand reads free of bank conflicts is applied on the global
+// side: LDS chunk p of key r holds source chunk p ^ f(r).
+// Per key the only traffic is its c_I bf16 values and one float score; the
+// scores collect in LDS and leave in one pass at the end.  The kernel also
+// records, per group of up to 256 keys, the largest score (as an
 // order-preserving key): the k-th largest of these group maxima bounds the
 // k-th largest score from below, which lets selection discard almost every
 // key in one pass.
 // ---------------------------------------------------------------------------
-template <int NHB, int KS>
+template <int NHB, int KS, int D>
 __global__ __launch_bounds__(256) void index_scores_stream(
     const bf16_t* __restrict__ qI, const float* __restrict__ w, const bf16_t* __restrict__ KI,
-    int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t cand_per_wg,
+    int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
     float* __restrict__ scores, uint32_t* __restrict__ gmax, int64_t ld_gmax) {
   constexpr int CI = KS * 16;
   constexpr int NH = NHB * 32;
-  const int wave = threadIdx.x >> 6;
+  constexpr int NCH = 2 * KS;     // 16-byte chunks per key row
+  constexpr int KPI = 64 / NCH;   // key rows per 1 KiB DMA instruction
+  constexpr int SDIV = 16 / NCH;  // f(r) = (r / SDIV) % NCH spreads 16 rows over 64 banks
+  constexpr int TU4 = 32 * NCH;   // 16-byte chunks per tile
+  static_assert(NCH == 8 || NCH == 16, "c_I must be 64 or 128");
+  __shared__ uint4 ring[4][D][TU4];
+  __shared__ float sbuf[8192];  // the workgroup's scores, written out at the end
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const int64_t qrow = blockIdx.x;
   const int64_t bi = blockIdx.z;
   int64_t vis = (t0 + qrow + 1) / m;
   if (vis > n_comp) vis = n_comp;
-  const int64_t c0 = (int64_t)blockIdx.y * cand_per_wg;
-  int64_t c1 = c0 + cand_per_wg;
-  if (c1 > vis) c1 = vis;
-  const int64_t first = c0 + 32 * wave;
+  // The row's keys are dealt to the gridDim.y workgroups in 128-key chunks,
+  // round robin (chunk c goes to workgroup c % gridDim.y), so that the
+  // workgroups in flight read neighbouring chunks rather than the same
+  // offset of distant ranges; within a chunk, wave w takes keys 32 w .. +32.
+  const int64_t first = 128 * (int64_t)blockIdx.y + 32 * wave;  // the wave's first key
+  const int64_t kstep = 128 * (int64_t)gridDim.y;                // distance between its tiles
+  const int64_t c1 = vis;
   // group maxima (order-preserving keys, 0 = no key): lanes 4q..4q+3 of a
   // wave form one group, i.e. 4 keys of each of its 32-key tiles; every
-  // group of the grid is written, empty ones as 0
+  // group of the grid is written, empty ones as 0.  Any partition of the keys
+  // into groups gives a valid bound.
   uint32_t gm = 0;
   auto write_gmax = [&]() {
     if (gmax == nullptr) return;
@@ -209,10 +239,39 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     if (l < 32 && (l & 3) == 0)
       gmax[(bi * n_q + qrow) * ld_gmax + (int64_t)blockIdx.y * 32 + wave * 8 + (l >> 2)] = gm;
   };
-  if (first >= c1) {
+  if (vis <= 0) {  // uniform over the workgroup
     write_gmax();
     return;
   }
+  // at most 64 tiles per wave (128 * gridDim.y * 64 >= vis, set by the host)
+  const int ntiles = first >= c1 ? 0 : (int)((c1 - first + kstep - 1) / kstep);
+
+  const bf16_t* kbase = KI + bi * comp_bs;
+  const int64_t lastkey = c1 - 1;
+  // DMA: instruction i, lane l fills LDS chunk 64 i + l of the tile = chunk
+  // l % NCH of row i * KPI + l / NCH, from source chunk (l % NCH) ^ f(row)
+  int src_off[KS];
+#pragma unroll
+  for (int i = 0; i < KS; ++i) {
+    const int r = i * KPI + l / NCH;
+    src_off[i] = r * CI + (((l % NCH) ^ ((r / SDIV) % NCH)) * 8);
+  }
+  auto issue = [&](int j, int slot) {
+    // rows past the last key re-read the last key (in bounds; their scores
+    // are dropped), and so does a tile wholly past the end
+    int64_t kb = first + kstep * j;
+    kb = kb < lastkey ? kb : lastkey;
+    const int room = (int)(lastkey - kb < 32 ? lastkey - kb : 32);
+    const uint32_t lds = (uint32_t)(uintptr_t)&ring[wave][slot][0];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int r = i * KPI + l / NCH;
+      const bf16_t* src = kbase + kb * CI + (r <= room ? src_off[i] : room * CI + (src_off[i] - r * CI));
+      dma_chunk16(src, lds + 1024 * i);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) issue(j, j);
 
   bf16x8 qa[NHB][KS];
   float wv[NHB][16];
@@ -227,30 +286,19 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     for (int r = 0; r < 16; ++r) wv[mb][r] = w[qoff + mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)];
   }
 
-  const bf16_t* kbase = KI + bi * comp_bs;
   float* srow = scores + (bi * n_q + qrow) * n_comp;
-  const int64_t lastkey = c1 - 1;
-  // lane's 16-byte slice of key (tile + l % 32), dims 8 * (l / 32) + 16 * ks
-  auto load_tile = [&](int64_t kb, uint4 (&dst)[KS]) {
-    int64_t key = kb + (l & 31);
-    key = key < lastkey ? key : lastkey;
-    const bf16_t* kp = kbase + key * CI + 8 * (l >> 5);
+  // B operand of 32x32x16 step ks: lane l holds dims 16 ks + 8 (l / 32) .. +8 of key l % 32
+  const int rr = l & 31;
+  int rd_off[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const uint4*>(kp + ks * 16);
-  };
-  // three tiles in registers: the current one and two in flight
-  uint4 cur[KS], nxt[KS], nx2[KS];
-  load_tile(first, cur);
-  if (first + 128 < c1) load_tile(first + 128, nxt);
-  for (int64_t kb = first; kb < c1; kb += 128) {
-    const bool more = kb + 128 < c1;
-    if (kb + 256 < c1) load_tile(kb + 256, nx2);
+  for (int ks = 0; ks < KS; ++ks) rd_off[ks] = rr * NCH + ((2 * ks + (l >> 5)) ^ ((rr / SDIV) % NCH));
+  auto compute = [&](int j, int slot) {
     f32x16 acc[NHB];
 #pragma unroll
     for (int mb = 0; mb < NHB; ++mb) acc[mb] = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, cur[ks]);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, ring[wave][slot][rd_off[ks]]);
 #pragma unroll
       for (int mb = 0; mb < NHB; ++mb)
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], bv, acc[mb], 0, 0, 0);
@@ -261,20 +309,35 @@ __global__ __launch_bounds__(256) void index_scores_stream(
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc = fmaf(fmaxf(acc[mb][r], 0.f), wv[mb][r], sc);
     sc += __shfl_xor(sc, 32, 64);
-    const int64_t key = kb + l;
-    if (l < 32 && key < c1) {
-      srow[key] = sc;
-      gm = max(gm, f2key(sc));
-    }
-    if (more) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        cur[ks] = nxt[ks];
-        nxt[ks] = nx2[ks];
-      }
-    }
+    const int64_t key = first + kstep * j + l;
+    if (l < 32) sbuf[128 * j + 32 * wave + l] = sc;
+    if (l < 32 && key < c1) gm = max(gm, f2key(sc));
+  };
+  // tile j sits in slot j % D; step j first issues tile j + D - 1 into the
+  // slot step j - 1 has finished reading.  Every step issues exactly one tile
+  // (those past the last tile re-read the last key row: they keep the wait
+  // counts static and cost no HBM traffic), so before step j's reads the
+  // D - 1 tiles issued after tile j ((D - 1) KS loads) may still be in
+  // flight; loads complete in order, and a pending score store only makes the
+  // wait stricter.
+  int slot = 0;
+  for (int j = 0; j < ntiles; ++j) {
+    issue(j + D - 1, slot == 0 ? D - 1 : slot - 1);
+    wait_vmem<(D - 1) * KS>();
+    compute(j, slot);
+    slot = slot == D - 1 ? 0 : slot + 1;
   }
+  wait_vmem<0>();
   write_gmax();
+  // The scores leave in one pass of full-line stores per workgroup: storing
+  // each tile's 128 bytes as it is scored interleaves small writes with the
+  // key stream and costs about a tenth of the kernel's time.
+  __syncthreads();
+  const int64_t nch = (c1 - 128 * (int64_t)blockIdx.y + kstep - 1) / kstep;  // the workgroup's chunks
+  for (int e = threadIdx.x; e < nch * 128; e += 256) {
+    const int64_t key = 128 * ((int64_t)blockIdx.y + (int64_t)gridDim.y * (e >> 7)) + (e & 127);
+    if (key < c1) srow[key] = sbuf[e];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -772,8 +835,9 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // keys per workgroup of the streaming (decode) scoring kernel, and its
 // group maxima per workgroup (4 waves x 8 groups)
-constexpr int64_t kStreamKeysPerWG = 4096;
+constexpr int64_t kStreamKeysPerWG = 8192;  // the scorer's LDS score buffer holds this many
 constexpr int64_t kStreamGroupsPerWG = 32;
+constexpr int kStreamRing = 3;  // LDS ring slots per wave of the streaming scorer
 
 // Workspace: scores [rows, n_comp] f32 | len A, len B [rows] i64 |
 //            pairs A, pairs B [rows, cap] (u32 key + i32 idx each) |
@@ -836,8 +900,8 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
     const int64_t cpw = kStreamKeysPerWG;
     const int64_t nsplit = std::max<int64_t>(1, (vmax + cpw - 1) / cpw);
     dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
-    hipLaunchKernelGGL((index_scores_stream<NHB, KS>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
-                       (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, scores, gmax, ld_gmax);
+    hipLaunchKernelGGL((index_scores_stream<NHB, KS, kStreamRing>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
+                       (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, scores, gmax, ld_gmax);
     *gmax_used = gmax != nullptr;
   }
   return hipGetLastError();
