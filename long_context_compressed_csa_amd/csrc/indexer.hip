@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
 // side: LDS chunk p of key r holds source chunk p ^ f(r).
 // Per key the only traffic is its c_I bf16 values and one float score; the
 // scores collect in LDS and leave in one pass at the end.  The kernel also
-// records, per group of up to 256 keys, the largest score (as an
+// records, per group of up to 512 keys, the largest score (as an
 // order-preserving key): the k-th largest of these group maxima bounds the
 // k-th largest score from below, which lets selection discard almost every
 // key in one pass.
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   constexpr int TU4 = 32 * NCH;   // 16-byte chunks per tile
   static_assert(NCH == 8 || NCH == 16, "c_I must be 64 or 128");
   __shared__ uint4 ring[4][D][TU4];
-  __shared__ float sbuf[8192];  // the workgroup's scores, written out at the end
+  __shared__ float sbuf[16384];  // the workgroup's scores, written out at the end
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const int64_t qrow = blockIdx.x;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     write_gmax();
     return;
   }
-  // at most 64 tiles per wave (128 * gridDim.y * 64 >= vis, set by the host)
+  // at most 128 tiles per wave (128 * gridDim.y * 128 >= vis, set by the host)
   const int ntiles = first >= c1 ? 0 : (int)((c1 - first + kstep - 1) / kstep);
 
   const bf16_t* kbase = KI + bi * comp_bs;
@@ -833,11 +833,23 @@ constexpr int64_t kBlockChunk = 256 * kBlockR;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// keys per workgroup of the streaming (decode) scoring kernel, and its
-// group maxima per workgroup (4 waves x 8 groups)
-constexpr int64_t kStreamKeysPerWG = 8192;  // the scorer's LDS score buffer holds this many
+// The streaming (decode) scoring kernel: at most kStreamKeysPerWG keys per
+// workgroup (its LDS score buffer), 32 group maxima per workgroup (4 waves x
+// 8 groups), kStreamRing LDS ring slots per wave.  One workgroup fills a CU
+// (160 KiB of LDS), so each row's keys are split over enough workgroups for
+// about one per CU of the 256 on the chip (more when the buffer requires it,
+// fewer when the row has fewer 128-key chunks): a grid just above the CU
+// count would run a nearly empty second round.
+constexpr int64_t kStreamKeysPerWG = 16384;
 constexpr int64_t kStreamGroupsPerWG = 32;
-constexpr int kStreamRing = 3;  // LDS ring slots per wave of the streaming scorer
+constexpr int kStreamRing = 3;
+constexpr int64_t kStreamTargetWGs = 256;
+static int64_t stream_splits(int64_t b, int64_t n_q, int64_t vmax) {
+  const int64_t need = (vmax + kStreamKeysPerWG - 1) / kStreamKeysPerWG;
+  const int64_t want = kStreamTargetWGs / std::max<int64_t>(1, b * n_q);
+  const int64_t chunks = (vmax + 127) / 128;
+  return std::max<int64_t>(1, std::min(chunks, std::max(need, want)));
+}
 
 // Workspace: scores [rows, n_comp] f32 | len A, len B [rows] i64 |
 //            pairs A, pairs B [rows, cap] (u32 key + i32 idx each) |
@@ -852,7 +864,7 @@ static TopkLayout topk_layout(int64_t b, int64_t n_q, int64_t n_comp, int64_t k)
   const int64_t nch = (n_comp + kWaveChunk - 1) / kWaveChunk;
   L.nseg = nch;
   L.cap = nch > 1 ? nch * k : 0;
-  L.gcap = nch > 1 ? (n_comp + kStreamKeysPerWG - 1) / kStreamKeysPerWG * kStreamGroupsPerWG : 0;
+  L.gcap = nch > 1 ? stream_splits(b, n_q, n_comp) * kStreamGroupsPerWG : 0;  // grows with n_comp
   size_t off = 0;
   L.scores = off; off = align256(off + (size_t)rows * n_comp * 4);
   L.lenA = off; off = align256(off + (size_t)rows * 8);
@@ -897,8 +909,7 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
                        (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores);
   } else {
     // few queries (decode): split each query's keys over many workgroups
-    const int64_t cpw = kStreamKeysPerWG;
-    const int64_t nsplit = std::max<int64_t>(1, (vmax + cpw - 1) / cpw);
+    const int64_t nsplit = stream_splits(b, n_q, vmax);
     dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
     hipLaunchKernelGGL((index_scores_stream<NHB, KS, kStreamRing>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
                        (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, scores, gmax, ld_gmax);
@@ -961,7 +972,7 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
     // group maxima, a filtering pass per 2048-key segment, one exact merge
     uint32_t* tau = (uint32_t*)(W + L.tau);
     int32_t* cnt = (int32_t*)(W + L.cnt);
-    const int64_t G = std::max<int64_t>(1, (lmax + kStreamKeysPerWG - 1) / kStreamKeysPerWG) * kStreamGroupsPerWG;
+    const int64_t G = stream_splits(b, n_q, lmax) * kStreamGroupsPerWG;
     hipLaunchKernelGGL(topk_threshold, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows,
                        k, tau);
     hipLaunchKernelGGL(topk_filter, dim3((unsigned)((rows * nseg + 3) / 4)), dim3(256), 0, st, scores, n_comp, tau,
