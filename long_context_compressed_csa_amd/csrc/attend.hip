@@ -652,7 +652,10 @@ static int attend_nsplit(int64_t b, int64_t n_q, int64_t n_h, int64_t nmax) {
   const int64_t items = b * n_q * (n_h / kHG);
   if (items >= 512) return 1;
   int64_t ns = (1024 + items - 1) / items;
-  const int64_t cap = (nmax + 2 * kT - 1) / (2 * kT);  // at least two tiles per split
+  // at least eight tiles per split: a split pays a fixed cost (index
+  // compaction, the first gathers, a 128 KiB float partial written and
+  // merged again) that fewer tiles do not amortise
+  const int64_t cap = (nmax + 8 * kT - 1) / (8 * kT);
   if (ns > cap) ns = cap;
   if (ns < 1) ns = 1;
   if (ns > 64) ns = 64;
