@@ -22,8 +22,12 @@ namespace csa {
 // lds + 16 l (lds is wave-uniform, passed in M0).  Written as inline asm so
 // that the compiler does not track these writes: the kernels that use it
 // order them with explicit vmcnt waits (wait_vmem) before reading the LDS.
+// M0 is restored afterwards, since the compiler does not accept it as a
+// clobber.
 __device__ __forceinline__ void dma_chunk16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
 }
 // wait until at most N vector-memory operations of this wave are in flight
 template <int N>
@@ -70,12 +74,29 @@ __global__ __launch_bounds__(256) void index_scores_generic(
 //   A[i][k] : lane holds A[l%32][8*(l/32) + j]
 //   B[k][n] : lane holds B[8*(l/32) + j][l%32]
 //   D[i][n] : lane holds D[8*(r/4) + 4*(l/32) + r%4][l%32] in register r
+//
+// FUSED (QW == 4, at most 2048 candidates): the workgroup holds every score
+// of its four queries, in LDS rather than HBM, and each wave then selects
+// its query's top k from there and writes the final indices (and scores), as
+// the single-wave selection stage would from the score rows.
 // ---------------------------------------------------------------------------
-template <int NHB, int KS, int QW>
+template <int NT, int R>
+__device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const bool (&val)[R], int nval, int k,
+                                               bool (&sel)[R], uint32_t* red, uint32_t* pre);
+template <int NT, int R>
+__device__ __forceinline__ void segment_positions(const bool (&sel)[R], uint32_t (&pos)[R], uint32_t* pre);
+template <int R>
+__device__ __forceinline__ void wave_select_radix(const uint32_t (&key)[R], const bool (&val)[R], int nval, int k,
+                                                  bool (&sel)[R], uint32_t* hist);
+constexpr int kFusedMaxKeys = 2048;
+
+template <int NHB, int KS, int QW, int FUSED>
 __global__ __launch_bounds__(256) void index_scores_mfma(
     const bf16_t* __restrict__ qI, const float* __restrict__ w, const bf16_t* __restrict__ KI,
     int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t cand_per_wg,
-    int64_t n_qblocks, float* __restrict__ scores) {
+    int64_t n_qblocks, float* __restrict__ scores, int64_t k, int32_t* __restrict__ idx,
+    float* __restrict__ score_out) {
+  static_assert(!FUSED || QW == 4, "the fused selection takes one query per wave");
   constexpr int CI = KS * 16;
   constexpr int NH = NHB * 32;
   constexpr int SUB = 4 / QW;            // waves sharing one query
@@ -85,6 +106,8 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
   constexpr int LOADS = TN * U4_PER_ROW / 256;
   static_assert(LOADS >= 1 && (TN * U4_PER_ROW) % 256 == 0, "tile must split over 256 threads");
   __shared__ __attribute__((aligned(16))) unsigned char lds[TN * ROWB];
+  __shared__ float ssc[FUSED ? 4 : 1][FUSED ? kFusedMaxKeys : 1];   // FUSED: the queries' scores
+  __shared__ __attribute__((aligned(16))) uint32_t hist[FUSED ? 4 : 1][FUSED ? 256 : 4];   // FUSED: radix bins
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -105,7 +128,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
   const int64_t c0 = (int64_t)blockIdx.y * cand_per_wg;
   int64_t c1 = c0 + cand_per_wg;
   if (c1 > vis_wg) c1 = vis_wg;
-  if (c0 >= c1) return;
+  if (!FUSED && c0 >= c1) return;
 
   // query operand and head weights in registers
   bf16x8 qa[NHB][KS];
@@ -135,7 +158,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
                             : make_uint4(0, 0, 0, 0);
     }
   };
-  load_tile(c0);
+  if (c0 < c1) load_tile(c0);
   for (int64_t tb = c0; tb < c1; tb += TN) {
     __syncthreads();
 #pragma unroll
@@ -176,7 +199,41 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
         s2[nb] = s + __shfl_xor(s, 32, 64);
       }
       const int64_t cand = kb + l;
-      if (cand < vis_q) srow[cand] = (l < 32) ? s2[0] : s2[1];
+      if (cand < vis_q) {
+        if constexpr (FUSED) ssc[wave][cand] = (l < 32) ? s2[0] : s2[1];
+        else srow[cand] = (l < 32) ? s2[0] : s2[1];
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    // Each wave selects over its own query's scores (slot r, lane l holds
+    // entry 64 r + l): the top k, ties to the lower index, written in
+    // ascending index order and padded with -1.  The wave wrote these LDS
+    // words itself, so no barrier is needed.
+    constexpr int R = kFusedMaxKeys / 64;
+    const int len = (int)vis_q;
+    uint32_t key[R];
+    bool val[R], sel[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      val[r] = r * 64 + l < len;
+      key[r] = val[r] ? f2key(ssc[wave][r * 64 + l]) : 0u;
+    }
+    wave_select_radix<R>(key, val, len, (int)k, sel, hist[wave]);
+    uint32_t pos[R];
+    segment_positions<64, R>(sel, pos, nullptr);
+    if (qvalid) {
+      const int64_t row = bi * n_q + qrow;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (sel[r]) {
+          idx[row * k + pos[r]] = r * 64 + l;
+          if (score_out) score_out[row * k + pos[r]] = key2f(key[r]);
+        }
+      for (int64_t p = (len < k ? len : k) + l; p < k; p += 64) {
+        idx[row * k + p] = -1;
+        if (score_out) score_out[row * k + p] = 0.f;
+      }
     }
   }
 }
@@ -396,6 +453,9 @@ struct SegReduce {
 // scratch of 2 * NT/64 words (unused for NT == 64); `pre` is LDS scratch of
 // R * NT/64 words used for list-order ranks.
 template <int NT, int R>
+__device__ __forceinline__ void segment_take(const uint32_t (&key)[R], const bool (&val)[R], int k, uint32_t T,
+                                             bool (&sel)[R], uint32_t* red, uint32_t* pre, int parity);
+template <int NT, int R>
 __device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const bool (&val)[R], int nval, int k,
                                                bool (&sel)[R], uint32_t* red, uint32_t* pre) {
   const int tid = threadIdx.x % NT, wave = tid >> 6, l = tid & 63;
@@ -428,6 +488,15 @@ __device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const b
       if (c >= (uint32_t)k) T = cand;
     }
   }
+  segment_take<NT, R>(key, val, k, T, sel, red, pre, parity);
+}
+
+// Given T, the k-th largest key of the segment, flag the elements taken: keys
+// above T, then keys equal to T in list order until k are taken.
+template <int NT, int R>
+__device__ __forceinline__ void segment_take(const uint32_t (&key)[R], const bool (&val)[R], int k, uint32_t T,
+                                             bool (&sel)[R], uint32_t* red, uint32_t* pre, int parity) {
+  const int tid = threadIdx.x % NT, wave = tid >> 6, l = tid & 63;
   uint32_t gt = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) gt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(val[r] && key[r] > T));
@@ -462,6 +531,72 @@ __device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const b
     run += slot_total;
   }
   if (NT > 64) __syncthreads();   // pre[] is reused by the caller's compaction
+}
+
+// Top k of a segment held by one wave (R keys per lane, valid where val[],
+// nval of them, the same in every lane), by radix selection on 8-bit digits
+// from the top: each pass counts, in a 256-bin LDS histogram private to the
+// wave (hist, 256 words), the keys that share the digits fixed so far, and
+// fixes the next digit of the k-th largest key T.  Four passes of one atomic
+// per key replace the 32 single-bit steps of segment_select; the taking rule
+// is the same (segment_take).
+template <int R>
+__device__ __forceinline__ void wave_select_radix(const uint32_t (&key)[R], const bool (&val)[R], int nval, int k,
+                                                  bool (&sel)[R], uint32_t* hist) {
+  const int l = threadIdx.x & 63;
+  if (nval <= k) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sel[r] = val[r];
+    return;
+  }
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t need = (uint32_t)k;   // rank of T among the keys that match the prefix
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    reinterpret_cast<uint4*>(hist)[l] = make_uint4(0u, 0u, 0u, 0u);   // one wave's LDS ops stay in order
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (val[r] && (key[r] & pmask) == prefix) atomicAdd(&hist[(key[r] >> shift) & 255u], 1u);
+    const uint4 h = reinterpret_cast<const uint4*>(hist)[l];   // bins 4l .. 4l+3
+    // suf: keys whose digit is >= 4l (suffix sum over the lanes)
+    uint32_t suf = h.x + h.y + h.z + h.w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = (uint32_t)__shfl((int)suf, (l + o) & 63, 64);
+      if (l + o < 64) suf += v;
+    }
+    // the digit of T is the largest d with (keys of digit >= d) >= need; its
+    // lane is the highest with suf >= need (lane 0 always qualifies)
+    const uint64_t qual = __builtin_amdgcn_ballot_w64(suf >= need);
+    const int lt = 63 - __clzll(qual);
+    const uint32_t nxt = (uint32_t)__shfl((int)suf, (lt + 1) & 63, 64);
+    uint32_t above = lt == 63 ? 0u : nxt;   // keys with digit >= 4 lt + 4
+    const uint32_t b0 = (uint32_t)__shfl((int)h.x, lt, 64), b1 = (uint32_t)__shfl((int)h.y, lt, 64);
+    const uint32_t b2 = (uint32_t)__shfl((int)h.z, lt, 64), b3 = (uint32_t)__shfl((int)h.w, lt, 64);
+    uint32_t d;
+    if (above + b3 >= need) {
+      d = 3;
+    } else {
+      above += b3;
+      if (above + b2 >= need) {
+        d = 2;
+      } else {
+        above += b2;
+        if (above + b1 >= need) {
+          d = 1;
+        } else {
+          above += b1;
+          d = 0;
+        }
+      }
+    }
+    (void)b0;
+    need -= above;
+    prefix |= (uint32_t)(4 * lt + d) << shift;
+    pmask |= 255u << shift;
+  }
+  segment_take<64, R>(key, val, k, prefix, sel, nullptr, nullptr, 0);
 }
 
 // Compact the selected elements in list order: returns each element's output
@@ -898,15 +1033,19 @@ template <int NHB, int KS>
 static hipError_t launch_scores_mfma(const void* qI, const float* w, const void* KI, int64_t cbs,
                                      int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
                                      float* scores, uint32_t* gmax, int64_t ld_gmax, bool* gmax_used,
-                                     hipStream_t st) {
+                                     int64_t k, int32_t* idx, float* score_out, hipStream_t st) {
   const int64_t vmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
   *gmax_used = false;
   if (n_q >= 4) {
     const int64_t nqb = (n_q + 3) / 4;
     const int64_t cpw = ((vmax + 63) / 64) * 64;
     dim3 grid((unsigned)nqb, 1, (unsigned)b);
-    hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 4>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
-                       (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores);
+    if (idx != nullptr)   // every list fits one workgroup: selection fused (the caller checked)
+      hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 4, 1>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
+                         (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, idx, score_out);
+    else
+      hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 4, 0>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
+                         (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, nullptr, nullptr);
   } else {
     // few queries (decode): split each query's keys over many workgroups
     const int64_t nsplit = stream_splits(b, n_q, vmax);
@@ -928,14 +1067,18 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
   uint32_t* gmax = L.gcap > 0 ? (uint32_t*)(W + L.gmax) : nullptr;
   bool gmax_used = false;
   hipError_t err = hipSuccess;
-  if (n_comp > 0) {
+  // four or more queries whose lists fit one 2048-key segment: the scoring
+  // kernel selects as well (also when n_comp == 0: it writes the padding)
+  const bool mfma_shape = dtype == 1 && (nh == 32 || nh == 64 || nh == 128) && (cI == 64 || cI == 128);
+  const bool fused = mfma_shape && n_q >= 4 && n_comp <= kFusedMaxKeys;
+  if (n_comp > 0 || fused) {
     bool done = false;
     if (dtype == 1 && nh % 32 == 0 && cI % 16 == 0) {
       const int nhb = (int)(nh / 32), ks = (int)(cI / 16);
 #define CSA_SCORES_CASE(A, B)                                                                       \
   if (!done && nhb == A && ks == B) {                                                               \
     err = launch_scores_mfma<A, B>(qI, w, KI, cbs, b, n_q, t0, n_comp, m, scores, gmax, L.gcap,     \
-                                   &gmax_used, st);                                                 \
+                                   &gmax_used, k, fused ? idx : nullptr, score, st);                \
     done = true;                                                                                    \
   }
       CSA_SCORES_CASE(1, 4) CSA_SCORES_CASE(1, 8) CSA_SCORES_CASE(2, 4) CSA_SCORES_CASE(2, 8)
@@ -953,6 +1096,7 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
       err = hipGetLastError();
     }
     if (err != hipSuccess) return err;
+    if (fused && done) return hipSuccess;
   }
   const int64_t rows = b * n_q;
   int64_t lmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
