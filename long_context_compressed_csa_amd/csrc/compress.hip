@@ -232,9 +232,99 @@ __global__ __launch_bounds__(256) void compress_generic(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pooling compressor (no overlap), for blocks of many rows (HCA, m' = 128):
+// one workgroup per entry and CPW channels of V values.  Thread t takes
+// channel t % CPW and rows p, p+P, ... of the block (part p = t / CPW, P =
+// 256 / CPW parts), so the lanes of a wave read whole contiguous row
+// segments; NR rows per round are loaded together (row indices clamped, rows
+// past the block weighted 0) before any is used, with one running max / sum
+// / weighted sum per value.  The parts' states merge in part order through
+// LDS.
+// ---------------------------------------------------------------------------
+template <typename T, int V, int NR, int CPW>
+__global__ __launch_bounds__(256) void compress_pool(const T* __restrict__ C, const T* __restrict__ Z,
+                                                     const T* __restrict__ B, int64_t n, int c, int64_t m,
+                                                     T* __restrict__ out, int64_t obs) {
+  constexpr int P = 256 / CPW;
+  __shared__ float st[P - 1][3 * V][CPW];   // parts 1..P-1: max, sum, acc per value and channel
+  const int part = threadIdx.x / CPW, cl = threadIdx.x % CPW;
+  const int64_t e = blockIdx.x, s = blockIdx.z;
+  const int ch = blockIdx.y * CPW + cl;
+  const bool active = ch < c / V;
+  const int d0 = (active ? ch : 0) * V;
+  const T* zrow = Z + (s * n + m * e) * (int64_t)c + d0;
+  const T* crow = C + (s * n + m * e) * (int64_t)c + d0;
+  const T* brow = B + d0;
+  float mx[V], sum[V], acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) { mx[v] = -INFINITY; sum[v] = 0.f; acc[v] = 0.f; }
+  for (int64_t r0 = part; r0 < m; r0 += P * NR) {
+    float z[NR][V], cv[NR][V], bv[NR][V];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      int64_t r = r0 + P * q;
+      r = r < m ? r : m - 1;
+      RowIO<T, V>::ld(zrow + r * (int64_t)c, z[q]);
+      RowIO<T, V>::ld(crow + r * (int64_t)c, cv[q]);
+      RowIO<T, V>::ld(brow + r * (int64_t)c, bv[q]);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float bm = mx[v];
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        z[q][v] = (r0 + P * q < m) ? z[q][v] + bv[q][v] : -INFINITY;
+        bm = fmaxf(bm, z[q][v]);
+      }
+      const float sc = fast_exp(mx[v] - bm);   // bm is finite: row r0 < m exists
+      float sd = sum[v] * sc, ad = acc[v] * sc;
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        const float p = fast_exp(z[q][v] - bm);
+        sd += p;
+        ad = fmaf(p, cv[q][v], ad);
+      }
+      mx[v] = bm;
+      sum[v] = sd;
+      acc[v] = ad;
+    }
+  }
+  if (part > 0) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      st[part - 1][v][cl] = mx[v];
+      st[part - 1][V + v][cl] = sum[v];
+      st[part - 1][2 * V + v][cl] = acc[v];
+    }
+  }
+  __syncthreads();
+  if (part == 0 && active) {
+    for (int w = 0; w < P - 1; ++w) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float om = st[w][v][cl];
+        if (om == -INFINITY) continue;   // that part saw no rows
+        const float nm = fmaxf(mx[v], om);
+        const float a = fast_exp(mx[v] - nm), b = fast_exp(om - nm);
+        sum[v] = sum[v] * a + st[w][V + v][cl] * b;
+        acc[v] = acc[v] * a + st[w][2 * V + v][cl] * b;
+        mx[v] = nm;
+      }
+    }
+    float res[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) res[v] = acc[v] / sum[v];
+    RowIO<T, V>::st(out + s * obs + e * (int64_t)c + d0, res);
+  }
+}
+
 }  // namespace csa
 
 namespace csa {
+
+constexpr int kPoolChannels = 64;   // channels (of 16 bytes) per workgroup of the pooling kernel
+constexpr int kPoolRows = 8;        // rows per thread and round
 
 template <typename T>
 static hipError_t launch_compress_t(const void* Ca, const void* Cb, const void* Za, const void* Zb,
@@ -254,6 +344,14 @@ static hipError_t launch_compress_t(const void* Ca, const void* Cb, const void* 
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL((compress_overlap_fixed<T, 4>), dim3((unsigned)blocks), dim3(256), 0, st,
                        ca, cb, za, zb, ba, bb, pcb, pzb, n, (int)c, ne, total, o, obs);
+    return hipGetLastError();
+  }
+  if (!overlap && m >= 32 && c % V == 0) {
+    const int CH = (int)(c / V);
+    constexpr int CPW = kPoolChannels;
+    dim3 grid((unsigned)ne, (unsigned)((CH + CPW - 1) / CPW), (unsigned)b);
+    hipLaunchKernelGGL((compress_pool<T, V, kPoolRows, CPW>), grid, dim3(256), 0, st, ca, za, ba, n, (int)c, m,
+                       o, obs);
     return hipGetLastError();
   }
   // generic path: rows split over P parts of one workgroup

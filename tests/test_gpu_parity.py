@@ -227,6 +227,38 @@ def test_index_topk_long_lists_exact_ties(n_comp, k, bump):
     assert idx[0, 0].cpu().numpy().tolist() == want[0].tolist()
 
 
+@pytest.mark.parametrize("n_distinct,k", [(1, 300), (3, 700), (17, 512)])
+def test_index_topk_fused_selection_ties(n_distinct, k):
+    # four or more queries whose lists fit one segment select inside the
+    # scoring kernel: keys drawn from a few distinct rows make long runs of
+    # exactly equal scores around the k-th, which the lower indices must win
+    say(f"index fused selection ties n_distinct={n_distinct} k={k}")
+    m, n_q, n_comp = 1, 9, 2048
+    t0 = n_comp - n_q
+    gen = torch.Generator().manual_seed(25)
+    rows = torch.randn((n_distinct, 128), generator=gen)
+    KI = rows[torch.randint(0, n_distinct, (n_comp,), generator=gen)].to(torch.bfloat16)
+    qI = torch.randn((n_q, 64, 128), generator=gen).to(torch.bfloat16)
+    w = torch.nn.functional.softplus(torch.randn((n_q, 64), generator=gen))
+    idx = L.csa_index_topk(g(qI), g(w), g(KI), t0, m, k)
+    torch.cuda.synchronize()
+    want, osc, vis = _oracle_index(qI, w, KI, np.arange(t0, t0 + n_q), m, k)
+    # equal keys give bit-equal scores on both sides, so the sets must agree exactly
+    assert np.array_equal(idx[0].cpu().numpy(), want)
+
+
+def test_index_topk_fused_nothing_visible():
+    # no entry is complete for any query: every index is padding
+    say("index fused, no visible entries")
+    m, n_q, k = 8, 4, 16
+    qI = torch.randn((n_q, 64, 128)).to(torch.bfloat16)
+    KI = torch.zeros((1, 128), dtype=torch.bfloat16)
+    w = torch.ones((n_q, 64))
+    idx = L.csa_index_topk(g(qI), g(w), g(KI), 0, m, k, n_comp=0)
+    torch.cuda.synchronize()
+    assert (idx.cpu() == -1).all()
+
+
 def test_index_topk_long_lists_rows_differ():
     # few queries whose visible counts differ (4095, 4095, 4096 entries)
     say("index long lists, rows with different visibility")
