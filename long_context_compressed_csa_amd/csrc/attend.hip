@@ -128,12 +128,12 @@ __global__ __launch_bounds__(256) void attend_generic(
 //                      MFMAs, which do not depend on them.
 // A lane's 32x32 A operand (head l%32, entries 8(l/32)..+7) is its own 4
 // weights of that head plus the 4 held by lane l^16, exchanged with one
-// v_permlane16_swap per register.  LDS rows are 1024 + 64 bytes apart and
-// the four 16-byte chunks of every 64-byte column block of row r are
-// XOR-permuted by (r/4)%4: with gfx950's 64 LDS banks both the b128 row
-// reads (16 lanes = 16 consecutive rows) and the transposed reads (16 lanes
-// = 4 rows x 4 chunks) are conflict-free, and column block nb stays at the
-// constant offset 64*nb.
+// v_permlane16_swap per register.  A tile is stored column-block major: the
+// 64-byte column block b of all 16 rows fills 1 KiB at b * 1024, and inside
+// it chunk c of row r sits at c * 256 + (r ^ 4c) * 16.  One gather
+// instruction then fills one block with 16 B per lane, and with gfx950's 64
+// LDS banks both the b128 row reads (16 lanes = 16 rows of one chunk) and the
+// transposed reads (16 lanes = 4 rows x 4 chunks) are conflict-free.
 // ---------------------------------------------------------------------------
 constexpr int kC = 512;
 constexpr int kHG = 64;              // heads per head group
