@@ -30,72 +30,72 @@ __global__ __launch_bounds__(256) void compress_overlap_fixed(
     int64_t total, T* __restrict__ out, int64_t obs) {
   constexpr int V = Vec16<T>::N;
   const int CH = c / V;
-  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= total) return;
-  const int ch = (int)(u % CH);
-  const int64_t rest = u / CH;
-  const int64_t e = rest % ne;
-  const int64_t s = rest / ne;
-  const int d0 = ch * V;
-  const int64_t seq = s * n * (int64_t)c;
-
-  float za[M][V], ca[M][V], zb[M][V], cb[M][V], ba[M][V], bb[M][V];
-  const T* zap = Za + seq + (M * e) * (int64_t)c + d0;
-  const T* cap = Ca + seq + (M * e) * (int64_t)c + d0;
+  // grid-stride over (sequence, entry, channel) units.  When the stride is a
+  // multiple of CH (c = 512 and 128: 256 threads per block), a thread keeps
+  // its channel and loads that channel's bias rows once.
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  float ba[M][V], bb[M][V];
+  int chb = -1;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += stride) {
+    const int ch = (int)(u % CH);
+    const int d0 = ch * V;
+    if (ch != chb) {
 #pragma unroll
-  for (int j = 0; j < M; ++j) {
-    Vec16<T>::ld(zap + j * (int64_t)c, za[j]);
-    Vec16<T>::ld(cap + j * (int64_t)c, ca[j]);
-  }
-  const bool hasb = (e > 0) || (pZb != nullptr);
-  if (hasb) {
-    const T* zbp = e > 0 ? Zb + seq + (M * (e - 1)) * (int64_t)c + d0 : pZb + s * M * (int64_t)c + d0;
-    const T* cbp = e > 0 ? Cb + seq + (M * (e - 1)) * (int64_t)c + d0 : pCb + s * M * (int64_t)c + d0;
+      for (int j = 0; j < M; ++j) {
+        Vec16<T>::ld(Ba + j * (int64_t)c + d0, ba[j]);
+        Vec16<T>::ld(Bb + j * (int64_t)c + d0, bb[j]);
+      }
+      chb = ch;
+    }
+    const int64_t rest = u / CH;
+    const int64_t e = rest % ne;
+    const int64_t s = rest / ne;
+    const int64_t seq = s * n * (int64_t)c;
+    float za[M][V], ca[M][V], zb[M][V], cb[M][V];
+    const T* zap = Za + seq + (M * e) * (int64_t)c + d0;
+    const T* cap = Ca + seq + (M * e) * (int64_t)c + d0;
+    // block e-1 of stream b, or the caller's previous block; at the sequence
+    // start with no previous block, rows of block e stand in (weight 0)
+    const bool hasb = (e > 0) || (pZb != nullptr);
+    const T* zbp = e > 0 ? Zb + seq + (M * (e - 1)) * (int64_t)c + d0
+                         : (pZb != nullptr ? pZb + s * M * (int64_t)c + d0 : zap);
+    const T* cbp = e > 0 ? Cb + seq + (M * (e - 1)) * (int64_t)c + d0
+                         : (pCb != nullptr ? pCb + s * M * (int64_t)c + d0 : cap);
 #pragma unroll
     for (int j = 0; j < M; ++j) {
+      Vec16<T>::ld(zap + j * (int64_t)c, za[j]);
+      Vec16<T>::ld(cap + j * (int64_t)c, ca[j]);
       Vec16<T>::ld(zbp + j * (int64_t)c, zb[j]);
       Vec16<T>::ld(cbp + j * (int64_t)c, cb[j]);
     }
-  }
+    float res[V];
 #pragma unroll
-  for (int j = 0; j < M; ++j) {
-    Vec16<T>::ld(Ba + j * (int64_t)c + d0, ba[j]);
-    Vec16<T>::ld(Bb + j * (int64_t)c + d0, bb[j]);
-  }
-  float res[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < M; ++j) {
-      za[j][v] += ba[j][v];
-      mx = fmaxf(mx, za[j][v]);
-    }
-    if (hasb) {
+    for (int v = 0; v < V; ++v) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < M; ++j) {
-        zb[j][v] += bb[j][v];
+        za[j][v] += ba[j][v];
+        mx = fmaxf(mx, za[j][v]);
+        zb[j][v] = hasb ? zb[j][v] + bb[j][v] : -INFINITY;
         mx = fmaxf(mx, zb[j][v]);
       }
-    }
-    float sum = 0.f, acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < M; ++j) {
-      const float p = fast_exp(za[j][v] - mx);
-      sum += p;
-      acc = fmaf(p, ca[j][v], acc);
-    }
-    if (hasb) {
+      float sum = 0.f, acc = 0.f;
 #pragma unroll
       for (int j = 0; j < M; ++j) {
-        const float p = fast_exp(zb[j][v] - mx);
+        const float p = fast_exp(za[j][v] - mx);
+        sum += p;
+        acc = fmaf(p, ca[j][v], acc);
+      }
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        const float p = fast_exp(zb[j][v] - mx);   // 0 for the padded block -1
         sum += p;
         acc = fmaf(p, cb[j][v], acc);
       }
+      res[v] = acc / sum;
     }
-    res[v] = acc / sum;
+    Vec16<T>::st(out + s * obs + e * (int64_t)c + d0, res);
   }
-  Vec16<T>::st(out + s * obs + e * (int64_t)c + d0, res);
 }
 
 // Row access for the generic kernel: VEC = Vec16<T>::N with 16-byte loads,
@@ -323,6 +323,7 @@ __global__ __launch_bounds__(256) void compress_pool(const T* __restrict__ C, co
 
 namespace csa {
 
+constexpr int kOverlapWGsPerCU = 16;  // grid cap of the overlapped compressor: workgroups per CU
 constexpr int kPoolChannels = 64;   // channels (of 16 bytes) per workgroup of the pooling kernel
 constexpr int kPoolRows = 8;        // rows per thread and round
 
@@ -341,7 +342,9 @@ static hipError_t launch_compress_t(const void* Ca, const void* Cb, const void* 
   T* o = (T*)out;
   if (overlap && m == 4 && c % V == 0) {
     const int64_t total = b * ne * (c / V);
-    const int64_t blocks = (total + 255) / 256;
+    // kOverlapWGsPerCU workgroups per CU of the 256, each thread looping over
+    // the units of one channel
+    const int64_t blocks = std::min<int64_t>((total + 255) / 256, 256 * kOverlapWGsPerCU);
     hipLaunchKernelGGL((compress_overlap_fixed<T, 4>), dim3((unsigned)blocks), dim3(256), 0, st,
                        ca, cb, za, zb, ba, bb, pcb, pzb, n, (int)c, ne, total, o, obs);
     return hipGetLastError();
