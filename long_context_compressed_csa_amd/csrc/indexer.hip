@@ -65,63 +65,148 @@ __global__ __launch_bounds__(256) void index_scores_generic(
 
 // ---------------------------------------------------------------------------
 // MFMA scoring, bf16.  NHB = heads / 32, KS = c_I / 16.  A workgroup has 4
-// waves; QW of them (1 or 4) carry distinct queries and the 4/QW waves that
-// share a query split each key tile.  The workgroup stages TN = 64*(4/QW)
-// keys per tile in LDS; each wave multiplies its query block by 64 keys with
-// v_mfma_f32_32x32x16_bf16 and reduces over heads in registers.
+// waves, one query each.  Key tiles of 64 rows (c_I x 2 bytes each, one
+// contiguous block in HBM) stream through a three-slot LDS ring filled with
+// 1 KiB LDS-DMA loads (global_load_lds_dwordx4, a quarter of each tile per
+// wave) two tiles ahead, with one barrier per tile; each wave multiplies its
+// query block by the 64 keys with v_mfma_f32_32x32x16_bf16 and reduces over
+// heads in registers.  LDS chunk p of key row r holds source chunk p ^ f(r),
+// which keeps the B operand reads free of bank conflicts.
 //
 // Operand layouts of the 32x32x16 MFMA (lane l, j < 8):
 //   A[i][k] : lane holds A[l%32][8*(l/32) + j]
 //   B[k][n] : lane holds B[8*(l/32) + j][l%32]
 //   D[i][n] : lane holds D[8*(r/4) + 4*(l/32) + r%4][l%32] in register r
 //
-// FUSED (QW == 4, at most 2048 candidates): the workgroup holds every score
+// FUSED (at most 2048 candidates): the workgroup holds every score
 // of its four queries, in LDS rather than HBM, and each wave then selects
 // its query's top k from there and writes the final indices (and scores), as
 // the single-wave selection stage would from the score rows.
 // ---------------------------------------------------------------------------
-template <int NT, int R>
-__device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const bool (&val)[R], int nval, int k,
-                                               bool (&sel)[R], uint32_t* red, uint32_t* pre);
-template <int NT, int R>
-__device__ __forceinline__ void segment_positions(const bool (&sel)[R], uint32_t (&pos)[R], uint32_t* pre);
-template <int R>
-__device__ __forceinline__ void wave_select_radix(const uint32_t (&key)[R], const bool (&val)[R], int nval, int k,
-                                                  bool (&sel)[R], uint32_t* hist);
 constexpr int kFusedMaxKeys = 2048;
 
-template <int NHB, int KS, int QW, int FUSED>
+// ---------------------------------------------------------------------------
+// Single-wave selection.  The wave holds a list of up to 64 R elements: slot r
+// of lane l is element 64 r + l; its key (the order-preserving image of a
+// score) is 0 for an empty slot, and every finite score's key is >= 1.
+// Counts are per-lane VALU sums reduced with six bit ballots, and selections
+// are per-lane bit masks, so that nothing of size R lives in scalar
+// registers.
+// ---------------------------------------------------------------------------
+// Wave sum of a per-lane count below 64.
+__device__ __forceinline__ uint32_t wave_sum_small(uint32_t c) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) t += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64((c >> b) & 1u)) << b;
+  return t;
+}
+// Keys >= cand over the wave (cand >= 1, so empty slots never count).
+template <int R>
+__device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[R], uint32_t cand) {
+  static_assert(R < 64, "per-lane counts must stay below 64");
+  uint32_t c = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) c += key[r] >= cand ? 1u : 0u;
+  return wave_sum_small(c);
+}
+// The k-th largest key T of the list (more than k non-empty slots): the
+// largest T with at least k keys >= T, found bit by bit from the top below
+// the common prefix of the largest and smallest key.
+template <int R>
+__device__ __forceinline__ uint32_t wave_kth(const uint32_t (&key)[R], int k) {
+  uint32_t hi = 0, lo = 0xffffffffu;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (key[r] != 0u) { hi = max(hi, key[r]); lo = min(lo, key[r]); }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+  }
+  const uint32_t diff = hi ^ lo;
+  if (diff == 0) return hi;
+  const int top = 31 - __clz(diff);
+  uint32_t T = top == 31 ? 0u : (hi >> (top + 1)) << (top + 1);
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    if (wave_count_ge(key, cand) >= (uint32_t)k) T = cand;
+  }
+  return T;
+}
+// The top k of the list (nval non-empty slots, the same in every lane): keys
+// above the k-th largest T, then keys equal to T in list order until k are
+// taken (ties go to the lower index).  Returns the lane's slots as a bit mask.
+template <int R>
+__device__ __forceinline__ uint32_t wave_select(const uint32_t (&key)[R], int nval, int k) {
+  static_assert(R <= 32, "one mask bit per slot");
+  uint32_t sel = 0;
+  if (nval <= k) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sel |= (key[r] != 0u ? 1u : 0u) << r;
+    return sel;
+  }
+  const uint32_t T = wave_kth(key, k);
+  const uint32_t gt = T == 0xffffffffu ? 0u : wave_count_ge(key, T + 1);
+  const uint32_t eq = wave_count_ge(key, T) - gt;
+  const uint32_t need = (uint32_t)k - gt;
+#pragma unroll
+  for (int r = 0; r < R; ++r) sel |= (key[r] > T ? 1u : 0u) << r;
+  if (eq <= need) {   // every tie is taken (the usual case: T is one key)
+#pragma unroll
+    for (int r = 0; r < R; ++r) sel |= (key[r] == T ? 1u : 0u) << r;
+  } else {
+    uint32_t run = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(key[r] == T);
+      const uint32_t before = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (key[r] == T && before < need) sel |= 1u << r;
+      run += (uint32_t)__popcll(m);
+    }
+  }
+  return sel;
+}
+// Output positions of the selected slots, compacted in list order.
+template <int R>
+__device__ __forceinline__ void wave_positions(uint32_t sel, uint32_t (&pos)[R]) {
+  uint32_t run = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64((sel >> r) & 1u);
+    pos[r] = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    run += (uint32_t)__popcll(m);
+  }
+}
+
+template <int NHB, int KS, int FUSED>
 __global__ __launch_bounds__(256) void index_scores_mfma(
     const bf16_t* __restrict__ qI, const float* __restrict__ w, const bf16_t* __restrict__ KI,
     int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t cand_per_wg,
     int64_t n_qblocks, float* __restrict__ scores, int64_t k, int32_t* __restrict__ idx,
     float* __restrict__ score_out) {
-  static_assert(!FUSED || QW == 4, "the fused selection takes one query per wave");
   constexpr int CI = KS * 16;
   constexpr int NH = NHB * 32;
-  constexpr int SUB = 4 / QW;            // waves sharing one query
-  constexpr int TN = 64 * SUB;           // keys per LDS tile
-  constexpr int ROWB = CI * 2 + 16;      // padded LDS row (bytes): conflict-free b128 reads
-  constexpr int U4_PER_ROW = CI / 8;     // 16-byte pieces per key row
-  constexpr int LOADS = TN * U4_PER_ROW / 256;
-  static_assert(LOADS >= 1 && (TN * U4_PER_ROW) % 256 == 0, "tile must split over 256 threads");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[TN * ROWB];
+  constexpr int TN = 64;                 // keys per tile
+  constexpr int NCH = 2 * KS;            // 16-byte chunks per key row
+  constexpr int KPI = 64 / NCH;          // key rows per 1 KiB DMA instruction
+  constexpr int DPW = TN / KPI / 4;      // DMA instructions per wave and tile
+  constexpr int SDIV = 16 / NCH;         // f(r) = (r / SDIV) % NCH spreads 16 rows over 64 banks
+  static_assert(NCH == 8 || NCH == 16, "c_I must be 64 or 128");
+  __shared__ uint4 ring[3][TN * NCH];
   __shared__ float ssc[FUSED ? 4 : 1][FUSED ? kFusedMaxKeys : 1];   // FUSED: the queries' scores
-  __shared__ __attribute__((aligned(16))) uint32_t hist[FUSED ? 4 : 1][FUSED ? 256 : 4];   // FUSED: radix bins
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   // heaviest (latest) query blocks first: causal work grows with position
   const int64_t qb = n_qblocks - 1 - blockIdx.x;
   const int64_t bi = blockIdx.z;
-  const int64_t qrow = qb * QW + (wave % QW);
-  const int sub = wave / QW;
+  const int64_t qrow = qb * 4 + wave;
   const bool qvalid = qrow < n_q;
 
   int64_t vis_q = qvalid ? (t0 + qrow + 1) / m : 0;
   if (vis_q > n_comp) vis_q = n_comp;
-  int64_t last = qb * QW + QW - 1;
+  int64_t last = qb * 4 + 3;
   if (last > n_q - 1) last = n_q - 1;
   int64_t vis_wg = (t0 + last + 1) / m;
   if (vis_wg > n_comp) vis_wg = n_comp;
@@ -129,6 +214,37 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
   int64_t c1 = c0 + cand_per_wg;
   if (c1 > vis_wg) c1 = vis_wg;
   if (!FUSED && c0 >= c1) return;
+  const int ntl = c0 < c1 ? (int)((c1 - c0 + TN - 1) / TN) : 0;   // uniform over the workgroup
+
+  const bf16_t* kbase = KI + bi * comp_bs;
+  const int64_t lastkey = c1 - 1;
+  // DMA of tile j into a ring slot: this wave's instructions i = DPW*wave ..
+  // +DPW; lane l fills chunk l % NCH of row i*KPI + l/NCH from source chunk
+  // (l % NCH) ^ f(row).  Rows past the last key re-read it (in bounds; their
+  // scores are not stored), and so does a tile wholly past the end.
+  int src_off[DPW];
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int r = (DPW * wave + d) * KPI + l / NCH;
+    src_off[d] = r * CI + (((l % NCH) ^ ((r / SDIV) % NCH)) * 8);
+  }
+  auto issue = [&](int j, int slot) {
+    int64_t kb = c0 + (int64_t)TN * j;
+    kb = kb < lastkey ? kb : lastkey;
+    const int room = (int)(lastkey - kb < TN ? lastkey - kb : TN);
+    const uint32_t lds = (uint32_t)(uintptr_t)&ring[slot][0];
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int i = DPW * wave + d;
+      const int r = i * KPI + l / NCH;
+      const bf16_t* src = kbase + kb * CI + (r <= room ? src_off[d] : room * CI + (src_off[d] - r * CI));
+      dma_chunk16(src, lds + 1024 * i);
+    }
+  };
+  if (ntl > 0) {
+    issue(0, 0);
+    issue(1, 1);
+  }
 
   // query operand and head weights in registers
   bf16x8 qa[NHB][KS];
@@ -144,33 +260,38 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
     for (int r = 0; r < 16; ++r)
       wv[mb][r] = qvalid ? w[qoff + mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)] : 0.f;
   }
+  // Consume the operand loads here, so that the compiler waits for them once,
+  // before the key loop: a wait it placed inside the loop would also drain
+  // the DMA loads in flight, which it does not count.
+#pragma unroll
+  for (int mb = 0; mb < NHB; ++mb) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qa[mb][ks]));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(wv[mb][r]));
+  }
 
-  const bf16_t* kbase = KI + bi * comp_bs;
   float* srow = scores + (bi * n_q + (qvalid ? qrow : 0)) * n_comp;
-  uint4 pre[LOADS];
-  auto load_tile = [&](int64_t tb) {
+  // B operand of step (ks, nb): lane l holds dims 16 ks + 8 (l / 32) .. +8 of
+  // key row 32 nb + l % 32
+  int rd_off[2][KS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int p = i * 256 + tid;
-      const int row = p / U4_PER_ROW, col = p % U4_PER_ROW;
-      const int64_t key = tb + row;
-      pre[i] = key < n_comp ? *reinterpret_cast<const uint4*>(kbase + key * CI + col * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-  };
-  if (c0 < c1) load_tile(c0);
-  for (int64_t tb = c0; tb < c1; tb += TN) {
-    __syncthreads();
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = nb * 32 + (l & 31);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int p = i * 256 + tid;
-      const int row = p / U4_PER_ROW, col = p % U4_PER_ROW;
-      *reinterpret_cast<uint4*>(lds + row * ROWB + col * 16) = pre[i];
-    }
+    for (int ks = 0; ks < KS; ++ks) rd_off[nb][ks] = r * NCH + ((2 * ks + (l >> 5)) ^ ((r / SDIV) % NCH));
+  }
+  // Step j: this wave's part of tile j has landed once at most the DPW loads
+  // of tile j + 1 are in flight (loads complete in order; a pending score
+  // store only makes the wait stricter); after the barrier every wave's part
+  // has, and every wave is done with tile j - 1, whose slot receives tile
+  // j + 2.
+  int slot = 0;
+  for (int j = 0; j < ntl; ++j) {
+    wait_vmem<DPW>();
     __syncthreads();
-    if (tb + TN < c1) load_tile(tb + TN);
-
-    const int64_t kb = tb + sub * 64;  // this wave's 64 keys
+    issue(j + 2, slot == 0 ? 2 : slot - 1);
+    const int64_t kb = c0 + (int64_t)TN * j;
     if (qvalid && kb < vis_q) {
       f32x16 acc[NHB][2];
 #pragma unroll
@@ -181,8 +302,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          const int row = sub * 64 + nb * 32 + (l & 31);
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lds + row * ROWB + ks * 32 + 16 * (l >> 5));
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, ring[slot][rd_off[nb][ks]]);
 #pragma unroll
           for (int mb = 0; mb < NHB; ++mb)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], bv, acc[mb][nb], 0, 0, 0);
@@ -204,7 +324,9 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
         else srow[cand] = (l < 32) ? s2[0] : s2[1];
       }
     }
+    slot = slot == 2 ? 0 : slot + 1;
   }
+  wait_vmem<0>();   // the look-ahead tiles past the end
   if constexpr (FUSED) {
     // Each wave selects over its own query's scores (slot r, lane l holds
     // entry 64 r + l): the top k, ties to the lower index, written in
@@ -213,20 +335,16 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
     constexpr int R = kFusedMaxKeys / 64;
     const int len = (int)vis_q;
     uint32_t key[R];
-    bool val[R], sel[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      val[r] = r * 64 + l < len;
-      key[r] = val[r] ? f2key(ssc[wave][r * 64 + l]) : 0u;
-    }
-    wave_select_radix<R>(key, val, len, (int)k, sel, hist[wave]);
+    for (int r = 0; r < R; ++r) key[r] = r * 64 + l < len ? f2key(ssc[wave][r * 64 + l]) : 0u;
+    const uint32_t sel = wave_select<R>(key, len, (int)k);
     uint32_t pos[R];
-    segment_positions<64, R>(sel, pos, nullptr);
+    wave_positions<R>(sel, pos);
     if (qvalid) {
       const int64_t row = bi * n_q + qrow;
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (sel[r]) {
+        if ((sel >> r) & 1u) {
           idx[row * k + pos[r]] = r * 64 + l;
           if (score_out) score_out[row * k + pos[r]] = key2f(key[r]);
         }
@@ -533,72 +651,6 @@ __device__ __forceinline__ void segment_take(const uint32_t (&key)[R], const boo
   if (NT > 64) __syncthreads();   // pre[] is reused by the caller's compaction
 }
 
-// Top k of a segment held by one wave (R keys per lane, valid where val[],
-// nval of them, the same in every lane), by radix selection on 8-bit digits
-// from the top: each pass counts, in a 256-bin LDS histogram private to the
-// wave (hist, 256 words), the keys that share the digits fixed so far, and
-// fixes the next digit of the k-th largest key T.  Four passes of one atomic
-// per key replace the 32 single-bit steps of segment_select; the taking rule
-// is the same (segment_take).
-template <int R>
-__device__ __forceinline__ void wave_select_radix(const uint32_t (&key)[R], const bool (&val)[R], int nval, int k,
-                                                  bool (&sel)[R], uint32_t* hist) {
-  const int l = threadIdx.x & 63;
-  if (nval <= k) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) sel[r] = val[r];
-    return;
-  }
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t need = (uint32_t)k;   // rank of T among the keys that match the prefix
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    reinterpret_cast<uint4*>(hist)[l] = make_uint4(0u, 0u, 0u, 0u);   // one wave's LDS ops stay in order
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (val[r] && (key[r] & pmask) == prefix) atomicAdd(&hist[(key[r] >> shift) & 255u], 1u);
-    const uint4 h = reinterpret_cast<const uint4*>(hist)[l];   // bins 4l .. 4l+3
-    // suf: keys whose digit is >= 4l (suffix sum over the lanes)
-    uint32_t suf = h.x + h.y + h.z + h.w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = (uint32_t)__shfl((int)suf, (l + o) & 63, 64);
-      if (l + o < 64) suf += v;
-    }
-    // the digit of T is the largest d with (keys of digit >= d) >= need; its
-    // lane is the highest with suf >= need (lane 0 always qualifies)
-    const uint64_t qual = __builtin_amdgcn_ballot_w64(suf >= need);
-    const int lt = 63 - __clzll(qual);
-    const uint32_t nxt = (uint32_t)__shfl((int)suf, (lt + 1) & 63, 64);
-    uint32_t above = lt == 63 ? 0u : nxt;   // keys with digit >= 4 lt + 4
-    const uint32_t b0 = (uint32_t)__shfl((int)h.x, lt, 64), b1 = (uint32_t)__shfl((int)h.y, lt, 64);
-    const uint32_t b2 = (uint32_t)__shfl((int)h.z, lt, 64), b3 = (uint32_t)__shfl((int)h.w, lt, 64);
-    uint32_t d;
-    if (above + b3 >= need) {
-      d = 3;
-    } else {
-      above += b3;
-      if (above + b2 >= need) {
-        d = 2;
-      } else {
-        above += b2;
-        if (above + b1 >= need) {
-          d = 1;
-        } else {
-          above += b1;
-          d = 0;
-        }
-      }
-    }
-    (void)b0;
-    need -= above;
-    prefix |= (uint32_t)(4 * lt + d) << shift;
-    pmask |= 255u << shift;
-  }
-  segment_take<64, R>(key, val, k, prefix, sel, nullptr, nullptr, 0);
-}
-
 // Compact the selected elements in list order: returns each element's output
 // position (valid where sel) through pos[].
 template <int NT, int R>
@@ -794,7 +846,6 @@ __global__ __launch_bounds__(256) void topk_filter(const float* __restrict__ sco
                                                    uint32_t* __restrict__ kout, int32_t* __restrict__ iout, int64_t ld_out,
                                                    int32_t* __restrict__ cnt) {
   constexpr int R = 32, CH = 64 * R;
-  __shared__ uint32_t pre_all[4][R + 1];
   const int sub = threadIdx.x >> 6, tid = threadIdx.x & 63;
   const int64_t gseg = (int64_t)blockIdx.x * 4 + sub;
   if (gseg >= n_rows * nseg) return;   // whole wave
@@ -808,7 +859,6 @@ __global__ __launch_bounds__(256) void topk_filter(const float* __restrict__ sco
   const int len = (int)len64;
   const uint32_t th = tau[row];
   uint32_t key[R];
-  bool val[R], sel[R];
   if (len > 0) {
     const float* src = scores + row * ld_scores + base;
     float raw[R];
@@ -817,20 +867,19 @@ __global__ __launch_bounds__(256) void topk_filter(const float* __restrict__ sco
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t kk = f2key(raw[r]);
-      val[r] = r * 64 + tid < len && kk >= th;
-      key[r] = val[r] ? kk : 0u;
+      key[r] = r * 64 + tid < len && kk >= th ? kk : 0u;   // th >= 1
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) { val[r] = false; key[r] = 0u; }
+    for (int r = 0; r < R; ++r) key[r] = 0u;
   }
-  const int nval = wave_count(val);
-  segment_select<64, R>(key, val, nval, (int)k, sel, nullptr, pre_all[sub]);
+  const int nval = (int)wave_count_ge(key, 1u);
+  const uint32_t sel = wave_select<R>(key, nval, (int)k);
   uint32_t pos[R];
-  segment_positions<64, R>(sel, pos, pre_all[sub]);
+  wave_positions<R>(sel, pos);
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (sel[r]) {
+    if ((sel >> r) & 1u) {
       kout[row * ld_out + seg * k + pos[r]] = key[r];
       iout[row * ld_out + seg * k + pos[r]] = (int32_t)(base + r * 64 + tid);
     }
@@ -1041,10 +1090,10 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
     const int64_t cpw = ((vmax + 63) / 64) * 64;
     dim3 grid((unsigned)nqb, 1, (unsigned)b);
     if (idx != nullptr)   // every list fits one workgroup: selection fused (the caller checked)
-      hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 4, 1>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
+      hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 1>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
                          (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, idx, score_out);
     else
-      hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 4, 0>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
+      hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 0>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
                          (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, nullptr, nullptr);
   } else {
     // few queries (decode): split each query's keys over many workgroups
