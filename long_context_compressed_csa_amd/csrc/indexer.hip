@@ -10,9 +10,13 @@
 // Scoring is a GEMM (query heads x keys, contracted over c_I) with a fused
 // ReLU * w reduction over the heads, so it runs on the bf16 MFMA unit: each
 // wave keeps its query's 32*NHB x c_I operand in registers and streams key
-// tiles that the workgroup stages once in LDS.  Selection is a radix-style
-// threshold search over order-preserving 32-bit keys, then an ordered
-// compaction, with a fixed reduction order everywhere.
+// tiles through LDS.  Selection searches the k-th largest of the
+// order-preserving 32-bit images of the scores bit by bit, then compacts the
+// taken elements in list order, with a fixed reduction order everywhere.
+// Prefill (four or more queries, at most 2048 candidates) selects inside the
+// scoring kernel; decode (few queries, long lists) bounds each row's k-th
+// score from group maxima, filters, and merges; other shapes take a general
+// multi-stage selection.
 #include "common.hpp"
 #include "kernels.hpp"
 
