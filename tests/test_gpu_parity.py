@@ -65,6 +65,8 @@ def test_compress_overlap(dtype, n, c, m, b):
     (torch.float32, 300, 20, 8, 2),
     (torch.bfloat16, 640, 512, 4, 1),
     (torch.float32, 1, 8, 1, 1),          # degenerate ratio 1: the entry is the row itself
+    (torch.float32, 40 * 5 + 13, 24, 40, 2),   # one workgroup per entry: partial last round, few channels
+    (torch.bfloat16, 64 * 3, 128, 64, 1),      # one workgroup per entry, c = 128
 ])
 def test_compress_pool(dtype, n, c, mp, b):
     say(f"compress pool dtype={dtype} n={n} c={c} m'={mp} b={b}")
@@ -76,6 +78,19 @@ def test_compress_pool(dtype, n, c, mp, b):
         assert_close(out[s], want, dtype, f"seq {s}")
     if mp == 1:
         assert torch.equal(out.cpu(), d["C"][:, : n].to(out.dtype))
+
+
+def test_compress_overlap_grid_stride_channel_reload():
+    # more (entry, channel) units than the grid has threads, with a channel
+    # count (9) that does not divide the grid stride: threads loop over
+    # several units and change channel between them
+    say("compress overlap grid-stride, 9 channels")
+    n, c, m = 4 * 120_000, 36, 4
+    d = synth.compress_inputs(True, n=n, c=c, m=m, dtype=torch.float32, seed=14)
+    out = L.csa_compress(*(g(d[k]) for k in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m)
+    torch.cuda.synchronize()
+    want = O.compress_overlap(*(to64(d[k][0]) for k in ("Ca", "Cb", "Za", "Zb")), to64(d["Ba"]), to64(d["Bb"]), m)
+    assert_close(out[0], want, torch.float32, "grid stride")
 
 
 def test_compress_continues_from_previous_block_state():
