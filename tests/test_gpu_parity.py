@@ -692,3 +692,74 @@ def test_decode_one_million_context_sampled():
                                 to64(d["sink"]), [t], nw, d["scale"])
             if set(idx[s, 0].cpu().numpy().tolist()) == set(oi.tolist()):
                 assert_close(out[s], want, torch.bfloat16, f"t={t} seq {s}")
+
+
+def test_graph_replay_matches_eager():
+    # The library allocates nothing and records no memset, so whole layer
+    # steps can be captured in a HIP graph: a prefill-shaped step (both
+    # compressors, scoring with fused selection, attention) and a
+    # decode-shaped step (streaming scorer, threshold top-k, split attention)
+    # are replayed three times, with eager work between the replays, and every
+    # replay must reproduce the eager results bit for bit.
+    say("graph capture and replay")
+    m, nw = 4, 128
+    p = synth.prefill_inputs(n=1024, device=DEV, k=64)
+    n, c, k = p["params"]["n"], p["params"]["c"], p["params"]["k"]
+    ne = n // m
+    Cc = torch.empty((1, ne, c), dtype=torch.bfloat16, device=DEV)
+    KI = torch.empty((1, ne, 128), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((1, n, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((1, n, 64, c), dtype=torch.bfloat16, device=DEV)
+    lib = L.load_library()
+    wsI = torch.empty(max(lib.csa_index_topk_workspace_size(1, n, ne, k), 256), dtype=torch.uint8, device=DEV)
+    wsA = torch.empty(max(lib.csa_attend_workspace_size(1, n, 0, ne, 64, c, k, m, nw, 1), 256),
+                      dtype=torch.uint8, device=DEV)
+    # decode-shaped: 2 sequences, 20000 entries, one query each
+    gen = torch.Generator().manual_seed(31)
+    b, nd, kd = 2, 20000, 512
+    td = nd * m - 1
+    dq = g(torch.randn((b, 1, 64, c), generator=gen) / math.sqrt(c)).to(torch.bfloat16)
+    dqI = g(torch.randn((b, 1, 64, 128), generator=gen) / math.sqrt(128)).to(torch.bfloat16)
+    dw = g(torch.nn.functional.softplus(torch.randn((b, 1, 64), generator=gen)))
+    dKI = g(torch.randn((b, nd, 128), generator=gen) / math.sqrt(128)).to(torch.bfloat16)
+    dCc = g(torch.randn((b, nd, c), generator=gen) / math.sqrt(c)).to(torch.bfloat16)
+    dwin = g(torch.randn((b, nw, c), generator=gen) / math.sqrt(c)).to(torch.bfloat16)
+    dsink = g(torch.randn(64, generator=gen))
+    didx = torch.empty((b, 1, kd), dtype=torch.int32, device=DEV)
+    dout = torch.empty((b, 1, 64, c), dtype=torch.bfloat16, device=DEV)
+    dwsI = torch.empty(max(lib.csa_index_topk_workspace_size(b, 1, nd, kd), 256), dtype=torch.uint8, device=DEV)
+    dwsA = torch.empty(max(lib.csa_attend_workspace_size(b, 1, td, nd, 64, c, kd, m, nw, 1), 256),
+                       dtype=torch.uint8, device=DEV)
+    outs = (Cc, KI, idx, out, didx, dout)
+
+    def body(s):
+        L.csa_compress(*(p[x] for x in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m, out=Cc, stream=s)
+        L.csa_compress(*(p[x] for x in ("ICa", "ICb", "IZa", "IZb", "IBa", "IBb")), m, out=KI, stream=s)
+        L.csa_index_topk(p["qI"], p["w"], KI, 0, m, k, idx=idx, workspace=wsI, stream=s)
+        L.csa_attend(p["q"], Cc, idx, p["kv_raw"], p["sink"], 0, m, nw, out=out, workspace=wsA, stream=s)
+        L.csa_index_topk(dqI, dw, dKI, td, m, kd, idx=didx, workspace=dwsI, stream=s)
+        L.csa_attend(dq, dCc, didx, dwin, dsink, td, m, nw, raw_pos0=td - nw + 1, out=dout, workspace=dwsA,
+                     stream=s)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        body(s)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        body(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(t, r), f"replay {rep}: output {i} differs from the eager run"
+    # and the eager results are right: the decode selection against the oracle
+    for sq in range(b):
+        sc = O.index_scores(to64(dqI[sq, 0])[None], to64(dw[sq, 0])[None], to64(dKI[sq]), [td], m)
+        oi = O.topk_select(sc[0], nd, kd)
+        assert_index_sets(didx[sq].cpu().numpy(), oi[None], sc, [nd], kd, f"graph decode seq {sq}")
