@@ -44,6 +44,10 @@ template <> struct Elem<bf16_t> {
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {
   static constexpr int N = 4;
+  // element i of a 16-byte vector loaded raw
+  static __device__ __forceinline__ float get(const uint4& r, int i) {
+    return __uint_as_float(i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w);
+  }
   static __device__ __forceinline__ void ld(const float* p, float (&o)[4]) {
     float4 v = *reinterpret_cast<const float4*>(p);
     o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
@@ -54,6 +58,10 @@ template <> struct Vec16<float> {
 };
 template <> struct Vec16<bf16_t> {
   static constexpr int N = 8;
+  static __device__ __forceinline__ float get(const uint4& r, int i) {
+    const uint32_t w = (i >> 1) == 0 ? r.x : (i >> 1) == 1 ? r.y : (i >> 1) == 2 ? r.z : r.w;
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
   static __device__ __forceinline__ void ld(const bf16_t* p, float (&o)[8]) {
     uint4 v = *reinterpret_cast<const uint4*>(p);
     uint32_t w[4] = {v.x, v.y, v.z, v.w};

@@ -260,30 +260,32 @@ __global__ __launch_bounds__(256) void compress_pool(const T* __restrict__ C, co
 #pragma unroll
   for (int v = 0; v < V; ++v) { mx[v] = -INFINITY; sum[v] = 0.f; acc[v] = 0.f; }
   for (int64_t r0 = part; r0 < m; r0 += P * NR) {
-    float z[NR][V], cv[NR][V], bv[NR][V];
+    // the round's rows stay packed (16 bytes each) until they are used
+    uint4 zr[NR], cr[NR], br[NR];
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       int64_t r = r0 + P * q;
       r = r < m ? r : m - 1;
-      RowIO<T, V>::ld(zrow + r * (int64_t)c, z[q]);
-      RowIO<T, V>::ld(crow + r * (int64_t)c, cv[q]);
-      RowIO<T, V>::ld(brow + r * (int64_t)c, bv[q]);
+      zr[q] = *reinterpret_cast<const uint4*>(zrow + r * (int64_t)c);
+      cr[q] = *reinterpret_cast<const uint4*>(crow + r * (int64_t)c);
+      br[q] = *reinterpret_cast<const uint4*>(brow + r * (int64_t)c);
     }
 #pragma unroll
     for (int v = 0; v < V; ++v) {
+      float z[NR];
       float bm = mx[v];
 #pragma unroll
       for (int q = 0; q < NR; ++q) {
-        z[q][v] = (r0 + P * q < m) ? z[q][v] + bv[q][v] : -INFINITY;
-        bm = fmaxf(bm, z[q][v]);
+        z[q] = (r0 + P * q < m) ? Vec16<T>::get(zr[q], v) + Vec16<T>::get(br[q], v) : -INFINITY;
+        bm = fmaxf(bm, z[q]);
       }
       const float sc = fast_exp(mx[v] - bm);   // bm is finite: row r0 < m exists
       float sd = sum[v] * sc, ad = acc[v] * sc;
 #pragma unroll
       for (int q = 0; q < NR; ++q) {
-        const float p = fast_exp(z[q][v] - bm);
+        const float p = fast_exp(z[q] - bm);
         sd += p;
-        ad = fmaf(p, cv[q][v], ad);
+        ad = fmaf(p, Vec16<T>::get(cr[q], v), ad);
       }
       mx[v] = bm;
       sum[v] = sd;
