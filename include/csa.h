@@ -9,7 +9,7 @@
  *    after the call returns.  Inputs are never written.
  *  - `dtype` (csa_dtype) is the element type of every floating-point tensor
  *    argument except `w`, `sink` and `score`, which are always float32.
- *    Arithmetic is float32 in both modes; bfloat16 results are rounded to
+ *    Arithmetic is float32 in every mode; bfloat16 results are rounded to
  *    nearest-even when stored.
  *  - Positions are 0-based token positions.  A query at position t may read
  *    compressed entry s only if s < (t + 1) / m (integer division): entry s
@@ -37,7 +37,12 @@
 extern "C" {
 #endif
 
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+/* CSA_FP8 is the 8-bit E4M3 floating-point format of the OCP 8-bit floating
+ * point specification (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * no infinities; 0x7F and 0xFF are NaN; largest finite value 448).  Only
+ * csa_index_topk accepts it (for qI and KIcomp: the low-precision indexer);
+ * every other entry point returns CSA_ENOTSUP for it. */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8 = 2 } csa_dtype;
 
 enum {
   CSA_OK = 0,
@@ -101,6 +106,12 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
  *  score   out [b, n_q, k] float32 scores of idx (0 at padding), or NULL
  *  workspace  device scratch of at least csa_index_topk_workspace_size()
  *          bytes, 256-byte aligned; its contents on return are unspecified.
+ *
+ * dtype: CSA_F32, CSA_BF16 or CSA_FP8 for qI and KIcomp.  With CSA_FP8 the
+ * scores are the same weighted ReLU sums of the decoded E4M3 values,
+ * accumulated in float32 (any scaling of the codes is the caller's: a
+ * positive factor on all keys, or on one head's queries folded into that
+ * head's w, leaves the selection unchanged).
  *
  * Errors: CSA_EINVAL for sizes < 1 (n_comp may be 0), t0 < 0, NULL required
  * pointers, or n_comp > (t0 + n_q)/m (entries that no query could have

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 CSA_F32 = 0
 CSA_BF16 = 1
-_DT = {torch.float32: CSA_F32, torch.bfloat16: CSA_BF16}
+CSA_FP8 = 2   # OCP E4M3 (torch.float8_e4m3fn): indexer queries and keys only
+_DT = {torch.float32: CSA_F32, torch.bfloat16: CSA_BF16, torch.float8_e4m3fn: CSA_FP8}
 
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p

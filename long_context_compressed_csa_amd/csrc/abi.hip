@@ -93,7 +93,7 @@ int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t c
                    int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI, int64_t c_I,
                    int64_t m, int64_t k, int dtype, int32_t* idx, float* score, void* workspace,
                    size_t ws_bytes, void* stream) {
-  if (!dtype_ok(dtype)) return CSA_ENOTSUP;
+  if (!dtype_ok(dtype) && dtype != CSA_FP8) return CSA_ENOTSUP;
   if (!qI || !w || !idx || !workspace) return CSA_EINVAL;
   if (n_comp > 0 && !KIcomp) return CSA_EINVAL;
   if (b < 1 || n_q < 1 || n_hI < 1 || c_I < 1 || m < 1 || k < 1 || t0 < 0 || n_comp < 0)

@@ -8,6 +8,7 @@
 namespace csa {
 
 typedef uint16_t bf16_t;
+typedef uint8_t fp8_t;   // OCP E4M3 code
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -38,6 +39,11 @@ template <> struct Elem<float> {
 template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
   static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+};
+// 8-bit E4M3 (OCP), read only: the hardware conversion decodes every code
+// exactly (NaN codes to NaN).
+template <> struct Elem<fp8_t> {
+  static __device__ __forceinline__ float ld(const fp8_t* p) { return __builtin_amdgcn_cvt_f32_fp8((int)*p, 0); }
 };
 
 // 16-byte vector loads/stores: VEC = 16 / sizeof(T) elements widened to float.

@@ -379,18 +379,42 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
 // k-th largest score from below, which lets selection discard almost every
 // key in one pass.
 // ---------------------------------------------------------------------------
-template <int NHB, int KS, int D>
+// One lane's operand of a 32x32x16 MFMA step (8 elements: 16 bytes of bf16,
+// 8 of E4M3) and the MFMA itself, per key element type.
+template <typename E> struct ScoreOps;
+template <> struct ScoreOps<bf16_t> {
+  typedef bf16x8 op_t;
+  static __device__ __forceinline__ op_t ld(const void* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  }
+  static __device__ __forceinline__ f32x16 mfma(op_t a, op_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct ScoreOps<fp8_t> {
+  typedef long op_t;
+  static __device__ __forceinline__ op_t ld(const void* p) { return *reinterpret_cast<const long*>(p); }
+  static __device__ __forceinline__ f32x16 mfma(op_t a, op_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int NHB, int KS, int D, typename E>
 __global__ __launch_bounds__(256) void index_scores_stream(
-    const bf16_t* __restrict__ qI, const float* __restrict__ w, const bf16_t* __restrict__ KI,
+    const E* __restrict__ qI, const float* __restrict__ w, const E* __restrict__ KI,
     int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
     float* __restrict__ scores, uint32_t* __restrict__ gmax, int64_t ld_gmax) {
+  typedef ScoreOps<E> Ops;
   constexpr int CI = KS * 16;
   constexpr int NH = NHB * 32;
-  constexpr int NCH = 2 * KS;     // 16-byte chunks per key row
-  constexpr int KPI = 64 / NCH;   // key rows per 1 KiB DMA instruction
-  constexpr int SDIV = 16 / NCH;  // f(r) = (r / SDIV) % NCH spreads 16 rows over 64 banks
-  constexpr int TU4 = 32 * NCH;   // 16-byte chunks per tile
-  static_assert(NCH == 8 || NCH == 16, "c_I must be 64 or 128");
+  constexpr int ES = (int)sizeof(E);
+  constexpr int ROWB = CI * ES;      // bytes per key row
+  constexpr int NCH = ROWB / 16;     // 16-byte chunks per key row
+  constexpr int KPI = 64 / NCH;      // key rows per 1 KiB DMA instruction
+  constexpr int NDMA = NCH / 2;      // 1 KiB DMA instructions per 32-key tile
+  constexpr int SDIV = 16 / NCH;     // f(r) = (r / SDIV) % NCH spreads 16 rows over 64 banks
+  constexpr int TU4 = 32 * NCH;      // 16-byte chunks per tile
+  static_assert(NCH == 4 || NCH == 8 || NCH == 16, "c_I must be 64 or 128");
   __shared__ uint4 ring[4][D][TU4];
   __shared__ float sbuf[16384];  // the workgroup's scores, written out at the end
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -425,15 +449,15 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   // at most 128 tiles per wave (128 * gridDim.y * 128 >= vis, set by the host)
   const int ntiles = first >= c1 ? 0 : (int)((c1 - first + kstep - 1) / kstep);
 
-  const bf16_t* kbase = KI + bi * comp_bs;
+  const E* kbase = KI + bi * comp_bs;
   const int64_t lastkey = c1 - 1;
   // DMA: instruction i, lane l fills LDS chunk 64 i + l of the tile = chunk
   // l % NCH of row i * KPI + l / NCH, from source chunk (l % NCH) ^ f(row)
-  int src_off[KS];
+  int src_off[NDMA];   // elements from the tile's first row
 #pragma unroll
-  for (int i = 0; i < KS; ++i) {
+  for (int i = 0; i < NDMA; ++i) {
     const int r = i * KPI + l / NCH;
-    src_off[i] = r * CI + (((l % NCH) ^ ((r / SDIV) % NCH)) * 8);
+    src_off[i] = r * CI + (((l % NCH) ^ ((r / SDIV) % NCH)) * (16 / ES));
   }
   auto issue = [&](int j, int slot) {
     // rows past the last key re-read the last key (in bounds; their scores
@@ -443,44 +467,48 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     const int room = (int)(lastkey - kb < 32 ? lastkey - kb : 32);
     const uint32_t lds = (uint32_t)(uintptr_t)&ring[wave][slot][0];
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
+    for (int i = 0; i < NDMA; ++i) {
       const int r = i * KPI + l / NCH;
-      const bf16_t* src = kbase + kb * CI + (r <= room ? src_off[i] : room * CI + (src_off[i] - r * CI));
+      const E* src = kbase + kb * CI + (r <= room ? src_off[i] : room * CI + (src_off[i] - r * CI));
       dma_chunk16(src, lds + 1024 * i);
     }
   };
 #pragma unroll
   for (int j = 0; j < D - 1; ++j) issue(j, j);
 
-  bf16x8 qa[NHB][KS];
+  typename Ops::op_t qa[NHB][KS];
   float wv[NHB][16];
   const int64_t qoff = (bi * n_q + qrow) * (int64_t)NH;
 #pragma unroll
   for (int mb = 0; mb < NHB; ++mb) {
-    const bf16_t* qp = qI + (qoff + mb * 32 + (l & 31)) * CI + 8 * (l >> 5);
+    const E* qp = qI + (qoff + mb * 32 + (l & 31)) * CI + 8 * (l >> 5);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qa[mb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
+    for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = Ops::ld(qp + ks * 16);
 #pragma unroll
     for (int r = 0; r < 16; ++r) wv[mb][r] = w[qoff + mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)];
   }
 
   float* srow = scores + (bi * n_q + qrow) * n_comp;
-  // B operand of 32x32x16 step ks: lane l holds dims 16 ks + 8 (l / 32) .. +8 of key l % 32
+  // B operand of 32x32x16 step ks: lane l holds elements 16 ks + 8 (l / 32)
+  // .. +8 of key l % 32: byte b = ES (16 ks + 8 (l / 32)) of the row, in
+  // 16-byte chunk b / 16 at byte b % 16
   const int rr = l & 31;
-  int rd_off[KS];
+  int rd_off[KS];   // bytes from the slot's start
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) rd_off[ks] = rr * NCH + ((2 * ks + (l >> 5)) ^ ((rr / SDIV) % NCH));
+  for (int ks = 0; ks < KS; ++ks) {
+    const int bb = ES * (16 * ks + 8 * (l >> 5));
+    rd_off[ks] = rr * ROWB + (((bb >> 4) ^ ((rr / SDIV) % NCH)) << 4) + (bb & 15);
+  }
   auto compute = [&](int j, int slot) {
+    const unsigned char* tile = reinterpret_cast<const unsigned char*>(&ring[wave][slot][0]);
     f32x16 acc[NHB];
 #pragma unroll
     for (int mb = 0; mb < NHB; ++mb) acc[mb] = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, ring[wave][slot][rd_off[ks]]);
+      const typename Ops::op_t bv = Ops::ld(tile + rd_off[ks]);
 #pragma unroll
-      for (int mb = 0; mb < NHB; ++mb)
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], bv, acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < NHB; ++mb) acc[mb] = Ops::mfma(qa[mb][ks], bv, acc[mb]);
     }
     float sc = 0.f;
 #pragma unroll
@@ -496,13 +524,13 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   // slot step j - 1 has finished reading.  Every step issues exactly one tile
   // (those past the last tile re-read the last key row: they keep the wait
   // counts static and cost no HBM traffic), so before step j's reads the
-  // D - 1 tiles issued after tile j ((D - 1) KS loads) may still be in
+  // D - 1 tiles issued after tile j ((D - 1) NDMA loads) may still be in
   // flight; loads complete in order, and a pending score store only makes the
   // wait stricter.
   int slot = 0;
   for (int j = 0; j < ntiles; ++j) {
     issue(j + D - 1, slot == 0 ? D - 1 : slot - 1);
-    wait_vmem<(D - 1) * KS>();
+    wait_vmem<(D - 1) * NDMA>();
     compute(j, slot);
     slot = slot == D - 1 ? 0 : slot + 1;
   }
@@ -1080,6 +1108,21 @@ bool index_topk_supported(int64_t n_comp, int64_t k) {
   return k <= kWaveChunk / 2 && (n_comp + kWaveChunk - 1) / kWaveChunk <= kMergeMaxSeg;
 }
 
+// Streaming scoring for few queries (decode): each query's keys split over
+// many workgroups.  Writes the group maxima when gmax is given.
+template <int NHB, int KS, typename E>
+static hipError_t launch_scores_stream(const void* qI, const float* w, const void* KI, int64_t cbs, int64_t b,
+                                       int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, float* scores,
+                                       uint32_t* gmax, int64_t ld_gmax, bool* gmax_used, hipStream_t st) {
+  const int64_t vmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
+  const int64_t nsplit = stream_splits(b, n_q, vmax);
+  dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
+  hipLaunchKernelGGL((index_scores_stream<NHB, KS, kStreamRing, E>), grid, dim3(256), 0, st, (const E*)qI, w,
+                     (const E*)KI, cbs, n_q, t0, n_comp, m, scores, gmax, ld_gmax);
+  *gmax_used = gmax != nullptr;
+  return hipGetLastError();
+}
+
 // Scoring on MFMA.  Returns through *gmax_used whether the group maxima
 // were written (the streaming kernel writes them when gmax is given).
 template <int NHB, int KS>
@@ -1100,12 +1143,8 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
       hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 0>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
                          (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, nullptr, nullptr);
   } else {
-    // few queries (decode): split each query's keys over many workgroups
-    const int64_t nsplit = stream_splits(b, n_q, vmax);
-    dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
-    hipLaunchKernelGGL((index_scores_stream<NHB, KS, kStreamRing>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
-                       (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, scores, gmax, ld_gmax);
-    *gmax_used = gmax != nullptr;
+    return launch_scores_stream<NHB, KS, bf16_t>(qI, w, KI, cbs, b, n_q, t0, n_comp, m, scores, gmax, ld_gmax,
+                                                 gmax_used, st);
   }
   return hipGetLastError();
 }
@@ -1138,11 +1177,27 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
       CSA_SCORES_CASE(4, 4) CSA_SCORES_CASE(4, 8)
 #undef CSA_SCORES_CASE
     }
+    // E4M3 keys and queries, few queries: the streaming kernel on the FP8 MFMA
+    if (dtype == 2 && n_q < 4 && nh % 32 == 0 && cI % 16 == 0) {
+      const int nhb = (int)(nh / 32), ks = (int)(cI / 16);
+#define CSA_STREAM8_CASE(A, B)                                                                          \
+  if (!done && nhb == A && ks == B) {                                                                   \
+    err = launch_scores_stream<A, B, fp8_t>(qI, w, KI, cbs, b, n_q, t0, n_comp, m, scores, gmax, L.gcap, \
+                                            &gmax_used, st);                                            \
+    done = true;                                                                                        \
+  }
+      CSA_STREAM8_CASE(1, 4) CSA_STREAM8_CASE(1, 8) CSA_STREAM8_CASE(2, 4) CSA_STREAM8_CASE(2, 8)
+      CSA_STREAM8_CASE(4, 4) CSA_STREAM8_CASE(4, 8)
+#undef CSA_STREAM8_CASE
+    }
     if (!done) {
       dim3 grid((unsigned)((n_comp + 255) / 256), (unsigned)n_q, (unsigned)b);
       if (dtype == 1)
         hipLaunchKernelGGL((index_scores_generic<bf16_t>), grid, dim3(256), 0, st, (const bf16_t*)qI,
                            w, (const bf16_t*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores);
+      else if (dtype == 2)
+        hipLaunchKernelGGL((index_scores_generic<fp8_t>), grid, dim3(256), 0, st, (const fp8_t*)qI,
+                           w, (const fp8_t*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores);
       else
         hipLaunchKernelGGL((index_scores_generic<float>), grid, dim3(256), 0, st, (const float*)qI,
                            w, (const float*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores);

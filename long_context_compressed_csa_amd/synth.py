@@ -68,6 +68,12 @@ def softplus_normal(shape, g, device="cpu"):
     return torch.nn.functional.softplus(x)
 
 
+def to_fp8(x):
+    """Round a tensor to 8-bit E4M3 codes (torch.float8_e4m3fn, nearest
+    even); the draws here stay far inside its +-448 range."""
+    return x.float().to(torch.float8_e4m3fn)
+
+
 def tiny_inputs(seed=None, n=None):
     """The tiny float32 CSA layer."""
     p = dict(TINY)

@@ -201,6 +201,25 @@ def index_scores(qI, w, KI, t_pos, m: int, chunk: int = 64):
     return out
 
 
+def fp8_e4m3_decode(codes):
+    """Values of 8-bit E4M3 codes (uint8 array), float64.
+
+    The low-precision indexer of [P1] B9 (estimate paragraph) and B11 runs
+    the indexer's query/key path in a narrow float format; this build takes
+    the 8-bit E4M3 format of the OCP 8-bit floating point specification:
+    bit 7 sign, bits 6-3 exponent e (bias 7), bits 2-0 mantissa f; e = 0
+    gives the subnormals (f / 8) * 2^-6, e > 0 gives (1 + f / 8) * 2^(e - 7);
+    there are no infinities, and the two codes with e = 15, f = 7 are NaN.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >= 128, -1.0, 1.0)
+    e = (c >> 3) & 15
+    f = (c & 7).astype(F64)
+    mag = np.where(e == 0, (f / 8.0) * 2.0 ** -6, (1.0 + f / 8.0) * np.exp2((e - 7).astype(F64)))
+    out = sign * mag
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, out)
+
+
 def topk_select(scores_row, v: int, k: int):
     """Indices of the top-k among the first v scores of one query.
 

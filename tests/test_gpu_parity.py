@@ -274,6 +274,45 @@ def test_index_topk_fused_nothing_visible():
     assert (idx.cpu() == -1).all()
 
 
+def _fp8_oracle_index(qI8, w, KI8, t_pos, m, k):
+    # the oracle scores the values the codes stand for
+    dq = O.fp8_e4m3_decode(qI8.view(torch.uint8).numpy())
+    dk = O.fp8_e4m3_decode(KI8.view(torch.uint8).numpy())
+    sc = O.index_scores(dq, to64(w), dk, t_pos, m)
+    n_comp = KI8.shape[0]
+    vis = np.array([min((int(t) + 1) // m, n_comp) for t in t_pos])
+    idx = np.stack([O.topk_select(sc[r], vis[r], k) for r in range(len(t_pos))])
+    return idx, sc, vis
+
+
+@pytest.mark.parametrize("b,n_q,n_comp,k,nh,cI", [
+    (2, 1, 20000, 512, 64, 128),    # streaming FP8 scorer, threshold selection
+    (2, 3, 1500, 100, 64, 128),     # streaming FP8 scorer, one segment per row, rows of different length
+    (1, 2, 9000, 300, 32, 64),      # other head / dimension counts
+    (1, 6, 1200, 64, 64, 128),      # four or more queries: generic scoring of the codes
+    (1, 2, 700, 40, 48, 40),        # shape without an MFMA kernel: generic scoring
+])
+def test_index_topk_fp8(b, n_q, n_comp, k, nh, cI):
+    # E4M3 indexer queries and keys: the same selection as the oracle's over
+    # the decoded values, apart from near ties
+    say(f"index fp8 b={b} n_q={n_q} n_comp={n_comp} k={k} nh={nh} cI={cI}")
+    m = 4
+    t0 = n_comp * m - n_q
+    gen = torch.Generator().manual_seed(26)
+    qI = synth.to_fp8(torch.randn((b, n_q, nh, cI), generator=gen) / math.sqrt(cI))
+    KI = synth.to_fp8(torch.randn((b, n_comp, cI), generator=gen) / math.sqrt(cI))
+    w = torch.nn.functional.softplus(torch.randn((b, n_q, nh), generator=gen))
+    idx, sc = L.csa_index_topk(g(qI), g(w), g(KI), t0, m, k, score=True)
+    torch.cuda.synchronize()
+    for s in range(b):
+        want, osc, vis = _fp8_oracle_index(qI[s], w[s], KI[s], np.arange(t0, t0 + n_q), m, k)
+        assert_index_sets(idx[s].cpu().numpy(), want, osc, vis, k, f"seq {s}")
+        gi, gs = idx[s].cpu().numpy(), sc[s].cpu().double().numpy()
+        sel = gi >= 0
+        ref = osc[np.nonzero(sel)[0], gi[sel]]
+        assert np.max(np.abs(gs[sel] - ref)) <= 1e-3 * max(1.0, np.abs(ref).max())
+
+
 def test_index_topk_long_lists_rows_differ():
     # few queries whose visible counts differ (4095, 4095, 4096 entries)
     say("index long lists, rows with different visibility")

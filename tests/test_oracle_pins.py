@@ -395,3 +395,35 @@ def test_decode_steps_equal_one_shot_prefill():
             assert np.abs(o_t - out[t]).max() < 1e-13
     assert np.abs(np.array(state.Ccomp) - Cc).max() < 1e-13
     assert np.abs(np.array(state.KIcomp) - KIc).max() < 1e-13
+
+
+# ---------------------------------------------------------------- E4M3 ----
+
+def test_fp8_e4m3_decode_fixed_values():
+    # values the E4M3 definition fixes: 1.0, the largest finite 448, the
+    # smallest normal 2^-6 and subnormal 2^-9, signed zero, the NaN codes
+    v = O.fp8_e4m3_decode(np.array([0x38, 0x7E, 0x08, 0x01, 0x07, 0x00, 0x80, 0xB8, 0xFE, 0x7F, 0xFF],
+                                   dtype=np.uint8))
+    assert v[0] == 1.0 and v[1] == 448.0 and v[2] == 2.0 ** -6 and v[3] == 2.0 ** -9
+    assert v[4] == 7 * 2.0 ** -9 and v[5] == 0.0 and v[6] == 0.0 and np.signbit(v[6])
+    assert v[7] == -1.0 and v[8] == -448.0 and np.isnan(v[9]) and np.isnan(v[10])
+
+
+def test_fp8_e4m3_decode_is_monotonic_and_symmetric():
+    pos = O.fp8_e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8))
+    neg = O.fp8_e4m3_decode(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)                  # strictly increasing over 0x00..0x7E
+    assert np.array_equal(neg, -pos)
+    assert len(np.unique(np.concatenate([pos, neg]))) == 253   # +-0 coincide
+    # between consecutive powers of two (normal range) the step is 1/8 of the power
+    for e in range(1, 15):
+        seg = O.fp8_e4m3_decode(np.arange(8 * e, 8 * e + 8, dtype=np.uint8))
+        assert np.allclose(np.diff(seg), 2.0 ** (e - 7) / 8)
+
+
+def test_fp8_e4m3_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.fp8_e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
