@@ -399,7 +399,7 @@ template <> struct ScoreOps<fp8_t> {
   }
 };
 
-template <int NHB, int KS, int D, typename E>
+template <int NHB, int KS, int D, typename E, int SBK>
 __global__ __launch_bounds__(256) void index_scores_stream(
     const E* __restrict__ qI, const float* __restrict__ w, const E* __restrict__ KI,
     int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   constexpr int TU4 = 32 * NCH;      // 16-byte chunks per tile
   static_assert(NCH == 4 || NCH == 8 || NCH == 16, "c_I must be 64 or 128");
   __shared__ uint4 ring[4][D][TU4];
-  __shared__ float sbuf[16384];  // the workgroup's scores, written out at the end
+  __shared__ float sbuf[SBK];  // the workgroup's scores (at most SBK), written out at the end
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const int64_t qrow = blockIdx.x;
@@ -446,7 +446,8 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     write_gmax();
     return;
   }
-  // at most 128 tiles per wave (128 * gridDim.y * 128 >= vis, set by the host)
+  // at most SBK / 128 tiles per wave (the host splits each row over enough
+  // workgroups)
   const int ntiles = first >= c1 ? 0 : (int)((c1 - first + kstep - 1) / kstep);
 
   const E* kbase = KI + bi * comp_bs;
@@ -557,18 +558,23 @@ __global__ __launch_bounds__(256) void index_scores_stream(
 // The k-th largest key T is found bit by bit from the top, starting below the
 // common prefix of the segment's smallest and largest key; each step counts
 // the keys >= a candidate with wave ballots and scalar popcounts (plus one LDS
-// exchange per step in the workgroup form).  Keys > T are taken, then keys
+// exchange per step in the workgroup form, where a step settles two bits).  Keys > T are taken, then keys
 // == T in list order until k are taken (ties go to the lower index), and the
 // taken elements are compacted in list order.
 // ---------------------------------------------------------------------------
 template <int NT>
 struct SegReduce {
+  // Exchanges alternate between two halves of the buffer (parity), so one
+  // exchange's writes never meet the previous exchange's reads; each half
+  // holds three values per wave.
+  static constexpr int kStride = 3 * (NT / 64);
+  static constexpr int kRedSize = 2 * kStride + 1;
   // sum of a wave-uniform count over the NT/64 waves (LDS exchange when NT > 64)
   static __device__ __forceinline__ uint32_t sum(uint32_t c, uint32_t* red, int wave, int& parity) {
     if constexpr (NT == 64) {
       return c;
     } else {
-      uint32_t* slot = red + parity * (NT / 64);
+      uint32_t* slot = red + parity * kStride;
       parity ^= 1;
       if ((threadIdx.x & 63) == 0) slot[wave] = c;
       __syncthreads();
@@ -578,13 +584,32 @@ struct SegReduce {
       return t;
     }
   }
+  // three counts at once (one exchange)
+  static __device__ __forceinline__ void sum3(uint32_t (&c)[3], uint32_t* red, int wave, int& parity) {
+    if constexpr (NT > 64) {
+      uint32_t* slot = red + parity * kStride;
+      parity ^= 1;
+      if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) slot[j * (NT / 64) + wave] = c[j];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) t += slot[j * (NT / 64) + w];
+        c[j] = t;
+      }
+    }
+  }
   static __device__ __forceinline__ uint32_t umax(uint32_t v, uint32_t* red, int wave, int& parity) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
     if constexpr (NT == 64) {
       return v;
     } else {
-      uint32_t* slot = red + parity * (NT / 64);
+      uint32_t* slot = red + parity * kStride;
       parity ^= 1;
       if ((threadIdx.x & 63) == 0) slot[wave] = v;
       __syncthreads();
@@ -629,7 +654,23 @@ __device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const b
   } else {
     const int top = 31 - __clz(diff);
     T = top == 31 ? 0u : (hi >> (top + 1)) << (top + 1);
-    for (int bit = top; bit >= 0; --bit) {
+    int bit = top;
+    if constexpr (NT > 64) {
+      // two bits per exchange: the counts >= T + u, T + 2u, T + 3u (u the
+      // lower of the two bits, both clear in T) settle both at once
+      for (; bit >= 1; bit -= 2) {
+        const uint32_t u = 1u << (bit - 1);
+        uint32_t c[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            c[j] += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key[r] >= T + (uint32_t)(j + 1) * u));
+        SegReduce<NT>::sum3(c, red, wave, parity);
+        T = c[2] >= (uint32_t)k ? T + 3u * u : c[1] >= (uint32_t)k ? T + 2u * u : c[0] >= (uint32_t)k ? T + u : T;
+      }
+    }
+    for (; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       uint32_t c = 0;
 #pragma unroll
@@ -731,7 +772,7 @@ __global__ __launch_bounds__(256) void topk_stage(
     int64_t k, const int64_t* __restrict__ len_in, int64_t nseg) {
   constexpr int CH = NT * R;
   constexpr int SEGS = 256 / NT;   // segments per workgroup
-  __shared__ uint32_t red_all[SEGS][2 * (NT / 64) + 1];
+  __shared__ uint32_t red_all[SEGS][SegReduce<NT>::kRedSize];
   __shared__ uint32_t pre_all[SEGS][R * (NT / 64) + 1];
   const int sub = threadIdx.x / NT;
   const int tid = threadIdx.x % NT;
@@ -823,49 +864,61 @@ __device__ __forceinline__ int wave_count(const bool (&val)[R]) {
   return c;
 }
 
-// tau[row] = the k-th largest of the row's first min(G, 2048) group maxima,
-// or 1 (every valid key) when fewer than k of them are non-empty.  Each
-// maximum is a distinct key of the row, so at least k keys are >= tau.  One
-// workgroup of 256 threads (8 maxima each) per row.
+// tau[row] = a lower bound on the k-th largest of the row's first
+// min(G, 2048) group maxima, or 1 (every valid key) when fewer than k of them
+// are non-empty.  Each maximum is a distinct key of the row, so at least k
+// keys are >= tau.  The bound is the k-th largest found to kThresholdBits
+// bits below the common prefix of the largest and smallest maximum: the bit
+// search keeps count(>= T) >= k at every step, so stopping it early still
+// gives a valid bound, one that lets through only the keys within 2^-12 of
+// the maxima's range below the exact value.  One workgroup of 256 threads
+// (8 maxima each) per row.
+constexpr int kThresholdBits = 12;
 __global__ __launch_bounds__(256) void topk_threshold(const uint32_t* __restrict__ gmax, int64_t ld_gmax, int64_t G,
                                                       int64_t rows, int64_t k, uint32_t* __restrict__ tau) {
   constexpr int NT = 256, R = 8;
-  __shared__ uint32_t red[2 * (NT / 64) + 1];
-  __shared__ uint32_t pre[R * (NT / 64) + 1];
-  __shared__ uint32_t wmin[NT / 64];
-  __shared__ int wcnt[NT / 64];
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  __shared__ uint32_t red[SegReduce<NT>::kRedSize];
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int g = (int)(G < NT * R ? G : NT * R);
   const uint32_t* src = gmax + row * ld_gmax;
   uint32_t key[R];
-  bool val[R], sel[R];
+  uint32_t c = 0, hi = 0, lo = 0xffffffffu;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int e = r * NT + tid;
     const uint32_t v = src[min(e, g - 1)];
-    val[r] = e < g && v != 0u;
-    key[r] = val[r] ? v : 0u;
+    key[r] = e < g ? v : 0u;   // 0 = empty
   }
-  const int c = wave_count(val);
-  if (l == 0) wcnt[wave] = c;
-  __syncthreads();
-  const int nval = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-  if (nval <= k) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    c += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key[r] != 0u));
+    if (key[r] != 0u) { hi = max(hi, key[r]); lo = min(lo, key[r]); }
+  }
+  int parity = 0;
+  const uint32_t nval = SegReduce<NT>::sum(c, red, wave, parity);
+  if (nval <= (uint32_t)k) {
     if (tid == 0) tau[row] = 1u;
     return;   // uniform
   }
-  segment_select<NT, R>(key, val, nval, (int)k, sel, red, pre);
-  // the k-th largest is the smallest selected key
-  uint32_t mn = 0xffffffffu;
+  hi = SegReduce<NT>::umax(hi, red, wave, parity);
+  lo = ~SegReduce<NT>::umax(~lo, red, wave, parity);
+  const uint32_t diff = hi ^ lo;
+  uint32_t T = hi;
+  if (diff != 0) {
+    const int top = 31 - __clz(diff);
+    T = top == 31 ? 0u : (hi >> (top + 1)) << (top + 1);   // <= lo: count(>= T) = nval >= k
+    const int last = max(0, top - (kThresholdBits - 1));
+    for (int bit = top; bit >= last; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      uint32_t cc = 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (sel[r]) mn = min(mn, key[r]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-  if (l == 0) wmin[wave] = mn;
-  __syncthreads();
-  if (tid == 0) tau[row] = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
+      for (int r = 0; r < R; ++r) cc += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key[r] >= cand));
+      cc = SegReduce<NT>::sum(cc, red, wave, parity);
+      if (cc >= (uint32_t)k) T = cand;
+    }
+  }
+  if (tid == 0) tau[row] = max(T, 1u);
 }
 
 // One wave per (row, 2048-key segment): the top k of the segment's scores
@@ -931,7 +984,7 @@ __global__ __launch_bounds__(256) void topk_merge(const uint32_t* __restrict__ k
   __shared__ int32_t pref[kMergeMaxSeg + 1];
   __shared__ uint32_t runK[1024];
   __shared__ int32_t runI[1024];
-  __shared__ uint32_t red[2 * (NT / 64) + 1];
+  __shared__ uint32_t red[SegReduce<NT>::kRedSize];
   __shared__ uint32_t pre[R * (NT / 64) + 1];
   __shared__ int32_t part[NT / 64];
   const int tid = threadIdx.x;
@@ -1049,22 +1102,28 @@ constexpr int64_t kBlockChunk = 256 * kBlockR;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The streaming (decode) scoring kernel: at most kStreamKeysPerWG keys per
+// The streaming (decode) scoring kernel: at most StreamPolicy::keys keys per
 // workgroup (its LDS score buffer), 32 group maxima per workgroup (4 waves x
-// 8 groups), kStreamRing LDS ring slots per wave.  One workgroup fills a CU
-// (160 KiB of LDS), so each row's keys are split over enough workgroups for
-// about one per CU of the 256 on the chip (more when the buffer requires it,
-// fewer when the row has fewer 128-key chunks): a grid just above the CU
-// count would run a nearly empty second round.
-constexpr int64_t kStreamKeysPerWG = 16384;
+// 8 groups).  bf16: a 3-slot ring of 8 KiB tiles per wave plus a 64 KiB score
+// buffer fill a CU (160 KiB of LDS), so each row's keys are split over
+// enough workgroups for about one per CU of the 256 on the chip; E4M3: a
+// 3-slot ring of 4 KiB tiles plus a 32 KiB buffer leave room for two per CU.
+// More splits when the buffer requires them, fewer when the row has fewer
+// 128-key chunks: a grid just above the CU slots would run a nearly empty
+// second round.
 constexpr int64_t kStreamGroupsPerWG = 32;
-constexpr int kStreamRing = 3;
-constexpr int64_t kStreamTargetWGs = 256;
-static int64_t stream_splits(int64_t b, int64_t n_q, int64_t vmax) {
-  const int64_t need = (vmax + kStreamKeysPerWG - 1) / kStreamKeysPerWG;
-  const int64_t want = kStreamTargetWGs / std::max<int64_t>(1, b * n_q);
+template <int ES> struct StreamPolicy;
+template <> struct StreamPolicy<2> { static constexpr int64_t keys = 16384, wgs = 256; static constexpr int ring = 3; };
+template <> struct StreamPolicy<1> { static constexpr int64_t keys = 8192, wgs = 512; static constexpr int ring = 3; };
+static int64_t stream_splits(int64_t b, int64_t n_q, int64_t vmax, int64_t keys, int64_t wgs) {
+  const int64_t need = (vmax + keys - 1) / keys;
+  const int64_t want = wgs / std::max<int64_t>(1, b * n_q);
   const int64_t chunks = (vmax + 127) / 128;
   return std::max<int64_t>(1, std::min(chunks, std::max(need, want)));
+}
+static int64_t stream_splits_for(int dtype, int64_t b, int64_t n_q, int64_t vmax) {
+  return dtype == 2 ? stream_splits(b, n_q, vmax, StreamPolicy<1>::keys, StreamPolicy<1>::wgs)
+                    : stream_splits(b, n_q, vmax, StreamPolicy<2>::keys, StreamPolicy<2>::wgs);
 }
 
 // Workspace: scores [rows, n_comp] f32 | len A, len B [rows] i64 |
@@ -1080,7 +1139,10 @@ static TopkLayout topk_layout(int64_t b, int64_t n_q, int64_t n_comp, int64_t k)
   const int64_t nch = (n_comp + kWaveChunk - 1) / kWaveChunk;
   L.nseg = nch;
   L.cap = nch > 1 ? nch * k : 0;
-  L.gcap = nch > 1 ? stream_splits(b, n_q, n_comp) * kStreamGroupsPerWG : 0;  // grows with n_comp
+  // grows with n_comp; the larger of the two element types' splits
+  L.gcap = nch > 1 ? std::max(stream_splits_for(1, b, n_q, n_comp), stream_splits_for(2, b, n_q, n_comp)) *
+                         kStreamGroupsPerWG
+                   : 0;
   size_t off = 0;
   L.scores = off; off = align256(off + (size_t)rows * n_comp * 4);
   L.lenA = off; off = align256(off + (size_t)rows * 8);
@@ -1115,9 +1177,11 @@ static hipError_t launch_scores_stream(const void* qI, const float* w, const voi
                                        int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, float* scores,
                                        uint32_t* gmax, int64_t ld_gmax, bool* gmax_used, hipStream_t st) {
   const int64_t vmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
-  const int64_t nsplit = stream_splits(b, n_q, vmax);
+  typedef StreamPolicy<(int)sizeof(E)> Pol;
+  const int64_t nsplit = stream_splits(b, n_q, vmax, Pol::keys, Pol::wgs);
   dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
-  hipLaunchKernelGGL((index_scores_stream<NHB, KS, kStreamRing, E>), grid, dim3(256), 0, st, (const E*)qI, w,
+  hipLaunchKernelGGL((index_scores_stream<NHB, KS, Pol::ring, E, (int)Pol::keys>), grid, dim3(256), 0, st,
+                     (const E*)qI, w,
                      (const E*)KI, cbs, n_q, t0, n_comp, m, scores, gmax, ld_gmax);
   *gmax_used = gmax != nullptr;
   return hipGetLastError();
@@ -1224,7 +1288,7 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
     // group maxima, a filtering pass per 2048-key segment, one exact merge
     uint32_t* tau = (uint32_t*)(W + L.tau);
     int32_t* cnt = (int32_t*)(W + L.cnt);
-    const int64_t G = stream_splits(b, n_q, lmax) * kStreamGroupsPerWG;
+    const int64_t G = stream_splits_for(dtype, b, n_q, lmax) * kStreamGroupsPerWG;
     hipLaunchKernelGGL(topk_threshold, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows,
                        k, tau);
     hipLaunchKernelGGL(topk_filter, dim3((unsigned)((rows * nseg + 3) / 4)), dim3(256), 0, st, scores, n_comp, tau,

@@ -205,8 +205,8 @@ def fp8_e4m3_decode(codes):
     """Values of 8-bit E4M3 codes (uint8 array), float64.
 
     The low-precision indexer of [P1] B9 (estimate paragraph) and B11 runs
-    the indexer's query/key path in a narrow float format; this build takes
-    the 8-bit E4M3 format of the OCP 8-bit floating point specification:
+    the indexer's query/key path in a narrow float format; the format taken
+    here is 8-bit E4M3 of the OCP 8-bit floating point specification:
     bit 7 sign, bits 6-3 exponent e (bias 7), bits 2-0 mantissa f; e = 0
     gives the subnormals (f / 8) * 2^-6, e > 0 gives (1 + f / 8) * 2^(e - 7);
     there are no infinities, and the two codes with e = 15, f = 7 are NaN.

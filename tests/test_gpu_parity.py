@@ -313,6 +313,28 @@ def test_index_topk_fp8(b, n_q, n_comp, k, nh, cI):
         assert np.max(np.abs(gs[sel] - ref)) <= 1e-3 * max(1.0, np.abs(ref).max())
 
 
+def test_index_topk_fp8_one_million_context_sampled():
+    # the 1M-token decode shape (8 sequences x 262144 entries, one query
+    # each, 64 x 128 indexer, k = 512) with E4M3 codes: the launch the
+    # decode step makes, checked on two sequences
+    say("index fp8 8 x 262144 entries (sampled sequences)")
+    b, n_comp, nh, cI, m, k = 8, 262144, 64, 128, 4, 512
+    gen = torch.Generator(device=DEV).manual_seed(29)
+    KI = synth.to_fp8(torch.randn((b, n_comp, cI), generator=gen, device=DEV) / math.sqrt(cI))
+    qI = synth.to_fp8(torch.randn((b, 1, nh, cI), generator=gen, device=DEV) / math.sqrt(cI))
+    w = torch.nn.functional.softplus(torch.randn((b, 1, nh), generator=gen, device=DEV))
+    t0 = n_comp * m - 1
+    idx, sc = L.csa_index_topk(qI, w, KI, t0, m, k, score=True)
+    torch.cuda.synchronize()
+    for s in (0, b - 1):
+        want, osc, vis = _fp8_oracle_index(qI[s].cpu(), w[s].cpu(), KI[s].cpu(), np.array([t0]), m, k)
+        assert vis[0] == n_comp
+        assert_index_sets(idx[s].cpu().numpy(), want, osc, vis, k, f"seq {s}")
+        gi, gs = idx[s, 0].cpu().numpy(), sc[s, 0].cpu().double().numpy()
+        ref = osc[0, gi]
+        assert np.max(np.abs(gs - ref)) <= 1e-3 * max(1.0, np.abs(ref).max())
+
+
 def test_index_topk_long_lists_rows_differ():
     # few queries whose visible counts differ (4095, 4095, 4096 entries)
     say("index long lists, rows with different visibility")
