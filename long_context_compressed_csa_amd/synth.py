@@ -74,6 +74,32 @@ def to_fp8(x):
     return x.float().to(torch.float8_e4m3fn)
 
 
+def to_mxfp4(x):
+    """Round a tensor to OCP MXFP4 along its last dimension (a multiple of
+    32): returns (codes, scales), uint8 tensors [..., c / 2] and [..., c / 32].
+    Each block of 32 takes the E8M0 scale 2^(floor(log2 max|x|) - 2) (the
+    largest E2M1 magnitude is 6 = 1.5 * 2^2); every element divided by it is
+    rounded to the nearest E2M1 value (the smaller magnitude on a tie) and
+    saturated at 6.  Byte j of a row holds element 2j in its low nibble and
+    element 2j + 1 in its high nibble.  An all-zero block gets scale 2^-127."""
+    x = x.float().cpu()
+    *lead, c = x.shape
+    assert c % 32 == 0, "MXFP4 blocks are 32 elements"
+    blk = x.reshape(*lead, c // 32, 32)
+    amax = blk.abs().amax(dim=-1, keepdim=True)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2,
+                    torch.full_like(amax, -127.0)).clamp(-127, 127)
+    y = (blk / torch.exp2(e)).abs()
+    mags = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    mids = (mags[1:] + mags[:-1]) / 2
+    code = torch.bucketize(y, mids)            # nearest magnitude (ties to the smaller)
+    code = code | torch.where(blk < 0, 8, 0)   # sign bit
+    code = code.reshape(*lead, c).to(torch.uint8)
+    codes = (code[..., 0::2] | (code[..., 1::2] << 4)).to(torch.uint8)
+    scales = (e.squeeze(-1) + 127).to(torch.uint8)
+    return codes, scales
+
+
 def tiny_inputs(seed=None, n=None):
     """The tiny float32 CSA layer."""
     p = dict(TINY)

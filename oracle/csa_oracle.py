@@ -32,7 +32,13 @@ design notes):
     min(k, n/m); [P5] section 2 ledger);
   * the sliding window for position t holds raw rows max(0, t-n_win+1)..t and
     is kept separate from the compressed entries, never de-duplicated ([P5]
-    section 2).
+    section 2);
+  * the low-precision indexer ([P1] B9 estimate paragraph and B11; [P2]
+    section 13.3; [P3] section 7, FP4 quantization-aware training): the
+    indexer queries and keys are taken as 8-bit E4M3 codes, or as OCP MXFP4
+    (E2M1 elements, one E8M0 power-of-two scale per 32 consecutive
+    dimensions); the scores are the same weighted ReLU sums of the values the
+    codes stand for.
 
 parity unpinned: none of the routines here.  Each has at least one test that
 pins it to something other than itself (closed forms, invariants, library
@@ -218,6 +224,46 @@ def fp8_e4m3_decode(codes):
     mag = np.where(e == 0, (f / 8.0) * 2.0 ** -6, (1.0 + f / 8.0) * np.exp2((e - 7).astype(F64)))
     out = sign * mag
     return np.where((e == 15) & ((c & 7) == 7), np.nan, out)
+
+
+def e2m1_decode(nibbles):
+    """Values of 4-bit E2M1 codes (integer array of 0..15), float64.
+
+    OCP Microscaling Formats (MX) specification v1.0, FP4 element: bit 3
+    sign, bits 2-1 exponent e (bias 1), bit 0 mantissa f; e = 0 gives the
+    subnormals f / 2, e > 0 gives (1 + f / 2) * 2^(e - 1).  No infinities or
+    NaN.  [P2] section 13.3 and [P3] section 7 put the indexer's query/key
+    path in this 4-bit format.
+    """
+    c = np.asarray(nibbles).astype(np.int64) & 15
+    sign = np.where(c >= 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    f = (c & 1).astype(F64)
+    mag = np.where(e == 0, f / 2.0, (1.0 + f / 2.0) * np.exp2((e - 1).astype(F64)))
+    return sign * mag
+
+
+def e8m0_decode(codes):
+    """Values of 8-bit E8M0 scales (uint8 array), float64: 2^(s - 127), and
+    NaN for s = 255 (OCP MX specification v1.0, shared scale)."""
+    s = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(s == 255, np.nan, np.exp2((s - 127).astype(F64)))
+
+
+def mxfp4_decode(codes, scales, block: int = 32):
+    """Values of MXFP4 vectors, float64 [..., c].
+
+    codes [..., c / 2] uint8: byte j holds element 2j in its low nibble and
+    element 2j + 1 in its high nibble; scales [..., c / block] uint8 E8M0:
+    element d is e2m1(code of d) * e8m0(scale of block d // block) (OCP MX
+    specification v1.0: one shared scale per block of 32 elements).
+    """
+    b = np.asarray(codes, dtype=np.uint8)
+    lo = e2m1_decode(b & 15)
+    hi = e2m1_decode(b >> 4)
+    el = np.stack([lo, hi], axis=-1).reshape(*b.shape[:-1], 2 * b.shape[-1])
+    sc = np.repeat(e8m0_decode(scales), block, axis=-1)
+    return el * sc
 
 
 def topk_select(scores_row, v: int, k: int):

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle as O
+from long_context_compressed_csa_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -427,3 +428,74 @@ def test_fp8_e4m3_decode_matches_torch():
     got = O.fp8_e4m3_decode(codes)
     assert np.array_equal(np.isnan(got), np.isnan(want))
     assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+
+
+# --------------------------------------------------------------- MXFP4 ----
+def test_e2m1_decode_fixed_values():
+    # the eight magnitudes the E2M1 format fixes (OCP MX specification v1.0,
+    # FP4 element), in code order, and their negatives under the sign bit
+    got = O.e2m1_decode(np.arange(16))
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(got[:8]) == mags
+    assert list(got[8:]) == [-v for v in mags]
+
+
+def test_e8m0_decode_matches_torch():
+    # library cross-check: torch's float8_e8m0fnu reads the same bytes the same way
+    codes = np.array([0, 1, 100, 126, 127, 128, 131, 200, 254], dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(O.e8m0_decode(codes), want)
+    assert np.isnan(O.e8m0_decode(np.array([255], dtype=np.uint8))[0])
+
+
+def test_mxfp4_decode_packing_and_block_scales():
+    # hand-made row of 64 elements: byte j = element 2j (low nibble) and
+    # element 2j+1 (high nibble); block 0 scaled by 2^-3, block 1 by 2^4
+    codes = np.zeros((1, 32), dtype=np.uint8)
+    codes[0, 0] = 0x72    # elements 0, 1 = 1.0, 6.0
+    codes[0, 15] = 0xA9   # elements 30, 31 = -0.5, -1.0
+    codes[0, 16] = 0x05   # elements 32, 33 = 3.0, 0.0
+    codes[0, 31] = 0xF3   # elements 62, 63 = 1.5, -6.0
+    scales = np.array([[127 - 3, 127 + 4]], dtype=np.uint8)
+    v = O.mxfp4_decode(codes, scales)
+    assert v.shape == (1, 64)
+    want = np.zeros(64)
+    want[[0, 1, 30, 31]] = np.array([1.0, 6.0, -0.5, -1.0]) / 8
+    want[[32, 33, 62, 63]] = np.array([3.0, 0.0, 1.5, -6.0]) * 16
+    assert np.array_equal(v[0], want)
+
+
+def test_mxfp4_roundtrip_of_representable_values():
+    # values that are exactly MXFP4 (an E2M1 magnitude times the block's
+    # power-of-two scale, with 6 * scale present in every block) survive the
+    # quantiser and the decoder unchanged
+    gen = torch.Generator().manual_seed(3)
+    mags = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    pick = torch.randint(0, 8, (5, 128), generator=gen)
+    sign = torch.where(torch.rand((5, 128), generator=gen) < 0.5, -1.0, 1.0)
+    x = mags[pick] * sign
+    x[:, ::32] = 6.0
+    blk_exp = torch.randint(-6, 7, (5, 4), generator=gen).float()
+    x = x * torch.exp2(blk_exp).repeat_interleave(32, dim=1)
+    codes, scales = synth.to_mxfp4(x)
+    assert np.array_equal(O.mxfp4_decode(codes.numpy(), scales.numpy()), x.double().numpy())
+
+
+def test_mxfp4_index_scores_equal_scores_of_decoded_values():
+    # the indexer over MXFP4 inputs is the indexer over the values they stand
+    # for: brute-force scalar loops on a tiny case
+    gen = torch.Generator().manual_seed(4)
+    q = torch.randn((2, 3, 64), generator=gen)
+    K = torch.randn((5, 64), generator=gen)
+    w = torch.rand((2, 3), generator=gen)
+    qc, qs = synth.to_mxfp4(q)
+    kc, ks = synth.to_mxfp4(K)
+    dq = O.mxfp4_decode(qc.numpy(), qs.numpy())
+    dk = O.mxfp4_decode(kc.numpy(), ks.numpy())
+    sc = O.index_scores(dq, w.double().numpy(), dk, [19, 19], 4)
+    for t in range(2):
+        for s_ in range(5):
+            ref = 0.0
+            for h in range(3):
+                ref += float(w[t, h]) * max(0.0, sum(dq[t, h, d] * dk[s_, d] for d in range(64)))
+            assert abs(sc[t, s_] - ref) <= 1e-12 * max(1.0, abs(ref))
