@@ -258,6 +258,39 @@ def run_decode(args, torch, L, synth):
     res["fp8_indexer"] = {"us_per_step": us8, "bytes_per_step": bytes8,
                           "hbm_gbs": bytes8 / (us8 * 1e-6) / 1e9,
                           "steps": f"the {n8} steps of a block that complete no entry"}
+    del KI8
+
+    # The FP4 indexer (OCP MXFP4 codes and block scales, quantised before
+    # timing), over the same steps.
+    KIc, KIs = synth.to_mxfp4(d["KIcomp"])
+    qIq = [synth.to_mxfp4(d["qI"][i]) for i in range(n8)]
+
+    def step4(i):
+        t = hist + i
+        n_comp = (t + 1) // m
+        rc = lib.csa_index_topk_mxfp4(P(qIq[i][0]), P(qIq[i][1]), P(d["w"][i]), P(KIc), P(KIs), cap, b, 1, t,
+                                      n_comp, nI, cI, m, k, P(idx), None, P(wsI), wsI_bytes, st)
+        rc |= lib.csa_attend(P(d["q"][i]), P(d["Ccomp"]), cap * c, P(idx), P(win), (nw + steps) * c, raw_pos0,
+                             P(d["sink"]), b, 1, t, n_comp, nw + steps, nh, c, k, m, nw, d["scale"], 1,
+                             P(wsA), wsA.numel(), P(out), st)
+        if rc != 0:
+            raise RuntimeError("mxfp4 decode step failed")
+
+    for i in range(n8):
+        step4(i)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        for i in range(n8):
+            step4(i)
+    bb.record()
+    torch.cuda.synchronize()
+    us4 = 1000.0 * a.elapsed_time(bb) / (reps * n8)
+    bytes4 = b * ne0 * (cI // 2 + cI // 32) + gathered + b * (nh * c * 2 * 2 + nI * (cI // 2 + cI // 32) + nI * 4
+                                                             + k * 4)
+    res["mxfp4_indexer"] = {"us_per_step": us4, "bytes_per_step": bytes4,
+                            "hbm_gbs": bytes4 / (us4 * 1e-6) / 1e9,
+                            "steps": f"the {n8} steps of a block that complete no entry"}
     return res
 
 

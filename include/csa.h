@@ -125,6 +125,41 @@ int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t c
 size_t csa_index_topk_workspace_size(int64_t b, int64_t n_q, int64_t n_comp, int64_t k);
 
 /*
+ * csa_index_topk_mxfp4 -- csa_index_topk with the indexer queries and keys
+ * in OCP MXFP4 (songhuiming "DeepSeek-V4 百万 token 上下文" section 13.3 and
+ * AirCoding "deepseek-paper-analysis" section 7, FP4 quantization-aware
+ * training: the indexer's query/key path is cached, loaded and multiplied
+ * in FP4; the element and scale formats are those of the OCP Microscaling
+ * (MX) specification v1.0, which the pages name for the expert weights).
+ * The scores are the weighted ReLU sums of the values the codes stand for,
+ * accumulated in float32; selection, ties and output are as for
+ * csa_index_topk.
+ *
+ *  qI        [b, n_q, n_hI, c_I/2] uint8  E2M1 codes, two per byte: byte j
+ *            holds element 2j in its low nibble, 2j+1 in its high nibble
+ *  qI_scale  [b, n_q, n_hI, c_I/32] uint8  E8M0 scale of each block of 32
+ *            elements: value = e2m1(code) * 2^(scale - 127)
+ *  w         [b, n_q, n_hI] float32
+ *  KIcomp    [b, *, c_I/2] uint8 codes and KI_scale [b, *, c_I/32] uint8
+ *            scales of the compressed keys, laid out the same way
+ *  comp_bstride  entries (rows) from one sequence's first key to the next's,
+ *            for both KIcomp and KI_scale (0 = n_comp)
+ *  idx, score, workspace: as for csa_index_topk (same workspace size).
+ *
+ * Scale 255 (NaN in the MX specification) is not supported.  All pointers
+ * are device memory owned by the caller; nothing is allocated.
+ * Errors: CSA_EINVAL as for csa_index_topk, also for NULL scale pointers or
+ * c_I not a multiple of 32; CSA_ENOTSUP for shapes without a kernel (the
+ * streaming kernel takes fewer than 4 queries with c_I = 128 and 32, 64 or
+ * 128 heads; every other shape needs n_hI * c_I <= 8192); CSA_ENOSPC if
+ * ws_bytes is too small.
+ */
+int csa_index_topk_mxfp4(const void* qI, const void* qI_scale, const float* w, const void* KIcomp,
+                         const void* KI_scale, int64_t comp_bstride, int64_t b, int64_t n_q, int64_t t0,
+                         int64_t n_comp, int64_t n_hI, int64_t c_I, int64_t m, int64_t k, int32_t* idx,
+                         float* score, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * csa_attend -- shared key/value multi-query attention over the selected
  * compressed entries plus the causal sliding window, with one softmax whose
  * denominator also holds the per-head sink (AirCoding

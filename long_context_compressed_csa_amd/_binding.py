@@ -37,6 +37,7 @@ SIGNATURES = {
     "csa_compress": (_int, [_vp] * 8 + [_i64] * 4 + [_int, _int, _vp, _i64, _vp]),
     "csa_index_topk": (_int, [_vp, _vp, _vp, _i64] + [_i64] * 8 + [_int, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_workspace_size": (_sz, [_i64] * 4),
+    "csa_index_topk_mxfp4": (_int, [_vp] * 5 + [_i64] * 9 + [_vp, _vp, _vp, _sz, _vp]),
     "csa_attend": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp] + [_i64] * 10
                    + [_f32, _int, _vp, _sz, _vp, _vp]),
     "csa_attend_workspace_size": (_sz, [_i64] * 9 + [_int]),
@@ -189,6 +190,37 @@ def csa_index_topk(qI, w, KIcomp, t0, m, k, n_comp=None, score=False, idx=None,
                             n_comp, nh, cI, m, k, dt, _ptr(idx), _ptr(sc), _ptr(workspace),
                             workspace.numel(), _stream(stream))
     _check(rc, "csa_index_topk")
+    return (idx, sc) if score else idx
+
+
+def csa_index_topk_mxfp4(qI, qI_scale, w, KIcomp, KI_scale, t0, m, k, n_comp=None, score=False, idx=None,
+                         workspace=None, stream=None):
+    """Indexer scores + top-k over OCP MXFP4 queries and keys.  qI [b, n_q,
+    n_hI, c_I/2] uint8 E2M1 pairs and qI_scale [b, n_q, n_hI, c_I/32] uint8
+    E8M0; w [b, n_q, n_hI] f32; KIcomp [b, cap, c_I/2] and KI_scale [b, cap,
+    c_I/32] uint8 (first n_comp rows used).  Returns idx int32 [b, n_q, k]
+    (and the scores when score=True)."""
+    qI, qI_scale, w = _batched(qI, 4), _batched(qI_scale, 4), _batched(w, 3)
+    KIcomp, KI_scale = _batched(KIcomp, 3), _batched(KI_scale, 3)
+    for t, name in ((qI, "qI"), (qI_scale, "qI_scale"), (KIcomp, "KIcomp"), (KI_scale, "KI_scale")):
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be uint8 (packed E2M1 codes or E8M0 scales)")
+    b, n_q, nh, half = qI.shape
+    cI = 2 * half
+    if KIcomp.shape[1] != KI_scale.shape[1] or KIcomp.shape[2] != half or KI_scale.shape[2] * 32 != cI:
+        raise ValueError("KIcomp / KI_scale shapes do not match qI")
+    n_comp = KIcomp.shape[1] if n_comp is None else n_comp
+    lib = load_library()
+    need = lib.csa_index_topk_workspace_size(b, n_q, n_comp, k)
+    if workspace is None:
+        workspace = _workspace(max(need, 256), qI.device)
+    if idx is None:
+        idx = torch.empty((b, n_q, k), dtype=torch.int32, device=qI.device)
+    sc = torch.empty((b, n_q, k), dtype=torch.float32, device=qI.device) if score else None
+    rc = lib.csa_index_topk_mxfp4(_ptr(qI), _ptr(qI_scale), _f32c(w, "w"), _ptr(KIcomp), _ptr(KI_scale),
+                                  KIcomp.shape[1], b, n_q, t0, n_comp, nh, cI, m, k, _ptr(idx), _ptr(sc),
+                                  _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "csa_index_topk_mxfp4")
     return (idx, sc) if score else idx
 
 

@@ -109,6 +109,26 @@ int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t c
                                          dtype, idx, score, workspace, (hipStream_t)stream));
 }
 
+int csa_index_topk_mxfp4(const void* qI, const void* qI_scale, const float* w, const void* KIcomp,
+                         const void* KI_scale, int64_t comp_bstride, int64_t b, int64_t n_q, int64_t t0,
+                         int64_t n_comp, int64_t n_hI, int64_t c_I, int64_t m, int64_t k, int32_t* idx,
+                         float* score, void* workspace, size_t ws_bytes, void* stream) {
+  if (!qI || !qI_scale || !w || !idx || !workspace) return CSA_EINVAL;
+  if (n_comp > 0 && (!KIcomp || !KI_scale)) return CSA_EINVAL;
+  if (b < 1 || n_q < 1 || n_hI < 1 || c_I < 1 || m < 1 || k < 1 || t0 < 0 || n_comp < 0)
+    return CSA_EINVAL;
+  if (c_I % 32 != 0) return CSA_EINVAL;
+  if (n_comp > visible(t0 + n_q - 1, m)) return CSA_EINVAL;
+  if (comp_bstride < 0 || (comp_bstride > 0 && comp_bstride < n_comp)) return CSA_EINVAL;
+  if (n_q > 65535 || b > 65535) return CSA_ENOTSUP;
+  if (!csa::index_topk_supported(n_comp, k) || !csa::index_topk_mx_supported(n_q, n_hI, c_I)) return CSA_ENOTSUP;
+  if (((uintptr_t)workspace & 255u) != 0) return CSA_EINVAL;
+  if (ws_bytes < csa::index_topk_workspace_bytes(b, n_q, n_comp, k)) return CSA_ENOSPC;
+  const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp;
+  return launched(csa::launch_index_topk_mx(qI, qI_scale, w, KIcomp, KI_scale, cbs, b, n_q, t0, n_comp, n_hI, c_I,
+                                            m, k, idx, score, workspace, (hipStream_t)stream));
+}
+
 size_t csa_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
                                  int64_t c, int64_t k, int64_t m, int64_t n_win, int dtype) {
   if (b < 1 || n_q < 1 || m < 1 || t0 < 0 || k < 0 || n_win < 1) return 0;

@@ -549,6 +549,223 @@ __global__ __launch_bounds__(256) void index_scores_stream(
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 scoring (OCP MX: E2M1 elements, one E8M0 scale per 32 dimensions).
+//
+// Streaming form (decode; c_I = 128): the layout of index_scores_stream with
+// 64-byte code rows, on the block-scaled MFMA v_mfma_scale_f32_32x32x64
+// (E2M1 x E2M1, float32 accumulation).  Per 64-dimension step a lane's
+// operand is 16 bytes = 32 consecutive dimensions of its row, i.e. exactly one
+// MX block, and the MFMA takes one scale byte per lane and operand (chosen by
+// an immediate byte select from a 32-bit register).  Queries and keys are
+// read in the same storage order, so the products pair the right elements
+// whatever order the unit uses inside a lane.  A tile's 32 scale words (4
+// bytes per key) reach LDS by one dword LDS-DMA next to the code DMA.
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void dma_dword(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
+}
+
+// 16 code bytes in the low half of the 32-byte operand (the E2M1 form reads
+// only that half)
+__device__ __forceinline__ i32x8 mx_operand(const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  return (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+}
+
+template <int NHB, int D, int SBK>
+__global__ __launch_bounds__(256) void index_scores_stream_mx(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qS, const float* __restrict__ w,
+    const uint8_t* __restrict__ KI, const uint8_t* __restrict__ KS, int64_t comp_bs, int64_t n_q, int64_t t0,
+    int64_t n_comp, int64_t m, float* __restrict__ scores, uint32_t* __restrict__ gmax, int64_t ld_gmax) {
+  constexpr int CI = 128;
+  constexpr int NH = NHB * 32;
+  constexpr int ROWB = CI / 2;       // code bytes per key row
+  constexpr int NB = CI / 32;        // scale bytes per key (one 32-bit word)
+  constexpr int NCH = ROWB / 16;     // 16-byte chunks per row
+  constexpr int KPI = 64 / NCH;      // rows per 1 KiB DMA instruction
+  constexpr int NDMA = NCH / 2;      // 1 KiB DMA instructions per 32-key tile
+  constexpr int SDIV = 16 / NCH;     // f(r) = (r / SDIV) % NCH spreads rows over the banks
+  constexpr int TU4 = 32 * NCH;      // 16-byte chunks per tile
+  static_assert(NB == 4, "one scale word per key");
+  __shared__ uint4 ring[4][D][TU4];
+  // a tile's 32 scale words (dword LDS-DMA writes lane l's word at 4 l)
+  __shared__ uint32_t sring[4][D][32];
+  __shared__ float sbuf[SBK];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  const int h = l >> 5;
+  const int64_t qrow = blockIdx.x;
+  const int64_t bi = blockIdx.z;
+  int64_t vis = (t0 + qrow + 1) / m;
+  if (vis > n_comp) vis = n_comp;
+  // 128-key chunks dealt to the gridDim.y workgroups round robin; wave w
+  // takes keys 32 w .. +32 of each chunk
+  const int64_t first = 128 * (int64_t)blockIdx.y + 32 * wave;
+  const int64_t kstep = 128 * (int64_t)gridDim.y;
+  const int64_t c1 = vis;
+  uint32_t gm = 0;
+  auto write_gmax = [&]() {
+    if (gmax == nullptr) return;
+    gm = max(gm, (uint32_t)__shfl_xor((int)gm, 1, 64));
+    gm = max(gm, (uint32_t)__shfl_xor((int)gm, 2, 64));
+    if (l < 32 && (l & 3) == 0)
+      gmax[(bi * n_q + qrow) * ld_gmax + (int64_t)blockIdx.y * 32 + wave * 8 + (l >> 2)] = gm;
+  };
+  if (vis <= 0) {
+    write_gmax();
+    return;
+  }
+  // at most SBK / 128 tiles per wave (the host splits each row over enough
+  // workgroups)
+  const int ntiles = first >= c1 ? 0 : (int)((c1 - first + kstep - 1) / kstep);
+  const uint8_t* kbase = KI + bi * comp_bs * ROWB;
+  const uint8_t* sbase = KS + bi * comp_bs * NB;
+  const int64_t lastkey = c1 - 1;
+  int src_off[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int r = i * KPI + l / NCH;
+    src_off[i] = r * ROWB + (((l % NCH) ^ ((r / SDIV) % NCH)) * 16);
+  }
+  auto issue = [&](int j, int slot) {
+    // rows past the last key re-read the last key (in bounds; their scores
+    // are dropped), and so does a tile wholly past the end
+    int64_t kb = first + kstep * j;
+    kb = kb < lastkey ? kb : lastkey;
+    const int room = (int)(lastkey - kb < 32 ? lastkey - kb : 32);
+    const uint32_t lds = (uint32_t)(uintptr_t)&ring[wave][slot][0];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int r = i * KPI + l / NCH;
+      const uint8_t* src = kbase + kb * ROWB + (r <= room ? src_off[i] : room * ROWB + (src_off[i] - r * ROWB));
+      dma_chunk16(src, lds + 1024 * i);
+    }
+    if (l < 32) {
+      const int r = l <= room ? l : room;
+      dma_dword(sbase + (kb + r) * NB, (uint32_t)(uintptr_t)&sring[wave][slot][0]);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) issue(j, j);
+
+  // query operands and scale words (shifted so that byte 0 / byte 2 select
+  // blocks h / 2 + h, the dimensions this lane's half holds in steps 0 / 1)
+  i32x8 qa[NHB][2];
+  uint32_t qsw[NHB];
+  float wv[NHB][16];
+  const int64_t qoff = (bi * n_q + qrow) * (int64_t)NH;
+#pragma unroll
+  for (int mb = 0; mb < NHB; ++mb) {
+    const int64_t hr = qoff + mb * 32 + (l & 31);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qa[mb][ks] = mx_operand(qI + hr * ROWB + 32 * ks + 16 * h);
+    qsw[mb] = *reinterpret_cast<const uint32_t*>(qS + hr * NB) >> (8 * h);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wv[mb][r] = w[qoff + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+  }
+
+  float* srow = scores + (bi * n_q + qrow) * n_comp;
+  const int rr = l & 31;
+  int rd_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) rd_off[ks] = rr * ROWB + ((((2 * ks + h)) ^ ((rr / SDIV) % NCH)) << 4);
+  auto compute = [&](int j, int slot) {
+    const unsigned char* tile = reinterpret_cast<const unsigned char*>(&ring[wave][slot][0]);
+    const uint32_t ksw = sring[wave][slot][rr] >> (8 * h);
+    const i32x8 b0 = mx_operand(tile + rd_off[0]);
+    const i32x8 b1 = mx_operand(tile + rd_off[1]);
+    f32x16 acc[NHB];
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb) {
+      acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][0], b0, (f32x16){}, 4, 4, 0, (int)qsw[mb], 0,
+                                                                 (int)ksw);
+      acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][1], b1, acc[mb], 4, 4, 2, (int)qsw[mb], 2,
+                                                                 (int)ksw);
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc = fmaf(fmaxf(acc[mb][r], 0.f), wv[mb][r], sc);
+    sc += __shfl_xor(sc, 32, 64);
+    const int64_t key = first + kstep * j + l;
+    if (l < 32) sbuf[128 * j + 32 * wave + l] = sc;
+    if (l < 32 && key < c1) gm = max(gm, f2key(sc));
+  };
+  // as in index_scores_stream, with NDMA + 1 loads per tile: before step j's
+  // reads the D - 1 tiles issued after tile j may still be in flight
+  int slot = 0;
+  for (int j = 0; j < ntiles; ++j) {
+    issue(j + D - 1, slot == 0 ? D - 1 : slot - 1);
+    wait_vmem<(D - 1) * (NDMA + 1)>();
+    compute(j, slot);
+    slot = slot == D - 1 ? 0 : slot + 1;
+  }
+  wait_vmem<0>();
+  write_gmax();
+  __syncthreads();
+  const int64_t nch = (c1 - 128 * (int64_t)blockIdx.y + kstep - 1) / kstep;
+  for (int e = threadIdx.x; e < nch * 128; e += 256) {
+    const int64_t key = 128 * ((int64_t)blockIdx.y + (int64_t)gridDim.y * (e >> 7)) + (e & 127);
+    if (key < c1) srow[key] = sbuf[e];
+  }
+}
+
+// Generic MXFP4 scoring (any head count, c_I a multiple of 32, n_hI * c_I
+// at most kMxGenericMaxQ): one thread per (key, query row); the row's query
+// values are decoded into LDS once; each key's values are decoded on the fly
+// (E2M1 times the block's E8M0 scale, both exact in float32) and the
+// products summed in dimension order.
+constexpr int kMxGenericMaxQ = 8192;
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+  const uint32_t e = (nib >> 1) & 3, f = nib & 1;
+  const float mag = e == 0 ? 0.5f * (float)f : (1.f + 0.5f * (float)f) * (float)(1u << (e - 1));
+  return (nib & 8) ? -mag : mag;
+}
+__device__ __forceinline__ float e8m0_value(uint32_t s) {
+  return s == 0 ? 0x1p-127f : __uint_as_float(s << 23);   // 2^(s - 127) (s = 255 gives inf, not NaN)
+}
+__global__ __launch_bounds__(256) void index_scores_generic_mx(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qS, const float* __restrict__ w,
+    const uint8_t* __restrict__ KI, const uint8_t* __restrict__ KS, int64_t comp_bs, int64_t n_q, int64_t t0,
+    int64_t n_comp, int nh, int cI, int64_t m, float* __restrict__ scores) {
+  __shared__ float qv[kMxGenericMaxQ];
+  const int64_t r = blockIdx.y, bi = blockIdx.z;
+  const int64_t qoff = (bi * n_q + r) * (int64_t)nh;
+  const int half = cI / 2, nb = cI / 32;
+  for (int e = threadIdx.x; e < nh * cI; e += 256) {
+    const int hh = e / cI, d = e % cI;
+    const uint8_t byte = qI[(qoff + hh) * half + d / 2];
+    qv[e] = e2m1_value((d & 1) ? (byte >> 4) : (byte & 15)) * e8m0_value(qS[(qoff + hh) * nb + d / 32]);
+  }
+  __syncthreads();
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= n_comp) return;
+  int64_t vis = (t0 + r + 1) / m;
+  if (vis > n_comp) vis = n_comp;
+  if (s >= vis) return;
+  float* out = scores + (bi * n_q + r) * n_comp + s;
+  const uint8_t* krow = KI + (bi * comp_bs + s) * half;
+  const uint8_t* srow = KS + (bi * comp_bs + s) * nb;
+  float acc = 0.f;
+  for (int hh = 0; hh < nh; ++hh) {
+    float dot = 0.f;
+    for (int d = 0; d < cI; d += 2) {
+      const uint8_t byte = krow[d / 2];
+      const float sc = e8m0_value(srow[d / 32]);
+      dot = fmaf(qv[hh * cI + d], e2m1_value(byte & 15) * sc, dot);
+      dot = fmaf(qv[hh * cI + d + 1], e2m1_value(byte >> 4) * sc, dot);
+    }
+    acc = fmaf(w[qoff + hh], fmaxf(dot, 0.f), acc);
+  }
+  *out = acc;
+}
+
+// ---------------------------------------------------------------------------
 // Top-k selection.  A segment (one query's candidate list, or one chunk of
 // it) is held in registers by NT threads (one wave or a 256-thread
 // workgroup), R keys each; element e of the segment sits in thread e % NT,
@@ -1121,7 +1338,12 @@ static int64_t stream_splits(int64_t b, int64_t n_q, int64_t vmax, int64_t keys,
   const int64_t chunks = (vmax + 127) / 128;
   return std::max<int64_t>(1, std::min(chunks, std::max(need, want)));
 }
+// MXFP4 codes: a tile is 2 KiB of codes and 128 bytes of scales, so a wave
+// has little in flight; small score buffers (2048 keys) let four workgroups
+// share a CU, and about four per CU are launched
+struct StreamPolicyMx { static constexpr int64_t keys = 2048, wgs = 1024; static constexpr int ring = 3; };
 static int64_t stream_splits_for(int dtype, int64_t b, int64_t n_q, int64_t vmax) {
+  if (dtype == 3) return stream_splits(b, n_q, vmax, StreamPolicyMx::keys, StreamPolicyMx::wgs);
   return dtype == 2 ? stream_splits(b, n_q, vmax, StreamPolicy<1>::keys, StreamPolicy<1>::wgs)
                     : stream_splits(b, n_q, vmax, StreamPolicy<2>::keys, StreamPolicy<2>::wgs);
 }
@@ -1139,8 +1361,9 @@ static TopkLayout topk_layout(int64_t b, int64_t n_q, int64_t n_comp, int64_t k)
   const int64_t nch = (n_comp + kWaveChunk - 1) / kWaveChunk;
   L.nseg = nch;
   L.cap = nch > 1 ? nch * k : 0;
-  // grows with n_comp; the larger of the two element types' splits
-  L.gcap = nch > 1 ? std::max(stream_splits_for(1, b, n_q, n_comp), stream_splits_for(2, b, n_q, n_comp)) *
+  // grows with n_comp; the largest of the element types' splits
+  L.gcap = nch > 1 ? std::max({stream_splits_for(1, b, n_q, n_comp), stream_splits_for(2, b, n_q, n_comp),
+                               stream_splits_for(3, b, n_q, n_comp)}) *
                          kStreamGroupsPerWG
                    : 0;
   size_t off = 0;
@@ -1213,6 +1436,68 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
   return hipGetLastError();
 }
 
+// Selection from the score rows in the workspace (every path's scoring
+// kernel leaves them there): the threshold path when the scorer recorded
+// group maxima, else wave segments and workgroup segments until one is left.
+static hipError_t finish_topk(const TopkLayout& L, unsigned char* W, float* scores, uint32_t* gmax,
+                              bool gmax_used, int dtype, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp,
+                              int64_t m, int64_t k, int32_t* idx, float* score, hipStream_t st) {
+  const int64_t rows = b * n_q;
+  int64_t lmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
+  int64_t nseg = std::max<int64_t>(1, (lmax + kWaveChunk - 1) / kWaveChunk);
+  // one wave per row when every list fits one segment
+  if (nseg == 1) {
+    const int64_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL((topk_stage<64, kWaveR>), dim3((unsigned)blocks), dim3(256), 0, st, 1, 1, scores,
+                       n_comp, nullptr, nullptr, 0, nullptr, nullptr, 0, idx, score, rows, n_q, t0, n_comp,
+                       m, k, nullptr, (int64_t)1);
+    return hipGetLastError();
+  }
+  uint32_t* kbuf[2] = {(uint32_t*)(W + L.kA), (uint32_t*)(W + L.kB)};
+  int32_t* ibuf[2] = {(int32_t*)(W + L.iA), (int32_t*)(W + L.iB)};
+  if (gmax_used) {
+    // threshold path: a lower bound on each row's k-th largest score from the
+    // group maxima, a filtering pass per 2048-key segment, one exact merge
+    uint32_t* tau = (uint32_t*)(W + L.tau);
+    int32_t* cnt = (int32_t*)(W + L.cnt);
+    const int64_t G = stream_splits_for(dtype, b, n_q, lmax) * kStreamGroupsPerWG;
+    hipLaunchKernelGGL(topk_threshold, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows,
+                       k, tau);
+    hipLaunchKernelGGL(topk_filter, dim3((unsigned)((rows * nseg + 3) / 4)), dim3(256), 0, st, scores, n_comp, tau,
+                       rows, n_q, t0, n_comp, m, k, nseg, kbuf[0], ibuf[0], L.cap, cnt);
+    hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(256), 0, st, kbuf[0], ibuf[0], L.cap, cnt, nseg, k,
+                       idx, score);
+    return hipGetLastError();
+  }
+  // general path: wave segments first, then workgroup segments until one
+  // segment is left
+  int64_t* lbuf[2] = {(int64_t*)(W + L.lenA), (int64_t*)(W + L.lenB)};
+  const unsigned lgrid = (unsigned)((rows + 255) / 256);
+  {
+    const int64_t blocks = (rows * nseg + 3) / 4;
+    hipLaunchKernelGGL((topk_stage<64, kWaveR>), dim3((unsigned)blocks), dim3(256), 0, st, 1, 0, scores,
+                       n_comp, nullptr, nullptr, 0, kbuf[0], ibuf[0], L.cap, nullptr, nullptr, rows, n_q, t0,
+                       n_comp, m, k, nullptr, nseg);
+    hipLaunchKernelGGL(topk_next_len, dim3(lgrid), dim3(256), 0, st, rows, n_q, t0, n_comp, m, k,
+                       kWaveChunk, nullptr, lbuf[0]);
+  }
+  lmax = (nseg - 1) * k + std::min<int64_t>(k, kWaveChunk);   // bound on every next list
+  int cur = 0;
+  while (true) {
+    const int64_t nseg2 = std::max<int64_t>(1, (lmax + kBlockChunk - 1) / kBlockChunk);
+    const int fin = nseg2 == 1 ? 1 : 0;
+    hipLaunchKernelGGL((topk_stage<256, kBlockR>), dim3((unsigned)(rows * nseg2)), dim3(256), 0, st, 0, fin,
+                       nullptr, 0, kbuf[cur], ibuf[cur], L.cap, kbuf[cur ^ 1], ibuf[cur ^ 1], L.cap, idx, score,
+                       rows, n_q, t0, n_comp, m, k, lbuf[cur], nseg2);
+    if (fin) break;
+    hipLaunchKernelGGL(topk_next_len, dim3(lgrid), dim3(256), 0, st, rows, n_q, t0, n_comp, m, k,
+                       kBlockChunk, lbuf[cur], lbuf[cur ^ 1]);
+    lmax = (nseg2 - 1) * k + std::min<int64_t>(k, kBlockChunk);
+    cur ^= 1;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int64_t cbs, int64_t b,
                              int64_t n_q, int64_t t0, int64_t n_comp, int64_t nh, int64_t cI,
                              int64_t m, int64_t k, int dtype, int32_t* idx, float* score,
@@ -1270,60 +1555,58 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
     if (err != hipSuccess) return err;
     if (fused && done) return hipSuccess;
   }
-  const int64_t rows = b * n_q;
-  int64_t lmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
-  int64_t nseg = std::max<int64_t>(1, (lmax + kWaveChunk - 1) / kWaveChunk);
-  // one wave per row when every list fits one segment
-  if (nseg == 1) {
-    const int64_t blocks = (rows + 3) / 4;
-    hipLaunchKernelGGL((topk_stage<64, kWaveR>), dim3((unsigned)blocks), dim3(256), 0, st, 1, 1, scores,
-                       n_comp, nullptr, nullptr, 0, nullptr, nullptr, 0, idx, score, rows, n_q, t0, n_comp,
-                       m, k, nullptr, (int64_t)1);
-    return hipGetLastError();
+  return finish_topk(L, W, scores, gmax, gmax_used, dtype, b, n_q, t0, n_comp, m, k, idx, score, st);
+}
+
+// MXFP4 queries and keys: the streaming scorer for few queries at c_I = 128
+// and 32-head multiples, generic scoring otherwise; the same selection.
+static bool mx_stream_shape(int64_t n_q, int64_t nh, int64_t cI) {
+  return n_q < 4 && cI == 128 && (nh == 32 || nh == 64 || nh == 128);
+}
+
+bool index_topk_mx_supported(int64_t n_q, int64_t nh, int64_t cI) {
+  if (cI < 32 || cI % 32 != 0) return false;
+  return mx_stream_shape(n_q, nh, cI) || nh * cI <= kMxGenericMaxQ;
+}
+
+hipError_t launch_index_topk_mx(const void* qI, const void* qS, const float* w, const void* KI, const void* KS,
+                                int64_t cbs, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t nh,
+                                int64_t cI, int64_t m, int64_t k, int32_t* idx, float* score, void* ws,
+                                hipStream_t st) {
+  const TopkLayout L = topk_layout(b, n_q, n_comp, k);
+  unsigned char* W = (unsigned char*)ws;
+  float* scores = (float*)(W + L.scores);
+  uint32_t* gmax = L.gcap > 0 ? (uint32_t*)(W + L.gmax) : nullptr;
+  bool gmax_used = false;
+  const uint8_t* q8 = (const uint8_t*)qI;
+  const uint8_t* qs8 = (const uint8_t*)qS;
+  const uint8_t* k8 = (const uint8_t*)KI;
+  const uint8_t* ks8 = (const uint8_t*)KS;
+  if (n_comp > 0) {
+    if (mx_stream_shape(n_q, nh, cI)) {
+      const int64_t vmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
+      const int64_t nsplit = stream_splits(b, n_q, vmax, StreamPolicyMx::keys, StreamPolicyMx::wgs);
+      dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
+      constexpr int D = StreamPolicyMx::ring, SBK = (int)StreamPolicyMx::keys;
+      if (nh == 32)
+        hipLaunchKernelGGL((index_scores_stream_mx<1, D, SBK>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs,
+                           n_q, t0, n_comp, m, scores, gmax, L.gcap);
+      else if (nh == 64)
+        hipLaunchKernelGGL((index_scores_stream_mx<2, D, SBK>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs,
+                           n_q, t0, n_comp, m, scores, gmax, L.gcap);
+      else
+        hipLaunchKernelGGL((index_scores_stream_mx<4, D, SBK>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs,
+                           n_q, t0, n_comp, m, scores, gmax, L.gcap);
+      gmax_used = gmax != nullptr;
+    } else {
+      dim3 grid((unsigned)((n_comp + 255) / 256), (unsigned)n_q, (unsigned)b);
+      hipLaunchKernelGGL(index_scores_generic_mx, grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs, n_q, t0,
+                         n_comp, (int)nh, (int)cI, m, scores);
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  uint32_t* kbuf[2] = {(uint32_t*)(W + L.kA), (uint32_t*)(W + L.kB)};
-  int32_t* ibuf[2] = {(int32_t*)(W + L.iA), (int32_t*)(W + L.iB)};
-  if (gmax_used) {
-    // threshold path: a lower bound on each row's k-th largest score from the
-    // group maxima, a filtering pass per 2048-key segment, one exact merge
-    uint32_t* tau = (uint32_t*)(W + L.tau);
-    int32_t* cnt = (int32_t*)(W + L.cnt);
-    const int64_t G = stream_splits_for(dtype, b, n_q, lmax) * kStreamGroupsPerWG;
-    hipLaunchKernelGGL(topk_threshold, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows,
-                       k, tau);
-    hipLaunchKernelGGL(topk_filter, dim3((unsigned)((rows * nseg + 3) / 4)), dim3(256), 0, st, scores, n_comp, tau,
-                       rows, n_q, t0, n_comp, m, k, nseg, kbuf[0], ibuf[0], L.cap, cnt);
-    hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(256), 0, st, kbuf[0], ibuf[0], L.cap, cnt, nseg, k,
-                       idx, score);
-    return hipGetLastError();
-  }
-  // general path: wave segments first, then workgroup segments until one
-  // segment is left
-  int64_t* lbuf[2] = {(int64_t*)(W + L.lenA), (int64_t*)(W + L.lenB)};
-  const unsigned lgrid = (unsigned)((rows + 255) / 256);
-  {
-    const int64_t blocks = (rows * nseg + 3) / 4;
-    hipLaunchKernelGGL((topk_stage<64, kWaveR>), dim3((unsigned)blocks), dim3(256), 0, st, 1, 0, scores,
-                       n_comp, nullptr, nullptr, 0, kbuf[0], ibuf[0], L.cap, nullptr, nullptr, rows, n_q, t0,
-                       n_comp, m, k, nullptr, nseg);
-    hipLaunchKernelGGL(topk_next_len, dim3(lgrid), dim3(256), 0, st, rows, n_q, t0, n_comp, m, k,
-                       kWaveChunk, nullptr, lbuf[0]);
-  }
-  lmax = (nseg - 1) * k + std::min<int64_t>(k, kWaveChunk);   // bound on every next list
-  int cur = 0;
-  while (true) {
-    const int64_t nseg2 = std::max<int64_t>(1, (lmax + kBlockChunk - 1) / kBlockChunk);
-    const int fin = nseg2 == 1 ? 1 : 0;
-    hipLaunchKernelGGL((topk_stage<256, kBlockR>), dim3((unsigned)(rows * nseg2)), dim3(256), 0, st, 0, fin,
-                       nullptr, 0, kbuf[cur], ibuf[cur], L.cap, kbuf[cur ^ 1], ibuf[cur ^ 1], L.cap, idx, score,
-                       rows, n_q, t0, n_comp, m, k, lbuf[cur], nseg2);
-    if (fin) break;
-    hipLaunchKernelGGL(topk_next_len, dim3(lgrid), dim3(256), 0, st, rows, n_q, t0, n_comp, m, k,
-                       kBlockChunk, lbuf[cur], lbuf[cur ^ 1]);
-    lmax = (nseg2 - 1) * k + std::min<int64_t>(k, kBlockChunk);
-    cur ^= 1;
-  }
-  return hipGetLastError();
+  return finish_topk(L, W, scores, gmax, gmax_used, 3, b, n_q, t0, n_comp, m, k, idx, score, st);
 }
 
 }  // namespace csa

@@ -82,7 +82,7 @@ def to_mxfp4(x):
     rounded to the nearest E2M1 value (the smaller magnitude on a tie) and
     saturated at 6.  Byte j of a row holds element 2j in its low nibble and
     element 2j + 1 in its high nibble.  An all-zero block gets scale 2^-127."""
-    x = x.float().cpu()
+    x = x.float()
     *lead, c = x.shape
     assert c % 32 == 0, "MXFP4 blocks are 32 elements"
     blk = x.reshape(*lead, c // 32, 32)
@@ -90,7 +90,7 @@ def to_mxfp4(x):
     e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2,
                     torch.full_like(amax, -127.0)).clamp(-127, 127)
     y = (blk / torch.exp2(e)).abs()
-    mags = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    mags = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device=x.device)
     mids = (mags[1:] + mags[:-1]) / 2
     code = torch.bucketize(y, mids)            # nearest magnitude (ties to the smaller)
     code = code | torch.where(blk < 0, 8, 0)   # sign bit

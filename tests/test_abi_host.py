@@ -102,6 +102,28 @@ def test_index_topk_rejects_bad_arguments(lib):
     assert _topk(lib, n_q=1, t0=4 * 10000, n_comp=10000, k=4000, ws_bytes=1 << 30) == ENOTSUP
 
 
+def _topk_mx(lib, ws_bytes=1 << 20, **kw):
+    a = dict(qI=FAKE, qS=FAKE, w=FAKE, KI=FAKE, KS=FAKE, cbs=0, b=1, n_q=8, t0=0, n_comp=2, nh=2, cI=64, m=4,
+             k=4, idx=FAKE, score=None, ws=0x100000)
+    a.update(kw)
+    return lib.csa_index_topk_mxfp4(a["qI"], a["qS"], a["w"], a["KI"], a["KS"], a["cbs"], a["b"], a["n_q"],
+                                    a["t0"], a["n_comp"], a["nh"], a["cI"], a["m"], a["k"], a["idx"],
+                                    a["score"], a["ws"], ws_bytes, None)
+
+
+def test_index_topk_mxfp4_rejects_bad_arguments(lib):
+    assert _topk_mx(lib, qS=None) == EINVAL
+    assert _topk_mx(lib, KS=None) == EINVAL
+    assert _topk_mx(lib, cI=48) == EINVAL          # MX blocks are 32 elements
+    assert _topk_mx(lib, k=0) == EINVAL
+    assert _topk_mx(lib, n_comp=3) == EINVAL       # 8 queries from t0=0 complete only 2 entries
+    assert _topk_mx(lib, cbs=1) == EINVAL          # fewer rows per sequence than n_comp
+    assert _topk_mx(lib, ws=0x100010) == EINVAL
+    assert _topk_mx(lib, ws_bytes=16) == ENOSPC
+    # generic scoring holds the row's query values in LDS: n_hI * c_I <= 8192
+    assert _topk_mx(lib, nh=128, cI=96) == ENOTSUP
+
+
 def test_index_topk_workspace_size_grows_with_candidates(lib):
     small = lib.csa_index_topk_workspace_size(1, 4, 100, 8)
     big = lib.csa_index_topk_workspace_size(1, 4, 100000, 8)

@@ -335,6 +335,91 @@ def test_index_topk_fp8_one_million_context_sampled():
         assert np.max(np.abs(gs - ref)) <= 1e-3 * max(1.0, np.abs(ref).max())
 
 
+def _mx_oracle_index(qc, qs, w, kc, ks, t_pos, m, k):
+    # the oracle scores the values the MXFP4 codes stand for
+    dq = O.mxfp4_decode(qc.numpy(), qs.numpy())
+    dk = O.mxfp4_decode(kc.numpy(), ks.numpy())
+    sc = O.index_scores(dq, to64(w), dk, t_pos, m)
+    n_comp = kc.shape[0]
+    vis = np.array([min((int(t) + 1) // m, n_comp) for t in t_pos])
+    idx = np.stack([O.topk_select(sc[r], vis[r], k) for r in range(len(t_pos))])
+    return idx, sc, vis
+
+
+@pytest.mark.parametrize("b,n_q,n_comp,k,nh,cI", [
+    (2, 1, 20000, 512, 64, 128),    # streaming MXFP4 scorer, threshold selection
+    (2, 3, 1500, 100, 64, 128),     # streaming, one segment per row, rows of different length
+    (1, 2, 9000, 300, 32, 128),     # 32 heads
+    (1, 1, 5000, 200, 128, 128),    # 128 heads
+    (1, 6, 1200, 64, 64, 128),      # four or more queries: generic scoring
+    (1, 2, 700, 40, 48, 64),        # no streaming kernel for this shape: generic scoring
+])
+def test_index_topk_mxfp4(b, n_q, n_comp, k, nh, cI):
+    # MXFP4 indexer queries and keys: the same selection as the oracle's over
+    # the decoded values, apart from near ties
+    say(f"index mxfp4 b={b} n_q={n_q} n_comp={n_comp} k={k} nh={nh} cI={cI}")
+    m = 4
+    t0 = n_comp * m - n_q
+    gen = torch.Generator().manual_seed(31)
+    qc, qs = synth.to_mxfp4(torch.randn((b, n_q, nh, cI), generator=gen) / math.sqrt(cI))
+    kc, ks = synth.to_mxfp4(torch.randn((b, n_comp, cI), generator=gen) / math.sqrt(cI))
+    w = torch.nn.functional.softplus(torch.randn((b, n_q, nh), generator=gen))
+    idx, sc = L.csa_index_topk_mxfp4(g(qc), g(qs), g(w), g(kc), g(ks), t0, m, k, score=True)
+    torch.cuda.synchronize()
+    for s in range(b):
+        want, osc, vis = _mx_oracle_index(qc[s], qs[s], w[s], kc[s], ks[s], np.arange(t0, t0 + n_q), m, k)
+        assert_index_sets(idx[s].cpu().numpy(), want, osc, vis, k, f"seq {s}")
+        gi, gs = idx[s].cpu().numpy(), sc[s].cpu().double().numpy()
+        sel = gi >= 0
+        ref = osc[np.nonzero(sel)[0], gi[sel]]
+        assert np.max(np.abs(gs[sel] - ref)) <= 1e-4 * max(1.0, np.abs(ref).max())
+
+
+def test_index_topk_mxfp4_one_million_context_sampled():
+    # the 1M-token decode shape with MXFP4 codes (Gaussian keys and queries
+    # quantised on the GPU): the launch the decode step makes, checked on two
+    # sequences
+    say("index mxfp4 8 x 262144 entries (sampled sequences)")
+    b, n_comp, nh, cI, m, k = 8, 262144, 64, 128, 4, 512
+    gen = torch.Generator(device=DEV).manual_seed(37)
+    kc, ks = synth.to_mxfp4(torch.randn((b, n_comp, cI), generator=gen, device=DEV) / math.sqrt(cI))
+    qc, qs = synth.to_mxfp4(torch.randn((b, 1, nh, cI), generator=gen, device=DEV) / math.sqrt(cI))
+    w = torch.nn.functional.softplus(torch.randn((b, 1, nh), generator=gen, device=DEV))
+    t0 = n_comp * m - 1
+    idx, sc = L.csa_index_topk_mxfp4(qc, qs, w, kc, ks, t0, m, k, score=True)
+    torch.cuda.synchronize()
+    for s in (0, b - 1):
+        want, osc, vis = _mx_oracle_index(qc[s].cpu(), qs[s].cpu(), w[s].cpu(), kc[s].cpu(), ks[s].cpu(),
+                                          np.array([t0]), m, k)
+        assert vis[0] == n_comp
+        assert_index_sets(idx[s].cpu().numpy(), want, osc, vis, k, f"seq {s}")
+        gi, gs = idx[s, 0].cpu().numpy(), sc[s, 0].cpu().double().numpy()
+        ref = osc[0, gi]
+        assert np.max(np.abs(gs - ref)) <= 1e-4 * max(1.0, np.abs(ref).max())
+
+
+def test_index_topk_mxfp4_matches_decoded_fp32_path():
+    # the same codes through the float32 entry point (decoded on the host):
+    # identical selection, scores within float32 summation-order error
+    say("index mxfp4 vs decoded float32")
+    b, n_q, n_comp, nh, cI, m, k = 2, 1, 12000, 64, 128, 4, 256
+    gen = torch.Generator().manual_seed(41)
+    qc, qs = synth.to_mxfp4(torch.randn((b, n_q, nh, cI), generator=gen) / math.sqrt(cI))
+    kc, ks = synth.to_mxfp4(torch.randn((b, n_comp, cI), generator=gen) / math.sqrt(cI))
+    w = torch.nn.functional.softplus(torch.randn((b, n_q, nh), generator=gen))
+    t0 = n_comp * m - 1
+    dq = torch.from_numpy(O.mxfp4_decode(qc.numpy(), qs.numpy())).float()
+    dk = torch.from_numpy(O.mxfp4_decode(kc.numpy(), ks.numpy())).float()
+    i1, s1 = L.csa_index_topk_mxfp4(g(qc), g(qs), g(w), g(kc), g(ks), t0, m, k, score=True)
+    i2, s2 = L.csa_index_topk(g(dq), g(w), g(dk), t0, m, k, score=True)
+    torch.cuda.synchronize()
+    for s in range(b):
+        a1, a2 = set(i1[s, 0].cpu().tolist()), set(i2[s, 0].cpu().tolist())
+        assert len(a1 ^ a2) <= 4, len(a1 ^ a2)   # near-ties only
+        if a1 == a2:
+            assert torch.allclose(s1[s], s2[s], rtol=1e-5, atol=1e-6)
+
+
 def test_index_topk_long_lists_rows_differ():
     # few queries whose visible counts differ (4095, 4095, 4096 entries)
     say("index long lists, rows with different visibility")
