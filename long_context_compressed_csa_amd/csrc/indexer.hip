@@ -113,11 +113,14 @@ __device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[R], uint
   for (int r = 0; r < R; ++r) c += key[r] >= cand ? 1u : 0u;
   return wave_sum_small(c);
 }
-// The k-th largest key T of the list (more than k non-empty slots): the
-// largest T with at least k keys >= T, found bit by bit from the top below
-// the common prefix of the largest and smallest key.
+// A threshold T of the list (more than k non-empty slots) with at least k
+// keys >= T, found bit by bit from the top below the common prefix of the
+// largest and smallest key: the k-th largest key, unless a candidate with
+// exactly k keys at or above it turns up first (then *exact is set and those
+// k keys are the selection, ties included).
 template <int R>
-__device__ __forceinline__ uint32_t wave_kth(const uint32_t (&key)[R], int k) {
+__device__ __forceinline__ uint32_t wave_kth(const uint32_t (&key)[R], int k, bool* exact) {
+  *exact = false;
   uint32_t hi = 0, lo = 0xffffffffu;
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -133,7 +136,14 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&key)[R], int k) {
   uint32_t T = top == 31 ? 0u : (hi >> (top + 1)) << (top + 1);
   for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
-    if (wave_count_ge(key, cand) >= (uint32_t)k) T = cand;
+    const uint32_t c = wave_count_ge(key, cand);
+    if (c >= (uint32_t)k) {
+      T = cand;
+      if (c == (uint32_t)k) {
+        *exact = true;
+        break;
+      }
+    }
   }
   return T;
 }
@@ -149,7 +159,13 @@ __device__ __forceinline__ uint32_t wave_select(const uint32_t (&key)[R], int nv
     for (int r = 0; r < R; ++r) sel |= (key[r] != 0u ? 1u : 0u) << r;
     return sel;
   }
-  const uint32_t T = wave_kth(key, k);
+  bool exact;
+  const uint32_t T = wave_kth(key, k, &exact);
+  if (exact) {   // exactly k keys are >= T
+#pragma unroll
+    for (int r = 0; r < R; ++r) sel |= (key[r] >= T ? 1u : 0u) << r;
+    return sel;
+  }
   const uint32_t gt = T == 0xffffffffu ? 0u : wave_count_ge(key, T + 1);
   const uint32_t eq = wave_count_ge(key, T) - gt;
   const uint32_t need = (uint32_t)k - gt;
@@ -866,6 +882,10 @@ __device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const b
   lo = ~SegReduce<NT>::umax(~lo, red, wave, parity);
   const uint32_t diff = hi ^ lo;
   uint32_t T = 0;
+  // a candidate with exactly k keys at or above it settles the selection
+  // (ties included); the counts are the same in every lane, so the exit is
+  // uniform
+  bool exact = false;
   if (diff == 0) {
     T = hi;
   } else {
@@ -884,17 +904,32 @@ __device__ __forceinline__ void segment_select(const uint32_t (&key)[R], const b
           for (int r = 0; r < R; ++r)
             c[j] += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key[r] >= T + (uint32_t)(j + 1) * u));
         SegReduce<NT>::sum3(c, red, wave, parity);
-        T = c[2] >= (uint32_t)k ? T + 3u * u : c[1] >= (uint32_t)k ? T + 2u * u : c[0] >= (uint32_t)k ? T + u : T;
+        const int js = c[2] >= (uint32_t)k ? 3 : c[1] >= (uint32_t)k ? 2 : c[0] >= (uint32_t)k ? 1 : 0;
+        if (js > 0) {
+          T += (uint32_t)js * u;
+          if (c[js - 1] == (uint32_t)k) {
+            exact = true;
+            break;
+          }
+        }
       }
     }
-    for (; bit >= 0; --bit) {
+    for (; !exact && bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       uint32_t c = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) c += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key[r] >= cand));
       c = SegReduce<NT>::sum(c, red, wave, parity);
-      if (c >= (uint32_t)k) T = cand;
+      if (c >= (uint32_t)k) {
+        T = cand;
+        exact = c == (uint32_t)k;
+      }
     }
+  }
+  if (exact) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sel[r] = val[r] && key[r] >= T;
+    return;
   }
   segment_take<NT, R>(key, val, k, T, sel, red, pre, parity);
 }
@@ -1132,7 +1167,10 @@ __global__ __launch_bounds__(256) void topk_threshold(const uint32_t* __restrict
 #pragma unroll
       for (int r = 0; r < R; ++r) cc += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key[r] >= cand));
       cc = SegReduce<NT>::sum(cc, red, wave, parity);
-      if (cc >= (uint32_t)k) T = cand;
+      if (cc >= (uint32_t)k) {
+        T = cand;
+        if (cc == (uint32_t)k) break;   // the exact k-th largest maximum bounds it as well
+      }
     }
   }
   if (tid == 0) tau[row] = max(T, 1u);
