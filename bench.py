@@ -127,6 +127,26 @@ def run_prefill(args, torch, L, synth):
     timer.collect()
     stage_us = {name: timer.avg_us(name) for name, _ in stages}
 
+    # The FP4 indexer at this shape: the step's queries and keys quantised to
+    # MXFP4 before timing, the index + top-k timed like the stages (the step
+    # above keeps the bf16 indexer: the library has no quantising compressor).
+    qc, qs = synth.to_mxfp4(d["qI"])
+    kc, ks = synth.to_mxfp4(KI)
+
+    def index_mx():
+        return lib.csa_index_topk_mxfp4(P(qc), P(qs), P(d["w"]), P(kc), P(ks), 0, 1, n, 0, ne, nI, cI, m, k,
+                                        P(idx), None, P(ws), ws_bytes, st)
+
+    timer4 = KernelTimer(torch)
+    for _ in range(2):
+        index_mx()
+    for _ in range(args.steps):
+        if timer4.run("index_topk_mxfp4", index_mx) != 0:
+            raise RuntimeError("mxfp4 index failed")
+    timer4.collect()
+    index_mx_us = timer4.avg_us("index_topk_mxfp4")
+    del qc, qs, kc, ks
+
     sel, win = prefill_pairs(n, m, k, nw)
     flop_attend = (sel + win) * 4 * nh * c
     vis_pairs = sum(min((t + 1) // m, ne) for t in range(n))
@@ -140,6 +160,7 @@ def run_prefill(args, torch, L, synth):
         "flop_index": flop_index,
         "attend_tflops": att_tflops,
         "index_tflops": flop_index / (stage_us["index_topk"] * 1e-6) / 1e12,
+        "index_topk_mxfp4_us": index_mx_us,
         "step_tflops": (flop_attend + flop_index) / (ms * 1e-3) / 1e12,
         "inputs": d,
     }
@@ -581,6 +602,7 @@ def main(argv=None):
         "stage_us": pre["stage_us"],
         "step_mfma_frac": pre["step_tflops"] / PEAK_BF16_TFLOPS,
         "index_tflops": pre["index_tflops"],
+        "index_topk_mxfp4_us": pre["index_topk_mxfp4_us"],
     }
     if "decode_1m" in extras:
         line["decode_us_per_step"] = extras["decode_1m"]["us_per_step"]

@@ -731,6 +731,171 @@ __global__ __launch_bounds__(256) void index_scores_stream_mx(
   }
 }
 
+// Many-query MXFP4 scoring (prefill; c_I = 128): index_scores_mfma's
+// layout -- four queries per workgroup, one per wave, sharing 64-key tiles
+// that reach a 3-slot LDS ring by LDS-DMA two tiles ahead, one barrier per
+// tile -- with 64-byte code rows, the tile's 64 scale words DMA'd beside them
+// (16 per wave), and the block-scaled FP4 MFMA.  FUSED: every list fits one
+// workgroup (at most kFusedMaxKeys keys) and each wave selects its query's
+// top k from LDS as in index_scores_mfma; else the scores are written.
+template <int NHB, int FUSED>
+__global__ __launch_bounds__(256) void index_scores_mfma_mx(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qS, const float* __restrict__ w,
+    const uint8_t* __restrict__ KI, const uint8_t* __restrict__ KS, int64_t comp_bs, int64_t n_q, int64_t t0,
+    int64_t n_comp, int64_t m, int64_t n_qblocks, float* __restrict__ scores, int64_t k,
+    int32_t* __restrict__ idx, float* __restrict__ score_out) {
+  constexpr int CI = 128;
+  constexpr int NH = NHB * 32;
+  constexpr int TN = 64;                 // keys per tile
+  constexpr int ROWB = CI / 2;           // code bytes per key
+  constexpr int NB = CI / 32;            // scale bytes per key (one word)
+  constexpr int NCH = ROWB / 16;         // 16-byte chunks per row
+  constexpr int KPI = 64 / NCH;          // rows per 1 KiB DMA instruction (one per wave and tile)
+  constexpr int SDIV = 16 / NCH;
+  static_assert(KPI * 4 == TN, "one code DMA per wave and tile");
+  __shared__ uint4 ring[3][TN * NCH];
+  __shared__ uint32_t sring[3][TN];
+  __shared__ float ssc[FUSED ? 4 : 1][FUSED ? kFusedMaxKeys : 1];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int h = l >> 5;
+  const int64_t qb = n_qblocks - 1 - blockIdx.x;   // heaviest (latest) query blocks first
+  const int64_t bi = blockIdx.z;
+  const int64_t qrow = qb * 4 + wave;
+  const bool qvalid = qrow < n_q;
+  int64_t vis_q = qvalid ? (t0 + qrow + 1) / m : 0;
+  if (vis_q > n_comp) vis_q = n_comp;
+  int64_t last = qb * 4 + 3;
+  if (last > n_q - 1) last = n_q - 1;
+  int64_t c1 = (t0 + last + 1) / m;   // the workgroup's keys: 0 .. c1-1
+  if (c1 > n_comp) c1 = n_comp;
+  const int ntl = (int)((c1 + TN - 1) / TN);   // uniform over the workgroup
+
+  const uint8_t* kbase = KI + bi * comp_bs * ROWB;
+  const uint8_t* sbase = KS + bi * comp_bs * NB;
+  const int64_t lastkey = c1 - 1;
+  const int dr = wave * KPI + l / NCH;   // tile row this lane's code DMA fills
+  const int src_off = dr * ROWB + (((l % NCH) ^ ((dr / SDIV) % NCH)) * 16);
+  auto issue = [&](int j, int slot) {
+    int64_t kb = (int64_t)TN * j;
+    kb = kb < lastkey ? kb : lastkey;
+    const int room = (int)(lastkey - kb < TN ? lastkey - kb : TN);
+    const uint8_t* src = kbase + kb * ROWB + (dr <= room ? src_off : room * ROWB + (src_off - dr * ROWB));
+    dma_chunk16(src, (uint32_t)(uintptr_t)&ring[slot][0] + 1024 * wave);
+    if (l < 16) {
+      const int r = 16 * wave + l;
+      dma_dword(sbase + (kb + (r <= room ? r : room)) * NB, (uint32_t)(uintptr_t)&sring[slot][16 * wave]);
+    }
+  };
+  if (ntl > 0) {
+    issue(0, 0);
+    issue(1, 1);
+  }
+
+  // query operands (two 64-dimension steps), scale words shifted so that
+  // bytes 0 / 2 select the blocks this lane's half holds, head weights
+  i32x8 qa[NHB][2];
+  uint32_t qsw[NHB];
+  float wv[NHB][16];
+  const int64_t qoff = (bi * n_q + (qvalid ? qrow : 0)) * (int64_t)NH;
+#pragma unroll
+  for (int mb = 0; mb < NHB; ++mb) {
+    const int64_t hr = qoff + mb * 32 + (l & 31);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qa[mb][ks] = mx_operand(qI + hr * ROWB + 32 * ks + 16 * h);
+    qsw[mb] = *reinterpret_cast<const uint32_t*>(qS + hr * NB) >> (8 * h);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wv[mb][r] = qvalid ? w[qoff + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)] : 0.f;
+  }
+  // consume the operand loads before the key loop (see index_scores_mfma)
+#pragma unroll
+  for (int mb = 0; mb < NHB; ++mb) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)   // the four loaded dwords (a 32-byte vector has no host-side constraint)
+      asm volatile("" ::"v"(qa[mb][ks][0]), "v"(qa[mb][ks][1]), "v"(qa[mb][ks][2]), "v"(qa[mb][ks][3]));
+    asm volatile("" ::"v"(qsw[mb]));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(wv[mb][r]));
+  }
+
+  float* srow = scores + (bi * n_q + (qvalid ? qrow : 0)) * n_comp;
+  int rd_off[2][2];   // bytes from the slot's start: key row 32 nb + l % 32, chunk 2 ks + h
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = nb * 32 + (l & 31);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) rd_off[nb][ks] = r * ROWB + (((2 * ks + h) ^ ((r / SDIV) % NCH)) << 4);
+  }
+  int slot = 0;
+  for (int j = 0; j < ntl; ++j) {
+    // this wave's part of tile j has landed once at most tile j + 1's two
+    // loads are in flight; after the barrier every wave's part has
+    wait_vmem<2>();
+    __syncthreads();
+    issue(j + 2, slot == 0 ? 2 : slot - 1);
+    const int64_t kb = (int64_t)TN * j;
+    if (qvalid && kb < vis_q) {
+      const unsigned char* tile = reinterpret_cast<const unsigned char*>(&ring[slot][0]);
+      f32x16 acc[NHB][2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t ksw = sring[slot][32 * nb + (l & 31)] >> (8 * h);
+        const i32x8 b0 = mx_operand(tile + rd_off[nb][0]);
+        const i32x8 b1 = mx_operand(tile + rd_off[nb][1]);
+#pragma unroll
+        for (int mb = 0; mb < NHB; ++mb) {
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][0], b0, (f32x16){}, 4, 4, 0,
+                                                                       (int)qsw[mb], 0, (int)ksw);
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][1], b1, acc[mb][nb], 4, 4, 2,
+                                                                       (int)qsw[mb], 2, (int)ksw);
+        }
+      }
+      float s2[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float sacc = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < NHB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc = fmaf(fmaxf(acc[mb][nb][r], 0.f), wv[mb][r], sacc);
+        s2[nb] = sacc + __shfl_xor(sacc, 32, 64);
+      }
+      const int64_t cand = kb + l;
+      if (cand < vis_q) {
+        if constexpr (FUSED) ssc[wave][cand] = (l < 32) ? s2[0] : s2[1];
+        else srow[cand] = (l < 32) ? s2[0] : s2[1];
+      }
+    }
+    slot = slot == 2 ? 0 : slot + 1;
+  }
+  wait_vmem<0>();   // the look-ahead tiles past the end
+  if constexpr (FUSED) {
+    constexpr int R = kFusedMaxKeys / 64;
+    const int len = (int)vis_q;
+    uint32_t key[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) key[r] = r * 64 + l < len ? f2key(ssc[wave][r * 64 + l]) : 0u;
+    const uint32_t sel = wave_select<R>(key, len, (int)k);
+    uint32_t pos[R];
+    wave_positions<R>(sel, pos);
+    if (qvalid) {
+      const int64_t row = bi * n_q + qrow;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if ((sel >> r) & 1u) {
+          idx[row * k + pos[r]] = r * 64 + l;
+          if (score_out) score_out[row * k + pos[r]] = key2f(key[r]);
+        }
+      for (int64_t p = (len < k ? len : k) + l; p < k; p += 64) {
+        idx[row * k + p] = -1;
+        if (score_out) score_out[row * k + p] = 0.f;
+      }
+    }
+  }
+}
+
 // Generic MXFP4 scoring (any head count, c_I a multiple of 32, n_hI * c_I
 // at most kMxGenericMaxQ): one thread per (key, query row); the row's query
 // values are decoded into LDS once; each key's values are decoded on the fly
@@ -1604,7 +1769,7 @@ static bool mx_stream_shape(int64_t n_q, int64_t nh, int64_t cI) {
 
 bool index_topk_mx_supported(int64_t n_q, int64_t nh, int64_t cI) {
   if (cI < 32 || cI % 32 != 0) return false;
-  return mx_stream_shape(n_q, nh, cI) || nh * cI <= kMxGenericMaxQ;
+  return (cI == 128 && (nh == 32 || nh == 64 || nh == 128)) || nh * cI <= kMxGenericMaxQ;
 }
 
 hipError_t launch_index_topk_mx(const void* qI, const void* qS, const float* w, const void* KI, const void* KS,
@@ -1620,6 +1785,35 @@ hipError_t launch_index_topk_mx(const void* qI, const void* qS, const float* w, 
   const uint8_t* qs8 = (const uint8_t*)qS;
   const uint8_t* k8 = (const uint8_t*)KI;
   const uint8_t* ks8 = (const uint8_t*)KS;
+  const bool mfma_shape = cI == 128 && (nh == 32 || nh == 64 || nh == 128);
+  if (mfma_shape && n_q >= 4) {
+    // four queries per workgroup, every key of the block's lists in one
+    // workgroup; the selection is fused when every list fits it (also when
+    // n_comp == 0: the kernel writes the padding)
+    const bool fused = n_comp <= kFusedMaxKeys;
+    const int64_t nqb = (n_q + 3) / 4;
+    dim3 grid((unsigned)nqb, 1, (unsigned)b);
+    int32_t* fi = fused ? idx : nullptr;
+    float* fs = fused ? score : nullptr;
+#define CSA_MX_MFMA(NHB_)                                                                                        \
+  if (fused)                                                                                                      \
+    hipLaunchKernelGGL((index_scores_mfma_mx<NHB_, 1>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs, n_q, t0, \
+                       n_comp, m, nqb, scores, k, fi, fs);                                                         \
+  else                                                                                                            \
+    hipLaunchKernelGGL((index_scores_mfma_mx<NHB_, 0>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs, n_q, t0, \
+                       n_comp, m, nqb, scores, k, nullptr, nullptr);
+    if (nh == 32) {
+      CSA_MX_MFMA(1)
+    } else if (nh == 64) {
+      CSA_MX_MFMA(2)
+    } else {
+      CSA_MX_MFMA(4)
+    }
+#undef CSA_MX_MFMA
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || fused) return err;
+    return finish_topk(L, W, scores, gmax, false, 3, b, n_q, t0, n_comp, m, k, idx, score, st);
+  }
   if (n_comp > 0) {
     if (mx_stream_shape(n_q, nh, cI)) {
       const int64_t vmax = std::min<int64_t>((t0 + n_q) / m, n_comp);

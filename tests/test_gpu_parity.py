@@ -351,8 +351,12 @@ def _mx_oracle_index(qc, qs, w, kc, ks, t_pos, m, k):
     (2, 3, 1500, 100, 64, 128),     # streaming, one segment per row, rows of different length
     (1, 2, 9000, 300, 32, 128),     # 32 heads
     (1, 1, 5000, 200, 128, 128),    # 128 heads
-    (1, 6, 1200, 64, 64, 128),      # four or more queries: generic scoring
-    (1, 2, 700, 40, 48, 64),        # no streaming kernel for this shape: generic scoring
+    (1, 6, 1200, 64, 64, 128),      # four or more queries: MFMA scorer with fused selection
+    (2, 37, 1500, 300, 32, 128),    # fused, 32 heads, a partial last query block
+    (1, 5, 600, 40, 128, 128),      # fused, 128 heads
+    (1, 9, 3000, 100, 64, 128),     # lists longer than one workgroup: MFMA scores + general selection
+    (1, 6, 1200, 64, 48, 64),       # no MFMA kernel for this shape: generic scoring
+    (1, 2, 700, 40, 48, 64),        # the same with few queries
 ])
 def test_index_topk_mxfp4(b, n_q, n_comp, k, nh, cI):
     # MXFP4 indexer queries and keys: the same selection as the oracle's over
@@ -396,6 +400,23 @@ def test_index_topk_mxfp4_one_million_context_sampled():
         gi, gs = idx[s, 0].cpu().numpy(), sc[s, 0].cpu().double().numpy()
         ref = osc[0, gi]
         assert np.max(np.abs(gs - ref)) <= 1e-4 * max(1.0, np.abs(ref).max())
+
+
+def test_index_topk_mxfp4_prefill_full_size_sampled():
+    # the CSA prefill shape (n = 8192, 2048 entries, 64 x 128 indexer, k =
+    # 512) with MXFP4 codes: fused MFMA scorer, sampled queries
+    say("index mxfp4 prefill n=8192 (sampled queries)")
+    d = synth.prefill_inputs()
+    p = d["params"]
+    qc, qs = synth.to_mxfp4(d["qI"].float())
+    kc, ks = synth.to_mxfp4(d["KIcomp"].float())
+    idx, sc = L.csa_index_topk_mxfp4(g(qc), g(qs), g(d["w"]), g(kc), g(ks), 0, p["m"], p["k"], score=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(2040, 2056), np.arange(8184, 8192),
+                                     np.random.default_rng(1).integers(0, 8192, 40)]))
+    want, osc, vis = _mx_oracle_index(qc[rows], qs[rows], d["w"][rows], kc, ks, rows, p["m"], p["k"])
+    nt = assert_index_sets(idx[0, rows].cpu().numpy(), want, osc, vis, p["k"])
+    say(f"  sampled {len(rows)} queries, near-ties: {nt}")
 
 
 def test_index_topk_mxfp4_matches_decoded_fp32_path():
