@@ -266,6 +266,37 @@ def mxfp4_decode(codes, scales, block: int = 32):
     return el * sc
 
 
+def mxfp4_encode(x, block: int = 32):
+    """OCP MXFP4 encoding of x [..., c] (c a multiple of 32), float64 steps.
+
+    OCP MX specification v1.0, conversion to an MX format: each block of 32
+    takes the shared scale X = 2^(floor(log2 max|x|) - 2) (2 is the largest
+    E2M1 exponent), every element x / X is rounded to the nearest E2M1
+    magnitude, ties to the even code, and saturated at 6.  Reading taken
+    where the specification leaves a choice: an all-zero block gets scale
+    byte 0 (2^-127); the sign bit is set for x < 0 also when the magnitude
+    rounds to 0.  Returns (codes [..., c/2] uint8, element 2j in the low
+    nibble of byte j; scales [..., c/32] uint8, E8M0 biased by 127).
+    """
+    v = _f64(x)
+    *lead, c = v.shape
+    blk = v.reshape(*lead, c // block, block)
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))          # amax = f * 2^ex, f in [0.5, 1)
+    e = np.where(amax > 0, ex - 1 - 2, -127).clip(-127, 127)   # floor(log2 amax) - 2
+    y = np.abs(blk) / np.exp2(e.astype(F64))[..., None]
+    # nearest of 0, .5, 1, 1.5, 2, 3, 4, 6; on a midpoint the even code
+    # (mantissa bit 0) wins: the midpoints after codes 1, 3, 5 round up
+    mids = [(0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True), (5.0, False)]
+    code = np.zeros(y.shape, dtype=np.int64)
+    for mid, up in mids:
+        code += (y >= mid) if up else (y > mid)
+    code = code + np.where(blk < 0, 8, 0)
+    code = code.reshape(*lead, c)
+    codes = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return codes, (e + 127).astype(np.uint8)
+
+
 def topk_select(scores_row, v: int, k: int):
     """Indices of the top-k among the first v scores of one query.
 

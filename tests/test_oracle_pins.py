@@ -499,3 +499,51 @@ def test_mxfp4_index_scores_equal_scores_of_decoded_values():
             for h in range(3):
                 ref += float(w[t, h]) * max(0.0, sum(dq[t, h, d] * dk[s_, d] for d in range(64)))
             assert abs(sc[t, s_] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_mxfp4_encode_rounds_to_nearest_even_and_saturates():
+    # block maximum 4 (scale 2^0): the E2M1 midpoints and beyond, by the
+    # specification's round-to-nearest-even and saturation
+    x = np.zeros((1, 32))
+    vals = [4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.3, 2.9, -0.75, -5.5]
+    x[0, :len(vals)] = vals
+    codes, scales = O.mxfp4_encode(x)
+    assert scales[0, 0] == 127
+    got = O.mxfp4_decode(codes, scales)[0, :len(vals)]
+    assert list(got) == [4.0, 0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 0.5, 3.0, -1.0, -6.0]
+    # block maximum 7.9: still scale 2^0, saturating at 6; maximum 8: scale 2^1
+    x[0, 0] = 7.9
+    c2, s2 = O.mxfp4_encode(x)
+    assert s2[0, 0] == 127 and O.mxfp4_decode(c2, s2)[0, 0] == 6.0
+    x[0, 0] = 8.0
+    c3, s3 = O.mxfp4_encode(x)
+    assert s3[0, 0] == 128 and O.mxfp4_decode(c3, s3)[0, 0] == 8.0
+
+
+def test_mxfp4_encode_decode_is_nearest_representable():
+    # brute force: every decoded element is a nearest point of its block's
+    # grid {+-m * X} (m an E2M1 magnitude, X the block scale), saturated
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 64)) * np.exp2(rng.integers(-20, 20, (6, 1)))
+    x[2, 32:] = 0.0                     # an all-zero block
+    codes, scales = O.mxfp4_encode(x)
+    dec = O.mxfp4_decode(codes, scales)
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    for r in range(6):
+        for bl in range(2):
+            X = 2.0 ** (int(scales[r, bl]) - 127)
+            for d in range(32 * bl, 32 * bl + 32):
+                grid = np.concatenate([mags, -mags]) * X
+                best = np.min(np.abs(grid - x[r, d]))
+                assert abs(dec[r, d] - x[r, d]) <= best * (1 + 1e-12) + 1e-300
+    assert scales[2, 1] == 0 and not dec[2, 32:].any()
+
+
+def test_mxfp4_encode_roundtrips_representable_values():
+    gen = np.random.default_rng(6)
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    x = mags[gen.integers(0, 8, (4, 96))] * np.where(gen.random((4, 96)) < 0.5, -1.0, 1.0)
+    x[:, ::32] = 6.0
+    x = x * np.repeat(np.exp2(gen.integers(-9, 9, (4, 3)).astype(float)), 32, axis=1)
+    codes, scales = O.mxfp4_encode(x)
+    assert np.array_equal(O.mxfp4_decode(codes, scales), x)
