@@ -145,6 +145,29 @@ def run_prefill(args, torch, L, synth):
             raise RuntimeError("mxfp4 index failed")
     timer4.collect()
     index_mx_us = timer4.avg_us("index_topk_mxfp4")
+
+    # A whole step with the FP4 indexer: the key compressor's bf16 output is
+    # encoded to MXFP4 by the library each step; the indexer queries are
+    # given as MXFP4 codes (as the bf16 step is given its bf16 queries).
+    def quant_keys():
+        return lib.csa_quantize_mxfp4(P(KI), cI, ne, cI, 1, P(kc), cI // 2, P(ks), cI // 32, st)
+
+    stages4 = [("compress_main", comp_main), ("compress_index_keys", comp_index), ("quantize_keys", quant_keys),
+               ("index_topk_mxfp4", index_mx), ("attend", attend)]
+
+    def step4():
+        for name, fn in stages4:
+            if fn() != 0:
+                raise RuntimeError(f"{name} failed")
+
+    for _ in range(args.warmup):
+        step4()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step4()
+    torch.cuda.synchronize()
+    ms4 = 1000.0 * (time.perf_counter() - t0) / args.steps
     del qc, qs, kc, ks
 
     sel, win = prefill_pairs(n, m, k, nw)
@@ -161,6 +184,9 @@ def run_prefill(args, torch, L, synth):
         "attend_tflops": att_tflops,
         "index_tflops": flop_index / (stage_us["index_topk"] * 1e-6) / 1e12,
         "index_topk_mxfp4_us": index_mx_us,
+        "mxfp4_step": {"ms_per_step": ms4, "tokens_per_s": n / (ms4 / 1000.0),
+                       "stages": [name for name, _ in stages4],
+                       "queries": "indexer queries given as MXFP4 codes"},
         "step_tflops": (flop_attend + flop_index) / (ms * 1e-3) / 1e12,
         "inputs": d,
     }
@@ -281,37 +307,53 @@ def run_decode(args, torch, L, synth):
                           "steps": f"the {n8} steps of a block that complete no entry"}
     del KI8
 
-    # The FP4 indexer (OCP MXFP4 codes and block scales, quantised before
-    # timing), over the same steps.
+    # The FP4 indexer (OCP MXFP4 codes and block scales): the key cache is
+    # encoded once before timing (the history), the step's indexer query is
+    # given as MXFP4 codes, and the block-completing step encodes its new key
+    # entry into the FP4 cache in place with the library's encoder.  All
+    # steps of the block are timed.
     KIc, KIs = synth.to_mxfp4(d["KIcomp"])
-    qIq = [synth.to_mxfp4(d["qI"][i]) for i in range(n8)]
+    qIq = [synth.to_mxfp4(d["qI"][i]) for i in range(steps)]
+    knew = torch.empty((b, 1, cI), dtype=torch.bfloat16, device="cuda")
 
     def step4(i):
         t = hist + i
+        rc = 0
+        if (t + 1) % m == 0:
+            e = (t + 1) // m - 1
+            rc |= lib.csa_compress(P(tails["Ca"]), P(tails["Cb"]), P(tails["Za"]), P(tails["Zb"]), P(d["Ba"]),
+                                   P(d["Bb"]), P(d["prev_Cb"]), P(d["prev_Zb"]), b, m, c, m, 1, 1,
+                                   d["Ccomp"][:, e].data_ptr(), cap * c, st)
+            rc |= lib.csa_compress(P(tails["ICa"]), P(tails["ICb"]), P(tails["IZa"]), P(tails["IZb"]),
+                                   P(d["IBa"]), P(d["IBb"]), P(d["prev_ICb"]), P(d["prev_IZb"]), b, m, cI, m,
+                                   1, 1, P(knew), cI, st)
+            rc |= lib.csa_quantize_mxfp4(P(knew), cI, b, cI, 1, KIc[:, e].data_ptr(), cap * (cI // 2),
+                                         KIs[:, e].data_ptr(), cap * (cI // 32), st)
         n_comp = (t + 1) // m
-        rc = lib.csa_index_topk_mxfp4(P(qIq[i][0]), P(qIq[i][1]), P(d["w"][i]), P(KIc), P(KIs), cap, b, 1, t,
-                                      n_comp, nI, cI, m, k, P(idx), None, P(wsI), wsI_bytes, st)
+        rc |= lib.csa_index_topk_mxfp4(P(qIq[i][0]), P(qIq[i][1]), P(d["w"][i]), P(KIc), P(KIs), cap, b, 1, t,
+                                       n_comp, nI, cI, m, k, P(idx), None, P(wsI), wsI_bytes, st)
         rc |= lib.csa_attend(P(d["q"][i]), P(d["Ccomp"]), cap * c, P(idx), P(win), (nw + steps) * c, raw_pos0,
                              P(d["sink"]), b, 1, t, n_comp, nw + steps, nh, c, k, m, nw, d["scale"], 1,
                              P(wsA), wsA.numel(), P(out), st)
         if rc != 0:
             raise RuntimeError("mxfp4 decode step failed")
 
-    for i in range(n8):
+    for i in range(steps):
         step4(i)
     torch.cuda.synchronize()
     a.record()
     for _ in range(reps):
-        for i in range(n8):
+        for i in range(steps):
             step4(i)
     bb.record()
     torch.cuda.synchronize()
-    us4 = 1000.0 * a.elapsed_time(bb) / (reps * n8)
+    us4 = 1000.0 * a.elapsed_time(bb) / (reps * steps)
     bytes4 = b * ne0 * (cI // 2 + cI // 32) + gathered + b * (nh * c * 2 * 2 + nI * (cI // 2 + cI // 32) + nI * 4
                                                              + k * 4)
     res["mxfp4_indexer"] = {"us_per_step": us4, "bytes_per_step": bytes4,
                             "hbm_gbs": bytes4 / (us4 * 1e-6) / 1e9,
-                            "steps": f"the {n8} steps of a block that complete no entry"}
+                            "steps": f"all {steps} steps of a block; the last appends one entry to each cache, "
+                                     "the key entry encoded to MXFP4 in place"}
     return res
 
 
@@ -603,6 +645,7 @@ def main(argv=None):
         "step_mfma_frac": pre["step_tflops"] / PEAK_BF16_TFLOPS,
         "index_tflops": pre["index_tflops"],
         "index_topk_mxfp4_us": pre["index_topk_mxfp4_us"],
+        "prefill_mxfp4_indexer": pre["mxfp4_step"],
     }
     if "decode_1m" in extras:
         line["decode_us_per_step"] = extras["decode_1m"]["us_per_step"]

@@ -160,6 +160,33 @@ int csa_index_topk_mxfp4(const void* qI, const void* qI_scale, const float* w, c
                          float* score, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * csa_quantize_mxfp4 -- OCP MXFP4 encoding of `rows` rows of c values, for
+ * the indexer's FP4 query/key cache (songhuiming "DeepSeek-V4 百万 token
+ * 上下文" section 13.3; AirCoding "deepseek-paper-analysis" section 7, FP4
+ * quantization-aware training): the layout csa_index_topk_mxfp4 reads.
+ * OCP Microscaling (MX) specification v1.0 conversion: each block of 32
+ * values gets the E8M0 scale 2^(floor(log2 max|v|) - 2); each value divided
+ * by it is rounded to the nearest E2M1 value, ties to the even code, and
+ * saturated at 6.  An all-zero block gets scale byte 0; the sign bit is set
+ * for every v < 0.
+ *
+ *  x       [rows][x_rstride] float32 (CSA_F32) or bf16 (CSA_BF16); the first
+ *          c of each row are encoded; 16-byte aligned, x_rstride * element
+ *          size a multiple of 16
+ *  codes   out [rows][codes_rstride] bytes, c/2 used per row (element 2j in
+ *          the low nibble of byte j); 16-byte aligned, codes_rstride a
+ *          multiple of 16
+ *  scales  out [rows][scales_rstride] bytes, c/32 used per row
+ * Strides let a call write rows into a cache in place (one row per sequence
+ * at entry e: x, codes and scales offset to entry e, strides = the batch
+ * strides).  NaN or infinite inputs are not supported.
+ * Errors: CSA_EINVAL for NULL pointers, rows < 1, c not a positive multiple of
+ * 32, strides below the row size or misaligned; CSA_ENOTSUP for another dtype.
+ */
+int csa_quantize_mxfp4(const void* x, int64_t x_rstride, int64_t rows, int64_t c, int dtype, void* codes,
+                       int64_t codes_rstride, void* scales, int64_t scales_rstride, void* stream);
+
+/*
  * csa_attend -- shared key/value multi-query attention over the selected
  * compressed entries plus the causal sliding window, with one softmax whose
  * denominator also holds the per-head sink (AirCoding

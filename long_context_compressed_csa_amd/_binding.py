@@ -38,6 +38,7 @@ SIGNATURES = {
     "csa_index_topk": (_int, [_vp, _vp, _vp, _i64] + [_i64] * 8 + [_int, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_workspace_size": (_sz, [_i64] * 4),
     "csa_index_topk_mxfp4": (_int, [_vp] * 5 + [_i64] * 9 + [_vp, _vp, _vp, _sz, _vp]),
+    "csa_quantize_mxfp4": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp]),
     "csa_attend": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp] + [_i64] * 10
                    + [_f32, _int, _vp, _sz, _vp, _vp]),
     "csa_attend_workspace_size": (_sz, [_i64] * 9 + [_int]),
@@ -222,6 +223,24 @@ def csa_index_topk_mxfp4(qI, qI_scale, w, KIcomp, KI_scale, t0, m, k, n_comp=Non
                                   _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "csa_index_topk_mxfp4")
     return (idx, sc) if score else idx
+
+
+def csa_quantize_mxfp4(x, codes=None, scales=None, stream=None):
+    """OCP MXFP4 encoding of x [..., c] (float32 or bf16, c a multiple of 32)
+    along its last dimension.  Returns (codes [..., c/2], scales [..., c/32])
+    uint8; given output tensors (any leading shape, rows flattened) are
+    filled in place."""
+    c = x.shape[-1]
+    rows = x.numel() // c
+    if codes is None:
+        codes = torch.empty((*x.shape[:-1], c // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((*x.shape[:-1], c // 32), dtype=torch.uint8, device=x.device)
+    lib = load_library()
+    rc = lib.csa_quantize_mxfp4(_ptr(x), c, rows, c, _dtype(x, x), _ptr(codes), c // 2, _ptr(scales), c // 32,
+                                _stream(stream))
+    _check(rc, "csa_quantize_mxfp4")
+    return codes, scales
 
 
 def csa_attend(q, Ccomp, idx, kv_raw, sink, t0, m, n_win, scale=None, raw_pos0=0,

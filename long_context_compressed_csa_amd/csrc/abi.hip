@@ -129,6 +129,21 @@ int csa_index_topk_mxfp4(const void* qI, const void* qI_scale, const float* w, c
                                             m, k, idx, score, workspace, (hipStream_t)stream));
 }
 
+int csa_quantize_mxfp4(const void* x, int64_t x_rstride, int64_t rows, int64_t c, int dtype, void* codes,
+                       int64_t codes_rstride, void* scales, int64_t scales_rstride, void* stream) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return CSA_ENOTSUP;
+  if (!x || !codes || !scales) return CSA_EINVAL;
+  if (rows < 1 || c < 32 || c % 32 != 0) return CSA_EINVAL;
+  if (x_rstride < c || codes_rstride < c / 2 || scales_rstride < c / 32) return CSA_EINVAL;
+  const int64_t es = dtype == CSA_F32 ? 4 : 2;
+  // 16-byte loads of the values and stores of the codes
+  if (((uintptr_t)x & 15u) != 0 || (x_rstride * es) % 16 != 0 || ((uintptr_t)codes & 15u) != 0 ||
+      codes_rstride % 16 != 0)
+    return CSA_EINVAL;
+  return launched(csa::launch_quantize_mxfp4(x, x_rstride, rows, c, dtype, codes, codes_rstride, scales,
+                                             scales_rstride, (hipStream_t)stream));
+}
+
 size_t csa_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
                                  int64_t c, int64_t k, int64_t m, int64_t n_win, int dtype) {
   if (b < 1 || n_q < 1 || m < 1 || t0 < 0 || k < 0 || n_win < 1) return 0;

@@ -18,6 +18,8 @@ hipError_t launch_compress(const void* Ca, const void* Cb, const void* Za, const
 size_t index_topk_workspace_bytes(int64_t b, int64_t n_q, int64_t n_comp, int64_t k);
 bool index_topk_supported(int64_t n_comp, int64_t k);
 bool index_topk_mx_supported(int64_t n_q, int64_t nh, int64_t cI);
+hipError_t launch_quantize_mxfp4(const void* x, int64_t xrs, int64_t rows, int64_t c, int dtype, void* codes,
+                                 int64_t crs, void* scales, int64_t srs, hipStream_t st);
 hipError_t launch_index_topk_mx(const void* qI, const void* qS, const float* w, const void* KI, const void* KS,
                                 int64_t cbs, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t nh,
                                 int64_t cI, int64_t m, int64_t k, int32_t* idx, float* score, void* ws,

@@ -124,6 +124,25 @@ def test_index_topk_mxfp4_rejects_bad_arguments(lib):
     assert _topk_mx(lib, nh=128, cI=96) == ENOTSUP
 
 
+def _quant(lib, **kw):
+    a = dict(x=0x100000, xrs=64, rows=4, c=64, dtype=1, codes=0x200000, crs=32, scales=FAKE, srs=2)
+    a.update(kw)
+    return lib.csa_quantize_mxfp4(a["x"], a["xrs"], a["rows"], a["c"], a["dtype"], a["codes"], a["crs"],
+                                  a["scales"], a["srs"], None)
+
+
+def test_quantize_mxfp4_rejects_bad_arguments(lib):
+    assert _quant(lib, dtype=2) == ENOTSUP
+    assert _quant(lib, x=None) == EINVAL
+    assert _quant(lib, scales=None) == EINVAL
+    assert _quant(lib, c=48) == EINVAL            # MX blocks are 32 values
+    assert _quant(lib, rows=0) == EINVAL
+    assert _quant(lib, xrs=32) == EINVAL          # stride below the row
+    assert _quant(lib, crs=16) == EINVAL          # c/2 = 32 code bytes per row
+    assert _quant(lib, codes=0x200008) == EINVAL  # 16-byte stores
+    assert _quant(lib, xrs=68) == EINVAL          # bf16 rows must stay 16-byte aligned
+
+
 def test_index_topk_workspace_size_grows_with_candidates(lib):
     small = lib.csa_index_topk_workspace_size(1, 4, 100, 8)
     big = lib.csa_index_topk_workspace_size(1, 4, 100000, 8)

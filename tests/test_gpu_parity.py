@@ -441,6 +441,61 @@ def test_index_topk_mxfp4_matches_decoded_fp32_path():
             assert torch.allclose(s1[s], s2[s], rtol=1e-5, atol=1e-6)
 
 
+def _mx_edge_rows(gen, c):
+    # Gaussian rows at several magnitudes plus blocks that hit every rule:
+    # all zero, values on each E2M1 midpoint of their block scale, saturation,
+    # negative zero-rounding, tiny (subnormal range) and large magnitudes
+    x = torch.randn((12, c), generator=gen) * torch.exp2(torch.randint(-30, 30, (12, 1), generator=gen).float())
+    x[0, :32] = 0.0
+    mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.9])
+    x[1, :32] = torch.cat([torch.tensor([4.0]), mids, -mids, torch.zeros(15)]) * 2.0 ** -5
+    x[2, :32] = torch.linspace(-7.99, 7.99, 32) * 2.0 ** 40
+    x[3, :32] = torch.cat([torch.tensor([1.0]), -torch.full((31,), 0.01)])
+    x[4, :32] = torch.randn(32, generator=gen) * 2.0 ** -130
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_mxfp4_bit_exact(dtype):
+    # codes and scales byte for byte against the oracle's encoder of the same values
+    say(f"quantize mxfp4 {dtype}")
+    gen = torch.Generator().manual_seed(43)
+    for c in (32, 128, 512):
+        x = _mx_edge_rows(gen, c).to(dtype)
+        codes, scales = L.csa_quantize_mxfp4(g(x))
+        torch.cuda.synchronize()
+        wc, wsc = O.mxfp4_encode(to64(x))
+        assert np.array_equal(scales.cpu().numpy(), wsc), f"c={c} scales"
+        assert np.array_equal(codes.cpu().numpy(), wc), f"c={c} codes"
+    # a large batch: every row Gaussian at its own magnitude
+    x = (torch.randn((4096, 128), generator=gen) * torch.exp2(torch.randint(-8, 8, (4096, 1), generator=gen).float()))
+    x = x.to(dtype)
+    codes, scales = L.csa_quantize_mxfp4(g(x))
+    torch.cuda.synchronize()
+    wc, wsc = O.mxfp4_encode(to64(x))
+    assert np.array_equal(scales.cpu().numpy(), wsc) and np.array_equal(codes.cpu().numpy(), wc)
+
+
+def test_quantize_mxfp4_appends_rows_in_place():
+    # one row per sequence written at entry e of [b, cap, ...] caches through
+    # the batch strides, the rest of the caches untouched (the decode append)
+    say("quantize mxfp4 in-place append")
+    lib = L.load_library()
+    b, cap, c, e = 3, 10, 128, 7
+    gen = torch.Generator().manual_seed(47)
+    src = g(torch.randn((b, cap, c), generator=gen).to(torch.bfloat16))
+    codes = torch.full((b, cap, c // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((b, cap, c // 32), 0xA5, dtype=torch.uint8, device=DEV)
+    rc = lib.csa_quantize_mxfp4(src[:, e].data_ptr(), cap * c, b, c, 1, codes[:, e].data_ptr(), cap * c // 2,
+                                scales[:, e].data_ptr(), cap * c // 32, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    wc, wsc = O.mxfp4_encode(to64(src[:, e].cpu()))
+    assert np.array_equal(codes[:, e].cpu().numpy(), wc) and np.array_equal(scales[:, e].cpu().numpy(), wsc)
+    rest = [i for i in range(cap) if i != e]
+    assert (codes[:, rest] == 0x5A).all() and (scales[:, rest] == 0xA5).all()
+
+
 def test_index_topk_long_lists_rows_differ():
     # few queries whose visible counts differ (4095, 4095, 4096 entries)
     say("index long lists, rows with different visibility")
