@@ -432,7 +432,9 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   constexpr int TU4 = 32 * NCH;      // 16-byte chunks per tile
   static_assert(NCH == 4 || NCH == 8 || NCH == 16, "c_I must be 64 or 128");
   __shared__ uint4 ring[4][D][TU4];
-  __shared__ float sbuf[SBK];  // the workgroup's scores (at most SBK), written out at the end
+  // SBK > 0: the workgroup's scores (at most SBK) collect here and leave in
+  // one burst at the end; SBK == 0: each tile's 128 bytes are stored as made
+  __shared__ float sbuf[SBK > 0 ? SBK : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const int64_t qrow = blockIdx.x;
@@ -462,8 +464,8 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     write_gmax();
     return;
   }
-  // at most SBK / 128 tiles per wave (the host splits each row over enough
-  // workgroups)
+  // SBK > 0: at most SBK / 128 tiles per wave (the host splits each row over
+  // enough workgroups)
   const int ntiles = first >= c1 ? 0 : (int)((c1 - first + kstep - 1) / kstep);
 
   const E* kbase = KI + bi * comp_bs;
@@ -534,7 +536,11 @@ __global__ __launch_bounds__(256) void index_scores_stream(
       for (int r = 0; r < 16; ++r) sc = fmaf(fmaxf(acc[mb][r], 0.f), wv[mb][r], sc);
     sc += __shfl_xor(sc, 32, 64);
     const int64_t key = first + kstep * j + l;
-    if (l < 32) sbuf[128 * j + 32 * wave + l] = sc;
+    if constexpr (SBK > 0) {
+      if (l < 32) sbuf[128 * j + 32 * wave + l] = sc;
+    } else {
+      if (l < 32 && key < c1) srow[key] = sc;
+    }
     if (l < 32 && key < c1) gm = max(gm, f2key(sc));
   };
   // tile j sits in slot j % D; step j first issues tile j + D - 1 into the
@@ -553,14 +559,17 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   }
   wait_vmem<0>();
   write_gmax();
-  // The scores leave in one pass of full-line stores per workgroup: storing
-  // each tile's 128 bytes as it is scored interleaves small writes with the
-  // key stream and costs about a tenth of the kernel's time.
-  __syncthreads();
-  const int64_t nch = (c1 - 128 * (int64_t)blockIdx.y + kstep - 1) / kstep;  // the workgroup's chunks
-  for (int e = threadIdx.x; e < nch * 128; e += 256) {
-    const int64_t key = 128 * ((int64_t)blockIdx.y + (int64_t)gridDim.y * (e >> 7)) + (e & 127);
-    if (key < c1) srow[key] = sbuf[e];
+  // SBK > 0: the scores leave in one pass of full-line stores per workgroup
+  // (for bf16 keys, storing each tile's 128 bytes as it is scored costs about
+  // a tenth of the kernel's time; for narrower keys the LDS the buffer takes
+  // is worth more as ring slots)
+  if constexpr (SBK > 0) {
+    __syncthreads();
+    const int64_t nch = (c1 - 128 * (int64_t)blockIdx.y + kstep - 1) / kstep;  // the workgroup's chunks
+    for (int e = threadIdx.x; e < nch * 128; e += 256) {
+      const int64_t key = 128 * ((int64_t)blockIdx.y + (int64_t)gridDim.y * (e >> 7)) + (e & 127);
+      if (key < c1) srow[key] = sbuf[e];
+    }
   }
 }
 
@@ -610,7 +619,9 @@ __global__ __launch_bounds__(256) void index_scores_stream_mx(
   __shared__ uint4 ring[4][D][TU4];
   // a tile's 32 scale words (dword LDS-DMA writes lane l's word at 4 l)
   __shared__ uint32_t sring[4][D][32];
-  __shared__ float sbuf[SBK];
+  // SBK > 0: the scores collect in LDS and leave in one burst at the end;
+  // SBK == 0: each tile's 32 scores (128 bytes) are stored as they are made
+  __shared__ float sbuf[SBK > 0 ? SBK : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const int h = l >> 5;
@@ -635,8 +646,8 @@ __global__ __launch_bounds__(256) void index_scores_stream_mx(
     write_gmax();
     return;
   }
-  // at most SBK / 128 tiles per wave (the host splits each row over enough
-  // workgroups)
+  // SBK > 0: at most SBK / 128 tiles per wave (the host splits each row over
+  // enough workgroups)
   const int ntiles = first >= c1 ? 0 : (int)((c1 - first + kstep - 1) / kstep);
   const uint8_t* kbase = KI + bi * comp_bs * ROWB;
   const uint8_t* sbase = KS + bi * comp_bs * NB;
@@ -709,7 +720,11 @@ __global__ __launch_bounds__(256) void index_scores_stream_mx(
       for (int r = 0; r < 16; ++r) sc = fmaf(fmaxf(acc[mb][r], 0.f), wv[mb][r], sc);
     sc += __shfl_xor(sc, 32, 64);
     const int64_t key = first + kstep * j + l;
-    if (l < 32) sbuf[128 * j + 32 * wave + l] = sc;
+    if constexpr (SBK > 0) {
+      if (l < 32) sbuf[128 * j + 32 * wave + l] = sc;
+    } else {
+      if (l < 32 && key < c1) srow[key] = sc;
+    }
     if (l < 32 && key < c1) gm = max(gm, f2key(sc));
   };
   // as in index_scores_stream, with NDMA + 1 loads per tile: before step j's
@@ -723,11 +738,13 @@ __global__ __launch_bounds__(256) void index_scores_stream_mx(
   }
   wait_vmem<0>();
   write_gmax();
-  __syncthreads();
-  const int64_t nch = (c1 - 128 * (int64_t)blockIdx.y + kstep - 1) / kstep;
-  for (int e = threadIdx.x; e < nch * 128; e += 256) {
-    const int64_t key = 128 * ((int64_t)blockIdx.y + (int64_t)gridDim.y * (e >> 7)) + (e & 127);
-    if (key < c1) srow[key] = sbuf[e];
+  if constexpr (SBK > 0) {
+    __syncthreads();
+    const int64_t nch = (c1 - 128 * (int64_t)blockIdx.y + kstep - 1) / kstep;
+    for (int e = threadIdx.x; e < nch * 128; e += 256) {
+      const int64_t key = 128 * ((int64_t)blockIdx.y + (int64_t)gridDim.y * (e >> 7)) + (e & 127);
+      if (key < c1) srow[key] = sbuf[e];
+    }
   }
 }
 
@@ -1536,15 +1553,18 @@ template <int ES> struct StreamPolicy;
 template <> struct StreamPolicy<2> { static constexpr int64_t keys = 16384, wgs = 256; static constexpr int ring = 3; };
 template <> struct StreamPolicy<1> { static constexpr int64_t keys = 8192, wgs = 512; static constexpr int ring = 3; };
 static int64_t stream_splits(int64_t b, int64_t n_q, int64_t vmax, int64_t keys, int64_t wgs) {
+  if (keys <= 0) keys = (int64_t)1 << 40;   // no score buffer: any split
   const int64_t need = (vmax + keys - 1) / keys;
   const int64_t want = wgs / std::max<int64_t>(1, b * n_q);
   const int64_t chunks = (vmax + 127) / 128;
   return std::max<int64_t>(1, std::min(chunks, std::max(need, want)));
 }
-// MXFP4 codes: a tile is 2 KiB of codes and 128 bytes of scales, so a wave
-// has little in flight; small score buffers (2048 keys) let four workgroups
-// share a CU, and about four per CU are launched
-struct StreamPolicyMx { static constexpr int64_t keys = 2048, wgs = 1024; static constexpr int ring = 3; };
+// MXFP4 codes: a tile is 2 KiB of codes and 128 bytes of scales, so what a
+// CU keeps in flight is bounded by its ring slots.  keys == 0: no score
+// buffer (each tile's 128 bytes of scores are stored as they are made), so
+// a 4-slot ring still fits four workgroups per CU, and a row may be split
+// over any number of workgroups; about four per CU are launched.
+struct StreamPolicyMx { static constexpr int64_t keys = 0, wgs = 1024; static constexpr int ring = 4; };
 static int64_t stream_splits_for(int dtype, int64_t b, int64_t n_q, int64_t vmax) {
   if (dtype == 3) return stream_splits(b, n_q, vmax, StreamPolicyMx::keys, StreamPolicyMx::wgs);
   return dtype == 2 ? stream_splits(b, n_q, vmax, StreamPolicy<1>::keys, StreamPolicy<1>::wgs)
