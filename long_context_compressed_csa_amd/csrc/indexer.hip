@@ -1299,18 +1299,19 @@ __device__ __forceinline__ int wave_count(const bool (&val)[R]) {
 }
 
 // tau[row] = a lower bound on the k-th largest of the row's first
-// min(G, 2048) group maxima, or 1 (every valid key) when fewer than k of them
-// are non-empty.  Each maximum is a distinct key of the row, so at least k
+// min(G, 256 R) group maxima, or 1 (every valid key) when fewer than k of
+// them are non-empty.  Each maximum is a distinct key of the row, so at least k
 // keys are >= tau.  The bound is the k-th largest found to kThresholdBits
 // bits below the common prefix of the largest and smallest maximum: the bit
 // search keeps count(>= T) >= k at every step, so stopping it early still
 // gives a valid bound, one that lets through only the keys within 2^-12 of
 // the maxima's range below the exact value.  One workgroup of 256 threads
-// (8 maxima each) per row.
+// (R maxima each) per row.
 constexpr int kThresholdBits = 12;
+template <int R>
 __global__ __launch_bounds__(256) void topk_threshold(const uint32_t* __restrict__ gmax, int64_t ld_gmax, int64_t G,
                                                       int64_t rows, int64_t k, uint32_t* __restrict__ tau) {
-  constexpr int NT = 256, R = 8;
+  constexpr int NT = 256;
   __shared__ uint32_t red[SegReduce<NT>::kRedSize];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -1684,8 +1685,11 @@ static hipError_t finish_topk(const TopkLayout& L, unsigned char* W, float* scor
     uint32_t* tau = (uint32_t*)(W + L.tau);
     int32_t* cnt = (int32_t*)(W + L.cnt);
     const int64_t G = stream_splits_for(dtype, b, n_q, lmax) * kStreamGroupsPerWG;
-    hipLaunchKernelGGL(topk_threshold, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows,
-                       k, tau);
+    // every maximum counts (up to 4096 per row: more of them, a tighter bound)
+    if (G > 2048)
+      hipLaunchKernelGGL(topk_threshold<16>, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows, k, tau);
+    else
+      hipLaunchKernelGGL(topk_threshold<8>, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows, k, tau);
     hipLaunchKernelGGL(topk_filter, dim3((unsigned)((rows * nseg + 3) / 4)), dim3(256), 0, st, scores, n_comp, tau,
                        rows, n_q, t0, n_comp, m, k, nseg, kbuf[0], ibuf[0], L.cap, cnt);
     hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(256), 0, st, kbuf[0], ibuf[0], L.cap, cnt, nseg, k,
