@@ -8,9 +8,12 @@
 // cooking-agi "DeepSeek-V4: 压缩历史以后，还能读到什么？" section 3).
 //
 // Scoring is a GEMM (query heads x keys, contracted over c_I) with a fused
-// ReLU * w reduction over the heads, so it runs on the bf16 MFMA unit: each
-// wave keeps its query's 32*NHB x c_I operand in registers and streams key
-// tiles through LDS.  Selection searches the k-th largest of the
+// ReLU * w reduction over the heads, so it runs on the MFMA unit -- bf16,
+// 8-bit E4M3, or block-scaled MXFP4 operands for the low-precision indexer
+// (songhuiming "DeepSeek-V4 百万 token 上下文" section 13.3, AirCoding
+// section 7: the indexer's query/key path in FP4): each wave keeps its
+// query's 32*NHB x c_I operand in registers and streams key tiles through
+// LDS.  Selection searches the k-th largest of the
 // order-preserving 32-bit images of the scores bit by bit, then compacts the
 // taken elements in list order, with a fixed reduction order everywhere.
 // Prefill (four or more queries, at most 2048 candidates) selects inside the
@@ -34,6 +37,8 @@ __device__ __forceinline__ void dma_chunk16(const void* src, uint32_t lds) {
                : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
 }
 // wait until at most N vector-memory operations of this wave are in flight
+// (loads, stores and LDS-DMA leave the counter in issue order on this
+// architecture, so a pending store only makes such a wait stricter)
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
