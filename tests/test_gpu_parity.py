@@ -655,6 +655,36 @@ def test_attend_prefill_full_size_sampled():
     assert_close(out[0, rows], want, torch.bfloat16)
 
 
+def test_larger_model_shapes_prefill_sampled():
+    # the pages' larger model's layer shapes (128 query heads, top-1024,
+    # window 128, indexer 64 x 128, m = 4) at n = 8192: the library's
+    # selection on sampled queries, and attention over blocks of queries
+    # (oracle indices) at their positions
+    say("larger model shapes: n_h=128, k=1024, n=8192 (sampled)")
+    d = synth.prefill_inputs(n_h=128, k=1024)
+    p = d["params"]
+    n, m, k, nw = p["n"], p["m"], p["k"], p["n_win"]
+    assert (p["n_h"], k) == (128, 1024)
+    idx, sc = L.csa_index_topk(g(d["qI"]), g(d["w"]), g(d["KIcomp"]), 0, m, k, score=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(4092, 4100), np.arange(8188, 8192),
+                                     np.random.default_rng(2).integers(0, n, 16)]))
+    want, osc, vis = _oracle_index(d["qI"][rows], d["w"][rows], d["KIcomp"], rows, m, k)
+    assert_index_sets(idx[0, rows].cpu().numpy(), want, osc, vis, k)
+    Cc = O.compress_overlap(*(to64(d[x]) for x in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m)
+    Cc16 = torch.tensor(Cc, dtype=torch.float32).to(torch.bfloat16)
+    for t0, nb in ((4090, 12), (8180, 12)):
+        t_pos = np.arange(t0, t0 + nb)
+        oi = _oracle_idx_for(d["KIcomp"], d["qI"][t0:t0 + nb], d["w"][t0:t0 + nb], t_pos, m, k)
+        n_comp = min((t0 + nb) // m, Cc16.shape[0])
+        out = L.csa_attend(g(d["q"][t0:t0 + nb]), g(Cc16), g(torch.tensor(oi, dtype=torch.int32)), g(d["kv_raw"]),
+                           g(d["sink"]), t0, m, nw, d["scale"], n_comp=n_comp)
+        torch.cuda.synchronize()
+        w_out = O.csa_attend(to64(d["q"][t0:t0 + nb]), to64(Cc16), oi, to64(d["kv_raw"]), 0, to64(d["sink"]),
+                             t_pos, nw, d["scale"], m)
+        assert_close(out[0], w_out, torch.bfloat16, f"t0={t0}")
+
+
 # -------------------------------------------------------------------- HCA --
 
 @pytest.mark.parametrize("n,mp,nw,nh,dtype", [
