@@ -253,7 +253,7 @@ def run_decode(args, torch, L, synth):
             raise RuntimeError(f"decode attend failed: {L.strerror(rc)}")
 
     reps = max(1, args.decode_reps)
-    for _ in range(2):
+    for _ in range(20):   # untimed, also brings the clocks to their steady state
         for i in range(steps):
             one_step(i)
     torch.cuda.synchronize()
@@ -377,7 +377,8 @@ def run_hca(args, torch, L, synth):
         if rc != 0:
             raise RuntimeError(f"hca_layer failed: {L.strerror(rc)}")
 
-    step()
+    for _ in range(2):   # untimed
+        step()
     torch.cuda.synchronize()
     a, b = _events(torch)
     iters = max(1, args.hca_iters)
@@ -416,7 +417,7 @@ def run_compress(args, torch, L, synth):
             call = lambda: lib.csa_compress(P(d["C"]), None, P(d["Z"]), None, P(d["B"]), None, None, None, 1, n,
                                             c, m, 0, 1, P(out), 0, st)
             nbytes = 2 * n * c * 2 + m * c * 2 + (n // m) * c * 2
-        for _ in range(3):
+        for _ in range(200):   # untimed, also brings the clocks to their steady state
             call()
         torch.cuda.synchronize()
         a, b = _events(torch)
@@ -568,7 +569,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps before the timed ones; about 50 prefill steps bring the GPU clocks to "
+                         "their steady state (dispatch times fall by about a fifth over the first 25)")
     ap.add_argument("--only", choices=["prefill", "decode", "hca", "compress"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=8192)
