@@ -397,6 +397,42 @@ def run_hca(args, torch, L, synth):
             "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop": flop}
 
 
+def run_hca_decode(args, torch, L, synth):
+    """HCA attention at the 1M-context decode shape: 8 sequences, each with
+    8192 completed HCA entries (m' = 128) and a 128-row window, one query."""
+    d = synth.hca_decode_inputs(device="cuda")
+    p = d["params"]
+    b, ne, c, nh, mp, nw, t = p["b"], p["n_comp"], p["c"], p["n_h"], p["m_prime"], p["n_win"], p["t"]
+    Cc, win, q, sink = d["Ccomp"], d["window"], d["q"], d["sink"]
+    lib = L.load_library()
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda t_: t_.data_ptr()
+    out = torch.empty_like(q)
+    wsb = max(lib.hca_attend_workspace_size(b, 1, t, ne, nh, c, mp, nw, 1), 256)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def call():
+        rc = lib.hca_attend(P(q), P(Cc), ne * c, P(win), nw * c, t - nw + 1, P(sink), b, 1, t, ne, nw, nh, c, mp,
+                            nw, 1.0 / math.sqrt(c), 1, P(ws), wsb, P(out), st)
+        if rc != 0:
+            raise RuntimeError(f"hca_attend failed: {L.strerror(rc)}")
+
+    for _ in range(50):   # untimed
+        call()
+    torch.cuda.synchronize()
+    a, bb = _events(torch)
+    iters = 100
+    a.record()
+    for _ in range(iters):
+        call()
+    bb.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * a.elapsed_time(bb) / iters
+    nbytes = b * (ne + nw) * c * 2 + b * nh * c * 2 * 2
+    return {"us_per_call": us, "bytes": nbytes, "hbm_gbs": nbytes / (us * 1e-6) / 1e9, "b": b, "entries": ne,
+            "n_win": nw}
+
+
 # ------------------------------------------------------------ compressor ----
 
 def run_compress(args, torch, L, synth):
@@ -612,6 +648,7 @@ def main(argv=None):
     if a.only in (None, "hca"):
         print("[bench] hca", file=sys.stderr, flush=True)
         extras["hca_prefill"] = run_hca(a, torch, L, synth)
+        extras["hca_decode_1m"] = run_hca_decode(a, torch, L, synth)
     if a.only in (None, "compress"):
         print("[bench] compress", file=sys.stderr, flush=True)
         extras["compressor"] = run_compress(a, torch, L, synth)

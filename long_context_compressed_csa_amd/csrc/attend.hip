@@ -623,6 +623,7 @@ __global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ 
   const float Mf = fmaxf(M, z2);
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
   for (int s = 0; s < nsplit; ++s) {
     const float ms = part_ml[((base + s) * kHG + hh) * 2];
     const float ls = part_ml[((base + s) * kHG + hh) * 2 + 1];
@@ -651,7 +652,9 @@ static bool attend_mfma_ok(int dtype, int64_t n_h, int64_t c, int64_t k) {
 static int attend_nsplit(int64_t b, int64_t n_q, int64_t n_h, int64_t nmax) {
   const int64_t items = b * n_q * (n_h / kHG);
   if (items >= 512) return 1;
-  int64_t ns = (1024 + items - 1) / items;
+  // about one workgroup per CU: every split also writes (and the combine
+  // reads) a 128 KiB float partial, which more splits would multiply
+  int64_t ns = (256 + items - 1) / items;
   // at least eight tiles per split: a split pays a fixed cost (index
   // compaction, the first gathers, a 128 KiB float partial written and
   // merged again) that fewer tiles do not amortise
@@ -695,6 +698,9 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
       part_o = (float*)ws;
       part_ml = (float*)((unsigned char*)ws + osz);
     }
+    // dense lists: two consecutive queries share each workgroup's tiles (a
+    // single query leaves the second pair of waves redundant; a one-query
+    // instance of the kernel spills and is no faster)
     const int G = dense ? 2 : 1;
     dim3 grid((unsigned)((n_q + G - 1) / G), (unsigned)((n_h / kHG) * ns), (unsigned)b);
     if (dense)

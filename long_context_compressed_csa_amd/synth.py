@@ -74,6 +74,21 @@ def to_fp8(x):
     return x.float().to(torch.float8_e4m3fn)
 
 
+def hca_decode_inputs(device="cpu", seed=9):
+    """HCA attention state at the 1M-context decode shape: 8 sequences, each
+    with 2^20 / 128 = 8192 completed HCA entries and a 128-row window, one
+    query per sequence; entries, window and queries N(0,1)/sqrt(c), sink
+    logits N(0,1)."""
+    p = dict(b=8, n_comp=8192, c=512, n_h=64, m_prime=128, n_win=128, t=(1 << 20) + 3)
+    g = _gen(seed, device)
+    b, ne, c, nh, nw = p["b"], p["n_comp"], p["c"], p["n_h"], p["n_win"]
+    return {"params": p,
+            "Ccomp": scaled((b, ne, c), g, torch.bfloat16, device),
+            "window": scaled((b, nw, c), g, torch.bfloat16, device),
+            "q": scaled((b, 1, nh, c), g, torch.bfloat16, device),
+            "sink": normal((nh,), g, 1.0, torch.float32, device)}
+
+
 def to_mxfp4(x):
     """Round a tensor to OCP MXFP4 along its last dimension (a multiple of
     32): returns (codes, scales), uint8 tensors [..., c / 2] and [..., c / 32].

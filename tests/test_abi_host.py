@@ -194,7 +194,7 @@ def test_attend_decode_needs_workspace(lib):
 
 def test_hca_layer_rejects_bad_arguments(lib):
     def call(**kw):
-        a = dict(C=FAKE, Z=FAKE, B=FAKE, q=FAKE, raw=FAKE, sink=FAKE, b=1, n=256, c=512, mp=128,
+        a = dict(C=FAKE, Z=FAKE, B=FAKE, q=FAKE, raw=FAKE, sink=FAKE, b=1, n=128, c=512, mp=128,
                  n_h=64, n_win=128, scale=0.1, dtype=1, Cc=FAKE, ws=0x100000, wsb=1 << 30, out=FAKE)
         a.update(kw)
         return lib.hca_layer(a["C"], a["Z"], a["B"], a["q"], a["raw"], a["sink"], a["b"], a["n"], a["c"],
@@ -203,6 +203,8 @@ def test_hca_layer_rejects_bad_arguments(lib):
     assert call(C=None) == EINVAL
     assert call(mp=0) == EINVAL
     assert call(dtype=3) == ENOTSUP
+    # 128 queries: few enough work items that the attention splits its lists
+    assert lib.hca_layer_workspace_size(1, 128, 64, 512, 128, 128, 1) > 0
     assert call(wsb=0) == ENOSPC
     assert call(Cc=None) == EINVAL
 

@@ -732,6 +732,26 @@ def test_hca_attend_full_size_sampled():
     assert_close(out[0, torch.tensor(rows, device=DEV)], want, torch.bfloat16, "out")
 
 
+def test_hca_decode_one_million_context_sampled():
+    # HCA attention at the 1M-token decode shape: 8 sequences, 8192 completed
+    # entries (m' = 128) plus the 128-row window, one query each (the split
+    # launch and its combine), checked on two sequences
+    say("hca decode 8 x 8192 entries (sampled sequences)")
+    b, ne, c, nh, mp, nw = 8, 8192, 512, 64, 128, 128
+    gen = torch.Generator(device=DEV).manual_seed(53)
+    Cc = (torch.randn((b, ne, c), generator=gen, device=DEV) / math.sqrt(c)).to(torch.bfloat16)
+    win = (torch.randn((b, nw, c), generator=gen, device=DEV) / math.sqrt(c)).to(torch.bfloat16)
+    q = (torch.randn((b, 1, nh, c), generator=gen, device=DEV) / math.sqrt(c)).to(torch.bfloat16)
+    sink = torch.randn((nh,), generator=gen, device=DEV)
+    t = ne * mp + 5          # (t + 1) // m' = 8192 entries visible
+    out = L.hca_attend(q, Cc, win, sink, t, mp, nw, raw_pos0=t - nw + 1)
+    torch.cuda.synchronize()
+    for s in (0, b - 1):
+        want = O.hca_attend(to64(q[s].cpu()), to64(Cc[s].cpu()), to64(win[s].cpu()), t - nw + 1, to64(sink.cpu()),
+                            [t], mp, nw, 1 / math.sqrt(c))
+        assert_close(out[s], want, torch.bfloat16, f"seq {s}")
+
+
 # ------------------------------------------------------------- whole layer --
 
 def test_csa_layer_tiny_fp32_end_to_end():
