@@ -379,6 +379,25 @@ def test_index_topk_mxfp4(b, n_q, n_comp, k, nh, cI):
         assert np.max(np.abs(gs[sel] - ref)) <= 1e-4 * max(1.0, np.abs(ref).max())
 
 
+@pytest.mark.parametrize("n_q", [1, 6])
+def test_index_topk_mxfp4_keys_in_a_larger_cache(n_q):
+    # keys in a cache with spare rows (the per-sequence stride is the cache's
+    # capacity, not n_comp), for the streaming and the four-query scorer
+    say(f"index mxfp4 cache with spare rows n_q={n_q}")
+    b, n_comp, cap, nh, cI, m, k = 2, 3000, 3100, 64, 128, 4, 200
+    gen = torch.Generator().manual_seed(59)
+    qc, qs = synth.to_mxfp4(torch.randn((b, n_q, nh, cI), generator=gen) / math.sqrt(cI))
+    kc, ks = synth.to_mxfp4(torch.randn((b, cap, cI), generator=gen) / math.sqrt(cI))
+    w = torch.nn.functional.softplus(torch.randn((b, n_q, nh), generator=gen))
+    t0 = n_comp * m - n_q
+    idx, sc = L.csa_index_topk_mxfp4(g(qc), g(qs), g(w), g(kc), g(ks), t0, m, k, n_comp=n_comp, score=True)
+    torch.cuda.synchronize()
+    for s in range(b):
+        want, osc, vis = _mx_oracle_index(qc[s], qs[s], w[s], kc[s, :n_comp], ks[s, :n_comp],
+                                          np.arange(t0, t0 + n_q), m, k)
+        assert_index_sets(idx[s].cpu().numpy(), want, osc, vis, k, f"seq {s}")
+
+
 def test_index_topk_mxfp4_one_million_context_sampled():
     # the 1M-token decode shape with MXFP4 codes (Gaussian keys and queries
     # quantised on the GPU): the launch the decode step makes, checked on two
