@@ -146,6 +146,23 @@ def run_prefill(args, torch, L, synth):
     timer4.collect()
     index_mx_us = timer4.avg_us("index_topk_mxfp4")
 
+    # the E4M3 indexer at this shape (codes converted before timing)
+    qI8 = d["qI"].to(torch.float8_e4m3fn)
+    KI8 = KI.to(torch.float8_e4m3fn)
+
+    def index_f8():
+        return lib.csa_index_topk(P(qI8), P(d["w"]), P(KI8), 0, 1, n, 0, ne, nI, cI, m, k, 2, P(idx), None, P(ws),
+                                  ws_bytes, st)
+
+    for _ in range(2):
+        index_f8()
+    for _ in range(args.steps):
+        if timer4.run("index_topk_fp8", index_f8) != 0:
+            raise RuntimeError("fp8 index failed")
+    timer4.collect()
+    index_f8_us = timer4.avg_us("index_topk_fp8")
+    del qI8, KI8
+
     # A whole step with the FP4 indexer: the key compressor's bf16 output is
     # encoded to MXFP4 by the library each step; the indexer queries are
     # given as MXFP4 codes (as the bf16 step is given its bf16 queries).
@@ -184,6 +201,7 @@ def run_prefill(args, torch, L, synth):
         "attend_tflops": att_tflops,
         "index_tflops": flop_index / (stage_us["index_topk"] * 1e-6) / 1e12,
         "index_topk_mxfp4_us": index_mx_us,
+        "index_topk_fp8_us": index_f8_us,
         "mxfp4_step": {"ms_per_step": ms4, "tokens_per_s": n / (ms4 / 1000.0),
                        "stages": [name for name, _ in stages4],
                        "queries": "indexer queries given as MXFP4 codes"},
@@ -685,6 +703,7 @@ def main(argv=None):
         "step_mfma_frac": pre["step_tflops"] / PEAK_BF16_TFLOPS,
         "index_tflops": pre["index_tflops"],
         "index_topk_mxfp4_us": pre["index_topk_mxfp4_us"],
+        "index_topk_fp8_us": pre["index_topk_fp8_us"],
         "prefill_mxfp4_indexer": pre["mxfp4_step"],
     }
     if "decode_1m" in extras:

@@ -753,30 +753,37 @@ __global__ __launch_bounds__(256) void index_scores_stream_mx(
   }
 }
 
-// Many-query MXFP4 scoring (prefill; c_I = 128): index_scores_mfma's
+// Many-query low-precision scoring (prefill; c_I = 128): index_scores_mfma's
 // layout -- four queries per workgroup, one per wave, sharing 64-key tiles
 // that reach a 3-slot LDS ring by LDS-DMA two tiles ahead, one barrier per
-// tile -- with 64-byte code rows, the tile's 64 scale words DMA'd beside them
-// (16 per wave), and the block-scaled FP4 MFMA.  FUSED: every list fits one
-// workgroup (at most kFusedMaxKeys keys) and each wave selects its query's
-// top k from LDS as in index_scores_mfma; else the scores are written.
-template <int NHB, int FUSED>
+// tile -- on the block-scaled MFMA v_mfma_scale_f32_32x32x64.  FMT 4: MXFP4
+// (64-byte code rows; the tile's 64 scale words DMA'd beside them, 16 per
+// wave; a lane's operand is 16 bytes, one MX block); FMT 0: E4M3 codes
+// without scales (128-byte rows, 32-byte lane operands, unit scales).
+// FUSED: every list fits one workgroup (at most kFusedMaxKeys keys) and each
+// wave selects its query's top k from LDS as in index_scores_mfma; else the
+// scores are written.
+template <int NHB, int FUSED, int FMT>
 __global__ __launch_bounds__(256) void index_scores_mfma_mx(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qS, const float* __restrict__ w,
     const uint8_t* __restrict__ KI, const uint8_t* __restrict__ KS, int64_t comp_bs, int64_t n_q, int64_t t0,
     int64_t n_comp, int64_t m, int64_t n_qblocks, float* __restrict__ scores, int64_t k,
     int32_t* __restrict__ idx, float* __restrict__ score_out) {
+  static_assert(FMT == 4 || FMT == 0, "E2M1 or E4M3 operands");
+  constexpr bool MX = FMT == 4;
   constexpr int CI = 128;
   constexpr int NH = NHB * 32;
   constexpr int TN = 64;                 // keys per tile
-  constexpr int ROWB = CI / 2;           // code bytes per key
-  constexpr int NB = CI / 32;            // scale bytes per key (one word)
+  constexpr int ROWB = MX ? CI / 2 : CI; // code bytes per key
+  constexpr int OPB = MX ? 16 : 32;      // operand bytes per lane and 64-dimension step
+  constexpr int NB = CI / 32;            // MXFP4 scale bytes per key (one word)
   constexpr int NCH = ROWB / 16;         // 16-byte chunks per row
-  constexpr int KPI = 64 / NCH;          // rows per 1 KiB DMA instruction (one per wave and tile)
+  constexpr int KPI = 64 / NCH;          // rows per 1 KiB DMA instruction
+  constexpr int DPW = TN / KPI / 4;      // code DMAs per wave and tile
   constexpr int SDIV = 16 / NCH;
-  static_assert(KPI * 4 == TN, "one code DMA per wave and tile");
+  constexpr int LPT = DPW + (MX ? 1 : 0);   // vector-memory loads per wave and tile
   __shared__ uint4 ring[3][TN * NCH];
-  __shared__ uint32_t sring[3][TN];
+  __shared__ uint32_t sring[MX ? 3 : 1][MX ? TN : 1];
   __shared__ float ssc[FUSED ? 4 : 1][FUSED ? kFusedMaxKeys : 1];
 
   const int tid = threadIdx.x;
@@ -796,19 +803,29 @@ __global__ __launch_bounds__(256) void index_scores_mfma_mx(
   const int ntl = (int)((c1 + TN - 1) / TN);   // uniform over the workgroup
 
   const uint8_t* kbase = KI + bi * comp_bs * ROWB;
-  const uint8_t* sbase = KS + bi * comp_bs * NB;
+  const uint8_t* sbase = MX ? KS + bi * comp_bs * NB : nullptr;
   const int64_t lastkey = c1 - 1;
-  const int dr = wave * KPI + l / NCH;   // tile row this lane's code DMA fills
-  const int src_off = dr * ROWB + (((l % NCH) ^ ((dr / SDIV) % NCH)) * 16);
+  int dr[DPW], src_off[DPW];   // tile row each of this lane's code DMAs fills, and its source
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    dr[d] = (DPW * wave + d) * KPI + l / NCH;
+    src_off[d] = dr[d] * ROWB + (((l % NCH) ^ ((dr[d] / SDIV) % NCH)) * 16);
+  }
   auto issue = [&](int j, int slot) {
     int64_t kb = (int64_t)TN * j;
     kb = kb < lastkey ? kb : lastkey;
     const int room = (int)(lastkey - kb < TN ? lastkey - kb : TN);
-    const uint8_t* src = kbase + kb * ROWB + (dr <= room ? src_off : room * ROWB + (src_off - dr * ROWB));
-    dma_chunk16(src, (uint32_t)(uintptr_t)&ring[slot][0] + 1024 * wave);
-    if (l < 16) {
-      const int r = 16 * wave + l;
-      dma_dword(sbase + (kb + (r <= room ? r : room)) * NB, (uint32_t)(uintptr_t)&sring[slot][16 * wave]);
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const uint8_t* src =
+          kbase + kb * ROWB + (dr[d] <= room ? src_off[d] : room * ROWB + (src_off[d] - dr[d] * ROWB));
+      dma_chunk16(src, (uint32_t)(uintptr_t)&ring[slot][0] + 1024 * (DPW * wave + d));
+    }
+    if constexpr (MX) {
+      if (l < 16) {
+        const int r = 16 * wave + l;
+        dma_dword(sbase + (kb + (r <= room ? r : room)) * NB, (uint32_t)(uintptr_t)&sring[slot][16 * wave]);
+      }
     }
   };
   if (ntl > 0) {
@@ -816,8 +833,18 @@ __global__ __launch_bounds__(256) void index_scores_mfma_mx(
     issue(1, 1);
   }
 
-  // query operands (two 64-dimension steps), scale words shifted so that
-  // bytes 0 / 2 select the blocks this lane's half holds, head weights
+  // an operand: this lane's 32 dimensions of a 64-dimension step
+  auto operand = [&](const uint8_t* p) -> i32x8 {
+    if constexpr (MX) {
+      return mx_operand(p);
+    } else {
+      const uint4 a = reinterpret_cast<const uint4*>(p)[0], b = reinterpret_cast<const uint4*>(p)[1];
+      return (i32x8){(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    }
+  };
+  // query operands (two 64-dimension steps); MXFP4: scale words shifted so
+  // that bytes 0 / 2 select the blocks this lane's half holds (E4M3: the unit
+  // scale 2^0 in every byte); head weights
   i32x8 qa[NHB][2];
   uint32_t qsw[NHB];
   float wv[NHB][16];
@@ -826,8 +853,9 @@ __global__ __launch_bounds__(256) void index_scores_mfma_mx(
   for (int mb = 0; mb < NHB; ++mb) {
     const int64_t hr = qoff + mb * 32 + (l & 31);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qa[mb][ks] = mx_operand(qI + hr * ROWB + 32 * ks + 16 * h);
-    qsw[mb] = *reinterpret_cast<const uint32_t*>(qS + hr * NB) >> (8 * h);
+    for (int ks = 0; ks < 2; ++ks) qa[mb][ks] = operand(qI + hr * ROWB + 2 * OPB * ks + OPB * h);
+    if constexpr (MX) qsw[mb] = *reinterpret_cast<const uint32_t*>(qS + hr * NB) >> (8 * h);
+    else qsw[mb] = 0x7f7f7f7fu;
 #pragma unroll
     for (int r = 0; r < 16; ++r) wv[mb][r] = qvalid ? w[qoff + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)] : 0.f;
   }
@@ -835,26 +863,45 @@ __global__ __launch_bounds__(256) void index_scores_mfma_mx(
 #pragma unroll
   for (int mb = 0; mb < NHB; ++mb) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)   // the four loaded dwords (a 32-byte vector has no host-side constraint)
+    for (int ks = 0; ks < 2; ++ks) {   // the loaded dwords (a 32-byte vector has no host-side constraint)
       asm volatile("" ::"v"(qa[mb][ks][0]), "v"(qa[mb][ks][1]), "v"(qa[mb][ks][2]), "v"(qa[mb][ks][3]));
+      if constexpr (!MX)
+        asm volatile("" ::"v"(qa[mb][ks][4]), "v"(qa[mb][ks][5]), "v"(qa[mb][ks][6]), "v"(qa[mb][ks][7]));
+    }
     asm volatile("" ::"v"(qsw[mb]));
 #pragma unroll
     for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(wv[mb][r]));
   }
 
   float* srow = scores + (bi * n_q + (qvalid ? qrow : 0)) * n_comp;
-  int rd_off[2][2];   // bytes from the slot's start: key row 32 nb + l % 32, chunk 2 ks + h
+  // bytes from the slot's start of the 16-byte chunks of key row 32 nb + l % 32
+  // holding this lane's operand of step ks (OPB / 16 chunks from chunk
+  // (2 ks + h) OPB / 16)
+  constexpr int CPO = OPB / 16;
+  int rd_off[2][2][CPO];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int r = nb * 32 + (l & 31);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) rd_off[nb][ks] = r * ROWB + (((2 * ks + h) ^ ((r / SDIV) % NCH)) << 4);
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int u = 0; u < CPO; ++u)
+        rd_off[nb][ks][u] = r * ROWB + ((((2 * ks + h) * CPO + u) ^ ((r / SDIV) % NCH)) << 4);
   }
+  auto tile_operand = [&](const unsigned char* tile, int nb, int ks) -> i32x8 {
+    if constexpr (MX) {
+      return mx_operand(tile + rd_off[nb][ks][0]);
+    } else {
+      const uint4 a = *reinterpret_cast<const uint4*>(tile + rd_off[nb][ks][0]);
+      const uint4 b = *reinterpret_cast<const uint4*>(tile + rd_off[nb][ks][CPO - 1]);
+      return (i32x8){(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    }
+  };
   int slot = 0;
   for (int j = 0; j < ntl; ++j) {
-    // this wave's part of tile j has landed once at most tile j + 1's two
+    // this wave's part of tile j has landed once at most tile j + 1's LPT
     // loads are in flight; after the barrier every wave's part has
-    wait_vmem<2>();
+    wait_vmem<LPT>();
     __syncthreads();
     issue(j + 2, slot == 0 ? 2 : slot - 1);
     const int64_t kb = (int64_t)TN * j;
@@ -863,14 +910,15 @@ __global__ __launch_bounds__(256) void index_scores_mfma_mx(
       f32x16 acc[NHB][2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const uint32_t ksw = sring[slot][32 * nb + (l & 31)] >> (8 * h);
-        const i32x8 b0 = mx_operand(tile + rd_off[nb][0]);
-        const i32x8 b1 = mx_operand(tile + rd_off[nb][1]);
+        uint32_t ksw = 0x7f7f7f7fu;
+        if constexpr (MX) ksw = sring[slot][32 * nb + (l & 31)] >> (8 * h);
+        const i32x8 b0 = tile_operand(tile, nb, 0);
+        const i32x8 b1 = tile_operand(tile, nb, 1);
 #pragma unroll
         for (int mb = 0; mb < NHB; ++mb) {
-          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][0], b0, (f32x16){}, 4, 4, 0,
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][0], b0, (f32x16){}, FMT, FMT, 0,
                                                                        (int)qsw[mb], 0, (int)ksw);
-          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][1], b1, acc[mb][nb], 4, 4, 2,
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][1], b1, acc[mb][nb], FMT, FMT, 2,
                                                                        (int)qsw[mb], 2, (int)ksw);
         }
       }
@@ -1771,6 +1819,34 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
       CSA_STREAM8_CASE(4, 4) CSA_STREAM8_CASE(4, 8)
 #undef CSA_STREAM8_CASE
     }
+    // E4M3 codes, four or more queries: the block-scaled MFMA scorer with
+    // unit scales (selection fused when every list fits one workgroup)
+    if (!done && dtype == 2 && n_q >= 4 && cI == 128 && (nh == 32 || nh == 64 || nh == 128)) {
+      const bool f8fused = n_comp <= kFusedMaxKeys;
+      const int64_t nqb = (n_q + 3) / 4;
+      dim3 grid((unsigned)nqb, 1, (unsigned)b);
+      const uint8_t* q8 = (const uint8_t*)qI;
+      const uint8_t* k8 = (const uint8_t*)KI;
+      const int64_t cbe = cbs / cI;   // the stride in entries
+#define CSA_F8_MFMA(NHB_)                                                                                         \
+  if (f8fused)                                                                                                     \
+    hipLaunchKernelGGL((index_scores_mfma_mx<NHB_, 1, 0>), grid, dim3(256), 0, st, q8, nullptr, w, k8, nullptr,      \
+                       cbe, n_q, t0, n_comp, m, nqb, scores, k, idx, score);                                       \
+  else                                                                                                             \
+    hipLaunchKernelGGL((index_scores_mfma_mx<NHB_, 0, 0>), grid, dim3(256), 0, st, q8, nullptr, w, k8, nullptr,      \
+                       cbe, n_q, t0, n_comp, m, nqb, scores, k, nullptr, nullptr);
+      if (nh == 32) {
+        CSA_F8_MFMA(1)
+      } else if (nh == 64) {
+        CSA_F8_MFMA(2)
+      } else {
+        CSA_F8_MFMA(4)
+      }
+#undef CSA_F8_MFMA
+      err = hipGetLastError();
+      if (err != hipSuccess || f8fused) return err;
+      done = true;
+    }
     if (!done) {
       dim3 grid((unsigned)((n_comp + 255) / 256), (unsigned)n_q, (unsigned)b);
       if (dtype == 1)
@@ -1826,10 +1902,10 @@ hipError_t launch_index_topk_mx(const void* qI, const void* qS, const float* w, 
     float* fs = fused ? score : nullptr;
 #define CSA_MX_MFMA(NHB_)                                                                                        \
   if (fused)                                                                                                      \
-    hipLaunchKernelGGL((index_scores_mfma_mx<NHB_, 1>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs, n_q, t0, \
+    hipLaunchKernelGGL((index_scores_mfma_mx<NHB_, 1, 4>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs, n_q, t0, \
                        n_comp, m, nqb, scores, k, fi, fs);                                                         \
   else                                                                                                            \
-    hipLaunchKernelGGL((index_scores_mfma_mx<NHB_, 0>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs, n_q, t0, \
+    hipLaunchKernelGGL((index_scores_mfma_mx<NHB_, 0, 4>), grid, dim3(256), 0, st, q8, qs8, w, k8, ks8, cbs, n_q, t0, \
                        n_comp, m, nqb, scores, k, nullptr, nullptr);
     if (nh == 32) {
       CSA_MX_MFMA(1)

@@ -289,8 +289,12 @@ def _fp8_oracle_index(qI8, w, KI8, t_pos, m, k):
     (2, 1, 20000, 512, 64, 128),    # streaming FP8 scorer, threshold selection
     (2, 3, 1500, 100, 64, 128),     # streaming FP8 scorer, one segment per row, rows of different length
     (1, 2, 9000, 300, 32, 64),      # other head / dimension counts
-    (1, 6, 1200, 64, 64, 128),      # four or more queries: generic scoring of the codes
-    (1, 2, 700, 40, 48, 40),        # shape without an MFMA kernel: generic scoring
+    (1, 6, 1200, 64, 64, 128),      # four or more queries: block-scaled MFMA with fused selection
+    (2, 37, 1500, 300, 32, 128),    # fused, 32 heads, a partial last query block
+    (1, 5, 600, 40, 128, 128),      # fused, 128 heads
+    (1, 9, 3000, 100, 64, 128),     # lists longer than one workgroup: MFMA scores + general selection
+    (1, 6, 700, 40, 48, 64),        # shape without an MFMA kernel: generic scoring
+    (1, 2, 700, 40, 48, 40),        # the same with few queries
 ])
 def test_index_topk_fp8(b, n_q, n_comp, k, nh, cI):
     # E4M3 indexer queries and keys: the same selection as the oracle's over
@@ -311,6 +315,25 @@ def test_index_topk_fp8(b, n_q, n_comp, k, nh, cI):
         sel = gi >= 0
         ref = osc[np.nonzero(sel)[0], gi[sel]]
         assert np.max(np.abs(gs[sel] - ref)) <= 1e-3 * max(1.0, np.abs(ref).max())
+
+
+def test_index_topk_fp8_prefill_full_size_sampled():
+    # the CSA prefill shape (n = 8192, 2048 entries, 64 x 128 indexer, k =
+    # 512) with E4M3 codes, the keys in a cache with spare rows: fused MFMA
+    # scorer, sampled queries
+    say("index fp8 prefill n=8192 (sampled queries)")
+    d = synth.prefill_inputs()
+    p = d["params"]
+    qI = synth.to_fp8(d["qI"])
+    KI = synth.to_fp8(torch.cat([d["KIcomp"].float(), torch.randn((40, d["KIcomp"].shape[1]))]))
+    ne = d["KIcomp"].shape[0]
+    idx = L.csa_index_topk(g(qI), g(d["w"]), g(KI), 0, p["m"], p["k"], n_comp=ne)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(2040, 2056), np.arange(8184, 8192),
+                                     np.random.default_rng(3).integers(0, 8192, 40)]))
+    want, osc, vis = _fp8_oracle_index(qI[rows], d["w"][rows], KI[:ne], rows, p["m"], p["k"])
+    nt = assert_index_sets(idx[0, rows].cpu().numpy(), want, osc, vis, p["k"])
+    say(f"  sampled {len(rows)} queries, near-ties: {nt}")
 
 
 def test_index_topk_fp8_one_million_context_sampled():
