@@ -209,6 +209,14 @@ def test_hca_layer_rejects_bad_arguments(lib):
     assert call(Cc=None) == EINVAL
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no library, no fallback: every entry point goes through load_library,
+    # which raises when libcsa.so is absent
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.load_library(str(tmp_path / "libcsa.so"))
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(8, 4)
