@@ -1351,25 +1351,22 @@ __device__ __forceinline__ int wave_count(const bool (&val)[R]) {
   return c;
 }
 
-// tau[row] = a lower bound on the k-th largest of the row's first
-// min(G, 256 R) group maxima, or 1 (every valid key) when fewer than k of
-// them are non-empty.  Each maximum is a distinct key of the row, so at least k
-// keys are >= tau.  The bound is the k-th largest found to kThresholdBits
-// bits below the common prefix of the largest and smallest maximum: the bit
-// search keeps count(>= T) >= k at every step, so stopping it early still
-// gives a valid bound, one that lets through only the keys within 2^-12 of
-// the maxima's range below the exact value.  One workgroup of 256 threads
-// (R maxima each) per row.
+// A lower bound tau on the k-th largest score of a row, from its first
+// min(G, 256 R) group maxima (src): their k-th largest, or 1 (every valid
+// key) when fewer than k are non-empty.  Each maximum is a distinct key of
+// the row, so at least k keys are >= tau.  The k-th largest is found to
+// kThresholdBits bits below the common prefix of the largest and smallest
+// maximum: the bit search keeps count(>= T) >= k at every step, so stopping
+// it early still gives a valid bound, one that lets through only the keys
+// within 2^-12 of the maxima's range below the exact value.  Every thread of
+// a 256-thread workgroup calls it (R maxima each).
 constexpr int kThresholdBits = 12;
 template <int R>
-__global__ __launch_bounds__(256) void topk_threshold(const uint32_t* __restrict__ gmax, int64_t ld_gmax, int64_t G,
-                                                      int64_t rows, int64_t k, uint32_t* __restrict__ tau) {
-  constexpr int NT = 256;
-  __shared__ uint32_t red[SegReduce<NT>::kRedSize];
+__device__ __forceinline__ uint32_t row_threshold(const uint32_t* __restrict__ src, int64_t G, int64_t k,
+                                                  uint32_t* red) {
+  constexpr int NT = 256;   // the whole workgroup takes part
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
   const int g = (int)(G < NT * R ? G : NT * R);
-  const uint32_t* src = gmax + row * ld_gmax;
   uint32_t key[R];
   uint32_t c = 0, hi = 0, lo = 0xffffffffu;
 #pragma unroll
@@ -1385,10 +1382,7 @@ __global__ __launch_bounds__(256) void topk_threshold(const uint32_t* __restrict
   }
   int parity = 0;
   const uint32_t nval = SegReduce<NT>::sum(c, red, wave, parity);
-  if (nval <= (uint32_t)k) {
-    if (tid == 0) tau[row] = 1u;
-    return;   // uniform
-  }
+  if (nval <= (uint32_t)k) return 1u;   // every valid key (uniform)
   hi = SegReduce<NT>::umax(hi, red, wave, parity);
   lo = ~SegReduce<NT>::umax(~lo, red, wave, parity);
   const uint32_t diff = hi ^ lo;
@@ -1409,41 +1403,49 @@ __global__ __launch_bounds__(256) void topk_threshold(const uint32_t* __restrict
       }
     }
   }
-  if (tid == 0) tau[row] = max(T, 1u);
+  return max(T, 1u);
 }
 
-// One wave per (row, 2048-key segment): the top k of the segment's scores
-// that are >= tau[row] (usually all of them: only a few keys pass), written
-// in list order at slot seg*k of the row's pair list, their count in
-// cnt[row][seg].  Every count of the grid is written.
-__global__ __launch_bounds__(256) void topk_filter(const float* __restrict__ scores, int64_t ld_scores,
-                                                   const uint32_t* __restrict__ tau, int64_t n_rows, int64_t n_q,
-                                                   int64_t t0, int64_t n_comp, int64_t m, int64_t k, int64_t nseg,
-                                                   uint32_t* __restrict__ kout, int32_t* __restrict__ iout, int64_t ld_out,
-                                                   int32_t* __restrict__ cnt) {
+// Threshold and filter in one launch: a workgroup takes four 2048-key
+// segments of one row, one per wave.  Its 256 threads first find the row's
+// bound from the group maxima (the search above; each of the row's
+// workgroups repeats it), then each wave keeps the top k of its segment's
+// scores at or above the bound (usually all of them: only a few keys pass),
+// written in list order at slot seg*k of the row's pair list, their count in
+// cnt[row][seg].  The segment's score loads are issued before the search, so
+// their latency overlaps it.  Every count of the grid is written.
+template <int RT>
+__global__ __launch_bounds__(256) void topk_threshold_filter(
+    const float* __restrict__ scores, int64_t ld_scores, const uint32_t* __restrict__ gmax, int64_t ld_gmax,
+    int64_t G, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t k, int64_t nseg,
+    uint32_t* __restrict__ kout, int32_t* __restrict__ iout, int64_t ld_out, int32_t* __restrict__ cnt) {
   constexpr int R = 32, CH = 64 * R;
+  __shared__ uint32_t red[SegReduce<256>::kRedSize];
   const int sub = threadIdx.x >> 6, tid = threadIdx.x & 63;
-  const int64_t gseg = (int64_t)blockIdx.x * 4 + sub;
-  if (gseg >= n_rows * nseg) return;   // whole wave
-  const int64_t row = gseg / nseg, seg = gseg % nseg;
+  const int64_t row = blockIdx.x;                          // rows on x: up to 2^31 of them
+  const int64_t seg = (int64_t)blockIdx.y * 4 + sub;      // at most kMergeMaxSeg / 4 groups on y
+  const bool active = seg < nseg;   // a wave past the row's last segment only helps the search
   int64_t L = (t0 + row % n_q + 1) / m;
   if (L > n_comp) L = n_comp;
   const int64_t base = seg * CH;
   int64_t len64 = L - base;
   if (len64 > CH) len64 = CH;
-  if (len64 < 0) len64 = 0;
+  if (len64 < 0 || !active) len64 = 0;
   const int len = (int)len64;
-  const uint32_t th = tau[row];
-  uint32_t key[R];
+  float raw[R];
   if (len > 0) {
     const float* src = scores + row * ld_scores + base;
-    float raw[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) raw[r] = src[min(r * 64 + tid, len - 1)];
+  }
+  const uint32_t th = row_threshold<RT>(gmax + row * ld_gmax, G, k, red);   // >= 1
+  if (!active) return;   // whole wave, after the workgroup's last barrier
+  uint32_t key[R];
+  if (len > 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t kk = f2key(raw[r]);
-      key[r] = r * 64 + tid < len && kk >= th ? kk : 0u;   // th >= 1
+      key[r] = r * 64 + tid < len && kk >= th ? kk : 0u;
     }
   } else {
 #pragma unroll
@@ -1735,16 +1737,16 @@ static hipError_t finish_topk(const TopkLayout& L, unsigned char* W, float* scor
   if (gmax_used) {
     // threshold path: a lower bound on each row's k-th largest score from the
     // group maxima, a filtering pass per 2048-key segment, one exact merge
-    uint32_t* tau = (uint32_t*)(W + L.tau);
     int32_t* cnt = (int32_t*)(W + L.cnt);
     const int64_t G = stream_splits_for(dtype, b, n_q, lmax) * kStreamGroupsPerWG;
     // every maximum counts (up to 4096 per row: more of them, a tighter bound)
+    const dim3 fgrid((unsigned)rows, (unsigned)((nseg + 3) / 4));
     if (G > 2048)
-      hipLaunchKernelGGL(topk_threshold<16>, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows, k, tau);
+      hipLaunchKernelGGL(topk_threshold_filter<16>, fgrid, dim3(256), 0, st, scores, n_comp, gmax, L.gcap, G, n_q,
+                         t0, n_comp, m, k, nseg, kbuf[0], ibuf[0], L.cap, cnt);
     else
-      hipLaunchKernelGGL(topk_threshold<8>, dim3((unsigned)rows), dim3(256), 0, st, gmax, L.gcap, G, rows, k, tau);
-    hipLaunchKernelGGL(topk_filter, dim3((unsigned)((rows * nseg + 3) / 4)), dim3(256), 0, st, scores, n_comp, tau,
-                       rows, n_q, t0, n_comp, m, k, nseg, kbuf[0], ibuf[0], L.cap, cnt);
+      hipLaunchKernelGGL(topk_threshold_filter<8>, fgrid, dim3(256), 0, st, scores, n_comp, gmax, L.gcap, G, n_q,
+                         t0, n_comp, m, k, nseg, kbuf[0], ibuf[0], L.cap, cnt);
     hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(256), 0, st, kbuf[0], ibuf[0], L.cap, cnt, nseg, k,
                        idx, score);
     return hipGetLastError();
