@@ -38,7 +38,12 @@ design notes):
     indexer queries and keys are taken as 8-bit E4M3 codes, or as OCP MXFP4
     (E2M1 elements, one E8M0 power-of-two scale per 32 consecutive
     dimensions); the scores are the same weighted ReLU sums of the values the
-    codes stand for.
+    codes stand for;
+  * normalisation and partial RoPE ([P2] section 4.5, [P3] section 7.1): RMSNorm
+    with a per-dimension gain and explicit eps, then rotation of the last 64
+    dimensions as adjacent pairs with frequencies base^(-2i/64); a compressed
+    entry sits at the position of its block's first token; the attention
+    output is rotated back by -t.
 
 parity unpinned: none of the routines here.  Each has at least one test that
 pins it to something other than itself (closed forms, invariants, library
@@ -425,6 +430,86 @@ def csa_layer(streams, istreams, q, qI, w, kv_raw, sink, m: int, k: int,
     idx, _ = index_topk(_f64(qI)[rows], _f64(w)[rows], KIcomp, rows, m, k)
     out = csa_attend(_f64(q)[rows], Ccomp, idx, kv_raw, 0, sink, rows, n_win, scale, m)
     return Ccomp, KIcomp, idx, out
+
+
+# --------------------------------------------------------------------------
+# Normalisation and partial rotary embedding around the core attention
+# ([P2] section 4.5 "other details"; [P3] section 7.1 "Partial RoPE")
+# --------------------------------------------------------------------------
+
+def rms_norm(x, gamma, eps: float):
+    """RMSNorm along the last axis: x / sqrt(mean(x^2) + eps) * gamma.
+
+    [P2] section 4.5: every query head and every KV entry is normalised this
+    way before the core attention, which keeps the logits bounded.  Readings:
+    one learned gain per dimension (gamma [c]) and an explicit eps; the pages
+    give neither.
+    """
+    x = _f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * _f64(gamma)
+
+
+def rope_frequencies(dims: int, base: float):
+    """Angular frequency of rotation pair i < dims/2: base^(-2i/dims).
+
+    Reading: the standard rotary frequencies; [P2] section 4.5 and [P3]
+    section 7.1 name RoPE on the last 64 dimensions without its constants.
+    """
+    i = np.arange(dims // 2, dtype=F64)
+    return float(base) ** (-2.0 * i / dims)
+
+
+def rope(x, pos, dims: int, base: float):
+    """Rotary embedding of the last `dims` dimensions at the given positions.
+
+    x [rows, ..., c], pos [rows] (any integers, negative included).  Pair i is
+    the adjacent dimensions (c - dims + 2i, c - dims + 2i + 1), read as the
+    complex number a + ib and multiplied by exp(i * pos * theta_i) (reading:
+    interleaved pairs; the pages do not say how the 64 dimensions pair up).
+    The other c - dims dimensions are unchanged.
+    """
+    x = _f64(x).copy()
+    c = x.shape[-1]
+    lo = c - dims
+    ang = np.asarray(pos, dtype=F64).reshape((-1,) + (1,) * (x.ndim - 1)) * rope_frequencies(dims, base)
+    cos, sin = np.cos(ang), np.sin(ang)
+    a = x[..., lo::2].copy()
+    b = x[..., lo + 1::2].copy()
+    x[..., lo::2] = a * cos - b * sin
+    x[..., lo + 1::2] = a * sin + b * cos
+    return x
+
+
+def norm_rope(x, gamma, eps: float, pos, dims: int, base: float):
+    """RMSNorm (skipped when gamma is None), then the rotary embedding.
+
+    Reading: the norm comes first and its gain applies before the rotation.
+    """
+    y = _f64(x) if gamma is None else rms_norm(x, gamma, eps)
+    return rope(y, pos, dims, base) if dims else y
+
+
+def csa_attend_rope(q, Ccomp, idx, kv_raw, raw_pos0: int, sink, t_pos, n_win: int,
+                    scale: float, m: int, gamma_q, gamma_kv, eps: float, dims: int,
+                    base: float, entry_pos0: int = 0):
+    """CSA attention with the normalisation and partial RoPE of [P2] section
+    4.5 and [P3] section 7.1 around it.
+
+    Query heads at t and KV entries are normalised and rotated at their own
+    positions; the attention output's last `dims` dimensions are then rotated
+    by -t, so that only relative positions remain in it.  Readings: compressed
+    entry s sits at position entry_pos0 + m*s (the first token of its block),
+    a raw window row at its token position; the window rows take the same
+    norm gain as the compressed entries.  With m = m' and every visible entry
+    selected this is the HCA form.
+    """
+    t_pos = np.asarray(t_pos)
+    qn = norm_rope(q, gamma_q, eps, t_pos, dims, base)
+    Cn = norm_rope(Ccomp, gamma_kv, eps, entry_pos0 + m * np.arange(_f64(Ccomp).shape[0]), dims, base)
+    Rn = norm_rope(kv_raw, gamma_kv, eps, raw_pos0 + np.arange(_f64(kv_raw).shape[0]), dims, base)
+    o = csa_attend(qn, Cn, idx, Rn, raw_pos0, sink, t_pos, n_win, scale, m)
+    return rope(o, -t_pos, dims, base)
 
 
 # --------------------------------------------------------------------------

@@ -547,3 +547,120 @@ def test_mxfp4_encode_roundtrips_representable_values():
     x = x * np.repeat(np.exp2(gen.integers(-9, 9, (4, 3)).astype(float)), 32, axis=1)
     codes, scales = O.mxfp4_encode(x)
     assert np.array_equal(O.mxfp4_decode(codes, scales), x)
+
+
+# ------------------------------------------------- RMSNorm and partial RoPE ----
+# [P2] section 4.5 and [P3] section 7.1: query heads and KV entries are
+# RMS-normalised before the core attention; the last 64 dimensions of queries,
+# entries and outputs carry a rotary embedding, the output's at position -t.
+
+def test_rms_norm_closed_forms():
+    # hand value: (3, 4) has mean square 12.5
+    y = O.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    assert np.allclose(y, [3.0 / math.sqrt(12.5), 4.0 / math.sqrt(12.5)], rtol=0, atol=1e-15)
+    x = _rng(11).standard_normal((5, 7, 64))
+    # unit gain, no eps: unit mean square; with eps: ms / (ms + eps) exactly
+    assert np.allclose(np.mean(O.rms_norm(x, np.ones(64), 0.0) ** 2, axis=-1), 1.0, atol=1e-12)
+    ms = np.mean(x * x, axis=-1)
+    assert np.allclose(np.mean(O.rms_norm(x, np.ones(64), 0.5) ** 2, axis=-1), ms / (ms + 0.5), atol=1e-12)
+    # scale invariance without eps, and the gain acts per dimension on the last axis
+    assert np.allclose(O.rms_norm(7.5 * x, np.ones(64), 0.0), O.rms_norm(x, np.ones(64), 0.0), atol=1e-12)
+    g = np.arange(1.0, 65.0)
+    assert np.allclose(O.rms_norm(x, g, 0.0)[..., 9], O.rms_norm(x, np.ones(64), 0.0)[..., 9] * 10.0, atol=1e-12)
+
+
+def test_rope_hand_values_pairing_and_sign():
+    # c = 6, rotary part 4 dims, base 100: frequencies 1 and 0.1
+    assert np.allclose(O.rope_frequencies(4, 100.0), [1.0, 0.1], atol=1e-15)
+    y = O.rope(np.array([[5.0, -7.0, 1.0, 0.0, 0.0, 1.0]]), [10], 4, 100.0)[0]
+    # (1, 0) turned by 10 rad, (0, 1) by 1 rad, counter-clockwise; dims 0-1 untouched
+    want = [5.0, -7.0, math.cos(10.0), math.sin(10.0), -math.sin(1.0), math.cos(1.0)]
+    assert np.allclose(y, want, rtol=0, atol=1e-15)
+    # position 0 is the identity
+    x = _rng(12).standard_normal((3, 2, 128))
+    assert np.array_equal(O.rope(x, [0, 0, 0], 64, 10000.0), x)
+
+
+def test_rope_group_and_relative_properties():
+    rng = _rng(13)
+    x = rng.standard_normal((4, 3, 512))
+    a = np.array([0, 5, 1_000_003, -77])
+    b = np.array([9, -5, 12, 1_048_575])
+    ra = O.rope(x, a, 64, 10000.0)
+    # only the last 64 dimensions move, and every pair keeps its length
+    assert np.array_equal(ra[..., :448], x[..., :448])
+    assert np.allclose(np.hypot(ra[..., 448::2], ra[..., 449::2]), np.hypot(x[..., 448::2], x[..., 449::2]), atol=1e-12)
+    # R(b) R(a) = R(a + b); R(-a) undoes R(a)
+    assert np.allclose(O.rope(ra, b, 64, 10000.0), O.rope(x, a + b, 64, 10000.0), atol=1e-9)
+    assert np.allclose(O.rope(ra, -a, 64, 10000.0), x, atol=1e-9)
+    # <R(a) q, R(b) k> depends on a - b only
+    q, k = x[:, 0], x[:, 1]
+    lhs = np.sum(O.rope(q, a, 64, 10000.0) * O.rope(k, b, 64, 10000.0), axis=-1)
+    rhs = np.sum(O.rope(q, a - b, 64, 10000.0) * k, axis=-1)
+    assert np.allclose(lhs, rhs, atol=1e-9)
+
+
+def _rope_case(seed, n=48, n_h=3, c=16, m=4, k=3, n_win=6, dims=8):
+    rng = _rng(seed)
+    q = rng.standard_normal((n, n_h, c))
+    Cc = rng.standard_normal((n // m, c))
+    raw = rng.standard_normal((n, c))
+    sink = rng.standard_normal(n_h)
+    t = np.arange(n)
+    idx = np.full((n, k), -1)
+    for r in range(n):
+        v = O.visible_entries(r, m)
+        sel = np.sort(rng.permutation(v)[:k])
+        idx[r, :len(sel)] = sel
+    gq, gk = 1.0 + 0.1 * rng.standard_normal(c), 1.0 + 0.1 * rng.standard_normal(c)
+    return dict(q=q, Ccomp=Cc, idx=idx, kv_raw=raw, sink=sink, t=t, m=m, n_win=n_win,
+                dims=dims, gq=gq, gk=gk, scale=1.0 / math.sqrt(c))
+
+
+def test_rope_attention_output_depends_on_relative_positions_only():
+    # [P2] section 4.5 / [P3] section 7.1: turning the output back by -t leaves
+    # only relative positions in it.  The same entries seen D tokens later
+    # (D a multiple of m: D rows and D/m entries of other data in front, the
+    # selected indices moved by D/m) give the same output for every query
+    # whose window is full in both cases.
+    d = _rope_case(14)
+    rng = _rng(16)
+    D = 4 * 300
+    c = d["q"].shape[-1]
+    kw = dict(eps=1e-6, dims=d["dims"], base=10.0)
+    base = O.csa_attend_rope(d["q"], d["Ccomp"], d["idx"], d["kv_raw"], 0, d["sink"], d["t"], d["n_win"],
+                             d["scale"], d["m"], d["gq"], d["gk"], **kw)
+    Cs = np.concatenate([rng.standard_normal((D // d["m"], c)), d["Ccomp"]])
+    Rs = np.concatenate([rng.standard_normal((D, c)), d["kv_raw"]])
+    idx_s = np.where(d["idx"] >= 0, d["idx"] + D // d["m"], -1)
+    moved = O.csa_attend_rope(d["q"], Cs, idx_s, Rs, 0, d["sink"], d["t"] + D, d["n_win"],
+                              d["scale"], d["m"], d["gq"], d["gk"], **kw)
+    full = slice(d["n_win"] - 1, None)
+    assert np.allclose(moved[full], base[full], atol=1e-10)
+    # the test has teeth: without the output's -t rotation the result moves
+    assert not np.allclose(O.rope(moved, d["t"] + D, d["dims"], 10.0)[full],
+                           O.rope(base, d["t"], d["dims"], 10.0)[full], atol=1e-3)
+    # and a rotary part changes the result at all
+    plain = O.csa_attend(O.rms_norm(d["q"], d["gq"], 1e-6), O.rms_norm(d["Ccomp"], d["gk"], 1e-6), d["idx"],
+                         O.rms_norm(d["kv_raw"], d["gk"], 1e-6), 0, d["sink"], d["t"], d["n_win"], d["scale"], d["m"])
+    assert not np.allclose(plain, base, atol=1e-3)
+
+
+def test_rope_attention_brute_force_relative_rotation():
+    # independent formulation for one query: each logit uses the key rotated by
+    # (p - t) against the unrotated normalised query, and each value enters
+    # rotated by (p - t); no rotation is applied to the query or the output
+    d = _rope_case(15)
+    r = 41
+    out = O.csa_attend_rope(d["q"], d["Ccomp"], d["idx"], d["kv_raw"], 0, d["sink"], d["t"], d["n_win"],
+                            d["scale"], d["m"], d["gq"], d["gk"], 1e-6, d["dims"], 10.0)[r]
+    qn = O.rms_norm(d["q"][r], d["gq"], 1e-6)
+    sel = [s for s in d["idx"][r] if s >= 0]
+    rows = [(O.rms_norm(d["Ccomp"][s], d["gk"], 1e-6), d["m"] * s) for s in sel]
+    rows += [(O.rms_norm(d["kv_raw"][p], d["gk"], 1e-6), p) for p in range(max(0, r - d["n_win"] + 1), r + 1)]
+    E = np.stack([O.rope(e[None], [p - r], d["dims"], 10.0)[0] for e, p in rows])
+    logits = d["scale"] * qn @ E.T
+    mx = np.maximum(logits.max(axis=1), d["sink"])
+    w = np.exp(logits - mx[:, None])
+    want = (w @ E) / (w.sum(axis=1) + np.exp(d["sink"] - mx))[:, None]
+    assert np.allclose(out, want, atol=1e-12)
