@@ -187,6 +187,69 @@ def run_prefill(args, torch, L, synth):
     ms4 = 1000.0 * (time.perf_counter() - t0) / args.steps
     del qc, qs, kc, ks
 
+    # A whole step with the normalisation and partial RoPE around the core
+    # attention: compressed entries (at m * s), window rows and query heads are
+    # RMS-normalised and rotated on their last 64 dims, and the output is
+    # turned back by -t in place.  Gains are seeded synthetic values.
+    _, gq = synth.norm_rope_inputs(1, 1, c, seed=46, device="cuda")
+    _, gk = synth.norm_rope_inputs(1, 1, c, seed=47, device="cuda")
+    qn = torch.empty_like(d["q"])
+    Cn = torch.empty_like(Cc)
+    Rn = torch.empty_like(d["kv_raw"])
+    eps, rd, base = 1e-6, 64, 10000.0
+
+    def norm_entries():
+        return lib.csa_norm_rope(P(Cc), c, P(Cn), c, P(gk), eps, ne, 1, c, rd, base, 0, m, 1, st)
+
+    def norm_window_rows():
+        return lib.csa_norm_rope(P(d["kv_raw"]), c, P(Rn), c, P(gk), eps, n, 1, c, rd, base, 0, 1, 1, st)
+
+    def norm_queries():
+        return lib.csa_norm_rope(P(d["q"]), nh * c, P(qn), nh * c, P(gq), eps, n, nh, c, rd, base, 0, 1, 1, st)
+
+    def attend_normed():
+        return lib.csa_attend(P(qn), P(Cn), 0, P(idx), P(Rn), 0, 0, P(d["sink"]), 1, n, 0, ne, n, nh, c, k, m, nw,
+                              d["scale"], 1, None, 0, P(out), st)
+
+    def rotate_output():
+        return lib.csa_norm_rope(P(out), nh * c, P(out), nh * c, None, 0.0, n, nh, c, rd, base, 0, -1, 1, st)
+
+    stagesR = [("compress_main", comp_main), ("compress_index_keys", comp_index),
+               ("norm_rope_entries", norm_entries), ("norm_rope_window_rows", norm_window_rows),
+               ("norm_rope_queries", norm_queries), ("index_topk", index_topk), ("attend", attend_normed),
+               ("rotate_output", rotate_output)]
+
+    def stepR(timer=None):
+        for name, fn in stagesR:
+            rc = timer.run(name, fn) if timer else fn()
+            if rc != 0:
+                raise RuntimeError(f"{name} failed: {L.strerror(rc)}")
+
+    for _ in range(args.warmup):
+        stepR()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        stepR()
+    torch.cuda.synchronize()
+    msR = 1000.0 * (time.perf_counter() - t0) / args.steps
+    timerR = KernelTimer(torch)
+    for _ in range(args.steps):
+        stepR(timerR)
+    timerR.collect()
+    nq_bytes = 2 * n * nh * c * 2            # query heads read and written once
+    rot_bytes = 2 * n * nh * rd * 2          # rotated output dims read and written
+    nr_us = {name: timerR.avg_us(name) for name, _ in stagesR if name.startswith(("norm", "rotate"))}
+    norm_rope_step = {
+        "ms_per_step": msR, "tokens_per_s": n / (msR / 1000.0), "stages": [name for name, _ in stagesR],
+        "stage_us": nr_us,
+        "queries_gbs": nq_bytes / (nr_us["norm_rope_queries"] * 1e-6) / 1e9,
+        "queries_hbm_frac": nq_bytes / (nr_us["norm_rope_queries"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "rotate_output_gbs": rot_bytes / (nr_us["rotate_output"] * 1e-6) / 1e9,
+        "gains": "seeded synthetic (1 + N(0, 0.1^2) per dim); eps 1e-6, RoPE base 10000 on the last 64 dims",
+    }
+    del qn, Cn, Rn
+
     sel, win = prefill_pairs(n, m, k, nw)
     flop_attend = (sel + win) * 4 * nh * c
     vis_pairs = sum(min((t + 1) // m, ne) for t in range(n))
@@ -202,6 +265,7 @@ def run_prefill(args, torch, L, synth):
         "index_tflops": flop_index / (stage_us["index_topk"] * 1e-6) / 1e12,
         "index_topk_mxfp4_us": index_mx_us,
         "index_topk_fp8_us": index_f8_us,
+        "norm_rope_step": norm_rope_step,
         "mxfp4_step": {"ms_per_step": ms4, "tokens_per_s": n / (ms4 / 1000.0),
                        "stages": [name for name, _ in stages4],
                        "queries": "indexer queries given as MXFP4 codes"},
@@ -705,6 +769,7 @@ def main(argv=None):
         "index_topk_mxfp4_us": pre["index_topk_mxfp4_us"],
         "index_topk_fp8_us": pre["index_topk_fp8_us"],
         "prefill_mxfp4_indexer": pre["mxfp4_step"],
+        "prefill_norm_rope": pre["norm_rope_step"],
     }
     if "decode_1m" in extras:
         line["decode_us_per_step"] = extras["decode_1m"]["us_per_step"]

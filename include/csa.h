@@ -160,6 +160,52 @@ int csa_index_topk_mxfp4(const void* qI, const void* qI_scale, const float* w, c
                          float* score, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * csa_norm_rope -- RMSNorm and partial rotary position embedding of query
+ * heads, KV entries and attention outputs (songhuiming "DeepSeek-V4 百万
+ * token 上下文" section 4.5; AirCoding "deepseek-paper-analysis" section
+ * 7.1): before the core attention every query head and every KV entry is
+ * RMS-normalised, and the last 64 dimensions of queries and entries carry a
+ * rotary embedding at their positions; the attention output's last 64
+ * dimensions are then turned back by -t so that only relative positions
+ * remain in it.
+ *
+ * For each of `rows` rows holding `heads` vectors of c values:
+ *   y = x / sqrt(mean(x^2) + eps) * gamma     (skipped when gamma is NULL)
+ *   then for i < rope_dims/2 the pair (y[c-rope_dims+2i], y[c-rope_dims+2i+1])
+ *   = (a, b) becomes (a cos A - b sin A, a sin A + b cos A) with
+ *   A = pos * base^(-2i/rope_dims), pos = pos0 + row * pos_step.
+ * Computed in float32 (angles in float64), stored in the storage type with
+ * round-to-nearest-even.
+ *
+ *  x        [rows][x_rstride] float32 (CSA_F32) or bf16 (CSA_BF16); row r
+ *           holds heads * c values: vector h at x + r*x_rstride + h*c
+ *  out      [rows][out_rstride], same layout; may be x itself (same
+ *           stride) for an in-place update, otherwise must not overlap x
+ *  gamma    [c] float32 per-dimension gain, or NULL for no normalisation
+ *  eps      >= 0, added to the mean square
+ *  rope_dims  even, 0 (no rotation) .. min(c, 512)
+ *  base     > 0, the rotary base (only read when rope_dims > 0)
+ *  pos0, pos_step  positions of the rows, |value| <= 2^40 for every row
+ * Typical calls: query heads of a prefill block (heads = n_h, pos0 = t0,
+ * pos_step = 1); compressed entries (heads = 1, pos_step = m); raw window
+ * rows (heads = 1, pos0 = their first position); the attention output
+ * (gamma NULL, pos0 = -t0, pos_step = -1); one decode step of b sequences
+ * (rows = b, pos_step = 0).
+ * x, out and gamma must be 16-byte aligned and the row strides times the
+ * element size multiples of 16.  All pointers are device memory owned by
+ * the caller; nothing is allocated.
+ * Errors: CSA_EINVAL for negative rows, heads or c < 1, odd or out-of-range
+ * rope_dims, eps < 0, base <= 0, positions out of range, strides below
+ * heads * c, misalignment, NULL x/out with rows > 0, or partial overlap of x
+ * and out; CSA_ENOTSUP for other dtypes, c not a multiple of 8 (bf16) or 4
+ * (float32), c above 2048 (bf16) or 1024 (float32), rope_dims > 512, or more
+ * than 2^31 - 1 rows.
+ */
+int csa_norm_rope(const void* x, int64_t x_rstride, void* out, int64_t out_rstride, const float* gamma,
+                  float eps, int64_t rows, int64_t heads, int64_t c, int64_t rope_dims, double base,
+                  int64_t pos0, int64_t pos_step, int dtype, void* stream);
+
+/*
  * csa_quantize_mxfp4 -- OCP MXFP4 encoding of `rows` rows of c values, for
  * the indexer's FP4 query/key cache (songhuiming "DeepSeek-V4 百万 token
  * 上下文" section 13.3; AirCoding "deepseek-paper-analysis" section 7, FP4

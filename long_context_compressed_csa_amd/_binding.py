@@ -39,6 +39,8 @@ SIGNATURES = {
     "csa_index_topk_workspace_size": (_sz, [_i64] * 4),
     "csa_index_topk_mxfp4": (_int, [_vp] * 5 + [_i64] * 9 + [_vp, _vp, _vp, _sz, _vp]),
     "csa_quantize_mxfp4": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp]),
+    "csa_norm_rope": (_int, [_vp, _i64, _vp, _i64, _vp, _f32, _i64, _i64, _i64, _i64, ctypes.c_double,
+                             _i64, _i64, _int, _vp]),
     "csa_attend": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp] + [_i64] * 10
                    + [_f32, _int, _vp, _sz, _vp, _vp]),
     "csa_attend_workspace_size": (_sz, [_i64] * 9 + [_int]),
@@ -241,6 +243,27 @@ def csa_quantize_mxfp4(x, codes=None, scales=None, stream=None):
                                 _stream(stream))
     _check(rc, "csa_quantize_mxfp4")
     return codes, scales
+
+
+def csa_norm_rope(x, gamma=None, eps=1e-6, rope_dims=64, base=10000.0, pos0=0, pos_step=1, out=None,
+                  stream=None):
+    """RMSNorm (gamma [c] float32, or None for none) and rotary embedding of
+    the last rope_dims dimensions of every vector of x [rows, c] or
+    [rows, heads, c]; row r at position pos0 + r * pos_step.  Returns out
+    (x itself when out is x: in place)."""
+    c = x.shape[-1]
+    rows = x.shape[0] if x.dim() > 1 else 1
+    heads = x.numel() // (rows * c) if x.numel() else 1
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    lib = load_library()
+    g = None if gamma is None else _f32c(gamma, "gamma")
+    rc = lib.csa_norm_rope(_ptr(x), heads * c, _ptr(out), heads * c, g, float(eps), rows, heads, c,
+                           int(rope_dims), float(base), int(pos0), int(pos_step), _dtype(x, out), _stream(stream))
+    _check(rc, "csa_norm_rope")
+    return out
 
 
 def csa_attend(q, Ccomp, idx, kv_raw, sink, t0, m, n_win, scale=None, raw_pos0=0,

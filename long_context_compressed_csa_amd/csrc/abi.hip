@@ -144,6 +144,40 @@ int csa_quantize_mxfp4(const void* x, int64_t x_rstride, int64_t rows, int64_t c
                                              scales_rstride, (hipStream_t)stream));
 }
 
+int csa_norm_rope(const void* x, int64_t x_rstride, void* out, int64_t out_rstride, const float* gamma,
+                  float eps, int64_t rows, int64_t heads, int64_t c, int64_t rope_dims, double base,
+                  int64_t pos0, int64_t pos_step, int dtype, void* stream) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return CSA_ENOTSUP;
+  if (rows < 0 || heads < 1 || c < 1) return CSA_EINVAL;
+  if (rope_dims < 0 || rope_dims > c || (rope_dims & 1)) return CSA_EINVAL;
+  if (!(eps >= 0.f) || !isfinite(eps)) return CSA_EINVAL;
+  if (rope_dims > 0 && !(base > 0.0 && isfinite(base))) return CSA_EINVAL;
+  const int64_t es = dtype == CSA_F32 ? 4 : 2, V = 16 / es;
+  if (x_rstride < heads * c || out_rstride < heads * c) return CSA_EINVAL;
+  // positions stay far inside the range where float64 holds them and their angles exactly
+  const int64_t kPosMax = 1LL << 40;
+  if (pos0 > kPosMax || pos0 < -kPosMax || pos_step > kPosMax || pos_step < -kPosMax) return CSA_EINVAL;
+  if (rows > 0) {
+    const int64_t last = pos0 + (rows - 1) * pos_step;
+    if (rows > kPosMax || last > kPosMax || last < -kPosMax) return CSA_EINVAL;
+  }
+  if (c % V != 0 || c > 256 * V || rope_dims > 512) return CSA_ENOTSUP;
+  if (rows > 2147483647LL || heads * c > 2147483647LL) return CSA_ENOTSUP;
+  if (rows == 0) return CSA_OK;
+  if (!x || !out) return CSA_EINVAL;
+  // 16-byte loads and stores
+  if (((uintptr_t)x & 15u) != 0 || ((uintptr_t)out & 15u) != 0 || (x_rstride * es) % 16 != 0 ||
+      (out_rstride * es) % 16 != 0 || ((uintptr_t)gamma & 15u) != 0)
+    return CSA_EINVAL;
+  // in place (same pointer and stride) or disjoint
+  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
+  const uintptr_t xe = xa + (uintptr_t)(((rows - 1) * x_rstride + heads * c) * es);
+  const uintptr_t oe = oa + (uintptr_t)(((rows - 1) * out_rstride + heads * c) * es);
+  if (!(xa == oa && x_rstride == out_rstride) && xa < oe && oa < xe) return CSA_EINVAL;
+  return launched(csa::launch_norm_rope(x, x_rstride, out, out_rstride, gamma, eps, rows, heads, c, rope_dims,
+                                        base, pos0, pos_step, dtype, (hipStream_t)stream));
+}
+
 size_t csa_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
                                  int64_t c, int64_t k, int64_t m, int64_t n_win, int dtype) {
   if (b < 1 || n_q < 1 || m < 1 || t0 < 0 || k < 0 || n_win < 1) return 0;

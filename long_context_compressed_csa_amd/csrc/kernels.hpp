@@ -38,4 +38,8 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
                          int64_t c, int64_t k, int64_t m, int64_t n_win, float scale, int dtype,
                          void* ws, void* out, hipStream_t st);
 
+hipError_t launch_norm_rope(const void* x, int64_t xrs, void* out, int64_t ors, const float* gamma, float eps,
+                            int64_t rows, int64_t heads, int64_t c, int64_t rope_dims, double base, int64_t pos0,
+                            int64_t pos_step, int dtype, hipStream_t st);
+
 }  // namespace csa

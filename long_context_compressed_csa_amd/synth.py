@@ -197,6 +197,15 @@ def prefill_inputs(n=None, seed=None, device="cpu", n_h=None, k=None, unscaled=F
     return d
 
 
+def norm_rope_inputs(rows, heads, c, dtype=torch.bfloat16, seed=0, device="cpu", std=3.0, gain=True):
+    """Vectors x [rows, heads, c] ~ N(0, std^2) and per-dimension norm gains
+    gamma [c] = 1 + N(0, 0.1^2) in float32 (None when gain is False)."""
+    g = _gen(seed, device)
+    x = normal((rows, heads, c), g, std, dtype, device)
+    gamma = (1.0 + normal((c,), g, 0.1, torch.float32, device)) if gain else None
+    return x, gamma
+
+
 def hca_inputs(n=None, seed=None, device="cpu", n_h=None, m_prime=None):
     """HCA prefill layer; q is the big tensor ([n, n_h, c])."""
     p = dict(HCA)

@@ -143,6 +143,39 @@ def test_quantize_mxfp4_rejects_bad_arguments(lib):
     assert _quant(lib, xrs=68) == EINVAL          # bf16 rows must stay 16-byte aligned
 
 
+def _nr(lib, **kw):
+    a = dict(x=0x100000, xrs=128, out=0x300000, ors=128, gamma=0x400000, eps=1e-6, rows=4, heads=2, c=64,
+             rd=16, base=10000.0, pos0=0, step=1, dtype=1)
+    a.update(kw)
+    return lib.csa_norm_rope(a["x"], a["xrs"], a["out"], a["ors"], a["gamma"], a["eps"], a["rows"], a["heads"],
+                             a["c"], a["rd"], a["base"], a["pos0"], a["step"], a["dtype"], None)
+
+
+def test_norm_rope_rejects_bad_arguments(lib):
+    assert _nr(lib, rows=0) == 0                      # nothing to do
+    assert _nr(lib, dtype=2) == ENOTSUP
+    assert _nr(lib, x=None) == EINVAL
+    assert _nr(lib, out=None) == EINVAL
+    assert _nr(lib, rows=-1) == EINVAL
+    assert _nr(lib, heads=0) == EINVAL
+    assert _nr(lib, rd=15) == EINVAL                  # pairs
+    assert _nr(lib, rd=66) == EINVAL                  # more than c
+    assert _nr(lib, eps=-1.0) == EINVAL
+    assert _nr(lib, eps=float("nan")) == EINVAL
+    assert _nr(lib, base=0.0) == EINVAL
+    assert _nr(lib, base=float("inf")) == EINVAL
+    assert _nr(lib, xrs=120) == EINVAL                # below heads * c
+    assert _nr(lib, x=0x100008) == EINVAL             # 16-byte loads
+    assert _nr(lib, gamma=0x400004) == EINVAL         # 16-byte gain loads
+    assert _nr(lib, xrs=132) == EINVAL                # bf16 rows must stay 16-byte aligned
+    assert _nr(lib, pos0=1 << 41) == EINVAL
+    assert _nr(lib, pos0=(1 << 40) - 2, step=1) == EINVAL   # the last row passes the limit
+    assert _nr(lib, out=0x100100) == EINVAL           # partial overlap with x
+    assert _nr(lib, c=68, xrs=136, ors=136) == ENOTSUP   # bf16 c must be a multiple of 8
+    assert _nr(lib, c=2056, xrs=4112, ors=4112, rd=0) == ENOTSUP   # above 2048 bf16 values
+    assert _nr(lib, c=1024, xrs=2048, ors=2048, rd=514) == ENOTSUP   # at most 256 rotation pairs
+
+
 def test_index_topk_workspace_size_grows_with_candidates(lib):
     small = lib.csa_index_topk_workspace_size(1, 4, 100, 8)
     big = lib.csa_index_topk_workspace_size(1, 4, 100000, 8)

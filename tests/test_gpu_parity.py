@@ -1077,3 +1077,136 @@ def test_graph_replay_matches_eager():
         sc = O.index_scores(to64(dqI[sq, 0])[None], to64(dw[sq, 0])[None], to64(dKI[sq]), [td], m)
         oi = O.topk_select(sc[0], nd, kd)
         assert_index_sets(didx[sq].cpu().numpy(), oi[None], sc, [nd], kd, f"graph decode seq {sq}")
+
+
+# ------------------------------------------------ RMSNorm and partial RoPE --
+
+@pytest.mark.parametrize("dtype,rows,heads,c,rd,gain,pos0,step", [
+    (torch.float32, 37, 3, 64, 16, True, 0, 1),              # heads per wave, ragged last pass
+    (torch.bfloat16, 6, 64, 512, 64, True, 1000, 1),         # query heads of a prefill block
+    (torch.bfloat16, 300, 1, 512, 64, True, 0, 4),           # compressed entries at m * s
+    (torch.bfloat16, 5, 64, 512, 64, False, -1048579, -1),   # output turned back by -t near 2^20
+    (torch.bfloat16, 8, 64, 512, 64, True, 1048576, 0),      # one decode step of 8 sequences
+    (torch.bfloat16, 9, 2, 1024, 128, True, 3, 7),           # two chunks per lane
+    (torch.bfloat16, 4, 1, 2048, 512, True, -5, 3),          # four chunks per lane, widest rotation
+    (torch.float32, 7, 5, 1024, 0, True, 0, 1),              # norm only
+    (torch.float32, 3, 1, 520, 64, False, 9, 1),             # rotation only, ragged chunk count
+])
+def test_norm_rope(dtype, rows, heads, c, rd, gain, pos0, step):
+    say(f"norm_rope {dtype} rows={rows} heads={heads} c={c} rope={rd} gain={gain} pos0={pos0} step={step}")
+    x, gamma = synth.norm_rope_inputs(rows, heads, c, dtype, seed=rows * 7 + c, gain=gain)
+    out = L.csa_norm_rope(g(x), None if gamma is None else g(gamma), 1e-6, rd, 10000.0, pos0, step)
+    torch.cuda.synchronize()
+    pos = pos0 + step * np.arange(rows)
+    want = O.norm_rope(to64(x), None if gamma is None else to64(gamma), 1e-6, pos, rd, 10000.0)
+    assert_close(out, want, dtype, "norm_rope")
+
+
+@pytest.mark.parametrize("dtype,c,rd", [
+    (torch.bfloat16, 512, 64),     # the attention output's back-rotation
+    (torch.float32, 520, 62),      # rotated part starting inside a 16-byte chunk
+    (torch.bfloat16, 64, 0),       # nothing rotated: unchanged
+])
+def test_norm_rope_rotation_only_in_place(dtype, c, rd):
+    # no gain and out == x: only the chunks holding rotated dimensions are
+    # read and written; every other value must stay bit for bit
+    say(f"norm_rope rotation only, in place {dtype} c={c} rope={rd}")
+    rows, heads = 11, 5
+    x, _ = synth.norm_rope_inputs(rows, heads, c, dtype, seed=c + rd, gain=False)
+    xd = g(x)
+    got = L.csa_norm_rope(xd, None, 0.0, rd, 10000.0, -40, -3, out=xd)
+    torch.cuda.synchronize()
+    assert got.data_ptr() == xd.data_ptr()
+    got = got.cpu()
+    assert torch.equal(got[..., :c - rd], x[..., :c - rd])
+    want = O.rope(to64(x), -40 - 3 * np.arange(rows), rd, 10000.0)
+    assert_close(got, want, dtype, "rotation in place")
+
+
+def test_norm_rope_in_place_on_strided_rows():
+    # the first vector of every cache row, updated in place through the row
+    # stride; the second vector of each row must not move
+    say("norm_rope in place, strided rows")
+    rows, c = 33, 512
+    x, gamma = synth.norm_rope_inputs(rows, 2, c, torch.bfloat16, seed=77)
+    xd = g(x)
+    lib = L.load_library()
+    rc = lib.csa_norm_rope(xd.data_ptr(), 2 * c, xd.data_ptr(), 2 * c, g(gamma).data_ptr(), 1e-6, rows, 1, c,
+                           64, 10000.0, 12, 4, L.CSA_BF16, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    got = xd.cpu()
+    assert torch.equal(got[:, 1], x[:, 1])
+    want = O.norm_rope(to64(x[:, 0]), to64(gamma), 1e-6, 12 + 4 * np.arange(rows), 64, 10000.0)
+    assert_close(got[:, 0], want, torch.bfloat16, "in place")
+
+
+def _norm_rope_layer_case(n, nh, k, seed):
+    d = synth.prefill_inputs(n=n, seed=seed, n_h=nh, k=k, unscaled=True)
+    _, gq = synth.norm_rope_inputs(1, 1, 512, seed=seed + 1)
+    _, gk = synth.norm_rope_inputs(1, 1, 512, seed=seed + 2)
+    m = 4
+    Cc = torch.tensor(O.compress_overlap(*(to64(d[x]) for x in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m),
+                      dtype=torch.float32)
+    idx = torch.tensor(_oracle_idx_for(d["KIcomp"], d["qI"], d["w"], np.arange(n), m, k), dtype=torch.int32)
+    return d, gq, gk, Cc, idx, m
+
+
+def _norm_rope_layer_gpu(q, Cc, idx, raw, sink, gq, gk, m, nw, scale, eps, rd, base):
+    qn = L.csa_norm_rope(g(q), g(gq), eps, rd, base, 0, 1)
+    Cn = L.csa_norm_rope(g(Cc), g(gk), eps, rd, base, 0, m)
+    Rn = L.csa_norm_rope(g(raw), g(gk), eps, rd, base, 0, 1)
+    o = L.csa_attend(qn[None], Cn[None], g(idx)[None], Rn[None], g(sink), 0, m, nw, scale)[0]
+    L.csa_norm_rope(o, None, 0.0, rd, base, 0, -1, out=o)
+    torch.cuda.synchronize()
+    return o
+
+
+def test_csa_layer_with_norm_and_rope_fp32():
+    # the composition (positions of queries, entries at m*s and window rows,
+    # the output turned back by -t) against the oracle's composed definition,
+    # float32 throughout so that the strict float32 bound applies
+    n, nh, k, nw = 128, 64, 16, 48
+    say(f"csa layer with norm and rope, float32 n={n} n_h={nh} k={k} n_win={nw}")
+    d, gq, gk, Cc, idx, m = _norm_rope_layer_case(n, nh, k, 43)
+    f = lambda t: t.to(torch.float32)
+    eps, rd, base = 1e-6, 64, 10000.0
+    o = _norm_rope_layer_gpu(f(d["q"]), Cc, idx, f(d["kv_raw"]), d["sink"], gq, gk, m, nw, d["scale"], eps, rd,
+                             base)
+    want = O.csa_attend_rope(to64(d["q"]), to64(Cc), idx.numpy(), to64(d["kv_raw"]), 0, to64(d["sink"]),
+                             np.arange(n), nw, d["scale"], m, to64(gq), to64(gk), eps, rd, base)
+    assert_close(o, want, torch.float32, "layer with norm and rope, float32")
+
+
+def test_csa_layer_with_norm_and_rope_bf16():
+    # the bf16 production path: normalised queries, entries and window rows
+    # and the output are stored in bf16 between the calls.  The reference
+    # composes the oracle's pieces with the same round-to-nearest-even
+    # storage at those points (torch conversion), so the bound measures the
+    # kernels, not the storage format (four bf16 stores alone move single
+    # outputs by up to 3% of their row RMS at this shape)
+    n, nh, k, nw = 512, 64, 64, 128
+    say(f"csa layer with norm and rope, bf16 n={n} n_h={nh} k={k}")
+    d, gq, gk, Cc, idx, m = _norm_rope_layer_case(n, nh, k, 43)
+    Cc = Cc.to(torch.bfloat16)
+    eps, rd, base = 1e-6, 64, 10000.0
+    o = _norm_rope_layer_gpu(d["q"], Cc, idx, d["kv_raw"], d["sink"], gq, gk, m, nw, d["scale"], eps, rd, base)
+    st = lambda a: to64(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+    t = np.arange(n)
+    qn = st(O.norm_rope(to64(d["q"]), to64(gq), eps, t, rd, base))
+    Cn = st(O.norm_rope(to64(Cc), to64(gk), eps, m * np.arange(Cc.shape[0]), rd, base))
+    Rn = st(O.norm_rope(to64(d["kv_raw"]), to64(gk), eps, t, rd, base))
+    att = st(O.csa_attend(qn, Cn, idx.numpy(), Rn, 0, to64(d["sink"]), t, nw, d["scale"], m))
+    want = O.rope(att, -t, rd, base)
+    lo = want.shape[-1] - rd
+    assert_close(o[..., :lo], want[..., :lo], torch.bfloat16, "layer with norm and rope, bf16, unrotated dims")
+    # rotated dims: the output was stored in bf16 before its rotation, so each
+    # element also carries the storage error of its pair partner; a rotation
+    # keeps the pair's norm, so both half-ulps are at most 2^-9 of that norm
+    got = to64(o)
+    rms = np.sqrt(np.mean(want ** 2, axis=-1, keepdims=True))
+    pair = np.sqrt(want[..., lo::2] ** 2 + want[..., lo + 1::2] ** 2).repeat(2, axis=-1)
+    bound = 2e-2 * rms + 2.0 ** -8 * np.abs(want[..., lo:]) + 2.0 ** -8 * pair
+    excess = np.abs(got[..., lo:] - want[..., lo:]) - bound
+    i = np.unravel_index(int(np.argmax(excess)), excess.shape)
+    assert excess[i] <= 0, ("rotated dims", i, got[..., lo:][i], want[..., lo:][i], bound[i])
