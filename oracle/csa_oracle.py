@@ -43,7 +43,11 @@ design notes):
     with a per-dimension gain and explicit eps, then rotation of the last 64
     dimensions as adjacent pairs with frequencies base^(-2i/64); a compressed
     entry sits at the position of its block's first token; the attention
-    output is rotated back by -t.
+    output is rotated back by -t;
+  * grouped output projection ([P2] section 4.4): groups of consecutive
+    heads, each group's heads concatenated in head order, the group results
+    concatenated in group order; weights stored with the input dimension
+    contiguous ([g, d_g, (n_h/g) c] and [d, g d_g]).
 
 parity unpinned: none of the routines here.  Each has at least one test that
 pins it to something other than itself (closed forms, invariants, library
@@ -510,6 +514,32 @@ def csa_attend_rope(q, Ccomp, idx, kv_raw, raw_pos0: int, sink, t_pos, n_win: in
     Rn = norm_rope(kv_raw, gamma_kv, eps, raw_pos0 + np.arange(_f64(kv_raw).shape[0]), dims, base)
     o = csa_attend(qn, Cn, idx, Rn, raw_pos0, sink, t_pos, n_win, scale, m)
     return rope(o, -t_pos, dims, base)
+
+
+# --------------------------------------------------------------------------
+# Grouped output projection ([P2] section 4.4; [P3] section 7.1)
+# --------------------------------------------------------------------------
+
+def grouped_out_proj(o, WG, WO, g: int, mid_round=None):
+    """u_t = W^O [W^G_1 o^1_t; ...; W^G_g o^g_t].
+
+    [P2] section 4.4: the n_h head outputs of a token are split into g groups
+    of n_h/g consecutive heads; group j's concatenated output o^j_t (head
+    order, then dimension) is projected to d_g values, and the g results,
+    concatenated in group order, are projected to d.  [P3] section 7.1 gives
+    the Flash shape g = 8, d_g = 1024, d = 4096.
+    o [n, n_h, c]; WG [g, d_g, (n_h/g)*c] (group j maps o^j to W^G_j o^j);
+    WO [d, g*d_g].  Returns (mid [n, g*d_g], u [n, d]).  mid_round, when
+    given, is applied to mid before the second projection (the storage format
+    of an intermediate kept between two calls).
+    """
+    o, WG, WO = _f64(o), _f64(WG), _f64(WO)
+    n, n_h, c = o.shape
+    hpg = n_h // g
+    parts = [o[:, j * hpg:(j + 1) * hpg, :].reshape(n, hpg * c) @ WG[j].T for j in range(g)]
+    mid = np.concatenate(parts, axis=1)
+    mid2 = mid if mid_round is None else _f64(mid_round(mid))
+    return mid, mid2 @ WO.T
 
 
 # --------------------------------------------------------------------------

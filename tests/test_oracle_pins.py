@@ -664,3 +664,49 @@ def test_rope_attention_brute_force_relative_rotation():
     w = np.exp(logits - mx[:, None])
     want = (w @ E) / (w.sum(axis=1) + np.exp(d["sink"] - mx))[:, None]
     assert np.allclose(out, want, atol=1e-12)
+
+
+# ------------------------------------------------ grouped output projection ----
+# [P2] section 4.4: heads in g groups, each group's concatenated output
+# projected to d_g, the concatenation of the g results projected to d.
+
+def test_grouped_out_proj_brute_force_scalar_loops():
+    rng = _rng(21)
+    n, n_h, c, g, d_g, d = 2, 4, 3, 2, 5, 3
+    o = rng.standard_normal((n, n_h, c))
+    WG = rng.standard_normal((g, d_g, (n_h // g) * c))
+    WO = rng.standard_normal((d, g * d_g))
+    mid, u = O.grouped_out_proj(o, WG, WO, g)
+    for t in range(n):
+        for j in range(g):
+            for r in range(d_g):
+                acc = 0.0
+                for hh in range(n_h // g):          # heads j*n_h/g .. in order
+                    for x in range(c):
+                        acc += WG[j, r, hh * c + x] * o[t, j * (n_h // g) + hh, x]
+                assert abs(mid[t, j * d_g + r] - acc) < 1e-12
+        for e in range(d):
+            acc = sum(WO[e, q] * mid[t, q] for q in range(g * d_g))
+            assert abs(u[t, e] - acc) < 1e-12
+
+
+def test_grouped_out_proj_equals_block_diagonal_projection():
+    # the same map as one block-diagonal matrix over the flat head outputs
+    rng = _rng(22)
+    n, n_h, c, g, d_g, d = 7, 8, 16, 4, 6, 10
+    o = rng.standard_normal((n, n_h, c))
+    WG = rng.standard_normal((g, d_g, (n_h // g) * c))
+    WO = rng.standard_normal((d, g * d_g))
+    BD = np.zeros((g * d_g, n_h * c))
+    for j in range(g):
+        BD[j * d_g:(j + 1) * d_g, j * (n_h // g) * c:(j + 1) * (n_h // g) * c] = WG[j]
+    mid, u = O.grouped_out_proj(o, WG, WO, g)
+    assert np.allclose(mid, o.reshape(n, -1) @ BD.T, atol=1e-12)
+    assert np.allclose(u, (o.reshape(n, -1) @ BD.T) @ WO.T, atol=1e-12)
+    # one group: two plain products; a group's weights touch only its heads
+    mid1, u1 = O.grouped_out_proj(o, BD[None, :d_g], WO[:, :d_g], 1)
+    assert np.allclose(mid1, o.reshape(n, -1) @ BD[:d_g].T, atol=1e-12)
+    assert np.allclose(u1, mid1 @ WO[:, :d_g].T, atol=1e-12)
+    o2 = o.copy()
+    o2[:, n_h // g:, :] += 1.0                     # heads outside group 0
+    assert np.allclose(O.grouped_out_proj(o2, WG, WO, g)[0][:, :d_g], mid[:, :d_g], atol=1e-12)
