@@ -250,6 +250,32 @@ def run_prefill(args, torch, L, synth):
     }
     del qn, Cn, Rn
 
+    # The grouped output projection of the step's attention output at the
+    # Flash shape (g = 8 groups of 8 heads, d_g = 1024, d = 4096), seeded
+    # synthetic weights: two bf16 MFMA products, timed together.
+    g_, dg_, dm_ = 8, 1024, 4096
+    _, WG, WO = synth.out_proj_inputs(1, nh, c, g_, dg_, dm_, seed=48, device="cuda")
+    mid = torch.empty((n, g_ * dg_), dtype=torch.bfloat16, device="cuda")
+    proj = torch.empty((n, dm_), dtype=torch.bfloat16, device="cuda")
+
+    def out_proj():
+        return lib.csa_grouped_out_proj(P(out), P(WG), P(WO), n, nh, c, g_, dg_, dm_, 1, P(mid), P(proj), st)
+
+    timerP = KernelTimer(torch)
+    for _ in range(5):
+        out_proj()
+    for _ in range(args.steps):
+        if timerP.run("grouped_out_proj", out_proj) != 0:
+            raise RuntimeError("grouped output projection failed")
+    timerP.collect()
+    proj_us = timerP.avg_us("grouped_out_proj")
+    proj_flop = 2 * n * (nh * c) * dg_ + 2 * n * (g_ * dg_) * dm_
+    out_proj_rec = {"us": proj_us, "flop": proj_flop, "tflops": proj_flop / (proj_us * 1e-6) / 1e12,
+                    "mfma_frac": proj_flop / (proj_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                    "shape": "n=8192, 64 heads x 512 -> 8 groups x 1024 -> 4096, bf16",
+                    "weights": "seeded synthetic, N(0,1)/sqrt(fan-in)"}
+    del WG, WO, mid, proj
+
     sel, win = prefill_pairs(n, m, k, nw)
     flop_attend = (sel + win) * 4 * nh * c
     vis_pairs = sum(min((t + 1) // m, ne) for t in range(n))
@@ -266,6 +292,7 @@ def run_prefill(args, torch, L, synth):
         "index_topk_mxfp4_us": index_mx_us,
         "index_topk_fp8_us": index_f8_us,
         "norm_rope_step": norm_rope_step,
+        "out_proj": out_proj_rec,
         "mxfp4_step": {"ms_per_step": ms4, "tokens_per_s": n / (ms4 / 1000.0),
                        "stages": [name for name, _ in stages4],
                        "queries": "indexer queries given as MXFP4 codes"},
@@ -770,6 +797,7 @@ def main(argv=None):
         "index_topk_fp8_us": pre["index_topk_fp8_us"],
         "prefill_mxfp4_indexer": pre["mxfp4_step"],
         "prefill_norm_rope": pre["norm_rope_step"],
+        "grouped_out_proj": pre["out_proj"],
     }
     if "decode_1m" in extras:
         line["decode_us_per_step"] = extras["decode_1m"]["us_per_step"]

@@ -206,6 +206,35 @@ int csa_norm_rope(const void* x, int64_t x_rstride, void* out, int64_t out_rstri
                   int64_t pos0, int64_t pos_step, int dtype, void* stream);
 
 /*
+ * csa_grouped_out_proj -- grouped output projection of the attention outputs
+ * (songhuiming "DeepSeek-V4 百万 token 上下文" section 4.4; AirCoding
+ * "deepseek-paper-analysis" section 7.1, which gives g = 8, d_g = 1024,
+ * d = 4096 for the Flash model): the n_h heads of a token form g groups of
+ * n_h/g consecutive heads; group j's outputs, concatenated in head order,
+ * are projected to d_g values by W^G_j; the g results, concatenated in group
+ * order, are projected to d by W^O:
+ *   mid[t, j*d_g + r] = sum_q WG[j][r][q] * o[t, j*(n_h/g) + q/c, q%c]
+ *   out[t, e]         = sum_p WO[e][p] * mid[t, p]
+ * bf16 operands, float32 accumulation (MFMA), bf16 results; mid is stored in
+ * bf16 and the second projection reads it back.
+ *
+ *  o    [n, n_h, c] bf16 (the attention output)
+ *  WG   [g, d_g, (n_h/g)*c] bf16, input dimension contiguous
+ *  WO   [d, g*d_g] bf16, input dimension contiguous
+ *  mid  out [n, g*d_g] bf16 (the intermediate; caller-owned)
+ *  out  out [n, d] bf16
+ * o, WG, WO and mid must be 16-byte aligned.  All pointers are device memory
+ * owned by the caller; nothing is allocated.  Results are reproducible run to
+ * run (fixed accumulation order).
+ * Errors: CSA_EINVAL for negative n, sizes < 1, n_h not a multiple of g,
+ * NULL pointers with n > 0, or misalignment; CSA_ENOTSUP for a dtype other
+ * than CSA_BF16, (n_h/g)*c or g*d_g not a multiple of 64, or sizes beyond
+ * the launch limits.
+ */
+int csa_grouped_out_proj(const void* o, const void* WG, const void* WO, int64_t n, int64_t n_h, int64_t c,
+                         int64_t g, int64_t d_g, int64_t d, int dtype, void* mid, void* out, void* stream);
+
+/*
  * csa_quantize_mxfp4 -- OCP MXFP4 encoding of `rows` rows of c values, for
  * the indexer's FP4 query/key cache (songhuiming "DeepSeek-V4 百万 token
  * 上下文" section 13.3; AirCoding "deepseek-paper-analysis" section 7, FP4

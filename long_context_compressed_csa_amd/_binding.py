@@ -39,6 +39,7 @@ SIGNATURES = {
     "csa_index_topk_workspace_size": (_sz, [_i64] * 4),
     "csa_index_topk_mxfp4": (_int, [_vp] * 5 + [_i64] * 9 + [_vp, _vp, _vp, _sz, _vp]),
     "csa_quantize_mxfp4": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp]),
+    "csa_grouped_out_proj": (_int, [_vp, _vp, _vp] + [_i64] * 6 + [_int, _vp, _vp, _vp]),
     "csa_norm_rope": (_int, [_vp, _i64, _vp, _i64, _vp, _f32, _i64, _i64, _i64, _i64, ctypes.c_double,
                              _i64, _i64, _int, _vp]),
     "csa_attend": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp] + [_i64] * 10
@@ -264,6 +265,25 @@ def csa_norm_rope(x, gamma=None, eps=1e-6, rope_dims=64, base=10000.0, pos0=0, p
                            int(rope_dims), float(base), int(pos0), int(pos_step), _dtype(x, out), _stream(stream))
     _check(rc, "csa_norm_rope")
     return out
+
+
+def csa_grouped_out_proj(o, WG, WO, mid=None, out=None, stream=None):
+    """Grouped output projection: o [n, n_h, c]; WG [g, d_g, (n_h/g)*c];
+    WO [d, g*d_g], all bf16.  Returns (mid [n, g*d_g], out [n, d])."""
+    n, n_h, c = o.shape
+    g, d_g, _ = WG.shape
+    d = WO.shape[0]
+    if mid is None:
+        mid = torch.empty((n, g * d_g), dtype=o.dtype, device=o.device)
+    if out is None:
+        out = torch.empty((n, d), dtype=o.dtype, device=o.device)
+    if WG.shape[2] * g != n_h * c or WO.shape[1] != g * d_g:
+        raise ValueError("weight shapes do not match o")
+    lib = load_library()
+    rc = lib.csa_grouped_out_proj(_ptr(o), _ptr(WG), _ptr(WO), n, n_h, c, g, d_g, d, _dtype(o, WG, WO, mid, out),
+                                  _ptr(mid), _ptr(out), _stream(stream))
+    _check(rc, "csa_grouped_out_proj")
+    return mid, out
 
 
 def csa_attend(q, Ccomp, idx, kv_raw, sink, t0, m, n_win, scale=None, raw_pos0=0,

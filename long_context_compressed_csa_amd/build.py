@@ -37,6 +37,9 @@ CXXFLAGS = [
 # the AMDGPU trackers, without which its main loop spills.
 EXTRA_FLAGS = {
     "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-use-amdgpu-trackers=1"],
+    # outproj.hip: 128 accumulators + operands fit 256 VGPRs; in AGPRs the
+    # compiler moves them back and forth around the K loop
+    "outproj.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -178,6 +178,28 @@ int csa_norm_rope(const void* x, int64_t x_rstride, void* out, int64_t out_rstri
                                         base, pos0, pos_step, dtype, (hipStream_t)stream));
 }
 
+int csa_grouped_out_proj(const void* o, const void* WG, const void* WO, int64_t n, int64_t n_h, int64_t c,
+                         int64_t g, int64_t d_g, int64_t d, int dtype, void* mid, void* out, void* stream) {
+  if (n < 0 || n_h < 1 || c < 1 || g < 1 || d_g < 1 || d < 1) return CSA_EINVAL;
+  if (n_h % g != 0) return CSA_EINVAL;
+  if (dtype != CSA_BF16) return CSA_ENOTSUP;
+  const int64_t K1 = (n_h / g) * c, K2 = g * d_g;
+  // K advances 64 values at a time; rows are gathered 16 bytes per lane
+  if (K1 % 64 != 0 || K2 % 64 != 0) return CSA_ENOTSUP;
+  if (n > 2147483647LL || d_g > 2147483647LL || d > 2147483647LL || g > 65535 || K1 > 2147483647LL ||
+      K2 > 2147483647LL)
+    return CSA_ENOTSUP;
+  if ((int64_t)((n + 255) / 256) * ((d_g + 127) / 128) > 2147483647LL ||
+      (int64_t)((n + 255) / 256) * ((d + 127) / 128) > 2147483647LL)
+    return CSA_ENOTSUP;
+  if (n == 0) return CSA_OK;
+  if (!o || !WG || !WO || !mid || !out) return CSA_EINVAL;
+  if (((uintptr_t)o & 15u) != 0 || ((uintptr_t)WG & 15u) != 0 || ((uintptr_t)WO & 15u) != 0 ||
+      ((uintptr_t)mid & 15u) != 0)
+    return CSA_EINVAL;
+  return launched(csa::launch_grouped_out_proj(o, WG, WO, n, n_h, c, g, d_g, d, mid, out, (hipStream_t)stream));
+}
+
 size_t csa_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
                                  int64_t c, int64_t k, int64_t m, int64_t n_win, int dtype) {
   if (b < 1 || n_q < 1 || m < 1 || t0 < 0 || k < 0 || n_win < 1) return 0;

@@ -42,4 +42,7 @@ hipError_t launch_norm_rope(const void* x, int64_t xrs, void* out, int64_t ors, 
                             int64_t rows, int64_t heads, int64_t c, int64_t rope_dims, double base, int64_t pos0,
                             int64_t pos_step, int dtype, hipStream_t st);
 
+hipError_t launch_grouped_out_proj(const void* o, const void* WG, const void* WO, int64_t n, int64_t n_h, int64_t c,
+                                   int64_t g, int64_t d_g, int64_t d, void* mid, void* out, hipStream_t st);
+
 }  // namespace csa

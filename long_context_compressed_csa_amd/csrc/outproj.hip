@@ -1,0 +1,191 @@
+// Grouped output projection (songhuiming "DeepSeek-V4 百万 token 上下文"
+// section 4.4; AirCoding "deepseek-paper-analysis" section 7.1): the n_h head
+// outputs of a token split into g groups of consecutive heads; group j's
+// concatenated output is projected to d_g values by W^G_j, and the g results,
+// concatenated in group order, are projected to d by W^O.
+//
+// Both projections are one kernel: C[b] (M x N) = A[b] (M x K) B[b]^T, where
+// B[b] is N x K, bf16 operands with K contiguous, float32 accumulation on
+// v_mfma_f32_32x32x16_bf16, bf16 results.  The first projection is a batch
+// of g products (A = the group's columns of the head outputs, B = W^G_j, C =
+// the group's columns of the intermediate), the second a single product.
+//
+// A workgroup (4 waves) computes a 256 x 128 tile of C; wave w owns rows
+// 128*(w/2) .. +127 and columns 64*(w%2) .. +63 as 4 x 2 blocks of 32 x 32,
+// so every 16-byte operand read from LDS feeds 2 (A) or 4 (B) MFMAs.  K
+// advances 64 at a time through a ring of three LDS stages (48 KiB each: 256
+// A rows and 128 B rows of 128 bytes), filled by LDS-DMA two stages ahead
+// (global_load_lds_dwordx4, 8 rows of 128 B per wave instruction).  Chunk c
+// (16 B) of tile row r sits at position c ^ ((r >> 1) & 7) of its row, so the
+// operand reads of 16 consecutive rows at one chunk hit 16 distinct bank
+// groups.  Workgroups are ordered so that each XCD (dispatch index mod 8)
+// gets a contiguous range of tiles, row-block major: tiles sharing A rows
+// share that XCD's L2.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace csa {
+
+constexpr int kGBM = 256, kGBN = 128, kGBK = 64;
+constexpr int kGRowB = kGBK * 2;                   // bytes per tile row
+constexpr int kGStageB = (kGBM + kGBN) * kGRowB;   // 48 KiB
+constexpr int kGDmaPerWave = (kGBM + kGBN) * kGRowB / 1024 / 4;   // 12 gathers per wave and stage
+
+typedef __attribute__((address_space(3))) void glds_void_t;
+
+template <int N>
+__device__ __forceinline__ void gemm_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// barrier that leaves later gathers in flight (a full fence would drain them)
+__device__ __forceinline__ void gemm_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int gemm_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A, int64_t lda, int64_t sa,
+                                                    const bf16_t* __restrict__ B, int64_t ldb, int64_t sb,
+                                                    bf16_t* __restrict__ C, int64_t ldc, int64_t sc, int M, int N,
+                                                    int K, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) unsigned char S0[kGStageB];
+  __shared__ __attribute__((aligned(16))) unsigned char S1[kGStageB];
+  __shared__ __attribute__((aligned(16))) unsigned char S2[kGStageB];
+  const int T = tiles_m * tiles_n;
+  const int L = blockIdx.x;
+  const int t = (T & 7) == 0 ? (L & 7) * (T >> 3) + (L >> 3) : L;
+  const int m0 = (t / tiles_n) * kGBM, n0 = (t % tiles_n) * kGBN;
+  const int64_t bz = blockIdx.y;
+  A += bz * sa;
+  B += bz * sb;
+  C += bz * sc;
+  const int l = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk = K / kGBK;
+
+  // gather stage kt: instruction `ins` fills tile rows 8*ins .. 8*ins+7, lane l
+  // row 8*ins + l/8 at position l%8, i.e. the row's chunk (l%8) ^ f(row)
+  const int lrow = l >> 3, lpos = l & 7;
+  auto issue = [&](int kt, unsigned char* buf) {
+    const int k0 = kt * kGBK;
+#pragma unroll
+    for (int i = 0; i < kGBM / 32; ++i) {
+      const int ins = wave + 4 * i;
+      const int r = ins * 8 + lrow;
+      const int gr = m0 + r < M ? m0 + r : M - 1;
+      const bf16_t* p = A + (int64_t)gr * lda + k0 + 8 * gemm_pos(r, lpos);
+      __builtin_amdgcn_global_load_lds((const void*)p, (glds_void_t*)(buf + ins * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kGBN / 32; ++i) {
+      const int ins = wave + 4 * i;
+      const int r = ins * 8 + lrow;
+      const int gr = n0 + r < N ? n0 + r : N - 1;
+      const bf16_t* p = B + (int64_t)gr * ldb + k0 + 8 * gemm_pos(r, lpos);
+      __builtin_amdgcn_global_load_lds((const void*)p, (glds_void_t*)(buf + kGBM * kGRowB + ins * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = (f32x16){};
+
+  // 64 values of K from one stage, in 4 steps of 16: lane l reads row l%32 of
+  // each block at chunk 2*ks + l/32 (K values 16 ks + 8 (l/32) .. +7).  The
+  // operands of step ks+1 are read while step ks multiplies (two register
+  // sets); scheduling fences keep that order, which the scheduler would
+  // otherwise replace by all 24 reads up front and run out of registers.
+  auto compute = [&](const unsigned char* buf) {
+    bf16x8 a[2][4], b[2][2];
+    auto read = [&](int ks, bf16x8 (&av)[4], bf16x8 (&bv)[2]) {
+      const int ch = 2 * ks + (l >> 5);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int r = wm * 128 + 32 * mi + (l & 31);
+        av[mi] = *reinterpret_cast<const bf16x8*>(buf + r * kGRowB + 16 * gemm_pos(r, ch));
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int r = wn * 64 + 32 * ni + (l & 31);
+        bv[ni] = *reinterpret_cast<const bf16x8*>(buf + kGBM * kGRowB + r * kGRowB + 16 * gemm_pos(r, ch));
+      }
+    };
+    read(0, a[0], b[0]);
+#pragma unroll
+    for (int ks = 0; ks < kGBK / 16; ++ks) {
+      if (ks + 1 < kGBK / 16) read(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][mi], b[ks & 1][ni], acc[mi][ni], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // step 0 reads
+#pragma unroll
+    for (int ks = 0; ks < kGBK / 16 - 1; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // reads of step ks+1
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // MFMAs of step ks
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+  // one K step: stage kt is in `cur` (its gathers waited for here); stage
+  // kt + 2 goes to `ahead`, whose previous stage (kt - 1) every wave has
+  // finished once past the barrier
+  auto step = [&](int kt, const unsigned char* cur, unsigned char* ahead) {
+    if (kt + 1 < nk) gemm_wait_vm<kGDmaPerWave>();
+    else gemm_wait_vm<0>();
+    gemm_barrier();
+    if (kt + 2 < nk) issue(kt + 2, ahead);
+    compute(cur);
+  };
+
+  issue(0, S0);
+  if (nk > 1) issue(1, S1);
+  // whole rounds of the three stages, then at most two more steps; a loop
+  // with early exits makes the register allocator move all 128 accumulators
+  // at every exit
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    step(kt, S0, S2);
+    step(kt + 1, S1, S0);
+    step(kt + 2, S2, S1);
+  }
+  if (kt < nk) step(kt, S0, S2);
+  if (kt + 1 < nk) step(kt + 1, S1, S0);
+
+  // D layout of the 32 x 32 MFMA: register r of lane l is row
+  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int col = n0 + wn * 64 + 32 * ni + (l & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 128 + 32 * mi + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        if (row < M && col < N) C[(int64_t)row * ldc + col] = f2bf(acc[mi][ni][r]);
+      }
+    }
+}
+
+static hipError_t launch_gemm_nt(const bf16_t* A, int64_t lda, int64_t sa, const bf16_t* B, int64_t ldb,
+                                 int64_t sb, bf16_t* C, int64_t ldc, int64_t sc, int64_t M, int64_t N, int64_t K,
+                                 int64_t batch, hipStream_t st) {
+  const int tm = (int)((M + kGBM - 1) / kGBM), tn = (int)((N + kGBN - 1) / kGBN);
+  hipLaunchKernelGGL(gemm_nt_bf16, dim3((unsigned)(tm * tn), (unsigned)batch), dim3(256), 0, st, A, lda, sa, B, ldb,
+                     sb, C, ldc, sc, (int)M, (int)N, (int)K, tm, tn);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_out_proj(const void* o, const void* WG, const void* WO, int64_t n, int64_t n_h, int64_t c,
+                                   int64_t g, int64_t d_g, int64_t d, void* mid, void* out, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t K1 = (n_h / g) * c, K2 = g * d_g;
+  hipError_t e = launch_gemm_nt((const bf16_t*)o, n_h * c, K1, (const bf16_t*)WG, K1, d_g * K1, (bf16_t*)mid, K2,
+                                d_g, n, d_g, K1, g, st);
+  if (e != hipSuccess) return e;
+  return launch_gemm_nt((const bf16_t*)mid, K2, 0, (const bf16_t*)WO, K2, 0, (bf16_t*)out, d, 0, n, d, K2, 1, st);
+}
+
+}  // namespace csa

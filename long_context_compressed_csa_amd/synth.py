@@ -206,6 +206,16 @@ def norm_rope_inputs(rows, heads, c, dtype=torch.bfloat16, seed=0, device="cpu",
     return x, gamma
 
 
+def out_proj_inputs(n, n_h, c, g, d_g, d, seed=0, device="cpu", dtype=torch.bfloat16):
+    """Grouped output projection: head outputs o [n, n_h, c] ~ N(0,1) and
+    weights WG [g, d_g, (n_h/g) c], WO [d, g d_g], each N(0,1) / sqrt(fan-in)."""
+    gen = _gen(seed, device)
+    o = normal((n, n_h, c), gen, 1.0, dtype, device)
+    WG = scaled((g, d_g, (n_h // g) * c), gen, dtype, device)
+    WO = scaled((d, g * d_g), gen, dtype, device)
+    return o, WG, WO
+
+
 def hca_inputs(n=None, seed=None, device="cpu", n_h=None, m_prime=None):
     """HCA prefill layer; q is the big tensor ([n, n_h, c])."""
     p = dict(HCA)

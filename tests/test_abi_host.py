@@ -176,6 +176,27 @@ def test_norm_rope_rejects_bad_arguments(lib):
     assert _nr(lib, c=1024, xrs=2048, ors=2048, rd=514) == ENOTSUP   # at most 256 rotation pairs
 
 
+def _gop(lib, **kw):
+    a = dict(o=0x100000, WG=0x200000, WO=0x300000, n=300, n_h=8, c=64, g=2, d_g=128, d=320, dtype=1,
+             mid=0x400000, out=0x500000)
+    a.update(kw)
+    return lib.csa_grouped_out_proj(a["o"], a["WG"], a["WO"], a["n"], a["n_h"], a["c"], a["g"], a["d_g"], a["d"],
+                                    a["dtype"], a["mid"], a["out"], None)
+
+
+def test_grouped_out_proj_rejects_bad_arguments(lib):
+    assert _gop(lib, n=0) == 0                       # nothing to do
+    assert _gop(lib, n=-1) == EINVAL
+    assert _gop(lib, g=3) == EINVAL                  # heads do not split into 3 groups
+    assert _gop(lib, d=0) == EINVAL
+    assert _gop(lib, o=None) == EINVAL
+    assert _gop(lib, mid=None) == EINVAL
+    assert _gop(lib, WG=0x200008) == EINVAL          # 16-byte gathers
+    assert _gop(lib, dtype=0) == ENOTSUP             # bf16 only
+    assert _gop(lib, c=40) == ENOTSUP                # (n_h/g) c = 160: not a multiple of 64
+    assert _gop(lib, d_g=100) == ENOTSUP             # g d_g = 200
+
+
 def test_index_topk_workspace_size_grows_with_candidates(lib):
     small = lib.csa_index_topk_workspace_size(1, 4, 100, 8)
     big = lib.csa_index_topk_workspace_size(1, 4, 100000, 8)

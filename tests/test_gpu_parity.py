@@ -1210,3 +1210,41 @@ def test_csa_layer_with_norm_and_rope_bf16():
     excess = np.abs(got[..., lo:] - want[..., lo:]) - bound
     i = np.unravel_index(int(np.argmax(excess)), excess.shape)
     assert excess[i] <= 0, ("rotated dims", i, got[..., lo:][i], want[..., lo:][i], bound[i])
+
+
+# ------------------------------------------------ grouped output projection --
+
+def _check_out_proj(o, WG, WO, what):
+    g = WG.shape[0]
+    mid, out = L.csa_grouped_out_proj(g_(o), g_(WG), g_(WO))
+    torch.cuda.synchronize()
+    want_mid, _ = O.grouped_out_proj(to64(o), to64(WG), to64(WO), g)
+    assert_close(mid, want_mid, torch.bfloat16, f"{what}: intermediate")
+    # the intermediate is stored in bf16 between the two products: the
+    # reference rounds the oracle's at the same point
+    st = lambda a: to64(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+    _, want = O.grouped_out_proj(to64(o), to64(WG), to64(WO), g, mid_round=st)
+    assert_close(out, want, torch.bfloat16, f"{what}: output")
+
+
+g_ = g
+
+
+@pytest.mark.parametrize("n,n_h,c,g,d_g,d", [
+    (37, 8, 64, 2, 192, 320),      # ragged rows and columns, 4 and 6 K stages
+    (5, 2, 32, 1, 128, 64),        # one and two K stages
+    (600, 4, 160, 2, 64, 200),     # three row tiles, 5 and 2 K stages
+])
+def test_grouped_out_proj(n, n_h, c, g, d_g, d):
+    say(f"grouped out proj n={n} n_h={n_h} c={c} g={g} d_g={d_g} d={d}")
+    o, WG, WO = synth.out_proj_inputs(n, n_h, c, g, d_g, d, seed=n + d)
+    _check_out_proj(o, WG, WO, "small")
+
+
+def test_grouped_out_proj_flash_shape():
+    # the Flash shape (g = 8, d_g = 1024, d = 4096 for 64 heads of 512) over
+    # 300 tokens: 64 and 128 K stages, two row tiles
+    n = 300
+    say(f"grouped out proj Flash shape n={n}")
+    o, WG, WO = synth.out_proj_inputs(n, 64, 512, 8, 1024, 4096, seed=61)
+    _check_out_proj(o, WG, WO, "flash")
