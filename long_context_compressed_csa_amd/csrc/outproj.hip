@@ -31,7 +31,18 @@ constexpr int kGRowB = kGBK * 2;                   // bytes per tile row
 constexpr int kGStageB = (kGBM + kGBN) * kGRowB;   // 48 KiB
 constexpr int kGDmaPerWave = (kGBM + kGBN) * kGRowB / 1024 / 4;   // 12 gathers per wave and stage
 
-typedef __attribute__((address_space(3))) void glds_void_t;
+// LDS-DMA of 16 bytes per lane (lane l to LDS address lds + 16 l) issued as
+// inline assembly: the compiler then does not treat the pending LDS writes as
+// aliasing the operand reads and inserts no wait of its own (with the builtin
+// it drains every gather at the top of the K loop); the waits are explicit
+// (gemm_wait_vm before the barrier of each step).  M0 is restored
+// afterwards, since the compiler does not accept it as a clobber.  No
+// register results: nothing is left for a later instruction to overwrite.
+__device__ __forceinline__ void gemm_dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
+}
 
 template <int N>
 __device__ __forceinline__ void gemm_wait_vm() {
@@ -73,7 +84,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A
       const int r = ins * 8 + lrow;
       const int gr = m0 + r < M ? m0 + r : M - 1;
       const bf16_t* p = A + (int64_t)gr * lda + k0 + 8 * gemm_pos(r, lpos);
-      __builtin_amdgcn_global_load_lds((const void*)p, (glds_void_t*)(buf + ins * 1024), 16, 0, 0);
+      gemm_dma16(p, (uint32_t)(uintptr_t)buf + ins * 1024);
     }
 #pragma unroll
     for (int i = 0; i < kGBN / 32; ++i) {
@@ -81,7 +92,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A
       const int r = ins * 8 + lrow;
       const int gr = n0 + r < N ? n0 + r : N - 1;
       const bf16_t* p = B + (int64_t)gr * ldb + k0 + 8 * gemm_pos(r, lpos);
-      __builtin_amdgcn_global_load_lds((const void*)p, (glds_void_t*)(buf + kGBM * kGRowB + ins * 1024), 16, 0, 0);
+      gemm_dma16(p, (uint32_t)(uintptr_t)buf + kGBM * kGRowB + ins * 1024);
     }
   };
 
