@@ -28,8 +28,11 @@ namespace csa {
 
 constexpr int kGBM = 256, kGBN = 128, kGBK = 64;
 constexpr int kGRowB = kGBK * 2;                   // bytes per tile row
+constexpr int kGCPR = kGBK / 8;                    // 16-byte chunks per tile row
+constexpr int kGRPI = 1024 / kGRowB;               // tile rows per gather instruction
+constexpr int kGSwzShift = kGCPR == 8 ? 1 : 2;     // rows sharing one chunk permutation: 2 or 4
 constexpr int kGStageB = (kGBM + kGBN) * kGRowB;   // 48 KiB
-constexpr int kGDmaPerWave = (kGBM + kGBN) * kGRowB / 1024 / 4;   // 12 gathers per wave and stage
+constexpr int kGDmaPerWave = (kGBM + kGBN) / kGRPI / 4;   // gathers per wave and stage
 
 // LDS-DMA of 16 bytes per lane (lane l to LDS address lds + 16 l) issued as
 // inline assembly: the compiler then does not treat the pending LDS writes as
@@ -51,7 +54,7 @@ __device__ __forceinline__ void gemm_wait_vm() {
 // barrier that leaves later gathers in flight (a full fence would drain them)
 __device__ __forceinline__ void gemm_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ int gemm_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int gemm_pos(int r, int c) { return c ^ ((r >> kGSwzShift) & (kGCPR - 1)); }
 
 __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A, int64_t lda, int64_t sa,
                                                     const bf16_t* __restrict__ B, int64_t ldb, int64_t sb,
@@ -75,21 +78,21 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A
 
   // gather stage kt: instruction `ins` fills tile rows 8*ins .. 8*ins+7, lane l
   // row 8*ins + l/8 at position l%8, i.e. the row's chunk (l%8) ^ f(row)
-  const int lrow = l >> 3, lpos = l & 7;
+  const int lrow = l / kGCPR, lpos = l % kGCPR;
   auto issue = [&](int kt, unsigned char* buf) {
     const int k0 = kt * kGBK;
 #pragma unroll
-    for (int i = 0; i < kGBM / 32; ++i) {
+    for (int i = 0; i < kGBM / kGRPI / 4; ++i) {
       const int ins = wave + 4 * i;
-      const int r = ins * 8 + lrow;
+      const int r = ins * kGRPI + lrow;
       const int gr = m0 + r < M ? m0 + r : M - 1;
       const bf16_t* p = A + (int64_t)gr * lda + k0 + 8 * gemm_pos(r, lpos);
       gemm_dma16(p, (uint32_t)(uintptr_t)buf + ins * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < kGBN / 32; ++i) {
+    for (int i = 0; i < kGBN / kGRPI / 4; ++i) {
       const int ins = wave + 4 * i;
-      const int r = ins * 8 + lrow;
+      const int r = ins * kGRPI + lrow;
       const int gr = n0 + r < N ? n0 + r : N - 1;
       const bf16_t* p = B + (int64_t)gr * ldb + k0 + 8 * gemm_pos(r, lpos);
       gemm_dma16(p, (uint32_t)(uintptr_t)buf + kGBM * kGRowB + ins * 1024);
