@@ -1248,3 +1248,31 @@ def test_grouped_out_proj_flash_shape():
     say(f"grouped out proj Flash shape n={n}")
     o, WG, WO = synth.out_proj_inputs(n, 64, 512, 8, 1024, 4096, seed=61)
     _check_out_proj(o, WG, WO, "flash")
+
+
+def test_hca_layer_with_norm_and_rope_fp32():
+    # HCA with normalised, rotated queries and entries (entry s at m' * s)
+    # and the output turned back by -t: the oracle's composed definition with
+    # every visible entry selected
+    n, mp, nh, nw = 200, 16, 64, 40
+    say(f"hca layer with norm and rope, float32 n={n} m'={mp} n_h={nh} n_win={nw}")
+    d = synth.hca_inputs(n=n, seed=52, n_h=nh, m_prime=mp)
+    d = {k2: (v.float() if isinstance(v, torch.Tensor) and v.dtype == torch.bfloat16 else v) for k2, v in d.items()}
+    _, gq = synth.norm_rope_inputs(1, 1, 512, seed=53)
+    _, gk = synth.norm_rope_inputs(1, 1, 512, seed=54)
+    Cc = torch.tensor(O.compress_pool(to64(d["C"]), to64(d["Z"]), to64(d["B"]), mp), dtype=torch.float32)
+    eps, rd, base = 1e-6, 64, 10000.0
+    qn = L.csa_norm_rope(g(d["q"]), g(gq), eps, rd, base, 0, 1)
+    Cn = L.csa_norm_rope(g(Cc), g(gk), eps, rd, base, 0, mp)
+    Rn = L.csa_norm_rope(g(d["kv_raw"]), g(gk), eps, rd, base, 0, 1)
+    o = L.hca_attend(qn[None], Cn[None], Rn[None], g(d["sink"]), 0, mp, nw, d["scale"])[0]
+    L.csa_norm_rope(o, None, 0.0, rd, base, 0, -1, out=o)
+    torch.cuda.synchronize()
+    t = np.arange(n)
+    vis = [O.visible_entries(int(x), mp) for x in t]
+    idx = np.full((n, max(vis)), -1)
+    for r, v in enumerate(vis):
+        idx[r, :v] = np.arange(v)
+    want = O.csa_attend_rope(to64(d["q"]), to64(Cc), idx, to64(d["kv_raw"]), 0, to64(d["sink"]), t, nw,
+                             d["scale"], mp, to64(gq), to64(gk), eps, rd, base)
+    assert_close(o, want, torch.float32, "hca layer with norm and rope, float32")
