@@ -10,13 +10,15 @@
 // of g products (A = the group's columns of the head outputs, B = W^G_j, C =
 // the group's columns of the intermediate), the second a single product.
 //
-// A workgroup (4 waves) computes a 256 x 128 tile of C; wave w owns rows
-// 128*(w/2) .. +127 and columns 64*(w%2) .. +63 as 4 x 2 blocks of 32 x 32,
-// so every 16-byte operand read from LDS feeds 2 (A) or 4 (B) MFMAs.  K
-// advances 64 at a time through a ring of three LDS stages (48 KiB each: 256
-// A rows and 128 B rows of 128 bytes), filled by LDS-DMA two stages ahead
-// (global_load_lds_dwordx4, 8 rows of 128 B per wave instruction).  Chunk c
-// (16 B) of tile row r sits at position c ^ ((r >> 1) & 7) of its row, so the
+// A workgroup (4 waves) computes a 256 x 256 tile of C; wave w owns rows
+// 128*(w/2) .. +127 and columns 128*(w%2) .. +127 as 4 x 4 blocks of 32 x 32
+// (256 accumulators, in the accumulation registers), so every 16-byte
+// operand read from LDS feeds four MFMAs: the LDS port, shared by the
+// gathers and the operand reads, stays below the MFMA rate.  K advances 32
+// at a time through a ring of four LDS stages (32 KiB each: 256 A rows and
+// 256 B rows of 64 bytes), filled by LDS-DMA three stages ahead
+// (global_load_lds_dwordx4, 16 rows of 64 B per wave instruction).  Chunk c
+// (16 B) of tile row r sits at position c ^ ((r >> 2) & 3) of its row, so the
 // operand reads of 16 consecutive rows at one chunk hit 16 distinct bank
 // groups.  Workgroups are ordered so that each XCD (dispatch index mod 8)
 // gets a contiguous range of tiles, row-block major: tiles sharing A rows
@@ -26,13 +28,13 @@
 
 namespace csa {
 
-constexpr int kGBM = 256, kGBN = 128, kGBK = 64;
+constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
 constexpr int kGRowB = kGBK * 2;                   // bytes per tile row
 constexpr int kGCPR = kGBK / 8;                    // 16-byte chunks per tile row
 constexpr int kGRPI = 1024 / kGRowB;               // tile rows per gather instruction
 constexpr int kGSwzShift = kGCPR == 8 ? 1 : 2;     // rows sharing one chunk permutation: 2 or 4
-constexpr int kGStageB = (kGBM + kGBN) * kGRowB;   // 48 KiB
-constexpr int kGDmaPerWave = (kGBM + kGBN) / kGRPI / 4;   // gathers per wave and stage
+constexpr int kGStageB = (kGBM + kGBN) * kGRowB;   // 32 KiB
+constexpr int kGDmaPerWave = (kGBM + kGBN) / kGRPI / 4;   // gathers per wave and stage (8)
 
 // LDS-DMA of 16 bytes per lane (lane l to LDS address lds + 16 l) issued as
 // inline assembly: the compiler then does not treat the pending LDS writes as
@@ -46,7 +48,6 @@ __device__ __forceinline__ void gemm_dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
 }
-
 template <int N>
 __device__ __forceinline__ void gemm_wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -56,6 +57,16 @@ __device__ __forceinline__ void gemm_barrier() { asm volatile("s_waitcnt lgkmcnt
 
 __device__ __forceinline__ int gemm_pos(int r, int c) { return c ^ ((r >> kGSwzShift) & (kGCPR - 1)); }
 
+// acc += a b on the 32x32x16 bf16 MFMA with acc pinned to accumulation
+// registers: the 256 accumulators of a wave fill them exactly.  The compiler
+// sees only an asm statement, so where compiled code touches acc next to
+// these instructions (zeroing before the first, reading after the last) the
+// kernel pads with gemm_acc_pad.
+__device__ __forceinline__ void gemm_mfma(f32x16& acc, const bf16x8 a, const bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void gemm_acc_pad() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A, int64_t lda, int64_t sa,
                                                     const bf16_t* __restrict__ B, int64_t ldb, int64_t sb,
                                                     bf16_t* __restrict__ C, int64_t ldc, int64_t sc, int M, int N,
@@ -63,6 +74,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A
   __shared__ __attribute__((aligned(16))) unsigned char S0[kGStageB];
   __shared__ __attribute__((aligned(16))) unsigned char S1[kGStageB];
   __shared__ __attribute__((aligned(16))) unsigned char S2[kGStageB];
+  __shared__ __attribute__((aligned(16))) unsigned char S3[kGStageB];
   const int T = tiles_m * tiles_n;
   const int L = blockIdx.x;
   const int t = (T & 7) == 0 ? (L & 7) * (T >> 3) + (L >> 3) : L;
@@ -76,8 +88,9 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = K / kGBK;
 
-  // gather stage kt: instruction `ins` fills tile rows 8*ins .. 8*ins+7, lane l
-  // row 8*ins + l/8 at position l%8, i.e. the row's chunk (l%8) ^ f(row)
+  // gather stage kt: instruction `ins` fills tile rows kGRPI*ins .. +kGRPI-1,
+  // lane l row kGRPI*ins + l/kGCPR at position l%kGCPR, i.e. the row's chunk
+  // (l%kGCPR) ^ f(row)
   const int lrow = l / kGCPR, lpos = l % kGCPR;
   auto issue = [&](int kt, unsigned char* buf) {
     const int k0 = kt * kGBK;
@@ -99,82 +112,75 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = (f32x16){};
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = (f32x16){};
+  gemm_acc_pad();
 
-  // 64 values of K from one stage, in 4 steps of 16: lane l reads row l%32 of
-  // each block at chunk 2*ks + l/32 (K values 16 ks + 8 (l/32) .. +7).  The
-  // operands of step ks+1 are read while step ks multiplies (two register
-  // sets); scheduling fences keep that order, which the scheduler would
-  // otherwise replace by all 24 reads up front and run out of registers.
+  // 32 values of K from one stage, in 2 steps of 16: lane l reads row l%32
+  // of each block at chunk 2*ks + l/32 (K values 16 ks + 8 (l/32) .. +7);
+  // the wave owns rows 128 wm .. +127 and columns 128 wn .. +127 as 4 x 4
+  // blocks, so each operand read feeds four MFMAs.  The second step's
+  // operands are read before the first step's MFMAs.
   auto compute = [&](const unsigned char* buf) {
-    bf16x8 a[2][4], b[2][2];
-    auto read = [&](int ks, bf16x8 (&av)[4], bf16x8 (&bv)[2]) {
+    bf16x8 a[2][4], b[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
       const int ch = 2 * ks + (l >> 5);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int r = wm * 128 + 32 * mi + (l & 31);
-        av[mi] = *reinterpret_cast<const bf16x8*>(buf + r * kGRowB + 16 * gemm_pos(r, ch));
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 128 + 32 * i + (l & 31);
+        a[ks][i] = *reinterpret_cast<const bf16x8*>(buf + ra * kGRowB + 16 * gemm_pos(ra, ch));
+        const int rb = wn * 128 + 32 * i + (l & 31);
+        b[ks][i] = *reinterpret_cast<const bf16x8*>(buf + kGBM * kGRowB + rb * kGRowB + 16 * gemm_pos(rb, ch));
       }
+    }
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int r = wn * 64 + 32 * ni + (l & 31);
-        bv[ni] = *reinterpret_cast<const bf16x8*>(buf + kGBM * kGRowB + r * kGRowB + 16 * gemm_pos(r, ch));
-      }
-    };
-    read(0, a[0], b[0]);
-#pragma unroll
-    for (int ks = 0; ks < kGBK / 16; ++ks) {
-      if (ks + 1 < kGBK / 16) read(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][mi], b[ks & 1][ni], acc[mi][ni], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // step 0 reads
-#pragma unroll
-    for (int ks = 0; ks < kGBK / 16 - 1; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // reads of step ks+1
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // MFMAs of step ks
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        for (int ni = 0; ni < 4; ++ni) gemm_mfma(acc[mi][ni], a[ks][mi], b[ks][ni]);
   };
-  // one K step: stage kt is in `cur` (its gathers waited for here); stage
-  // kt + 2 goes to `ahead`, whose previous stage (kt - 1) every wave has
-  // finished once past the barrier
+  // one K step: stage kt is in `cur` (its gathers waited for here: the
+  // gathers of the up to two later stages may stay in flight); stage kt + 3
+  // goes to `ahead`, whose previous stage (kt - 1) every wave has finished
+  // once past the barrier
   auto step = [&](int kt, const unsigned char* cur, unsigned char* ahead) {
-    if (kt + 1 < nk) gemm_wait_vm<kGDmaPerWave>();
+    if (kt + 2 < nk) gemm_wait_vm<2 * kGDmaPerWave>();
+    else if (kt + 1 < nk) gemm_wait_vm<kGDmaPerWave>();
     else gemm_wait_vm<0>();
     gemm_barrier();
-    if (kt + 2 < nk) issue(kt + 2, ahead);
+    if (kt + 3 < nk) issue(kt + 3, ahead);
     compute(cur);
   };
 
   issue(0, S0);
   if (nk > 1) issue(1, S1);
-  // whole rounds of the three stages, then at most two more steps; a loop
-  // with early exits makes the register allocator move all 128 accumulators
-  // at every exit
+  if (nk > 2) issue(2, S2);
+  // whole rounds of the four stages, then at most three more steps (a loop
+  // with early exits costs moves of the accumulators at every exit)
   int kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {
-    step(kt, S0, S2);
+  for (; kt + 4 <= nk; kt += 4) {
+    step(kt, S0, S3);
     step(kt + 1, S1, S0);
     step(kt + 2, S2, S1);
+    step(kt + 3, S3, S2);
   }
-  if (kt < nk) step(kt, S0, S2);
+  if (kt < nk) step(kt, S0, S3);
   if (kt + 1 < nk) step(kt + 1, S1, S0);
+  if (kt + 2 < nk) step(kt + 2, S2, S1);
+  gemm_acc_pad();
 
   // D layout of the 32 x 32 MFMA: register r of lane l is row
   // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int col = n0 + wn * 64 + 32 * ni + (l & 31);
+    for (int ni = 0; ni < 4; ++ni) {
+      const int col = n0 + wn * 128 + 32 * ni + (l & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * 128 + 32 * mi + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
