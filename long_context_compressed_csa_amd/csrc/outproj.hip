@@ -17,7 +17,9 @@
 // gathers and the operand reads, stays below the MFMA rate.  K advances 32
 // at a time through a ring of four LDS stages (32 KiB each: 256 A rows and
 // 256 B rows of 64 bytes), filled by LDS-DMA three stages ahead
-// (global_load_lds_dwordx4, 16 rows of 64 B per wave instruction).  Chunk c
+// (global_load_lds_dwordx4, 16 rows of 64 B per wave instruction); each
+// step's barrier also covers the next stage, whose operands are read into a
+// second register set while the current stage's MFMAs run.  Chunk c
 // (16 B) of tile row r sits at position c ^ ((r >> 2) & 3) of its row, so the
 // operand reads of 16 consecutive rows at one chunk hit 16 distinct bank
 // groups.  Workgroups are ordered so that each XCD (dispatch index mod 8)
@@ -122,56 +124,65 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A
   // 32 values of K from one stage, in 2 steps of 16: lane l reads row l%32
   // of each block at chunk 2*ks + l/32 (K values 16 ks + 8 (l/32) .. +7);
   // the wave owns rows 128 wm .. +127 and columns 128 wn .. +127 as 4 x 4
-  // blocks, so each operand read feeds four MFMAs.  The second step's
-  // operands are read before the first step's MFMAs.
-  auto compute = [&](const unsigned char* buf) {
-    bf16x8 a[2][4], b[2][4];
+  // blocks, so each operand read feeds four MFMAs.
+  auto read_stage = [&](const unsigned char* buf, bf16x8 (&av)[2][4], bf16x8 (&bv)[2][4]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int ch = 2 * ks + (l >> 5);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ra = wm * 128 + 32 * i + (l & 31);
-        a[ks][i] = *reinterpret_cast<const bf16x8*>(buf + ra * kGRowB + 16 * gemm_pos(ra, ch));
+        av[ks][i] = *reinterpret_cast<const bf16x8*>(buf + ra * kGRowB + 16 * gemm_pos(ra, ch));
         const int rb = wn * 128 + 32 * i + (l & 31);
-        b[ks][i] = *reinterpret_cast<const bf16x8*>(buf + kGBM * kGRowB + rb * kGRowB + 16 * gemm_pos(rb, ch));
+        bv[ks][i] = *reinterpret_cast<const bf16x8*>(buf + kGBM * kGRowB + rb * kGRowB + 16 * gemm_pos(rb, ch));
       }
     }
+  };
+  auto mma = [&](const bf16x8 (&av)[2][4], const bf16x8 (&bv)[2][4]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) gemm_mfma(acc[mi][ni], a[ks][mi], b[ks][ni]);
+        for (int ni = 0; ni < 4; ++ni) gemm_mfma(acc[mi][ni], av[ks][mi], bv[ks][ni]);
   };
-  // one K step: stage kt is in `cur` (its gathers waited for here: the
-  // gathers of the up to two later stages may stay in flight); stage kt + 3
-  // goes to `ahead`, whose previous stage (kt - 1) every wave has finished
-  // once past the barrier
-  auto step = [&](int kt, const unsigned char* cur, unsigned char* ahead) {
-    if (kt + 2 < nk) gemm_wait_vm<2 * kGDmaPerWave>();
-    else if (kt + 1 < nk) gemm_wait_vm<kGDmaPerWave>();
+  // One K step.  The operands of stage kt are already in registers (pa, pb);
+  // past the barrier stages kt and kt + 1 have landed (each wave waited for
+  // its own gathers up to kt + 1; kt + 2 may still be in flight), so the wave
+  // reads stage kt + 1's operands into (qa, qb) while stage kt's MFMAs run.
+  // Stage kt + 3 goes to `ahead`, the buffer of stage kt - 1, whose operands
+  // every wave read during step kt - 2.
+  auto step = [&](int kt, const unsigned char* nxt, unsigned char* ahead, const bf16x8 (&pa)[2][4],
+                  const bf16x8 (&pb)[2][4], bf16x8 (&qa)[2][4], bf16x8 (&qb)[2][4]) {
+    if (kt + 2 < nk) gemm_wait_vm<kGDmaPerWave>();
     else gemm_wait_vm<0>();
     gemm_barrier();
     if (kt + 3 < nk) issue(kt + 3, ahead);
-    compute(cur);
+    if (kt + 1 < nk) read_stage(nxt, qa, qb);
+    mma(pa, pb);
   };
 
+  bf16x8 xa[2][4], xb[2][4], ya[2][4], yb[2][4];
   issue(0, S0);
   if (nk > 1) issue(1, S1);
   if (nk > 2) issue(2, S2);
+  if (nk > 2) gemm_wait_vm<2 * kGDmaPerWave>();
+  else if (nk > 1) gemm_wait_vm<kGDmaPerWave>();
+  else gemm_wait_vm<0>();
+  gemm_barrier();
+  read_stage(S0, xa, xb);
   // whole rounds of the four stages, then at most three more steps (a loop
   // with early exits costs moves of the accumulators at every exit)
   int kt = 0;
   for (; kt + 4 <= nk; kt += 4) {
-    step(kt, S0, S3);
-    step(kt + 1, S1, S0);
-    step(kt + 2, S2, S1);
-    step(kt + 3, S3, S2);
+    step(kt, S1, S3, xa, xb, ya, yb);
+    step(kt + 1, S2, S0, ya, yb, xa, xb);
+    step(kt + 2, S3, S1, xa, xb, ya, yb);
+    step(kt + 3, S0, S2, ya, yb, xa, xb);
   }
-  if (kt < nk) step(kt, S0, S3);
-  if (kt + 1 < nk) step(kt + 1, S1, S0);
-  if (kt + 2 < nk) step(kt + 2, S2, S1);
+  if (kt < nk) step(kt, S1, S3, xa, xb, ya, yb);
+  if (kt + 1 < nk) step(kt + 1, S2, S0, ya, yb, xa, xb);
+  if (kt + 2 < nk) step(kt + 2, S3, S1, xa, xb, ya, yb);
   gemm_acc_pad();
 
   // D layout of the 32 x 32 MFMA: register r of lane l is row
