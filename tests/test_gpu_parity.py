@@ -1011,7 +1011,9 @@ def test_decode_one_million_context_sampled():
 def test_graph_replay_matches_eager():
     # The library allocates nothing and records no memset, so whole layer
     # steps can be captured in a HIP graph: a prefill-shaped step (both
-    # compressors, scoring with fused selection, attention) and a
+    # compressors, scoring with fused selection, attention, query norm and
+    # rotation, the output's in-place back-rotation, the grouped output
+    # projection) and a
     # decode-shaped step (streaming scorer, threshold top-k, split attention)
     # are replayed three times, with eager work between the replays, and every
     # replay must reproduce the eager results bit for bit.
@@ -1044,13 +1046,21 @@ def test_graph_replay_matches_eager():
     dwsI = torch.empty(max(lib.csa_index_topk_workspace_size(b, 1, nd, kd), 256), dtype=torch.uint8, device=DEV)
     dwsA = torch.empty(max(lib.csa_attend_workspace_size(b, 1, td, nd, 64, c, kd, m, nw, 1), 256),
                        dtype=torch.uint8, device=DEV)
-    outs = (Cc, KI, idx, out, didx, dout)
+    _, gq = synth.norm_rope_inputs(1, 1, c, seed=71, device=DEV)
+    _, WG, WO = synth.out_proj_inputs(1, 64, c, 8, 256, 512, seed=72, device=DEV)
+    qn = torch.empty_like(p["q"])
+    mid = torch.empty((n, 8 * 256), dtype=torch.bfloat16, device=DEV)
+    proj = torch.empty((n, 512), dtype=torch.bfloat16, device=DEV)
+    outs = (Cc, KI, idx, out, didx, dout, qn, mid, proj)
 
     def body(s):
         L.csa_compress(*(p[x] for x in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m, out=Cc, stream=s)
         L.csa_compress(*(p[x] for x in ("ICa", "ICb", "IZa", "IZb", "IBa", "IBb")), m, out=KI, stream=s)
         L.csa_index_topk(p["qI"], p["w"], KI, 0, m, k, idx=idx, workspace=wsI, stream=s)
         L.csa_attend(p["q"], Cc, idx, p["kv_raw"], p["sink"], 0, m, nw, out=out, workspace=wsA, stream=s)
+        L.csa_norm_rope(p["q"], gq, 1e-6, 64, 10000.0, 0, 1, out=qn, stream=s)
+        L.csa_norm_rope(out[0], None, 0.0, 64, 10000.0, 0, -1, out=out[0], stream=s)
+        L.csa_grouped_out_proj(out[0], WG, WO, mid=mid, out=proj, stream=s)
         L.csa_index_topk(dqI, dw, dKI, td, m, kd, idx=didx, workspace=dwsI, stream=s)
         L.csa_attend(dq, dCc, didx, dwin, dsink, td, m, nw, raw_pos0=td - nw + 1, out=dout, workspace=dwsA,
                      stream=s)
