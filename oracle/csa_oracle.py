@@ -86,29 +86,28 @@ def visible_entries(t: int, m: int) -> int:
     return (t + 1) // m
 
 
-def read_counts(history: int, m: int, m_prime: int, k: int, n_win: int) -> dict:
-    """Entries stored and read by one query, by layer type.
+@dataclass(frozen=True)
+class LayerReads:
+    """What one query of one compressed layer stores and reads."""
+    stored: int   # completed compressed entries
+    tail: int     # processed tokens still waiting in the open block
+    reads: int    # entries in the main attention's softmax (window included)
 
-    [P5] section 2 (storage vs reads ledger) and [P1] B9 (read count of one
-    CSA layer is min(k, n/m) + n_win; of one HCA layer n/m' + n_win).
-    `history` counts processed positions including the current query.
+
+def layer_reads(history: int, ratio: int, n_win: int, k: int | None = None) -> LayerReads:
+    """Entries a query reads in one layer, after `history` processed positions.
+
+    Closed form of [P1] B9 (per-query read count of a CSA layer is
+    min(k, n/m) + n_win, of an HCA layer n/m' + n_win) with the completed
+    count of [P5] section 3 ((t + 1) // m at the newest position t =
+    history - 1).  k = None is the dense HCA read of every completed entry;
+    a window never holds more rows than exist.  The worked values of [P5]
+    section 2 pin it.
     """
-    for v in (history, m, m_prime, k, n_win):
-        if int(v) != v or v <= 0:
-            raise ValueError("all counts must be positive integers")
-    if m_prime <= m:
-        raise ValueError("the heavy ratio must exceed the light ratio")
-    csa_stored = history // m
-    hca_stored = history // m_prime
-    window = min(history, n_win)
-    return {
-        "csa_stored": csa_stored,
-        "hca_stored": hca_stored,
-        "csa_reads": min(k, csa_stored) + window,
-        "hca_reads": hca_stored + window,
-        "csa_tail": history % m,
-        "hca_tail": history % m_prime,
-    }
+    done = visible_entries(history - 1, ratio)
+    picked = done if k is None else min(int(k), done)
+    return LayerReads(stored=done, tail=history - done * ratio,
+                      reads=picked + min(history, int(n_win)))
 
 
 # --------------------------------------------------------------------------

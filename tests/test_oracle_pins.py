@@ -34,24 +34,32 @@ def _rng(seed=0):
 def test_read_ledger_worked_example():
     g = _golden("read_ledger.json")
     for case in g["cases"]:
-        r = O.read_counts(case["history"], case["m"], case["m_prime"], case["k"], case["n_win"])
-        for key in ("csa_reads", "hca_reads", "csa_tail"):
-            if key in case:
-                assert r[key] == case[key], (key, r)
+        light = O.layer_reads(case["history"], case["m"], case["n_win"], k=case["k"])
+        heavy = O.layer_reads(case["history"], case["m_prime"], case["n_win"])
+        if "csa_reads" in case:
+            assert light.reads == case["csa_reads"], light
+        if "hca_reads" in case:
+            assert heavy.reads == case["hca_reads"], heavy
+        if "csa_tail" in case:
+            assert light.tail == case["csa_tail"], light
 
 
 def test_read_ledger_one_million():
     g = _golden("one_million_counts.json")
-    r = O.read_counts(g["history"], g["m"], g["m_prime"], g["k"], g["n_win"])
-    for key in ("csa_stored", "hca_stored", "csa_reads", "hca_reads"):
-        assert r[key] == g[key], key
+    light = O.layer_reads(g["history"], g["m"], g["n_win"], k=g["k"])
+    heavy = O.layer_reads(g["history"], g["m_prime"], g["n_win"])
+    assert (light.stored, light.reads) == (g["csa_stored"], g["csa_reads"])
+    assert (heavy.stored, heavy.reads) == (g["hca_stored"], g["hca_reads"])
 
 
-def test_read_ledger_rejects_bad_counts():
+def test_read_ledger_small_histories():
+    # before the first block completes only the window is read; the window
+    # never holds more rows than have been processed
+    assert O.layer_reads(3, 4, 128, k=32) == O.LayerReads(stored=0, tail=3, reads=3)
+    assert O.layer_reads(4, 4, 128, k=32) == O.LayerReads(stored=1, tail=0, reads=5)
+    assert O.layer_reads(200, 128, 16) == O.LayerReads(stored=1, tail=72, reads=17)
     with pytest.raises(ValueError):
-        O.read_counts(0, 4, 128, 32, 128)
-    with pytest.raises(ValueError):
-        O.read_counts(16, 4, 4, 32, 128)
+        O.layer_reads(0, 4, 128, k=32)
 
 
 def test_visibility_boundaries():
