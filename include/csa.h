@@ -18,6 +18,13 @@
  *  - `*_bstride` arguments give the distance, in elements, between two
  *    consecutive sequences of a batched cache, so that a cache may be larger
  *    than the part in use; 0 means "dense" (rows-in-use * row length).
+ *  - Alignment: every pointer must be aligned to its element size.  Rows
+ *    whose length in bytes is a multiple of 16 are moved with 16-byte vector
+ *    loads and stores; their pointers must then be 16-byte aligned and their
+ *    row and batch strides multiples of 16 bytes (csa_attend / hca_attend:
+ *    on the bf16 c = 512 path, for q, Ccomp, kv_raw and out; csa_compress:
+ *    every stream, bias, state and output; csa_index_topk: qI and KIcomp).
+ *    Violations return CSA_EINVAL before anything is enqueued.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns without synchronising.
  *  - Errors: arguments are validated on the host before anything is

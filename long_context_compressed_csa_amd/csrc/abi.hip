@@ -11,6 +11,17 @@
 namespace {
 
 inline bool dtype_ok(int dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+inline int64_t elem_bytes(int dt) { return dt == CSA_F32 ? 4 : dt == CSA_BF16 ? 2 : 1; }
+
+// NULL, or a multiple of `a` bytes
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Rows whose byte length is a multiple of 16 are moved with 16-byte vector
+// loads and stores: their pointers must then be 16-byte aligned and every
+// row/batch stride a multiple of 16 bytes; other rows need only the
+// element's natural alignment.
+inline uintptr_t row_align(int64_t row_bytes, int64_t es) { return row_bytes % 16 == 0 ? 16 : (uintptr_t)es; }
+inline bool stride_ok(int64_t stride_elems, int64_t es, uintptr_t a) { return (stride_elems * es) % (int64_t)a == 0; }
 inline int launched(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_EHIP; }
 
 inline int64_t visible(int64_t t, int64_t m) { return (t + 1) / m; }
@@ -42,6 +53,12 @@ int check_attend(const void* q, const void* Ccomp, int64_t cbs, const void* kv_r
   if (cbs > 0 && cbs < n_comp * c) return CSA_EINVAL;
   if (rbs > 0 && rbs < n_raw * c) return CSA_EINVAL;
   if (!window_covered(t0, n_q, n_win, raw_pos0, n_raw)) return CSA_EINVAL;
+  // the MFMA path (bf16, c = 512) gathers and stores whole rows 16 bytes per lane
+  const int64_t es = elem_bytes(dtype);
+  const uintptr_t a = (dtype == CSA_BF16 && c == 512 && n_h % 64 == 0) ? 16 : (uintptr_t)es;
+  if (!aligned(q, a) || !aligned(Ccomp, a) || !aligned(kv_raw, a) || !aligned(out, a) || !aligned(sink, 4))
+    return CSA_EINVAL;
+  if (!stride_ok(cbs, es, a) || !stride_ok(rbs, es, a)) return CSA_EINVAL;
   return CSA_OK;
 }
 
@@ -78,6 +95,14 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
   }
   const int64_t ne = n / m;
   if (out_bstride < 0 || (out_bstride > 0 && out_bstride < ne * c)) return CSA_EINVAL;
+  {
+    const int64_t es = elem_bytes(dtype);
+    const uintptr_t a = row_align(c * es, es);
+    const void* ps[] = {Ca, Cb, Za, Zb, Ba, Bb, prev_Cb, prev_Zb, Ccomp};
+    for (const void* p : ps)
+      if (!aligned(p, a)) return CSA_EINVAL;
+    if (!stride_ok(out_bstride, es, a)) return CSA_EINVAL;
+  }
   if (b > 65535) return CSA_ENOTSUP;
   const int64_t obs = out_bstride > 0 ? out_bstride : ne * c;
   return launched(csa::launch_compress(Ca, Cb, Za, Zb, Ba, Bb, prev_Cb, prev_Zb, b, n, c, m,
@@ -100,6 +125,12 @@ int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t c
     return CSA_EINVAL;
   if (n_comp > visible(t0 + n_q - 1, m)) return CSA_EINVAL;
   if (comp_bstride < 0 || (comp_bstride > 0 && comp_bstride < n_comp * c_I)) return CSA_EINVAL;
+  {
+    const int64_t es = elem_bytes(dtype);
+    const uintptr_t a = row_align(c_I * es, es);
+    if (!aligned(qI, a) || !aligned(KIcomp, a) || !stride_ok(comp_bstride, es, a)) return CSA_EINVAL;
+    if (!aligned(w, 4) || !aligned(idx, 4) || !aligned(score, 4)) return CSA_EINVAL;
+  }
   if (n_q > 65535 || b > 65535) return CSA_ENOTSUP;
   if (!csa::index_topk_supported(n_comp, k)) return CSA_ENOTSUP;
   if (((uintptr_t)workspace & 255u) != 0) return CSA_EINVAL;
@@ -120,6 +151,15 @@ int csa_index_topk_mxfp4(const void* qI, const void* qI_scale, const float* w, c
   if (c_I % 32 != 0) return CSA_EINVAL;
   if (n_comp > visible(t0 + n_q - 1, m)) return CSA_EINVAL;
   if (comp_bstride < 0 || (comp_bstride > 0 && comp_bstride < n_comp)) return CSA_EINVAL;
+  // code rows (c_I/2 bytes, a multiple of 16) are loaded 16 bytes at a time,
+  // a head's or key's scales (c_I/32 bytes) 4 at a time when they fill words
+  {
+    const uintptr_t as = (c_I / 32) % 4 == 0 ? 4 : 1;
+    if (!aligned(qI, 16) || !aligned(KIcomp, 16) || !aligned(qI_scale, as) || !aligned(KI_scale, as))
+      return CSA_EINVAL;
+    if (((comp_bstride * (c_I / 32)) % (int64_t)as) != 0) return CSA_EINVAL;
+    if (!aligned(w, 4) || !aligned(idx, 4) || !aligned(score, 4)) return CSA_EINVAL;
+  }
   if (n_q > 65535 || b > 65535) return CSA_ENOTSUP;
   if (!csa::index_topk_supported(n_comp, k) || !csa::index_topk_mx_supported(n_q, n_hI, c_I)) return CSA_ENOTSUP;
   if (((uintptr_t)workspace & 255u) != 0) return CSA_EINVAL;
@@ -273,6 +313,11 @@ int hca_layer(const void* C, const void* Z, const void* B, const void* q, const 
   int rc = check_attend(q, Ccomp, 0, kv_raw, 0, 0, sink, b, n, 0, ne, n, n_h, c, m_prime, n_win,
                         scale, dtype, out);
   if (rc != CSA_OK) return rc;
+  {
+    const int64_t es = elem_bytes(dtype);
+    const uintptr_t a = row_align(c * es, es);
+    if (!aligned(C, a) || !aligned(Z, a) || !aligned(B, a) || !aligned(Ccomp, a)) return CSA_EINVAL;
+  }
   if (b > 65535 || n_h > 65535) return CSA_ENOTSUP;
   if (!csa::attend_supported(dtype, n_h, c, 0)) return CSA_ENOTSUP;
   const size_t need = hca_layer_workspace_size(b, n, n_h, c, m_prime, n_win, dtype);

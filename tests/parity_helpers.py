@@ -3,11 +3,13 @@
 Floats: RMS is taken per output vector (one attention output o[t, h, :] or
 one compressed entry C[i, :], the last axis), so that rows of very different
 scale -- a query reading 3 entries next to one reading 600 -- are each held
-to their own scale.  Then |got - want| <= 2e-2 * RMS + 2^-8 * |want|
-element-wise for bfloat16 storage (the stated bound plus half a bfloat16 ulp
-of the element itself: storing a result in bfloat16 alone moves it by up to
-2^-8 of its magnitude, which exceeds 2e-2 * RMS for elements above
-5.12 * RMS), and |got - want| <= 1e-4 * min(1, RMS) for float32.  Index sets: equal, except that a
+to their own scale.  Then |got - want| <= max(2e-2 * RMS, 2^-8 * |want|)
+element-wise for bfloat16 storage: the stated bound, except for elements
+above 5.12 * RMS, where storing the result in bfloat16 alone may move it by
+up to 2^-8 of its magnitude (half a bfloat16 ulp), more than 2e-2 * RMS; and
+|got - want| <= 1e-4 * min(1, RMS) for float32.  Every comparison prints its
+worst error as a fraction of its bound and of the plain 2e-2 * RMS (1e-4 *
+min(1, RMS)) bound, so the margin is on record.  Index sets: equal, except that a
 member of the symmetric difference may lie within 1e-3 of the k-th oracle
 score (a near-tie decided differently by float32 and float64 sums); sizes,
 ascending order and -1 padding must match exactly.
@@ -37,15 +39,21 @@ def assert_close(got, want, dtype, what=""):
     rms = np.sqrt(np.mean(want ** 2, axis=-1, keepdims=True))
     diff = np.abs(got - want)
     if dtype == torch.bfloat16:
-        bound = BF16_TOL * rms + BF16_HALF_ULP * np.abs(want)
+        plain = BF16_TOL * rms + 0.0 * want
+        bound = np.maximum(plain, BF16_HALF_ULP * np.abs(want))
     else:
-        bound = F32_TOL * np.minimum(1.0, rms) + 0.0 * want
-    excess = diff - bound
-    i = int(np.argmax(excess))
+        plain = F32_TOL * np.minimum(1.0, rms) + 0.0 * want
+        bound = plain
+    # a zero bound (an all-zero oracle row) demands an exact zero
+    ratio = np.where(bound > 0, diff / np.where(bound > 0, bound, 1.0), np.where(diff > 0, np.inf, 0.0))
+    plain_ratio = np.where(plain > 0, diff / np.where(plain > 0, plain, 1.0), np.where(diff > 0, np.inf, 0.0))
+    i = int(np.argmax(ratio))
     idx = np.unravel_index(i, want.shape)
     row_rms = float(rms[idx[:-1] + (0,)])
-    assert excess.flat[i] <= 0, (f"{what}: |err| {diff.flat[i]:.3e} > bound {bound.flat[i]:.3e} at "
-                                 f"{idx} (want {want.flat[i]:.4e}, row rms {row_rms:.3e})")
+    print(f"[margin] {what or 'output'}: worst err/bound {ratio.flat[i]:.3f}, "
+          f"worst err/plain bound {float(plain_ratio.max()):.3f}", flush=True)
+    assert ratio.flat[i] <= 1.0, (f"{what}: |err| {diff.flat[i]:.3e} > bound {bound.flat[i]:.3e} at "
+                                  f"{idx} (want {want.flat[i]:.4e}, row rms {row_rms:.3e})")
     return float(diff.max()), float(np.sqrt(np.mean(want ** 2)))
 
 

@@ -276,3 +276,30 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(8, 4)
     with pytest.raises(ValueError):
         L.csa_compress(x, x, x, x, torch.zeros(4, 4), torch.zeros(4, 4), 4)
+
+
+def test_misaligned_rows_are_rejected(lib):
+    # rows moved 16 bytes per lane (bf16 MFMA attention at c = 512, vector
+    # compressor and indexer rows) need 16-byte aligned pointers and strides
+    dec = dict(n_q=1, t0=4095, n_comp=1024, n_raw=128, pos0=3968, n_h=64, c=512, k=512, dtype=1, n_win=128,
+               ws=0x100000, ws_bytes=1 << 30)
+    for bad in (dict(q=FAKE + 2), dict(Cc=FAKE + 8), dict(raw=FAKE + 4), dict(out=FAKE + 2),
+                dict(cbs=1024 * 512 + 1), dict(rbs=128 * 512 + 4), dict(sink=FAKE + 2)):
+        kw = dict(dec)
+        kw.update(bad)
+        assert _attend(lib, **kw) == EINVAL, bad
+        assert _attend(lib, "hca_attend", **kw) == EINVAL, bad
+    # the generic float32 path reads elements one at a time: natural alignment
+    assert _attend(lib, q=FAKE + 2) == EINVAL
+    # compressor: c = 8 bf16 is one 16-byte vector per row
+    for bad in (dict(Ca=FAKE + 2), dict(Zb=FAKE + 8), dict(out=FAKE + 4), dict(obs=4 * 8 + 1),
+                dict(pCb=FAKE + 2, pZb=FAKE)):
+        assert _compress(lib, dtype=1, **bad) == EINVAL, bad
+    # indexer: bf16 keys of 16 dims (32 bytes per row)
+    for bad in (dict(qI=FAKE + 2), dict(KI=FAKE + 16 + 2), dict(cbs=2 * 16 + 1), dict(w=FAKE + 2),
+                dict(idx=FAKE + 1)):
+        assert _topk(lib, dtype=1, **bad) == EINVAL, bad
+    # MXFP4: code rows 16-byte aligned, 4-byte scale words
+    assert _topk_mx(lib, qI=FAKE + 8) == EINVAL
+    assert _topk_mx(lib, KI=FAKE + 8) == EINVAL
+    assert _topk_mx(lib, cI=128, KS=FAKE + 2) == EINVAL

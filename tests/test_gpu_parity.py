@@ -934,6 +934,7 @@ def test_decode_steps_match_oracle_decode_state():
         for t in range(n0):
             o.append({x: to64(st[x][s, t]) for x in st}, {x: to64(v) for x, v in B.items()})
         states.append(o)
+    chained = tie_steps = 0
     for t in range(n0, n):
         idx, out = drv.step(t, {x: g(st[x][:, t]) for x in st}, g(q[:, t:t + 1]), g(qI[:, t:t + 1]),
                             g(w[:, t:t + 1]))
@@ -952,9 +953,23 @@ def test_decode_steps_match_oracle_decode_state():
             raw = np.stack([r for _, r in states[s].window])
             want = O.csa_attend(to64(q[s, t])[None], to64(Cco16), oi[None], raw, pos0, to64(sink), [t], nw,
                                 scale, m)
+            # always: the GPU attention step on the oracle's selection (the
+            # chained output uses the GPU's own selection, which may settle a
+            # near-tie the other way)
+            o_sel = L.csa_attend(g(q[s:s + 1, t:t + 1]), drv.Cc[s:s + 1], g(torch.tensor(oi[None, None], dtype=torch.int32)),
+                                 drv.win[s:s + 1], drv.sink, t, m, nw, scale, raw_pos0=drv.win_pos0,
+                                 n_comp=drv.n_comp)
+            torch.cuda.synchronize()
+            assert_close(o_sel[0], want, torch.bfloat16, f"t={t} seq {s}, oracle selection")
             if set(idx[s, 0].cpu().numpy().tolist()) == set(oi.tolist()):
-                assert_close(out[s], want, torch.bfloat16, f"t={t} seq {s}")
-        # the caches match the oracle's entries
+                assert_close(out[s], want, torch.bfloat16, f"t={t} seq {s}, chained")
+                chained += 1
+            else:
+                tie_steps += 1
+    print(f"[ties] decode continuity: {tie_steps} of {chained + tie_steps} (step, sequence) selections settled a "
+          f"near-tie differently; the chained output was compared on the other {chained}", flush=True)
+    assert chained >= (chained + tie_steps) // 2
+    # the caches match the oracle's entries
     for s in range(b):
         assert_close(drv.Cc[s, : drv.n_comp], np.array(states[s].Ccomp), torch.bfloat16, "Ccomp")
         assert_close(drv.KI[s, : drv.n_comp], np.array(states[s].KIcomp), torch.bfloat16, "KIcomp")
@@ -1004,8 +1019,19 @@ def test_decode_one_million_context_sampled():
             win_rows = to64(d["window"][s])
             want = O.csa_attend(to64(d["q"][i][s]), Csel, np.arange(len(Csel))[None], win_rows, d["window_pos0"],
                                 to64(d["sink"]), [t], nw, d["scale"])
+            # always: the GPU attention step over the whole cache with the
+            # oracle's selection; the chained output too when the GPU chose
+            # the same set (a near-tie may be settled the other way)
+            o_sel = L.csa_attend(d["q"][i][s:s + 1], d["Ccomp"][s:s + 1], g(torch.tensor(oi[None, None], dtype=torch.int32)),
+                                 d["window"][s:s + 1], d["sink"], t, m, nw, d["scale"], raw_pos0=d["window_pos0"],
+                                 n_comp=n_comp)
+            torch.cuda.synchronize()
+            assert_close(o_sel[0], want, torch.bfloat16, f"t={t} seq {s}, oracle selection")
             if set(idx[s, 0].cpu().numpy().tolist()) == set(oi.tolist()):
-                assert_close(out[s], want, torch.bfloat16, f"t={t} seq {s}")
+                assert_close(out[s], want, torch.bfloat16, f"t={t} seq {s}, chained")
+            else:
+                print(f"[ties] t={t} seq {s}: the GPU settled a near-tie differently; chained output not compared",
+                      flush=True)
 
 
 def test_graph_replay_matches_eager():
@@ -1216,10 +1242,11 @@ def test_csa_layer_with_norm_and_rope_bf16():
     got = to64(o)
     rms = np.sqrt(np.mean(want ** 2, axis=-1, keepdims=True))
     pair = np.sqrt(want[..., lo::2] ** 2 + want[..., lo + 1::2] ** 2).repeat(2, axis=-1)
-    bound = 2e-2 * rms + 2.0 ** -8 * np.abs(want[..., lo:]) + 2.0 ** -8 * pair
-    excess = np.abs(got[..., lo:] - want[..., lo:]) - bound
-    i = np.unravel_index(int(np.argmax(excess)), excess.shape)
-    assert excess[i] <= 0, ("rotated dims", i, got[..., lo:][i], want[..., lo:][i], bound[i])
+    bound = np.maximum(2e-2 * rms, 2.0 ** -8 * np.abs(want[..., lo:]) + 2.0 ** -8 * pair)
+    ratio = np.abs(got[..., lo:] - want[..., lo:]) / bound
+    i = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    print(f"[margin] rotated dims: worst err/bound {ratio[i]:.3f}", flush=True)
+    assert ratio[i] <= 1.0, ("rotated dims", i, got[..., lo:][i], want[..., lo:][i], bound[i])
 
 
 # ------------------------------------------------ grouped output projection --
