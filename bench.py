@@ -62,6 +62,36 @@ class KernelTimer:
         return 1000.0 * self.total[name] / self.count[name]
 
 
+def prewarm(torch, fn, seconds=0.3):
+    """Run fn untimed for at least `seconds` of GPU time so that the clocks
+    reach their steady state before the warm-up and timed steps."""
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
+def timed_steps(torch, fn, steps):
+    """Time `steps` calls of fn: a HIP event on the stream before the first
+    and after each one, synchronised on both sides.  Returns (median of the
+    per-step event intervals in ms, wall-clock mean in ms)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = 1000.0 * (time.perf_counter() - t0) / steps
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    mid = len(per) // 2
+    med = per[mid] if len(per) % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return med, wall
+
+
 # --------------------------------------------------------------- prefill ----
 
 def prefill_pairs(n, m, k, n_win):
@@ -111,15 +141,11 @@ def run_prefill(args, torch, L, synth):
             if rc != 0:
                 raise RuntimeError(f"{name} failed: {L.strerror(rc)}")
 
+    prewarm(torch, step)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    # whole-step wall time: K steps between two synchronisations
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = 1000.0 * (time.perf_counter() - t0) / args.steps
+    # K steps: median of the per-step HIP-event intervals (and the wall mean)
+    ms, ms_wall = timed_steps(torch, step, args.steps)
     # per-kernel HIP-event timings over a second pass of K steps
     timer = KernelTimer(torch)
     for _ in range(args.steps):
@@ -179,12 +205,7 @@ def run_prefill(args, torch, L, synth):
 
     for _ in range(args.warmup):
         step4()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step4()
-    torch.cuda.synchronize()
-    ms4 = 1000.0 * (time.perf_counter() - t0) / args.steps
+    ms4, _ = timed_steps(torch, step4, args.steps)
     del qc, qs, kc, ks
 
     # A whole step with the normalisation and partial RoPE around the core
@@ -227,12 +248,7 @@ def run_prefill(args, torch, L, synth):
 
     for _ in range(args.warmup):
         stepR()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        stepR()
-    torch.cuda.synchronize()
-    msR = 1000.0 * (time.perf_counter() - t0) / args.steps
+    msR, _ = timed_steps(torch, stepR, args.steps)
     timerR = KernelTimer(torch)
     for _ in range(args.steps):
         stepR(timerR)
@@ -283,6 +299,7 @@ def run_prefill(args, torch, L, synth):
     att_tflops = flop_attend / (stage_us["attend"] * 1e-6) / 1e12
     return {
         "ms_per_step": ms,
+        "ms_per_step_wall": ms_wall,
         "tokens_per_s": n / (ms / 1000.0),
         "stage_us": stage_us,
         "flop_attend": flop_attend,
@@ -777,6 +794,10 @@ def main(argv=None):
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": pre["ms_per_step"],
+        "ms_per_step_wall_mean": pre["ms_per_step_wall"],
+        "timing": "ms_per_step is the median of the K per-step HIP-event intervals (after 0.3 s of untimed "
+                  "steps for the clocks and W warm-up steps); the wall-clock mean of the same K steps is "
+                  "ms_per_step_wall_mean",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
