@@ -153,6 +153,9 @@ def run_prefill(args, torch, L, synth):
     timer.collect()
     stage_us = {name: timer.avg_us(name) for name, _ in stages}
 
+    if args.core:
+        return {"ms_per_step": ms, "ms_per_step_wall": ms_wall, "stage_us": stage_us}
+
     # The FP4 indexer at this shape: the step's queries and keys quantised to
     # MXFP4 before timing, the index + top-k timed like the stages (the step
     # above keeps the bf16 indexer: the library has no quantising compressor).
@@ -397,6 +400,8 @@ def run_decode(args, torch, L, synth):
     step_bytes = key_bytes + gathered + small
     res = {"us_per_step": us, "bytes_per_step": step_bytes,
            "hbm_gbs": step_bytes / (us * 1e-6) / 1e9, "b": b, "history": hist, "k": k}
+    if args.core:
+        return res
 
     # The low-precision indexer: the same state with the indexer keys and
     # queries as E4M3 codes (converted before timing), over the first
@@ -740,6 +745,8 @@ def main(argv=None):
     ap.add_argument("--decode-reps", type=int, default=10)
     ap.add_argument("--hca-iters", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--core", action="store_true",
+                    help="with --only: time only the workload's main step (for profiler runs), no secondary lines")
     ap.add_argument("--traffic-summary", metavar="PMC_DIR", default=None,
                     help="summarise counter runs under PMC_DIR/{attend_fetch,attend_write,copy_fetch,"
                          "copy_write} into the traffic record under profiles/ (no GPU needed)")
@@ -778,7 +785,9 @@ def main(argv=None):
     if a.only in (None, "compress"):
         print("[bench] compress", file=sys.stderr, flush=True)
         extras["compressor"] = run_compress(a, torch, L, synth)
-    if pre is None:
+    if pre is None or a.core:
+        if pre is not None:
+            extras["prefill"] = {k: v for k, v in pre.items() if k != "inputs"}
         print(json.dumps({"extras": extras}))
         return
     cpu = None

@@ -132,6 +132,34 @@ int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t c
 size_t csa_index_topk_workspace_size(int64_t b, int64_t n_q, int64_t n_comp, int64_t k);
 
 /*
+ * csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same operation, arguments
+ * and results as csa_index_topk without `workspace` / `ws_bytes`; its
+ * scratch is a device array of CSA_NOALLOC_SCRATCH_BYTES that the library's
+ * code object holds on each GPU it runs on until the process ends (no
+ * allocation call is made, on the first call or any other).
+ *
+ *  - Uses the scratch of the device current at the call; `stream` must
+ *    belong to that device.
+ *  - Every call on one GPU shares that GPU's array: calls that may overlap
+ *    in time on one GPU (other streams, other host threads) race and must
+ *    be serialised by the caller.  The kernels write every scratch word they
+ *    read before reading it, so nothing is carried from one call to the next.
+ *
+ * Errors: as csa_index_topk; CSA_ENOSPC when
+ * csa_index_topk_workspace_size(b, n_q, n_comp, k) exceeds
+ * CSA_NOALLOC_SCRATCH_BYTES (80 MiB: e.g. 8 or 16 sequences of a 2^20-token
+ * decode, or a 8192-token prefill block with 2048 entries); CSA_EHIP if the
+ * scratch address cannot be obtained on the current device.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (80u * 1024u * 1024u)
+int csa_index_topk_noalloc(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride,
+                           int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI,
+                           int64_t c_I, int64_t m, int64_t k, int dtype, int32_t* idx, float* score,
+                           void* stream);
+
+/*
  * csa_index_topk_mxfp4 -- csa_index_topk with the indexer queries and keys
  * in OCP MXFP4 (songhuiming "DeepSeek-V4 百万 token 上下文" section 13.3 and
  * AirCoding "deepseek-paper-analysis" section 7, FP4 quantization-aware

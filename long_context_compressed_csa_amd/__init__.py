@@ -6,11 +6,13 @@ device memory and streams only.
 """
 
 from ._binding import (  # noqa: F401
-    CSA_BF16, CSA_F32, CsaError, LIB_PATH, csa_attend, csa_compress, csa_index_topk, csa_index_topk_mxfp4, csa_quantize_mxfp4, csa_norm_rope, csa_grouped_out_proj,
-    hca_attend, hca_layer, load_library, strerror, version,
+    CSA_BF16, CSA_F32, CsaError, LIB_PATH, csa_attend, csa_compress, csa_grouped_out_proj, csa_index_topk,
+    csa_index_topk_mxfp4, csa_index_topk_noalloc, csa_norm_rope, csa_quantize_mxfp4, hca_attend, hca_layer,
+    load_library, strerror, version,
 )
 
 __all__ = [
-    "csa_compress", "csa_index_topk", "csa_index_topk_mxfp4", "csa_quantize_mxfp4", "csa_norm_rope", "csa_grouped_out_proj", "csa_attend", "hca_attend", "hca_layer",
+    "csa_compress", "csa_index_topk", "csa_index_topk_noalloc", "csa_index_topk_mxfp4", "csa_quantize_mxfp4",
+    "csa_norm_rope", "csa_grouped_out_proj", "csa_attend", "hca_attend", "hca_layer",
     "load_library", "version", "strerror", "CsaError", "CSA_F32", "CSA_BF16", "LIB_PATH",
 ]

@@ -37,6 +37,7 @@ SIGNATURES = {
     "csa_compress": (_int, [_vp] * 8 + [_i64] * 4 + [_int, _int, _vp, _i64, _vp]),
     "csa_index_topk": (_int, [_vp, _vp, _vp, _i64] + [_i64] * 8 + [_int, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_workspace_size": (_sz, [_i64] * 4),
+    "csa_index_topk_noalloc": (_int, [_vp, _vp, _vp, _i64] + [_i64] * 8 + [_int, _vp, _vp, _vp]),
     "csa_index_topk_mxfp4": (_int, [_vp] * 5 + [_i64] * 9 + [_vp, _vp, _vp, _sz, _vp]),
     "csa_quantize_mxfp4": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp]),
     "csa_grouped_out_proj": (_int, [_vp, _vp, _vp] + [_i64] * 6 + [_int, _vp, _vp, _vp]),
@@ -194,6 +195,24 @@ def csa_index_topk(qI, w, KIcomp, t0, m, k, n_comp=None, score=False, idx=None,
                             n_comp, nh, cI, m, k, dt, _ptr(idx), _ptr(sc), _ptr(workspace),
                             workspace.numel(), _stream(stream))
     _check(rc, "csa_index_topk")
+    return (idx, sc) if score else idx
+
+
+def csa_index_topk_noalloc(qI, w, KIcomp, t0, m, k, n_comp=None, score=False, idx=None, stream=None):
+    """csa_index_topk on the library's own per-GPU scratch (no workspace
+    argument and no allocation for scratch; outputs are allocated here unless
+    given).  Calls that overlap on one GPU race on that scratch."""
+    qI, w, KIcomp = _batched(qI, 4), _batched(w, 3), _batched(KIcomp, 3)
+    b, n_q, nh, cI = qI.shape
+    n_comp = KIcomp.shape[1] if n_comp is None else n_comp
+    dt = _dtype(qI, KIcomp)
+    lib = load_library()
+    if idx is None:
+        idx = torch.empty((b, n_q, k), dtype=torch.int32, device=qI.device)
+    sc = torch.empty((b, n_q, k), dtype=torch.float32, device=qI.device) if score else None
+    rc = lib.csa_index_topk_noalloc(_ptr(qI), _f32c(w, "w"), _ptr(KIcomp), KIcomp.stride(0), b, n_q, t0, n_comp,
+                                    nh, cI, m, k, dt, _ptr(idx), _ptr(sc), _stream(stream))
+    _check(rc, "csa_index_topk_noalloc")
     return (idx, sc) if score else idx
 
 

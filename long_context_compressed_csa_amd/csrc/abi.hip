@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "csa.h"
 #include "kernels.hpp"
 
@@ -114,12 +116,15 @@ size_t csa_index_topk_workspace_size(int64_t b, int64_t n_q, int64_t n_comp, int
   return csa::index_topk_workspace_bytes(b, n_q, n_comp, k);
 }
 
-int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride,
-                   int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI, int64_t c_I,
-                   int64_t m, int64_t k, int dtype, int32_t* idx, float* score, void* workspace,
-                   size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int check_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride, int64_t b,
+                     int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI, int64_t c_I, int64_t m, int64_t k,
+                     int dtype, const int32_t* idx, const float* score) {
   if (!dtype_ok(dtype) && dtype != CSA_FP8) return CSA_ENOTSUP;
-  if (!qI || !w || !idx || !workspace) return CSA_EINVAL;
+  if (!qI || !w || !idx) return CSA_EINVAL;
   if (n_comp > 0 && !KIcomp) return CSA_EINVAL;
   if (b < 1 || n_q < 1 || n_hI < 1 || c_I < 1 || m < 1 || k < 1 || t0 < 0 || n_comp < 0)
     return CSA_EINVAL;
@@ -133,11 +138,63 @@ int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t c
   }
   if (n_q > 65535 || b > 65535) return CSA_ENOTSUP;
   if (!csa::index_topk_supported(n_comp, k)) return CSA_ENOTSUP;
-  if (((uintptr_t)workspace & 255u) != 0) return CSA_EINVAL;
+  return CSA_OK;
+}
+
+// Scratch of csa_index_topk_noalloc: one array per GPU, placed by the loader
+// with the code object (no allocation call at any time).  In host code the
+// array's name stands for a host-side shadow, not a device address: kernels
+// get the address hipGetSymbolAddress returns for the current device, looked
+// up on the first call on each device and kept here.
+static_assert(CSA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return CSA_EHIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride,
+                   int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI, int64_t c_I,
+                   int64_t m, int64_t k, int dtype, int32_t* idx, float* score, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  int rc = check_index_topk(qI, w, KIcomp, comp_bstride, b, n_q, t0, n_comp, n_hI, c_I, m, k, dtype, idx, score);
+  if (rc != CSA_OK) return rc;
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0) return CSA_EINVAL;
   if (ws_bytes < csa::index_topk_workspace_bytes(b, n_q, n_comp, k)) return CSA_ENOSPC;
   const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c_I;
   return launched(csa::launch_index_topk(qI, w, KIcomp, cbs, b, n_q, t0, n_comp, n_hI, c_I, m, k,
                                          dtype, idx, score, workspace, (hipStream_t)stream));
+}
+
+int csa_index_topk_noalloc(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride, int64_t b,
+                           int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI, int64_t c_I, int64_t m,
+                           int64_t k, int dtype, int32_t* idx, float* score, void* stream) {
+  int rc = check_index_topk(qI, w, KIcomp, comp_bstride, b, n_q, t0, n_comp, n_hI, c_I, m, k, dtype, idx, score);
+  if (rc != CSA_OK) return rc;
+  if (csa::index_topk_workspace_bytes(b, n_q, n_comp, k) > (size_t)CSA_NOALLOC_SCRATCH_BYTES) return CSA_ENOSPC;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != CSA_OK) return rc;
+  const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c_I;
+  return launched(csa::launch_index_topk(qI, w, KIcomp, cbs, b, n_q, t0, n_comp, n_hI, c_I, m, k,
+                                         dtype, idx, score, ws, (hipStream_t)stream));
 }
 
 int csa_index_topk_mxfp4(const void* qI, const void* qI_scale, const float* w, const void* KIcomp,

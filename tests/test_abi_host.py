@@ -303,3 +303,22 @@ def test_misaligned_rows_are_rejected(lib):
     assert _topk_mx(lib, qI=FAKE + 8) == EINVAL
     assert _topk_mx(lib, KI=FAKE + 8) == EINVAL
     assert _topk_mx(lib, cI=128, KS=FAKE + 2) == EINVAL
+
+
+def test_index_topk_noalloc_rejects_before_launch(lib):
+    def call(**kw):
+        a = dict(qI=FAKE, w=FAKE, KI=FAKE, cbs=0, b=1, n_q=8, t0=0, n_comp=2, nh=2, cI=16, m=4, k=4,
+                 dtype=0, idx=FAKE, score=None)
+        a.update(kw)
+        return lib.csa_index_topk_noalloc(a["qI"], a["w"], a["KI"], a["cbs"], a["b"], a["n_q"], a["t0"],
+                                          a["n_comp"], a["nh"], a["cI"], a["m"], a["k"], a["dtype"], a["idx"],
+                                          a["score"], None)
+    # the same validation as csa_index_topk
+    assert call(k=0) == EINVAL
+    assert call(n_comp=3) == EINVAL
+    assert call(dtype=9) == ENOTSUP
+    assert call(qI=FAKE + 2, dtype=1) == EINVAL
+    # 64 sequences of a 2^20-token decode need more than the 80 MiB scratch
+    big = dict(b=64, n_q=1, t0=262144 * 4 - 1, n_comp=262144, nh=64, cI=128, k=512, dtype=1)
+    assert lib.csa_index_topk_workspace_size(64, 1, 262144, 512) > 80 * 1024 * 1024
+    assert call(**big) == ENOSPC
