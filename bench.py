@@ -670,8 +670,9 @@ def _sources_sha256(paths):
     return h.hexdigest()
 
 
-def _pmc_mean(csv_dir, counter, name_regex):
-    """Mean of one counter over the dispatches whose kernel name matches."""
+def _pmc_mean(csv_dir, counter, name_regex, grid=None):
+    """Mean of one counter over the dispatches whose kernel name matches (and
+    whose grid has `grid` threads, when given)."""
     import csv
     import glob
     import re
@@ -679,7 +680,8 @@ def _pmc_mean(csv_dir, counter, name_regex):
     for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
             for row in csv.DictReader(f):
-                if row["Counter_Name"] == counter and re.search(name_regex, row["Kernel_Name"]):
+                if row["Counter_Name"] == counter and re.search(name_regex, row["Kernel_Name"]) and \
+                        (grid is None or int(row["Grid_Size"]) == grid):
                     vals.append(float(row["Counter_Value"]))
     if not vals:
         raise RuntimeError(f"no {counter} samples for /{name_regex}/ under {csv_dir}")
@@ -687,16 +689,18 @@ def _pmc_mean(csv_dir, counter, name_regex):
 
 
 def traffic_summary(pmc_dir, commands):
-    """Per-launch HBM bytes of the attention kernel from four counter runs
-    (attention FETCH_SIZE, attention WRITE_SIZE, copy FETCH_SIZE, copy
-    WRITE_SIZE, each in KiB per dispatch), every counter scaled by what it
-    reads for the 1 GiB copy."""
-    att = "attend_mfma_c512"
-    cp = "vectorized_elementwise_kernel"
-    f_att, nf = _pmc_mean(os.path.join(pmc_dir, "attend_fetch"), "FETCH_SIZE", att)
-    w_att, nw = _pmc_mean(os.path.join(pmc_dir, "attend_write"), "WRITE_SIZE", att)
-    f_cp, _ = _pmc_mean(os.path.join(pmc_dir, "copy_fetch"), "FETCH_SIZE", cp)
-    w_cp, _ = _pmc_mean(os.path.join(pmc_dir, "copy_write"), "WRITE_SIZE", cp)
+    """Per-launch HBM bytes of the prefill attention kernel from four counter
+    runs (prefill FETCH_SIZE, prefill WRITE_SIZE, copy FETCH_SIZE, copy
+    WRITE_SIZE, each in KiB per dispatch, in PMC_DIR/prefill-fetch,
+    prefill-write, copy-FETCH_SIZE, copy-WRITE_SIZE), every counter scaled by
+    what it reads for the 1 GiB copy."""
+    att = r"attend_mfma_c512<0, 1>"
+    grid = 8192 * 128   # the n = 8192 prefill launch: one 128-thread workgroup per query
+    cp = "vectorized_elementwise_kernel<4, at::native::AUnary"
+    f_att, nf = _pmc_mean(os.path.join(pmc_dir, "prefill-fetch"), "FETCH_SIZE", att, grid)
+    w_att, nw = _pmc_mean(os.path.join(pmc_dir, "prefill-write"), "WRITE_SIZE", att, grid)
+    f_cp, _ = _pmc_mean(os.path.join(pmc_dir, "copy-FETCH_SIZE"), "FETCH_SIZE", cp)
+    w_cp, _ = _pmc_mean(os.path.join(pmc_dir, "copy-WRITE_SIZE"), "WRITE_SIZE", cp)
     copy_bytes = float(1 << 30)
     f_scale = copy_bytes / (f_cp * 1024.0)
     w_scale = copy_bytes / (w_cp * 1024.0)
