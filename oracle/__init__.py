@@ -10,6 +10,6 @@ from .csa_oracle import (  # noqa: F401  (explicit re-exports for linters)
     visible_entries, LayerReads, layer_reads, compress_overlap, compress_pool,
     compress_weights_overlap, compress_weights_pool, index_scores, topk_select,
     index_topk, attend_entries, csa_attend, hca_attend, hca_layer, csa_layer,
-    CsaDecodeState, default_scale, window_rows, rms_norm, rope_frequencies,
+    CsaDecodeState, HcaDecodeState, block_geometry, default_scale, window_rows, rms_norm, rope_frequencies,
     rope, norm_rope, csa_attend_rope, grouped_out_proj,
 )

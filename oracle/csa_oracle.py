@@ -595,6 +595,63 @@ class CsaDecodeState:
         return idx[0], out[0]
 
 
+# --------------------------------------------------------------------------
+# Heterogeneous decode cache ([P3] section 7.6, "Inference KV Cache")
+# --------------------------------------------------------------------------
+
+def block_geometry(m: int, m_prime: int) -> tuple:
+    """Tokens per classical-cache block and the entries one block holds.
+
+    [P3] section 7.6: a block covers lcm(m, m') raw tokens, so it holds
+    lcm/m CSA entries and lcm/m' HCA entries (128, 32 and 1 for m = 4,
+    m' = 128).  Returns (tokens, csa_entries, hca_entries).
+    """
+    if m <= 0 or m_prime <= 0:
+        raise ValueError("ratios must be positive")
+    tokens = m * m_prime // math.gcd(m, m_prime)
+    return tokens, tokens // m, tokens // m_prime
+
+
+@dataclass
+class HcaDecodeState:
+    """Per-request decode state of one HCA layer: a sliding window of the
+    n_win most recent raw rows, the rows of the open m'-token block waiting
+    for compression, and the completed entries ([P3] section 7.6; [P1] B9
+    for the pooling compressor).  Window rows are the layer's C rows (the
+    reading used for the HCA prefill as well)."""
+    m_prime: int
+    n_win: int
+    entries: list = field(default_factory=list)
+    window: list = field(default_factory=list)          # (position, row)
+    tail: list = field(default_factory=list)            # (C, Z) rows of the open block
+    t: int = -1
+
+    def append(self, C_row, Z_row, B):
+        self.t += 1
+        self.window.append((self.t, _f64(C_row)))
+        self.window = self.window[-self.n_win:]
+        self.tail.append((_f64(C_row), _f64(Z_row)))
+        if len(self.tail) == self.m_prime:
+            C = np.stack([r[0] for r in self.tail])
+            Z = np.stack([r[1] for r in self.tail])
+            self.entries.append(compress_pool(C, Z, B, self.m_prime)[0])
+            self.tail = []
+
+    def query(self, q_t, sink, scale: float):
+        """Dense attention of the newest token's query over every completed
+        entry and the window."""
+        t = self.t
+        E = np.array(self.entries).reshape(-1, _f64(q_t).shape[-1])
+        pos0 = self.window[0][0]
+        raw = np.stack([r for _, r in self.window])
+        return hca_attend(_f64(q_t)[None], E, raw, pos0, sink, [t], self.m_prime, self.n_win, scale)[0]
+
+    def state_rows(self) -> int:
+        """Raw rows the state holds (window + open block): bounded by
+        n_win + 2 (m' - 1), whatever the request's length."""
+        return len(self.window) + 2 * len(self.tail)
+
+
 def default_scale(c: int) -> float:
     """Softmax scale 1/sqrt(c) (a reading: the pages never state it)."""
     return 1.0 / math.sqrt(c)

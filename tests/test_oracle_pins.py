@@ -718,3 +718,51 @@ def test_grouped_out_proj_equals_block_diagonal_projection():
     o2 = o.copy()
     o2[:, n_h // g:, :] += 1.0                     # heads outside group 0
     assert np.allclose(O.grouped_out_proj(o2, WG, WO, g)[0][:, :d_g], mid[:, :d_g], atol=1e-12)
+
+
+# ------------------------------------------- heterogeneous decode cache ----
+
+def test_block_geometry_from_the_page():
+    g = _golden("block_geometry.json")
+    assert O.block_geometry(g["m"], g["m_prime"]) == (g["tokens"], g["csa_entries"], g["hca_entries"])
+    # lcm: a block always holds whole blocks of both compressors
+    for m, mp in ((4, 6), (3, 128), (8, 8)):
+        L, e1, e2 = O.block_geometry(m, mp)
+        assert L % m == 0 and L % mp == 0 and e1 * m == L and e2 * mp == L
+        assert all(L2 % m or L2 % mp for L2 in range(1, L))
+
+
+def test_hca_decode_state_matches_prefill():
+    r = _rng(21)
+    n, c, mp, nw, nh = 70, 6, 8, 12, 3
+    C, Z = r.normal(size=(n, c)), 2 * r.normal(size=(n, c))
+    B = 0.1 * r.normal(size=(mp, c))
+    q = r.normal(size=(n, nh, c))
+    sink = r.normal(size=nh)
+    st = O.HcaDecodeState(m_prime=mp, n_win=nw)
+    for t in range(n):
+        st.append(C[t], Z[t], B)
+        if t in (0, 6, 7, 8, 15, 16, 40, n - 1):
+            got = st.query(q[t], sink, 0.4)
+            want = O.hca_attend(q[t][None], O.compress_pool(C[:t + 1], Z[:t + 1], B, mp), C, 0, sink, [t], mp, nw,
+                                0.4)[0]
+            assert np.abs(got - want).max() < 1e-12, t
+    full = O.compress_pool(C, Z, B, mp)
+    assert np.abs(np.array(st.entries) - full).max() < 1e-12
+
+
+def test_decode_state_is_fixed_size():
+    # the state cache holds the window and the open blocks only
+    r = _rng(22)
+    mp, nw, c = 8, 12, 4
+    B = 0.1 * r.normal(size=(mp, c))
+    st = O.HcaDecodeState(m_prime=mp, n_win=nw)
+    cs = O.CsaDecodeState(m=4, n_win=nw, c=c, c_I=c)
+    biases = {k: 0.1 * r.normal(size=(4, c)) for k in ("Ba", "Bb", "IBa", "IBb")}
+    for t in range(300):
+        row = r.normal(size=c)
+        st.append(row, row, B)
+        cs.append({k: r.normal(size=c) for k in ("Ca", "Cb", "Za", "Zb", "ICa", "ICb", "IZa", "IZb")}, biases)
+        assert st.state_rows() <= nw + 2 * (mp - 1)
+        assert len(cs.window) <= nw and len(cs.tail) < 4
+    assert len(st.entries) == 300 // mp and len(cs.Ccomp) == 300 // 4
