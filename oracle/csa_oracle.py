@@ -596,6 +596,138 @@ class CsaDecodeState:
 
 
 # --------------------------------------------------------------------------
+# Backward pass ([P3] section 7.6: training needs gradients of the layer;
+# the pages ask that the backward reductions be deterministic)
+# --------------------------------------------------------------------------
+
+def attend_entries_backward(q_t, E, sink, scale: float, g_t):
+    """Gradients of o = attend_entries(q_t, E, sink, scale) given dL/do = g_t.
+
+    Differentiating the softmax with the sink (weights p_j over the entries,
+    p_z for the sink, o = sum_j p_j e_j):
+      dl_j = p_j (g . e_j - g . o)         (logit l_j = scale q . e_j)
+      dz   = -p_z (g . o)                  (sink logit)
+      dq   = scale sum_j dl_j e_j
+      de_j = p_j g + scale dl_j q          (each entry is key and value)
+    per head, the entries shared by all heads (their gradients summed).
+    q_t, g_t [n_h, c]; E [N, c]; returns (dq [n_h, c], dE [N, c], dz [n_h]).
+    """
+    q_t, E, sink, g_t = _f64(q_t), _f64(E), _f64(sink), _f64(g_t)
+    logits = scale * (q_t @ E.T)                             # [n_h, N]
+    mx = np.maximum(logits.max(axis=1, initial=-np.inf), sink)
+    w = np.exp(logits - mx[:, None])
+    wz = np.exp(sink - mx)
+    den = w.sum(axis=1) + wz
+    p = w / den[:, None]
+    pz = wz / den
+    o = p @ E                                                # [n_h, c]
+    go = (g_t * o).sum(axis=1)                               # g . o per head
+    ge = g_t @ E.T                                           # g . e_j
+    dl = p * (ge - go[:, None])
+    dq = scale * (dl @ E)
+    dE = p.T @ g_t + scale * (dl.T @ q_t)
+    dz = -pz * go
+    return dq, dE, dz
+
+
+def csa_attend_backward(q, Ccomp, idx, kv_raw, raw_pos0: int, sink, t_pos, n_win: int,
+                        scale: float, dout, m: int | None = None):
+    """Gradients of csa_attend with respect to q, Ccomp, kv_raw and sink.
+
+    The entry set of each query is the forward's (selected rows, then the
+    window); an entry's gradient is the sum over every query and head that
+    read it.  Returns (dq [n_q, n_h, c], dCcomp like Ccomp, dkv_raw like
+    kv_raw, dsink [n_h]).
+    """
+    q, Ccomp, kv_raw, dout = _f64(q), _f64(Ccomp), _f64(kv_raw), _f64(dout)
+    dq = np.zeros_like(q)
+    dC = np.zeros_like(Ccomp)
+    dR = np.zeros_like(kv_raw)
+    dsink = np.zeros(q.shape[1])
+    for r, t in enumerate(np.asarray(t_pos)):
+        t = int(t)
+        sel = np.asarray(idx[r])
+        sel = sel[sel >= 0]
+        if m is not None and sel.size:
+            assert sel.max() < visible_entries(t, m), "index reads the future"
+        win = window_rows(t, n_win) - raw_pos0
+        E = np.concatenate([Ccomp[sel], kv_raw[win]], axis=0)
+        dq[r], dE, dz = attend_entries_backward(q[r], E, sink, scale, dout[r])
+        np.add.at(dC, sel, dE[: sel.size])
+        dR[win] += dE[sel.size:]
+        dsink += dz
+    return dq, dC, dR, dsink
+
+
+def hca_attend_backward(q, Ccomp, kv_raw, raw_pos0: int, sink, t_pos, m_prime: int,
+                        n_win: int, scale: float, dout):
+    """Gradients of hca_attend (every completed entry plus the window)."""
+    Ccomp = _f64(Ccomp)
+    n_comp = Ccomp.shape[0]
+    idx = np.stack([np.concatenate([np.arange(min(visible_entries(int(t), m_prime), n_comp)),
+                                    np.full(n_comp, -1)])[:max(n_comp, 1)]
+                    for t in np.asarray(t_pos)]) if len(t_pos) else np.zeros((0, 1), dtype=np.int64)
+    return csa_attend_backward(q, Ccomp, idx, kv_raw, raw_pos0, sink, t_pos, n_win, scale, dout, m_prime)
+
+
+def compress_overlap_backward(Ca, Cb, Za, Zb, Ba, Bb, m: int, dCc, prev_Cb=None, prev_Zb=None):
+    """Gradients of compress_overlap given dL/dC^Comp.
+
+    Entry i is sum_j S_j C_j over the 2m rows (block i of stream a, block
+    i-1 of stream b), S the per-dimension softmax of Z + B:
+      dC_j = S_j dCc_i,   dZ_j = S_j (C_j - Cc_i) dCc_i,
+    and a bias row collects dZ of that in-block row over every entry.
+    Rows no entry reads (the last block's stream-b rows, a ragged tail) get
+    zero.  Returns dict dCa, dCb, dZa, dZb, dBa, dBb (and dprev_Cb,
+    dprev_Zb when the previous-block state is given).
+    """
+    Ca, Cb = _f64(Ca), _f64(Cb)
+    dCc = _f64(dCc)
+    n, c = Ca.shape
+    ne = n // m
+    Sa, Sb = compress_weights_overlap(Za, Zb, Ba, Bb, m, prev_Zb)   # [ne, m, c] each
+    Cc = compress_overlap(Ca, Cb, Za, Zb, Ba, Bb, m, prev_Cb, prev_Zb)
+    ca = Ca[: ne * m].reshape(ne, m, c)
+    prev = np.zeros((1, m, c)) if prev_Cb is None else _f64(prev_Cb).reshape(1, m, c)
+    cb = np.concatenate([prev, Cb[: ne * m].reshape(ne, m, c)[: ne - 1]], axis=0)[:ne]
+    g = dCc[:, None, :]
+    dca = Sa * g
+    dza = Sa * (ca - Cc[:, None, :]) * g
+    dcb = Sb * g
+    dzb = Sb * (cb - Cc[:, None, :]) * g
+    out = {k: np.zeros((n, c)) for k in ("dCa", "dCb", "dZa", "dZb")}
+    out["dCa"][: ne * m] = dca.reshape(ne * m, c)
+    out["dZa"][: ne * m] = dza.reshape(ne * m, c)
+    # stream-b rows of block i feed entry i + 1
+    if ne > 1:
+        out["dCb"][: (ne - 1) * m] = dcb[1:].reshape((ne - 1) * m, c)
+        out["dZb"][: (ne - 1) * m] = dzb[1:].reshape((ne - 1) * m, c)
+    out["dBa"] = dza.sum(axis=0)
+    out["dBb"] = dzb.sum(axis=0)
+    if prev_Cb is not None and ne > 0:
+        out["dprev_Cb"] = dcb[0]
+        out["dprev_Zb"] = dzb[0]
+    return out
+
+
+def compress_pool_backward(C, Z, B, m_prime: int, dCc):
+    """Gradients of compress_pool: dC, dZ [n, c] and dB [m', c]."""
+    C, dCc = _f64(C), _f64(dCc)
+    n, c = C.shape
+    ne = n // m_prime
+    S = compress_weights_pool(Z, B, m_prime)                  # [ne, m', c]
+    Cc = compress_pool(C, Z, B, m_prime)
+    cb = C[: ne * m_prime].reshape(ne, m_prime, c)
+    g = dCc[:, None, :]
+    dC = np.zeros((n, c))
+    dZ = np.zeros((n, c))
+    dC[: ne * m_prime] = (S * g).reshape(-1, c)
+    dz = S * (cb - Cc[:, None, :]) * g
+    dZ[: ne * m_prime] = dz.reshape(-1, c)
+    return {"dC": dC, "dZ": dZ, "dB": dz.sum(axis=0)}
+
+
+# --------------------------------------------------------------------------
 # Heterogeneous decode cache ([P3] section 7.6, "Inference KV Cache")
 # --------------------------------------------------------------------------
 

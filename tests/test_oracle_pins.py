@@ -766,3 +766,108 @@ def test_decode_state_is_fixed_size():
         assert st.state_rows() <= nw + 2 * (mp - 1)
         assert len(cs.window) <= nw and len(cs.tail) < 4
     assert len(st.entries) == 300 // mp and len(cs.Ccomp) == 300 // 4
+
+
+# ---------------------------------------------------------- backward pass ----
+
+def _fd(f, x, h=1e-6):
+    """Central differences of the scalar f at every element of x (in place)."""
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = x[i]
+        x[i] = old + h
+        fp = f()
+        x[i] = old - h
+        fm = f()
+        x[i] = old
+        g[i] = (fp - fm) / (2 * h)
+    return g
+
+
+def _csa_case(seed=31, n=14, c=5, nh=3, m=2, k=3, nw=4):
+    r = _rng(seed)
+    q = r.normal(size=(n, nh, c))
+    Cc = r.normal(size=(n // m, c))
+    raw = r.normal(size=(n, c))
+    sink = r.normal(size=nh)
+    idx = np.stack([O.topk_select(r.normal(size=n // m), O.visible_entries(t, m), k) for t in range(n)])
+    g = r.normal(size=(n, nh, c))
+    return q, Cc, raw, sink, idx, g, m, nw
+
+
+def test_attend_backward_matches_finite_differences():
+    q, Cc, raw, sink, idx, g, m, nw = _csa_case()
+    n = q.shape[0]
+    t = np.arange(n)
+    f = lambda: float((O.csa_attend(q, Cc, idx, raw, 0, sink, t, nw, 0.7, m) * g).sum())
+    dq, dC, dR, ds = O.csa_attend_backward(q, Cc, idx, raw, 0, sink, t, nw, 0.7, g, m)
+    for got, x in ((dq, q), (dC, Cc), (dR, raw), (ds, sink)):
+        want = _fd(f, x)
+        assert np.abs(got - want).max() < 1e-6 * max(1.0, np.abs(want).max()), np.abs(got - want).max()
+
+
+def test_attend_backward_matches_torch_autograd():
+    # an independent dense formulation (one masked score matrix per query
+    # with a sink column), differentiated by torch in float64
+    q, Cc, raw, sink, idx, g, m, nw = _csa_case(seed=32, n=20, c=6, nh=2, m=4, k=2, nw=5)
+    n, nh, c = q.shape
+    tq, tC, tR, ts = (torch.tensor(x, requires_grad=True) for x in (q, Cc, raw, sink))
+    outs = []
+    for t in range(n):
+        keep_c = torch.zeros(Cc.shape[0], dtype=torch.bool)
+        for s in idx[t]:
+            if s >= 0:
+                keep_c[int(s)] = True
+        keep_r = torch.tensor([(t - nw < p <= t) for p in range(n)])
+        E = torch.cat([tC, tR])
+        keep = torch.cat([keep_c, keep_r])
+        logits = 0.3 * tq[t] @ E.T
+        logits = torch.where(keep[None, :], logits, torch.tensor(-float("inf"), dtype=torch.float64))
+        full = torch.cat([logits, ts[:, None]], dim=1)
+        p = torch.softmax(full, dim=1)[:, :-1]
+        outs.append(p @ E)
+    (torch.stack(outs) * torch.tensor(g)).sum().backward()
+    dq, dC, dR, ds = O.csa_attend_backward(q, Cc, idx, raw, 0, sink, np.arange(n), nw, 0.3, g, m)
+    for got, want in ((dq, tq.grad), (dC, tC.grad), (dR, tR.grad), (ds, ts.grad)):
+        assert np.abs(got - want.numpy()).max() < 1e-12
+
+
+def test_hca_backward_is_the_all_selected_case():
+    r = _rng(33)
+    n, c, nh, mp, nw = 24, 4, 2, 4, 6
+    q, Cc, raw = r.normal(size=(n, nh, c)), r.normal(size=(n // mp, c)), r.normal(size=(n, c))
+    sink, g = r.normal(size=nh), r.normal(size=(n, nh, c))
+    t = np.arange(n)
+    f = lambda: float((O.hca_attend(q, Cc, raw, 0, sink, t, mp, nw, 0.5) * g).sum())
+    dq, dC, dR, ds = O.hca_attend_backward(q, Cc, raw, 0, sink, t, mp, nw, 0.5, g)
+    for got, x in ((dq, q), (dC, Cc), (dR, raw), (ds, sink)):
+        want = _fd(f, x)
+        assert np.abs(got - want).max() < 1e-6 * max(1.0, np.abs(want).max())
+
+
+def test_compress_backward_matches_finite_differences():
+    r = _rng(34)
+    n, c, m = 11, 3, 2                     # a ragged tail row
+    Ca, Cb, Za, Zb = (r.normal(size=(n, c)) for _ in range(4))
+    Ba, Bb = 0.3 * r.normal(size=(m, c)), 0.3 * r.normal(size=(m, c))
+    pC, pZ = r.normal(size=(m, c)), r.normal(size=(m, c))
+    g = r.normal(size=(n // m, c))
+    for prev in (False, True):
+        kw = dict(prev_Cb=pC, prev_Zb=pZ) if prev else {}
+        f = lambda: float((O.compress_overlap(Ca, Cb, Za, Zb, Ba, Bb, m, **kw) * g).sum())
+        got = O.compress_overlap_backward(Ca, Cb, Za, Zb, Ba, Bb, m, g, **kw)
+        pairs = [("dCa", Ca), ("dCb", Cb), ("dZa", Za), ("dZb", Zb), ("dBa", Ba), ("dBb", Bb)]
+        if prev:
+            pairs += [("dprev_Cb", pC), ("dprev_Zb", pZ)]
+        for key, x in pairs:
+            want = _fd(f, x)
+            assert np.abs(got[key] - want).max() < 1e-6, (prev, key)
+    C, Z = r.normal(size=(n, c)), r.normal(size=(n, c))
+    B = 0.3 * r.normal(size=(4, c))
+    g = r.normal(size=(n // 4, c))
+    f = lambda: float((O.compress_pool(C, Z, B, 4) * g).sum())
+    got = O.compress_pool_backward(C, Z, B, 4, g)
+    for key, x in (("dC", C), ("dZ", Z), ("dB", B)):
+        assert np.abs(got[key] - _fd(f, x)).max() < 1e-6, key
