@@ -376,6 +376,127 @@ int hca_layer(const void* C, const void* Z, const void* B, const void* q, const 
 size_t hca_layer_workspace_size(int64_t b, int64_t n, int64_t n_h, int64_t c, int64_t m_prime,
                                 int64_t n_win, int dtype);
 
+/* ------------------------------------------------------------------------
+ * Heterogeneous decode cache (AirCoding "deepseek-paper-analysis" section
+ * 7.6, Inference KV Cache) for one CSA layer and one HCA layer, batched over
+ * requests of different lengths.
+ *
+ * Classical cache: a pool of blocks in one device array; block j starts at
+ * blocks + j * csa_paged_block_bytes().  A block covers L = lcm(m, m')
+ * tokens and holds, in bf16, [L/m][c] CSA entries, [L/m][c_I] indexer keys
+ * and [L/m'][c] HCA entries, in that order (m = 4, m' = 128: 32, 32 and 1;
+ * 41 KiB at c = 512, c_I = 128).  CSA entry s of a request lives in block
+ * block_table[req][s / (L/m)], at slot s % (L/m); HCA entry s in block
+ * block_table[req][s / (L/m')].  The caller owns the table
+ * ([requests][bt_stride] int32, device) and fills it from a block pool
+ * (csa_block_pool_*): block floor(t / L) must be in place before token t is
+ * appended.  Block ids are clamped into [0, n_blocks) before use.
+ *
+ * State cache: csa_paged_state_bytes() per request, fixed whatever the
+ * request's length: the CSA window ring [n_win][c] (rows C^a at slot
+ * t % n_win), the open CSA block [4][m][c] (C^a, C^b, Z^a, Z^b at slot
+ * t % m), the previous block's [2][m][c] (C^b, Z^b), the same two for the
+ * indexer-key streams with c_I, the HCA window ring [n_win][c] (rows C) and
+ * the open HCA block [2][m'][c] (C, Z).  Request r's state starts at
+ * state + r * csa_paged_state_bytes(); its contents are private to the
+ * library; it needs no initialisation (every word is written before it is
+ * read), so a slot can be reused for a new request as it is.
+ *
+ * Batches: row i of a call is request req_slot[i] (req_slot NULL: request
+ * i), whose newest token is at position pos[i] (int64, device).  Queries
+ * are one per row, at pos[i].  n_comp_max / n_hca_max bound every row's
+ * completed entries ((pos+1)/m, (pos+1)/m'); rows are clamped to them.
+ * dtype must be CSA_BF16; c and c_I multiples of 8; L/m a power of two of
+ * at least 32 and L/m' a power of two; c_I * L/m a multiple of c.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of one classical-cache block, and of one request's state (0 for
+ * sizes without a layout). */
+size_t csa_paged_block_bytes(int64_t c, int64_t c_I, int64_t m, int64_t m_prime);
+size_t csa_paged_state_bytes(int64_t c, int64_t c_I, int64_t m, int64_t m_prime, int64_t n_win);
+
+/*
+ * csa_paged_append -- add each row's newest token (position pos[i]) to its
+ * request: the token's rows of the CSA streams (Ca, Cb, Za, Zb [b][c]), the
+ * indexer-key streams (ICa, ICb, IZa, IZb [b][c_I]) and the HCA streams
+ * (C_h, Z_h [b][c]) go into the state cache; when position pos[i] completes
+ * a CSA block ((pos+1) % m == 0) the overlapped compressor (biases Ba, Bb
+ * [m][c] and IBa, IBb [m][c_I]; block -1 padded) writes CSA entry and
+ * indexer key (pos+1)/m - 1 into the request's block, and when it completes
+ * an HCA block ((pos+1) % m' == 0) the pooling compressor (bias B_h [m'][c])
+ * writes HCA entry (pos+1)/m' - 1.  Positions must be appended in order,
+ * 0, 1, 2, ... per request.  All tensors 16-byte aligned.
+ * Errors: CSA_EINVAL for NULL or misaligned pointers and sizes < 1;
+ * CSA_ENOTSUP for other dtypes or geometries without a layout.
+ */
+int csa_paged_append(void* state, void* blocks, int64_t n_blocks, const int32_t* block_table, int64_t bt_stride,
+                     const int32_t* req_slot, const int64_t* pos, int64_t b, const void* Ca, const void* Cb,
+                     const void* Za, const void* Zb, const void* ICa, const void* ICb, const void* IZa,
+                     const void* IZb, const void* C_h, const void* Z_h, const void* Ba, const void* Bb,
+                     const void* IBa, const void* IBb, const void* B_h, int64_t c, int64_t c_I, int64_t m,
+                     int64_t m_prime, int64_t n_win, int dtype, void* stream);
+
+/*
+ * csa_paged_index_topk -- csa_index_topk for one query per row (qI
+ * [b][n_hI][c_I], w [b][n_hI]) at position pos[i], over the request's
+ * (pos+1)/m indexer keys in its blocks.  idx [b][k] holds entry numbers s
+ * (ascending, -1 padded), as csa_paged_attend takes them.  Workspace:
+ * csa_index_topk_workspace_size(b, 1, n_comp_max, k) bytes, 256-byte
+ * aligned.  n_hI in {32, 64, 128}, c_I in {64, 128}.
+ * Errors: as csa_index_topk; CSA_EINVAL if n_comp_max exceeds the entries
+ * bt_stride blocks hold.
+ */
+int csa_paged_index_topk(const void* qI, const float* w, const void* blocks, int64_t n_blocks,
+                         const int32_t* block_table, int64_t bt_stride, const int32_t* req_slot, const int64_t* pos,
+                         int64_t b, int64_t n_comp_max, int64_t n_hI, int64_t c_I, int64_t c, int64_t m,
+                         int64_t m_prime, int64_t k, int dtype, int32_t* idx, float* score, void* workspace,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * csa_paged_attend -- csa_attend for one query per row (q [b][n_h][c]) at
+ * position pos[i]: the selected CSA entries (idx [b][k], entry numbers;
+ * indices outside [0, (pos+1)/m) skipped) from the request's blocks plus the
+ * window rows of positions max(0, pos-n_win+1) .. pos from its CSA window
+ * ring, one softmax with the sink.  out [b][n_h][c].  c = 512, n_h a
+ * multiple of 64, k <= 2048.  Workspace: csa_paged_attend_workspace_size()
+ * bytes (0: none).
+ */
+int csa_paged_attend(const void* q, const void* blocks, int64_t n_blocks, const int32_t* block_table,
+                     int64_t bt_stride, const int32_t* req_slot, const int64_t* pos, const int32_t* idx,
+                     const void* state, const float* sink, int64_t b, int64_t n_comp_max, int64_t n_h, int64_t c,
+                     int64_t c_I, int64_t k, int64_t m, int64_t m_prime, int64_t n_win, float scale, int dtype,
+                     void* workspace, size_t ws_bytes, void* out, void* stream);
+size_t csa_paged_attend_workspace_size(int64_t b, int64_t n_h, int64_t k, int64_t n_win);
+
+/*
+ * hca_paged_attend -- hca_attend for one query per row at position pos[i]:
+ * every completed HCA entry ((pos+1)/m') of the request's blocks plus the
+ * window from its HCA window ring.  As csa_paged_attend otherwise.
+ */
+int hca_paged_attend(const void* q, const void* blocks, int64_t n_blocks, const int32_t* block_table,
+                     int64_t bt_stride, const int32_t* req_slot, const int64_t* pos, const void* state,
+                     const float* sink, int64_t b, int64_t n_hca_max, int64_t n_h, int64_t c, int64_t c_I, int64_t m,
+                     int64_t m_prime, int64_t n_win, float scale, int dtype, void* workspace, size_t ws_bytes,
+                     void* out, void* stream);
+size_t hca_paged_attend_workspace_size(int64_t b, int64_t n_h, int64_t n_hca_max, int64_t n_win);
+
+/*
+ * Block pool (host memory only): hands out the ids 0 .. n_blocks-1 of one
+ * device block array and takes them back; thread-safe.
+ *  csa_block_pool_create   NULL if n_blocks < 1 or out of host memory
+ *  csa_block_pool_alloc    n ids into ids[] (host array); CSA_ENOSPC, with
+ *                          nothing taken, if fewer than n are free
+ *  csa_block_pool_release  CSA_EINVAL, with nothing released, if an id is
+ *                          not allocated or appears twice
+ *  csa_block_pool_available  free ids (-1 for a NULL pool)
+ */
+typedef struct csa_block_pool csa_block_pool;
+csa_block_pool* csa_block_pool_create(int64_t n_blocks);
+void csa_block_pool_destroy(csa_block_pool* pool);
+int csa_block_pool_alloc(csa_block_pool* pool, int64_t n, int32_t* ids);
+int csa_block_pool_release(csa_block_pool* pool, int64_t n, const int32_t* ids);
+int64_t csa_block_pool_available(csa_block_pool* pool);
+
 #ifdef __cplusplus
 }
 #endif

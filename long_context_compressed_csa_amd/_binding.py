@@ -51,6 +51,23 @@ SIGNATURES = {
     "hca_attend_workspace_size": (_sz, [_i64] * 8 + [_int]),
     "hca_layer": (_int, [_vp] * 6 + [_i64] * 6 + [_f32, _int, _vp, _vp, _sz, _vp, _vp]),
     "hca_layer_workspace_size": (_sz, [_i64] * 6 + [_int]),
+    "csa_paged_block_bytes": (_sz, [_i64] * 4),
+    "csa_paged_state_bytes": (_sz, [_i64] * 5),
+    "csa_paged_append": (_int, [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _i64] + [_vp] * 15 + [_i64] * 5
+                         + [_int, _vp]),
+    "csa_paged_index_topk": (_int, [_vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp] + [_i64] * 8
+                             + [_int, _vp, _vp, _vp, _sz, _vp]),
+    "csa_paged_attend": (_int, [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp] + [_i64] * 9
+                         + [_f32, _int, _vp, _sz, _vp, _vp]),
+    "csa_paged_attend_workspace_size": (_sz, [_i64] * 4),
+    "hca_paged_attend": (_int, [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp] + [_i64] * 8
+                         + [_f32, _int, _vp, _sz, _vp, _vp]),
+    "hca_paged_attend_workspace_size": (_sz, [_i64] * 4),
+    "csa_block_pool_create": (_vp, [_i64]),
+    "csa_block_pool_destroy": (None, [_vp]),
+    "csa_block_pool_alloc": (_int, [_vp, _i64, _vp]),
+    "csa_block_pool_release": (_int, [_vp, _i64, _vp]),
+    "csa_block_pool_available": (_i64, [_vp]),
 }
 
 
@@ -378,3 +395,137 @@ def hca_layer(C, Z, B, q, kv_raw, sink, m_prime, n_win, scale=None, Ccomp=None, 
                        0 if workspace is None else workspace.numel(), _ptr(out), _stream(stream))
     _check(rc, "hca_layer")
     return Ccomp, out
+
+
+# ----------------------------------------------- heterogeneous decode cache --
+
+class BlockPool:
+    """The library's host-side block allocator (csa_block_pool_*)."""
+
+    def __init__(self, n_blocks):
+        self._lib = load_library()
+        self._p = self._lib.csa_block_pool_create(int(n_blocks))
+        if not self._p:
+            raise CsaError(-1, "csa_block_pool_create")
+
+    def alloc(self, n):
+        ids = (ctypes.c_int32 * max(1, n))()
+        _check(self._lib.csa_block_pool_alloc(self._p, n, ids), "csa_block_pool_alloc")
+        return list(ids)[:n]
+
+    def release(self, ids):
+        arr = (ctypes.c_int32 * max(1, len(ids)))(*ids)
+        _check(self._lib.csa_block_pool_release(self._p, len(ids), arr), "csa_block_pool_release")
+
+    def available(self):
+        return self._lib.csa_block_pool_available(self._p)
+
+    def close(self):
+        if self._p:
+            self._lib.csa_block_pool_destroy(self._p)
+            self._p = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class PagedCache:
+    """Device arrays of the heterogeneous decode cache: the block pool array
+    and one state per request slot (their layouts are the library's).
+    Argument marshalling only; the caller fills `table` [slots, bt_stride]
+    int32 from a BlockPool."""
+
+    def __init__(self, n_blocks, slots, bt_stride, c=512, c_I=128, m=4, m_prime=128, n_win=128,
+                 device="cuda"):
+        lib = load_library()
+        self.c, self.c_I, self.m, self.m_prime, self.n_win = c, c_I, m, m_prime, n_win
+        self.block_bytes = lib.csa_paged_block_bytes(c, c_I, m, m_prime)
+        self.state_bytes = lib.csa_paged_state_bytes(c, c_I, m, m_prime, n_win)
+        if not self.block_bytes or not self.state_bytes:
+            raise CsaError(-2, "paged cache geometry")
+        self.n_blocks, self.slots, self.bt_stride = n_blocks, slots, bt_stride
+        self.blocks = torch.empty(n_blocks * self.block_bytes // 2, dtype=torch.bfloat16, device=device)
+        self.state = torch.empty(slots * self.state_bytes // 2, dtype=torch.bfloat16, device=device)
+        self.table = torch.zeros((slots, bt_stride), dtype=torch.int32, device=device)
+
+
+def csa_paged_append(cache, pos, tok, biases, req_slot=None, stream=None):
+    """tok: dict of [b, c] / [b, c_I] bf16 rows Ca, Cb, Za, Zb, ICa, ICb, IZa,
+    IZb, C_h, Z_h; biases: Ba, Bb [m, c], IBa, IBb [m, c_I], B_h [m', c];
+    pos [b] int64 (positions of the tokens)."""
+    if pos.dtype != torch.int64:
+        raise ValueError("pos must be int64")
+    if req_slot is not None and req_slot.dtype != torch.int32:
+        raise ValueError("req_slot must be int32")
+    b = pos.shape[0]
+    lib = load_library()
+    rc = lib.csa_paged_append(_ptr(cache.state), _ptr(cache.blocks), cache.n_blocks, _ptr(cache.table),
+                              cache.bt_stride, _ptr(req_slot), _ptr(pos), b,
+                              *(_ptr(tok[x]) for x in ("Ca", "Cb", "Za", "Zb", "ICa", "ICb", "IZa", "IZb", "C_h", "Z_h")),
+                              *(_ptr(biases[x]) for x in ("Ba", "Bb", "IBa", "IBb", "B_h")),
+                              cache.c, cache.c_I, cache.m, cache.m_prime, cache.n_win, CSA_BF16, _stream(stream))
+    _check(rc, "csa_paged_append")
+
+
+def csa_paged_index_topk(cache, qI, w, pos, n_comp_max, k, req_slot=None, score=False, idx=None, workspace=None,
+                         stream=None):
+    """qI [b, n_hI, c_I] bf16, w [b, n_hI] f32; returns idx [b, k] int32
+    (entry numbers) and the scores when score=True."""
+    b, nh, cI = qI.shape
+    lib = load_library()
+    need = lib.csa_index_topk_workspace_size(b, 1, n_comp_max, k)
+    if workspace is None:
+        workspace = _workspace(max(need, 256), qI.device)
+    if idx is None:
+        idx = torch.empty((b, k), dtype=torch.int32, device=qI.device)
+    sc = torch.empty((b, k), dtype=torch.float32, device=qI.device) if score else None
+    rc = lib.csa_paged_index_topk(_ptr(qI), _f32c(w, "w"), _ptr(cache.blocks), cache.n_blocks, _ptr(cache.table),
+                                  cache.bt_stride, _ptr(req_slot), _ptr(pos), b, n_comp_max, nh, cI, cache.c,
+                                  cache.m, cache.m_prime, k, _dtype(qI, qI), _ptr(idx), _ptr(sc), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    _check(rc, "csa_paged_index_topk")
+    return (idx, sc) if score else idx
+
+
+def csa_paged_attend(cache, q, idx, sink, pos, n_comp_max, scale=None, req_slot=None, out=None, workspace=None,
+                     stream=None):
+    """q [b, n_h, c] bf16, idx [b, k] int32; returns out [b, n_h, c]."""
+    b, n_h, c = q.shape
+    k = idx.shape[1]
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    lib = load_library()
+    need = lib.csa_paged_attend_workspace_size(b, n_h, k, cache.n_win)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.csa_paged_attend(_ptr(q), _ptr(cache.blocks), cache.n_blocks, _ptr(cache.table), cache.bt_stride,
+                              _ptr(req_slot), _ptr(pos), _ptr(idx), _ptr(cache.state), _f32c(sink, "sink"), b,
+                              n_comp_max, n_h, c, cache.c_I, k, cache.m, cache.m_prime, cache.n_win, scale,
+                              _dtype(q, q), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                              _ptr(out), _stream(stream))
+    _check(rc, "csa_paged_attend")
+    return out
+
+
+def hca_paged_attend(cache, q, sink, pos, n_hca_max, scale=None, req_slot=None, out=None, workspace=None,
+                     stream=None):
+    """q [b, n_h, c] bf16; returns out [b, n_h, c]."""
+    b, n_h, c = q.shape
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    lib = load_library()
+    need = lib.hca_paged_attend_workspace_size(b, n_h, n_hca_max, cache.n_win)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.hca_paged_attend(_ptr(q), _ptr(cache.blocks), cache.n_blocks, _ptr(cache.table), cache.bt_stride,
+                              _ptr(req_slot), _ptr(pos), _ptr(cache.state), _f32c(sink, "sink"), b, n_hca_max, n_h,
+                              c, cache.c_I, cache.m, cache.m_prime, cache.n_win, scale, _dtype(q, q),
+                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _ptr(out),
+                              _stream(stream))
+    _check(rc, "hca_paged_attend")
+    return out

@@ -390,4 +390,193 @@ int hca_layer(const void* C, const void* Z, const void* B, const void* q, const 
                                      ne, n_h, c, 0, m_prime, n_win, scale, dtype, workspace, out, st));
 }
 
+// ---------------------------------------------------------------------------
+// Heterogeneous decode cache (paged)
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+struct PagedGeom {
+  int64_t L, e1, e2;        // tokens per block, CSA entries and HCA entries per block
+  int64_t blk_elems;        // bf16 elements per block
+  int l1, l2;               // log2 of e1, e2
+};
+
+int ilog2_exact(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return (int64_t(1) << l) == x ? l : -1;
+}
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b) { const int64_t t = a % b; a = b; b = t; }
+  return a;
+}
+
+// Geometry of the block layout [e1][c] CSA entries, [e1][c_I] keys, [e2][c]
+// HCA entries; CSA_ENOTSUP unless e1 and e2 are powers of two, e1 a
+// multiple of 32 (a key tile never spans two blocks) and every array starts
+// on a whole c-element row.
+int paged_geom(int64_t c, int64_t cI, int64_t m, int64_t mp, PagedGeom* g) {
+  if (c < 8 || cI < 8 || m < 1 || mp < 1 || c % 8 || cI % 8) return CSA_EINVAL;
+  if (m > (int64_t(1) << 20) || mp > (int64_t(1) << 20)) return CSA_ENOTSUP;
+  g->L = m / gcd64(m, mp) * mp;
+  g->e1 = g->L / m;
+  g->e2 = g->L / mp;
+  g->l1 = ilog2_exact(g->e1);
+  g->l2 = ilog2_exact(g->e2);
+  if (g->l1 < 5 || g->l2 < 0) return CSA_ENOTSUP;
+  if ((g->e1 * cI) % c != 0) return CSA_ENOTSUP;
+  g->blk_elems = g->e1 * (c + cI) + g->e2 * c;
+  return CSA_OK;
+}
+
+csa::Rows paged_rows(const int32_t* table, int64_t bt_stride, const int32_t* slot, const PagedGeom& g,
+                     int64_t n_blocks, int64_t off, int lg) {
+  return csa::Rows{0, table, slot, bt_stride, g.blk_elems, off, n_blocks, lg};
+}
+
+int check_paged_common(const void* blocks, int64_t n_blocks, const int32_t* table, int64_t bt_stride,
+                       const int64_t* pos, int64_t b, int dtype) {
+  if (dtype != CSA_BF16) return CSA_ENOTSUP;
+  if (!blocks || !table || !pos || b < 1 || n_blocks < 1 || bt_stride < 1) return CSA_EINVAL;
+  if (!aligned(blocks, 16) || !aligned(table, 4) || !aligned(pos, 8)) return CSA_EINVAL;
+  if (b > 2147483647LL || n_blocks > 2147483647LL) return CSA_ENOTSUP;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t csa_paged_block_bytes(int64_t c, int64_t c_I, int64_t m, int64_t m_prime) {
+  PagedGeom g;
+  if (paged_geom(c, c_I, m, m_prime, &g) != CSA_OK) return 0;
+  return (size_t)g.blk_elems * 2;
+}
+
+size_t csa_paged_state_bytes(int64_t c, int64_t c_I, int64_t m, int64_t m_prime, int64_t n_win) {
+  if (c < 8 || c_I < 8 || m < 1 || m_prime < 1 || n_win < 1 || c % 8 || c_I % 8) return 0;
+  return (size_t)csa::paged_state_layout(c, c_I, m, m_prime, n_win).stride * 2;
+}
+
+int csa_paged_append(void* state, void* blocks, int64_t n_blocks, const int32_t* block_table, int64_t bt_stride,
+                     const int32_t* req_slot, const int64_t* pos, int64_t b, const void* Ca, const void* Cb,
+                     const void* Za, const void* Zb, const void* ICa, const void* ICb, const void* IZa,
+                     const void* IZb, const void* C_h, const void* Z_h, const void* Ba, const void* Bb,
+                     const void* IBa, const void* IBb, const void* B_h, int64_t c, int64_t c_I, int64_t m,
+                     int64_t m_prime, int64_t n_win, int dtype, void* stream) {
+  int rc = check_paged_common(blocks, n_blocks, block_table, bt_stride, pos, b, dtype);
+  if (rc != CSA_OK) return rc;
+  PagedGeom g;
+  rc = paged_geom(c, c_I, m, m_prime, &g);
+  if (rc != CSA_OK) return rc;
+  if (!state || n_win < 1 || !aligned(state, 16) || !aligned(req_slot, 4)) return CSA_EINVAL;
+  const void* tok[10] = {Ca, Cb, Za, Zb, ICa, ICb, IZa, IZb, C_h, Z_h};
+  const void* bias[5] = {Ba, Bb, IBa, IBb, B_h};
+  for (const void* p : tok)
+    if (!p || !aligned(p, 16)) return CSA_EINVAL;
+  for (const void* p : bias)
+    if (!p || !aligned(p, 16)) return CSA_EINVAL;
+  if (c > 2048 || c_I > 2048 || n_win > (int64_t(1) << 20)) return CSA_ENOTSUP;
+  const csa::PagedState L = csa::paged_state_layout(c, c_I, m, m_prime, n_win);
+  const csa::Rows er = paged_rows(block_table, bt_stride, req_slot, g, n_blocks, 0, g.l1);
+  const csa::Rows kr = paged_rows(block_table, bt_stride, req_slot, g, n_blocks, g.e1 * c, g.l1);
+  const csa::Rows hr = paged_rows(block_table, bt_stride, req_slot, g, n_blocks, g.e1 * (c + c_I), g.l2);
+  return launched(csa::launch_paged_append(state, L, blocks, er, kr, hr, pos, b, tok, bias, (hipStream_t)stream));
+}
+
+int csa_paged_index_topk(const void* qI, const float* w, const void* blocks, int64_t n_blocks,
+                         const int32_t* block_table, int64_t bt_stride, const int32_t* req_slot, const int64_t* pos,
+                         int64_t b, int64_t n_comp_max, int64_t n_hI, int64_t c_I, int64_t c, int64_t m,
+                         int64_t m_prime, int64_t k, int dtype, int32_t* idx, float* score, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  int rc = check_paged_common(blocks, n_blocks, block_table, bt_stride, pos, b, dtype);
+  if (rc != CSA_OK) return rc;
+  PagedGeom g;
+  rc = paged_geom(c, c_I, m, m_prime, &g);
+  if (rc != CSA_OK) return rc;
+  if (!qI || !w || !idx || !workspace || n_comp_max < 0 || n_hI < 1 || k < 1) return CSA_EINVAL;
+  if (!aligned(qI, 16) || !aligned(w, 4) || !aligned(idx, 4) || !aligned(score, 4) || !aligned(req_slot, 4) ||
+      !aligned(workspace, 256))
+    return CSA_EINVAL;
+  if (n_comp_max > bt_stride * g.e1) return CSA_EINVAL;   // more entries than the table's blocks hold
+  if (!csa::index_topk_paged_supported(n_hI, c_I) || !csa::index_topk_supported(n_comp_max, k)) return CSA_ENOTSUP;
+  if (b > 65535) return CSA_ENOTSUP;
+  if (ws_bytes < csa::index_topk_workspace_bytes(b, 1, n_comp_max, k)) return CSA_ENOSPC;
+  const csa::Rows kr = paged_rows(block_table, bt_stride, req_slot, g, n_blocks, g.e1 * c, g.l1);
+  return launched(csa::launch_index_topk_paged(qI, w, blocks, kr, pos, b, n_comp_max, n_hI, c_I, m, k, idx, score,
+                                               workspace, (hipStream_t)stream));
+}
+
+size_t csa_paged_attend_workspace_size(int64_t b, int64_t n_h, int64_t k, int64_t n_win) {
+  if (b < 1 || n_h < 64 || n_h % 64 || k < 0 || n_win < 1) return 0;
+  return csa::attend_paged_workspace_bytes(0, b, n_h, k + n_win);
+}
+
+size_t hca_paged_attend_workspace_size(int64_t b, int64_t n_h, int64_t n_hca_max, int64_t n_win) {
+  if (b < 1 || n_h < 64 || n_h % 64 || n_hca_max < 0 || n_win < 1) return 0;
+  return csa::attend_paged_workspace_bytes(1, b, n_h, n_hca_max + n_win);
+}
+
+}  // extern "C"
+
+namespace {
+
+int paged_attend_common(int dense, const void* q, const void* blocks, int64_t n_blocks, const int32_t* block_table,
+                        int64_t bt_stride, const int32_t* req_slot, const int64_t* pos, const int32_t* idx,
+                        const void* state, const float* sink, int64_t b, int64_t n_max, int64_t n_h, int64_t c,
+                        int64_t c_I, int64_t k, int64_t m, int64_t m_prime, int64_t n_win, float scale, int dtype,
+                        void* workspace, size_t ws_bytes, void* out, void* stream) {
+  int rc = check_paged_common(blocks, n_blocks, block_table, bt_stride, pos, b, dtype);
+  if (rc != CSA_OK) return rc;
+  PagedGeom g;
+  rc = paged_geom(c, c_I, m, m_prime, &g);
+  if (rc != CSA_OK) return rc;
+  if (!q || !state || !sink || !out || (!dense && !idx) || n_win < 1 || n_h < 1 || n_max < 0 || (!dense && k < 0))
+    return CSA_EINVAL;
+  if (!isfinite(scale) || !(scale > 0.f)) return CSA_EINVAL;
+  if (!aligned(q, 16) || !aligned(state, 16) || !aligned(out, 16) || !aligned(sink, 4) || !aligned(idx, 4) ||
+      !aligned(req_slot, 4))
+    return CSA_EINVAL;
+  if (n_max > bt_stride * (dense ? g.e2 : g.e1)) return CSA_EINVAL;
+  // the MFMA path only: c = 512, 64-head groups, at most 2048 selected entries
+  if (c != 512 || n_h % 64 != 0 || (!dense && k > 2048) || b > 65535 || n_h > 65535) return CSA_ENOTSUP;
+  const size_t need = csa::attend_paged_workspace_bytes(dense, b, n_h, (dense ? n_max : k) + n_win);
+  if (need > 0 && (!workspace || !aligned(workspace, 256))) return CSA_EINVAL;
+  if (ws_bytes < need) return CSA_ENOSPC;
+  const csa::PagedState L = csa::paged_state_layout(c, c_I, m, m_prime, n_win);
+  const csa::Rows er = dense ? paged_rows(block_table, bt_stride, req_slot, g, n_blocks, g.e1 * (c + c_I), g.l2)
+                             : paged_rows(block_table, bt_stride, req_slot, g, n_blocks, 0, g.l1);
+  const uint16_t* win = (const uint16_t*)state + (dense ? L.hca_win : L.csa_win);
+  return launched(csa::launch_attend_paged(dense, q, blocks, er, idx, win, L.stride, n_win, pos, sink, b, n_max, n_h,
+                                           k, dense ? m_prime : m, n_win, scale, workspace, out,
+                                           (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_paged_attend(const void* q, const void* blocks, int64_t n_blocks, const int32_t* block_table,
+                     int64_t bt_stride, const int32_t* req_slot, const int64_t* pos, const int32_t* idx,
+                     const void* state, const float* sink, int64_t b, int64_t n_comp_max, int64_t n_h, int64_t c,
+                     int64_t c_I, int64_t k, int64_t m, int64_t m_prime, int64_t n_win, float scale, int dtype,
+                     void* workspace, size_t ws_bytes, void* out, void* stream) {
+  return paged_attend_common(0, q, blocks, n_blocks, block_table, bt_stride, req_slot, pos, idx, state, sink, b,
+                             n_comp_max, n_h, c, c_I, k, m, m_prime, n_win, scale, dtype, workspace, ws_bytes, out,
+                             stream);
+}
+
+int hca_paged_attend(const void* q, const void* blocks, int64_t n_blocks, const int32_t* block_table,
+                     int64_t bt_stride, const int32_t* req_slot, const int64_t* pos, const void* state,
+                     const float* sink, int64_t b, int64_t n_hca_max, int64_t n_h, int64_t c, int64_t c_I, int64_t m,
+                     int64_t m_prime, int64_t n_win, float scale, int dtype, void* workspace, size_t ws_bytes,
+                     void* out, void* stream) {
+  return paged_attend_common(1, q, blocks, n_blocks, block_table, bt_stride, req_slot, pos, nullptr, state, sink, b,
+                             n_hca_max, n_h, c, c_I, 0, m, m_prime, n_win, scale, dtype, workspace, ws_bytes, out,
+                             stream);
+}
+
 }  // extern "C"

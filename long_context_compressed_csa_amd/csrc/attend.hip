@@ -197,13 +197,18 @@ struct AttnSmem {
   int32_t gen;                                   // restart generation (see the softmax note)
 };
 
-template <int DENSE, int G>
+// PG = 1 (paged decode cache): each batch row has its own position pos[b]
+// (t0 is unused), compressed entries are located through the block table of
+// `er`, and the window rows live in a ring of `ring` slots per request (row
+// for position p at slot p % ring of kv_raw + req(b) * rbs).
+template <int DENSE, int G, int PG>
 __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Ccomp, int64_t cbs,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ kv_raw, int64_t rbs,
-    int64_t raw_pos0, const float* __restrict__ sink, int64_t n_q, int64_t t0, int64_t n_comp,
+    int64_t raw_pos0, const float* __restrict__ sink, int64_t n_q, int64_t t0_arg, int64_t n_comp,
     int n_h, int64_t k, int64_t m, int64_t n_win, float scale, int nsplit,
-    float* __restrict__ part_o, float* __restrict__ part_ml, bf16_t* __restrict__ out) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, bf16_t* __restrict__ out,
+    Rows er, int64_t ring, const int64_t* __restrict__ pos) {
   constexpr int NW = 2 * G;        // waves per workgroup
   constexpr int R = kT / NW;       // gathered rows per wave and tile
   __shared__ AttnSmem<DENSE, G> sm;
@@ -223,6 +228,7 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   const int hg = blockIdx.y / nsplit;
   const int split = blockIdx.y % nsplit;
   const int64_t bi = blockIdx.z;
+  const int64_t t0 = PG ? pos[bi] : t0_arg;
   const int64_t r0 = grp * G;
   const int64_t rlast = (r0 + G - 1 < n_q) ? r0 + G - 1 : n_q - 1;
   const int64_t rq = r0 + qw;
@@ -274,6 +280,12 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
       mk[u] = __builtin_amdgcn_ballot_w64(sv[u] >= 0 && sv[u] < vis);
       if (l == 0) sm.cnt[u][wave] = __popcll(mk[u]);
     }
+    if (PG) {
+      // a selected entry becomes its row number in the block pool
+#pragma unroll
+      for (int u = 0; u < NR; ++u)
+        if ((mk[u] >> l) & 1) sv[u] = (int32_t)(er.at(bi, sv[u], kC) / kC);
+    }
     __syncthreads();
     const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
     int64_t base = 0;
@@ -302,8 +314,8 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
     if (t_q < t_last) exW_abs = nsel + (t_last - wlo);       // union ends one row later
   }
 
-  const bf16_t* cbase = Ccomp + bi * cbs;
-  const bf16_t* rbase = kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
+  const bf16_t* cbase = PG ? Ccomp : Ccomp + bi * cbs;
+  const bf16_t* rbase = PG ? kv_raw + er.req(bi) * rbs : kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
   // Gather tile ti into a buffer.  Lane l (< 16) resolves the address of
   // tile row l (rows past the split's end repeat its first entry, weight 0);
   // wave w loads rows w, w+NW, ... with the row base broadcast to scalar
@@ -333,7 +345,16 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
       asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(selj) : "v"(a));
     }
     const int e = j < nseli ? selj : j - nseli;
-    const bf16_t* p = (j < nseli ? cbase : rbase) + (int64_t)e * kC + 8 * g4;
+    const bf16_t* p;
+    if (PG) {
+      // compressed: pool row (CSA lists hold pool rows already; HCA looks
+      // the block up); window: ring slot of the row's position
+      const int64_t off = j < nseli ? (DENSE ? er.at(bi, e, kC) : (int64_t)e * kC)
+                                    : ((wlo + e) % ring) * (int64_t)kC;
+      p = (j < nseli ? cbase : rbase) + off + 8 * g4;
+    } else {
+      p = (j < nseli ? cbase : rbase) + (int64_t)e * kC + 8 * g4;
+    }
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       const int b = wave_u + rr * NW;
@@ -703,16 +724,17 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
     // instance of the kernel spills and is no faster)
     const int G = dense ? 2 : 1;
     dim3 grid((unsigned)((n_q + G - 1) / G), (unsigned)((n_h / kHG) * ns), (unsigned)b);
+    const Rows none = dense_rows(cbs);
     if (dense)
-      hipLaunchKernelGGL((attend_mfma_c512<1, 2>), grid, dim3(256), 0, st, (const bf16_t*)q,
+      hipLaunchKernelGGL((attend_mfma_c512<1, 2, 0>), grid, dim3(256), 0, st, (const bf16_t*)q,
                          (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
                          n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
-                         (bf16_t*)out);
+                         (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr);
     else
-      hipLaunchKernelGGL((attend_mfma_c512<0, 1>), grid, dim3(128), 0, st, (const bf16_t*)q,
+      hipLaunchKernelGGL((attend_mfma_c512<0, 1, 0>), grid, dim3(128), 0, st, (const bf16_t*)q,
                          (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
                          n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
-                         (bf16_t*)out);
+                         (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr);
     if (ns > 1)
       hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q), (unsigned)n_h), dim3(128), 0, st,
                          part_o, part_ml, sink, (int)n_h, ns, (bf16_t*)out);
@@ -727,6 +749,49 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
     hipLaunchKernelGGL((attend_generic<float>), grid, dim3(256), 0, st, (const float*)q,
                        (const float*)Ccomp, cbs, idx, (const float*)kv_raw, rbs, raw_pos0, sink, n_q,
                        t0, n_comp, (int)n_h, (int)c, k, m, n_win, scale, dense, (float*)out);
+  return hipGetLastError();
+}
+
+// Paged decode: one query per batch row at its own position, entries via
+// the block table, window rows from the request's ring.  bf16, c = 512,
+// 64-head groups (the caller checked).
+size_t attend_paged_workspace_bytes(int dense, int64_t b, int64_t n_h, int64_t nmax) {
+  const int ns = attend_nsplit(b, 1, n_h, nmax);
+  if (ns == 1) return 0;
+  const int64_t slots = b * (n_h / kHG) * ns;
+  return ((((size_t)slots * kHG * kC * 4) + 255) & ~(size_t)255) + (size_t)slots * kHG * 2 * 4;
+}
+
+hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const Rows& er, const int32_t* idx,
+                               const void* state, int64_t state_elems, int64_t ring, const int64_t* pos,
+                               const float* sink, int64_t b, int64_t n_comp_max, int64_t n_h, int64_t k, int64_t m,
+                               int64_t n_win, float scale, void* ws, void* out, hipStream_t st) {
+  if (b == 0) return hipSuccess;
+  const int64_t nmax = (dense ? n_comp_max : k) + n_win;
+  const int ns = attend_nsplit(b, 1, n_h, nmax);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (ns > 1) {
+    const int64_t slots = b * (n_h / kHG) * ns;
+    const size_t osz = ((size_t)slots * kHG * kC * 4 + 255) & ~(size_t)255;
+    part_o = (float*)ws;
+    part_ml = (float*)((unsigned char*)ws + osz);
+  }
+  const int G = dense ? 2 : 1;
+  dim3 grid(1u, (unsigned)((n_h / kHG) * ns), (unsigned)b);
+  if (dense)
+    hipLaunchKernelGGL((attend_mfma_c512<1, 2, 1>), grid, dim3(128 * G), 0, st, (const bf16_t*)q,
+                       (const bf16_t*)pool, (int64_t)0, idx, (const bf16_t*)state, state_elems, (int64_t)0, sink,
+                       (int64_t)1, (int64_t)0, n_comp_max, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
+                       (bf16_t*)out, er, ring, pos);
+  else
+    hipLaunchKernelGGL((attend_mfma_c512<0, 1, 1>), grid, dim3(128 * G), 0, st, (const bf16_t*)q,
+                       (const bf16_t*)pool, (int64_t)0, idx, (const bf16_t*)state, state_elems, (int64_t)0, sink,
+                       (int64_t)1, (int64_t)0, n_comp_max, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
+                       (bf16_t*)out, er, ring, pos);
+  if (ns > 1)
+    hipLaunchKernelGGL(attend_combine, dim3((unsigned)b, (unsigned)n_h), dim3(128), 0, st, part_o, part_ml, sink,
+                       (int)n_h, ns, (bf16_t*)out);
   return hipGetLastError();
 }
 

@@ -112,4 +112,35 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 
+// Position of query row r of batch row s: t0 + r for one block of
+// consecutive queries shared by the batch, or pos[s] + r when every batch row
+// carries a position of its own (variable-length batched decode).
+struct QPos {
+  int64_t t0;
+  const int64_t* pos;
+  __device__ __forceinline__ int64_t at(int64_t s, int64_t r) const { return (pos ? pos[s] : t0) + r; }
+};
+
+// Where row i of one cached array (compressed entries, indexer keys, HCA
+// entries) of batch row s lives.  Dense: at s * bstride + i * rowlen
+// elements.  Paged: row i sits in block table[req(s)][i >> pb_log2] (clamped
+// into [0, n_blocks)), at off + (i & (per_block - 1)) * rowlen elements from
+// that block's start; req(s) maps a batch row to its request slot.
+struct Rows {
+  int64_t bstride;
+  const int32_t* table;
+  const int32_t* slot;
+  int64_t table_stride, blk_elems, off, n_blocks;
+  int pb_log2;
+  __device__ __forceinline__ int64_t req(int64_t s) const { return slot ? (int64_t)slot[s] : s; }
+  __device__ __forceinline__ int64_t at(int64_t s, int64_t i, int64_t rowlen) const {
+    if (table == nullptr) return s * bstride + i * rowlen;
+    int64_t b = table[req(s) * table_stride + (i >> pb_log2)];
+    b = b < 0 ? 0 : (b >= n_blocks ? n_blocks - 1 : b);
+    return b * blk_elems + off + (i & ((1 << pb_log2) - 1)) * rowlen;
+  }
+};
+
+inline Rows dense_rows(int64_t bstride) { return Rows{bstride, nullptr, nullptr, 0, 0, 0, 1, 0}; }
+
 }  // namespace csa

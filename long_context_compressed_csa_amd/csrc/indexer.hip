@@ -423,7 +423,7 @@ template <> struct ScoreOps<fp8_t> {
 template <int NHB, int KS, int D, typename E, int SBK>
 __global__ __launch_bounds__(256) void index_scores_stream(
     const E* __restrict__ qI, const float* __restrict__ w, const E* __restrict__ KI,
-    int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
+    Rows kr, int64_t n_q, QPos qp, int64_t n_comp, int64_t m,
     float* __restrict__ scores, uint32_t* __restrict__ gmax, int64_t ld_gmax) {
   typedef ScoreOps<E> Ops;
   constexpr int CI = KS * 16;
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   const int l = threadIdx.x & 63;
   const int64_t qrow = blockIdx.x;
   const int64_t bi = blockIdx.z;
-  int64_t vis = (t0 + qrow + 1) / m;
+  int64_t vis = (qp.at(bi, qrow) + 1) / m;
   if (vis > n_comp) vis = n_comp;
   // The row's keys are dealt to the gridDim.y workgroups in 128-key chunks,
   // round robin (chunk c goes to workgroup c % gridDim.y), so that the
@@ -473,7 +473,6 @@ __global__ __launch_bounds__(256) void index_scores_stream(
   // enough workgroups)
   const int ntiles = first >= c1 ? 0 : (int)((c1 - first + kstep - 1) / kstep);
 
-  const E* kbase = KI + bi * comp_bs;
   const int64_t lastkey = c1 - 1;
   // DMA: instruction i, lane l fills LDS chunk 64 i + l of the tile = chunk
   // l % NCH of row i * KPI + l / NCH, from source chunk (l % NCH) ^ f(row)
@@ -490,10 +489,13 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     kb = kb < lastkey ? kb : lastkey;
     const int room = (int)(lastkey - kb < 32 ? lastkey - kb : 32);
     const uint32_t lds = (uint32_t)(uintptr_t)&ring[wave][slot][0];
+    // the tile's rows kb .. kb + room lie in one block when paged (blocks
+    // hold a multiple of 32 keys, and kb is a multiple of 32 or the last key)
+    const E* tb = KI + kr.at(bi, kb, CI);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int r = i * KPI + l / NCH;
-      const E* src = kbase + kb * CI + (r <= room ? src_off[i] : room * CI + (src_off[i] - r * CI));
+      const E* src = tb + (r <= room ? src_off[i] : room * CI + (src_off[i] - r * CI));
       dma_chunk16(src, lds + 1024 * i);
     }
   };
@@ -1255,7 +1257,7 @@ __global__ __launch_bounds__(256) void topk_stage(
     int from_scores, int final_stage, const float* __restrict__ scores, int64_t ld_scores,
     const uint32_t* __restrict__ kin, const int32_t* __restrict__ iin, int64_t ld_in,
     uint32_t* __restrict__ kout, int32_t* __restrict__ iout, int64_t ld_out, int32_t* __restrict__ idx,
-    float* __restrict__ score_out, int64_t n_rows, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
+    float* __restrict__ score_out, int64_t n_rows, int64_t n_q, QPos qp, int64_t n_comp, int64_t m,
     int64_t k, const int64_t* __restrict__ len_in, int64_t nseg) {
   constexpr int CH = NT * R;
   constexpr int SEGS = 256 / NT;   // segments per workgroup
@@ -1269,7 +1271,7 @@ __global__ __launch_bounds__(256) void topk_stage(
   const int64_t seg = active ? gseg % nseg : 0;
   int64_t L;
   if (from_scores) {
-    L = (t0 + row % n_q + 1) / m;
+    L = (qp.at(row / n_q, row % n_q) + 1) / m;
     if (L > n_comp) L = n_comp;
   } else {
     L = len_in[row];
@@ -1417,7 +1419,7 @@ __device__ __forceinline__ uint32_t row_threshold(const uint32_t* __restrict__ s
 template <int RT>
 __global__ __launch_bounds__(256) void topk_threshold_filter(
     const float* __restrict__ scores, int64_t ld_scores, const uint32_t* __restrict__ gmax, int64_t ld_gmax,
-    int64_t G, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t k, int64_t nseg,
+    int64_t G, int64_t n_q, QPos qp, int64_t n_comp, int64_t m, int64_t k, int64_t nseg,
     uint32_t* __restrict__ kout, int32_t* __restrict__ iout, int64_t ld_out, int32_t* __restrict__ cnt) {
   constexpr int R = 32, CH = 64 * R;
   __shared__ uint32_t red[SegReduce<256>::kRedSize];
@@ -1425,7 +1427,7 @@ __global__ __launch_bounds__(256) void topk_threshold_filter(
   const int64_t row = blockIdx.x;                          // rows on x: up to 2^31 of them
   const int64_t seg = (int64_t)blockIdx.y * 4 + sub;      // at most kMergeMaxSeg / 4 groups on y
   const bool active = seg < nseg;   // a wave past the row's last segment only helps the search
-  int64_t L = (t0 + row % n_q + 1) / m;
+  int64_t L = (qp.at(row / n_q, row % n_q) + 1) / m;
   if (L > n_comp) L = n_comp;
   const int64_t base = seg * CH;
   int64_t len64 = L - base;
@@ -1567,14 +1569,14 @@ __global__ __launch_bounds__(256) void topk_merge(const uint32_t* __restrict__ k
 }
 
 // Next-stage list length per row: (nseg - 1) * k + min(k, last segment).
-__global__ void topk_next_len(int64_t n_rows, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
+__global__ void topk_next_len(int64_t n_rows, int64_t n_q, QPos qp, int64_t n_comp, int64_t m,
                               int64_t k, int64_t chunk, const int64_t* __restrict__ len_in,
                               int64_t* __restrict__ len_out) {
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= n_rows) return;
   int64_t L;
   if (len_in == nullptr) {
-    L = (t0 + row % n_q + 1) / m;
+    L = (qp.at(row / n_q, row % n_q) + 1) / m;
     if (L > n_comp) L = n_comp;
   } else {
     L = len_in[row];
@@ -1675,16 +1677,16 @@ bool index_topk_supported(int64_t n_comp, int64_t k) {
 // Streaming scoring for few queries (decode): each query's keys split over
 // many workgroups.  Writes the group maxima when gmax is given.
 template <int NHB, int KS, typename E>
-static hipError_t launch_scores_stream(const void* qI, const float* w, const void* KI, int64_t cbs, int64_t b,
-                                       int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, float* scores,
-                                       uint32_t* gmax, int64_t ld_gmax, bool* gmax_used, hipStream_t st) {
-  const int64_t vmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
+static hipError_t launch_scores_stream(const void* qI, const float* w, const void* KI, const Rows& kr, int64_t b,
+                                       int64_t n_q, QPos qp, int64_t vmax, int64_t n_comp, int64_t m,
+                                       float* scores, uint32_t* gmax, int64_t ld_gmax, bool* gmax_used,
+                                       hipStream_t st) {
   typedef StreamPolicy<(int)sizeof(E)> Pol;
   const int64_t nsplit = stream_splits(b, n_q, vmax, Pol::keys, Pol::wgs);
   dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
   hipLaunchKernelGGL((index_scores_stream<NHB, KS, Pol::ring, E, (int)Pol::keys>), grid, dim3(256), 0, st,
                      (const E*)qI, w,
-                     (const E*)KI, cbs, n_q, t0, n_comp, m, scores, gmax, ld_gmax);
+                     (const E*)KI, kr, n_q, qp, n_comp, m, scores, gmax, ld_gmax);
   *gmax_used = gmax != nullptr;
   return hipGetLastError();
 }
@@ -1709,8 +1711,8 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
       hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 0>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
                          (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, nullptr, nullptr);
   } else {
-    return launch_scores_stream<NHB, KS, bf16_t>(qI, w, KI, cbs, b, n_q, t0, n_comp, m, scores, gmax, ld_gmax,
-                                                 gmax_used, st);
+    return launch_scores_stream<NHB, KS, bf16_t>(qI, w, KI, dense_rows(cbs), b, n_q, QPos{t0, nullptr}, vmax,
+                                                 n_comp, m, scores, gmax, ld_gmax, gmax_used, st);
   }
   return hipGetLastError();
 }
@@ -1719,10 +1721,9 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
 // kernel leaves them there): the threshold path when the scorer recorded
 // group maxima, else wave segments and workgroup segments until one is left.
 static hipError_t finish_topk(const TopkLayout& L, unsigned char* W, float* scores, uint32_t* gmax,
-                              bool gmax_used, int dtype, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp,
-                              int64_t m, int64_t k, int32_t* idx, float* score, hipStream_t st) {
+                              bool gmax_used, int dtype, int64_t b, int64_t n_q, QPos t0, int64_t lmax,
+                              int64_t n_comp, int64_t m, int64_t k, int32_t* idx, float* score, hipStream_t st) {
   const int64_t rows = b * n_q;
-  int64_t lmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
   int64_t nseg = std::max<int64_t>(1, (lmax + kWaveChunk - 1) / kWaveChunk);
   // one wave per row when every list fits one segment
   if (nseg == 1) {
@@ -1813,8 +1814,9 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
       const int nhb = (int)(nh / 32), ks = (int)(cI / 16);
 #define CSA_STREAM8_CASE(A, B)                                                                          \
   if (!done && nhb == A && ks == B) {                                                                   \
-    err = launch_scores_stream<A, B, fp8_t>(qI, w, KI, cbs, b, n_q, t0, n_comp, m, scores, gmax, L.gcap, \
-                                            &gmax_used, st);                                            \
+    err = launch_scores_stream<A, B, fp8_t>(qI, w, KI, dense_rows(cbs), b, n_q, QPos{t0, nullptr},      \
+                                            std::min<int64_t>((t0 + n_q) / m, n_comp), n_comp, m, scores, \
+                                            gmax, L.gcap, &gmax_used, st);                              \
     done = true;                                                                                        \
   }
       CSA_STREAM8_CASE(1, 4) CSA_STREAM8_CASE(1, 8) CSA_STREAM8_CASE(2, 4) CSA_STREAM8_CASE(2, 8)
@@ -1865,7 +1867,8 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
     if (err != hipSuccess) return err;
     if (fused && done) return hipSuccess;
   }
-  return finish_topk(L, W, scores, gmax, gmax_used, dtype, b, n_q, t0, n_comp, m, k, idx, score, st);
+  return finish_topk(L, W, scores, gmax, gmax_used, dtype, b, n_q, QPos{t0, nullptr},
+                     std::min<int64_t>((t0 + n_q) / m, n_comp), n_comp, m, k, idx, score, st);
 }
 
 // MXFP4 queries and keys: the streaming scorer for few queries at c_I = 128
@@ -1919,7 +1922,8 @@ hipError_t launch_index_topk_mx(const void* qI, const void* qS, const float* w, 
 #undef CSA_MX_MFMA
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess || fused) return err;
-    return finish_topk(L, W, scores, gmax, false, 3, b, n_q, t0, n_comp, m, k, idx, score, st);
+    return finish_topk(L, W, scores, gmax, false, 3, b, n_q, QPos{t0, nullptr},
+                       std::min<int64_t>((t0 + n_q) / m, n_comp), n_comp, m, k, idx, score, st);
   }
   if (n_comp > 0) {
     if (mx_stream_shape(n_q, nh, cI)) {
@@ -1945,7 +1949,48 @@ hipError_t launch_index_topk_mx(const void* qI, const void* qS, const float* w, 
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  return finish_topk(L, W, scores, gmax, gmax_used, 3, b, n_q, t0, n_comp, m, k, idx, score, st);
+  return finish_topk(L, W, scores, gmax, gmax_used, 3, b, n_q, QPos{t0, nullptr},
+                     std::min<int64_t>((t0 + n_q) / m, n_comp), n_comp, m, k, idx, score, st);
+}
+
+// Paged decode: one query per batch row at its own position pos[b], keys
+// located through the block table (a block holds a multiple of 32 keys, so
+// every 32-key tile lies in one block); the streaming scorer, then the same
+// selection as csa_index_topk.  bf16 keys, 32/64/128 heads, c_I = 64 or 128.
+bool index_topk_paged_supported(int64_t nh, int64_t cI) {
+  return (nh == 32 || nh == 64 || nh == 128) && (cI == 64 || cI == 128);
+}
+
+hipError_t launch_index_topk_paged(const void* qI, const float* w, const void* pool, const Rows& kr,
+                                   const int64_t* pos, int64_t b, int64_t n_comp_max, int64_t nh, int64_t cI,
+                                   int64_t m, int64_t k, int32_t* idx, float* score, void* ws, hipStream_t st) {
+  const TopkLayout L = topk_layout(b, 1, n_comp_max, k);
+  unsigned char* W = (unsigned char*)ws;
+  float* scores = (float*)(W + L.scores);
+  uint32_t* gmax = L.gcap > 0 ? (uint32_t*)(W + L.gmax) : nullptr;
+  bool gmax_used = false;
+  hipError_t err = hipSuccess;
+  const QPos qp{0, pos};
+  if (n_comp_max > 0) {
+    const int nhb = (int)(nh / 32);
+    if (cI == 128) {
+      if (nhb == 1) err = launch_scores_stream<1, 8, bf16_t>(qI, w, pool, kr, b, 1, qp, n_comp_max, n_comp_max, m,
+                                                             scores, gmax, L.gcap, &gmax_used, st);
+      else if (nhb == 2) err = launch_scores_stream<2, 8, bf16_t>(qI, w, pool, kr, b, 1, qp, n_comp_max, n_comp_max,
+                                                                  m, scores, gmax, L.gcap, &gmax_used, st);
+      else err = launch_scores_stream<4, 8, bf16_t>(qI, w, pool, kr, b, 1, qp, n_comp_max, n_comp_max, m, scores,
+                                                    gmax, L.gcap, &gmax_used, st);
+    } else {
+      if (nhb == 1) err = launch_scores_stream<1, 4, bf16_t>(qI, w, pool, kr, b, 1, qp, n_comp_max, n_comp_max, m,
+                                                             scores, gmax, L.gcap, &gmax_used, st);
+      else if (nhb == 2) err = launch_scores_stream<2, 4, bf16_t>(qI, w, pool, kr, b, 1, qp, n_comp_max, n_comp_max,
+                                                                  m, scores, gmax, L.gcap, &gmax_used, st);
+      else err = launch_scores_stream<4, 4, bf16_t>(qI, w, pool, kr, b, 1, qp, n_comp_max, n_comp_max, m, scores,
+                                                    gmax, L.gcap, &gmax_used, st);
+    }
+    if (err != hipSuccess) return err;
+  }
+  return finish_topk(L, W, scores, gmax, gmax_used, 1, b, 1, qp, n_comp_max, n_comp_max, m, k, idx, score, st);
 }
 
 }  // namespace csa

@@ -8,6 +8,8 @@
 
 #include <algorithm>
 
+#include "common.hpp"
+
 namespace csa {
 
 hipError_t launch_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
@@ -44,5 +46,41 @@ hipError_t launch_norm_rope(const void* x, int64_t xrs, void* out, int64_t ors, 
 
 hipError_t launch_grouped_out_proj(const void* o, const void* WG, const void* WO, int64_t n, int64_t n_h, int64_t c,
                                    int64_t g, int64_t d_g, int64_t d, void* mid, void* out, hipStream_t st);
+
+// ---- heterogeneous decode cache (paged) ----
+// Per-request state cache layout (bf16 elements from the request's start).
+struct PagedState {
+  int64_t stride;                                  // elements per request (a multiple of 128)
+  int64_t csa_win, csa_open, csa_prev;             // [n_win][c], [4][m][c] (C^a, C^b, Z^a, Z^b), [2][m][c] (C^b, Z^b)
+  int64_t key_open, key_prev;                      // [4][m][c_I], [2][m][c_I]
+  int64_t hca_win, hca_open;                       // [n_win][c], [2][m'][c] (C, Z)
+  int c, c_I, m, m_prime, n_win;
+};
+inline PagedState paged_state_layout(int64_t c, int64_t cI, int64_t m, int64_t mp, int64_t n_win) {
+  PagedState L{};
+  int64_t off = 0;
+  L.csa_win = off; off += n_win * c;
+  L.csa_open = off; off += 4 * m * c;
+  L.csa_prev = off; off += 2 * m * c;
+  L.key_open = off; off += 4 * m * cI;
+  L.key_prev = off; off += 2 * m * cI;
+  L.hca_win = off; off += n_win * c;
+  L.hca_open = off; off += 2 * mp * c;
+  L.stride = (off + 127) / 128 * 128;
+  L.c = (int)c; L.c_I = (int)cI; L.m = (int)m; L.m_prime = (int)mp; L.n_win = (int)n_win;
+  return L;
+}
+hipError_t launch_paged_append(void* state, const PagedState& L, void* pool, const Rows& csa_rows,
+                               const Rows& key_rows, const Rows& hca_rows, const int64_t* pos, int64_t b,
+                               const void* const* tok, const void* const* bias, hipStream_t st);
+bool index_topk_paged_supported(int64_t nh, int64_t cI);
+hipError_t launch_index_topk_paged(const void* qI, const float* w, const void* pool, const Rows& kr,
+                                   const int64_t* pos, int64_t b, int64_t n_comp_max, int64_t nh, int64_t cI,
+                                   int64_t m, int64_t k, int32_t* idx, float* score, void* ws, hipStream_t st);
+size_t attend_paged_workspace_bytes(int dense, int64_t b, int64_t n_h, int64_t nmax);
+hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const Rows& er, const int32_t* idx,
+                               const void* state, int64_t state_elems, int64_t ring, const int64_t* pos,
+                               const float* sink, int64_t b, int64_t n_comp_max, int64_t n_h, int64_t k, int64_t m,
+                               int64_t n_win, float scale, void* ws, void* out, hipStream_t st);
 
 }  // namespace csa

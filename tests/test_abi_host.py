@@ -322,3 +322,54 @@ def test_index_topk_noalloc_rejects_before_launch(lib):
     big = dict(b=64, n_q=1, t0=262144 * 4 - 1, n_comp=262144, nh=64, cI=128, k=512, dtype=1)
     assert lib.csa_index_topk_workspace_size(64, 1, 262144, 512) > 80 * 1024 * 1024
     assert call(**big) == ENOSPC
+
+
+def test_block_pool_hands_out_and_takes_back_ids():
+    pool = B.BlockPool(5)
+    a = pool.alloc(3)
+    assert sorted(a) == [0, 1, 2] and pool.available() == 2
+    with pytest.raises(L.CsaError):
+        pool.alloc(3)                      # only 2 left: nothing taken
+    assert pool.available() == 2
+    pool.release([a[1]])
+    assert pool.alloc(1) == [a[1]]        # the last released id comes back first
+    with pytest.raises(L.CsaError):
+        pool.release([a[0], a[0]])         # listed twice: nothing released
+    with pytest.raises(L.CsaError):
+        pool.release([4])                  # never allocated
+    assert pool.available() == 2
+    pool.release(a)
+    assert pool.available() == 5
+    pool.close()
+    lib = L.load_library()
+    assert lib.csa_block_pool_create(0) is None
+    assert lib.csa_block_pool_available(None) == -1
+
+
+def test_paged_geometry_and_validation(lib):
+    # m = 4, m' = 128: 32 CSA entries, 32 keys and 1 HCA entry per block
+    assert lib.csa_paged_block_bytes(512, 128, 4, 128) == 2 * (32 * 512 + 32 * 128 + 512)
+    assert lib.csa_paged_block_bytes(512, 128, 4, 6) == 0    # 12-token blocks: 3 CSA entries, not a power of two
+    st = lib.csa_paged_state_bytes(512, 128, 4, 128, 128)
+    assert st >= 2 * (2 * 128 * 512 + 6 * 4 * 512 + 6 * 4 * 128 + 2 * 128 * 512) and st % 256 == 0
+    z = [FAKE] * 15
+    ok = dict(state=FAKE, blocks=FAKE, nb=8, table=FAKE, bts=4, slot=None, pos=FAKE, b=2)
+    def app(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.csa_paged_append(a["state"], a["blocks"], a["nb"], a["table"], a["bts"], a["slot"], a["pos"],
+                                    a["b"], *z, 512, 128, 4, 128, 128, kw.get("dtype", 1), None)
+    assert app(dtype=0) == ENOTSUP
+    assert app(state=None) == EINVAL
+    assert app(pos=FAKE + 4) == EINVAL     # int64 positions
+    assert app(nb=0) == EINVAL
+    # attention: c = 512 MFMA path only; the table must hold n_comp_max entries
+    def att(**kw):
+        a = dict(n_max=64, c=512, nh=64, k=64, dtype=1)
+        a.update(kw)
+        return lib.csa_paged_attend(FAKE, FAKE, 8, FAKE, 4, None, FAKE, FAKE, FAKE, FAKE, 2, a["n_max"], a["nh"],
+                                    a["c"], 128, a["k"], 4, 128, 128, 0.05, a["dtype"], FAKE, 1 << 30, FAKE, None)
+    assert att(c=256) == ENOTSUP
+    assert att(nh=32) == ENOTSUP
+    assert att(n_max=4 * 32 + 1) == EINVAL
+    assert att(dtype=0) == ENOTSUP
