@@ -12,5 +12,6 @@ from .csa_oracle import (  # noqa: F401  (explicit re-exports for linters)
     index_topk, attend_entries, csa_attend, hca_attend, hca_layer, csa_layer,
     CsaDecodeState, HcaDecodeState, block_geometry, default_scale, window_rows, rms_norm, rope_frequencies,
     rope, norm_rope, csa_attend_rope, grouped_out_proj, attend_entries_backward, csa_attend_backward,
-    hca_attend_backward, compress_overlap_backward, compress_pool_backward,
+    hca_attend_backward, compress_overlap_backward, compress_pool_backward, fp8_e4m3_encode, kv_fp8_encode,
+    kv_fp8_decode,
 )

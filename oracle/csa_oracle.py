@@ -234,6 +234,60 @@ def fp8_e4m3_decode(codes):
     return np.where((e == 15) & ((c & 7) == 7), np.nan, out)
 
 
+def fp8_e4m3_encode(x):
+    """E4M3 codes of finite values |x| <= 448: the nearest representable
+    value, ties to the code with an even mantissa (round to nearest even),
+    the sign kept for negative values (a negative value that rounds to 0
+    keeps its sign bit).  Brute force over the 127 non-negative finite codes
+    decoded by fp8_e4m3_decode, so the two share the format's definition."""
+    x = _f64(x)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > 448.0):
+        raise ValueError("E4M3 holds finite values up to 448")
+    grid = fp8_e4m3_decode(np.arange(127, dtype=np.uint8))          # codes 0x00..0x7E, increasing
+    a = np.abs(x).reshape(-1)
+    out = np.empty(a.shape, dtype=np.uint8)
+    for lo in range(0, a.size, 1 << 16):
+        blk = a[lo:lo + (1 << 16)]
+        d = np.abs(blk[:, None] - grid[None, :])
+        best = d.min(axis=1, keepdims=True)
+        tie = d == best
+        # among the nearest codes (at most two), the even one
+        even = tie & (np.arange(127)[None, :] % 2 == 0)
+        pick = np.where(even.any(axis=1), even.argmax(axis=1), tie.argmax(axis=1))
+        out[lo:lo + blk.size] = pick
+    out = out.reshape(x.shape)
+    return np.where(np.signbit(x), out | 0x80, out).astype(np.uint8)
+
+
+def kv_fp8_encode(E, rope_dims: int = 64):
+    """Mixed-precision storage of KV entries ([P3] section 7.3, KV mixed
+    precision storage; [P1] B9: the RoPE dimensions stay BF16, the other
+    dimensions are FP8).  Readings: the RoPE dimensions are the last
+    rope_dims (the partial RoPE of [P2] section 4.5 rotates the last 64);
+    the FP8 format is E4M3 with one power-of-two scale per entry, the
+    smallest 2^e with max |x| / 2^e <= 448 (2^0 for an all-zero entry), so
+    that every entry uses the format's whole range.  E [n, c] holds the
+    values to store (the RoPE part is kept as given).
+    Returns (codes [n, c - rope_dims] uint8, rope [n, rope_dims] float64,
+    scale [n] float64)."""
+    E = _f64(E)
+    head = E[:, : E.shape[1] - rope_dims]
+    amax = np.abs(head).max(axis=1) if head.shape[1] else np.zeros(E.shape[0])
+    e = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 0.0)
+    scale = np.exp2(e)
+    # max |x| / scale may exceed 448 by rounding of log2: step up once more
+    over = np.abs(head).max(axis=1, initial=0.0) / scale > 448.0
+    scale = np.where(over, scale * 2.0, scale)
+    codes = fp8_e4m3_encode(head / scale[:, None])
+    return codes, E[:, E.shape[1] - rope_dims:].copy(), scale
+
+
+def kv_fp8_decode(codes, rope, scale):
+    """Values of entries stored by kv_fp8_encode: decoded E4M3 codes times
+    the entry's scale, then the RoPE dimensions."""
+    return np.concatenate([fp8_e4m3_decode(codes) * _f64(scale)[:, None], _f64(rope)], axis=1)
+
+
 def e2m1_decode(nibbles):
     """Values of 4-bit E2M1 codes (integer array of 0..15), float64.
 

@@ -871,3 +871,46 @@ def test_compress_backward_matches_finite_differences():
     got = O.compress_pool_backward(C, Z, B, 4, g)
     for key, x in (("dC", C), ("dZ", Z), ("dB", B)):
         assert np.abs(got[key] - _fd(f, x)).max() < 1e-6, key
+
+
+# ------------------------------------------------------ FP8 KV storage ----
+
+def test_e4m3_encoder_round_trips_and_rounds_to_nearest_even():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.fp8_e4m3_decode(codes)
+    finite = ~np.isnan(vals)
+    # every finite code decodes and encodes back to itself (-0 keeps its sign)
+    assert np.array_equal(O.fp8_e4m3_encode(vals[finite]), codes[finite])
+    # midpoints between neighbours go to the even code; just off them, to the nearer
+    grid = O.fp8_e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (grid[1:] + grid[:-1]) / 2
+    got = O.fp8_e4m3_encode(mids)
+    lo = np.arange(126)
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))
+    assert np.array_equal(O.fp8_e4m3_encode(mids - 1e-9 * grid[1:]), lo)
+    assert np.array_equal(O.fp8_e4m3_encode(mids + 1e-9 * grid[1:]), lo + 1)
+    # torch's own E4M3 conversion (round to nearest even) agrees on random values
+    x = np.random.default_rng(5).normal(size=4000) * 40
+    x = np.clip(x, -448, 448)
+    want = torch.tensor(x, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp8_e4m3_encode(x.astype(np.float32).astype(np.float64)), want)
+
+
+def test_kv_fp8_storage():
+    r = _rng(40)
+    E = r.normal(size=(50, 96)) * np.exp2(r.integers(-12, 8, size=(50, 1)))
+    E[3] = 0.0
+    codes, rope, scale = O.kv_fp8_encode(E, rope_dims=32)
+    assert codes.shape == (50, 64) and rope.shape == (50, 32)
+    # power-of-two scales that use the whole range: max |x| / scale in (224, 448]
+    assert np.all(np.log2(scale) == np.round(np.log2(scale)))
+    amax = np.abs(E[:, :64]).max(axis=1)
+    ratio = amax[amax > 0] / scale[amax > 0]
+    assert np.all((ratio > 224) & (ratio <= 448))
+    assert scale[3] == 1.0 and np.all(codes[3] == 0)
+    back = O.kv_fp8_decode(codes, rope, scale)
+    assert np.array_equal(back[:, 64:], E[:, 64:])
+    # E4M3 keeps 3 mantissa bits: relative error at most 2^-4 for normal values
+    head = E[:, :64]
+    big = np.abs(head) >= 2.0 ** -6 * scale[:, None]
+    assert np.all(np.abs(back[:, :64] - head)[big] <= 2.0 ** -4 * np.abs(head)[big])
