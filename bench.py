@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA prefill tokens/s @n=8192 (% MFMA roofline); 1M-ctx decode µs/step"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3
 
 
 def _events(torch):
@@ -192,14 +193,17 @@ def run_prefill(args, torch, L, synth):
     index_f8_us = timer4.avg_us("index_topk_fp8")
     del qI8, KI8
 
-    # A whole step with the FP4 indexer: the key compressor's bf16 output is
-    # encoded to MXFP4 by the library each step; the indexer queries are
-    # given as MXFP4 codes (as the bf16 step is given its bf16 queries).
+    # A whole step with the FP4 indexer: the library encodes the key
+    # compressor's bf16 output and the step's bf16 indexer queries to MXFP4
+    # inside the step, then indexes over the codes.
     def quant_keys():
         return lib.csa_quantize_mxfp4(P(KI), cI, ne, cI, 1, P(kc), cI // 2, P(ks), cI // 32, st)
 
+    def quant_queries():
+        return lib.csa_quantize_mxfp4(P(d["qI"]), cI, n * nI, cI, 1, P(qc), cI // 2, P(qs), cI // 32, st)
+
     stages4 = [("compress_main", comp_main), ("compress_index_keys", comp_index), ("quantize_keys", quant_keys),
-               ("index_topk_mxfp4", index_mx), ("attend", attend)]
+               ("quantize_queries", quant_queries), ("index_topk_mxfp4", index_mx), ("attend", attend)]
 
     def step4():
         for name, fn in stages4:
@@ -315,7 +319,7 @@ def run_prefill(args, torch, L, synth):
         "out_proj": out_proj_rec,
         "mxfp4_step": {"ms_per_step": ms4, "tokens_per_s": n / (ms4 / 1000.0),
                        "stages": [name for name, _ in stages4],
-                       "queries": "indexer queries given as MXFP4 codes"},
+                       "queries": "bf16 indexer queries and keys encoded to MXFP4 inside the step"},
         "step_tflops": (flop_attend + flop_index) / (ms * 1e-3) / 1e12,
         "inputs": d,
     }
@@ -564,6 +568,189 @@ def run_hca_decode(args, torch, L, synth):
             "n_win": nw}
 
 
+# ----------------------------------- paged decode, backward, FP8 KV, BF16 ----
+
+def _event_us(torch, fn, iters, warm=3):
+    for _ in range(warm):
+        fn()
+    a, b = _events(torch)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return 1000.0 * a.elapsed_time(b) / iters
+
+
+def _recall(torch, ref, got, n_comp):
+    """Mean over rows of the share of ref's selected entries that got also
+    selected (rows with no selection are left out)."""
+    rows = ref.shape[0]
+    mask = torch.zeros((rows, n_comp + 1), dtype=torch.bool, device=ref.device)
+    mask.scatter_(1, torch.where(ref >= 0, ref, n_comp).long(), True)
+    mask[:, n_comp] = False
+    hit = torch.gather(mask, 1, torch.where(got >= 0, got, n_comp).long()) & (got >= 0)
+    n_ref = (ref >= 0).sum(1)
+    ok = n_ref > 0
+    return float((hit.sum(1)[ok].double() / n_ref[ok].double()).mean())
+
+
+def run_paged_decode(args, torch, L, synth):
+    """1M-context decode of 8 requests through the paged heterogeneous
+    cache: per step, each request's token is appended (state update; CSA
+    entry and key on block completion), then indexer + top-k, CSA attention
+    and HCA attention; blocks are scattered over the pool."""
+    b, hist, c, cI, m, mp, nw, nh, nI, k = 8, 1 << 20, 512, 128, 4, 128, 128, 64, 64, 512
+    blocks_per_req = hist // 128 + 1
+    n_blocks = b * blocks_per_req
+    cache = L.PagedCache(n_blocks, b, blocks_per_req, c, cI, m, mp, nw, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    pv = cache.blocks.view(n_blocks, cache.block_bytes // 2)
+    pv[:, : 32 * c].normal_(0.0, 1.0 / math.sqrt(c), generator=g)
+    pv[:, 32 * c: 32 * (c + cI)].normal_(0.0, 1.0 / math.sqrt(cI), generator=g)
+    pv[:, 32 * (c + cI):].normal_(0.0, 1.0 / math.sqrt(c), generator=g)
+    cache.state.normal_(0.0, 1.0 / math.sqrt(c), generator=g)
+    perm = torch.randperm(n_blocks, device="cuda", generator=g).to(torch.int32)
+    cache.table.copy_(perm.view(b, blocks_per_req))
+    sc = lambda *s_, d=c: (torch.randn(s_, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    biases = {"Ba": sc(m, c), "Bb": sc(m, c), "IBa": sc(m, cI, d=cI), "IBb": sc(m, cI, d=cI), "B_h": sc(mp, c)}
+    steps = 4
+    toks = [{x: sc(b, c) for x in ("Ca", "Cb", "Za", "Zb", "C_h", "Z_h")} for _ in range(steps)]
+    for tk in toks:
+        tk.update({x: sc(b, cI, d=cI) for x in ("ICa", "ICb", "IZa", "IZb")})
+    q = [sc(b, nh, c) for _ in range(steps)]
+    qI = [sc(b, nI, cI, d=cI) for _ in range(steps)]
+    w = [torch.nn.functional.softplus(torch.randn((b, nI), device="cuda", generator=g)) for _ in range(steps)]
+    sink = torch.randn(nh, device="cuda", generator=g)
+    pos = [torch.full((b,), hist + i, dtype=torch.int64, device="cuda") for i in range(steps)]
+    lib = L.load_library()
+    n_comp_max = (hist + steps) // m
+    n_hca_max = (hist + steps) // mp
+    wsI = torch.empty(lib.csa_index_topk_workspace_size(b, 1, n_comp_max, k), dtype=torch.uint8, device="cuda")
+    wsA = torch.empty(max(lib.csa_paged_attend_workspace_size(b, nh, k, nw), 256), dtype=torch.uint8, device="cuda")
+    wsH = torch.empty(max(lib.hca_paged_attend_workspace_size(b, nh, n_hca_max, nw), 256), dtype=torch.uint8,
+                      device="cuda")
+    idx = torch.empty((b, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((b, nh, c), dtype=torch.bfloat16, device="cuda")
+    hout = torch.empty_like(out)
+
+    def step(i):
+        L.csa_paged_append(cache, pos[i], toks[i], biases)
+        L.csa_paged_index_topk(cache, qI[i], w[i], pos[i], n_comp_max, k, idx=idx, workspace=wsI)
+        L.csa_paged_attend(cache, q[i], idx, sink, pos[i], n_comp_max, out=out, workspace=wsA)
+        L.hca_paged_attend(cache, q[i], sink, pos[i], n_hca_max, out=hout, workspace=wsH)
+
+    for _ in range(10):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    us = _event_us(torch, lambda: [step(i) for i in range(steps)], 5, warm=0) / steps
+    key_bytes = b * (hist // m) * cI * 2
+    hca_bytes = b * (hist // mp) * c * 2
+    return {"us_per_step": us, "b": b, "history": hist, "k": k, "blocks": n_blocks,
+            "block_bytes": cache.block_bytes, "state_bytes_per_request": cache.state_bytes,
+            "stages": "append (state + compression on block completion), CSA index + top-k, CSA attention, "
+                      "HCA attention, all through the block table",
+            "hbm_bytes_per_step": key_bytes + hca_bytes + b * (k + 2 * nw) * c * 2,
+            "hbm_gbs": (key_bytes + hca_bytes + b * (k + 2 * nw) * c * 2) / (us * 1e-6) / 1e9}
+
+
+def run_backward(args, torch, L, synth):
+    """CSA attention backward at the prefill head shape (n = 4096, k = 512,
+    window 128, 64 heads, c = 512) and the overlapped compressor backward at
+    n = 65536, c = 512."""
+    n, m, k, nw = 4096, 4, 512, 128
+    d = synth.prefill_inputs(n=n, device="cuda", k=k)
+    nh, c = d["params"]["n_h"], d["params"]["c"]
+    Cc = L.csa_compress(*(d[x] for x in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m)
+    KI = L.csa_compress(*(d[x] for x in ("ICa", "ICb", "IZa", "IZb", "IBa", "IBb")), m)
+    idx = L.csa_index_topk(d["qI"], d["w"], KI, 0, m, k)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    dout = (torch.randn(d["q"].shape, device="cuda", generator=g) / math.sqrt(c)).to(torch.bfloat16)
+    lib = L.load_library()
+    ws = torch.empty(lib.csa_attend_backward_workspace_size(1, n, nh, c, k, nw), dtype=torch.uint8, device="cuda")
+    f = dict(dtype=torch.float32, device="cuda")
+    grads = (torch.empty((1, n, nh, c), **f), torch.empty((1, n // m, c), **f), torch.empty((1, n, c), **f),
+             torch.empty(nh, **f))
+    call = lambda: L.csa_attend_backward(d["q"], Cc, idx, d["kv_raw"], d["sink"], dout, 0, m, nw, d["scale"],
+                                         grads=grads, workspace=ws)
+    us = _event_us(torch, call, 3, warm=1)
+    sel, win = prefill_pairs(n, m, k, nw)
+    flop = (sel + win) * nh * 10 * c      # q.e, g.e, dq, and both roles of de: 10 c flops per (pair, head)
+    res = {"csa_attend_backward": {"us": us, "n": n, "k": k, "flop": flop, "tflops": flop / (us * 1e-6) / 1e12,
+                                   "valu_fp32_frac": flop / (us * 1e-6) / 1e12 / PEAK_FP32_TFLOPS,
+                                   "bound": "alu (float32 vector arithmetic)"}}
+    del d, dout, ws, grads
+    cd = synth.compress_inputs(True, device="cuda")
+    nc, cc, mc = synth.COMPRESS["n"], synth.COMPRESS["c"], cd["m"]
+    dCc = torch.randn((1, nc // mc, cc), device="cuda", generator=g)
+    callc = lambda: L.csa_compress_backward(cd["Ca"], cd["Cb"], cd["Za"], cd["Zb"], cd["Ba"], cd["Bb"], mc, dCc)
+    usc = _event_us(torch, callc, 5, warm=2)
+    nbytes = 4 * nc * cc * 2 + (nc // mc) * cc * 4 + 4 * nc * cc * 4
+    res["compress_backward"] = {"us": usc, "n": nc, "bytes": nbytes, "gbs": nbytes / (usc * 1e-6) / 1e9,
+                                "hbm_frac": nbytes / (usc * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return res
+
+
+def run_fp8kv_and_bf16_scores(args, torch, L, synth):
+    """Attention over FP8-stored entries (prefill n = 8192; decode 8 x 2^18
+    entries) and the selection on BF16 index scores: time and recall against
+    the float32-score selection."""
+    res = {}
+    n, m, k, nw = 8192, 4, 512, 128
+    d = synth.prefill_inputs(device="cuda")
+    Cc = L.csa_compress(*(d[x] for x in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m)
+    KI = L.csa_compress(*(d[x] for x in ("ICa", "ICb", "IZa", "IZb", "IBa", "IBb")), m)
+    idx = L.csa_index_topk(d["qI"], d["w"], KI, 0, m, k)
+    idx16 = L.csa_index_topk(d["qI"], d["w"], KI, 0, m, k, bf16_scores=True)
+    lib = L.load_library()
+    wsI = torch.empty(lib.csa_index_topk_workspace_size(1, n, n // m, k), dtype=torch.uint8, device="cuda")
+    us32 = _event_us(torch, lambda: L.csa_index_topk(d["qI"], d["w"], KI, 0, m, k, idx=idx, workspace=wsI), 10)
+    us16 = _event_us(torch, lambda: L.csa_index_topk(d["qI"], d["w"], KI, 0, m, k, idx=idx16, workspace=wsI,
+                                                     bf16_scores=True), 10)
+    res["bf16_scores_prefill"] = {"recall": _recall(torch, idx[0], idx16[0], n // m), "index_topk_us": us16,
+                                  "index_topk_fp32_scores_us": us32}
+    codes, rope, scale = L.csa_quantize_kv_fp8(Cc)
+    out = torch.empty_like(d["q"])
+    wsF = torch.empty(lib.csa_attend_fp8kv_workspace_size(1, n, 0, n // m, 64, 512, k, m, nw), dtype=torch.uint8,
+                      device="cuda")
+    usq = _event_us(torch, lambda: L.csa_quantize_kv_fp8(Cc), 10)
+    usa = _event_us(torch, lambda: L.csa_attend_fp8kv(d["q"], codes, rope, scale, idx, d["kv_raw"], d["sink"], 0, m,
+                                                       nw, out=out, workspace=wsF), 5)
+    res["fp8_kv_prefill"] = {"attend_us": usa, "quantize_entries_us": usq, "entries": n // m,
+                             "entry_bytes": 448 + 128 + 4,
+                             "note": "every entry decoded to bf16 in the workspace, then the bf16 MFMA attention"}
+    del d, out, wsF, wsI
+    dd = synth.decode_inputs(device="cuda")
+    p = dd["params"]
+    b, hist, nh, c, cI, nI = p["b"], p["history"], p["n_h"], p["c"], p["c_I"], p["n_hI"]
+    ne = dd["n_comp0"]
+    t = hist
+    cap = dd["Ccomp"].shape[1]
+    i32 = L.csa_index_topk(dd["qI"][0], dd["w"][0], dd["KIcomp"], t, m, k, n_comp=ne)
+    i16 = L.csa_index_topk(dd["qI"][0], dd["w"][0], dd["KIcomp"], t, m, k, n_comp=ne, bf16_scores=True)
+    res["bf16_scores_decode"] = {"recall": _recall(torch, i32[:, 0], i16[:, 0], ne), "b": b, "candidates": ne}
+    codes, rope, scale = L.csa_quantize_kv_fp8(dd["Ccomp"])
+    dout = torch.empty_like(dd["q"][0])
+    need = lib.csa_attend_fp8kv_workspace_size(b, 1, t, ne, nh, c, k, m, nw)
+    wsD = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    win = dd["window"]
+    usd = _event_us(torch, lambda: L.csa_attend_fp8kv(dd["q"][0], codes, rope, scale, i32, win, dd["sink"], t, m, nw,
+                                                       raw_pos0=dd["window_pos0"], n_comp=ne, out=dout, workspace=wsD),
+                    20, warm=5)
+    wsB = torch.empty(max(lib.csa_attend_workspace_size(b, 1, t, ne, nh, c, k, m, nw, 1), 256), dtype=torch.uint8,
+                      device="cuda")
+    usb = _event_us(torch, lambda: L.csa_attend(dd["q"][0], dd["Ccomp"], i32, win, dd["sink"], t, m, nw,
+                                                 raw_pos0=dd["window_pos0"], n_comp=ne, out=dout, workspace=wsB),
+                    20, warm=5)
+    res["fp8_kv_decode"] = {"attend_us": usd, "bf16_attend_us": usb, "b": b, "entries": ne,
+                            "cache_bytes": b * ne * (448 + 128 + 4), "bf16_cache_bytes": b * ne * c * 2,
+                            "note": "the selected entries decoded to bf16, then the bf16 decode attention"}
+    return res
+
+
 # ------------------------------------------------------------ compressor ----
 
 def run_compress(args, torch, L, synth):
@@ -743,7 +930,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps before the timed ones; about 50 prefill steps bring the GPU clocks to "
                          "their steady state (dispatch times fall by about a fifth over the first 25)")
-    ap.add_argument("--only", choices=["prefill", "decode", "hca", "compress"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "hca", "compress", "next"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=8192)
     ap.add_argument("--decode-reps", type=int, default=10)
@@ -789,6 +976,16 @@ def main(argv=None):
     if a.only in (None, "compress"):
         print("[bench] compress", file=sys.stderr, flush=True)
         extras["compressor"] = run_compress(a, torch, L, synth)
+    if a.only in (None, "next") and not a.core:
+        print("[bench] paged decode", file=sys.stderr, flush=True)
+        extras["paged_decode_1m"] = run_paged_decode(a, torch, L, synth)
+        torch.cuda.empty_cache()
+        print("[bench] backward", file=sys.stderr, flush=True)
+        extras["backward"] = run_backward(a, torch, L, synth)
+        torch.cuda.empty_cache()
+        print("[bench] fp8 kv, bf16 scores", file=sys.stderr, flush=True)
+        extras.update(run_fp8kv_and_bf16_scores(a, torch, L, synth))
+        torch.cuda.empty_cache()
     if pre is None or a.core:
         if pre is not None:
             extras["prefill"] = {k: v for k, v in pre.items() if k != "inputs"}

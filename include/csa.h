@@ -46,9 +46,10 @@ extern "C" {
 
 /* CSA_FP8 is the 8-bit E4M3 floating-point format of the OCP 8-bit floating
  * point specification (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
- * no infinities; 0x7F and 0xFF are NaN; largest finite value 448).  Only
- * csa_index_topk accepts it (for qI and KIcomp: the low-precision indexer);
- * every other entry point returns CSA_ENOTSUP for it. */
+ * no infinities; 0x7F and 0xFF are NaN; largest finite value 448).  As a
+ * dtype only csa_index_topk accepts it (for qI and KIcomp: the
+ * low-precision indexer); the FP8 KV entries have entry points of their own
+ * (csa_quantize_kv_fp8, csa_attend_fp8kv). */
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8 = 2 } csa_dtype;
 
 enum {
@@ -124,6 +125,14 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
  * pointers, or n_comp > (t0 + n_q)/m (entries that no query could have
  * completed).  CSA_ENOSPC if ws_bytes is too small.
  */
+/* CSA_SCORE_BF16 may be OR-ed into csa_index_topk's dtype when it is CSA_F32
+ * or CSA_BF16 (also for csa_index_topk_noalloc): every score is rounded to
+ * bfloat16 (nearest even) before the selection, the BF16 index scores of
+ * AirCoding "deepseek-paper-analysis" section 7.8 (the pages report 99.7%
+ * recall against float32 scores).  Ties among equal rounded scores go to
+ * the lower index, as always; `score` returns the rounded values. */
+#define CSA_SCORE_BF16 0x100
+
 int csa_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride,
                    int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI,
                    int64_t c_I, int64_t m, int64_t k, int dtype, int32_t* idx, float* score,
@@ -375,6 +384,118 @@ int hca_layer(const void* C, const void* Z, const void* B, const void* q, const 
 
 size_t hca_layer_workspace_size(int64_t b, int64_t n, int64_t n_h, int64_t c, int64_t m_prime,
                                 int64_t n_win, int dtype);
+
+/* ------------------------------------------------------------------------
+ * FP8 KV entries (AirCoding "deepseek-paper-analysis" section 7.3, KV mixed
+ * precision storage; polysight "06-formulas" B9): compressed entries keep
+ * their RoPE dimensions (the last rope_dims) in BF16 and store the others
+ * as OCP E4M3 codes with one power-of-two scale per entry.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * csa_quantize_kv_fp8 -- encode `rows` entries x [rows][x_rstride] (float32
+ * or bf16, the first c values of a row): scale[i] = the smallest 2^e with
+ * max |x[i][d]| / 2^e <= 448 over the non-RoPE dims d < c - rope_dims (2^0
+ * for an all-zero row); codes[i][d] = the E4M3 code nearest to
+ * x[i][d] / scale[i] (ties to the even code, sign kept);
+ * rope[i][d] = bf16(x[i][c - rope_dims + d]).
+ *  codes [rows][codes_rstride] uint8, rope [rows][rope_rstride] bf16,
+ *  scale [rows] float32.  rope_dims and c - rope_dims multiples of 8.
+ * Errors: CSA_EINVAL for NULL pointers, rows < 1, sizes or strides out of
+ * range, misalignment; CSA_ENOTSUP for another dtype.
+ */
+int csa_quantize_kv_fp8(const void* x, int64_t x_rstride, int64_t rows, int64_t c, int64_t rope_dims, int dtype,
+                        void* codes, int64_t codes_rstride, void* rope, int64_t rope_rstride, float* scale,
+                        void* stream);
+
+/*
+ * csa_attend_fp8kv -- csa_attend (bf16 queries, window rows and output)
+ * with the compressed entries stored by csa_quantize_kv_fp8: codes
+ * [b][*][c - rope_dims], rope [b][*][rope_dims], scale [b][*], dense rows,
+ * comp_bstride entries from one sequence's first entry to the next (0 =
+ * n_comp).  The attention reads the values the stored entries stand for: it
+ * decodes the entries the call reads into bf16 rows in the workspace (every
+ * entry for a block of queries; for one query per sequence with more
+ * entries than k, only the selected ones) and attends over them.  Workspace:
+ * csa_attend_fp8kv_workspace_size() bytes, 256-byte aligned.
+ * Errors: as csa_attend; CSA_ENOTSUP for k > 2048.
+ */
+int csa_attend_fp8kv(const void* q, const void* codes, const void* rope, const float* scale, int64_t comp_bstride,
+                     const int32_t* idx, const void* kv_raw, int64_t raw_bstride, int64_t raw_pos0, const float* sink,
+                     int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c,
+                     int64_t rope_dims, int64_t k, int64_t m, int64_t n_win, float sm_scale, void* workspace,
+                     size_t ws_bytes, void* out, void* stream);
+size_t csa_attend_fp8kv_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h, int64_t c,
+                                       int64_t k, int64_t m, int64_t n_win);
+
+/* ------------------------------------------------------------------------
+ * Backward pass (training needs the layer's gradients; AirCoding
+ * "deepseek-paper-analysis" section 7.6 asks that the attention backward's
+ * reductions be deterministic: per-unit accumulation buffers summed in a
+ * fixed order, no floating-point atomics).  Gradients are float32 whatever
+ * the storage type of the inputs.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * csa_attend_backward -- gradients of csa_attend (same arguments, same entry
+ * sets) given dout = dL/dout [b, n_q, n_h, c] in the storage type:
+ *   dl_j = p_j (g . e_j - g . o),  dz_h = -p_sink (g . o),
+ *   dq = scale sum_j dl_j e_j,     de_j = p_j g + scale dl_j q
+ * (p the softmax weights, g = dout of the head, o its output; each entry is
+ * both key and value, so its gradient sums both roles over every head and
+ * every query that read it).
+ *  dq      out [b, n_q, n_h, c] float32
+ *  dCcomp  out [b, *, c] float32 (dcomp_bstride, 0 = dense): rows of entries
+ *          no query of the block selected get 0
+ *  dkv_raw out [b, n_raw, c] float32 (draw_bstride): window rows
+ *  dsink   out [n_h] float32, summed over sequences and queries
+ *  accumulate  0: write the gradients; 1: add them to dCcomp, dkv_raw and
+ *          dsink (process the queries of a long sequence in blocks, in
+ *          order; dq is always written)
+ * Each idx row must list its valid entries in ascending order without
+ * repeats (as csa_index_topk returns them).  Workspace:
+ * csa_attend_backward_workspace_size() bytes, 256-byte aligned: the
+ * per-(query, slot) contributions, 4 (k + n_win) c bytes per query plus
+ * 8 n_h (k + n_win) bytes per query.  The sums run over queries in order.
+ * Errors: as csa_attend; CSA_ENOTSUP for c > 1024 or n_h > 512.
+ */
+int csa_attend_backward(const void* q, const void* Ccomp, int64_t comp_bstride, const int32_t* idx,
+                        const void* kv_raw, int64_t raw_bstride, int64_t raw_pos0, const float* sink, const void* dout,
+                        int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c,
+                        int64_t k, int64_t m, int64_t n_win, float scale, int dtype, int accumulate, float* dq,
+                        float* dCcomp, int64_t dcomp_bstride, float* dkv_raw, int64_t draw_bstride, float* dsink,
+                        void* workspace, size_t ws_bytes, void* stream);
+size_t csa_attend_backward_workspace_size(int64_t b, int64_t n_q, int64_t n_h, int64_t c, int64_t k, int64_t n_win);
+
+/* hca_attend_backward -- the same for hca_attend (every completed entry
+ * read; workspace grows with n_comp instead of k). */
+int hca_attend_backward(const void* q, const void* Ccomp, int64_t comp_bstride, const void* kv_raw,
+                        int64_t raw_bstride, int64_t raw_pos0, const float* sink, const void* dout, int64_t b,
+                        int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c,
+                        int64_t m_prime, int64_t n_win, float scale, int dtype, int accumulate, float* dq,
+                        float* dCcomp, int64_t dcomp_bstride, float* dkv_raw, int64_t draw_bstride, float* dsink,
+                        void* workspace, size_t ws_bytes, void* stream);
+size_t hca_attend_backward_workspace_size(int64_t b, int64_t n_q, int64_t n_h, int64_t c, int64_t n_comp,
+                                          int64_t n_win);
+
+/*
+ * csa_compress_backward -- gradients of csa_compress (same inputs) given
+ * dCcomp [b, n/m, c] float32 (dense): with S the weights of entry i and
+ * Cc_i its value, every row j the entry reads gets dC_j = S_j dCcomp_i and
+ * dZ_j = S_j (C_j - Cc_i) dCcomp_i; rows no entry reads (the last block's
+ * stream-b rows, a ragged tail) get 0; dBa / dBb [m, c] sum dZ of each
+ * in-block row over entries and sequences, in order.  dCa, dCb, dZa, dZb
+ * [b, n, c] float32; dprev_Cb, dprev_Zb [b, m, c] float32, required when
+ * prev_Cb / prev_Zb are given (else may be NULL).  overlap = 0: the pooling
+ * form (Cb, Zb, Bb, dCb, dZb, dBb NULL).  Workspace:
+ * csa_compress_backward_workspace_size() bytes, 256-byte aligned.
+ */
+int csa_compress_backward(const void* Ca, const void* Cb, const void* Za, const void* Zb, const void* Ba,
+                          const void* Bb, const void* prev_Cb, const void* prev_Zb, const float* dCcomp, int64_t b,
+                          int64_t n, int64_t c, int64_t m, int overlap, int dtype, float* dCa, float* dCb, float* dZa,
+                          float* dZb, float* dBa, float* dBb, float* dprev_Cb, float* dprev_Zb, void* workspace,
+                          size_t ws_bytes, void* stream);
+size_t csa_compress_backward_workspace_size(int64_t n, int64_t c, int64_t m);
 
 /* ------------------------------------------------------------------------
  * Heterogeneous decode cache (AirCoding "deepseek-paper-analysis" section

@@ -63,6 +63,18 @@ SIGNATURES = {
     "hca_paged_attend": (_int, [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp] + [_i64] * 8
                          + [_f32, _int, _vp, _sz, _vp, _vp]),
     "hca_paged_attend_workspace_size": (_sz, [_i64] * 4),
+    "csa_quantize_kv_fp8": (_int, [_vp, _i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "csa_attend_fp8kv": (_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp] + [_i64] * 11
+                         + [_f32, _vp, _sz, _vp, _vp]),
+    "csa_attend_fp8kv_workspace_size": (_sz, [_i64] * 9),
+    "csa_attend_backward": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp] + [_i64] * 10
+                            + [_f32, _int, _int, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "csa_attend_backward_workspace_size": (_sz, [_i64] * 6),
+    "hca_attend_backward": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp] + [_i64] * 9
+                            + [_f32, _int, _int, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "hca_attend_backward_workspace_size": (_sz, [_i64] * 6),
+    "csa_compress_backward": (_int, [_vp] * 9 + [_i64] * 4 + [_int, _int] + [_vp] * 9 + [_sz, _vp]),
+    "csa_compress_backward_workspace_size": (_sz, [_i64] * 3),
     "csa_block_pool_create": (_vp, [_i64]),
     "csa_block_pool_destroy": (None, [_vp]),
     "csa_block_pool_alloc": (_int, [_vp, _i64, _vp]),
@@ -192,15 +204,19 @@ def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, m, prev_Cb=None, prev_Zb=None, out=None
     return ret
 
 
+CSA_SCORE_BF16 = 0x100
+
+
 def csa_index_topk(qI, w, KIcomp, t0, m, k, n_comp=None, score=False, idx=None,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, bf16_scores=False):
     """Indexer scores + top-k.  qI [b, n_q, n_hI, c_I]; w [b, n_q, n_hI] f32;
     KIcomp [b, cap, c_I] (first n_comp rows used).  Returns idx int32
-    [b, n_q, k] (and the scores when score=True)."""
+    [b, n_q, k] (and the scores when score=True).  bf16_scores: select on
+    scores rounded to bfloat16 (CSA_SCORE_BF16)."""
     qI, w, KIcomp = _batched(qI, 4), _batched(w, 3), _batched(KIcomp, 3)
     b, n_q, nh, cI = qI.shape
     n_comp = KIcomp.shape[1] if n_comp is None else n_comp
-    dt = _dtype(qI, KIcomp)
+    dt = _dtype(qI, KIcomp) | (CSA_SCORE_BF16 if bf16_scores else 0)
     lib = load_library()
     need = lib.csa_index_topk_workspace_size(b, n_q, n_comp, k)
     if workspace is None:
@@ -528,4 +544,139 @@ def hca_paged_attend(cache, q, sink, pos, n_hca_max, scale=None, req_slot=None, 
                               _ptr(workspace), 0 if workspace is None else workspace.numel(), _ptr(out),
                               _stream(stream))
     _check(rc, "hca_paged_attend")
+    return out
+
+
+# ------------------------------------------------------------ backward pass --
+
+def csa_attend_backward(q, Ccomp, idx, kv_raw, sink, dout, t0, m, n_win, scale=None, raw_pos0=0, n_comp=None,
+                        n_raw=None, accumulate=False, grads=None, workspace=None, stream=None):
+    """Gradients of csa_attend: returns (dq, dCcomp, dkv_raw, dsink), float32,
+    shaped like q, Ccomp, kv_raw and sink.  `grads` (that tuple) receives
+    them in place; with accumulate=True the last three are added to."""
+    q, Ccomp, idx, kv_raw, dout = (_batched(q, 4), _batched(Ccomp, 3), _batched(idx, 3), _batched(kv_raw, 3),
+                                   _batched(dout, 4))
+    return _attend_backward(False, q, Ccomp, idx, kv_raw, sink, dout, t0, m, n_win, scale, raw_pos0, n_comp, n_raw,
+                            accumulate, grads, workspace, stream)
+
+
+def hca_attend_backward(q, Ccomp, kv_raw, sink, dout, t0, m_prime, n_win, scale=None, raw_pos0=0, n_comp=None,
+                        n_raw=None, accumulate=False, grads=None, workspace=None, stream=None):
+    """Gradients of hca_attend (see csa_attend_backward)."""
+    q, Ccomp, kv_raw, dout = _batched(q, 4), _batched(Ccomp, 3), _batched(kv_raw, 3), _batched(dout, 4)
+    return _attend_backward(True, q, Ccomp, None, kv_raw, sink, dout, t0, m_prime, n_win, scale, raw_pos0, n_comp,
+                            n_raw, accumulate, grads, workspace, stream)
+
+
+def _attend_backward(dense, q, Ccomp, idx, kv_raw, sink, dout, t0, m, n_win, scale, raw_pos0, n_comp, n_raw,
+                     accumulate, grads, workspace, stream):
+    b, n_q, n_h, c = q.shape
+    n_comp = Ccomp.shape[1] if n_comp is None else n_comp
+    n_raw = kv_raw.shape[1] if n_raw is None else n_raw
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(q, Ccomp, kv_raw, dout)
+    lib = load_library()
+    k = 0 if dense else idx.shape[2]
+    need = (lib.hca_attend_backward_workspace_size(b, n_q, n_h, c, n_comp, n_win) if dense
+            else lib.csa_attend_backward_workspace_size(b, n_q, n_h, c, k, n_win))
+    if workspace is None:
+        workspace = _workspace(max(need, 256), q.device)
+    if grads is None:
+        f = dict(dtype=torch.float32, device=q.device)
+        grads = (torch.empty(q.shape, **f), torch.zeros(Ccomp.shape, **f), torch.zeros(kv_raw.shape, **f),
+                 torch.zeros(n_h, **f))
+    dq, dC, dR, ds = grads
+    for t_ in grads:
+        if t_.dtype != torch.float32:
+            raise ValueError("gradients are float32")
+    dC3, dR3 = _batched(dC, 3), _batched(dR, 3)
+    if dense:
+        rc = lib.hca_attend_backward(_ptr(q), _ptr(Ccomp), Ccomp.stride(0), _ptr(kv_raw), kv_raw.stride(0), raw_pos0,
+                                     _f32c(sink, "sink"), _ptr(dout), b, n_q, t0, n_comp, n_raw, n_h, c, m, n_win,
+                                     scale, dt, int(accumulate), _ptr(dq), _ptr(dC3), dC3.stride(0), _ptr(dR3),
+                                     dR3.stride(0), _ptr(ds), _ptr(workspace), workspace.numel(), _stream(stream))
+    else:
+        if idx.dtype != torch.int32:
+            raise ValueError("idx must be int32")
+        rc = lib.csa_attend_backward(_ptr(q), _ptr(Ccomp), Ccomp.stride(0), _ptr(idx), _ptr(kv_raw), kv_raw.stride(0),
+                                     raw_pos0, _f32c(sink, "sink"), _ptr(dout), b, n_q, t0, n_comp, n_raw, n_h, c, k,
+                                     m, n_win, scale, dt, int(accumulate), _ptr(dq), _ptr(dC3), dC3.stride(0),
+                                     _ptr(dR3), dR3.stride(0), _ptr(ds), _ptr(workspace), workspace.numel(),
+                                     _stream(stream))
+    _check(rc, "hca_attend_backward" if dense else "csa_attend_backward")
+    return grads
+
+
+def csa_compress_backward(Ca, Cb, Za, Zb, Ba, Bb, m, dCcomp, prev_Cb=None, prev_Zb=None, overlap=True,
+                          workspace=None, stream=None):
+    """Gradients of csa_compress: dict of float32 tensors dCa, dZa, dBa (and
+    dCb, dZb, dBb, plus dprev_Cb, dprev_Zb when the state is given)."""
+    Ca, Cb, Za, Zb = (_batched(x, 3) for x in (Ca, Cb, Za, Zb))
+    prev_Cb, prev_Zb = _batched(prev_Cb, 3), _batched(prev_Zb, 3)
+    dCcomp = _batched(dCcomp, 3)
+    b, n, c = Ca.shape
+    dt = _dtype(Ca, Cb, Za, Zb, Ba, Bb, prev_Cb, prev_Zb)
+    f = dict(dtype=torch.float32, device=Ca.device)
+    g = {"dCa": torch.empty((b, n, c), **f), "dZa": torch.empty((b, n, c), **f), "dBa": torch.empty((m, c), **f)}
+    if overlap:
+        g.update({"dCb": torch.empty((b, n, c), **f), "dZb": torch.empty((b, n, c), **f),
+                  "dBb": torch.empty((m, c), **f)})
+        if prev_Cb is not None:
+            g.update({"dprev_Cb": torch.empty((b, m, c), **f), "dprev_Zb": torch.empty((b, m, c), **f)})
+    lib = load_library()
+    need = lib.csa_compress_backward_workspace_size(n, c, m)
+    if workspace is None:
+        workspace = _workspace(max(need, 256), Ca.device)
+    rc = lib.csa_compress_backward(_ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(prev_Cb),
+                                   _ptr(prev_Zb), _f32c(dCcomp, "dCcomp"), b, n, c, m, 1 if overlap else 0, dt,
+                                   *(_ptr(g.get(x)) for x in ("dCa", "dCb", "dZa", "dZb", "dBa", "dBb", "dprev_Cb",
+                                                              "dprev_Zb")),
+                                   _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "csa_compress_backward")
+    return g
+
+
+# --------------------------------------------------------- FP8 KV entries --
+
+def csa_quantize_kv_fp8(x, rope_dims=64, stream=None):
+    """Encode entries x [..., c] (float32 or bf16): returns (codes [..., c - r]
+    uint8, rope [..., r] bf16, scale [...] float32)."""
+    c = x.shape[-1]
+    rows = x.numel() // c
+    lead = x.shape[:-1]
+    codes = torch.empty((*lead, c - rope_dims), dtype=torch.uint8, device=x.device)
+    rope = torch.empty((*lead, rope_dims), dtype=torch.bfloat16, device=x.device)
+    scale = torch.empty(lead, dtype=torch.float32, device=x.device)
+    lib = load_library()
+    rc = lib.csa_quantize_kv_fp8(_ptr(x), c, rows, c, rope_dims, _dtype(x, x), _ptr(codes), c - rope_dims, _ptr(rope),
+                                 rope_dims, _ptr(scale), _stream(stream))
+    _check(rc, "csa_quantize_kv_fp8")
+    return codes, rope, scale
+
+
+def csa_attend_fp8kv(q, codes, rope, scale, idx, kv_raw, sink, t0, m, n_win, sm_scale=None, raw_pos0=0, n_comp=None,
+                     n_raw=None, out=None, workspace=None, stream=None):
+    """csa_attend over FP8-stored entries (codes [b, cap, c - r], rope
+    [b, cap, r], scale [b, cap])."""
+    q, idx, kv_raw = _batched(q, 4), _batched(idx, 3), _batched(kv_raw, 3)
+    codes, rope = _batched(codes, 3), _batched(rope, 3)
+    scale = scale if scale.dim() == 2 else scale.unsqueeze(0)
+    b, n_q, n_h, c = q.shape
+    k = idx.shape[2]
+    r = rope.shape[2]
+    n_comp = codes.shape[1] if n_comp is None else n_comp
+    n_raw = kv_raw.shape[1] if n_raw is None else n_raw
+    sm_scale = 1.0 / math.sqrt(c) if sm_scale is None else sm_scale
+    if idx.dtype != torch.int32 or codes.dtype != torch.uint8 or scale.dtype != torch.float32:
+        raise ValueError("idx int32, codes uint8, scale float32")
+    lib = load_library()
+    need = lib.csa_attend_fp8kv_workspace_size(b, n_q, t0, n_comp, n_h, c, k, m, n_win)
+    if workspace is None:
+        workspace = _workspace(max(need, 256), q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.csa_attend_fp8kv(_ptr(q), _ptr(codes), _ptr(rope), _ptr(scale), codes.shape[1], _ptr(idx), _ptr(kv_raw),
+                              kv_raw.stride(0), raw_pos0, _f32c(sink, "sink"), b, n_q, t0, n_comp, n_raw, n_h, c, r, k,
+                              m, n_win, sm_scale, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream))
+    _check(rc, "csa_attend_fp8kv")
     return out

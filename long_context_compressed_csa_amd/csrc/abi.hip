@@ -122,7 +122,11 @@ namespace {
 
 int check_index_topk(const void* qI, const float* w, const void* KIcomp, int64_t comp_bstride, int64_t b,
                      int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_hI, int64_t c_I, int64_t m, int64_t k,
-                     int dtype, const int32_t* idx, const float* score) {
+                     int dtype_flags, const int32_t* idx, const float* score) {
+  // the element type, and CSA_SCORE_BF16 for float32 / bf16 queries and keys
+  const int dtype = dtype_flags & 0xff;
+  if ((dtype_flags & ~0x1ff) != 0) return CSA_ENOTSUP;
+  if ((dtype_flags & CSA_SCORE_BF16) && dtype == CSA_FP8) return CSA_ENOTSUP;
   if (!dtype_ok(dtype) && dtype != CSA_FP8) return CSA_ENOTSUP;
   if (!qI || !w || !idx) return CSA_EINVAL;
   if (n_comp > 0 && !KIcomp) return CSA_EINVAL;
@@ -577,6 +581,165 @@ int hca_paged_attend(const void* q, const void* blocks, int64_t n_blocks, const 
   return paged_attend_common(1, q, blocks, n_blocks, block_table, bt_stride, req_slot, pos, nullptr, state, sink, b,
                              n_hca_max, n_h, c, c_I, 0, m, m_prime, n_win, scale, dtype, workspace, ws_bytes, out,
                              stream);
+}
+
+// ---------------------------------------------------------------------------
+// Backward pass
+// ---------------------------------------------------------------------------
+size_t csa_attend_backward_workspace_size(int64_t b, int64_t n_q, int64_t n_h, int64_t c, int64_t k, int64_t n_win) {
+  if (b < 1 || n_q < 1 || n_h < 1 || c < 1 || k < 0 || n_win < 1) return 0;
+  return csa::attend_backward_workspace_bytes(b, n_q, n_h, c, k, n_win);
+}
+
+size_t hca_attend_backward_workspace_size(int64_t b, int64_t n_q, int64_t n_h, int64_t c, int64_t n_comp,
+                                          int64_t n_win) {
+  if (b < 1 || n_q < 1 || n_h < 1 || c < 1 || n_comp < 0 || n_win < 1) return 0;
+  return csa::attend_backward_workspace_bytes(b, n_q, n_h, c, n_comp, n_win);
+}
+
+}  // extern "C"
+
+namespace {
+
+int attend_backward_common(int dense, const void* q, const void* Ccomp, int64_t cbs, const int32_t* idx,
+                           const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink, const void* dout,
+                           int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c,
+                           int64_t k, int64_t m, int64_t n_win, float scale, int dtype, int accumulate, float* dq,
+                           float* dCcomp, int64_t dcbs, float* dkv_raw, int64_t drbs, float* dsink, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  int rc = check_attend(q, Ccomp, cbs, kv_raw, rbs, raw_pos0, sink, b, n_q, t0, n_comp, n_raw, n_h, c, m, n_win, scale,
+                        dtype, q);
+  if (rc != CSA_OK) return rc;
+  if (!dout || !dq || !dkv_raw || !dsink || (n_comp > 0 && !dCcomp) || (accumulate != 0 && accumulate != 1))
+    return CSA_EINVAL;
+  if (!dense && (k < 0 || (k > 0 && !idx))) return CSA_EINVAL;
+  const int64_t es = elem_bytes(dtype);
+  if (!aligned(dout, (uintptr_t)es) || !aligned(dq, 4) || !aligned(dCcomp, 4) || !aligned(dkv_raw, 4) ||
+      !aligned(dsink, 4) || !aligned(idx, 4) || !aligned(workspace, 256))
+    return CSA_EINVAL;
+  if (dcbs < 0 || drbs < 0 || (dcbs > 0 && dcbs < n_comp * c) || (drbs > 0 && drbs < n_raw * c)) return CSA_EINVAL;
+  if (c > 1024 || n_h > 512 || n_q > 65535 || b > 65535 || n_comp > 2147483647LL || n_raw > 2147483647LL)
+    return CSA_ENOTSUP;
+  const int64_t ks = dense ? n_comp : k;
+  if (ks + n_win > 2147483647LL) return CSA_ENOTSUP;
+  if (!workspace) return CSA_EINVAL;
+  if (ws_bytes < csa::attend_backward_workspace_bytes(b, n_q, n_h, c, ks, n_win)) return CSA_ENOSPC;
+  const int64_t cb = cbs > 0 ? cbs : n_comp * c;
+  const int64_t rb = rbs > 0 ? rbs : n_raw * c;
+  return launched(csa::launch_attend_backward(dense, q, Ccomp, cb, idx, kv_raw, rb, raw_pos0, sink, dout, b, n_q, t0,
+                                              n_comp, n_raw, n_h, c, k, m, n_win, scale, dtype, accumulate, dq, dCcomp,
+                                              dcbs > 0 ? dcbs : n_comp * c, dkv_raw, drbs > 0 ? drbs : n_raw * c,
+                                              dsink, workspace, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_attend_backward(const void* q, const void* Ccomp, int64_t comp_bstride, const int32_t* idx,
+                        const void* kv_raw, int64_t raw_bstride, int64_t raw_pos0, const float* sink, const void* dout,
+                        int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c,
+                        int64_t k, int64_t m, int64_t n_win, float scale, int dtype, int accumulate, float* dq,
+                        float* dCcomp, int64_t dcomp_bstride, float* dkv_raw, int64_t draw_bstride, float* dsink,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  return attend_backward_common(0, q, Ccomp, comp_bstride, idx, kv_raw, raw_bstride, raw_pos0, sink, dout, b, n_q, t0,
+                                n_comp, n_raw, n_h, c, k, m, n_win, scale, dtype, accumulate, dq, dCcomp,
+                                dcomp_bstride, dkv_raw, draw_bstride, dsink, workspace, ws_bytes, stream);
+}
+
+int hca_attend_backward(const void* q, const void* Ccomp, int64_t comp_bstride, const void* kv_raw,
+                        int64_t raw_bstride, int64_t raw_pos0, const float* sink, const void* dout, int64_t b,
+                        int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c,
+                        int64_t m_prime, int64_t n_win, float scale, int dtype, int accumulate, float* dq,
+                        float* dCcomp, int64_t dcomp_bstride, float* dkv_raw, int64_t draw_bstride, float* dsink,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  return attend_backward_common(1, q, Ccomp, comp_bstride, nullptr, kv_raw, raw_bstride, raw_pos0, sink, dout, b, n_q,
+                                t0, n_comp, n_raw, n_h, c, 0, m_prime, n_win, scale, dtype, accumulate, dq, dCcomp,
+                                dcomp_bstride, dkv_raw, draw_bstride, dsink, workspace, ws_bytes, stream);
+}
+
+size_t csa_compress_backward_workspace_size(int64_t n, int64_t c, int64_t m) {
+  if (n < 1 || c < 1 || m < 1) return 0;
+  return csa::compress_backward_workspace_bytes(n, c, m);
+}
+
+int csa_compress_backward(const void* Ca, const void* Cb, const void* Za, const void* Zb, const void* Ba,
+                          const void* Bb, const void* prev_Cb, const void* prev_Zb, const float* dCcomp, int64_t b,
+                          int64_t n, int64_t c, int64_t m, int overlap, int dtype, float* dCa, float* dCb, float* dZa,
+                          float* dZb, float* dBa, float* dBb, float* dprev_Cb, float* dprev_Zb, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ENOTSUP;
+  if (b < 1 || n < 1 || c < 1 || m < 1 || (overlap != 0 && overlap != 1)) return CSA_EINVAL;
+  if (!Ca || !Za || !Ba || !dCa || !dZa || !dBa || !workspace || (n / m > 0 && !dCcomp)) return CSA_EINVAL;
+  if (overlap) {
+    if (!Cb || !Zb || !Bb || !dCb || !dZb || !dBb) return CSA_EINVAL;
+    if ((prev_Cb == nullptr) != (prev_Zb == nullptr)) return CSA_EINVAL;
+    // the previous block's gradients are needed for stream b's bias
+    if (prev_Cb && (!dprev_Cb || !dprev_Zb)) return CSA_EINVAL;
+  } else if (Cb || Zb || Bb || prev_Cb || prev_Zb) {
+    return CSA_EINVAL;
+  }
+  const int64_t es = elem_bytes(dtype);
+  const void* in[] = {Ca, Cb, Za, Zb, Ba, Bb, prev_Cb, prev_Zb};
+  for (const void* p : in)
+    if (!aligned(p, (uintptr_t)es)) return CSA_EINVAL;
+  const void* outs[] = {dCcomp, dCa, dCb, dZa, dZb, dBa, dBb, dprev_Cb, dprev_Zb};
+  for (const void* p : outs)
+    if (!aligned(p, 4)) return CSA_EINVAL;
+  if (!aligned(workspace, 256)) return CSA_EINVAL;
+  if (b > 65535 || n > 2147483647LL || c > 65535) return CSA_ENOTSUP;
+  if (ws_bytes < csa::compress_backward_workspace_bytes(n, c, m)) return CSA_ENOSPC;
+  return launched(csa::launch_compress_backward(Ca, Cb, Za, Zb, Ba, Bb, prev_Cb, prev_Zb, dCcomp, b, n, c, m, overlap,
+                                                dtype, dCa, dCb, dZa, dZb, dBa, dBb, dprev_Cb, dprev_Zb, workspace,
+                                                (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// FP8 KV entries
+// ---------------------------------------------------------------------------
+int csa_quantize_kv_fp8(const void* x, int64_t x_rstride, int64_t rows, int64_t c, int64_t rope_dims, int dtype,
+                        void* codes, int64_t codes_rstride, void* rope, int64_t rope_rstride, float* scale,
+                        void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ENOTSUP;
+  if (!x || !codes || !rope || !scale || rows < 1 || c < 16) return CSA_EINVAL;
+  if (rope_dims < 8 || rope_dims % 8 || (c - rope_dims) < 8 || (c - rope_dims) % 8) return CSA_EINVAL;
+  if (x_rstride < c || codes_rstride < c - rope_dims || rope_rstride < rope_dims) return CSA_EINVAL;
+  const int64_t es = elem_bytes(dtype);
+  if (!aligned(x, (uintptr_t)es) || !aligned(rope, 2) || !aligned(scale, 4)) return CSA_EINVAL;
+  if (c > 65535 || rows > 2147483647LL * 4) return CSA_ENOTSUP;
+  return launched(csa::launch_quantize_kv_fp8(x, x_rstride, rows, c, rope_dims, dtype, codes, codes_rstride, rope,
+                                              rope_rstride, scale, (hipStream_t)stream));
+}
+
+size_t csa_attend_fp8kv_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h, int64_t c,
+                                       int64_t k, int64_t m, int64_t n_win) {
+  if (b < 1 || n_q < 1 || t0 < 0 || n_comp < 0 || n_h < 1 || c < 1 || k < 0 || m < 1 || n_win < 1) return 0;
+  return csa::attend_fp8kv_workspace_bytes(b, n_q, t0, n_comp, n_h, c, k, m, n_win);
+}
+
+int csa_attend_fp8kv(const void* q, const void* codes, const void* rope, const float* scale, int64_t comp_bstride,
+                     const int32_t* idx, const void* kv_raw, int64_t raw_bstride, int64_t raw_pos0, const float* sink,
+                     int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c,
+                     int64_t rope_dims, int64_t k, int64_t m, int64_t n_win, float sm_scale, void* workspace,
+                     size_t ws_bytes, void* out, void* stream) {
+  int rc = check_attend(q, codes, 0, kv_raw, raw_bstride, raw_pos0, sink, b, n_q, t0, n_comp, n_raw, n_h, c, m,
+                        n_win, sm_scale, CSA_BF16, out);
+  if (rc != CSA_OK) return rc;
+  if (n_comp > 0 && (!rope || !scale)) return CSA_EINVAL;
+  if (k < 0 || (k > 0 && !idx)) return CSA_EINVAL;
+  if (rope_dims < 8 || rope_dims % 8 || c - rope_dims < 8 || (c - rope_dims) % 8) return CSA_EINVAL;
+  if (comp_bstride < 0 || (comp_bstride > 0 && comp_bstride < n_comp)) return CSA_EINVAL;
+  if (!aligned(codes, 8) || !aligned(rope, 16) || !aligned(scale, 4) || !aligned(idx, 4)) return CSA_EINVAL;
+  if (n_q > 2147483647LL || b > 65535 || n_h > 65535 || k > 2048) return CSA_ENOTSUP;
+  if (!csa::attend_supported(CSA_BF16, n_h, c, k)) return CSA_ENOTSUP;
+  const size_t need = csa::attend_fp8kv_workspace_bytes(b, n_q, t0, n_comp, n_h, c, k, m, n_win);
+  if (!workspace || !aligned(workspace, 256)) return CSA_EINVAL;
+  if (ws_bytes < need) return CSA_ENOSPC;
+  const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp;
+  const int64_t rbs = raw_bstride > 0 ? raw_bstride : n_raw * c;
+  return launched(csa::launch_attend_fp8kv(q, codes, rope, scale, cbs, idx, kv_raw, rbs, raw_pos0, sink, b, n_q, t0,
+                                           n_comp, n_h, c, rope_dims, k, m, n_win, sm_scale, workspace, out,
+                                           (hipStream_t)stream));
 }
 
 }  // extern "C"

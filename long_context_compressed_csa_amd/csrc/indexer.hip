@@ -53,7 +53,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void index_scores_generic(
     const T* __restrict__ qI, const float* __restrict__ w, const T* __restrict__ KI,
     int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int nh, int cI, int64_t m,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, int sbf) {
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r = blockIdx.y;
   const int64_t bi = blockIdx.z;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void index_scores_generic(
     for (int j = 0; j < cI; ++j) d = fmaf(Elem<T>::ld(q + h * cI + j), Elem<T>::ld(key + j), d);
     tot = fmaf(wr[h], fmaxf(d, 0.f), tot);
   }
-  scores[(bi * n_q + r) * n_comp + s] = tot;
+  scores[(bi * n_q + r) * n_comp + s] = sbf ? bf2f(f2bf(tot)) : tot;
 }
 
 // ---------------------------------------------------------------------------
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
     const bf16_t* __restrict__ qI, const float* __restrict__ w, const bf16_t* __restrict__ KI,
     int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t cand_per_wg,
     int64_t n_qblocks, float* __restrict__ scores, int64_t k, int32_t* __restrict__ idx,
-    float* __restrict__ score_out) {
+    float* __restrict__ score_out, int sbf) {
   constexpr int CI = KS * 16;
   constexpr int NH = NHB * 32;
   constexpr int TN = 64;                 // keys per tile
@@ -345,8 +345,10 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
       }
       const int64_t cand = kb + l;
       if (cand < vis_q) {
-        if constexpr (FUSED) ssc[wave][cand] = (l < 32) ? s2[0] : s2[1];
-        else srow[cand] = (l < 32) ? s2[0] : s2[1];
+        const float v = (l < 32) ? s2[0] : s2[1];
+        const float vs = sbf ? bf2f(f2bf(v)) : v;   // bf16 index scores: rounded before the selection
+        if constexpr (FUSED) ssc[wave][cand] = vs;
+        else srow[cand] = vs;
       }
     }
     slot = slot == 2 ? 0 : slot + 1;
@@ -424,7 +426,7 @@ template <int NHB, int KS, int D, typename E, int SBK>
 __global__ __launch_bounds__(256) void index_scores_stream(
     const E* __restrict__ qI, const float* __restrict__ w, const E* __restrict__ KI,
     Rows kr, int64_t n_q, QPos qp, int64_t n_comp, int64_t m,
-    float* __restrict__ scores, uint32_t* __restrict__ gmax, int64_t ld_gmax) {
+    float* __restrict__ scores, uint32_t* __restrict__ gmax, int64_t ld_gmax, int sbf) {
   typedef ScoreOps<E> Ops;
   constexpr int CI = KS * 16;
   constexpr int NH = NHB * 32;
@@ -542,6 +544,7 @@ __global__ __launch_bounds__(256) void index_scores_stream(
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc = fmaf(fmaxf(acc[mb][r], 0.f), wv[mb][r], sc);
     sc += __shfl_xor(sc, 32, 64);
+    if (sbf) sc = bf2f(f2bf(sc));   // bf16 index scores: rounded before the selection
     const int64_t key = first + kstep * j + l;
     if constexpr (SBK > 0) {
       if (l < 32) sbuf[128 * j + 32 * wave + l] = sc;
@@ -1680,13 +1683,13 @@ template <int NHB, int KS, typename E>
 static hipError_t launch_scores_stream(const void* qI, const float* w, const void* KI, const Rows& kr, int64_t b,
                                        int64_t n_q, QPos qp, int64_t vmax, int64_t n_comp, int64_t m,
                                        float* scores, uint32_t* gmax, int64_t ld_gmax, bool* gmax_used,
-                                       hipStream_t st) {
+                                       hipStream_t st, int sbf = 0) {
   typedef StreamPolicy<(int)sizeof(E)> Pol;
   const int64_t nsplit = stream_splits(b, n_q, vmax, Pol::keys, Pol::wgs);
   dim3 grid((unsigned)n_q, (unsigned)nsplit, (unsigned)b);
   hipLaunchKernelGGL((index_scores_stream<NHB, KS, Pol::ring, E, (int)Pol::keys>), grid, dim3(256), 0, st,
                      (const E*)qI, w,
-                     (const E*)KI, kr, n_q, qp, n_comp, m, scores, gmax, ld_gmax);
+                     (const E*)KI, kr, n_q, qp, n_comp, m, scores, gmax, ld_gmax, sbf);
   *gmax_used = gmax != nullptr;
   return hipGetLastError();
 }
@@ -1697,7 +1700,7 @@ template <int NHB, int KS>
 static hipError_t launch_scores_mfma(const void* qI, const float* w, const void* KI, int64_t cbs,
                                      int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m,
                                      float* scores, uint32_t* gmax, int64_t ld_gmax, bool* gmax_used,
-                                     int64_t k, int32_t* idx, float* score_out, hipStream_t st) {
+                                     int64_t k, int32_t* idx, float* score_out, hipStream_t st, int sbf) {
   const int64_t vmax = std::min<int64_t>((t0 + n_q) / m, n_comp);
   *gmax_used = false;
   if (n_q >= 4) {
@@ -1706,13 +1709,13 @@ static hipError_t launch_scores_mfma(const void* qI, const float* w, const void*
     dim3 grid((unsigned)nqb, 1, (unsigned)b);
     if (idx != nullptr)   // every list fits one workgroup: selection fused (the caller checked)
       hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 1>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
-                         (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, idx, score_out);
+                         (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, idx, score_out, sbf);
     else
       hipLaunchKernelGGL((index_scores_mfma<NHB, KS, 0>), grid, dim3(256), 0, st, (const bf16_t*)qI, w,
-                         (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, nullptr, nullptr);
+                         (const bf16_t*)KI, cbs, n_q, t0, n_comp, m, cpw, nqb, scores, k, nullptr, nullptr, sbf);
   } else {
     return launch_scores_stream<NHB, KS, bf16_t>(qI, w, KI, dense_rows(cbs), b, n_q, QPos{t0, nullptr}, vmax,
-                                                 n_comp, m, scores, gmax, ld_gmax, gmax_used, st);
+                                                 n_comp, m, scores, gmax, ld_gmax, gmax_used, st, sbf);
   }
   return hipGetLastError();
 }
@@ -1783,8 +1786,10 @@ static hipError_t finish_topk(const TopkLayout& L, unsigned char* W, float* scor
 
 hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int64_t cbs, int64_t b,
                              int64_t n_q, int64_t t0, int64_t n_comp, int64_t nh, int64_t cI,
-                             int64_t m, int64_t k, int dtype, int32_t* idx, float* score,
+                             int64_t m, int64_t k, int dtype_flags, int32_t* idx, float* score,
                              void* ws, hipStream_t st) {
+  const int dtype = dtype_flags & 0xff;
+  const int sbf = (dtype_flags & 0x100) ? 1 : 0;   // bf16 index scores
   const TopkLayout L = topk_layout(b, n_q, n_comp, k);
   unsigned char* W = (unsigned char*)ws;
   float* scores = (float*)(W + L.scores);
@@ -1802,7 +1807,7 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
 #define CSA_SCORES_CASE(A, B)                                                                       \
   if (!done && nhb == A && ks == B) {                                                               \
     err = launch_scores_mfma<A, B>(qI, w, KI, cbs, b, n_q, t0, n_comp, m, scores, gmax, L.gcap,     \
-                                   &gmax_used, k, fused ? idx : nullptr, score, st);                \
+                                   &gmax_used, k, fused ? idx : nullptr, score, st, sbf);           \
     done = true;                                                                                    \
   }
       CSA_SCORES_CASE(1, 4) CSA_SCORES_CASE(1, 8) CSA_SCORES_CASE(2, 4) CSA_SCORES_CASE(2, 8)
@@ -1816,7 +1821,7 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
   if (!done && nhb == A && ks == B) {                                                                   \
     err = launch_scores_stream<A, B, fp8_t>(qI, w, KI, dense_rows(cbs), b, n_q, QPos{t0, nullptr},      \
                                             std::min<int64_t>((t0 + n_q) / m, n_comp), n_comp, m, scores, \
-                                            gmax, L.gcap, &gmax_used, st);                              \
+                                            gmax, L.gcap, &gmax_used, st, sbf);                         \
     done = true;                                                                                        \
   }
       CSA_STREAM8_CASE(1, 4) CSA_STREAM8_CASE(1, 8) CSA_STREAM8_CASE(2, 4) CSA_STREAM8_CASE(2, 8)
@@ -1855,13 +1860,13 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
       dim3 grid((unsigned)((n_comp + 255) / 256), (unsigned)n_q, (unsigned)b);
       if (dtype == 1)
         hipLaunchKernelGGL((index_scores_generic<bf16_t>), grid, dim3(256), 0, st, (const bf16_t*)qI,
-                           w, (const bf16_t*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores);
+                           w, (const bf16_t*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores, sbf);
       else if (dtype == 2)
         hipLaunchKernelGGL((index_scores_generic<fp8_t>), grid, dim3(256), 0, st, (const fp8_t*)qI,
-                           w, (const fp8_t*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores);
+                           w, (const fp8_t*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores, sbf);
       else
         hipLaunchKernelGGL((index_scores_generic<float>), grid, dim3(256), 0, st, (const float*)qI,
-                           w, (const float*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores);
+                           w, (const float*)KI, cbs, n_q, t0, n_comp, (int)nh, (int)cI, m, scores, sbf);
       err = hipGetLastError();
     }
     if (err != hipSuccess) return err;

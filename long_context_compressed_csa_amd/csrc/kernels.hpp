@@ -83,4 +83,30 @@ hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const
                                const float* sink, int64_t b, int64_t n_comp_max, int64_t n_h, int64_t k, int64_t m,
                                int64_t n_win, float scale, void* ws, void* out, hipStream_t st);
 
+// ---- FP8 KV entries ----
+hipError_t launch_quantize_kv_fp8(const void* x, int64_t xrs, int64_t rows, int64_t c, int64_t r, int dtype,
+                                  void* codes, int64_t crs, void* rope, int64_t rrs, float* scale, hipStream_t st);
+size_t attend_fp8kv_workspace_bytes(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h, int64_t c,
+                                    int64_t k, int64_t m, int64_t n_win);
+hipError_t launch_attend_fp8kv(const void* q, const void* codes, const void* rope, const float* scale, int64_t cbs,
+                               const int32_t* idx, const void* kv_raw, int64_t rbs, int64_t raw_pos0,
+                               const float* sink, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
+                               int64_t c, int64_t r, int64_t k, int64_t m, int64_t n_win, float sc, void* ws,
+                               void* out, hipStream_t st);
+
+// ---- backward pass ----
+size_t attend_backward_workspace_bytes(int64_t b, int64_t n_q, int64_t n_h, int64_t c, int64_t ks, int64_t n_win);
+hipError_t launch_attend_backward(int dense, const void* q, const void* Ccomp, int64_t cbs, const int32_t* idx,
+                                  const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink,
+                                  const void* dout, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp,
+                                  int64_t n_raw, int64_t n_h, int64_t c, int64_t k, int64_t m, int64_t n_win,
+                                  float scale, int dtype, int accumulate, float* dq, float* dC, int64_t dcbs,
+                                  float* dR, int64_t drbs, float* dsink, void* ws, hipStream_t st);
+size_t compress_backward_workspace_bytes(int64_t n, int64_t c, int64_t m);
+hipError_t launch_compress_backward(const void* Ca, const void* Cb, const void* Za, const void* Zb, const void* Ba,
+                                    const void* Bb, const void* pCb, const void* pZb, const float* dCc, int64_t b,
+                                    int64_t n, int64_t c, int64_t m, int overlap, int dtype, float* dCa, float* dCb,
+                                    float* dZa, float* dZb, float* dBa, float* dBb, float* dpCb, float* dpZb,
+                                    void* ws, hipStream_t st);
+
 }  // namespace csa

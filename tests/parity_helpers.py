@@ -67,8 +67,10 @@ def assert_close(got, want, dtype, what=""):
     return float(diff.max()), float(np.sqrt(np.mean(want ** 2)))
 
 
-def assert_index_sets(got_idx, want_idx, oracle_scores, vis, k, what=""):
-    """got_idx/want_idx [n_q, k]; oracle_scores [n_q, >=max vis]; vis [n_q]."""
+def assert_index_sets(got_idx, want_idx, oracle_scores, vis, k, what="", tie_tol=TIE_TOL):
+    """got_idx/want_idx [n_q, k]; oracle_scores [n_q, >=max vis]; vis [n_q].
+    tie_tol: how far from the k-th oracle score a member of the symmetric
+    difference may lie (1e-3 for float32 scores)."""
     got_idx = np.asarray(got_idx)
     want_idx = np.asarray(want_idx)
     n_ties = 0
@@ -83,6 +85,6 @@ def assert_index_sets(got_idx, want_idx, oracle_scores, vis, k, what=""):
         if diff:
             kth = np.sort(oracle_scores[r, : int(vis[r])])[::-1][take - 1]
             for s in diff:
-                assert abs(oracle_scores[r, s] - kth) <= TIE_TOL, (what, r, s, oracle_scores[r, s], kth)
+                assert abs(oracle_scores[r, s] - kth) <= tie_tol, (what, r, s, oracle_scores[r, s], kth)
             n_ties += 1
     return n_ties
