@@ -17,7 +17,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsa.so")
+# CSA_LIBRARY names another build of the same library (the host-sanitizer
+# build the CPU tests load); by default the in-tree libcsa.so.
+LIB_PATH = os.environ.get("CSA_LIBRARY") or os.path.join(_HERE, "libcsa.so")
 
 CSA_F32 = 0
 CSA_BF16 = 1

@@ -82,12 +82,55 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizer build: the files whose host code validates arguments
+# and keeps host state (abi.hip, blockpool.hip) are compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer on their host pass only
+# (device code is unchanged); every other object comes from the regular
+# build.  The result needs the sanitizer runtime preloaded (see
+# sanitizer_runtime()); the CPU tests load it through CSA_LIBRARY.
+HOSTSAN_SOURCES = ("abi.hip", "blockpool.hip")
+HOSTSAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+HOSTSAN_LIB = os.path.join(BUILD, "hostsan", "libcsa_hostsan.so")
+
+
+def sanitizer_runtime() -> str | None:
+    """The clang AddressSanitizer runtime of the ROCm toolchain, if present."""
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Build HOSTSAN_LIB; the regular objects must exist (build() first)."""
+    hipcc = _hipcc()
+    out = os.path.dirname(HOSTSAN_LIB)
+    os.makedirs(out, exist_ok=True)
+    objs = []
+    for s in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        name = os.path.basename(s)
+        if name in HOSTSAN_SOURCES:
+            o = os.path.join(out, name + ".o")
+            flags = [f for f in CXXFLAGS if f != "-O3"]
+            _run([hipcc, *flags, *HOSTSAN_FLAGS, "-c", s, "-o", o], verbose)
+        else:
+            o = os.path.join(BUILD, name + ".o")
+            if not os.path.exists(o):
+                raise RuntimeError(f"{o} is missing: run the regular build first")
+        objs.append(o)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", HOSTSAN_LIB, *objs], verbose)
+    return HOSTSAN_LIB
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=8)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--host-sanitize", action="store_true",
+                    help="also build the host-sanitizer variant of the library")
     a = ap.parse_args(argv)
     print(build(a.jobs, a.verbose))
+    if a.host_sanitize:
+        print(build_host_sanitized(a.verbose))
 
 
 if __name__ == "__main__":
