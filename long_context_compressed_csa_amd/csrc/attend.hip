@@ -189,9 +189,9 @@ __device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8 a, const bf16
 }
 __device__ __forceinline__ void o_hazard_pad() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-template <int DENSE, int G>
+template <int DENSE, int G, int PG>
 struct AttnSmem {
-  int32_t sel[DENSE ? 1 : kMaxSel];
+  int32_t sel[(DENSE && !PG) ? 1 : kMaxSel];   // selected entries (paged: pool rows)
   int32_t cnt[DENSE ? 1 : kMaxSel / 128][2];   // per-round valid counts of the compaction
   float bc[2 * G][kHW];                          // per-wave broadcast of per-head factors
   int32_t gen;                                   // restart generation (see the softmax note)
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
     Rows er, int64_t ring, const int64_t* __restrict__ pos) {
   constexpr int NW = 2 * G;        // waves per workgroup
   constexpr int R = kT / NW;       // gathered rows per wave and tile
-  __shared__ AttnSmem<DENSE, G> sm;
+  __shared__ AttnSmem<DENSE, G, PG> sm;
   // four tile buffers: tile i lives in buffer i % 4
   __shared__ __attribute__((aligned(16))) unsigned char T0[kTileB];
   __shared__ __attribute__((aligned(16))) unsigned char T1[kTileB];
@@ -305,6 +305,15 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   const int64_t jb = (int64_t)split * per;
   const int64_t je = jb + per < N ? jb + per : N;
   const int ntiles = je > jb ? (int)((je - jb + kT - 1) / kT) : 0;
+  if (DENSE && PG) {
+    // The split's compressed entries become pool rows once, here (the host
+    // keeps a split within kMaxSel entries).  Looked up in the tile loop,
+    // each block-table load's wait would also drain the gathers in flight.
+    int64_t ce = je < nsel ? je : nsel;
+    if (ce > jb + kMaxSel) ce = jb + kMaxSel;
+    for (int64_t j = jb + tid; j < ce; j += 64 * NW) sm.sel[j - jb] = (int32_t)(er.at(bi, j, kC) / kC);
+    __syncthreads();
+  }
   // entries of the group list this wave's query may not read (-1: none)
   int64_t exA_abs = -1, exW_abs = -1;
   if (DENSE) {
@@ -323,6 +332,10 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   // holds row chunk c ^ f(row).  Always exactly R loads per wave.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int jbi = (int)jb, jei = (int)je, nseli = (int)nsel;
+  // paged: ring slot of the first window row; window row e (< n_win <= ring)
+  // sits at slot wslot0 + e, wrapped once
+  const int ring_i = PG ? (int)ring : 1;
+  const int wslot0 = PG ? (int)(wlo % ring) : 0;
   // Tile layout in LDS (column-block major): 64-byte column block b of
   // tile row r, 16-byte chunk c of that block, lives at
   //   b * 1024 + c * 256 + ((r ^ 4c) * 16).
@@ -340,17 +353,19 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
     // creates push the Q operand out of registers.  The index is clamped so
     // that every lane reads, with no branch around the load.
     int selj = j;
-    if (!DENSE) {
-      const uint32_t a = (uint32_t)(uintptr_t)&sm.sel[j < nseli ? j : 0];
+    if (!DENSE || PG) {
+      const int si = j < nseli ? (DENSE ? j - jbi : j) : 0;
+      const uint32_t a = (uint32_t)(uintptr_t)&sm.sel[si];
       asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(selj) : "v"(a));
     }
     const int e = j < nseli ? selj : j - nseli;
     const bf16_t* p;
     if (PG) {
-      // compressed: pool row (CSA lists hold pool rows already; HCA looks
-      // the block up); window: ring slot of the row's position
-      const int64_t off = j < nseli ? (DENSE ? er.at(bi, e, kC) : (int64_t)e * kC)
-                                    : ((wlo + e) % ring) * (int64_t)kC;
+      // compressed: pool row (translated in the prologue); window: ring slot
+      // of the row's position
+      int ws = wslot0 + e;
+      ws = ws >= ring_i ? ws - ring_i : ws;
+      const int64_t off = (int64_t)(j < nseli ? e : ws) * kC;
       p = (j < nseli ? cbase : rbase) + off + 8 * g4;
     } else {
       p = (j < nseli ? cbase : rbase) + (int64_t)e * kC + 8 * g4;
@@ -755,8 +770,16 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
 // Paged decode: one query per batch row at its own position, entries via
 // the block table, window rows from the request's ring.  bf16, c = 512,
 // 64-head groups (the caller checked).
+// Paged HCA translates a split's compressed entries into kMaxSel LDS slots,
+// so it takes at least nmax / kMaxSel splits.
+static int attend_paged_nsplit(int dense, int64_t b, int64_t n_h, int64_t nmax) {
+  int ns = attend_nsplit(b, 1, n_h, nmax);
+  const int64_t need = dense ? (nmax + kMaxSel - 1) / kMaxSel : 1;
+  return ns < need ? (int)need : ns;
+}
+
 size_t attend_paged_workspace_bytes(int dense, int64_t b, int64_t n_h, int64_t nmax) {
-  const int ns = attend_nsplit(b, 1, n_h, nmax);
+  const int ns = attend_paged_nsplit(dense, b, n_h, nmax);
   if (ns == 1) return 0;
   const int64_t slots = b * (n_h / kHG) * ns;
   return ((((size_t)slots * kHG * kC * 4) + 255) & ~(size_t)255) + (size_t)slots * kHG * 2 * 4;
@@ -768,7 +791,7 @@ hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const
                                int64_t n_win, float scale, void* ws, void* out, hipStream_t st) {
   if (b == 0) return hipSuccess;
   const int64_t nmax = (dense ? n_comp_max : k) + n_win;
-  const int ns = attend_nsplit(b, 1, n_h, nmax);
+  const int ns = attend_paged_nsplit(dense, b, n_h, nmax);
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (ns > 1) {

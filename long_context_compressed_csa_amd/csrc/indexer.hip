@@ -484,6 +484,28 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     const int r = i * KPI + l / NCH;
     src_off[i] = r * CI + (((l % NCH) ^ ((r / SDIV) % NCH)) * (16 / ES));
   }
+  // Paged keys (SBK > 0: at most SBK / 128 tiles per wave): the block of
+  // every tile of the wave is looked up before the stream starts, tile j's
+  // in lane j % 64 of blk[j / 64] (tiles past the end: the last key's
+  // block).  Looked up as each tile is issued, the block-table load's wait
+  // would also drain the tiles already in flight.
+  constexpr int NBR = SBK > 0 ? (SBK / 128 + 63) / 64 : 1;
+  const bool paged = SBK > 0 && kr.table != nullptr;
+  int blk[NBR];
+  int blk_last = 0;
+  if (paged) {
+    const int32_t* trow = kr.table + kr.req(bi) * kr.table_stride;
+    auto block_of = [&](int64_t key) {
+      int64_t b = trow[key >> kr.pb_log2];
+      return (int)(b < 0 ? 0 : (b >= kr.n_blocks ? kr.n_blocks - 1 : b));
+    };
+#pragma unroll
+    for (int r = 0; r < NBR; ++r) {
+      const int64_t kb = first + kstep * (int64_t)(64 * r + l);
+      blk[r] = block_of(kb < lastkey ? kb : lastkey);
+    }
+    blk_last = block_of(lastkey);
+  }
   auto issue = [&](int j, int slot) {
     // rows past the last key re-read the last key (in bounds; their scores
     // are dropped), and so does a tile wholly past the end
@@ -493,7 +515,16 @@ __global__ __launch_bounds__(256) void index_scores_stream(
     const uint32_t lds = (uint32_t)(uintptr_t)&ring[wave][slot][0];
     // the tile's rows kb .. kb + room lie in one block when paged (blocks
     // hold a multiple of 32 keys, and kb is a multiple of 32 or the last key)
-    const E* tb = KI + kr.at(bi, kb, CI);
+    const E* tb;
+    if (paged) {
+      int b = blk_last;
+#pragma unroll
+      for (int r = 0; r < NBR; ++r)
+        if ((j >> 6) == r) b = __builtin_amdgcn_readlane(blk[r], j & 63);
+      tb = KI + (int64_t)b * kr.blk_elems + kr.off + (kb & ((1 << kr.pb_log2) - 1)) * CI;
+    } else {
+      tb = KI + kr.at(bi, kb, CI);
+    }
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int r = i * KPI + l / NCH;
