@@ -571,6 +571,8 @@ def run_hca_decode(args, torch, L, synth):
 # ----------------------------------- paged decode, backward, FP8 KV, BF16 ----
 
 def _event_us(torch, fn, iters, warm=3):
+    # clocks to their steady state first (see prewarm), then a few more calls
+    prewarm(torch, fn, 0.2)
     for _ in range(warm):
         fn()
     a, b = _events(torch)

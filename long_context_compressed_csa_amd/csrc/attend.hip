@@ -643,6 +643,372 @@ __global__ __launch_bounds__(128 * G) void attend_mfma_c512(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dimension-split form of the CSA path (one query per workgroup, no split of
+// its entry list).  Four waves: wave w owns heads 32 (w & 1) .. +31 of the
+// 64-head group and dimensions 256 (w >> 1) .. +255, so a wave keeps half of
+// the registers of the form above (Q operand 64 VGPRs, O 128 AGPRs) and two
+// waves share each SIMD, each hiding the other's LDS, barrier and softmax
+// latencies.  Scores need all 512 dimensions: a wave's partial S^T of tile
+// i+1 over its 256 dimensions goes to LDS, and in the next step its partner
+// (same heads, other dimensions) adds it to its own; both then hold the same
+// scores, maxima and weights.  Tiles, gathers and operand layouts are those
+// of attend_mfma_c512; three tile buffers, the next tile gathered during the
+// current step.
+// ---------------------------------------------------------------------------
+// LDS-DMA of 16 bytes per lane (lane l's bytes land at LDS byte address
+// lds + 16 l; lds is wave-uniform, passed in M0) issued as inline assembly:
+// the compiler does not track these LDS writes, so it adds no wait of its
+// own before the operand reads of other tile buffers; the kernel orders them
+// with explicit vmcnt waits and barriers.  M0 is restored afterwards, since
+// the compiler does not accept it as a clobber.  No register results.
+__device__ __forceinline__ void attn_dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
+}
+
+struct DsSmem {
+  int32_t sel[kMaxSel];
+  int32_t cnt[kMaxSel / 256][4];
+  float bc[4][kHW];
+  int32_t gen;
+};
+constexpr int kXB = 64 * 8 * 4;   // one wave's partial S^T: 64 lanes x 8 floats
+
+__global__ __launch_bounds__(256, 2) void attend_ds(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ Ccomp, int64_t cbs,
+    const int32_t* __restrict__ idx, const bf16_t* __restrict__ kv_raw, int64_t rbs,
+    int64_t raw_pos0, const float* __restrict__ sink, int64_t n_q, int64_t t0, int64_t n_comp,
+    int n_h, int64_t k, int64_t m, int64_t n_win, float scale, bf16_t* __restrict__ out) {
+  constexpr int NW = 4;
+  constexpr int R = kT / NW;   // gather loads per wave and tile
+  __shared__ DsSmem sm;
+  __shared__ __attribute__((aligned(16))) unsigned char T0[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char T1[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char T2[kTileB];
+  // partial S^T exchange of the four waves; also wave 3's output staging
+  __shared__ __attribute__((aligned(16))) unsigned char XB[NW * kXB];
+  static_assert(NW * kXB >= kHW * kStageRowB / 2, "half a wave's staging must fit the exchange buffer");
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int half = l >> 5;
+  const int g4 = l >> 4;
+  const bool up16 = (l & 16) != 0;
+  const int s16 = l & 15;
+  const int hw = wave & 1;           // which 32 heads of the group
+  const int dh = wave >> 1;          // which 256 dimensions
+  const int64_t rq = (int64_t)gridDim.x - 1 - blockIdx.x;   // later queries (more work) first
+  const int hg = blockIdx.y;
+  const int64_t bi = blockIdx.z;
+  const int64_t t = t0 + rq;
+  const int head0 = kHG * hg + kHW * hw;
+
+  // Q operand, this wave's dimensions: lane holds head head0 + 16 hb + l%16,
+  // dims 256 dh + 32 ks + 8 (l/16) + (0..7)
+  bf16x8 qB[8][2];
+  // compaction of the valid indices (0 <= s < visible), as attend_mfma_c512
+  constexpr int NT = 64 * NW;
+  constexpr int NR = kMaxSel / NT;
+  int64_t vis = (t + 1) / m;
+  if (vis > n_comp) vis = n_comp;
+  {
+    const int32_t* ir = idx + (bi * n_q + rq) * k;
+    int32_t sv[NR];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int64_t j = (int64_t)u * NT + tid;
+      sv[u] = j < k ? ir[j] : -1;
+    }
+    uint64_t mk[NR];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      mk[u] = __builtin_amdgcn_ballot_w64(sv[u] >= 0 && sv[u] < vis);
+      if (l == 0) sm.cnt[u][wave] = __popcll(mk[u]);
+    }
+    __syncthreads();
+    const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+    int64_t base = 0;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      int pre = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) pre += w < wave ? sm.cnt[u][w] : 0;
+      const int64_t pos = base + pre + __popcll(mk[u] & below);
+      if (((mk[u] >> l) & 1) && pos < kMaxSel) sm.sel[pos] = sv[u];
+      base += sm.cnt[u][0] + sm.cnt[u][1] + sm.cnt[u][2] + sm.cnt[u][3];
+    }
+    __syncthreads();
+    sm.gen = 0;   // every thread writes the same value; read after the next barrier
+  }
+  {
+    const bf16_t* qp = q + ((bi * n_q + rq) * n_h + head0 + s16) * (int64_t)kC + 256 * dh + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) qB[ks][hb] = *reinterpret_cast<const bf16x8*>(qp + hb * 16 * kC + ks * 32);
+    // Q must have arrived before the first gather is issued: the compiler
+    // does not count the gathers (inline asm), so a wait it placed for Q
+    // later on would also drain every gather in flight
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) asm volatile("" ::"v"(qB[ks][hb]));
+  }
+  int64_t nsel = 0;
+#pragma unroll
+  for (int u = 0; u < NR; ++u) nsel += sm.cnt[u][0] + sm.cnt[u][1] + sm.cnt[u][2] + sm.cnt[u][3];
+  if (nsel > kMaxSel) nsel = kMaxSel;
+  const int64_t wlo = t - n_win + 1 > 0 ? t - n_win + 1 : 0;
+  const int64_t N = nsel + (t - wlo + 1);
+  const int ntiles = (int)((N + kT - 1) / kT);
+
+  const bf16_t* cbase = Ccomp + bi * cbs;
+  const bf16_t* rbase = kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int Ni = (int)N, nseli = (int)nsel;
+  const int grow = s16 ^ (4 * g4);   // tile row this lane fetches
+  auto issue_tile = [&](int ti, unsigned char* buf) {
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)buf);
+    int j = ti * kT + grow;
+    if (j >= Ni) j = 0;
+    int selj;
+    {
+      const uint32_t a = (uint32_t)(uintptr_t)&sm.sel[j < nseli ? j : 0];
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(selj) : "v"(a));
+    }
+    const int e = j < nseli ? selj : j - nseli;
+    const bf16_t* p = (j < nseli ? cbase : rbase) + (int64_t)e * kC + 8 * g4;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int b = wave_u + rr * NW;
+      attn_dma16(p + 32 * b, lbase + (uint32_t)(b * kBlkB));
+    }
+  };
+
+  const int sA = g4 * 256 + ((s16 ^ (4 * g4)) * 16) + kBlkB * 8 * dh;
+  const int cpart = 2 * (g4 & 1) + ((s16 & 3) >> 1);
+  auto trbase = [&](int row) { return cpart * 256 + ((row ^ (4 * cpart)) * 16) + 8 * (s16 & 1); };
+  const int trB0 = trbase(8 * half + (s16 >> 2)) + kBlkB * 8 * dh;
+  const int trB1 = trbase(8 * half + 4 + (s16 >> 2)) + kBlkB * 8 * dh;
+
+  constexpr float kLogHeadroom = 64.f;
+  const float sl2 = scale * kLog2e;
+  f32x16 o[8];
+  float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY};
+  float l_part = 0.f;
+
+  // partial S^T of one tile over this wave's 256 dimensions
+  auto s_part = [&](const unsigned char* B, f32x4 (&sp)[2]) {
+    f32x4 c0 = (f32x4){}, c1 = (f32x4){};
+    const unsigned char* a = B + sA;
+    constexpr int D = 2;
+    bf16x8 av[D + 1];
+#pragma unroll
+    for (int u = 0; u < D; ++u) av[u] = *reinterpret_cast<const bf16x8*>(a + kBlkB * u);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + D < 8) av[(ks + D) % (D + 1)] = *reinterpret_cast<const bf16x8*>(a + kBlkB * (ks + D));
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks % (D + 1)], qB[ks][0], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks % (D + 1)], qB[ks][1], c1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+#pragma unroll
+    for (int ks = 0; ks < 8 - D; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * D, 0);
+    sp[0] = c0;
+    sp[1] = c1;
+  };
+  auto put_part = [&](const f32x4 (&sp)[2]) {
+    unsigned char* x = XB + wave * kXB + 16 * l;
+    *reinterpret_cast<f32x4*>(x) = sp[0];
+    *reinterpret_cast<f32x4*>(x + 1024) = sp[1];
+  };
+  auto add_partner = [&](f32x4 (&sp)[2]) {
+    const unsigned char* x = XB + (wave ^ 2) * kXB + 16 * l;
+    sp[0] += *reinterpret_cast<const f32x4*>(x);
+    sp[1] += *reinterpret_cast<const f32x4*>(x + 1024);
+  };
+  // weights of tile ti from its full S^T (as attend_mfma_c512)
+  auto weights = [&](int ti, const f32x4 (&sacc)[2]) -> bf16x8 {
+    const int rem0 = Ni - ti * kT;
+    const int rem = rem0 < 0 ? 0 : (rem0 < kT ? rem0 : kT);
+    float sv[2][4], tmax[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      tmax[hb] = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int loc = 4 * g4 + r;
+        sv[hb][r] = loc < rem ? sacc[hb][r] * sl2 : -INFINITY;
+        tmax[hb] = fmaxf(tmax[hb], sv[hb][r]);
+      }
+      m_seen[hb] = fmaxf(m_seen[hb], tmax[hb]);
+    }
+    if (__builtin_amdgcn_ballot_w64(m_ref[0] == -INFINITY || m_ref[1] == -INFINITY)) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        float x = fmaxf(tmax[hb], __uint_as_float(from_lane_xor16(__float_as_uint(tmax[hb]), up16)));
+        x = half_max(x);
+        if (m_ref[hb] == -INFINITY) m_ref[hb] = x;
+      }
+    }
+    uint32_t pk[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float mb = (m_ref[hb] == -INFINITY) ? 0.f : m_ref[hb];
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[hb][r] - mb);
+        const float p1 = __builtin_amdgcn_exp2f(sv[hb][r + 1] - mb);
+        pk[hb][r >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t));
+      }
+    }
+    uint32_t own[2], lo[2], hi[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      own[i] = up16 ? pk[1][i] : pk[0][i];
+      const uint32_t recv = from_lane_xor16(up16 ? pk[0][i] : pk[1][i], up16);
+      lo[i] = up16 ? recv : own[i];
+      hi[i] = up16 ? own[i] : recv;
+    }
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float rs = l_part;
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo[0]), ones, rs, false);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo[1]), ones, rs, false);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi[0]), ones, rs, false);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi[1]), ones, rs, false);
+    l_part = rs;
+    return __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], hi[0], hi[1]));
+  };
+  // O[head][dim] += P E over this wave's 8 column blocks
+  auto pv_part = [&](const unsigned char* B, bf16x8 pa) {
+    // pa may come straight from VALU code (the last step has no S product
+    // in between) and the asm MFMAs below are opaque to the compiler's
+    // hazard checks: wait out the VALU-write / MFMA-read hazard here (pa is
+    // an operand, so its producers stay above the wait)
+    asm volatile("s_nop 4" : "+v"(pa));
+    bf16x4 tr[3][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      tr[u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB0 + kBlkB * u));
+      tr[u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB1 + kBlkB * u));
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      if (nb + 2 < 8) {
+        tr[(nb + 2) % 3][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB0 + kBlkB * (nb + 2)));
+        tr[(nb + 2) % 3][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB1 + kBlkB * (nb + 2)));
+      }
+      const bf16x8 bv = __builtin_shufflevector(tr[nb % 3][0], tr[nb % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      mfma_acc(o[nb], pa, bv);
+    }
+  };
+  // step i: tile i in Bc (waited for here), tile i+1 in flight, tile i+2
+  // gathered into Bf, whose previous tile (i-1) every wave has finished once
+  // past the first barrier; the second barrier publishes the partial S^T
+  auto step = [&](int i, const unsigned char* Bc, unsigned char* Bf) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<R>();
+    tile_barrier();
+    issue_tile(i + 2, Bf);
+    f32x4 sp[2];
+    s_part(Bc, sp);
+    put_part(sp);
+    tile_barrier();
+    add_partner(sp);
+    const bf16x8 pa = weights(i, sp);
+    pv_part(Bc, pa);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  __syncthreads();
+  int gen = 0;
+  for (;;) {
+    {
+      // O = 0 * 0 + 0, defined straight in the accumulation registers (a
+      // plain zero would be materialised in VGPRs and copied)
+      const bf16x8 z8 = {};
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o[nb]) : "v"(z8));
+    }
+    l_part = 0.f;
+    issue_tile(0, T0);
+    issue_tile(1, T1);
+    for (int it = 0; it < ntiles; it += 3) {
+      step(it, T0, T2);
+      if (it + 1 >= ntiles) break;
+      step(it + 1, T1, T0);
+      if (it + 2 >= ntiles) break;
+      step(it + 2, T2, T1);
+    }
+    wait_vm<0>();   // the look-ahead gathers past the last tile
+    o_hazard_pad();
+    bool over = false;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float x = fmaxf(m_seen[hb], __uint_as_float(from_lane_xor16(__float_as_uint(m_seen[hb]), up16)));
+      x = half_max(x);
+      m_seen[hb] = x;
+      over |= x > m_ref[hb] + kLogHeadroom;
+    }
+    if (over) sm.gen = gen + 1;
+    __syncthreads();
+    if (sm.gen == gen) break;
+    ++gen;
+    m_ref[0] = m_seen[0];
+    m_ref[1] = m_seen[1];
+  }
+  const float m_run = up16 ? m_ref[1] : m_ref[0];
+  const float l_run = half_sum(l_part);
+  if (l < 32) {
+    const float z2 = sink[head0 + l] * kLog2e;
+    const float Mf = fmaxf(m_run, z2);
+    const float fac = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - Mf);
+    sm.bc[wave][l] = fac / (l_run * fac + __builtin_amdgcn_exp2f(z2 - Mf));
+  }
+  __syncthreads();   // every wave is done with the tile and exchange buffers; bc is visible
+  float4 g4v[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) g4v[g] = *reinterpret_cast<const float4*>(&sm.bc[wave][8 * g + 4 * half]);
+  unsigned char* stg = wave == 0 ? T0 : wave == 1 ? T1 : wave == 2 ? T2 : XB;
+  bf16_t* ob = out + ((bi * n_q + rq) * n_h + head0) * (int64_t)kC + 256 * dh;
+  // two passes of 16 head rows (8 KiB of staging each)
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int nb8 = 0; nb8 < 8; ++nb8) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * pass + gg;
+        const float gv[4] = {g4v[g].x, g4v[g].y, g4v[g].z, g4v[g].w};
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int hr = 8 * g + 4 * half + i;   // head row; staged at hr - 16 pass
+          const uint32_t pk = __builtin_bit_cast(
+              uint32_t, __builtin_convertvector((f32x2_t){o[nb8][4 * g + i] * gv[i], o[nb8][4 * g + i + 1] * gv[i + 1]},
+                                                bf16x2_t));
+          const int byte = ((nb8 * 32 + (l & 31)) * 2) ^ (((hr >> 2) & 1) << 6);
+          *reinterpret_cast<uint16_t*>(stg + (hr - 16 * pass) * kStageRowB + byte) = (uint16_t)pk;
+          *reinterpret_cast<uint16_t*>(stg + (hr + 1 - 16 * pass) * kStageRowB + byte) = (uint16_t)(pk >> 16);
+        }
+      }
+    }
+    // the staging area is private to this wave: its own writes are ordered
+    // before its reads
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int cidx = l + 64 * i;
+      const int hs = cidx >> 5, c16 = cidx & 31;   // staged row, 16-byte chunk
+      const int hr = hs + 16 * pass;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + hs * kStageRowB + ((c16 * 16) ^ (((hr >> 2) & 1) << 6)));
+      *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(ob + hr * (int64_t)kC) + c16 * 16) = v;
+    }
+  }
+}
+
 // Merge the splits of one (query, head) in split order (log2-domain maxima),
 // then apply the sink: out = sum_s O_s 2^{m_s - M} / (sum_s l_s 2^{m_s - M} + 2^{z - M}).
 __global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ part_o,
@@ -740,7 +1106,11 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
     const int G = dense ? 2 : 1;
     dim3 grid((unsigned)((n_q + G - 1) / G), (unsigned)((n_h / kHG) * ns), (unsigned)b);
     const Rows none = dense_rows(cbs);
-    if (dense)
+    if (!dense && ns == 1)
+      hipLaunchKernelGGL(attend_ds, dim3((unsigned)n_q, (unsigned)(n_h / kHG), (unsigned)b), dim3(256), 0, st,
+                         (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
+                         n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, (bf16_t*)out);
+    else if (dense)
       hipLaunchKernelGGL((attend_mfma_c512<1, 2, 0>), grid, dim3(256), 0, st, (const bf16_t*)q,
                          (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
                          n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
