@@ -676,11 +676,16 @@ struct DsSmem {
 };
 constexpr int kXB = 64 * 8 * 4;   // one wave's partial S^T: 64 lanes x 8 floats
 
+// SPLIT = 1: the entry list is split over nsplit workgroups that write
+// partial states for attend_combine; SPLIT = 0: nsplit is 1 and the output is
+// written here.
+template <int SPLIT>
 __global__ __launch_bounds__(256, 2) void attend_ds(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Ccomp, int64_t cbs,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ kv_raw, int64_t rbs,
     int64_t raw_pos0, const float* __restrict__ sink, int64_t n_q, int64_t t0, int64_t n_comp,
-    int n_h, int64_t k, int64_t m, int64_t n_win, float scale, bf16_t* __restrict__ out) {
+    int n_h, int64_t k, int64_t m, int64_t n_win, float scale, int nsplit, float* __restrict__ part_o,
+    float* __restrict__ part_ml, bf16_t* __restrict__ out) {
   constexpr int NW = 4;
   constexpr int R = kT / NW;   // gather loads per wave and tile
   __shared__ DsSmem sm;
@@ -698,7 +703,8 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   const int hw = wave & 1;           // which 32 heads of the group
   const int dh = wave >> 1;          // which 256 dimensions
   const int64_t rq = (int64_t)gridDim.x - 1 - blockIdx.x;   // later queries (more work) first
-  const int hg = blockIdx.y;
+  const int hg = blockIdx.y / nsplit;
+  const int split = blockIdx.y % nsplit;
   const int64_t bi = blockIdx.z;
   const int64_t t = t0 + rq;
   const int head0 = kHG * hg + kHW * hw;
@@ -760,17 +766,21 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   if (nsel > kMaxSel) nsel = kMaxSel;
   const int64_t wlo = t - n_win + 1 > 0 ? t - n_win + 1 : 0;
   const int64_t N = nsel + (t - wlo + 1);
-  const int ntiles = (int)((N + kT - 1) / kT);
+  // this workgroup's part of the entry list (all of it when nsplit = 1)
+  const int64_t per = (N + nsplit - 1) / nsplit;
+  const int64_t jb = (int64_t)split * per;
+  const int64_t je = jb + per < N ? jb + per : N;
+  const int ntiles = je > jb ? (int)((je - jb + kT - 1) / kT) : 0;
 
   const bf16_t* cbase = Ccomp + bi * cbs;
   const bf16_t* rbase = kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int Ni = (int)N, nseli = (int)nsel;
+  const int jbi = (int)jb, jei = (int)je, nseli = (int)nsel;
   const int grow = s16 ^ (4 * g4);   // tile row this lane fetches
   auto issue_tile = [&](int ti, unsigned char* buf) {
     const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)buf);
-    int j = ti * kT + grow;
-    if (j >= Ni) j = 0;
+    int j = jbi + ti * kT + grow;
+    if (j >= jei) j = jbi;
     int selj;
     {
       const uint32_t a = (uint32_t)(uintptr_t)&sm.sel[j < nseli ? j : 0];
@@ -833,7 +843,7 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   };
   // weights of tile ti from its full S^T (as attend_mfma_c512)
   auto weights = [&](int ti, const f32x4 (&sacc)[2]) -> bf16x8 {
-    const int rem0 = Ni - ti * kT;
+    const int rem0 = jei - (jbi + ti * kT);
     const int rem = rem0 < 0 ? 0 : (rem0 < kT ? rem0 : kT);
     float sv[2][4], tmax[2];
 #pragma unroll
@@ -963,6 +973,24 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   }
   const float m_run = up16 ? m_ref[1] : m_ref[0];
   const float l_run = half_sum(l_part);
+  if (SPLIT) {
+    // partial state of this split: O over this wave's dimensions, and (once
+    // per head, from the first dimension half) the maximum and the sum
+    const int64_t slot = ((bi * n_q + rq) * (n_h / kHG) + hg) * nsplit + split;
+    float* po = part_o + slot * (int64_t)kHG * kC + (int64_t)kHW * hw * kC + 256 * dh + (l & 31);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int hr = 8 * (r >> 2) + 4 * half + (r & 3);
+        po[hr * (int64_t)kC + nb * 32] = o[nb][r];
+      }
+    if (dh == 0 && l < 32) {
+      part_ml[(slot * kHG + kHW * hw + l) * 2 + 0] = m_run;
+      part_ml[(slot * kHG + kHW * hw + l) * 2 + 1] = l_run;
+    }
+    return;
+  }
   if (l < 32) {
     const float z2 = sink[head0 + l] * kLog2e;
     const float Mf = fmaxf(m_run, z2);
@@ -1107,9 +1135,13 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
     dim3 grid((unsigned)((n_q + G - 1) / G), (unsigned)((n_h / kHG) * ns), (unsigned)b);
     const Rows none = dense_rows(cbs);
     if (!dense && ns == 1)
-      hipLaunchKernelGGL(attend_ds, dim3((unsigned)n_q, (unsigned)(n_h / kHG), (unsigned)b), dim3(256), 0, st,
+      hipLaunchKernelGGL(attend_ds<0>, dim3((unsigned)n_q, (unsigned)(n_h / kHG), (unsigned)b), dim3(256), 0, st,
                          (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
-                         n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, (bf16_t*)out);
+                         n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, 1, part_o, part_ml, (bf16_t*)out);
+    else if (!dense)
+      hipLaunchKernelGGL(attend_ds<1>, dim3((unsigned)n_q, (unsigned)((n_h / kHG) * ns), (unsigned)b), dim3(256), 0, st,
+                         (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
+                         n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml, (bf16_t*)out);
     else if (dense)
       hipLaunchKernelGGL((attend_mfma_c512<1, 2, 0>), grid, dim3(256), 0, st, (const bf16_t*)q,
                          (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
