@@ -678,14 +678,18 @@ constexpr int kXB = 64 * 8 * 4;   // one wave's partial S^T: 64 lanes x 8 floats
 
 // SPLIT = 1: the entry list is split over nsplit workgroups that write
 // partial states for attend_combine; SPLIT = 0: nsplit is 1 and the output is
-// written here.
-template <int SPLIT>
+// written here.  PG = 1 (paged decode cache): the query of batch row b sits
+// at pos[b], compressed entries are pool rows found through the block table
+// of `er` (translated during the compaction), window rows live in a ring of
+// `ring` slots per request.
+template <int SPLIT, int PG>
 __global__ __launch_bounds__(256, 2) void attend_ds(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Ccomp, int64_t cbs,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ kv_raw, int64_t rbs,
     int64_t raw_pos0, const float* __restrict__ sink, int64_t n_q, int64_t t0, int64_t n_comp,
     int n_h, int64_t k, int64_t m, int64_t n_win, float scale, int nsplit, float* __restrict__ part_o,
-    float* __restrict__ part_ml, bf16_t* __restrict__ out) {
+    float* __restrict__ part_ml, bf16_t* __restrict__ out, Rows er, int64_t ring,
+    const int64_t* __restrict__ pos) {
   constexpr int NW = 4;
   constexpr int R = kT / NW;   // gather loads per wave and tile
   __shared__ DsSmem sm;
@@ -706,7 +710,7 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   const int hg = blockIdx.y / nsplit;
   const int split = blockIdx.y % nsplit;
   const int64_t bi = blockIdx.z;
-  const int64_t t = t0 + rq;
+  const int64_t t = (PG ? pos[bi] : t0) + rq;
   const int head0 = kHG * hg + kHW * hw;
 
   // Q operand, this wave's dimensions: lane holds head head0 + 16 hb + l%16,
@@ -730,6 +734,12 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
     for (int u = 0; u < NR; ++u) {
       mk[u] = __builtin_amdgcn_ballot_w64(sv[u] >= 0 && sv[u] < vis);
       if (l == 0) sm.cnt[u][wave] = __popcll(mk[u]);
+    }
+    if (PG) {
+      // a selected entry becomes its row number in the block pool
+#pragma unroll
+      for (int u = 0; u < NR; ++u)
+        if ((mk[u] >> l) & 1) sv[u] = (int32_t)(er.at(bi, sv[u], kC) / kC);
     }
     __syncthreads();
     const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
@@ -772,8 +782,12 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   const int64_t je = jb + per < N ? jb + per : N;
   const int ntiles = je > jb ? (int)((je - jb + kT - 1) / kT) : 0;
 
-  const bf16_t* cbase = Ccomp + bi * cbs;
-  const bf16_t* rbase = kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
+  const bf16_t* cbase = PG ? Ccomp : Ccomp + bi * cbs;
+  const bf16_t* rbase = PG ? kv_raw + er.req(bi) * rbs : kv_raw + bi * rbs + (wlo - raw_pos0) * (int64_t)kC;
+  // paged: ring slot of the first window row; window row e (< n_win <= ring)
+  // sits at slot wslot0 + e, wrapped once
+  const int ring_i = PG ? (int)ring : 1;
+  const int wslot0 = PG ? (int)(wlo % ring) : 0;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int jbi = (int)jb, jei = (int)je, nseli = (int)nsel;
   const int grow = s16 ^ (4 * g4);   // tile row this lane fetches
@@ -787,7 +801,12 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
       asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(selj) : "v"(a));
     }
     const int e = j < nseli ? selj : j - nseli;
-    const bf16_t* p = (j < nseli ? cbase : rbase) + (int64_t)e * kC + 8 * g4;
+    int we = e;
+    if (PG) {
+      we = wslot0 + e;
+      we = we >= ring_i ? we - ring_i : we;
+    }
+    const bf16_t* p = (j < nseli ? cbase + (int64_t)e * kC : rbase + (int64_t)we * kC) + 8 * g4;
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       const int b = wave_u + rr * NW;
@@ -1128,27 +1147,24 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
       part_o = (float*)ws;
       part_ml = (float*)((unsigned char*)ws + osz);
     }
-    // dense lists: two consecutive queries share each workgroup's tiles (a
-    // single query leaves the second pair of waves redundant; a one-query
-    // instance of the kernel spills and is no faster)
-    const int G = dense ? 2 : 1;
-    dim3 grid((unsigned)((n_q + G - 1) / G), (unsigned)((n_h / kHG) * ns), (unsigned)b);
+    // selected lists: attend_ds, one query per workgroup; dense lists: two
+    // consecutive queries share each workgroup's tiles (a single query leaves
+    // the second pair of waves redundant; a one-query instance of the kernel
+    // spills and is no faster)
+    dim3 grid((unsigned)((n_q + 1) / 2), (unsigned)((n_h / kHG) * ns), (unsigned)b);
     const Rows none = dense_rows(cbs);
     if (!dense && ns == 1)
-      hipLaunchKernelGGL(attend_ds<0>, dim3((unsigned)n_q, (unsigned)(n_h / kHG), (unsigned)b), dim3(256), 0, st,
+      hipLaunchKernelGGL((attend_ds<0, 0>), dim3((unsigned)n_q, (unsigned)(n_h / kHG), (unsigned)b), dim3(256), 0, st,
                          (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
-                         n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, 1, part_o, part_ml, (bf16_t*)out);
+                         n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, 1, part_o, part_ml, (bf16_t*)out, none,
+                         (int64_t)0, (const int64_t*)nullptr);
     else if (!dense)
-      hipLaunchKernelGGL(attend_ds<1>, dim3((unsigned)n_q, (unsigned)((n_h / kHG) * ns), (unsigned)b), dim3(256), 0, st,
-                         (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
-                         n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml, (bf16_t*)out);
-    else if (dense)
-      hipLaunchKernelGGL((attend_mfma_c512<1, 2, 0>), grid, dim3(256), 0, st, (const bf16_t*)q,
-                         (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
-                         n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
-                         (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr);
+      hipLaunchKernelGGL((attend_ds<1, 0>), dim3((unsigned)n_q, (unsigned)((n_h / kHG) * ns), (unsigned)b), dim3(256),
+                         0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0,
+                         sink, n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml, (bf16_t*)out, none,
+                         (int64_t)0, (const int64_t*)nullptr);
     else
-      hipLaunchKernelGGL((attend_mfma_c512<0, 1, 0>), grid, dim3(128), 0, st, (const bf16_t*)q,
+      hipLaunchKernelGGL((attend_mfma_c512<1, 2, 0>), grid, dim3(256), 0, st, (const bf16_t*)q,
                          (const bf16_t*)Ccomp, cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink,
                          n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
                          (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr);
@@ -1209,11 +1225,14 @@ hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const
                        (const bf16_t*)pool, (int64_t)0, idx, (const bf16_t*)state, state_elems, (int64_t)0, sink,
                        (int64_t)1, (int64_t)0, n_comp_max, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
                        (bf16_t*)out, er, ring, pos);
+  else if (ns > 1)
+    hipLaunchKernelGGL((attend_ds<1, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)pool, (int64_t)0,
+                       idx, (const bf16_t*)state, state_elems, (int64_t)0, sink, (int64_t)1, (int64_t)0, n_comp_max,
+                       (int)n_h, k, m, n_win, scale, ns, part_o, part_ml, (bf16_t*)out, er, ring, pos);
   else
-    hipLaunchKernelGGL((attend_mfma_c512<0, 1, 1>), grid, dim3(128 * G), 0, st, (const bf16_t*)q,
-                       (const bf16_t*)pool, (int64_t)0, idx, (const bf16_t*)state, state_elems, (int64_t)0, sink,
-                       (int64_t)1, (int64_t)0, n_comp_max, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml,
-                       (bf16_t*)out, er, ring, pos);
+    hipLaunchKernelGGL((attend_ds<0, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)pool, (int64_t)0,
+                       idx, (const bf16_t*)state, state_elems, (int64_t)0, sink, (int64_t)1, (int64_t)0, n_comp_max,
+                       (int)n_h, k, m, n_win, scale, 1, part_o, part_ml, (bf16_t*)out, er, ring, pos);
   if (ns > 1)
     hipLaunchKernelGGL(attend_combine, dim3((unsigned)b, (unsigned)n_h), dim3(128), 0, st, part_o, part_ml, sink,
                        (int)n_h, ns, (bf16_t*)out);
