@@ -183,12 +183,19 @@ __device__ __forceinline__ void wait_vm() {
 // O += A B on the 32x32x16 bf16 MFMA with O pinned to accumulation registers.
 // This file is compiled with MFMA results in VGPRs (the S^T accumulators are
 // read by VALU code); O alone, 128 registers per lane, is kept in AGPRs by
-// issuing its products (and its zeroing) as asm.  The compiler sees only asm
-// statements, so it neither checks their hazards nor pads for them: compiled
-// code reading O after the last product pads with o_hazard_pad, and operands
-// written by VALU code just before a product wait first (see pv_part).
+// issuing its products as asm (the first product of a query with C = 0, so
+// O needs no zeroing).  The compiler sees only asm statements, so it neither
+// checks their hazards nor pads for them: compiled code reading O after the
+// last product pads with o_hazard_pad, and VALU-written operands wait before
+// the first product that reads them and stay unchanged until a wait after
+// the last (see pv_part).
 __device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8 a, const bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// O = A B (the first product of an accumulation: C is the inline constant 0,
+// so no register holds the zeros)
+__device__ __forceinline__ void mfma_first(f32x16& acc, const bf16x8 a, const bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void o_hazard_pad() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
     return __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], hi[0], hi[1]));
   };
   // O[head][dim] += P E over this wave's 8 column blocks
-  auto pv_part = [&](const unsigned char* B, bf16x8 pa) {
+  auto pv_part = [&](const unsigned char* B, bf16x8 pa, bool first) {
     // pa may come straight from VALU code (the last step has no S product
     // in between) and the asm MFMAs below are opaque to the compiler's
     // hazard checks: wait out the VALU-write / MFMA-read hazard here (pa is
@@ -496,13 +503,20 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
         tr[(nb + 2) % 3][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(B + trB1 + kBlkB * (nb + 2)));
       }
       const bf16x8 bv = __builtin_shufflevector(tr[nb % 3][0], tr[nb % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
-      mfma_acc(o[nb], pa, bv);
+      if (first)
+        mfma_first(o[nb], pa, bv);
+      else
+        mfma_acc(o[nb], pa, bv);
     }
+    // the queued products may still read pa: keep its registers until they have
+    asm volatile("s_nop 7" ::"v"(pa));
   };
   // step i: tile i in Bc (waited for here), tile i+1 in flight, tile i+2
   // gathered into Bf, whose previous tile (i-1) every wave has finished once
   // past the first barrier; the second barrier publishes the partial S^T
-  auto step = [&](int i, const unsigned char* Bc, unsigned char* Bf) {
+  // (first: the first tile, whose P V product starts O; a constant at each
+  // call, so that O's first definition is one asm statement)
+  auto step = [&](int i, const unsigned char* Bc, unsigned char* Bf, bool first) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<R>();
     tile_barrier();
@@ -513,29 +527,23 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
     tile_barrier();
     add_partner(sp);
     const bf16x8 pa = weights(i, sp);
-    pv_part(Bc, pa);
+    pv_part(Bc, pa, first);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   __syncthreads();
   int gen = 0;
   for (;;) {
-    {
-      // O = 0 * 0 + 0, defined straight in the accumulation registers (a
-      // plain zero would be materialised in VGPRs and copied)
-      const bf16x8 z8 = {};
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o[nb]) : "v"(z8));
-    }
     l_part = 0.f;
     issue_tile(0, T0);
     issue_tile(1, T1);
-    for (int it = 0; it < ntiles; it += 3) {
-      step(it, T0, T2);
+    if (ntiles > 0) step(0, T0, T2, true);
+    for (int it = 1; it < ntiles; it += 3) {
+      step(it, T1, T0, false);
       if (it + 1 >= ntiles) break;
-      step(it + 1, T1, T0);
+      step(it + 1, T2, T1, false);
       if (it + 2 >= ntiles) break;
-      step(it + 2, T2, T1);
+      step(it + 2, T0, T2, false);
     }
     wait_vm<0>();   // the look-ahead gathers past the last tile
     o_hazard_pad();
@@ -561,12 +569,14 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
     // per head, from the first dimension half) the maximum and the sum
     const int64_t slot = ((bi * n_q + rq) * (n_h / kHG) + hg) * nsplit + split;
     float* po = part_o + slot * (int64_t)kHG * kC + (int64_t)kHW * hw * kC + 256 * dh + (l & 31);
+    // an empty split (no tiles: O was never written) leaves O = 0 and a
+    // maximum of -inf, which the combine weighs with 0
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int hr = 8 * (r >> 2) + 4 * half + (r & 3);
-        po[hr * (int64_t)kC + nb * 32] = o[nb][r];
+        po[hr * (int64_t)kC + nb * 32] = ntiles > 0 ? o[nb][r] : 0.f;
       }
     if (dh == 0 && l < 32) {
       part_ml[(slot * kHG + kHW * hw + l) * 2 + 0] = m_run;
@@ -618,6 +628,367 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
       *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(ob + hr * (int64_t)kC) + c16 * 16) = v;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the attention, per query (bf16, c = 512, 64-head groups): the
+// softmax statistics, p_j and dl_j of every entry slot, dq and the sink's dz
+// (the entry gradients follow from p and dl in a separate step).  With l_j =
+// scale q.e_j, dP_j = g.e_j, o = sum_j p_j e_j and g.o = sum_j p_j dP_j:
+//   dl_j = p_j (dP_j - g.o),  dq = scale sum_j dl_j e_j,  dz = -p_z g.o.
+// Same workgroup shape, tiles and gathers as attend_ds: four waves, wave w
+// owning heads 32 (w & 1) .. +31 and dimensions 256 (w >> 1) .. +255.  Each
+// wave holds Q and G (= dL/do) of its heads over its dimensions as MFMA
+// operands; per tile it forms partial S^T = E Q^T and dP^T = E G^T over its
+// dimensions and adds its partner's through LDS.  Slots are taken in order,
+// 16 per tile (slot j < ks: the j-th listed entry -- CSA: idx[t][j], valid
+// when 0 <= idx < visible; HCA: entry j, valid when j < visible --; slot
+// ks + i: window row wlo(t) + i, valid when <= t); invalid slots get p = dl
+// = 0 and gather the query's own row.  Pass 1 accumulates the maximum, the
+// denominator and sum_j exp(l_j - max) dP_j per head; pass 2 forms p and dl,
+// stores them and accumulates dq on the 32x32x16 MFMA, dl split into a bf16
+// high part and a bf16 remainder so that the product keeps about 16 bits.
+// ---------------------------------------------------------------------------
+struct BwdSmem {
+  int32_t sel[kMaxSel];   // CSA: idx[t][j], or -1 where not a valid entry
+};
+constexpr int kXB2 = 2 * kXB;   // one wave's partial S^T and dP^T
+
+template <int DENSE>
+__global__ __launch_bounds__(256) void attend_bwd_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ Ccomp, int64_t cbs, const int32_t* __restrict__ idx,
+    const bf16_t* __restrict__ kv_raw, int64_t rbs, int64_t raw_pos0, const float* __restrict__ sink,
+    const bf16_t* __restrict__ dout, int64_t n_q, int64_t t0, int64_t n_comp, int n_h, int64_t k, int64_t m,
+    int64_t n_win, int64_t ks, int64_t nslot, float scale, float* __restrict__ P, float* __restrict__ DL,
+    float* __restrict__ dq, float* __restrict__ dz) {
+  constexpr int NW = 4;
+  constexpr int R = kT / NW;
+  __shared__ BwdSmem sm;
+  __shared__ __attribute__((aligned(16))) unsigned char T0[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char T1[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char T2[kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char XB[NW * kXB2];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int half = l >> 5;
+  const int g4 = l >> 4;
+  const bool up16 = (l & 16) != 0;
+  const int s16 = l & 15;
+  const int hw = wave & 1;
+  const int dh = wave >> 1;
+  const int64_t rq = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int64_t bi = blockIdx.z;
+  const int64_t t = t0 + rq;
+  const int head0 = kHG * hg + kHW * hw;
+  int64_t vis = (t + 1) / m;
+  if (vis > n_comp) vis = n_comp;
+  const int64_t wlo = t - n_win + 1 > 0 ? t - n_win + 1 : 0;
+  if (!DENSE) {
+    const int32_t* ir = idx + (bi * n_q + rq) * k;
+    for (int64_t j = tid; j < k; j += 64 * NW) {
+      const int32_t v = ir[j];
+      sm.sel[j] = (v >= 0 && v < vis) ? v : -1;
+    }
+  }
+  bf16x8 qB[8][2], gB[8][2];
+  {
+    const int64_t off = ((bi * n_q + rq) * n_h + head0 + s16) * (int64_t)kC + 256 * dh + 8 * g4;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 8; ++ks2)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        qB[ks2][hb] = *reinterpret_cast<const bf16x8*>(q + off + hb * 16 * kC + ks2 * 32);
+        gB[ks2][hb] = *reinterpret_cast<const bf16x8*>(dout + off + hb * 16 * kC + ks2 * 32);
+      }
+    // the operands must have arrived before the first gather is issued (the
+    // compiler does not count the gathers)
+#pragma unroll
+    for (int ks2 = 0; ks2 < 8; ++ks2)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) asm volatile("" ::"v"(qB[ks2][hb]), "v"(gB[ks2][hb]));
+  }
+  __syncthreads();   // sel
+
+  const int ntiles = (int)((nslot + kT - 1) / kT);
+  const bf16_t* cbase = Ccomp + bi * cbs;
+  const bf16_t* rbase = kv_raw + bi * rbs;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int grow = s16 ^ (4 * g4);
+  // the row slot j reads, or -1 for an invalid slot
+  auto slot_row = [&](int64_t j, bool& comp) -> int64_t {
+    comp = j < ks;
+    if (j >= nslot) return -1;
+    if (comp) {
+      if (DENSE) return j < vis ? j : -1;
+      return (int64_t)sm.sel[j];
+    }
+    const int64_t p = wlo + (j - ks);
+    return p <= t ? p : -1;
+  };
+  auto issue_tile = [&](int ti, unsigned char* buf) {
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)buf);
+    bool comp;
+    const int64_t e = slot_row((int64_t)ti * kT + grow, comp);
+    const bf16_t* p = (e < 0 ? rbase + (t - raw_pos0) * (int64_t)kC
+                             : (comp ? cbase + e * kC : rbase + (e - raw_pos0) * (int64_t)kC)) + 8 * g4;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int b = wave_u + rr * NW;
+      attn_dma16(p + 32 * b, lbase + (uint32_t)(b * kBlkB));
+    }
+  };
+
+  const int sA = g4 * 256 + ((s16 ^ (4 * g4)) * 16) + kBlkB * 8 * dh;
+  const int cpart = 2 * (g4 & 1) + ((s16 & 3) >> 1);
+  auto trbase = [&](int row) { return cpart * 256 + ((row ^ (4 * cpart)) * 16) + 8 * (s16 & 1); };
+  const int trB0 = trbase(8 * half + (s16 >> 2)) + kBlkB * 8 * dh;
+  const int trB1 = trbase(8 * half + 4 + (s16 >> 2)) + kBlkB * 8 * dh;
+  const float sl2 = scale * kLog2e;
+  f32x16 o[8];
+
+  // partial S^T and dP^T of one tile over this wave's 256 dimensions
+  auto sd_part = [&](const unsigned char* B, f32x4 (&sp)[2], f32x4 (&dp)[2]) {
+    f32x4 c0 = (f32x4){}, c1 = (f32x4){}, c2 = (f32x4){}, c3 = (f32x4){};
+    const unsigned char* a = B + sA;
+    constexpr int D = 2;
+    bf16x8 av[D + 1];
+#pragma unroll
+    for (int u = 0; u < D; ++u) av[u] = *reinterpret_cast<const bf16x8*>(a + kBlkB * u);
+#pragma unroll
+    for (int ks2 = 0; ks2 < 8; ++ks2) {
+      if (ks2 + D < 8) av[(ks2 + D) % (D + 1)] = *reinterpret_cast<const bf16x8*>(a + kBlkB * (ks2 + D));
+      const bf16x8 x = av[ks2 % (D + 1)];
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qB[ks2][0], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qB[ks2][1], c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, gB[ks2][0], c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, gB[ks2][1], c3, 0, 0, 0);
+    }
+    sp[0] = c0;
+    sp[1] = c1;
+    dp[0] = c2;
+    dp[1] = c3;
+  };
+  auto exchange = [&](f32x4 (&sp)[2], f32x4 (&dp)[2]) {
+    unsigned char* x = XB + wave * kXB2 + 16 * l;
+    *reinterpret_cast<f32x4*>(x) = sp[0];
+    *reinterpret_cast<f32x4*>(x + 1024) = sp[1];
+    *reinterpret_cast<f32x4*>(x + 2048) = dp[0];
+    *reinterpret_cast<f32x4*>(x + 3072) = dp[1];
+    tile_barrier();
+    const unsigned char* y = XB + (wave ^ 2) * kXB2 + 16 * l;
+    sp[0] += *reinterpret_cast<const f32x4*>(y);
+    sp[1] += *reinterpret_cast<const f32x4*>(y + 1024);
+    dp[0] += *reinterpret_cast<const f32x4*>(y + 2048);
+    dp[1] += *reinterpret_cast<const f32x4*>(y + 3072);
+  };
+  // validity of this lane's 4 slots of tile ti (slots 16 ti + 4 (l/16) + r)
+  auto valid4 = [&](int ti, bool (&v)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bool comp;
+      v[r] = slot_row((int64_t)ti * kT + 4 * g4 + r, comp) >= 0;
+    }
+  };
+  // one pass over the tiles; body(i, Bc, sp, dp, first) runs after the
+  // exchange (first: a constant at each call, true for tile 0 only)
+  auto run_pass = [&](auto&& body) {
+    issue_tile(0, T0);
+    issue_tile(1, T1);
+    auto step = [&](int i, const unsigned char* Bc, unsigned char* Bf, bool first) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<R>();
+      tile_barrier();
+      issue_tile(i + 2, Bf);
+      f32x4 sp[2], dp[2];
+      sd_part(Bc, sp, dp);
+      exchange(sp, dp);
+      body(i, Bc, sp, dp, first);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    step(0, T0, T2, true);   // ntiles >= 1: the query's own window row
+    for (int it = 1; it < ntiles; it += 3) {
+      step(it, T1, T0, false);
+      if (it + 1 >= ntiles) break;
+      step(it + 1, T2, T1, false);
+      if (it + 2 >= ntiles) break;
+      step(it + 2, T0, T2, false);
+    }
+    wait_vm<0>();
+    tile_barrier();   // every wave is done with the buffers before they are reused
+  };
+
+  // pass 1: per lane and head block, running max (log2 domain), sum of
+  // weights and sum of weights times dP over the lane's slots
+  float mx[2] = {-INFINITY, -INFINITY}, den[2] = {0.f, 0.f}, acc[2] = {0.f, 0.f};
+  run_pass([&](int i, const unsigned char*, f32x4 (&sp)[2], f32x4 (&dp)[2], bool) {
+    bool v[4];
+    valid4(i, v);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float lg[4], tm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        lg[r] = v[r] ? sp[hb][r] * sl2 : -INFINITY;
+        tm = fmaxf(tm, lg[r]);
+      }
+      const float nm = fmaxf(mx[hb], tm);
+      if (nm != -INFINITY) {
+        const float f = __builtin_amdgcn_exp2f(mx[hb] - nm);   // 0 while mx is -inf
+        float sw = 0.f, swd = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float w = __builtin_amdgcn_exp2f(lg[r] - nm);
+          sw += w;
+          swd = fmaf(w, dp[hb][r], swd);
+        }
+        den[hb] = den[hb] * f + sw;
+        acc[hb] = acc[hb] * f + swd;
+        mx[hb] = nm;
+      }
+    }
+  });
+  // combine the four lanes that hold a head (l, l ^ 16, l ^ 32, l ^ 48),
+  // then add the sink: final max Mf, denominator Lt, g.o per head block
+  float Mf[2], Lt[2], go[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float m2, d2, a2;
+      if (st == 0) {
+        m2 = __uint_as_float(from_lane_xor16(__float_as_uint(mx[hb]), up16));
+        d2 = __uint_as_float(from_lane_xor16(__float_as_uint(den[hb]), up16));
+        a2 = __uint_as_float(from_lane_xor16(__float_as_uint(acc[hb]), up16));
+      } else {
+        const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[hb]), __float_as_uint(mx[hb]), false, false);
+        const auto rd = __builtin_amdgcn_permlane32_swap(__float_as_uint(den[hb]), __float_as_uint(den[hb]), false, false);
+        const auto ra = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[hb]), __float_as_uint(acc[hb]), false, false);
+        // {x[l & ~32], x[l | 32]}: the other half's value
+        m2 = __uint_as_float(half ? rm[0] : rm[1]);
+        d2 = __uint_as_float(half ? rd[0] : rd[1]);
+        a2 = __uint_as_float(half ? ra[0] : ra[1]);
+      }
+      const float nm = fmaxf(mx[hb], m2);
+      const float f1 = nm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx[hb] - nm);
+      const float f2 = nm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - nm);
+      den[hb] = den[hb] * f1 + d2 * f2;
+      acc[hb] = acc[hb] * f1 + a2 * f2;
+      mx[hb] = nm;
+    }
+    const float z2 = sink[head0 + 16 * hb + s16] * kLog2e;
+    Mf[hb] = fmaxf(mx[hb], z2);
+    const float f = mx[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx[hb] - Mf[hb]);
+    const float pz = __builtin_amdgcn_exp2f(z2 - Mf[hb]);
+    Lt[hb] = den[hb] * f + pz;
+    go[hb] = acc[hb] * f / Lt[hb];
+    if (dh == 0 && g4 == 0)
+      dz[(bi * n_q + rq) * n_h + head0 + 16 * hb + s16] = -(pz / Lt[hb]) * go[hb];
+  }
+
+  // pass 2: p and dl of every slot, stored, and dq += dl E
+  const float inv[2] = {1.f / Lt[0], 1.f / Lt[1]};
+  auto pack2 = [](float a, float b) -> uint32_t {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+  };
+  // A operand of the 32x32x16 MFMA (head l%32, entries 8(l/32)..+7) from this
+  // lane's values of its 4 entries of both head blocks (as in attend_ds)
+  auto a_operand = [&](const uint32_t (&pk)[2][2]) -> bf16x8 {
+    uint32_t own[2], lo[2], hi[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      own[i] = up16 ? pk[1][i] : pk[0][i];
+      const uint32_t recv = from_lane_xor16(up16 ? pk[0][i] : pk[1][i], up16);
+      lo[i] = up16 ? recv : own[i];
+      hi[i] = up16 ? own[i] : recv;
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], hi[0], hi[1]));
+  };
+  run_pass([&](int i, const unsigned char* Bc, f32x4 (&sp)[2], f32x4 (&dp)[2], bool first) {
+    bool v[4];
+    valid4(i, v);
+    uint32_t hiw[2][2], low[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float pr[4], dl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = v[r] ? __builtin_amdgcn_exp2f(sp[hb][r] * sl2 - Mf[hb]) * inv[hb] : 0.f;
+        dl[r] = pr[r] * (dp[hb][r] - go[hb]);
+      }
+      if (dh == 0) {
+        const int64_t slot0 = (int64_t)i * kT + 4 * g4;
+        const int64_t prow = ((bi * n_q + rq) * n_h + head0 + 16 * hb + s16) * nslot;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (slot0 + r < nslot) {
+            P[prow + slot0 + r] = pr[r];
+            DL[prow + slot0 + r] = dl[r];
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const uint32_t h2 = pack2(dl[r], dl[r + 1]);
+        hiw[hb][r >> 1] = h2;
+        low[hb][r >> 1] = pack2(dl[r] - __uint_as_float(h2 << 16), dl[r + 1] - __uint_as_float(h2 & 0xffff0000u));
+      }
+    }
+    bf16x8 ah = a_operand(hiw), al = a_operand(low);
+    // the operands come from VALU code just above, and the asm MFMAs below
+    // are opaque to the compiler's hazard checks
+    asm volatile("s_nop 4" : "+v"(ah), "+v"(al));
+    bf16x4 tr[3][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      tr[u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Bc + trB0 + kBlkB * u));
+      tr[u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Bc + trB1 + kBlkB * u));
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      if (nb + 2 < 8) {
+        tr[(nb + 2) % 3][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Bc + trB0 + kBlkB * (nb + 2)));
+        tr[(nb + 2) % 3][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Bc + trB1 + kBlkB * (nb + 2)));
+      }
+      const bf16x8 bv = __builtin_shufflevector(tr[nb % 3][0], tr[nb % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      if (first)
+        mfma_first(o[nb], ah, bv);
+      else
+        mfma_acc(o[nb], ah, bv);
+      mfma_acc(o[nb], al, bv);
+    }
+    // the queued products may still read ah and al
+    asm volatile("s_nop 7" ::"v"(ah), "v"(al));
+  });
+  o_hazard_pad();
+  // dq = scale * O over this wave's heads and dimensions
+  float* dqp = dq + ((bi * n_q + rq) * n_h + head0) * (int64_t)kC + 256 * dh + (l & 31);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hr = 8 * (r >> 2) + 4 * half + (r & 3);
+      dqp[hr * (int64_t)kC + nb * 32] = scale * o[nb][r];
+    }
+}
+
+bool attend_bwd_mfma_ok(int dtype, int64_t n_h, int64_t c, int64_t k) {
+  return dtype == 1 && c == kC && n_h % kHG == 0 && k <= kMaxSel;
+}
+
+hipError_t launch_attend_bwd_mfma(int dense, const void* q, const void* Ccomp, int64_t cbs, const int32_t* idx,
+                                  const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink,
+                                  const void* dout, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
+                                  int64_t k, int64_t m, int64_t n_win, int64_t ks, int64_t nslot, float scale,
+                                  float* P, float* DL, float* dq, float* dz, hipStream_t st) {
+  const dim3 grid((unsigned)n_q, (unsigned)(n_h / kHG), (unsigned)b);
+  if (dense)
+    hipLaunchKernelGGL(attend_bwd_mfma<1>, grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx,
+                       (const bf16_t*)kv_raw, rbs, raw_pos0, sink, (const bf16_t*)dout, n_q, t0, n_comp, (int)n_h, k,
+                       m, n_win, ks, nslot, scale, P, DL, dq, dz);
+  else
+    hipLaunchKernelGGL(attend_bwd_mfma<0>, grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx,
+                       (const bf16_t*)kv_raw, rbs, raw_pos0, sink, (const bf16_t*)dout, n_q, t0, n_comp, (int)n_h, k,
+                       m, n_win, ks, nslot, scale, P, DL, dq, dz);
+  return hipGetLastError();
 }
 
 // Merge the splits of one (query, head) in split order (log2-domain maxima),

@@ -344,7 +344,14 @@ hipError_t launch_attend_backward(int dense, const void* q, const void* Ccomp, i
   const dim3 qgrid((unsigned)n_q, (unsigned)n_h, (unsigned)b);
   const dim3 cgrid((unsigned)n_q, (unsigned)((G.nslot + kSlotsPerWG - 1) / kSlotsPerWG), (unsigned)b);
   const size_t csh = (size_t)n_h * 2 * kSlotsPerWG * 4;
-  if (dtype == 1) {
+  if (attend_bwd_mfma_ok(dtype, n_h, c, dense ? 0 : k)) {
+    // bf16, c = 512, 64-head groups: the per-query step on MFMA
+    const hipError_t e = launch_attend_bwd_mfma(dense, q, Ccomp, cbs, idx, kv_raw, rbs, raw_pos0, sink, dout, b, n_q,
+                                                t0, n_comp, n_h, k, m, n_win, G.ks, G.nslot, scale, P, DL, dq, dz, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attend_bwd_contrib<bf16_t>, cgrid, dim3(kBwdT), csh, st, G, (const bf16_t*)q,
+                       (const bf16_t*)dout, P, DL, contrib);
+  } else if (dtype == 1) {
     hipLaunchKernelGGL(attend_bwd_query<bf16_t>, qgrid, dim3(kBwdT), 0, st, G, (const bf16_t*)q, (const bf16_t*)Ccomp,
                        cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink, (const bf16_t*)dout, P, DL, dq, dz);
     hipLaunchKernelGGL(attend_bwd_contrib<bf16_t>, cgrid, dim3(kBwdT), csh, st, G, (const bf16_t*)q,
