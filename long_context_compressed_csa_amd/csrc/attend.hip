@@ -633,7 +633,8 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
 // ---------------------------------------------------------------------------
 // Backward of the attention, per query (bf16, c = 512, 64-head groups): the
 // softmax statistics, p_j and dl_j of every entry slot, dq and the sink's dz
-// (the entry gradients follow from p and dl in a separate step).  With l_j =
+// (the entry gradients follow from p and dl in a separate step; p and dl
+// are stored [row][slot][head]).  With l_j =
 // scale q.e_j, dP_j = g.e_j, o = sum_j p_j e_j and g.o = sum_j p_j dP_j:
 //   dl_j = p_j (dP_j - g.o),  dq = scale sum_j dl_j e_j,  dz = -p_z g.o.
 // Same workgroup shape, tiles and gathers as attend_ds: four waves, wave w
@@ -916,13 +917,14 @@ __global__ __launch_bounds__(256) void attend_bwd_mfma(
         dl[r] = pr[r] * (dp[hb][r] - go[hb]);
       }
       if (dh == 0) {
+        // [row][slot][head]: the heads of a slot are contiguous
         const int64_t slot0 = (int64_t)i * kT + 4 * g4;
-        const int64_t prow = ((bi * n_q + rq) * n_h + head0 + 16 * hb + s16) * nslot;
+        const int64_t base = (bi * n_q + rq) * nslot;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (slot0 + r < nslot) {
-            P[prow + slot0 + r] = pr[r];
-            DL[prow + slot0 + r] = dl[r];
+            P[(base + slot0 + r) * n_h + head0 + 16 * hb + s16] = pr[r];
+            DL[(base + slot0 + r) * n_h + head0 + 16 * hb + s16] = dl[r];
           }
       }
 #pragma unroll
@@ -968,6 +970,124 @@ __global__ __launch_bounds__(256) void attend_bwd_mfma(
       const int hr = 8 * (r >> 2) + 4 * half + (r & 3);
       dqp[hr * (int64_t)kC + nb * 32] = scale * o[nb][r];
     }
+}
+
+// Entry contributions of one query (64 heads, bf16, c = 512):
+//   contrib[t][j][:] = sum_h p[t][j][h] g_h + scale dl[t][j][h] q_h
+// for every slot j, a product over the heads: A = p (and scale dl) of 32
+// slots x 16 heads, split into a bf16 high part and remainder; B = G (and
+// Q) of 16 heads x 32 dimensions, bf16 as given.  One workgroup per query;
+// wave w owns dimensions 128 w .. +127 and keeps its B operands of all 64
+// heads in registers (loaded once through LDS, transposed by the tile read
+// of the attention's P V product), then walks the slots 32 at a time.
+__global__ __launch_bounds__(256) void attend_bwd_contrib_mfma(const bf16_t* __restrict__ q,
+                                                               const bf16_t* __restrict__ dout,
+                                                               const float* __restrict__ P,
+                                                               const float* __restrict__ DL, int64_t nslot,
+                                                               float scale, float* __restrict__ contrib) {
+  constexpr int NW = 4;
+  constexpr int R = kT / NW;
+  __shared__ __attribute__((aligned(16))) unsigned char GQ[8][kTileB];   // heads 16 i .. +15 of G (i < 4), Q (i >= 4)
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int half = l >> 5;
+  const int g4 = l >> 4;
+  const int s16 = l & 15;
+  const int64_t row = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;   // b * n_q + r
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int grow = s16 ^ (4 * g4);
+  // stage: tile i holds head rows 16 (i % 4) + 0..15 of G (i < 4) or Q
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16_t* src = (i < 4 ? dout : q) + (row * kHG + 16 * (i & 3) + grow) * (int64_t)kC + 8 * g4;
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&GQ[i][0]);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int b = wave_u + rr * NW;
+      attn_dma16(src + 32 * b, lbase + (uint32_t)(b * kBlkB));
+    }
+  }
+  wait_vm<0>();
+  __syncthreads();
+  // B operands: column block cb = 4 w + c, heads 16 kb + 8 (l/32) .. +7
+  const int cpart = 2 * (g4 & 1) + ((s16 & 3) >> 1);
+  auto trbase = [&](int r) { return cpart * 256 + ((r ^ (4 * cpart)) * 16) + 8 * (s16 & 1); };
+  const int trB0 = trbase(8 * half + (s16 >> 2)), trB1 = trbase(8 * half + 4 + (s16 >> 2));
+  bf16x8 Bg[4][4], Bq[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int cb = 4 * wave + c;
+      const bf16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(&GQ[kb][0] + trB0 + kBlkB * cb));
+      const bf16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(&GQ[kb][0] + trB1 + kBlkB * cb));
+      const bf16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(&GQ[4 + kb][0] + trB0 + kBlkB * cb));
+      const bf16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(&GQ[4 + kb][0] + trB1 + kBlkB * cb));
+      Bg[kb][c] = __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7);
+      Bq[kb][c] = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  auto split8 = [](const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+    uint32_t h[4], r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v[2 * i], v[2 * i + 1]}, bf16x2_t));
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                              (f32x2_t){v[2 * i] - __uint_as_float(h[i] << 16),
+                                                        v[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u)},
+                                              bf16x2_t));
+    }
+    hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(r[0], r[1], r[2], r[3]));
+  };
+  for (int64_t s0 = 0; s0 < nslot; s0 += 32) {
+    // A operands: slot s0 + l%32, heads 16 kb + 8 (l/32) .. +7
+    const int64_t slot = s0 + (l & 31);
+    const bool ok = slot < nslot;
+    const float* pr = P + (row * nslot + (ok ? slot : 0)) * kHG + 8 * half;
+    const float* dr = DL + (row * nslot + (ok ? slot : 0)) * kHG + 8 * half;
+    f32x16 acc[4] = {};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float pv[8], dv[8];
+      const float4 p0 = *reinterpret_cast<const float4*>(pr + 16 * kb);
+      const float4 p1 = *reinterpret_cast<const float4*>(pr + 16 * kb + 4);
+      const float4 d0 = *reinterpret_cast<const float4*>(dr + 16 * kb);
+      const float4 d1 = *reinterpret_cast<const float4*>(dr + 16 * kb + 4);
+      pv[0] = p0.x; pv[1] = p0.y; pv[2] = p0.z; pv[3] = p0.w; pv[4] = p1.x; pv[5] = p1.y; pv[6] = p1.z; pv[7] = p1.w;
+      dv[0] = d0.x; dv[1] = d0.y; dv[2] = d0.z; dv[3] = d0.w; dv[4] = d1.x; dv[5] = d1.y; dv[6] = d1.z; dv[7] = d1.w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = ok ? pv[i] : 0.f;
+        dv[i] = ok ? scale * dv[i] : 0.f;
+      }
+      bf16x8 ph, pl, dh, dlo;
+      split8(pv, ph, pl);
+      split8(dv, dh, dlo);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, Bg[kb][c], acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, Bg[kb][c], acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dh, Bq[kb][c], acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dlo, Bq[kb][c], acc[c], 0, 0, 0);
+      }
+    }
+    // rows (slots) 8 (r/4) + 4 (l/32) + r%4 of column (dimension) 32 cb + l%32
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t sl = s0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (sl < nslot) contrib[(row * nslot + sl) * kC + 32 * (4 * wave + c) + (l & 31)] = acc[c][r];
+      }
+  }
+}
+
+bool attend_bwd_contrib_mfma_ok(int dtype, int64_t n_h, int64_t c) { return dtype == 1 && c == kC && n_h == kHG; }
+
+hipError_t launch_attend_bwd_contrib_mfma(const void* q, const void* dout, const float* P, const float* DL, int64_t b,
+                                          int64_t n_q, int64_t nslot, float scale, float* contrib, hipStream_t st) {
+  hipLaunchKernelGGL(attend_bwd_contrib_mfma, dim3((unsigned)n_q, 1u, (unsigned)b), dim3(256), 0, st,
+                     (const bf16_t*)q, (const bf16_t*)dout, P, DL, nslot, scale, contrib);
+  return hipGetLastError();
 }
 
 bool attend_bwd_mfma_ok(int dtype, int64_t n_h, int64_t c, int64_t k) {

@@ -181,10 +181,12 @@ __global__ __launch_bounds__(kBwdT) void attend_bwd_query(
 // contrib[b][n_q][nslot][c] = sum over heads h (in order) of
 //   P[h][slot] g_h + scale DL[h][slot] q_h, for 16 slots per workgroup.
 constexpr int kSlotsPerWG = 16;
+// P and DL are [b][n_q][n_h][nslot] (slot_major = 0, the vector path's
+// layout) or [b][n_q][nslot][n_h] (slot_major = 1, the MFMA path's).
 template <typename T>
 __global__ __launch_bounds__(kBwdT) void attend_bwd_contrib(BwdGeom G, const T* __restrict__ q,
                                                             const T* __restrict__ dout, const float* __restrict__ P,
-                                                            const float* __restrict__ DL,
+                                                            const float* __restrict__ DL, int slot_major,
                                                             float* __restrict__ contrib) {
   extern __shared__ float pd[];   // [n_h][2][kSlotsPerWG]
   const int tid = threadIdx.x;
@@ -196,8 +198,9 @@ __global__ __launch_bounds__(kBwdT) void attend_bwd_contrib(BwdGeom G, const T* 
   for (int e = tid; e < nh * kSlotsPerWG; e += kBwdT) {
     const int h = e / kSlotsPerWG, s = e % kSlotsPerWG;
     const bool ok = s < ns;
-    pd[(h * 2 + 0) * kSlotsPerWG + s] = ok ? P[(prow0 + h) * G.nslot + s0 + s] : 0.f;
-    pd[(h * 2 + 1) * kSlotsPerWG + s] = ok ? G.scale * DL[(prow0 + h) * G.nslot + s0 + s] : 0.f;
+    const int64_t at = slot_major ? ((bi * G.n_q + r) * G.nslot + s0 + s) * nh + h : (prow0 + h) * G.nslot + s0 + s;
+    pd[(h * 2 + 0) * kSlotsPerWG + s] = ok ? P[at] : 0.f;
+    pd[(h * 2 + 1) * kSlotsPerWG + s] = ok ? G.scale * DL[at] : 0.f;
   }
   __syncthreads();
   for (int d0 = 0; d0 < c; d0 += kBwdT) {
@@ -349,18 +352,23 @@ hipError_t launch_attend_backward(int dense, const void* q, const void* Ccomp, i
     const hipError_t e = launch_attend_bwd_mfma(dense, q, Ccomp, cbs, idx, kv_raw, rbs, raw_pos0, sink, dout, b, n_q,
                                                 t0, n_comp, n_h, k, m, n_win, G.ks, G.nslot, scale, P, DL, dq, dz, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_bwd_contrib<bf16_t>, cgrid, dim3(kBwdT), csh, st, G, (const bf16_t*)q,
-                       (const bf16_t*)dout, P, DL, contrib);
+    if (attend_bwd_contrib_mfma_ok(dtype, n_h, c)) {
+      const hipError_t e2 = launch_attend_bwd_contrib_mfma(q, dout, P, DL, b, n_q, G.nslot, scale, contrib, st);
+      if (e2 != hipSuccess) return e2;
+    } else {
+      hipLaunchKernelGGL(attend_bwd_contrib<bf16_t>, cgrid, dim3(kBwdT), csh, st, G, (const bf16_t*)q,
+                         (const bf16_t*)dout, P, DL, 1, contrib);
+    }
   } else if (dtype == 1) {
     hipLaunchKernelGGL(attend_bwd_query<bf16_t>, qgrid, dim3(kBwdT), 0, st, G, (const bf16_t*)q, (const bf16_t*)Ccomp,
                        cbs, idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink, (const bf16_t*)dout, P, DL, dq, dz);
     hipLaunchKernelGGL(attend_bwd_contrib<bf16_t>, cgrid, dim3(kBwdT), csh, st, G, (const bf16_t*)q,
-                       (const bf16_t*)dout, P, DL, contrib);
+                       (const bf16_t*)dout, P, DL, 0, contrib);
   } else {
     hipLaunchKernelGGL(attend_bwd_query<float>, qgrid, dim3(kBwdT), 0, st, G, (const float*)q, (const float*)Ccomp,
                        cbs, idx, (const float*)kv_raw, rbs, raw_pos0, sink, (const float*)dout, P, DL, dq, dz);
     hipLaunchKernelGGL(attend_bwd_contrib<float>, cgrid, dim3(kBwdT), csh, st, G, (const float*)q,
-                       (const float*)dout, P, DL, contrib);
+                       (const float*)dout, P, DL, 0, contrib);
   }
   if (n_comp > 0)
     hipLaunchKernelGGL(attend_bwd_reduce_comp, dim3((unsigned)n_comp, (unsigned)b), dim3(kBwdT), 0, st, G, idx,

@@ -101,6 +101,9 @@ hipError_t launch_attend_bwd_mfma(int dense, const void* q, const void* Ccomp, i
                                   const void* dout, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,
                                   int64_t k, int64_t m, int64_t n_win, int64_t ks, int64_t nslot, float scale,
                                   float* P, float* DL, float* dq, float* dz, hipStream_t st);
+bool attend_bwd_contrib_mfma_ok(int dtype, int64_t n_h, int64_t c);
+hipError_t launch_attend_bwd_contrib_mfma(const void* q, const void* dout, const float* P, const float* DL, int64_t b,
+                                          int64_t n_q, int64_t nslot, float scale, float* contrib, hipStream_t st);
 size_t attend_backward_workspace_bytes(int64_t b, int64_t n_q, int64_t n_h, int64_t c, int64_t ks, int64_t n_win);
 hipError_t launch_attend_backward(int dense, const void* q, const void* Ccomp, int64_t cbs, const int32_t* idx,
                                   const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink,

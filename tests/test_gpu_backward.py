@@ -67,6 +67,7 @@ def _csa_case(n, nh, c, k, nw, m, dtype, seed, unscaled=True):
     (64, 4, 32, 4, 16, 4, torch.float32),      # the tiny layer's shape
     (96, 3, 40, 7, 9, 4, torch.float32),       # ragged slot tiles, odd sizes
     (256, 64, 512, 32, 64, 4, torch.bfloat16), # the layer's head shape
+    (72, 128, 512, 8, 16, 4, torch.bfloat16),  # two head groups (per-query step on MFMA, contributions not)
 ])
 def test_csa_attend_backward(n, nh, c, k, nw, m, dtype):
     say(f"csa attend backward n={n} n_h={nh} c={c} k={k} n_win={nw} {dtype}")
