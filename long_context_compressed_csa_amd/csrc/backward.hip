@@ -238,14 +238,38 @@ __device__ __forceinline__ int64_t bwd_slot_of(const BwdGeom& G, const int32_t* 
   return (lo < G.k && row[lo] == s) ? lo : -1;
 }
 
+// Inverse slot table of a CSA backward call: inv[b][s][r] = the slot of
+// entry s in query r's list (the lowest, should a row list it twice), or a
+// value >= k where r does not read s.  Built by a fill and a scatter of
+// every valid listed entry (atomicMin: the result does not depend on the
+// order of the writes).
+__global__ __launch_bounds__(kBwdT) void bwd_inv_fill(int32_t* __restrict__ inv, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * kBwdT + threadIdx.x; i < count; i += (int64_t)gridDim.x * kBwdT)
+    inv[i] = 0x7fffffff;
+}
+__global__ __launch_bounds__(kBwdT) void bwd_inv_scatter(BwdGeom G, const int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ inv) {
+  const int64_t r = blockIdx.x, bi = blockIdx.y;
+  const int64_t vis = G.vis(G.t_of(r));
+  const int32_t* row = idx + (bi * G.n_q + r) * G.k;
+  for (int64_t j = threadIdx.x; j < G.k; j += kBwdT) {
+    const int32_t s = row[j];
+    if (s >= 0 && s < vis) atomicMin(&inv[(bi * G.n_comp + s) * G.n_q + r], (int32_t)j);
+  }
+}
+
 // dCcomp[b][s] (+)= sum over the block's queries t (ascending) of
 // contrib[t][slot(t, s)].  One workgroup per (entry, sequence); the queries
-// are searched 256 at a time, the found ones summed in query order.
+// are looked up 256 at a time (in the inverse table when there is one, else
+// by a search of each query's list), the found ones compacted in query
+// order and their contributions summed in that order.
 __global__ __launch_bounds__(kBwdT) void attend_bwd_reduce_comp(BwdGeom G, const int32_t* __restrict__ idx,
+                                                                const int32_t* __restrict__ inv,
                                                                 const float* __restrict__ contrib, int accumulate,
                                                                 float* __restrict__ dC, int64_t dcbs) {
-  __shared__ int32_t slot[kBwdT];
-  const int tid = threadIdx.x;
+  __shared__ int32_t fr[kBwdT], fj[kBwdT];
+  __shared__ int32_t wcnt[kBwdT / 64];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int64_t s = blockIdx.x, bi = blockIdx.y;
   const int c = G.c;
   float acc[kBwdMaxC / kBwdT] = {};
@@ -254,19 +278,50 @@ __global__ __launch_bounds__(kBwdT) void attend_bwd_reduce_comp(BwdGeom G, const
   if (r_first < 0) r_first = 0;
   for (int64_t r0 = r_first; r0 < G.n_q; r0 += kBwdT) {
     const int64_t r = r0 + tid;
-    __syncthreads();
-    slot[tid] = r < G.n_q ? (int32_t)bwd_slot_of(G, idx, bi, r, s) : -1;
-    __syncthreads();
-    const int cnt = (int)(G.n_q - r0 < kBwdT ? G.n_q - r0 : kBwdT);
-    for (int i = 0; i < cnt; ++i) {
-      const int32_t j = slot[i];
-      if (j < 0) continue;
-      const float* src = contrib + ((bi * G.n_q + r0 + i) * G.nslot + j) * (int64_t)c;
-#pragma unroll
-      for (int u = 0; u < kBwdMaxC / kBwdT; ++u) {
-        const int d = tid + kBwdT * u;
-        if (d < c) acc[u] += src[d];
+    int32_t j = -1;
+    if (r < G.n_q) {
+      if (inv) {
+        const int32_t v = inv[(bi * G.n_comp + s) * G.n_q + r];
+        j = v < G.k ? v : -1;
+      } else {
+        j = (int32_t)bwd_slot_of(G, idx, bi, r, s);
       }
+    }
+    const uint64_t mk = __builtin_amdgcn_ballot_w64(j >= 0);
+    __syncthreads();   // the previous round's list has been read
+    if (l == 0) wcnt[wave] = __popcll(mk);
+    __syncthreads();
+    int pos = __popcll(mk & ((l == 0) ? 0ull : (~0ull >> (64 - l))));
+    int nf = 0;
+#pragma unroll
+    for (int w = 0; w < kBwdT / 64; ++w) {
+      pos += w < wave ? wcnt[w] : 0;
+      nf += wcnt[w];
+    }
+    if (j >= 0) {
+      fr[pos] = (int32_t)(r - r0);
+      fj[pos] = j;
+    }
+    __syncthreads();
+    // eight rows' loads in flight at a time, added in list order
+    constexpr int B8 = 8;
+    for (int i0 = 0; i0 < nf; i0 += B8) {
+      float v[B8][kBwdMaxC / kBwdT];
+#pragma unroll
+      for (int b8 = 0; b8 < B8; ++b8) {
+        const int i = i0 + b8 < nf ? i0 + b8 : i0;
+        const float* src = contrib + ((bi * G.n_q + r0 + fr[i]) * G.nslot + fj[i]) * (int64_t)c;
+#pragma unroll
+        for (int u = 0; u < kBwdMaxC / kBwdT; ++u) {
+          const int d = tid + kBwdT * u;
+          v[b8][u] = d < c ? src[d] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int b8 = 0; b8 < B8; ++b8)
+        if (i0 + b8 < nf)
+#pragma unroll
+          for (int u = 0; u < kBwdMaxC / kBwdT; ++u) acc[u] += v[b8][u];
     }
   }
 #pragma unroll
@@ -289,16 +344,30 @@ __global__ __launch_bounds__(kBwdT) void attend_bwd_reduce_raw(BwdGeom G, int64_
   const int64_t p = raw_pos0 + i;
   const int c = G.c;
   float acc[kBwdMaxC / kBwdT] = {};
-  for (int64_t t = p; t < p + G.n_win; ++t) {
-    const int64_t r = t - G.t0;
-    if (r < 0 || r >= G.n_q) continue;
-    const int64_t j = G.ks + (p - G.wlo(t));
-    const float* src = contrib + ((bi * G.n_q + r) * G.nslot + j) * (int64_t)c;
+  // the queries t = p .. p + n_win - 1 inside this block, ascending, eight
+  // rows' loads in flight at a time
+  int64_t tlo = p, thi = p + G.n_win;   // [tlo, thi)
+  if (tlo < G.t0) tlo = G.t0;
+  if (thi > G.t0 + G.n_q) thi = G.t0 + G.n_q;
+  constexpr int B8 = 8;
+  for (int64_t t0 = tlo; t0 < thi; t0 += B8) {
+    float v[B8][kBwdMaxC / kBwdT];
 #pragma unroll
-    for (int u = 0; u < kBwdMaxC / kBwdT; ++u) {
-      const int d = tid + kBwdT * u;
-      if (d < c) acc[u] += src[d];
+    for (int b8 = 0; b8 < B8; ++b8) {
+      const int64_t t = t0 + b8 < thi ? t0 + b8 : t0;
+      const int64_t j = G.ks + (p - G.wlo(t));
+      const float* src = contrib + ((bi * G.n_q + (t - G.t0)) * G.nslot + j) * (int64_t)c;
+#pragma unroll
+      for (int u = 0; u < kBwdMaxC / kBwdT; ++u) {
+        const int d = tid + kBwdT * u;
+        v[b8][u] = d < c ? src[d] : 0.f;
+      }
     }
+#pragma unroll
+    for (int b8 = 0; b8 < B8; ++b8)
+      if (t0 + b8 < thi)
+#pragma unroll
+        for (int u = 0; u < kBwdMaxC / kBwdT; ++u) acc[u] += v[b8][u];
   }
 #pragma unroll
   for (int u = 0; u < kBwdMaxC / kBwdT; ++u) {
@@ -370,9 +439,21 @@ hipError_t launch_attend_backward(int dense, const void* q, const void* Ccomp, i
     hipLaunchKernelGGL(attend_bwd_contrib<float>, cgrid, dim3(kBwdT), csh, st, G, (const float*)q,
                        (const float*)dout, P, DL, 0, contrib);
   }
-  if (n_comp > 0)
+  if (n_comp > 0) {
+    // CSA: the inverse slot table, in the P and DL arrays (read only by the
+    // contribution step, done by now) when it fits there
+    int32_t* inv = nullptr;
+    const size_t inv_n = (size_t)b * n_comp * n_q;
+    if (!dense && inv_n * 4 <= 2 * al(rows * n_h * G.nslot * 4)) {
+      inv = (int32_t*)P;
+      const int64_t blocks = (int64_t)((inv_n + kBwdT - 1) / kBwdT);
+      hipLaunchKernelGGL(bwd_inv_fill, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(kBwdT), 0, st, inv,
+                         (int64_t)inv_n);
+      hipLaunchKernelGGL(bwd_inv_scatter, dim3((unsigned)n_q, (unsigned)b), dim3(kBwdT), 0, st, G, idx, inv);
+    }
     hipLaunchKernelGGL(attend_bwd_reduce_comp, dim3((unsigned)n_comp, (unsigned)b), dim3(kBwdT), 0, st, G, idx,
-                       contrib, accumulate, dC, dcbs);
+                       (const int32_t*)inv, contrib, accumulate, dC, dcbs);
+  }
   hipLaunchKernelGGL(attend_bwd_reduce_raw, dim3((unsigned)n_raw, (unsigned)b), dim3(kBwdT), 0, st, G, raw_pos0,
                      contrib, accumulate, dR, drbs);
   hipLaunchKernelGGL(attend_bwd_reduce_sink, dim3((unsigned)n_h), dim3(kBwdT), 0, st, (int64_t)rows, (int)n_h, dz,
