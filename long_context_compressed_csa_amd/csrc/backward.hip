@@ -550,6 +550,145 @@ __global__ __launch_bounds__(kBwdT) void compress_bwd_rows(
   }
 }
 
+// The same per (sequence, entry, group of Vec16<T>::N dimensions): 16-byte
+// loads and stores (c a multiple of N, rows 16-byte aligned).
+template <typename T>
+__global__ __launch_bounds__(kBwdT) void compress_bwd_rows_v(
+    const T* __restrict__ Ca, const T* __restrict__ Cb, const T* __restrict__ Za, const T* __restrict__ Zb,
+    const T* __restrict__ Ba, const T* __restrict__ Bb, const T* __restrict__ pCb, const T* __restrict__ pZb,
+    const float* __restrict__ dCc, int64_t b, int64_t n, int c, int m, int overlap, float* __restrict__ dCa,
+    float* __restrict__ dCb, float* __restrict__ dZa, float* __restrict__ dZb, float* __restrict__ dpCb,
+    float* __restrict__ dpZb) {
+  constexpr int N = Vec16<T>::N;
+  typedef Vec16<float> F;
+  const int cv = c / N;
+  const int64_t ne = n / m;
+  const int64_t total = b * (ne + 1) * cv;
+  auto st_f = [](float* p, const float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float w[4] = {v[i], v[i + 1], v[i + 2], v[i + 3]};
+      F::st(p + i, w);
+    }
+  };
+  auto st_zero = [](float* p) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) *reinterpret_cast<float4*>(p + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+    const int d = (int)(u % cv) * N;
+    const int64_t rest = u / cv;
+    const int64_t e = rest % (ne + 1);
+    const int64_t s = rest / (ne + 1);
+    const int64_t sq = s * n * (int64_t)c;
+    if (e == ne) {
+      for (int64_t row = ne * m; row < n; ++row) {
+        st_zero(dCa + sq + row * c + d);
+        st_zero(dZa + sq + row * c + d);
+        if (overlap) { st_zero(dCb + sq + row * c + d); st_zero(dZb + sq + row * c + d); }
+      }
+      if (overlap && ne > 0)
+        for (int j = 0; j < m; ++j) {
+          const int64_t row = (ne - 1) * m + j;
+          st_zero(dCb + sq + row * c + d);
+          st_zero(dZb + sq + row * c + d);
+        }
+      if (overlap && ne == 0 && dpCb)
+        for (int j = 0; j < m; ++j) { st_zero(dpCb + (s * m + j) * c + d); st_zero(dpZb + (s * m + j) * c + d); }
+      continue;
+    }
+    const bool hasb = overlap && (e > 0 || pZb != nullptr);
+    auto zb_row = [&](int j) { return e > 0 ? Zb + sq + (m * (e - 1) + j) * c + d : pZb + (s * m + j) * c + d; };
+    auto cb_row = [&](int j) { return e > 0 ? Cb + sq + (m * (e - 1) + j) * c + d : pCb + (s * m + j) * c + d; };
+    float mx[N], den[N], num[N], g[N], cc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) { mx[i] = -INFINITY; den[i] = 0.f; num[i] = 0.f; }
+    for (int j = 0; j < m; ++j) {
+      float z[N], bb[N];
+      Vec16<T>::ld(Za + sq + (m * e + j) * c + d, z);
+      Vec16<T>::ld(Ba + j * c + d, bb);
+#pragma unroll
+      for (int i = 0; i < N; ++i) mx[i] = fmaxf(mx[i], z[i] + bb[i]);
+      if (hasb) {
+        Vec16<T>::ld(zb_row(j), z);
+        Vec16<T>::ld(Bb + j * c + d, bb);
+#pragma unroll
+        for (int i = 0; i < N; ++i) mx[i] = fmaxf(mx[i], z[i] + bb[i]);
+      }
+    }
+    for (int j = 0; j < m; ++j) {
+      float z[N], bb[N], cv8[N];
+      Vec16<T>::ld(Za + sq + (m * e + j) * c + d, z);
+      Vec16<T>::ld(Ba + j * c + d, bb);
+      Vec16<T>::ld(Ca + sq + (m * e + j) * c + d, cv8);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float pa = __expf(z[i] + bb[i] - mx[i]);
+        den[i] += pa;
+        num[i] = fmaf(pa, cv8[i], num[i]);
+      }
+      if (hasb) {
+        Vec16<T>::ld(zb_row(j), z);
+        Vec16<T>::ld(Bb + j * c + d, bb);
+        Vec16<T>::ld(cb_row(j), cv8);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float pb = __expf(z[i] + bb[i] - mx[i]);
+          den[i] += pb;
+          num[i] = fmaf(pb, cv8[i], num[i]);
+        }
+      }
+    }
+    {
+      float gg[4];
+#pragma unroll
+      for (int i = 0; i < N; i += 4) {
+        F::ld(dCc + (s * ne + e) * c + d + i, gg);
+        g[i] = gg[0]; g[i + 1] = gg[1]; g[i + 2] = gg[2]; g[i + 3] = gg[3];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) cc[i] = num[i] / den[i];
+    for (int j = 0; j < m; ++j) {
+      const int64_t ra = m * e + j;
+      float z[N], bb[N], cv8[N], o1[N], o2[N];
+      Vec16<T>::ld(Za + sq + ra * c + d, z);
+      Vec16<T>::ld(Ba + j * c + d, bb);
+      Vec16<T>::ld(Ca + sq + ra * c + d, cv8);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float sa = __expf(z[i] + bb[i] - mx[i]) / den[i];
+        o1[i] = sa * g[i];
+        o2[i] = sa * (cv8[i] - cc[i]) * g[i];
+      }
+      st_f(dCa + sq + ra * c + d, o1);
+      st_f(dZa + sq + ra * c + d, o2);
+      if (hasb) {
+        Vec16<T>::ld(zb_row(j), z);
+        Vec16<T>::ld(Bb + j * c + d, bb);
+        Vec16<T>::ld(cb_row(j), cv8);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float sb = __expf(z[i] + bb[i] - mx[i]) / den[i];
+          o1[i] = sb * g[i];
+          o2[i] = sb * (cv8[i] - cc[i]) * g[i];
+        }
+        if (e > 0) {
+          const int64_t rb = m * (e - 1) + j;
+          st_f(dCb + sq + rb * c + d, o1);
+          st_f(dZb + sq + rb * c + d, o2);
+        } else if (dpCb) {
+          st_f(dpCb + (s * m + j) * c + d, o1);
+          st_f(dpZb + (s * m + j) * c + d, o2);
+        }
+      } else if (overlap && e == 0 && dpCb) {
+        st_zero(dpCb + (s * m + j) * c + d);
+        st_zero(dpZb + (s * m + j) * c + d);
+      }
+    }
+  }
+}
+
 // Bias gradient, stage 1: per (chunk of 64 entries, in-block row j,
 // dimension d) the sum of dZ over the chunk's entries in order (over every
 // sequence); stage 2 adds the chunks in order.  stream b: entry e's rows
@@ -577,13 +716,31 @@ __global__ __launch_bounds__(kBwdT) void compress_bwd_bias_partial(const float* 
     }
   part[u] = a;
 }
+// One workgroup per 64 (row, dimension) outputs: wave w sums the chunks
+// w * q .. (w + 1) * q - 1 (q = nch / 4 rounded up) in order, eight loads in
+// flight, then the four wave sums are added in wave order.
 __global__ __launch_bounds__(kBwdT) void compress_bwd_bias_final(const float* __restrict__ part, int64_t nch, int c,
                                                                  int m, float* __restrict__ dB) {
-  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= (int64_t)m * c) return;
+  __shared__ float ws4[4][64];
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t mc = (int64_t)m * c;
+  const int64_t u = (int64_t)blockIdx.x * 64 + l;
+  const int64_t qn = (nch + 3) / 4;
+  const int64_t c0 = wave * qn, c1 = c0 + qn < nch ? c0 + qn : nch;
   float a = 0.f;
-  for (int64_t ch = 0; ch < nch; ++ch) a += part[ch * m * (int64_t)c + u];
-  dB[u] = a;
+  if (u < mc) {
+    for (int64_t ch = c0; ch < c1; ch += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ch + i < c1 ? part[(ch + i) * mc + u] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (ch + i < c1) a += v[i];
+    }
+  }
+  ws4[wave][l] = a;
+  __syncthreads();
+  if (wave == 0 && u < mc) dB[u] = ((ws4[0][l] + ws4[1][l]) + ws4[2][l]) + ws4[3][l];
 }
 
 size_t compress_backward_workspace_bytes(int64_t n, int64_t c, int64_t m) {
@@ -600,7 +757,18 @@ hipError_t launch_compress_backward(const void* Ca, const void* Cb, const void* 
   const int64_t ne = n / m;
   const int64_t total = b * (ne + 1) * c;
   const unsigned grid = (unsigned)std::min<int64_t>((total + kBwdT - 1) / kBwdT, 65535 * 4);
-  if (dtype == 1)
+  // bf16 with 16-byte rows and aligned arrays: 8 dimensions per thread
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const bool vec_ok = dtype == 1 && c % 8 == 0 && a16(Ca) && a16(Za) && a16(Ba) && a16(dCc) && a16(dCa) && a16(dZa) &&
+                      (!overlap || (a16(Cb) && a16(Zb) && a16(Bb) && a16(dCb) && a16(dZb))) && a16(pCb) && a16(pZb) &&
+                      a16(dpCb) && a16(dpZb);
+  const unsigned grid_v = (unsigned)std::min<int64_t>((b * (ne + 1) * (c / 8) + kBwdT - 1) / kBwdT, 65535 * 4);
+  if (vec_ok)
+    hipLaunchKernelGGL(compress_bwd_rows_v<bf16_t>, dim3(grid_v), dim3(kBwdT), 0, st, (const bf16_t*)Ca,
+                       (const bf16_t*)Cb, (const bf16_t*)Za, (const bf16_t*)Zb, (const bf16_t*)Ba, (const bf16_t*)Bb,
+                       (const bf16_t*)pCb, (const bf16_t*)pZb, dCc, b, n, (int)c, (int)m, overlap, dCa, dCb, dZa, dZb,
+                       dpCb, dpZb);
+  else if (dtype == 1)
     hipLaunchKernelGGL(compress_bwd_rows<bf16_t>, dim3(grid), dim3(kBwdT), 0, st, (const bf16_t*)Ca,
                        (const bf16_t*)Cb, (const bf16_t*)Za, (const bf16_t*)Zb, (const bf16_t*)Ba, (const bf16_t*)Bb,
                        (const bf16_t*)pCb, (const bf16_t*)pZb, dCc, b, n, (int)c, (int)m, overlap, dCa, dCb, dZa, dZb,
@@ -618,8 +786,8 @@ hipError_t launch_compress_backward(const void* Ca, const void* Cb, const void* 
       hipLaunchKernelGGL(compress_bwd_bias_partial, dim3((unsigned)((pu + kBwdT - 1) / kBwdT)), dim3(kBwdT), 0, st,
                          stream == 0 ? dZa : dZb, stream == 0 ? (const float*)nullptr : (const float*)dpZb, b, n,
                          (int)c, (int)m, stream, part);
-    hipLaunchKernelGGL(compress_bwd_bias_final, dim3((unsigned)((m * c + kBwdT - 1) / kBwdT)), dim3(kBwdT), 0, st,
-                       part, nch, (int)c, (int)m, dB);
+    hipLaunchKernelGGL(compress_bwd_bias_final, dim3((unsigned)((m * c + 63) / 64)), dim3(kBwdT), 0, st, part, nch,
+                       (int)c, (int)m, dB);
   }
   return hipGetLastError();
 }
