@@ -681,9 +681,15 @@ def run_backward(args, torch, L, synth):
     us = _event_us(torch, call, 3, warm=1)
     sel, win = prefill_pairs(n, m, k, nw)
     flop = (sel + win) * nh * 10 * c      # q.e, g.e, dq, and both roles of de: 10 c flops per (pair, head)
-    res = {"csa_attend_backward": {"us": us, "n": n, "k": k, "flop": flop, "tflops": flop / (us * 1e-6) / 1e12,
-                                   "valu_fp32_frac": flop / (us * 1e-6) / 1e12 / PEAK_FP32_TFLOPS,
-                                   "bound": "alu (float32 vector arithmetic)"}}
+    # every slot's entry contribution is written and read back once (float32)
+    contrib_bytes = n * (k + nw) * c * 4 * 2
+    tf = flop / (us * 1e-6) / 1e12
+    res = {"csa_attend_backward": {"us": us, "n": n, "k": k, "flop": flop, "tflops": tf,
+                                   "mfma_bf16_frac": tf / PEAK_BF16_TFLOPS,
+                                   "contrib_bytes": contrib_bytes,
+                                   "bound": "mfma (bf16 products of exact bf16 inputs, float32 accumulation; "
+                                            "p and dl as bf16 high part + remainder) and the float32 contribution "
+                                            "traffic"}}
     del d, dout, ws, grads
     cd = synth.compress_inputs(True, device="cuda")
     nc, cc, mc = synth.COMPRESS["n"], synth.COMPRESS["c"], cd["m"]
@@ -845,7 +851,7 @@ def calibrate_copy(torch):
 
 # ------------------------------------------------------- HBM traffic ----
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_mfma_c512_csa_prefill_n8192_hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_ds_csa_prefill_n8192_hbm_traffic.json")
 ATTEND_SOURCES = [os.path.join(ROOT, "long_context_compressed_csa_amd", "csrc", f)
                   for f in ("attend.hip", "common.hpp")]
 
@@ -883,8 +889,8 @@ def traffic_summary(pmc_dir, commands):
     WRITE_SIZE, each in KiB per dispatch, in PMC_DIR/prefill-fetch,
     prefill-write, copy-FETCH_SIZE, copy-WRITE_SIZE), every counter scaled by
     what it reads for the 1 GiB copy."""
-    att = r"attend_mfma_c512<0, 1>"
-    grid = 8192 * 128   # the n = 8192 prefill launch: one 128-thread workgroup per query
+    att = r"attend_ds<0, 0, 0>"
+    grid = 8192 * 256   # the n = 8192 prefill launch: one 256-thread workgroup per query
     cp = "vectorized_elementwise_kernel<4, at::native::AUnary"
     f_att, nf = _pmc_mean(os.path.join(pmc_dir, "prefill-fetch"), "FETCH_SIZE", att, grid)
     w_att, nw = _pmc_mean(os.path.join(pmc_dir, "prefill-write"), "WRITE_SIZE", att, grid)
@@ -896,7 +902,7 @@ def traffic_summary(pmc_dir, commands):
     read_b = f_att * 1024.0 * f_scale
     write_b = w_att * 1024.0 * w_scale
     rec = {
-        "kernel": "attend_mfma_c512<0,1> (csa_attend), CSA prefill n=8192, n_h=64, c=512, k=512, n_win=128",
+        "kernel": "attend_ds<0,0,0> (csa_attend), CSA prefill n=8192, n_h=64, c=512, k=512, n_win=128",
         "attend_sources_sha256": _sources_sha256(ATTEND_SOURCES),
         "fetch_kib_per_dispatch": f_att, "write_kib_per_dispatch": w_att,
         "dispatches": {"fetch": nf, "write": nw},
@@ -1018,7 +1024,7 @@ def main(argv=None):
         "config": {"workload": "CSA prefill layer, n=8192, n_h=64, c=512, m=4, k=512, n_win=128, "
                                "indexer 64x128, bf16, causal",
                    "global_batch": 1, "seq_len": 8192},
-        "roofline": {"bound": "mfma", "kernel": "attend_mfma_c512 (csa_attend)",
+        "roofline": {"bound": "mfma", "kernel": "attend_ds (csa_attend)",
                      "achieved": pre["attend_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": pre["attend_tflops"] / PEAK_BF16_TFLOPS, "traffic": recorded_traffic(),
                      "flop_per_launch": pre["flop_attend"], "avg_launch_us": att_us},
