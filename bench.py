@@ -260,6 +260,35 @@ def run_prefill(args, torch, L, synth):
     for _ in range(args.steps):
         stepR(timerR)
     timerR.collect()
+
+    # The same step with the query norm and rotation done in the attention's
+    # Q load and the output's -t rotation in its epilogue (csa_attend_norm_rope):
+    # the separate query and output passes are gone.
+    def attend_fused():
+        return lib.csa_attend_norm_rope(P(d["q"]), P(gq), eps, rd, base, P(Cn), 0, P(idx), P(Rn), 0, 0,
+                                        P(d["sink"]), 1, n, 0, ne, n, nh, c, k, m, nw, d["scale"], 1, None, 0,
+                                        P(out), st)
+
+    stagesF = [("compress_main", comp_main), ("compress_index_keys", comp_index),
+               ("norm_rope_entries", norm_entries), ("norm_rope_window_rows", norm_window_rows),
+               ("index_topk", index_topk), ("attend_norm_rope", attend_fused)]
+
+    def stepF(timer=None):
+        for name, fn in stagesF:
+            rc = timer.run(name, fn) if timer else fn()
+            if rc != 0:
+                raise RuntimeError(f"{name} failed: {L.strerror(rc)}")
+
+    for _ in range(args.warmup):
+        stepF()
+    msF, _ = timed_steps(torch, stepF, args.steps)
+    timerF = KernelTimer(torch)
+    for _ in range(args.steps):
+        stepF(timerF)
+    timerF.collect()
+    fused_step = {"ms_per_step": msF, "tokens_per_s": n / (msF / 1000.0),
+                  "stages": [name for name, _ in stagesF],
+                  "stage_us": {name: timerF.avg_us(name) for name, _ in stagesF}}
     nq_bytes = 2 * n * nh * c * 2            # query heads read and written once
     rot_bytes = 2 * n * nh * rd * 2          # rotated output dims read and written
     nr_us = {name: timerR.avg_us(name) for name, _ in stagesR if name.startswith(("norm", "rotate"))}
@@ -270,6 +299,7 @@ def run_prefill(args, torch, L, synth):
         "queries_hbm_frac": nq_bytes / (nr_us["norm_rope_queries"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
         "rotate_output_gbs": rot_bytes / (nr_us["rotate_output"] * 1e-6) / 1e9,
         "gains": "seeded synthetic (1 + N(0, 0.1^2) per dim); eps 1e-6, RoPE base 10000 on the last 64 dims",
+        "fused_queries": fused_step,
     }
     del qn, Cn, Rn
 
@@ -889,7 +919,7 @@ def traffic_summary(pmc_dir, commands):
     WRITE_SIZE, each in KiB per dispatch, in PMC_DIR/prefill-fetch,
     prefill-write, copy-FETCH_SIZE, copy-WRITE_SIZE), every counter scaled by
     what it reads for the 1 GiB copy."""
-    att = r"attend_ds<0, 0, 0>"
+    att = r"attend_ds<0, 0, 0, 0>"
     grid = 8192 * 256   # the n = 8192 prefill launch: one 256-thread workgroup per query
     cp = "vectorized_elementwise_kernel<4, at::native::AUnary"
     f_att, nf = _pmc_mean(os.path.join(pmc_dir, "prefill-fetch"), "FETCH_SIZE", att, grid)
@@ -902,7 +932,7 @@ def traffic_summary(pmc_dir, commands):
     read_b = f_att * 1024.0 * f_scale
     write_b = w_att * 1024.0 * w_scale
     rec = {
-        "kernel": "attend_ds<0,0,0> (csa_attend), CSA prefill n=8192, n_h=64, c=512, k=512, n_win=128",
+        "kernel": "attend_ds<0,0,0,0> (csa_attend), CSA prefill n=8192, n_h=64, c=512, k=512, n_win=128",
         "attend_sources_sha256": _sources_sha256(ATTEND_SOURCES),
         "fetch_kib_per_dispatch": f_att, "write_kib_per_dispatch": w_att,
         "dispatches": {"fetch": nf, "write": nw},

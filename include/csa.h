@@ -342,6 +342,36 @@ int csa_attend(const void* q, const void* Ccomp, int64_t comp_bstride, const int
                int64_t n_h, int64_t c, int64_t k, int64_t m, int64_t n_win, float scale,
                int dtype, void* workspace, size_t ws_bytes, void* out, void* stream);
 
+/*
+ * csa_attend_norm_rope -- csa_attend with the query side of the norm and
+ * partial RoPE folded in (songhuiming "DeepSeek-V4 百万 token 上下文"
+ * section 4.5; AirCoding "deepseek-paper-analysis" section 7.1): q holds the
+ * raw query heads; each head vector is RMS-normalised and its last rope_dims
+ * dimensions rotated at the query's position t, as csa_norm_rope does
+ * (y = x / sqrt(mean(x^2) + eps) * gamma_q, then the pair (y[c-rope_dims+2i],
+ * y[c-rope_dims+2i+1]) turned by t * base^(-2i/rope_dims), angles in
+ * float64), and rounded to bf16 before the products; the output's last
+ * rope_dims dimensions are turned back by -t in float32 and stored once in
+ * bf16.  The compressed entries and raw rows are read as given (normalise
+ * and rotate them with csa_norm_rope when they are stored).
+ *
+ *  gamma_q  [c] float32 per-dimension gain, 16-byte aligned
+ *  eps      >= 0;  rope_dims  even, 0 .. c;  base > 0 when rope_dims > 0
+ *  every other argument and the workspace as for csa_attend (the workspace
+ *  size is csa_attend_workspace_size()).
+ *
+ * Errors: as csa_attend, plus CSA_EINVAL for a NULL or misaligned gamma_q, a
+ * negative or non-finite eps, an odd or negative rope_dims or one above c, a
+ * bad base, or a position beyond 2^40; CSA_ENOTSUP outside bf16, c = 512,
+ * n_h a multiple of 64 and k <= 2048.
+ */
+int csa_attend_norm_rope(const void* q, const float* gamma_q, float eps, int64_t rope_dims, double base,
+                         const void* Ccomp, int64_t comp_bstride, const int32_t* idx, const void* kv_raw,
+                         int64_t raw_bstride, int64_t raw_pos0, const float* sink, int64_t b, int64_t n_q,
+                         int64_t t0, int64_t n_comp, int64_t n_raw, int64_t n_h, int64_t c, int64_t k, int64_t m,
+                         int64_t n_win, float scale, int dtype, void* workspace, size_t ws_bytes, void* out,
+                         void* stream);
+
 /* Device scratch csa_attend needs for these shapes (0 = none; then workspace
  * may be NULL).  Few queries (decode) split each query's entries over
  * several workgroups and merge the partial softmax states in a fixed order;

@@ -47,6 +47,8 @@ SIGNATURES = {
                              _i64, _i64, _int, _vp]),
     "csa_attend": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp] + [_i64] * 10
                    + [_f32, _int, _vp, _sz, _vp, _vp]),
+    "csa_attend_norm_rope": (_int, [_vp, _vp, _f32, _i64, ctypes.c_double, _vp, _i64, _vp, _vp, _i64, _i64, _vp]
+                             + [_i64] * 10 + [_f32, _int, _vp, _sz, _vp, _vp]),
     "csa_attend_workspace_size": (_sz, [_i64] * 9 + [_int]),
     "hca_attend": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp] + [_i64] * 9
                    + [_f32, _int, _vp, _sz, _vp, _vp]),
@@ -365,6 +367,37 @@ def csa_attend(q, Ccomp, idx, kv_raw, sink, t0, m, n_win, scale=None, raw_pos0=0
                         n_h, c, k, m, n_win, scale, dt, _ptr(workspace),
                         0 if workspace is None else workspace.numel(), _ptr(out), _stream(stream))
     _check(rc, "csa_attend")
+    return out
+
+
+def csa_attend_norm_rope(q, gamma_q, eps, rope_dims, base, Ccomp, idx, kv_raw, sink, t0, m, n_win,
+                         scale=None, raw_pos0=0, n_comp=None, n_raw=None, out=None, workspace=None,
+                         stream=None):
+    """csa_attend on raw query heads: each head is RMS-normalised with gain
+    gamma_q [c] f32 and its last rope_dims dimensions rotated at its position
+    inside the kernel; the output's last rope_dims dimensions are turned back
+    by -t before they are stored.  Other arguments as csa_attend."""
+    q, Ccomp, idx, kv_raw = _batched(q, 4), _batched(Ccomp, 3), _batched(idx, 3), _batched(kv_raw, 3)
+    b, n_q, n_h, c = q.shape
+    k = idx.shape[2]
+    n_comp = Ccomp.shape[1] if n_comp is None else n_comp
+    n_raw = kv_raw.shape[1] if n_raw is None else n_raw
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(q, Ccomp, kv_raw)
+    if idx.dtype != torch.int32:
+        raise ValueError("idx must be int32")
+    lib = load_library()
+    need = lib.csa_attend_workspace_size(b, n_q, t0, n_comp, n_h, c, k, m, n_win, dt)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.csa_attend_norm_rope(_ptr(q), _f32c(gamma_q, "gamma_q"), eps, rope_dims, base, _ptr(Ccomp),
+                                  Ccomp.stride(0), _ptr(idx), _ptr(kv_raw), kv_raw.stride(0), raw_pos0,
+                                  _f32c(sink, "sink"), b, n_q, t0, n_comp, n_raw, n_h, c, k, m, n_win, scale,
+                                  dt, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                  _ptr(out), _stream(stream))
+    _check(rc, "csa_attend_norm_rope")
     return out
 
 

@@ -227,18 +227,30 @@ constexpr int kXB = 64 * 8 * 4;   // one wave's partial S^T: 64 lanes x 8 floats
 // `ring` slots per request.  DENSE = 1 (HCA): the entry list is every
 // completed entry, s < (t+1)/m, with no index list (paged: a split's entries
 // are translated to pool rows in LDS before its tiles, so a split holds at
-// most kMaxSel of them).
-template <int SPLIT, int PG, int DENSE>
+// most kMaxSel of them).  NRQ = 1: q holds the raw query heads; each is
+// RMS-normalised (gain gq, eps), its last rope_dims dimensions turned by
+// t * base^(-2i / rope_dims), and rounded to bf16 as it becomes the MFMA
+// operand; the output's last rope_dims dimensions are turned back by -t in
+// float32 before the bf16 store (split partial states are turned before
+// they are written: the merge is linear).
+template <int SPLIT, int PG, int DENSE, int NRQ>
 __global__ __launch_bounds__(256, 2) void attend_ds(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Ccomp, int64_t cbs,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ kv_raw, int64_t rbs,
     int64_t raw_pos0, const float* __restrict__ sink, int64_t n_q, int64_t t0, int64_t n_comp,
     int n_h, int64_t k, int64_t m, int64_t n_win, float scale, int nsplit, float* __restrict__ part_o,
     float* __restrict__ part_ml, bf16_t* __restrict__ out, Rows er, int64_t ring,
-    const int64_t* __restrict__ pos) {
+    const int64_t* __restrict__ pos, const float* __restrict__ gq, float eps, int rope_dims, double base) {
   constexpr int NW = 4;
   constexpr int R = kT / NW;   // gather loads per wave and tile
   __shared__ DsSmem sm;
+  // NRQ: per-dimension coefficients (A, B) of the normalised, rotated
+  // query, q'[d] = inv (q[d] A_d + q[d ^ 1] B_d) with inv the head's
+  // 1 / rms (gains and rotation folded in); per pair of dimensions the
+  // rotation (cos, sin) for the output; the waves' partial sums of squares
+  __shared__ __attribute__((aligned(16))) float2 nr_ab[NRQ ? kC : 2];
+  __shared__ __attribute__((aligned(16))) float2 nr_pr[NRQ ? kC / 2 : 1];
+  __shared__ float nr_ss[NRQ ? NW : 1][NRQ ? kHW : 1];
   __shared__ __attribute__((aligned(16))) unsigned char T0[kTileB];
   __shared__ __attribute__((aligned(16))) unsigned char T1[kTileB];
   __shared__ __attribute__((aligned(16))) unsigned char T2[kTileB];
@@ -307,10 +319,34 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   }
   {
     const bf16_t* qp = q + ((bi * n_q + rq) * n_h + head0 + s16) * (int64_t)kC + 256 * dh + 8 * g4;
+    // NRQ: this thread's pair of gains, loaded ahead of Q so that waiting
+    // for it does not wait for Q
+    float2 gv = make_float2(0.f, 0.f);
+    if (NRQ) {
+      static_assert(2 * 64 * NW == kC, "one pair of dimensions per thread");
+      gv = reinterpret_cast<const float2*>(gq)[tid];
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) qB[ks][hb] = *reinterpret_cast<const bf16x8*>(qp + hb * 16 * kC + ks * 32);
+    if (NRQ) {
+      // the tables while Q is in flight, angles in float64 (positions reach
+      // 2^20 and beyond).  Thread tid: the pair of dimensions (2 tid,
+      // 2 tid + 1), rotated pair tid - lo/2 when 2 tid >= lo = c - rope_dims;
+      // the normalised pair (a, b) turns into (a cos - b sin, a sin + b cos)
+      const int lo2 = (kC - rope_dims) >> 1;
+      float c1 = 1.f, s1 = 0.f;
+      if (tid >= lo2) {
+        const double theta = pow(base, -2.0 * (double)(tid - lo2) / (double)rope_dims);
+        double sn, cs;
+        sincos((double)t * theta, &sn, &cs);
+        c1 = (float)cs;
+        s1 = (float)sn;
+      }
+      reinterpret_cast<float4*>(nr_ab)[tid] = make_float4(c1 * gv.x, -s1 * gv.y, c1 * gv.y, s1 * gv.x);
+      nr_pr[tid] = make_float2(c1, s1);
+    }
     // Q must have arrived before the first gather is issued: the compiler
     // does not count the gathers (inline asm), so a wait it placed for Q
     // later on would also drain every gather in flight
@@ -319,6 +355,20 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) asm volatile("" ::"v"(qB[ks][hb]));
   }
+  // NRQ: the back-rotation by -t of this lane's output column in block nb
+  // (dimension d = 256 dh + 32 nb + l % 32, the accumulator's column) as
+  // x' = x c + x_partner s', the pair partner held by lane l ^ 1: (c, s') =
+  // (cos, +sin) on the pair's first dimension, (cos, -sin) on its second,
+  // (1, 0) outside the rotated dimensions
+  auto rot_coef = [&](int nb) -> float2 {
+    const float2 r = nr_pr[128 * dh + 16 * nb + ((l & 31) >> 1)];
+    return make_float2(r.x, (l & 1) ? -r.y : r.y);
+  };
+  auto unrotate = [](float x, float2 cs) -> float {
+    // quad permutation (1, 0, 3, 2): the value of lane l ^ 1
+    const float y = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+    return fmaf(y, cs.y, x * cs.x);
+  };
   int64_t nsel = 0;
   if (DENSE) {
     nsel = vis;
@@ -533,10 +583,78 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
 
   __syncthreads();
   int gen = 0;
+  issue_tile(0, T0);
+  issue_tile(1, T1);
+  if (NRQ) {
+    // the query's norm and rotation while the first two tiles are gathered:
+    // this wave's sum of squares of each of its heads over its 256 dimensions
+    float ss[2] = {0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float v = (float)qB[ks][hb][i];
+          ss[hb] = fmaf(v, v, ss[hb]);
+        }
+    // the products below convert Q again: keeping the 128 converted values
+    // of this loop alive instead would not fit the registers
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) asm volatile("" : "+v"(qB[ks][hb]));
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      ss[hb] += __uint_as_float(from_lane_xor16(__float_as_uint(ss[hb]), up16));
+      ss[hb] = half_sum(ss[hb]);
+      if (g4 == 0) nr_ss[wave][16 * hb + s16] = ss[hb];
+    }
+    tile_barrier();   // not a fence: the first gathers stay in flight
+    float inv[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      // both dimension halves' sums, in a fixed order
+      const float tot = nr_ss[hw][16 * hb + s16] + nr_ss[hw + 2][16 * hb + s16];
+      inv[hb] = 1.f / sqrtf(tot / (float)kC + eps);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int d0 = 256 * dh + 32 * ks + 8 * g4;
+      // this lane's eight dimensions' coefficients, read in one batch
+      // (issued in order: the compiler would hoist every group's reads ahead
+      // of the products and run out of registers)
+      f32x4 ab[4];
+      const uint32_t ta = (uint32_t)(uintptr_t)&nr_ab[d0];
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:16\n\t"
+          "ds_read_b128 %2, %4 offset:32\n\t"
+          "ds_read_b128 %3, %4 offset:48\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(ab[0]), "=&v"(ab[1]), "=&v"(ab[2]), "=&v"(ab[3])
+          : "v"(ta)
+          : "memory");
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        float u[8], v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = (float)qB[ks][hb][i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = inv[hb] * fmaf(u[2 * j + 1], ab[j][1], u[2 * j] * ab[j][0]);
+          v[2 * j + 1] = inv[hb] * fmaf(u[2 * j], ab[j][3], u[2 * j + 1] * ab[j][2]);
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v[2 * i], v[2 * i + 1]}, bf16x2_t));
+        qB[ks][hb] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+    }
+  }
   for (;;) {
     l_part = 0.f;
-    issue_tile(0, T0);
-    issue_tile(1, T1);
     if (ntiles > 0) step(0, T0, T2, true);
     for (int it = 1; it < ntiles; it += 3) {
       step(it, T1, T0, false);
@@ -561,6 +679,9 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
     ++gen;
     m_ref[0] = m_seen[0];
     m_ref[1] = m_seen[1];
+    // again from the first tile
+    issue_tile(0, T0);
+    issue_tile(1, T1);
   }
   const float m_run = up16 ? m_ref[1] : m_ref[0];
   const float l_run = half_sum(l_part);
@@ -572,12 +693,15 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
     // an empty split (no tiles: O was never written) leaves O = 0 and a
     // maximum of -inf, which the combine weighs with 0
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
+    for (int nb = 0; nb < 8; ++nb) {
+      const float2 cs = NRQ ? rot_coef(nb) : make_float2(1.f, 0.f);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int hr = 8 * (r >> 2) + 4 * half + (r & 3);
-        po[hr * (int64_t)kC + nb * 32] = ntiles > 0 ? o[nb][r] : 0.f;
+        const float x = NRQ ? unrotate(o[nb][r], cs) : o[nb][r];
+        po[hr * (int64_t)kC + nb * 32] = ntiles > 0 ? x : 0.f;
       }
+    }
     if (dh == 0 && l < 32) {
       part_ml[(slot * kHG + kHW * hw + l) * 2 + 0] = m_run;
       part_ml[(slot * kHG + kHW * hw + l) * 2 + 1] = l_run;
@@ -594,6 +718,11 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   float4 g4v[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) g4v[g] = *reinterpret_cast<const float4*>(&sm.bc[wave][8 * g + 4 * half]);
+  float2 rcs[NRQ ? 8 : 1];
+  if (NRQ) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) rcs[nb] = rot_coef(nb);
+  }
   unsigned char* stg = wave == 0 ? T0 : wave == 1 ? T1 : wave == 2 ? T2 : XB;
   bf16_t* ob = out + ((bi * n_q + rq) * n_h + head0) * (int64_t)kC + 256 * dh;
   // two passes of 16 head rows (8 KiB of staging each)
@@ -608,9 +737,12 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
           const int hr = 8 * g + 4 * half + i;   // head row; staged at hr - 16 pass
-          const uint32_t pk = __builtin_bit_cast(
-              uint32_t, __builtin_convertvector((f32x2_t){o[nb8][4 * g + i] * gv[i], o[nb8][4 * g + i + 1] * gv[i + 1]},
-                                                bf16x2_t));
+          float x0 = o[nb8][4 * g + i] * gv[i], x1 = o[nb8][4 * g + i + 1] * gv[i + 1];
+          if (NRQ) {
+            x0 = unrotate(x0, rcs[nb8]);
+            x1 = unrotate(x1, rcs[nb8]);
+          }
+          const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));
           const int byte = ((nb8 * 32 + (l & 31)) * 2) ^ (((hr >> 2) & 1) << 6);
           *reinterpret_cast<uint16_t*>(stg + (hr - 16 * pass) * kStageRowB + byte) = (uint16_t)pk;
           *reinterpret_cast<uint16_t*>(stg + (hr + 1 - 16 * pass) * kStageRowB + byte) = (uint16_t)(pk >> 16);
@@ -1206,9 +1338,10 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
     const Rows none = dense_rows(cbs);
     const dim3 grid((unsigned)n_q, (unsigned)((n_h / kHG) * ns), (unsigned)b);
 #define CSA_ATTEND_DS(S, D)                                                                                          \
-  hipLaunchKernelGGL((attend_ds<S, 0, D>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx, \
-                     (const bf16_t*)kv_raw, rbs, raw_pos0, sink, n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns,  \
-                     part_o, part_ml, (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr)
+  hipLaunchKernelGGL((attend_ds<S, 0, D, 0>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs,    \
+                     idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink, n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, \
+                     ns, part_o, part_ml, (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr,                   \
+                     (const float*)nullptr, 0.f, 0, 0.0)
     if (ns == 1) {
       if (dense) CSA_ATTEND_DS(0, 1); else CSA_ATTEND_DS(0, 0);
     } else {
@@ -1229,6 +1362,42 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
     hipLaunchKernelGGL((attend_generic<float>), grid, dim3(256), 0, st, (const float*)q,
                        (const float*)Ccomp, cbs, idx, (const float*)kv_raw, rbs, raw_pos0, sink, n_q,
                        t0, n_comp, (int)n_h, (int)c, k, m, n_win, scale, dense, (float*)out);
+  return hipGetLastError();
+}
+
+// CSA attention with the query heads' RMSNorm and partial RoPE applied as
+// Q is loaded and the output turned back by -t before it is stored (bf16,
+// c = 512, 64-head groups, rope_dims even and <= 512; the caller checked).
+hipError_t launch_attend_norm_rope(const void* q, const float* gq, float eps, int64_t rope_dims, double base,
+                                   const void* Ccomp, int64_t cbs, const int32_t* idx, const void* kv_raw,
+                                   int64_t rbs, int64_t raw_pos0, const float* sink, int64_t b, int64_t n_q,
+                                   int64_t t0, int64_t n_comp, int64_t n_h, int64_t k, int64_t m, int64_t n_win,
+                                   float scale, void* ws, void* out, hipStream_t st) {
+  if (b == 0 || n_q == 0) return hipSuccess;
+  const int ns = attend_nsplit(b, n_q, n_h, k + n_win);   // as launch_attend for a selected list
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (ns > 1) {
+    const int64_t slots = b * n_q * (n_h / kHG) * ns;
+    const size_t osz = ((size_t)slots * kHG * kC * 4 + 255) & ~(size_t)255;
+    part_o = (float*)ws;
+    part_ml = (float*)((unsigned char*)ws + osz);
+  }
+  const Rows none = dense_rows(cbs);
+  const dim3 grid((unsigned)n_q, (unsigned)((n_h / kHG) * ns), (unsigned)b);
+  if (ns == 1)
+    hipLaunchKernelGGL((attend_ds<0, 0, 0, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx,
+                       (const bf16_t*)kv_raw, rbs, raw_pos0, sink, n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, 1,
+                       part_o, part_ml, (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr, gq, eps,
+                       (int)rope_dims, base);
+  else
+    hipLaunchKernelGGL((attend_ds<1, 0, 0, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx,
+                       (const bf16_t*)kv_raw, rbs, raw_pos0, sink, n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns,
+                       part_o, part_ml, (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr, gq, eps,
+                       (int)rope_dims, base);
+  if (ns > 1)
+    hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q), (unsigned)n_h), dim3(128), 0, st, part_o, part_ml,
+                       sink, (int)n_h, ns, (bf16_t*)out);
   return hipGetLastError();
 }
 
@@ -1267,9 +1436,10 @@ hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const
   }
   const dim3 grid(1u, (unsigned)((n_h / kHG) * ns), (unsigned)b);
 #define CSA_ATTEND_DS_PG(S, D)                                                                                        \
-  hipLaunchKernelGGL((attend_ds<S, 1, D>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)pool, (int64_t)0, \
-                     idx, (const bf16_t*)state, state_elems, (int64_t)0, sink, (int64_t)1, (int64_t)0, n_comp_max,   \
-                     (int)n_h, k, m, n_win, scale, ns, part_o, part_ml, (bf16_t*)out, er, ring, pos)
+  hipLaunchKernelGGL((attend_ds<S, 1, D, 0>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)pool,          \
+                     (int64_t)0, idx, (const bf16_t*)state, state_elems, (int64_t)0, sink, (int64_t)1, (int64_t)0,    \
+                     n_comp_max, (int)n_h, k, m, n_win, scale, ns, part_o, part_ml, (bf16_t*)out, er, ring, pos,      \
+                     (const float*)nullptr, 0.f, 0, 0.0)
   if (ns == 1) {
     if (dense) CSA_ATTEND_DS_PG(0, 1); else CSA_ATTEND_DS_PG(0, 0);
   } else {

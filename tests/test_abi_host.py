@@ -234,6 +234,41 @@ def test_attend_rejects_bad_arguments(lib, fn):
     assert _attend(lib, fn, rbs=3) == EINVAL
 
 
+def test_attend_norm_rope_rejects_bad_arguments(lib):
+    def call(ws_bytes=0, **kw):
+        a = dict(q=FAKE, gq=FAKE, eps=1e-6, rd=64, base=10000.0, Cc=FAKE, cbs=0, idx=FAKE, raw=FAKE, rbs=0,
+                 pos0=0, sink=FAKE, b=1, n_q=4, t0=0, n_comp=1, n_raw=4, n_h=64, c=512, k=2, m=4, n_win=4,
+                 scale=0.05, dtype=1, ws=None, out=FAKE)
+        a.update(kw)
+        return lib.csa_attend_norm_rope(a["q"], a["gq"], a["eps"], a["rd"], a["base"], a["Cc"], a["cbs"],
+                                        a["idx"], a["raw"], a["rbs"], a["pos0"], a["sink"], a["b"], a["n_q"],
+                                        a["t0"], a["n_comp"], a["n_raw"], a["n_h"], a["c"], a["k"], a["m"],
+                                        a["n_win"], a["scale"], a["dtype"], a["ws"], ws_bytes, a["out"], None)
+    assert call(q=None) == EINVAL
+    assert call(gq=None) == EINVAL
+    assert call(gq=FAKE + 4) == EINVAL          # gain not 16-byte aligned
+    assert call(eps=-1.0) == EINVAL
+    assert call(eps=float("inf")) == EINVAL
+    assert call(rd=63) == EINVAL
+    assert call(rd=-2) == EINVAL
+    assert call(rd=514) == EINVAL             # more rotated dimensions than a head has
+    assert call(base=0.0) == EINVAL
+    assert call(base=float("nan")) == EINVAL
+    assert call(n_q=1, t0=1 << 41, n_raw=4, pos0=(1 << 41) - 3) == EINVAL
+    assert call(n_raw=3) == EINVAL
+    assert call(k=3, idx=None) == EINVAL
+    # the fused form runs on the bf16 c = 512 tile path only
+    assert call(dtype=0) == ENOTSUP
+    assert call(c=256) == ENOTSUP
+    assert call(n_h=32, sink=FAKE) == ENOTSUP
+    assert call(k=4096) == ENOTSUP
+    # a split decode query needs the attention's workspace
+    kw = dict(n_q=1, t0=4095, n_comp=1024, n_raw=128, pos0=3968, k=512, n_win=128)
+    need = lib.csa_attend_workspace_size(1, 1, 4095, 1024, 64, 512, 512, 4, 128, 1)
+    assert call(ws=None, ws_bytes=need, **kw) == EINVAL
+    assert call(ws=0x100000, ws_bytes=need - 1, **kw) == ENOSPC
+
+
 def test_attend_decode_needs_workspace(lib):
     # one bf16 64-head c=512 query splits its entries: scratch is required
     need = lib.csa_attend_workspace_size(1, 1, 4095, 1024, 64, 512, 512, 4, 128, 1)

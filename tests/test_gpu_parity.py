@@ -1250,6 +1250,63 @@ def test_csa_layer_with_norm_and_rope_bf16():
     assert ratio[i] <= 1.0, ("rotated dims", i, got[..., lo:][i], want[..., lo:][i], bound[i])
 
 
+def test_attend_norm_rope_fused_prefill():
+    # the query norm and rotation done inside the attention's Q load and the
+    # -t rotation of the output in its epilogue: queries rounded to bf16 after
+    # norm and rotation (the kernel's operand precision), the output stored
+    # once, after the back-rotation
+    n, nh, k, nw = 512, 64, 64, 128
+    say(f"attend with fused query norm and rope, prefill n={n} n_h={nh} k={k}")
+    d, gq, gk, Cc, idx, m = _norm_rope_layer_case(n, nh, k, 47)
+    Cc = Cc.to(torch.bfloat16)
+    eps, rd, base = 1e-6, 64, 10000.0
+    Cn = L.csa_norm_rope(g(Cc), g(gk), eps, rd, base, 0, m)
+    Rn = L.csa_norm_rope(g(d["kv_raw"]), g(gk), eps, rd, base, 0, 1)
+    o = L.csa_attend_norm_rope(g(d["q"])[None], g(gq), eps, rd, base, Cn[None], g(idx)[None], Rn[None],
+                               g(d["sink"]), 0, m, nw, d["scale"])[0]
+    torch.cuda.synchronize()
+    st = lambda a: to64(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+    t = np.arange(n)
+    qn = st(O.norm_rope(to64(d["q"]), to64(gq), eps, t, rd, base))
+    Cw = st(O.norm_rope(to64(Cc), to64(gk), eps, m * np.arange(Cc.shape[0]), rd, base))
+    Rw = st(O.norm_rope(to64(d["kv_raw"]), to64(gk), eps, t, rd, base))
+    att = O.csa_attend(qn, Cw, idx.numpy(), Rw, 0, to64(d["sink"]), t, nw, d["scale"], m)
+    assert_close(o, O.rope(att, -t, rd, base), torch.bfloat16, "fused norm and rope, prefill")
+
+
+@pytest.mark.parametrize("nh,rd,t", [
+    (64, 64, 2002),          # the model's rotary width
+    (128, 0, 4099),          # norm only, two head groups
+    (64, 256, (1 << 20) + 3),  # wide rotation at a large position
+    (64, 510, 777),          # every dimension but the first pair rotated
+])
+def test_attend_norm_rope_fused_decode_split(nh, rd, t):
+    # one query per sequence: the entries are split over workgroups, each
+    # partial output turned back by -t before the merge
+    say(f"attend with fused query norm and rope, decode n_h={nh} rope_dims={rd} t={t}")
+    m, k, nw, b = 4, 96, 128, 2
+    n_comp = min((t + 1) // m, 600)    # the cache holds the last completed entries only
+    gen = torch.Generator().manual_seed(53 + rd)
+    q = (3.0 * torch.randn((b, 1, nh, 512), generator=gen)).to(torch.bfloat16)
+    gq = 0.5 + torch.rand(512, generator=gen)
+    Cc = torch.randn((b, n_comp, 512), generator=gen).to(torch.bfloat16)
+    raw = torch.randn((b, nw, 512), generator=gen).to(torch.bfloat16)
+    sink = torch.randn(nh, generator=gen)
+    idx = torch.stack([torch.sort(torch.randperm(n_comp, generator=gen)[:k]).values for _ in range(b)])
+    idx = idx.to(torch.int32)[:, None, :]
+    raw_pos0 = t - nw + 1
+    eps, base = 1e-6, 10000.0
+    out = L.csa_attend_norm_rope(g(q), g(gq), eps, rd, base, g(Cc), g(idx), g(raw), g(sink), t, m, nw,
+                                 1 / math.sqrt(512), raw_pos0=raw_pos0)
+    torch.cuda.synchronize()
+    st = lambda a: to64(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+    for s in range(b):
+        qn = st(O.norm_rope(to64(q[s]), to64(gq), eps, [t], rd, base))
+        att = O.csa_attend(qn, to64(Cc[s]), idx[s].numpy(), to64(raw[s]), raw_pos0, to64(sink), [t], nw,
+                           1 / math.sqrt(512), m)
+        assert_close(out[s], O.rope(att, -np.array([t]), rd, base), torch.bfloat16, f"seq {s}")
+
+
 # ------------------------------------------------ grouped output projection --
 
 def _check_out_proj(o, WG, WO, what):
