@@ -588,22 +588,20 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   if (NRQ) {
     // the query's norm and rotation while the first two tiles are gathered:
     // this wave's sum of squares of each of its heads over its 256 dimensions
+    // (bf16 pairs squared and summed in float32 by the dot instruction)
     float ss[2] = {0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint4 w = __builtin_bit_cast(uint4, qB[ks][hb]);
+        const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float v = (float)qB[ks][hb][i];
-          ss[hb] = fmaf(v, v, ss[hb]);
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, wv[i]);
+          ss[hb] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss[hb], false);
         }
-    // the products below convert Q again: keeping the 128 converted values
-    // of this loop alive instead would not fit the registers
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) asm volatile("" : "+v"(qB[ks][hb]));
+      }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       ss[hb] += __uint_as_float(from_lane_xor16(__float_as_uint(ss[hb]), up16));

@@ -327,7 +327,7 @@ namespace csa {
 
 constexpr int kOverlapWGsPerCU = 16;  // grid cap of the overlapped compressor: workgroups per CU
 constexpr int kPoolChannels = 64;   // channels (of 16 bytes) per workgroup of the pooling kernel
-constexpr int kPoolRows = 8;        // rows per thread and round
+constexpr int kPoolRows = 4;        // rows per thread and round
 
 template <typename T>
 static hipError_t launch_compress_t(const void* Ca, const void* Cb, const void* Za, const void* Zb,

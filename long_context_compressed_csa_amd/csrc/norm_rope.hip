@@ -130,6 +130,77 @@ __global__ __launch_bounds__(256) void norm_rope(const T* x, int64_t xrs, T* out
   }
 }
 
+// Norm (optional) and rotation of rows holding one or two vectors (KV
+// entries, window rows): one wave per row and four rows per workgroup, each
+// wave with its own rotation table, so that no wave of a workgroup idles.
+// Same arithmetic, in the same order, as norm_rope.
+template <typename T, int MC>
+__global__ __launch_bounds__(256) void norm_rope_rows(const T* x, int64_t xrs, T* out, int64_t ors,
+                                                      const float* __restrict__ gamma, float eps, int64_t rows,
+                                                      int heads, int c, int rope_dims, double base, int64_t pos0,
+                                                      int64_t pos_step) {
+  constexpr int V = Vec16<T>::N;
+  __shared__ float2 rot_all[4][kNrMaxPairs];
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;   // a whole wave; there is no workgroup barrier below
+  float2* rot = rot_all[wave];
+  const int lo = c - rope_dims;
+  const int nch = c / V;
+  const T* xr = x + row * xrs;
+  T* orow = out + row * ors;
+  for (int h = 0; h < heads; ++h) {
+    uint4 raw[MC];
+#pragma unroll
+    for (int j = 0; j < MC; ++j) {
+      const int ch = l + 64 * j;
+      raw[j] = ch < nch ? *reinterpret_cast<const uint4*>(xr + (int64_t)h * c + ch * V) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (h == 0) {
+      // the wave's table while its first vector is in flight; the LDS
+      // executes one wave's accesses in order, so the reads below see it
+      const int64_t pos = pos0 + row * pos_step;
+      for (int i = l; i < (rope_dims >> 1); i += 64) {
+        const double theta = pow(base, -2.0 * (double)i / (double)rope_dims);
+        double sn, co;
+        sincos((double)pos * theta, &sn, &co);
+        rot[i] = make_float2((float)co, (float)sn);
+      }
+    }
+    float inv = 1.f;
+    if (gamma) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < MC; ++j)
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const float v = Vec16<T>::get(raw[j], i);
+          ss = fmaf(v, v, ss);
+        }
+      ss = wave_sum(ss);
+      inv = 1.f / sqrtf(ss / (float)c + eps);
+    }
+#pragma unroll
+    for (int j = 0; j < MC; ++j) {
+      const int ch = l + 64 * j;
+      if (ch >= nch) continue;
+      const int d0 = ch * V;
+      float v[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = Vec16<T>::get(raw[j], i) * inv;
+      if (gamma) {
+#pragma unroll
+        for (int i = 0; i < V; i += 4) {
+          const float4 g = *reinterpret_cast<const float4*>(gamma + d0 + i);
+          v[i] *= g.x; v[i + 1] *= g.y; v[i + 2] *= g.z; v[i + 3] *= g.w;
+        }
+      }
+      rotate_chunk<V>(v, d0, lo, rot);
+      Vec16<T>::st(orow + (int64_t)h * c + d0, v);
+    }
+  }
+}
+
 // Rotation only, in place: just the 16-byte chunks holding rotated dims,
 // spread over the workgroup's threads across all vectors of the row (an
 // attention output's 64 rotated dims of 512 are 8 chunks per head).
@@ -187,9 +258,16 @@ hipError_t launch_norm_rope(const void* x, int64_t xrs, void* out, int64_t ors, 
   }
   const int64_t nch = c / (dtype == 1 ? 8 : 4);
   const int mc = nch <= 64 ? 1 : nch <= 128 ? 2 : 4;
-#define CSA_NR_LAUNCH(T, MCV)                                                                            \
-  hipLaunchKernelGGL((norm_rope<T, MCV>), dim3((unsigned)rows), dim3(256), 0, st, (const T*)x, xrs, (T*)out, \
-                     ors, gamma, eps, (int)heads, (int)c, (int)rope_dims, base, pos0, pos_step)
+  // rows of one or two vectors: a wave per row
+  const bool per_wave = heads <= 2;
+#define CSA_NR_LAUNCH(T, MCV)                                                                                  \
+  if (per_wave)                                                                                                \
+    hipLaunchKernelGGL((norm_rope_rows<T, MCV>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,          \
+                       (const T*)x, xrs, (T*)out, ors, gamma, eps, rows, (int)heads, (int)c, (int)rope_dims, base, \
+                       pos0, pos_step);                                                                       \
+  else                                                                                                         \
+    hipLaunchKernelGGL((norm_rope<T, MCV>), dim3((unsigned)rows), dim3(256), 0, st, (const T*)x, xrs, (T*)out,  \
+                       ors, gamma, eps, (int)heads, (int)c, (int)rope_dims, base, pos0, pos_step)
   if (dtype == 1) {
     if (mc == 1) CSA_NR_LAUNCH(bf16_t, 1);
     else if (mc == 2) CSA_NR_LAUNCH(bf16_t, 2);
