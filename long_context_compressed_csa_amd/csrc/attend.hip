@@ -274,6 +274,10 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   // Q operand, this wave's dimensions: lane holds head head0 + 16 hb + l%16,
   // dims 256 dh + 32 ks + 8 (l/16) + (0..7)
   bf16x8 qB[8][2];
+  // NRQ: whether this wave's 32-dimension block blk (dimensions 256 dh +
+  // 32 blk ..) holds rotated dimensions (uniform over the wave)
+  const int dh_u = __builtin_amdgcn_readfirstlane(dh);
+  auto rotated_block = [&](int blk) -> bool { return NRQ && 256 * dh_u + 32 * blk + 31 >= kC - rope_dims; };
   // stable compaction of the valid indices (0 <= s < visible); every index
   // load is issued before the first is used
   constexpr int NT = 64 * NW;
@@ -361,8 +365,11 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   // (cos, +sin) on the pair's first dimension, (cos, -sin) on its second,
   // (1, 0) outside the rotated dimensions
   auto rot_coef = [&](int nb) -> float2 {
-    const float2 r = nr_pr[128 * dh + 16 * nb + ((l & 31) >> 1)];
-    return make_float2(r.x, (l & 1) ? -r.y : r.y);
+    // the lane number recomputed here (mbcnt), so that nothing derived from
+    // it stays live through the main loop for this use
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const float2 r = nr_pr[128 * dh_u + 16 * nb + ((ln & 31) >> 1)];
+    return make_float2(r.x, (ln & 1) ? -r.y : r.y);
   };
   auto unrotate = [](float x, float2 cs) -> float {
     // quad permutation (1, 0, 3, 2): the value of lane l ^ 1
@@ -633,22 +640,35 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
           : "=&v"(ab[0]), "=&v"(ab[1]), "=&v"(ab[2]), "=&v"(ab[3])
           : "v"(ta)
           : "memory");
+      // q'[d] = inv (q[d] A_d + q[d ^ 1] B_d); B = 0 outside the rotated
+      // dimensions, whose blocks skip that product
+      auto norm_rot = [&](auto rot) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        float u[8], v[8];
+        for (int hb = 0; hb < 2; ++hb) {
+          float u[8], v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = (float)qB[ks][hb][i];
+          for (int i = 0; i < 8; ++i) u[i] = (float)qB[ks][hb][i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] = inv[hb] * fmaf(u[2 * j + 1], ab[j][1], u[2 * j] * ab[j][0]);
-          v[2 * j + 1] = inv[hb] * fmaf(u[2 * j], ab[j][3], u[2 * j + 1] * ab[j][2]);
+          for (int j = 0; j < 4; ++j) {
+            if (decltype(rot)::value) {
+              v[2 * j] = inv[hb] * fmaf(u[2 * j + 1], ab[j][1], u[2 * j] * ab[j][0]);
+              v[2 * j + 1] = inv[hb] * fmaf(u[2 * j], ab[j][3], u[2 * j + 1] * ab[j][2]);
+            } else {
+              v[2 * j] = inv[hb] * (u[2 * j] * ab[j][0]);
+              v[2 * j + 1] = inv[hb] * (u[2 * j + 1] * ab[j][2]);
+            }
+          }
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v[2 * i], v[2 * i + 1]}, bf16x2_t));
+          qB[ks][hb] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
         }
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v[2 * i], v[2 * i + 1]}, bf16x2_t));
-        qB[ks][hb] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-      }
+      };
+      if (rotated_block(ks))
+        norm_rot(std::true_type{});
+      else
+        norm_rot(std::false_type{});
     }
   }
   for (;;) {
@@ -696,7 +716,7 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int hr = 8 * (r >> 2) + 4 * half + (r & 3);
-        const float x = NRQ ? unrotate(o[nb][r], cs) : o[nb][r];
+        const float x = rotated_block(nb) ? unrotate(o[nb][r], cs) : o[nb][r];
         po[hr * (int64_t)kC + nb * 32] = ntiles > 0 ? x : 0.f;
       }
     }
@@ -716,11 +736,6 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   float4 g4v[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) g4v[g] = *reinterpret_cast<const float4*>(&sm.bc[wave][8 * g + 4 * half]);
-  float2 rcs[NRQ ? 8 : 1];
-  if (NRQ) {
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) rcs[nb] = rot_coef(nb);
-  }
   unsigned char* stg = wave == 0 ? T0 : wave == 1 ? T1 : wave == 2 ? T2 : XB;
   bf16_t* ob = out + ((bi * n_q + rq) * n_h + head0) * (int64_t)kC + 256 * dh;
   // two passes of 16 head rows (8 KiB of staging each)
@@ -736,9 +751,12 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
         for (int i = 0; i < 4; i += 2) {
           const int hr = 8 * g + 4 * half + i;   // head row; staged at hr - 16 pass
           float x0 = o[nb8][4 * g + i] * gv[i], x1 = o[nb8][4 * g + i + 1] * gv[i + 1];
-          if (NRQ) {
-            x0 = unrotate(x0, rcs[nb8]);
-            x1 = unrotate(x1, rcs[nb8]);
+          if (rotated_block(nb8)) {
+            // read where used: coefficients held across the passes would
+            // push live values to scratch
+            const float2 cs = rot_coef(nb8);
+            x0 = unrotate(x0, cs);
+            x1 = unrotate(x1, cs);
           }
           const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));
           const int byte = ((nb8 * 32 + (l & 31)) * 2) ^ (((hr >> 2) & 1) << 6);
