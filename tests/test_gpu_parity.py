@@ -1274,6 +1274,39 @@ def test_attend_norm_rope_fused_prefill():
     assert_close(o, O.rope(att, -t, rd, base), torch.bfloat16, "fused norm and rope, prefill")
 
 
+def test_attend_norm_rope_fused_chunk_batch_two_groups():
+    # a later chunk of two sequences (queries at t0 .. t0 + n_q - 1, window
+    # rows from t0 - n_win + 1), two 64-head groups, padded index lists
+    b, n_q, t0, nh, k, nw, m = 2, 96, 300, 128, 32, 64, 4
+    say(f"attend with fused query norm and rope, chunk b={b} n_q={n_q} t0={t0} n_h={nh} k={k}")
+    gen = torch.Generator().manual_seed(61)
+    n_comp = (t0 + n_q) // m
+    raw_pos0 = t0 - nw + 1
+    n_raw = t0 + n_q - raw_pos0
+    q = (2.5 * torch.randn((b, n_q, nh, 512), generator=gen)).to(torch.bfloat16)
+    gq = 0.5 + torch.rand(512, generator=gen)
+    Cc = torch.randn((b, n_comp, 512), generator=gen).to(torch.bfloat16)
+    raw = torch.randn((b, n_raw, 512), generator=gen).to(torch.bfloat16)
+    sink = torch.randn(nh, generator=gen)
+    t_pos = t0 + np.arange(n_q)
+    idx = np.full((b, n_q, k), -1, dtype=np.int32)
+    for s_ in range(b):
+        for r in range(n_q):
+            vis = (t_pos[r] + 1) // m
+            take = min(k - (r % 5), vis)     # some lists padded with -1
+            idx[s_, r, :take] = np.sort(torch.randperm(vis, generator=gen)[:take].numpy())
+    eps, rd, base = 1e-6, 64, 10000.0
+    out = L.csa_attend_norm_rope(g(q), g(gq), eps, rd, base, g(Cc), g(torch.tensor(idx)), g(raw), g(sink), t0, m,
+                                 nw, 1 / math.sqrt(512), raw_pos0=raw_pos0)
+    torch.cuda.synchronize()
+    st = lambda a: to64(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+    for s_ in range(b):
+        qn = st(O.norm_rope(to64(q[s_]), to64(gq), eps, t_pos, rd, base))
+        att = O.csa_attend(qn, to64(Cc[s_]), idx[s_], to64(raw[s_]), raw_pos0, to64(sink), t_pos, nw,
+                           1 / math.sqrt(512), m)
+        assert_close(out[s_], O.rope(att, -t_pos, rd, base), torch.bfloat16, f"seq {s_}")
+
+
 @pytest.mark.parametrize("nh,rd,t", [
     (64, 64, 2002),          # the model's rotary width
     (128, 0, 4099),          # norm only, two head groups
