@@ -203,8 +203,11 @@ __device__ __forceinline__ void wave_positions(uint32_t sel, uint32_t (&pos)[R])
   }
 }
 
+// Two workgroups per CU: the register budget this asks for (256 per lane)
+// fits the 64-head, 128-dimension form without spills, and its 80 KiB of
+// LDS fits twice.
 template <int NHB, int KS, int FUSED>
-__global__ __launch_bounds__(256) void index_scores_mfma(
+__global__ __launch_bounds__(256, 2) void index_scores_mfma(
     const bf16_t* __restrict__ qI, const float* __restrict__ w, const bf16_t* __restrict__ KI,
     int64_t comp_bs, int64_t n_q, int64_t t0, int64_t n_comp, int64_t m, int64_t cand_per_wg,
     int64_t n_qblocks, float* __restrict__ scores, int64_t k, int32_t* __restrict__ idx,
