@@ -689,6 +689,216 @@ __global__ __launch_bounds__(kBwdT) void compress_bwd_rows_v(
   }
 }
 
+// The same for m = 4 with the bias gradients folded in: a grid of at most
+// kBiasWGs workgroups walks the (sequence, entry, 8-dimension group) units
+// with a stride that is a multiple of c / 8, so a thread keeps one group of
+// dimensions and sums its rows' dZ per in-block row j for both streams
+// (stream b: the rows of block e - 1, or the previous-block state for
+// e = 0); the four threads of a workgroup that share a group add their sums
+// in thread order and the workgroup writes one partial [stream][j][c]; the
+// final kernel adds the partials in workgroup order.  Deterministic for a
+// given shape.
+constexpr int kBiasWGs = 512;
+template <typename T>
+__global__ __launch_bounds__(kBwdT) void compress_bwd_rows_v4b(
+    const T* __restrict__ Ca, const T* __restrict__ Cb, const T* __restrict__ Za, const T* __restrict__ Zb,
+    const T* __restrict__ Ba, const T* __restrict__ Bb, const T* __restrict__ pCb, const T* __restrict__ pZb,
+    const float* __restrict__ dCc, int64_t b, int64_t n, int c, float* __restrict__ dCa, float* __restrict__ dCb,
+    float* __restrict__ dZa, float* __restrict__ dZb, float* __restrict__ dpCb, float* __restrict__ dpZb,
+    float* __restrict__ part) {
+  constexpr int N = Vec16<T>::N;
+  constexpr int M = 4;
+  typedef Vec16<float> F;
+  __shared__ float red[kBwdT][2 * M][N];
+  const int cv = c / N;
+  const int64_t ne = n / M;
+  const int64_t total = b * (ne + 1) * cv;
+  auto st_f = [](float* p, const float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float w[4] = {v[i], v[i + 1], v[i + 2], v[i + 3]};
+      F::st(p + i, w);
+    }
+  };
+  auto st_zero = [](float* p) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) *reinterpret_cast<float4*>(p + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  float accA[M][N], accB[M][N];
+#pragma unroll
+  for (int j = 0; j < M; ++j)
+#pragma unroll
+    for (int i = 0; i < N; ++i) { accA[j][i] = 0.f; accB[j][i] = 0.f; }
+  const int64_t u0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int d = (int)(u0 % cv) * N;   // the stride keeps it
+  for (int64_t u = u0; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rest = u / cv;
+    const int64_t e = rest % (ne + 1);
+    const int64_t s = rest / (ne + 1);
+    const int64_t sq = s * n * (int64_t)c;
+    if (e == ne) {
+      for (int64_t row = ne * M; row < n; ++row) {
+        st_zero(dCa + sq + row * c + d);
+        st_zero(dZa + sq + row * c + d);
+        st_zero(dCb + sq + row * c + d);
+        st_zero(dZb + sq + row * c + d);
+      }
+      if (ne > 0)
+        for (int j = 0; j < M; ++j) {
+          const int64_t row = (ne - 1) * M + j;
+          st_zero(dCb + sq + row * c + d);
+          st_zero(dZb + sq + row * c + d);
+        }
+      if (ne == 0 && dpCb)
+        for (int j = 0; j < M; ++j) { st_zero(dpCb + (s * M + j) * c + d); st_zero(dpZb + (s * M + j) * c + d); }
+      continue;
+    }
+    const bool hasb = e > 0 || pZb != nullptr;
+    auto zb_row = [&](int j) { return e > 0 ? Zb + sq + (M * (e - 1) + j) * c + d : pZb + (s * M + j) * c + d; };
+    auto cb_row = [&](int j) { return e > 0 ? Cb + sq + (M * (e - 1) + j) * c + d : pCb + (s * M + j) * c + d; };
+    float mx[N], den[N], num[N], g[N], cc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) { mx[i] = -INFINITY; den[i] = 0.f; num[i] = 0.f; }
+    for (int j = 0; j < M; ++j) {
+      float z[N], bb[N];
+      Vec16<T>::ld(Za + sq + (M * e + j) * c + d, z);
+      Vec16<T>::ld(Ba + j * c + d, bb);
+#pragma unroll
+      for (int i = 0; i < N; ++i) mx[i] = fmaxf(mx[i], z[i] + bb[i]);
+      if (hasb) {
+        Vec16<T>::ld(zb_row(j), z);
+        Vec16<T>::ld(Bb + j * c + d, bb);
+#pragma unroll
+        for (int i = 0; i < N; ++i) mx[i] = fmaxf(mx[i], z[i] + bb[i]);
+      }
+    }
+    for (int j = 0; j < M; ++j) {
+      float z[N], bb[N], cv8[N];
+      Vec16<T>::ld(Za + sq + (M * e + j) * c + d, z);
+      Vec16<T>::ld(Ba + j * c + d, bb);
+      Vec16<T>::ld(Ca + sq + (M * e + j) * c + d, cv8);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float pa = __expf(z[i] + bb[i] - mx[i]);
+        den[i] += pa;
+        num[i] = fmaf(pa, cv8[i], num[i]);
+      }
+      if (hasb) {
+        Vec16<T>::ld(zb_row(j), z);
+        Vec16<T>::ld(Bb + j * c + d, bb);
+        Vec16<T>::ld(cb_row(j), cv8);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float pb = __expf(z[i] + bb[i] - mx[i]);
+          den[i] += pb;
+          num[i] = fmaf(pb, cv8[i], num[i]);
+        }
+      }
+    }
+    {
+      float gg[4];
+#pragma unroll
+      for (int i = 0; i < N; i += 4) {
+        F::ld(dCc + (s * ne + e) * c + d + i, gg);
+        g[i] = gg[0]; g[i + 1] = gg[1]; g[i + 2] = gg[2]; g[i + 3] = gg[3];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) cc[i] = num[i] / den[i];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const int64_t ra = M * e + j;
+      float z[N], bb[N], cv8[N], o1[N], o2[N];
+      Vec16<T>::ld(Za + sq + ra * c + d, z);
+      Vec16<T>::ld(Ba + j * c + d, bb);
+      Vec16<T>::ld(Ca + sq + ra * c + d, cv8);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float sa = __expf(z[i] + bb[i] - mx[i]) / den[i];
+        o1[i] = sa * g[i];
+        o2[i] = sa * (cv8[i] - cc[i]) * g[i];
+        accA[j][i] += o2[i];
+      }
+      st_f(dCa + sq + ra * c + d, o1);
+      st_f(dZa + sq + ra * c + d, o2);
+      if (hasb) {
+        Vec16<T>::ld(zb_row(j), z);
+        Vec16<T>::ld(Bb + j * c + d, bb);
+        Vec16<T>::ld(cb_row(j), cv8);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float sb = __expf(z[i] + bb[i] - mx[i]) / den[i];
+          o1[i] = sb * g[i];
+          o2[i] = sb * (cv8[i] - cc[i]) * g[i];
+          accB[j][i] += o2[i];
+        }
+        if (e > 0) {
+          const int64_t rb = M * (e - 1) + j;
+          st_f(dCb + sq + rb * c + d, o1);
+          st_f(dZb + sq + rb * c + d, o2);
+        } else {
+          st_f(dpCb + (s * M + j) * c + d, o1);
+          st_f(dpZb + (s * M + j) * c + d, o2);
+        }
+      } else if (e == 0 && dpCb) {
+        st_zero(dpCb + (s * M + j) * c + d);
+        st_zero(dpZb + (s * M + j) * c + d);
+      }
+    }
+  }
+  // the threads sharing this group of dimensions: t % cv, in thread order
+#pragma unroll
+  for (int j = 0; j < M; ++j)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      red[threadIdx.x][j][i] = accA[j][i];
+      red[threadIdx.x][M + j][i] = accB[j][i];
+    }
+  __syncthreads();
+  if ((int)threadIdx.x < cv) {
+    float* pw = part + (int64_t)blockIdx.x * 2 * M * c;
+    for (int r = 0; r < 2 * M; ++r) {
+      float v[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = 0.f;
+      for (int t = threadIdx.x; t < kBwdT; t += cv)
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += red[t][r][i];
+      st_f(pw + (int64_t)r * c + d, v);
+    }
+  }
+}
+// dB_stream[j][d] = sum over the workgroups' partials, in workgroup order:
+// one workgroup per 64 outputs, wave w adding a quarter of the partials
+// eight loads at a time, the quarters added in wave order.
+__global__ __launch_bounds__(kBwdT) void compress_bwd_bias4_final(const float* __restrict__ part, int nwg, int c,
+                                                                  float* __restrict__ dBa, float* __restrict__ dBb) {
+  __shared__ float ws4[4][64];
+  constexpr int M = 4;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t mc2 = (int64_t)2 * M * c;
+  const int64_t u = (int64_t)blockIdx.x * 64 + l;
+  const int qn = (nwg + 3) / 4;
+  const int w0 = wave * qn, w1 = w0 + qn < nwg ? w0 + qn : nwg;
+  float a = 0.f;
+  if (u < mc2) {
+    for (int w = w0; w < w1; w += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = w + i < w1 ? part[(int64_t)(w + i) * mc2 + u] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (w + i < w1) a += v[i];
+    }
+  }
+  ws4[wave][l] = a;
+  __syncthreads();
+  if (wave == 0 && u < mc2) {
+    const float r = ((ws4[0][l] + ws4[1][l]) + ws4[2][l]) + ws4[3][l];
+    if (u < (int64_t)M * c) dBa[u] = r; else dBb[u - (int64_t)M * c] = r;
+  }
+}
+
 // Bias gradient, stage 1: per (chunk of 64 entries, in-block row j,
 // dimension d) the sum of dZ over the chunk's entries in order (over every
 // sequence); stage 2 adds the chunks in order.  stream b: entry e's rows
@@ -743,10 +953,15 @@ __global__ __launch_bounds__(kBwdT) void compress_bwd_bias_final(const float* __
   if (wave == 0 && u < mc) dB[u] = ((ws4[0][l] + ws4[1][l]) + ws4[2][l]) + ws4[3][l];
 }
 
+// the m = 4 path with 16-byte rows whose dimension groups divide a workgroup
+static bool compress_bwd_v4b_ok(int64_t c, int64_t m) { return m == 4 && c % 8 == 0 && kBwdT % (c / 8) == 0; }
+
 size_t compress_backward_workspace_bytes(int64_t n, int64_t c, int64_t m) {
   const int64_t ne = n / m;
   const int64_t nch = (ne + kBiasChunk - 1) / kBiasChunk;
-  return (size_t)((nch > 0 ? nch : 1) * m * c * 4 + 255) & ~(size_t)255;
+  size_t bytes = (size_t)((nch > 0 ? nch : 1) * m * c * 4 + 255) & ~(size_t)255;
+  if (compress_bwd_v4b_ok(c, m)) bytes = std::max(bytes, (size_t)kBiasWGs * 2 * 4 * c * 4);
+  return bytes;
 }
 
 hipError_t launch_compress_backward(const void* Ca, const void* Cb, const void* Za, const void* Zb, const void* Ba,
@@ -763,6 +978,16 @@ hipError_t launch_compress_backward(const void* Ca, const void* Cb, const void* 
                       (!overlap || (a16(Cb) && a16(Zb) && a16(Bb) && a16(dCb) && a16(dZb))) && a16(pCb) && a16(pZb) &&
                       a16(dpCb) && a16(dpZb);
   const unsigned grid_v = (unsigned)std::min<int64_t>((b * (ne + 1) * (c / 8) + kBwdT - 1) / kBwdT, 65535 * 4);
+  if (vec_ok && overlap && compress_bwd_v4b_ok(c, m)) {
+    const int nwg = (int)std::min<int64_t>((b * (ne + 1) * (c / 8) + kBwdT - 1) / kBwdT, kBiasWGs);
+    hipLaunchKernelGGL(compress_bwd_rows_v4b<bf16_t>, dim3((unsigned)nwg), dim3(kBwdT), 0, st, (const bf16_t*)Ca,
+                       (const bf16_t*)Cb, (const bf16_t*)Za, (const bf16_t*)Zb, (const bf16_t*)Ba, (const bf16_t*)Bb,
+                       (const bf16_t*)pCb, (const bf16_t*)pZb, dCc, b, n, (int)c, dCa, dCb, dZa, dZb, dpCb, dpZb,
+                       (float*)ws);
+    hipLaunchKernelGGL(compress_bwd_bias4_final, dim3((unsigned)((2 * 4 * c + 63) / 64)), dim3(kBwdT), 0, st,
+                       (const float*)ws, nwg, (int)c, dBa, dBb);
+    return hipGetLastError();
+  }
   if (vec_ok)
     hipLaunchKernelGGL(compress_bwd_rows_v<bf16_t>, dim3(grid_v), dim3(kBwdT), 0, st, (const bf16_t*)Ca,
                        (const bf16_t*)Cb, (const bf16_t*)Za, (const bf16_t*)Zb, (const bf16_t*)Ba, (const bf16_t*)Bb,

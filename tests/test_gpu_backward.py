@@ -131,6 +131,8 @@ def test_hca_attend_backward(n, mp, nw, nh, c, dtype):
     (torch.float32, 38, 24, 4, 2, False, True),    # ragged tail, batch of 2
     (torch.float32, 40, 16, 4, 1, True, True),     # continuing from a previous block
     (torch.bfloat16, 1024, 512, 4, 1, False, True),
+    (torch.bfloat16, 1030, 512, 4, 2, True, True),  # bias sums in the row kernel: batch, state, ragged tail
+    (torch.bfloat16, 200, 64, 4, 3, True, True),    # eight dimension groups per row
     (torch.float32, 300, 16, 32, 1, False, False), # pooling, ragged tail
     (torch.bfloat16, 4096, 512, 128, 1, False, False),
 ])
