@@ -9,7 +9,8 @@ that, as the test checks from the inputs alone, a later tile does exceed the
 first one by that much for some heads; the outputs must still match the
 oracle: CSA prefill (one workgroup per query), CSA decode (a query's entries
 split over several workgroups, then merged), HCA prefill (two queries per
-workgroup over the dense entry list) and HCA decode.
+workgroup over the dense entry list) and HCA decode, and the CSA prefill and
+decode forms with the query norm and rotation fused in.
 """
 
 import sys
@@ -154,3 +155,72 @@ def test_hca_decode_split_restart():
     for s in range(b):
         want = O.hca_attend(to64(q[s]), to64(Cc[s]), to64(raw[s]), raw_pos0, to64(sink), [t], mp, nw, scale)
         assert_close(out[s], want, torch.bfloat16, f"hca decode seq {s}, restarted softmax")
+
+
+def _st(a):
+    return to64(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+
+
+def test_csa_prefill_restart_fused_norm_rope():
+    # the same fallback behind the fused query norm: queries of random signs,
+    # unit gain, eps 0 and no rotation, so that the normalised query is the
+    # raw one exactly on both sides (with logits this sharp a one-step bf16
+    # rounding difference of a query element between the float32 kernel and
+    # the float64 oracle would decide near-ties); the decode case below
+    # covers the rotation under the fallback
+    n, k, nw, m, scale = 256, 32, 64, 4, 1.0
+    eps, rd, base = 0.0, 0, 10000.0
+    say(f"sharp softmax: csa prefill with fused norm n={n} k={k} n_win={nw} scale={scale}")
+    d = synth.prefill_inputs(n=n, seed=65, k=k, unscaled=True)
+    q = torch.sign(d["q"].float()).where(d["q"] != 0, torch.ones(())).to(torch.bfloat16)
+    gq = torch.ones(512)
+    Cc = torch.tensor(O.compress_overlap(*(to64(d[x]) for x in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m),
+                      dtype=torch.float32).to(torch.bfloat16)
+    idx, _ = O.index_topk(to64(d["qI"]), to64(d["w"]), to64(d["KIcomp"]), np.arange(n), m, k)
+    t_pos = np.arange(n)
+    qn = O.norm_rope(to64(q), to64(gq), eps, t_pos, rd, base)
+    assert np.array_equal(qn, to64(q)), "the normalised query is the raw one"
+    over = 0
+    for t in range(0, n, 7):
+        sel = idx[t][idx[t] >= 0]
+        E = np.concatenate([to64(Cc)[sel], to64(d["kv_raw"])[max(0, t - nw + 1):t + 1]])
+        if E.shape[0] > 16:
+            over += _over_headroom(qn[t], E, scale)
+    print(f"[restart] (query, head) pairs past the headroom among sampled queries: {over}", flush=True)
+    assert over > 0
+    out = L.csa_attend_norm_rope(g(q)[None], g(gq), eps, rd, base, g(Cc)[None],
+                                 g(torch.tensor(idx, dtype=torch.int32))[None], g(d["kv_raw"])[None], g(d["sink"]),
+                                 0, m, nw, scale)
+    torch.cuda.synchronize()
+    want = O.csa_attend(qn, to64(Cc), idx, to64(d["kv_raw"]), 0, to64(d["sink"]), t_pos, nw, scale, m)
+    assert_close(out[0], want, torch.bfloat16, "fused csa prefill, restarted softmax")
+
+
+def test_csa_decode_split_restart_fused_norm_rope():
+    b, n_comp, k, nw, m, scale = 2, 1500, 512, 128, 4, 1.0
+    eps, rd, base = 1e-6, 64, 10000.0
+    t = n_comp * m + 1
+    say(f"sharp softmax: csa decode with fused norm and rope b={b} n_comp={n_comp} k={k} scale={scale}")
+    gen = torch.Generator().manual_seed(67)
+    q = (2.0 * torch.randn((b, 1, 64, 512), generator=gen)).to(torch.bfloat16)
+    gq = 1.0 + 0.1 * torch.randn(512, generator=gen)
+    Cc = torch.randn((b, n_comp, 512), generator=gen).to(torch.bfloat16)
+    raw = torch.randn((b, nw, 512), generator=gen).to(torch.bfloat16)
+    sink = torch.randn(64, generator=gen)
+    idx = torch.stack([torch.sort(torch.randperm(n_comp, generator=gen)[:k]).values for _ in range(b)])
+    idx = idx.to(torch.int32)[:, None, :]
+    qn = [_st(O.norm_rope(to64(q[s]), to64(gq), eps, [t], rd, base)) for s in range(b)]
+    # plant, in each sequence's second tile, an entry along one normalised head
+    for s in range(b):
+        Cc[s, idx[s, 0, 20]] = torch.tensor(2 * qn[s][0, 5], dtype=torch.float32).to(torch.bfloat16)
+    raw_pos0 = t - nw + 1
+    over = sum(_over_headroom(qn[s][0], Cc[s, idx[s, 0, :32].long()], scale) for s in range(b))
+    print(f"[restart] (sequence, head) pairs past the headroom: {over}", flush=True)
+    assert over > 0
+    out = L.csa_attend_norm_rope(g(q), g(gq), eps, rd, base, g(Cc), g(idx), g(raw), g(sink), t, m, nw, scale,
+                                 raw_pos0=raw_pos0)
+    torch.cuda.synchronize()
+    for s in range(b):
+        att = O.csa_attend(qn[s], to64(Cc[s]), idx[s].numpy(), to64(raw[s]), raw_pos0, to64(sink), [t], nw, scale, m)
+        assert_close(out[s], O.rope(att, -np.array([t]), rd, base), torch.bfloat16,
+                     f"fused csa decode seq {s}, restarted softmax")
