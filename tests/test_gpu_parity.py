@@ -1274,6 +1274,33 @@ def test_attend_norm_rope_fused_prefill():
     assert_close(o, O.rope(att, -t, rd, base), torch.bfloat16, "fused norm and rope, prefill")
 
 
+def test_attend_norm_rope_fused_prefill_full_size_sampled():
+    # the launch the benchmark's fused step times (n = 8192, 64 heads,
+    # k = 512, window 128) on oracle indices and oracle-normalised entries
+    # and window rows; sampled queries against the oracle
+    say("attend with fused query norm and rope, prefill n=8192 (oracle indices, sampled queries)")
+    d = synth.prefill_inputs()
+    p = d["params"]
+    n, m, k, nw = p["n"], p["m"], p["k"], p["n_win"]
+    _, gq = synth.norm_rope_inputs(1, 1, 512, seed=46)
+    _, gk = synth.norm_rope_inputs(1, 1, 512, seed=47)
+    eps, rd, base = 1e-6, 64, 10000.0
+    st = lambda a: torch.tensor(a, dtype=torch.float32).to(torch.bfloat16)
+    Cc = O.compress_overlap(*(to64(d[x]) for x in ("Ca", "Cb", "Za", "Zb", "Ba", "Bb")), m)
+    Cn = st(O.norm_rope(Cc, to64(gk), eps, m * np.arange(Cc.shape[0]), rd, base))
+    Rn = st(O.norm_rope(to64(d["kv_raw"]), to64(gk), eps, np.arange(n), rd, base))
+    idx = _oracle_idx_for(d["KIcomp"], d["qI"], d["w"], np.arange(n), m, k)
+    out = L.csa_attend_norm_rope(g(d["q"])[None], g(gq), eps, rd, base, g(Cn)[None],
+                                 g(torch.tensor(idx, dtype=torch.int32))[None], g(Rn)[None], g(d["sink"]), 0, m, nw,
+                                 d["scale"])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 6), [127, 128, 2047, 2048, 2051], np.arange(8188, 8192),
+                                     np.random.default_rng(2).integers(0, n, 24)]))
+    qn = to64(st(O.norm_rope(to64(d["q"][rows]), to64(gq), eps, rows, rd, base)))
+    att = O.csa_attend(qn, to64(Cn), idx[rows], to64(Rn), 0, to64(d["sink"]), rows, nw, d["scale"], m)
+    assert_close(out[0, rows], O.rope(att, -rows, rd, base), torch.bfloat16, "fused norm and rope, n=8192")
+
+
 def test_attend_norm_rope_fused_chunk_batch_two_groups():
     # a later chunk of two sequences (queries at t0 .. t0 + n_q - 1, window
     # rows from t0 - n_win + 1), two 64-head groups, padded index lists
