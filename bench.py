@@ -556,10 +556,39 @@ def run_hca(args, torch, L, synth):
     ne = n // mp
     pairs = sum(min((t + 1) // mp, ne) + min(t + 1, nw) for t in range(n))
     flop = pairs * 4 * nh * c
+
+    # The attention alone, plain and with the query norm and rotation fused
+    # in (hca_attend_norm_rope; seeded synthetic gain, eps 1e-6, RoPE base
+    # 10000 on the last 64 dims), on the layer's compressed entries.
+    _, gq = synth.norm_rope_inputs(1, 1, c, seed=49, device="cuda")
+    wsA = lib.hca_attend_workspace_size(1, n, 0, ne, nh, c, mp, nw, 1)
+    wsAt = torch.empty(max(wsA, 256), dtype=torch.uint8, device="cuda")
+
+    def attend_plain():
+        return lib.hca_attend(P(d["q"]), P(Cc), 0, P(d["kv_raw"]), 0, 0, P(d["sink"]), 1, n, 0, ne, n, nh, c, mp,
+                              nw, d["scale"], 1, P(wsAt), wsAt.numel(), P(out), st)
+
+    def attend_fused():
+        return lib.hca_attend_norm_rope(P(d["q"]), P(gq), 1e-6, 64, 10000.0, P(Cc), 0, P(d["kv_raw"]), 0, 0,
+                                        P(d["sink"]), 1, n, 0, ne, n, nh, c, mp, nw, d["scale"], 1, P(wsAt),
+                                        wsAt.numel(), P(out), st)
+
+    att_ms = {}
+    for name, fn in (("attend", attend_plain), ("attend_norm_rope", attend_fused)):
+        if fn() != 0:
+            raise RuntimeError(f"hca {name} failed")
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        att_ms[name] = a.elapsed_time(b) / iters
     del d, out
     torch.cuda.empty_cache()
     return {"ms_per_layer": ms, "tokens_per_s": n / (ms * 1e-3), "tflops": flop / (ms * 1e-3) / 1e12,
-            "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop": flop}
+            "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop": flop,
+            "attend_ms": att_ms["attend"], "attend_norm_rope_ms": att_ms["attend_norm_rope"]}
 
 
 def run_hca_decode(args, torch, L, synth):

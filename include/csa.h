@@ -392,6 +392,27 @@ int hca_attend(const void* q, const void* Ccomp, int64_t comp_bstride, const voi
                int64_t c, int64_t m_prime, int64_t n_win, float scale, int dtype,
                void* workspace, size_t ws_bytes, void* out, void* stream);
 
+/*
+ * hca_attend_norm_rope -- hca_attend with the query side of the norm and
+ * partial RoPE folded in, as csa_attend_norm_rope does for CSA (songhuiming
+ * "DeepSeek-V4 百万 token 上下文" sections 4.5 and 5.2; AirCoding
+ * "deepseek-paper-analysis" sections 7.1-7.2): q holds the raw query heads,
+ * each RMS-normalised with gain gamma_q and its last rope_dims dimensions
+ * rotated at the query's position as it is loaded (rounded to bf16 once);
+ * the output's rotated dimensions are turned back by -t in float32 and
+ * stored once in bf16.  gamma_q, eps, rope_dims and base as in
+ * csa_attend_norm_rope; every other argument and the workspace (size
+ * hca_attend_workspace_size()) as in hca_attend.
+ * Errors: as hca_attend, plus the gain, eps, rope_dims, base and position
+ * checks of csa_attend_norm_rope; CSA_ENOTSUP outside bf16, c = 512 and n_h
+ * a multiple of 64.
+ */
+int hca_attend_norm_rope(const void* q, const float* gamma_q, float eps, int64_t rope_dims, double base,
+                         const void* Ccomp, int64_t comp_bstride, const void* kv_raw, int64_t raw_bstride,
+                         int64_t raw_pos0, const float* sink, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp,
+                         int64_t n_raw, int64_t n_h, int64_t c, int64_t m_prime, int64_t n_win, float scale,
+                         int dtype, void* workspace, size_t ws_bytes, void* out, void* stream);
+
 size_t hca_attend_workspace_size(int64_t b, int64_t n_q, int64_t t0, int64_t n_comp,
                                  int64_t n_h, int64_t c, int64_t m_prime, int64_t n_win,
                                  int dtype);

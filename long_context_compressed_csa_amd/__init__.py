@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     load_library, strerror, version, BlockPool, PagedCache, csa_paged_append, csa_paged_index_topk,
     csa_paged_attend, hca_paged_attend, csa_attend_backward, hca_attend_backward, csa_compress_backward,
     csa_quantize_kv_fp8, csa_attend_fp8kv, csa_attend_norm_rope,
+    hca_attend_norm_rope,
 )
 
 __all__ = [
@@ -19,5 +20,5 @@ __all__ = [
     "load_library", "version", "strerror", "CsaError", "CSA_F32", "CSA_BF16", "LIB_PATH",
     "BlockPool", "PagedCache", "csa_paged_append", "csa_paged_index_topk", "csa_paged_attend", "hca_paged_attend",
     "csa_attend_backward", "hca_attend_backward", "csa_compress_backward", "csa_quantize_kv_fp8", "csa_attend_fp8kv",
-    "csa_attend_norm_rope",
+    "csa_attend_norm_rope", "hca_attend_norm_rope",
 ]

@@ -53,6 +53,8 @@ SIGNATURES = {
     "hca_attend": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp] + [_i64] * 9
                    + [_f32, _int, _vp, _sz, _vp, _vp]),
     "hca_attend_workspace_size": (_sz, [_i64] * 8 + [_int]),
+    "hca_attend_norm_rope": (_int, [_vp, _vp, _f32, _i64, ctypes.c_double, _vp, _i64, _vp, _i64, _i64, _vp]
+                             + [_i64] * 9 + [_f32, _int, _vp, _sz, _vp, _vp]),
     "hca_layer": (_int, [_vp] * 6 + [_i64] * 6 + [_f32, _int, _vp, _vp, _sz, _vp, _vp]),
     "hca_layer_workspace_size": (_sz, [_i64] * 6 + [_int]),
     "csa_paged_block_bytes": (_sz, [_i64] * 4),
@@ -398,6 +400,32 @@ def csa_attend_norm_rope(q, gamma_q, eps, rope_dims, base, Ccomp, idx, kv_raw, s
                                   dt, _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                   _ptr(out), _stream(stream))
     _check(rc, "csa_attend_norm_rope")
+    return out
+
+
+def hca_attend_norm_rope(q, gamma_q, eps, rope_dims, base, Ccomp, kv_raw, sink, t0, m_prime, n_win, scale=None,
+                         raw_pos0=0, n_comp=None, n_raw=None, out=None, workspace=None, stream=None):
+    """hca_attend on raw query heads, normalised (gain gamma_q [c] f32) and
+    rotated on their last rope_dims dimensions inside the kernel; the
+    output's rotated dimensions turned back by -t.  Other arguments as
+    hca_attend."""
+    q, Ccomp, kv_raw = _batched(q, 4), _batched(Ccomp, 3), _batched(kv_raw, 3)
+    b, n_q, n_h, c = q.shape
+    n_comp = Ccomp.shape[1] if n_comp is None else n_comp
+    n_raw = kv_raw.shape[1] if n_raw is None else n_raw
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(q, Ccomp, kv_raw)
+    lib = load_library()
+    need = lib.hca_attend_workspace_size(b, n_q, t0, n_comp, n_h, c, m_prime, n_win, dt)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.hca_attend_norm_rope(_ptr(q), _f32c(gamma_q, "gamma_q"), eps, rope_dims, base, _ptr(Ccomp),
+                                  Ccomp.stride(0), _ptr(kv_raw), kv_raw.stride(0), raw_pos0, _f32c(sink, "sink"), b,
+                                  n_q, t0, n_comp, n_raw, n_h, c, m_prime, n_win, scale, dt, _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _ptr(out), _stream(stream))
+    _check(rc, "hca_attend_norm_rope")
     return out
 
 

@@ -356,8 +356,32 @@ int csa_attend_norm_rope(const void* q, const float* gamma_q, float eps, int64_t
   if (ws_bytes < need) return CSA_ENOSPC;
   const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c;
   const int64_t rbs = raw_bstride > 0 ? raw_bstride : n_raw * c;
-  return launched(csa::launch_attend_norm_rope(q, gamma_q, eps, rope_dims, base, Ccomp, cbs, idx, kv_raw, rbs,
+  return launched(csa::launch_attend_norm_rope(0, q, gamma_q, eps, rope_dims, base, Ccomp, cbs, idx, kv_raw, rbs,
                                                raw_pos0, sink, b, n_q, t0, n_comp, n_h, k, m, n_win, scale,
+                                               workspace, out, (hipStream_t)stream));
+}
+
+int hca_attend_norm_rope(const void* q, const float* gamma_q, float eps, int64_t rope_dims, double base,
+                         const void* Ccomp, int64_t comp_bstride, const void* kv_raw, int64_t raw_bstride,
+                         int64_t raw_pos0, const float* sink, int64_t b, int64_t n_q, int64_t t0, int64_t n_comp,
+                         int64_t n_raw, int64_t n_h, int64_t c, int64_t m_prime, int64_t n_win, float scale,
+                         int dtype, void* workspace, size_t ws_bytes, void* out, void* stream) {
+  int rc = check_attend(q, Ccomp, comp_bstride, kv_raw, raw_bstride, raw_pos0, sink, b, n_q, t0,
+                        n_comp, n_raw, n_h, c, m_prime, n_win, scale, dtype, out);
+  if (rc != CSA_OK) return rc;
+  if (!gamma_q || !aligned(gamma_q, 16) || !(eps >= 0.f) || !isfinite(eps)) return CSA_EINVAL;
+  if (rope_dims < 0 || (rope_dims & 1) || rope_dims > c || (rope_dims > 0 && (!(base > 0.0) || !isfinite(base))))
+    return CSA_EINVAL;
+  if (t0 + n_q - 1 > (1LL << 40)) return CSA_EINVAL;
+  if (dtype != CSA_BF16 || c != 512 || n_h % 64 != 0) return CSA_ENOTSUP;
+  if (n_q > 2147483647LL || b > 65535 || n_h > 65535) return CSA_ENOTSUP;
+  const size_t need = hca_attend_workspace_size(b, n_q, t0, n_comp, n_h, c, m_prime, n_win, dtype);
+  if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) != 0)) return CSA_EINVAL;
+  if (ws_bytes < need) return CSA_ENOSPC;
+  const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c;
+  const int64_t rbs = raw_bstride > 0 ? raw_bstride : n_raw * c;
+  return launched(csa::launch_attend_norm_rope(1, q, gamma_q, eps, rope_dims, base, Ccomp, cbs, nullptr, kv_raw, rbs,
+                                               raw_pos0, sink, b, n_q, t0, n_comp, n_h, 0, m_prime, n_win, scale,
                                                workspace, out, (hipStream_t)stream));
 }
 

@@ -1381,16 +1381,20 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
   return hipGetLastError();
 }
 
-// CSA attention with the query heads' RMSNorm and partial RoPE applied as
-// Q is loaded and the output turned back by -t before it is stored (bf16,
-// c = 512, 64-head groups, rope_dims even and <= 512; the caller checked).
-hipError_t launch_attend_norm_rope(const void* q, const float* gq, float eps, int64_t rope_dims, double base,
-                                   const void* Ccomp, int64_t cbs, const int32_t* idx, const void* kv_raw,
-                                   int64_t rbs, int64_t raw_pos0, const float* sink, int64_t b, int64_t n_q,
-                                   int64_t t0, int64_t n_comp, int64_t n_h, int64_t k, int64_t m, int64_t n_win,
-                                   float scale, void* ws, void* out, hipStream_t st) {
+// CSA (dense = 0) or HCA (dense = 1) attention with the query heads' RMSNorm
+// and partial RoPE applied as Q is loaded and the output turned back by -t
+// before it is stored (bf16, c = 512, 64-head groups, rope_dims even and
+// <= 512; the caller checked).
+hipError_t launch_attend_norm_rope(int dense, const void* q, const float* gq, float eps, int64_t rope_dims,
+                                   double base, const void* Ccomp, int64_t cbs, const int32_t* idx,
+                                   const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink, int64_t b,
+                                   int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h, int64_t k, int64_t m,
+                                   int64_t n_win, float scale, void* ws, void* out, hipStream_t st) {
   if (b == 0 || n_q == 0) return hipSuccess;
-  const int ns = attend_nsplit(b, n_q, n_h, k + n_win);   // as launch_attend for a selected list
+  // the split count launch_attend takes for the same list
+  int64_t vmax = (t0 + n_q) / m;
+  if (vmax > n_comp) vmax = n_comp;
+  const int ns = attend_nsplit(b, n_q, n_h, (dense ? vmax : k) + n_win);
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (ns > 1) {
@@ -1401,16 +1405,17 @@ hipError_t launch_attend_norm_rope(const void* q, const float* gq, float eps, in
   }
   const Rows none = dense_rows(cbs);
   const dim3 grid((unsigned)n_q, (unsigned)((n_h / kHG) * ns), (unsigned)b);
-  if (ns == 1)
-    hipLaunchKernelGGL((attend_ds<0, 0, 0, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx,
-                       (const bf16_t*)kv_raw, rbs, raw_pos0, sink, n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, 1,
-                       part_o, part_ml, (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr, gq, eps,
-                       (int)rope_dims, base);
-  else
-    hipLaunchKernelGGL((attend_ds<1, 0, 0, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs, idx,
-                       (const bf16_t*)kv_raw, rbs, raw_pos0, sink, n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, ns,
-                       part_o, part_ml, (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr, gq, eps,
-                       (int)rope_dims, base);
+#define CSA_ATTEND_NRQ(S, D)                                                                                         \
+  hipLaunchKernelGGL((attend_ds<S, 0, D, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)Ccomp, cbs,    \
+                     idx, (const bf16_t*)kv_raw, rbs, raw_pos0, sink, n_q, t0, n_comp, (int)n_h, k, m, n_win, scale, \
+                     ns, part_o, part_ml, (bf16_t*)out, none, (int64_t)0, (const int64_t*)nullptr, gq, eps,          \
+                     (int)rope_dims, base)
+  if (ns == 1) {
+    if (dense) CSA_ATTEND_NRQ(0, 1); else CSA_ATTEND_NRQ(0, 0);
+  } else {
+    if (dense) CSA_ATTEND_NRQ(1, 1); else CSA_ATTEND_NRQ(1, 0);
+  }
+#undef CSA_ATTEND_NRQ
   if (ns > 1)
     hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q), (unsigned)n_h), dim3(128), 0, st, part_o, part_ml,
                        sink, (int)n_h, ns, (bf16_t*)out);

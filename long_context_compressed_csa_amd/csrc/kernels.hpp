@@ -34,11 +34,11 @@ hipError_t launch_index_topk(const void* qI, const float* w, const void* KI, int
 size_t attend_workspace_bytes(int dtype, int64_t b, int64_t n_q, int64_t n_h, int64_t c,
                               int64_t nmax);
 bool attend_supported(int dtype, int64_t n_h, int64_t c, int64_t k);
-hipError_t launch_attend_norm_rope(const void* q, const float* gq, float eps, int64_t rope_dims, double base,
-                                   const void* Ccomp, int64_t cbs, const int32_t* idx, const void* kv_raw,
-                                   int64_t rbs, int64_t raw_pos0, const float* sink, int64_t b, int64_t n_q,
-                                   int64_t t0, int64_t n_comp, int64_t n_h, int64_t k, int64_t m, int64_t n_win,
-                                   float scale, void* ws, void* out, hipStream_t st);
+hipError_t launch_attend_norm_rope(int dense, const void* q, const float* gq, float eps, int64_t rope_dims,
+                                   double base, const void* Ccomp, int64_t cbs, const int32_t* idx,
+                                   const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink, int64_t b,
+                                   int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h, int64_t k, int64_t m,
+                                   int64_t n_win, float scale, void* ws, void* out, hipStream_t st);
 hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cbs, const int32_t* idx,
                          const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink,
                          int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,

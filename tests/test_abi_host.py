@@ -269,6 +269,36 @@ def test_attend_norm_rope_rejects_bad_arguments(lib):
     assert call(ws=0x100000, ws_bytes=need - 1, **kw) == ENOSPC
 
 
+def test_hca_attend_norm_rope_rejects_bad_arguments(lib):
+    def call(ws_bytes=0, **kw):
+        a = dict(q=FAKE, gq=FAKE, eps=1e-6, rd=64, base=10000.0, Cc=FAKE, cbs=0, raw=FAKE, rbs=0, pos0=0, sink=FAKE,
+                 b=1, n_q=4, t0=0, n_comp=1, n_raw=4, n_h=64, c=512, mp=4, n_win=4, scale=0.05, dtype=1, ws=None,
+                 out=FAKE)
+        a.update(kw)
+        return lib.hca_attend_norm_rope(a["q"], a["gq"], a["eps"], a["rd"], a["base"], a["Cc"], a["cbs"], a["raw"],
+                                        a["rbs"], a["pos0"], a["sink"], a["b"], a["n_q"], a["t0"], a["n_comp"],
+                                        a["n_raw"], a["n_h"], a["c"], a["mp"], a["n_win"], a["scale"], a["dtype"],
+                                        a["ws"], ws_bytes, a["out"], None)
+    assert call(q=None) == EINVAL
+    assert call(gq=None) == EINVAL
+    assert call(gq=FAKE + 8) == EINVAL
+    assert call(eps=float("nan")) == EINVAL
+    assert call(rd=7) == EINVAL
+    assert call(rd=1024) == EINVAL
+    assert call(base=-1.0) == EINVAL
+    assert call(n_raw=3) == EINVAL
+    assert call(mp=0) == EINVAL
+    assert call(dtype=0) == ENOTSUP
+    assert call(c=256) == ENOTSUP
+    assert call(n_h=96) == ENOTSUP
+    # one query per sequence over 8192 entries splits: workspace required
+    kw = dict(n_q=1, t0=8192 * 128 + 5, n_comp=8192, n_raw=128, pos0=8192 * 128 + 5 - 127, mp=128, n_win=128)
+    need = lib.hca_attend_workspace_size(1, 1, 8192 * 128 + 5, 8192, 64, 512, 128, 128, 1)
+    assert need > 0
+    assert call(ws=None, ws_bytes=need, **kw) == EINVAL
+    assert call(ws=0x100000, ws_bytes=need - 1, **kw) == ENOSPC
+
+
 def test_attend_decode_needs_workspace(lib):
     # one bf16 64-head c=512 query splits its entries: scratch is required
     need = lib.csa_attend_workspace_size(1, 1, 4095, 1024, 64, 512, 512, 4, 128, 1)

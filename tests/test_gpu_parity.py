@@ -1431,3 +1431,51 @@ def test_hca_layer_with_norm_and_rope_fp32():
     want = O.csa_attend_rope(to64(d["q"]), to64(Cc), idx, to64(d["kv_raw"]), 0, to64(d["sink"]), t, nw,
                              d["scale"], mp, to64(gq), to64(gk), eps, rd, base)
     assert_close(o, want, torch.float32, "hca layer with norm and rope, float32")
+
+
+def test_hca_attend_norm_rope_fused_prefill():
+    # HCA with the query norm and rotation in the attention's Q load and the
+    # -t rotation in its epilogue: bf16 queries normalised and rotated, then
+    # rounded once, oracle-normalised entries (at m' s) and window rows
+    n, mp, nh, nw = 600, 16, 128, 64
+    say(f"hca attend with fused query norm and rope, prefill n={n} m'={mp} n_h={nh} n_win={nw}")
+    d = synth.hca_inputs(n=n, seed=57, n_h=nh, m_prime=mp)
+    _, gq = synth.norm_rope_inputs(1, 1, 512, seed=58)
+    _, gk = synth.norm_rope_inputs(1, 1, 512, seed=59)
+    eps, rd, base = 1e-6, 64, 10000.0
+    st = lambda a: torch.tensor(a, dtype=torch.float32).to(torch.bfloat16)
+    t = np.arange(n)
+    Cc = O.compress_pool(to64(d["C"]), to64(d["Z"]), to64(d["B"]), mp)
+    Cn = st(O.norm_rope(Cc, to64(gk), eps, mp * np.arange(Cc.shape[0]), rd, base))
+    Rn = st(O.norm_rope(to64(d["kv_raw"]), to64(gk), eps, t, rd, base))
+    out = L.hca_attend_norm_rope(g(d["q"])[None], g(gq), eps, rd, base, g(Cn)[None], g(Rn)[None], g(d["sink"]), 0,
+                                 mp, nw, d["scale"])[0]
+    torch.cuda.synchronize()
+    qn = to64(st(O.norm_rope(to64(d["q"]), to64(gq), eps, t, rd, base)))
+    att = O.hca_attend(qn, to64(Cn), to64(Rn), 0, to64(d["sink"]), t, mp, nw, d["scale"])
+    assert_close(out, O.rope(att, -t, rd, base), torch.bfloat16, "hca fused norm and rope, prefill")
+
+
+def test_hca_attend_norm_rope_fused_decode_split():
+    # one query per sequence over every completed entry: the list is split
+    # over workgroups and each partial output turned back before the merge
+    b, n_comp, nw, mp = 2, 3000, 128, 128
+    t = n_comp * mp + 9
+    eps, rd, base = 1e-6, 64, 10000.0
+    say(f"hca attend with fused query norm and rope, decode b={b} n_comp={n_comp} t={t}")
+    gen = torch.Generator().manual_seed(71)
+    q = (3.0 * torch.randn((b, 1, 64, 512), generator=gen)).to(torch.bfloat16)
+    gq = 0.5 + torch.rand(512, generator=gen)
+    Cc = torch.randn((b, n_comp, 512), generator=gen).to(torch.bfloat16)
+    raw = torch.randn((b, nw, 512), generator=gen).to(torch.bfloat16)
+    sink = torch.randn(64, generator=gen)
+    raw_pos0 = t - nw + 1
+    assert L.load_library().hca_attend_workspace_size(b, 1, t, n_comp, 64, 512, mp, nw, 1) > 0
+    out = L.hca_attend_norm_rope(g(q), g(gq), eps, rd, base, g(Cc), g(raw), g(sink), t, mp, nw, 1 / math.sqrt(512),
+                                 raw_pos0=raw_pos0)
+    torch.cuda.synchronize()
+    st = lambda a: to64(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+    for s in range(b):
+        qn = st(O.norm_rope(to64(q[s]), to64(gq), eps, [t], rd, base))
+        att = O.hca_attend(qn, to64(Cc[s]), to64(raw[s]), raw_pos0, to64(sink), [t], mp, nw, 1 / math.sqrt(512))
+        assert_close(out[s], O.rope(att, -np.array([t]), rd, base), torch.bfloat16, f"seq {s}")
