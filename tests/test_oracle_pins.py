@@ -914,3 +914,90 @@ def test_kv_fp8_storage():
     head = E[:, :64]
     big = np.abs(head) >= 2.0 ** -6 * scale[:, None]
     assert np.all(np.abs(back[:, :64] - head)[big] <= 2.0 ** -4 * np.abs(head)[big])
+
+
+# ------------------------------------------- window, scale, HCA layer ----
+
+def test_window_rows_positions():
+    # the causal window of a query at t: the n_win positions ending at t,
+    # fewer at the sequence start ([P2] section 4.5)
+    assert O.window_rows(0, 4).tolist() == [0]
+    assert O.window_rows(5, 3).tolist() == [3, 4, 5]
+    assert O.window_rows(2, 10).tolist() == [0, 1, 2]
+    assert len(O.window_rows(1000, 128)) == 128
+
+
+def test_default_scale_reading():
+    # the reading 1/sqrt(c): a logit of q.e with unit-variance entries and
+    # queries has unit variance after scaling
+    rng = _rng(9)
+    c = 512
+    q, e = rng.standard_normal((4000, c)), rng.standard_normal((4000, c))
+    z = O.default_scale(c) * np.sum(q * e, axis=1)
+    assert abs(O.default_scale(c) - 1 / math.sqrt(c)) == 0.0
+    assert 0.9 < float(np.std(z)) < 1.1
+
+
+def test_hca_layer_one_row_blocks_is_dense_attention_with_duplicates():
+    # m' = 1: each entry is its block's single row (softmax over one score),
+    # so query t reads every row 0..t as an entry and again its window rows;
+    # written independently as one masked score matrix with a sink column
+    rng = _rng(10)
+    n, c, nh, nw = 9, 6, 2, 3
+    C = rng.standard_normal((n, c))
+    Z = rng.standard_normal((n, c))
+    B = rng.standard_normal((1, c))
+    q = rng.standard_normal((n, nh, c))
+    sink = rng.standard_normal(nh)
+    scale = 0.7
+    Cc, out = O.hca_layer(C, Z, B, q, C, sink, 1, nw, scale)
+    assert np.allclose(Cc, C, rtol=0, atol=1e-15)
+    Ct = torch.tensor(C)
+    for t in range(n):
+        keys = torch.cat([Ct[: t + 1], Ct[max(0, t - nw + 1): t + 1]])      # entries, then the window
+        qt = torch.tensor(q[t])
+        logits = scale * qt @ keys.T                                          # [nh, N]
+        full = torch.cat([logits, torch.tensor(sink)[:, None]], dim=1)        # sink column
+        p = torch.softmax(full, dim=1)[:, :-1]
+        want = (p @ keys).numpy()
+        assert np.allclose(out[t], want, rtol=1e-12, atol=1e-12), t
+
+
+def test_attend_entries_backward_finite_differences():
+    # the per-query gradient routine against central differences of the
+    # forward attention (entries shared by the heads, sink in the denominator)
+    rng = _rng(11)
+    nh, c, N = 3, 5, 7
+    q = rng.standard_normal((nh, c))
+    E = rng.standard_normal((N, c))
+    sink = rng.standard_normal(nh)
+    g = rng.standard_normal((nh, c))
+    scale = 0.8
+    dq, dE, dz = O.attend_entries_backward(q, E, sink, scale, g)
+    L = lambda q_, E_, z_: float(np.sum(O.attend_entries(q_, E_, z_, scale) * g))
+    h = 1e-6
+    for arr, grad, name in ((q, dq, "q"), (E, dE, "E"), (sink, dz, "sink")):
+        num = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            up, dn = arr.copy(), arr.copy()
+            up[i] += h
+            dn[i] -= h
+            args_up = {"q": (up, E, sink), "E": (q, up, sink), "sink": (q, E, up)}[name]
+            args_dn = {"q": (dn, E, sink), "E": (q, dn, sink), "sink": (q, E, dn)}[name]
+            num[i] = (L(*args_up) - L(*args_dn)) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-7), name
+
+
+def test_norm_rope_special_cases():
+    # no gain: the rotation alone; no rotated dimensions: the norm alone;
+    # and a rotation keeps every pair's length, so the normalised vector's
+    # mean square (gain 1) is the same whichever of the two runs first
+    rng = _rng(12)
+    x = rng.standard_normal((5, 2, 16)) * 3
+    pos = np.arange(5) * 7
+    g = 1 + 0.1 * rng.standard_normal(16)
+    assert np.array_equal(O.norm_rope(x, None, 0.0, pos, 8, 100.0), O.rope(x, pos, 8, 100.0))
+    assert np.array_equal(O.norm_rope(x, g, 1e-6, pos, 0, 100.0), O.rms_norm(x, g, 1e-6))
+    y = O.norm_rope(x, np.ones(16), 0.0, pos, 8, 100.0)
+    assert np.allclose(np.mean(y ** 2, axis=-1), 1.0, rtol=1e-12)
+    assert np.allclose(y, O.rms_norm(O.rope(x, pos, 8, 100.0), np.ones(16), 0.0), rtol=1e-12, atol=1e-12)
