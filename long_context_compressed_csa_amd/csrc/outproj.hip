@@ -22,9 +22,10 @@
 // second register set while the current stage's MFMAs run.  Chunk c
 // (16 B) of tile row r sits at position c ^ ((r >> 2) & 3) of its row, so the
 // operand reads of 16 consecutive rows at one chunk hit 16 distinct bank
-// groups.  Workgroups are ordered so that each XCD (dispatch index mod 8)
-// gets a contiguous range of tiles, row-block major: tiles sharing A rows
-// share that XCD's L2.
+// groups.  The tile grid is split into an xr x xc grid of blocks, one per
+// XCD (dispatch index mod 8), the split chosen to read the least from HBM
+// (A once per column group, B once per row group): tiles sharing A rows or
+// B rows share that XCD's L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -72,15 +73,29 @@ __device__ __forceinline__ void gemm_acc_pad() { asm volatile("s_nop 7\n\ts_nop 
 __global__ __launch_bounds__(256) void gemm_nt_bf16(const bf16_t* __restrict__ A, int64_t lda, int64_t sa,
                                                     const bf16_t* __restrict__ B, int64_t ldb, int64_t sb,
                                                     bf16_t* __restrict__ C, int64_t ldc, int64_t sc, int M, int N,
-                                                    int K, int tiles_m, int tiles_n) {
+                                                    int K, int tiles_m, int tiles_n, int xr) {
   __shared__ __attribute__((aligned(16))) unsigned char S0[kGStageB];
   __shared__ __attribute__((aligned(16))) unsigned char S1[kGStageB];
   __shared__ __attribute__((aligned(16))) unsigned char S2[kGStageB];
   __shared__ __attribute__((aligned(16))) unsigned char S3[kGStageB];
   const int T = tiles_m * tiles_n;
   const int L = blockIdx.x;
-  const int t = (T & 7) == 0 ? (L & 7) * (T >> 3) + (L >> 3) : L;
-  const int m0 = (t / tiles_n) * kGBM, n0 = (t % tiles_n) * kGBN;
+  // XCD x (dispatch index mod 8) takes block (x / xc, x % xc) of an xr x xc
+  // grid of tile blocks (xr xc = 8), row-major inside its block; xr = 0:
+  // no such split (dispatch order)
+  int tm_, tn_;
+  if (xr > 0) {
+    const int xc = 8 / xr, bm = tiles_m / xr, bn = tiles_n / xc;
+    const int x = L & 7, loc = L >> 3;
+    tm_ = (x / xc) * bm + loc / bn;
+    tn_ = (x % xc) * bn + loc % bn;
+  } else {
+    // contiguous ranges of tiles per XCD, row-block major
+    const int t = (T & 7) == 0 ? (L & 7) * (T >> 3) + (L >> 3) : L;
+    tm_ = t / tiles_n;
+    tn_ = t % tiles_n;
+  }
+  const int m0 = tm_ * kGBM, n0 = tn_ * kGBN;
   const int64_t bz = blockIdx.y;
   A += bz * sa;
   B += bz * sb;
@@ -204,8 +219,18 @@ static hipError_t launch_gemm_nt(const bf16_t* A, int64_t lda, int64_t sa, const
                                  int64_t sb, bf16_t* C, int64_t ldc, int64_t sc, int64_t M, int64_t N, int64_t K,
                                  int64_t batch, hipStream_t st) {
   const int tm = (int)((M + kGBM - 1) / kGBM), tn = (int)((N + kGBN - 1) / kGBN);
+  // the split of the tile grid over the 8 XCDs (each with its own L2) that
+  // reads the least: A is read once per column group, B once per row group
+  int xr = 0;
+  double best = 0.0;
+  for (int r = 1; r <= 8; r *= 2) {
+    const int c = 8 / r;
+    if (tm % r || tn % c) continue;
+    const double bytes = (double)M * K * c + (double)N * K * r;
+    if (xr == 0 || bytes < best) { xr = r; best = bytes; }
+  }
   hipLaunchKernelGGL(gemm_nt_bf16, dim3((unsigned)(tm * tn), (unsigned)batch), dim3(256), 0, st, A, lda, sa, B, ldb,
-                     sb, C, ldc, sc, (int)M, (int)N, (int)K, tm, tn);
+                     sb, C, ldc, sc, (int)M, (int)N, (int)K, tm, tn, xr);
   return hipGetLastError();
 }
 
