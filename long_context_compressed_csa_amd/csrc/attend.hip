@@ -284,16 +284,34 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
   constexpr int NR = kMaxSel / NT;
   int64_t vis = (t + 1) / m;
   if (vis > n_comp) vis = n_comp;
-  if (DENSE) {
-    sm.gen = 0;   // every thread writes the same value; read after a later barrier
-  } else {
+  // the index list and Q are loaded together, the index list first: the
+  // compaction waits only for it, and Q's latency overlaps the compaction
+  int32_t sv[NR];
+  if (!DENSE) {
     const int32_t* ir = idx + (bi * n_q + rq) * k;
-    int32_t sv[NR];
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
       const int64_t j = (int64_t)u * NT + tid;
       sv[u] = j < k ? ir[j] : -1;
     }
+  }
+  // NRQ: this thread's pair of gains, loaded ahead of Q so that waiting
+  // for it does not wait for Q
+  float2 gv = make_float2(0.f, 0.f);
+  if (NRQ) {
+    static_assert(2 * 64 * NW == kC, "one pair of dimensions per thread");
+    gv = reinterpret_cast<const float2*>(gq)[tid];
+  }
+  {
+    const bf16_t* qp = q + ((bi * n_q + rq) * n_h + head0 + s16) * (int64_t)kC + 256 * dh + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) qB[ks][hb] = *reinterpret_cast<const bf16x8*>(qp + hb * 16 * kC + ks * 32);
+  }
+  if (DENSE) {
+    sm.gen = 0;   // every thread writes the same value; read after a later barrier
+  } else {
     uint64_t mk[NR];
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
@@ -322,18 +340,6 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
     sm.gen = 0;   // every thread writes the same value; read after the next barrier
   }
   {
-    const bf16_t* qp = q + ((bi * n_q + rq) * n_h + head0 + s16) * (int64_t)kC + 256 * dh + 8 * g4;
-    // NRQ: this thread's pair of gains, loaded ahead of Q so that waiting
-    // for it does not wait for Q
-    float2 gv = make_float2(0.f, 0.f);
-    if (NRQ) {
-      static_assert(2 * 64 * NW == kC, "one pair of dimensions per thread");
-      gv = reinterpret_cast<const float2*>(gq)[tid];
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) qB[ks][hb] = *reinterpret_cast<const bf16x8*>(qp + hb * 16 * kC + ks * 32);
     if (NRQ) {
       // the tables while Q is in flight, angles in float64 (positions reach
       // 2^20 and beyond).  Thread tid: the pair of dimensions (2 tid,
