@@ -1,6 +1,6 @@
 """Benchmark of one CSA layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|hca|compress|next|peaks]
                     [--no-cpu-baseline] [--calibrate-copy]
 
 One step is one CSA prefill layer at n = 8192 (64 heads, c = 512, m = 4,
@@ -10,7 +10,9 @@ on device-resident synthetic inputs.  The JSON line reports prefill tokens/s
 as `value`, the attention kernel's MFMA roofline fraction from HIP-event
 timings, and the CPU oracle's rate on a bounded sample.  Secondary lines in
 the same JSON object: 1M-context decode (8 sequences, microseconds per step),
-the HCA prefill layer (n = 131072) and the compressor sweep (n = 65536).
+the HCA prefill layer (n = 131072), the compressor sweep (n = 65536), and
+what a plain library copy and bf16 GEMM reach on the same GPU, beside the
+published peaks.
 """
 
 from __future__ import annotations
@@ -908,6 +910,33 @@ def calibrate_copy(torch):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}))
 
 
+def run_achievable_peaks(args, torch):
+    """What plain library work reaches on this GPU beside the published
+    peaks: an elementwise copy of 1 GiB (1 GiB read and 1 GiB written per
+    call) and a square bf16 GEMM (torch.mm, 8192^3, both operands
+    contiguous, float32 accumulation).  Context for the roofline fractions,
+    which stay against the published peaks."""
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    us_copy = _event_us(torch, lambda: torch.mul(a, 1.0, out=b), 20)
+    del a, b
+    nm = 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    x = torch.randn((nm, nm), device="cuda", generator=g).to(torch.bfloat16)
+    y = torch.randn((nm, nm), device="cuda", generator=g).to(torch.bfloat16)
+    z = torch.empty((nm, nm), dtype=torch.bfloat16, device="cuda")
+    us_mm = _event_us(torch, lambda: torch.mm(x, y, out=z), 20)
+    del x, y, z
+    gbs = 2 * nbytes / (us_copy * 1e-6) / 1e9
+    tf = 2 * nm ** 3 / (us_mm * 1e-6) / 1e12
+    return {"hbm_copy_gbs": gbs, "hbm_copy_frac": gbs / PEAK_HBM_GBS,
+            "bf16_gemm_tflops": tf, "bf16_gemm_frac": tf / PEAK_BF16_TFLOPS,
+            "copy": "torch elementwise copy, 1 GiB read + 1 GiB written per call",
+            "gemm": "torch.mm, 8192 x 8192 x 8192 bf16, contiguous operands"}
+
+
 # ------------------------------------------------------- HBM traffic ----
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_ds_csa_prefill_n8192_hbm_traffic.json")
@@ -997,7 +1026,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps before the timed ones; about 50 prefill steps bring the GPU clocks to "
                          "their steady state (dispatch times fall by about a fifth over the first 25)")
-    ap.add_argument("--only", choices=["prefill", "decode", "hca", "compress", "next"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "hca", "compress", "next", "peaks"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=8192)
     ap.add_argument("--decode-reps", type=int, default=10)
@@ -1052,6 +1081,10 @@ def main(argv=None):
         torch.cuda.empty_cache()
         print("[bench] fp8 kv, bf16 scores", file=sys.stderr, flush=True)
         extras.update(run_fp8kv_and_bf16_scores(a, torch, L, synth))
+        torch.cuda.empty_cache()
+    if a.only in (None, "peaks") and not a.core:
+        print("[bench] achievable peaks", file=sys.stderr, flush=True)
+        extras["achievable_peaks"] = run_achievable_peaks(a, torch)
         torch.cuda.empty_cache()
     if pre is None or a.core:
         if pre is not None:
