@@ -643,7 +643,10 @@ size_t csa_paged_attend_workspace_size(int64_t b, int64_t n_h, int64_t k, int64_
 /*
  * hca_paged_attend -- hca_attend for one query per row at position pos[i]:
  * every completed HCA entry ((pos+1)/m') of the request's blocks plus the
- * window from its HCA window ring.  As csa_paged_attend otherwise.
+ * window from its HCA window ring.  As csa_paged_attend otherwise;
+ * CSA_ENOTSUP also when n_hca_max + n_win exceeds 2^25 entries (the list is
+ * split at least every 2048 entries, and the split merge takes at most
+ * 16384 splits).
  */
 int hca_paged_attend(const void* q, const void* blocks, int64_t n_blocks, const int32_t* block_table,
                      int64_t bt_stride, const int32_t* req_slot, const int64_t* pos, const void* state,

@@ -597,6 +597,7 @@ int paged_attend_common(int dense, const void* q, const void* blocks, int64_t n_
   if (n_max > bt_stride * (dense ? g.e2 : g.e1)) return CSA_EINVAL;
   // the MFMA path only: c = 512, 64-head groups, at most 2048 selected entries
   if (c != 512 || n_h % 64 != 0 || (!dense && k > 2048) || b > 65535 || n_h > 65535) return CSA_ENOTSUP;
+  if (!csa::attend_paged_supported(dense, b, n_h, (dense ? n_max : k) + n_win)) return CSA_ENOTSUP;
   const size_t need = csa::attend_paged_workspace_bytes(dense, b, n_h, (dense ? n_max : k) + n_win);
   if (need > 0 && (!workspace || !aligned(workspace, 256))) return CSA_EINVAL;
   if (ws_bytes < need) return CSA_ENOSPC;

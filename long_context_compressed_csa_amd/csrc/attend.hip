@@ -1272,40 +1272,63 @@ hipError_t launch_attend_bwd_mfma(int dense, const void* q, const void* Ccomp, i
   return hipGetLastError();
 }
 
-// Merge the splits of one (query, head) in split order (log2-domain maxima),
-// then apply the sink: out = sum_s O_s 2^{m_s - M} / (sum_s l_s 2^{m_s - M} + 2^{z - M}).
+// Merge the splits of one (query, head), then apply the sink:
+//   out = sum_s O_s 2^{m_s - M} / (sum_s l_s 2^{m_s - M} + 2^{z - M}),
+// M the largest of the m_s and z (log2 domain).  The first wave loads every
+// split's (m_s, l_s) at once (lane s, s + 64, ...), reduces M and the
+// denominator over the wave in a fixed order and leaves each split's weight
+// 2^{m_s - M} in LDS (nsplit floats of dynamic LDS); then the workgroup's
+// 128 threads stream the partial rows, 4 values each, in split order.
 __global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const float* __restrict__ sink, int n_h,
                                                       int nsplit, bf16_t* __restrict__ out) {
+  extern __shared__ float split_w[];   // nsplit weights
+  __shared__ float den_sh;
+  const int tx = threadIdx.x;
   const int64_t qr = blockIdx.x;   // b * n_q + r
   const int h = blockIdx.y;
   const int hg = h / kHG, hh = h % kHG;
   const int64_t base = (qr * (n_h / kHG) + hg) * nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((base + s) * kHG + hh) * 2]);
-  const float z2 = sink[h] * kLog2e;
-  const float Mf = fmaxf(M, z2);
-  float L = 0.f;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml);
+  if (tx < 64) {
+    float M = -INFINITY;
+    for (int s = tx; s < nsplit; s += 64) M = fmaxf(M, ml[(base + s) * kHG + hh].x);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float z2 = sink[h] * kLog2e;
+    const float Mf = fmaxf(M, z2);
+    float L = 0.f;
+    for (int s = tx; s < nsplit; s += 64) {
+      const float2 v = ml[(base + s) * kHG + hh];
+      // an empty split (maximum -inf) has weight 0
+      const float f = (v.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(v.x - Mf);
+      L = fmaf(v.y, f, L);
+      split_w[s] = f;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o, 64);
+    if (tx == 0) den_sh = L + __builtin_amdgcn_exp2f(z2 - Mf);
+  }
+  __syncthreads();
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
-    const float ms = part_ml[((base + s) * kHG + hh) * 2];
-    const float ls = part_ml[((base + s) * kHG + hh) * 2 + 1];
-    const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - Mf);
-    L = fmaf(ls, f, L);
-    const float4 v = reinterpret_cast<const float4*>(part_o + ((base + s) * kHG + hh) * (int64_t)kC)[threadIdx.x];
+    const float f = split_w[s];
+    const float4 v = reinterpret_cast<const float4*>(part_o + ((base + s) * kHG + hh) * (int64_t)kC)[tx];
     acc.x = fmaf(v.x, f, acc.x);
     acc.y = fmaf(v.y, f, acc.y);
     acc.z = fmaf(v.z, f, acc.z);
     acc.w = fmaf(v.w, f, acc.w);
   }
-  const float inv = 1.f / (L + __builtin_amdgcn_exp2f(z2 - Mf));
-  bf16_t* ob = out + (qr * n_h + h) * (int64_t)kC + 4 * threadIdx.x;
+  const float inv = 1.f / den_sh;
+  bf16_t* ob = out + (qr * n_h + h) * (int64_t)kC + 4 * tx;
   const uint2 pk = make_uint2((uint32_t)f2bf(acc.x * inv) | ((uint32_t)f2bf(acc.y * inv) << 16),
                               (uint32_t)f2bf(acc.z * inv) | ((uint32_t)f2bf(acc.w * inv) << 16));
   *reinterpret_cast<uint2*>(ob) = pk;
 }
+// splits a combine takes: its weights fill at most 64 KiB of LDS
+constexpr int kCombineMaxSplits = 16384;
 
 // ---------------------------------------------------------------------------
 // Host side
@@ -1378,7 +1401,7 @@ hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cb
     }
 #undef CSA_ATTEND_DS
     if (ns > 1)
-      hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q), (unsigned)n_h), dim3(128), 0, st,
+      hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q), (unsigned)n_h), dim3(128), ns * sizeof(float), st,
                          part_o, part_ml, sink, (int)n_h, ns, (bf16_t*)out);
     return hipGetLastError();
   }
@@ -1430,7 +1453,7 @@ hipError_t launch_attend_norm_rope(int dense, const void* q, const float* gq, fl
   }
 #undef CSA_ATTEND_NRQ
   if (ns > 1)
-    hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q), (unsigned)n_h), dim3(128), 0, st, part_o, part_ml,
+    hipLaunchKernelGGL(attend_combine, dim3((unsigned)(b * n_q), (unsigned)n_h), dim3(128), ns * sizeof(float), st, part_o, part_ml,
                        sink, (int)n_h, ns, (bf16_t*)out);
   return hipGetLastError();
 }
@@ -1444,6 +1467,10 @@ static int attend_paged_nsplit(int dense, int64_t b, int64_t n_h, int64_t nmax) 
   int ns = attend_nsplit(b, 1, n_h, nmax);
   const int64_t need = dense ? (nmax + kMaxSel - 1) / kMaxSel : 1;
   return ns < need ? (int)need : ns;
+}
+
+bool attend_paged_supported(int dense, int64_t b, int64_t n_h, int64_t nmax) {
+  return attend_paged_nsplit(dense, b, n_h, nmax) <= kCombineMaxSplits;
 }
 
 size_t attend_paged_workspace_bytes(int dense, int64_t b, int64_t n_h, int64_t nmax) {
@@ -1460,6 +1487,7 @@ hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const
   if (b == 0) return hipSuccess;
   const int64_t nmax = (dense ? n_comp_max : k) + n_win;
   const int ns = attend_paged_nsplit(dense, b, n_h, nmax);
+  if (ns > kCombineMaxSplits) return hipErrorInvalidValue;   // the entry point rejects these first
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (ns > 1) {
@@ -1481,7 +1509,7 @@ hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const
   }
 #undef CSA_ATTEND_DS_PG
   if (ns > 1)
-    hipLaunchKernelGGL(attend_combine, dim3((unsigned)b, (unsigned)n_h), dim3(128), 0, st, part_o, part_ml, sink,
+    hipLaunchKernelGGL(attend_combine, dim3((unsigned)b, (unsigned)n_h), dim3(128), ns * sizeof(float), st, part_o, part_ml, sink,
                        (int)n_h, ns, (bf16_t*)out);
   return hipGetLastError();
 }

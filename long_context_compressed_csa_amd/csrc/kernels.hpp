@@ -82,6 +82,9 @@ bool index_topk_paged_supported(int64_t nh, int64_t cI);
 hipError_t launch_index_topk_paged(const void* qI, const float* w, const void* pool, const Rows& kr,
                                    const int64_t* pos, int64_t b, int64_t n_comp_max, int64_t nh, int64_t cI,
                                    int64_t m, int64_t k, int32_t* idx, float* score, void* ws, hipStream_t st);
+// whether the split combine can take a paged list of nmax entries (its
+// split weights fill at most 64 KiB of LDS)
+bool attend_paged_supported(int dense, int64_t b, int64_t n_h, int64_t nmax);
 size_t attend_paged_workspace_bytes(int dense, int64_t b, int64_t n_h, int64_t nmax);
 hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const Rows& er, const int32_t* idx,
                                const void* state, int64_t state_elems, int64_t ring, const int64_t* pos,

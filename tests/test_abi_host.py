@@ -438,3 +438,10 @@ def test_paged_geometry_and_validation(lib):
     assert att(nh=32) == ENOTSUP
     assert att(n_max=4 * 32 + 1) == EINVAL
     assert att(dtype=0) == ENOTSUP
+    # HCA: the list is split at least every 2048 entries and the split merge
+    # takes at most 16384 splits: 2^25 entries with the window
+    def hca(n_max, ws_bytes=1 << 30):
+        return lib.hca_paged_attend(FAKE, FAKE, 8, FAKE, 1 << 26, None, FAKE, FAKE, FAKE, 2, n_max, 64, 512, 128, 4,
+                                    128, 128, 0.05, 1, FAKE, ws_bytes, FAKE, None)
+    assert hca((1 << 25) - 127) == ENOTSUP
+    assert hca((1 << 25) - 128) == ENOSPC      # supported; its split partials need more workspace
