@@ -151,3 +151,56 @@ def test_paged_decode_mixed_lengths_matches_oracle():
           flush=True)
     assert n_checked >= 15
     pool.close()
+
+
+def test_hca_paged_attend_many_splits_matches_oracle():
+    """A paged HCA list long enough for more splits than one wave has lanes:
+    140,000 entries plus the window take 69 splits (one per 2048 entries), so
+    the split merge reads some splits' (maximum, sum) in a second round.  The
+    pool is filled with random entries, the request's last block is appended
+    token by token (its HCA entry, and the window ring, written by the
+    library), and the oracle attends over the entries read back from the
+    pool."""
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    L.load_library()
+    c, cI, m, mp, nw, nh = 512, 128, 4, 128, 128, 64
+    scale = 1.0 / math.sqrt(c)
+    n_prior = 139_999                   # HCA entries already in the pool
+    n_blocks = n_prior + 1              # one block per 128 tokens
+    P0 = mp * n_prior                   # first token of the last block
+    t = P0 + mp - 1                     # the query: the last block complete
+    n_vis = (t + 1) // mp               # 140,000 entries
+    say(f"paged HCA, {n_vis} entries + {nw} window rows, t = {t}")
+    cache = L.PagedCache(n_blocks, 1, n_blocks, c, cI, m, mp, nw, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17)
+    cache.blocks.normal_(0.0, 1.0 / math.sqrt(c), generator=g)
+    cache.state.zero_()
+    perm = torch.randperm(n_blocks, generator=g, device=DEV).to(torch.int32)
+    cache.table[0].copy_(perm)
+    gen = torch.Generator().manual_seed(18)
+    rnd = lambda *s: (torch.randn(s, generator=gen) / math.sqrt(s[-1])).to(torch.bfloat16)
+    biases = {"Ba": rnd(m, c), "Bb": rnd(m, c), "IBa": rnd(m, cI), "IBb": rnd(m, cI), "B_h": rnd(mp, c)}
+    gb = {x: v.to(DEV) for x, v in biases.items()}
+    slot = torch.zeros(1, dtype=torch.int32, device=DEV)
+    window = []
+    for p in range(P0, t + 1):
+        tok = {x: rnd(1, c) for x in ("Ca", "Cb", "Za", "Zb", "C_h", "Z_h")}
+        tok.update({x: rnd(1, cI) for x in ("ICa", "ICb", "IZa", "IZb")})
+        L.csa_paged_append(cache, torch.tensor([p], dtype=torch.int64, device=DEV),
+                           {x: v.to(DEV) for x, v in tok.items()}, gb, req_slot=slot)
+        window.append(to64(tok["C_h"][0]))
+    q = rnd(1, nh, c)
+    sink = torch.randn(nh, generator=gen)
+    out = L.hca_paged_attend(cache, q.to(DEV), sink.to(DEV), torch.tensor([t], dtype=torch.int64, device=DEV),
+                             n_vis, scale, req_slot=slot)
+    torch.cuda.synchronize()
+    # entry s sits in block table[s], after the block's 32 CSA entries and 32 keys
+    rows = cache.blocks.view(n_blocks, cache.block_bytes // 2)
+    off = 32 * (c + cI)
+    H = to64(rows[perm[:n_vis].long(), off: off + c].cpu())
+    want = O.hca_attend(to64(q[0])[None], H, np.stack(window), P0, to64(sink), [t], mp, nw, scale)
+    assert_close(out[0], want[0], torch.bfloat16, "paged HCA, 69 splits")
+    del cache, rows
+    torch.cuda.empty_cache()
