@@ -663,6 +663,42 @@ def test_attend_decode_split_and_invalid_indices():
         assert_close(out[s], want, torch.bfloat16, f"seq {s}")
 
 
+def test_attend_decode_split_extreme_sinks():
+    # the split merge's sink term at both ends: heads whose sink outweighs
+    # every logit by e^40 (outputs near 0, each split's weight 2^-57 or
+    # less), heads whose sink is negligible, the rest ordinary; CSA (5
+    # splits per sequence) and HCA (32 splits) decode
+    say("attend decode split, extreme sinks")
+    gen = torch.Generator().manual_seed(44)
+    sink = torch.randn(64, generator=gen)
+    sink[:16] = 40.0
+    sink[16:32] = -40.0
+    scale = 1 / math.sqrt(512)
+    m, k, nw, b, n_comp = 4, 96, 128, 2, 500
+    t = n_comp * m + 2
+    q = torch.randn((b, 1, 64, 512), generator=gen).to(torch.bfloat16)
+    Cc = torch.randn((b, n_comp, 512), generator=gen).to(torch.bfloat16)
+    raw = torch.randn((b, nw, 512), generator=gen).to(torch.bfloat16)
+    idx = torch.stack([torch.sort(torch.randperm(n_comp, generator=gen)[:k]).values for _ in range(b)])
+    idx = idx.to(torch.int32)[:, None, :]
+    raw_pos0 = t - nw + 1
+    assert L.load_library().csa_attend_workspace_size(b, 1, t, n_comp, 64, 512, k, m, nw, 1) > 0
+    out = L.csa_attend(g(q), g(Cc), g(idx), g(raw), g(sink), t, m, nw, scale, raw_pos0=raw_pos0)
+    mp, nh_comp = 128, 2000
+    th = nh_comp * mp + 5
+    Ch = torch.randn((b, nh_comp, 512), generator=gen).to(torch.bfloat16)
+    assert L.load_library().hca_attend_workspace_size(b, 1, th, nh_comp, 64, 512, mp, nw, 1) > 0
+    outh = L.hca_attend(g(q), g(Ch), g(raw), g(sink), th, mp, nw, scale, raw_pos0=th - nw + 1)
+    torch.cuda.synchronize()
+    for s in range(b):
+        want = O.csa_attend(to64(q[s]), to64(Cc[s]), idx[s].numpy(), to64(raw[s]), raw_pos0, to64(sink), [t], nw,
+                            scale, m)
+        assert_close(out[s], want, torch.bfloat16, f"csa seq {s}")
+        wanth = O.hca_attend(to64(q[s]), to64(Ch[s]), to64(raw[s]), th - nw + 1, to64(sink), [th], mp, nw, scale)
+        assert_close(outh[s], wanth, torch.bfloat16, f"hca seq {s}")
+        assert np.abs(want[0, :16]).max() < 1e-10 and np.abs(wanth[0, :16]).max() < 1e-10
+
+
 def test_attend_generic_bf16_small_heads():
     say("attend generic bf16")
     gen = torch.Generator().manual_seed(42)
