@@ -1337,16 +1337,20 @@ static bool attend_mfma_ok(int dtype, int64_t n_h, int64_t c, int64_t k) {
   return dtype == 1 && c == kC && n_h % kHG == 0 && k <= kMaxSel;
 }
 
+#ifndef CSA_SPLIT_MIN_TILES
+#define CSA_SPLIT_MIN_TILES 4
+#endif
+constexpr int64_t kSplitMinTiles = CSA_SPLIT_MIN_TILES;
 static int attend_nsplit(int64_t b, int64_t n_q, int64_t n_h, int64_t nmax) {
   const int64_t items = b * n_q * (n_h / kHG);
   if (items >= 512) return 1;
   // about one workgroup per CU: every split also writes (and the combine
   // reads) a 128 KiB float partial, which more splits would multiply
   int64_t ns = (256 + items - 1) / items;
-  // at least eight tiles per split: a split pays a fixed cost (index
+  // at least kSplitMinTiles tiles per split: a split pays a fixed cost (index
   // compaction, the first gathers, a 128 KiB float partial written and
   // merged again) that fewer tiles do not amortise
-  const int64_t cap = (nmax + 8 * kT - 1) / (8 * kT);
+  const int64_t cap = (nmax + kSplitMinTiles * kT - 1) / (kSplitMinTiles * kT);
   if (ns > cap) ns = cap;
   if (ns < 1) ns = 1;
   if (ns > 64) ns = 64;
