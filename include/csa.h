@@ -57,7 +57,8 @@ enum {
   CSA_EINVAL = -1,  /* an argument is out of range or inconsistent      */
   CSA_ENOTSUP = -2, /* valid, but no kernel handles this shape / dtype  */
   CSA_ENOSPC = -3,  /* the workspace given is smaller than required     */
-  CSA_EHIP = -4     /* the HIP runtime reported an error at launch      */
+  CSA_EHIP = -4,    /* the HIP runtime reported an error at launch      */
+  CSA_EBOUNDS = -5  /* debug builds only: a gather's bounds check failed */
 };
 
 /* Library version string, e.g. "csa-mi355x 0.1.0". */
@@ -65,6 +66,25 @@ const char* csa_version(void);
 
 /* Human-readable name of a return code. */
 const char* csa_strerror(int code);
+
+/*
+ * Debug builds.  libcsa_debug.so is the library compiled with CSA_DEBUG=1:
+ * csa_attend and hca_attend check every row their kernels gather from flat
+ * caches (a compressed entry s must satisfy 0 <= s < n_comp, a window row
+ * must lie between the query's first window row and its own row).  A row
+ * outside those bounds is not read; the call waits for its stream and
+ * returns CSA_EBOUNDS instead of CSA_OK.  Paged calls are not checked.
+ * Release builds export the same two functions: csa_debug_enabled returns
+ * 0 and csa_debug_set_entry_limit returns CSA_ENOTSUP.
+ *
+ * csa_debug_enabled -- 1 in a debug build, else 0.
+ * csa_debug_set_entry_limit -- a tighter bound on compressed entry rows
+ *   (rows >= limit fail the check; INT64_MAX restores the default), for
+ *   tests that exercise the check with valid inputs.  limit < 0 is
+ *   CSA_EINVAL.  Affects every later call on the current device.
+ */
+int csa_debug_enabled(void);
+int csa_debug_set_entry_limit(int64_t limit);
 
 /*
  * csa_compress -- token-level KV compressor, CSA (overlap = 1) or HCA

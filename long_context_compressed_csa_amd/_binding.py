@@ -36,6 +36,8 @@ _f32 = ctypes.c_float
 SIGNATURES = {
     "csa_version": (ctypes.c_char_p, []),
     "csa_strerror": (ctypes.c_char_p, [_int]),
+    "csa_debug_enabled": (_int, []),
+    "csa_debug_set_entry_limit": (_int, [ctypes.c_int64]),
     "csa_compress": (_int, [_vp] * 8 + [_i64] * 4 + [_int, _int, _vp, _i64, _vp]),
     "csa_index_topk": (_int, [_vp, _vp, _vp, _i64] + [_i64] * 8 + [_int, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_workspace_size": (_sz, [_i64] * 4),
@@ -105,13 +107,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         if not os.path.exists(path):
             raise RuntimeError(
                 f"{path} is missing: build it with `python -m long_context_compressed_csa_amd.build`")
-        lib = ctypes.CDLL(path)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = lib
+        _lib = open_library(path)
     return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A build of the library at `path` (e.g. the CSA_DEBUG build,
+    libcsa_debug.so) with every entry point's prototype set; not cached."""
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
 
 
 def strerror(code: int) -> str:

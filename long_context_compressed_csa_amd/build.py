@@ -23,6 +23,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
+# the bounds-checked debug library: attend.hip and abi.hip built with
+# CSA_DEBUG=1, every other object shared with the release build
+DEBUG_LIB = os.path.join(PKG, "libcsa_debug.so")
+DEBUG_SOURCES = ("attend.hip", "abi.hip")
 
 ARCH = "gfx950"
 CXXFLAGS = [
@@ -79,7 +83,30 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    build_debug(verbose)
     return LIB
+
+
+def build_debug(verbose: bool = False) -> str:
+    """Build DEBUG_LIB; the release objects must exist (build() does both)."""
+    hipcc = _hipcc()
+    out = os.path.join(BUILD, "debug")
+    os.makedirs(out, exist_ok=True)
+    objs, cmds = [], []
+    for s in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        name = os.path.basename(s)
+        if name in DEBUG_SOURCES:
+            o = os.path.join(out, name + ".o")
+            cmds.append([hipcc, *CXXFLAGS, *EXTRA_FLAGS.get(name, []), "-DCSA_DEBUG=1", "-c", s, "-o", o])
+        else:
+            o = os.path.join(BUILD, name + ".o")
+        objs.append(o)
+    with cf.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = DEBUG_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, DEBUG_LIB)
+    return DEBUG_LIB
 
 
 # Host-side sanitizer build: the files whose host code validates arguments

@@ -26,6 +26,16 @@ inline uintptr_t row_align(int64_t row_bytes, int64_t es) { return row_bytes % 1
 inline bool stride_ok(int64_t stride_elems, int64_t es, uintptr_t a) { return (stride_elems * es) % (int64_t)a == 0; }
 inline int launched(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_EHIP; }
 
+// Debug builds: a launch that went through turns into CSA_EBOUNDS when a
+// gather's bounds check failed (this waits for the stream).
+#if CSA_DEBUG
+inline int debug_checked(int rc, void* stream) {
+  return rc == CSA_OK && csa::debug_take_oob((hipStream_t)stream) ? CSA_EBOUNDS : rc;
+}
+#else
+inline int debug_checked(int rc, void*) { return rc; }
+#endif
+
 inline int64_t visible(int64_t t, int64_t m) { return (t + 1) / m; }
 
 // Window rows of queries t0..t0+n_q-1 must lie inside kv_raw.
@@ -77,8 +87,21 @@ const char* csa_strerror(int code) {
     case CSA_ENOTSUP: return "unsupported shape or dtype";
     case CSA_ENOSPC: return "workspace too small";
     case CSA_EHIP: return "HIP launch error";
+    case CSA_EBOUNDS: return "bounds check failed (debug build)";
     default: return "unknown error";
   }
+}
+
+int csa_debug_enabled(void) { return CSA_DEBUG ? 1 : 0; }
+
+int csa_debug_set_entry_limit(int64_t limit) {
+#if CSA_DEBUG
+  if (limit < 0) return CSA_EINVAL;
+  return launched(csa::debug_set_entry_limit(limit));
+#else
+  (void)limit;
+  return CSA_ENOTSUP;
+#endif
 }
 
 int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const void* Ba,
@@ -330,9 +353,9 @@ int csa_attend(const void* q, const void* Ccomp, int64_t comp_bstride, const int
   if (ws_bytes < need) return CSA_ENOSPC;
   const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c;
   const int64_t rbs = raw_bstride > 0 ? raw_bstride : n_raw * c;
-  return launched(csa::launch_attend(0, q, Ccomp, cbs, idx, kv_raw, rbs, raw_pos0, sink, b, n_q, t0,
+  return debug_checked(launched(csa::launch_attend(0, q, Ccomp, cbs, idx, kv_raw, rbs, raw_pos0, sink, b, n_q, t0,
                                      n_comp, n_h, c, k, m, n_win, scale, dtype, workspace, out,
-                                     (hipStream_t)stream));
+                                     (hipStream_t)stream)), stream);
 }
 
 int csa_attend_norm_rope(const void* q, const float* gamma_q, float eps, int64_t rope_dims, double base,
@@ -400,9 +423,9 @@ int hca_attend(const void* q, const void* Ccomp, int64_t comp_bstride, const voi
   if (ws_bytes < need) return CSA_ENOSPC;
   const int64_t cbs = comp_bstride > 0 ? comp_bstride : n_comp * c;
   const int64_t rbs = raw_bstride > 0 ? raw_bstride : n_raw * c;
-  return launched(csa::launch_attend(1, q, Ccomp, cbs, nullptr, kv_raw, rbs, raw_pos0, sink, b, n_q,
+  return debug_checked(launched(csa::launch_attend(1, q, Ccomp, cbs, nullptr, kv_raw, rbs, raw_pos0, sink, b, n_q,
                                      t0, n_comp, n_h, c, 0, m_prime, n_win, scale, dtype, workspace,
-                                     out, (hipStream_t)stream));
+                                     out, (hipStream_t)stream)), stream);
 }
 
 size_t hca_layer_workspace_size(int64_t b, int64_t n, int64_t n_h, int64_t c, int64_t m_prime,

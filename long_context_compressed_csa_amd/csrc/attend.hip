@@ -240,6 +240,17 @@ constexpr int kXB = 64 * 8 * 4;   // one wave's partial S^T: 64 lanes x 8 floats
 // operand; the output's last rope_dims dimensions are turned back by -t in
 // float32 before the bf16 store (split partial states are turned before
 // they are written: the merge is linear).
+#if CSA_DEBUG
+// Debug builds: every row the attention gathers (flat caches) is checked
+// against the bounds the call implies -- a compressed entry below n_comp
+// (and below a host-set limit, which tests lower to force the check), a
+// window row between the window's first row and the query's own.  A row
+// outside them is not read (the query's own window row is gathered in its
+// place) and the flag is raised; the host reports it after the launch.
+__device__ unsigned int csa_dbg_oob = 0;
+__device__ long long csa_dbg_entry_limit = 0x7fffffffffffffffLL;
+#endif
+
 template <int SPLIT, int PG, int DENSE, int NRQ>
 __global__ __launch_bounds__(256, 2) void attend_ds(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Ccomp, int64_t cbs,
@@ -438,6 +449,15 @@ __global__ __launch_bounds__(256, 2) void attend_ds(
       we = we >= ring_i ? we - ring_i : we;
     }
     const bf16_t* p = (j < nseli ? cbase + (int64_t)e * kC : rbase + (int64_t)we * kC) + 8 * g4;
+#if CSA_DEBUG
+    if (!PG) {
+      const bool bad = j < nseli ? (e < 0 || e >= n_comp || e >= csa_dbg_entry_limit) : (we < 0 || we > t - wlo);
+      if (bad) {
+        atomicOr(&csa_dbg_oob, 1u);
+        p = rbase + (t - wlo) * (int64_t)kC + 8 * g4;
+      }
+    }
+#endif
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       const int b = wave_u + rr * NW;
@@ -1517,5 +1537,20 @@ hipError_t launch_attend_paged(int dense, const void* q, const void* pool, const
                        (int)n_h, ns, (bf16_t*)out);
   return hipGetLastError();
 }
+
+#if CSA_DEBUG
+// Wait for the stream, then read and clear the bounds flag of the gathers.
+bool debug_take_oob(hipStream_t st) {
+  unsigned int v = 0, z = 0;
+  if (hipStreamSynchronize(st) != hipSuccess) return true;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(csa_dbg_oob), sizeof v) != hipSuccess) return true;
+  if (v != 0 && hipMemcpyToSymbol(HIP_SYMBOL(csa_dbg_oob), &z, sizeof z) != hipSuccess) return true;
+  return v != 0;
+}
+hipError_t debug_set_entry_limit(int64_t limit) {
+  const long long v = (long long)limit;
+  return hipMemcpyToSymbol(HIP_SYMBOL(csa_dbg_entry_limit), &v, sizeof v);
+}
+#endif
 
 }  // namespace csa

@@ -1,6 +1,10 @@
 // Device helpers shared by the CSA/HCA kernels (gfx950 / CDNA4).
 #pragma once
 
+// CSA_DEBUG=1 builds the bounds-checked debug library (libcsa_debug.so).
+#ifndef CSA_DEBUG
+#define CSA_DEBUG 0
+#endif
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>

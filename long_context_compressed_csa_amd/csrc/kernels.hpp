@@ -39,6 +39,10 @@ hipError_t launch_attend_norm_rope(int dense, const void* q, const float* gq, fl
                                    const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink, int64_t b,
                                    int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h, int64_t k, int64_t m,
                                    int64_t n_win, float scale, void* ws, void* out, hipStream_t st);
+#if CSA_DEBUG
+bool debug_take_oob(hipStream_t st);
+hipError_t debug_set_entry_limit(int64_t limit);
+#endif
 hipError_t launch_attend(int dense, const void* q, const void* Ccomp, int64_t cbs, const int32_t* idx,
                          const void* kv_raw, int64_t rbs, int64_t raw_pos0, const float* sink,
                          int64_t b, int64_t n_q, int64_t t0, int64_t n_comp, int64_t n_h,

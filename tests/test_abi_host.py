@@ -445,3 +445,20 @@ def test_paged_geometry_and_validation(lib):
                                     128, 128, 0.05, 1, FAKE, ws_bytes, FAKE, None)
     assert hca((1 << 25) - 127) == ENOTSUP
     assert hca((1 << 25) - 128) == ENOSPC      # supported; its split partials need more workspace
+
+
+def test_release_build_has_no_debug_checks(lib):
+    # the debug entry points exist in every build; the release build
+    # reports that it carries no bounds checks
+    assert lib.csa_debug_enabled() == 0
+    assert lib.csa_debug_set_entry_limit(10) == ENOTSUP
+    assert lib.csa_strerror(-5).decode() == "bounds check failed (debug build)"
+
+
+def test_debug_build_exports_and_enables_checks():
+    from long_context_compressed_csa_amd import build as B
+    if not os.path.exists(B.DEBUG_LIB):
+        pytest.fail(f"{B.DEBUG_LIB} is missing: the build makes it beside libcsa.so")
+    dbg = L._binding.open_library(B.DEBUG_LIB)
+    assert dbg.csa_debug_enabled() == 1
+    assert dbg.csa_debug_set_entry_limit(-1) == EINVAL
